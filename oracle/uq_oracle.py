@@ -1,0 +1,436 @@
+"""Plain float64 reference for the UltraQuant FP4 KV-cache write path and decode.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the library.
+
+Sources, cited by page title and section:
+  [review]      "[arXiv 2606.20474] UltraQuant: 컨텍스트가 긴 에이전트를 위한 4비트 KV 캐싱"
+                (manon006.tistory.com/395)
+  [commentary]  "kv-cache-4bit-serving-residency-collapse" commentary on the same
+                paper (pheeree.github.io, 2026-09-01), whose footnotes quote the paper
+  [tq-guide]    "TurboQuant 완전 정리 - 이론 최적에 근접한 KV 캐시·벡터 검색 양자화와
+                vLLM 실측" (juhoplayground.github.io)
+
+What the method computes ([review] §3.1, §3.2; [commentary] footnote 2):
+  write path   x = WHT(row); per 32-channel group m = max|x_i|; scale exponent E
+               stored as the UE8M0 byte E + 127; each x_i / 2**E rounded to an
+               FP4 E2M1 level; 32 codes packed two per byte plus the scale byte,
+               17 bytes per group (4.25 bits per element).
+  dequant      value = code * 2**(byte - 127).
+  decode       the query is rotated into the key basis and rounded to FP8 E4M3
+               ([review] §3.2, §4.2); attention runs over the dequantized cache.
+
+Readings where the pages are silent (each listed with its reason in the design doc):
+  R1  K and V are both rotated; the attention output is rotated back.
+  R2  WHT = Sylvester Hadamard in natural order, scaled by c_d = sqrt(1/d),
+      over the whole head_dim, no random signs.
+  R3  E = the least integer with m <= 6 * 2**E (never clips), clamped to
+      [-127, 127]; an all-zero group gets E = -127.
+  R4  E2M1 rounding is to nearest, ties to the even code; the sign bit is the
+      sign of the value, so a negative value that rounds to zero is code 8.
+  R5  Every rounding decision is taken on the float64 value (no float32 step).
+  R6  FP8 is OCP E4M3 (bias 7, max 448), round to nearest even, saturating at
+      448, sign copied for zero; no query scale.
+  R7  sm_scale multiplies the logits; GQA maps query head h to KV head
+      h // (H_q / H_kv).
+  R8  Cache page layout: see ``head_block_bytes`` and the ``*_offset`` helpers.
+
+Parity pins: tests/test_oracle_pins.py (no function here is "parity unpinned").
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "PAGE_SIZE", "GROUP", "FMT_FP4", "FMT_FP8", "FMT_BF16",
+    "sylvester_hadamard", "wht_scale", "wht",
+    "scale_exponent", "E2M1_LEVELS", "e2m1_encode", "e2m1_decode",
+    "quantize_fp4", "dequantize_fp4", "pack_nibbles", "unpack_nibbles",
+    "e4m3_decode", "e4m3_encode", "bf16_bits_to_f64", "f32_to_f64", "bf16_round_bits",
+    "head_block_bytes", "page_bytes", "new_pool",
+    "fp4_k_code_offset", "fp4_k_scale_offset", "fp4_v_code_offset", "fp4_v_scale_offset",
+    "fp8_k_offset", "fp8_v_offset", "bf16_k_index", "bf16_v_index",
+    "append", "gather_dequant", "rotate_quantize_query", "attention",
+    "decode_attention", "decode_attention_rows",
+]
+
+PAGE_SIZE = 16          # tokens per page (vLLM-style paged cache; [review] §6.5.1)
+GROUP = 32              # channels per scale group ([review] §3.1 table: "Group size")
+FMT_FP4, FMT_FP8, FMT_BF16 = 0, 1, 2
+
+
+# --------------------------------------------------------------------------
+# Rotation ([review] §3.1: Walsh-Hadamard rotation; reading R2)
+# --------------------------------------------------------------------------
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """Sylvester Hadamard matrix: H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("Hadamard order must be a power of two")
+    h = np.ones((1, 1), dtype=np.int64)
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def wht_scale(d: int) -> float:
+    """c_d = sqrt(1/d): makes c_d * H_d orthogonal (and, H being symmetric, self-inverse)."""
+    return float(np.sqrt(1.0 / d))
+
+
+def wht(x) -> np.ndarray:
+    """Normalized Walsh-Hadamard transform over the last axis: x -> c_d * (H_d x).
+
+    The sum is taken first and multiplied by c_d once.  For bf16 input rows whose
+    nonzero exponents span at most 38 binades (fp32: 22) every partial sum is an
+    exact float64, so any summation order gives the same result.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    h = sylvester_hadamard(d).astype(np.float64)
+    return (x @ h) * wht_scale(d)      # H symmetric: (H x)^T = x^T H
+
+
+# --------------------------------------------------------------------------
+# UE8M0 group scale ([review] §3.1, §3.2; [commentary] footnote 2; reading R3)
+# --------------------------------------------------------------------------
+def scale_exponent(m) -> np.ndarray:
+    """Least integer E with m <= 6 * 2**E, clamped to [-127, 127]; m == 0 gives -127.
+
+    A float estimate ceil(log2(m/6)) is corrected with exact comparisons against
+    6 * 2**E (exact in float64 for |E| <= 129) until E satisfies the definition:
+    m <= 6 * 2**E and m > 6 * 2**(E-1).
+    """
+    m = np.asarray(m, dtype=np.float64)
+    out = np.full(m.shape, -127, dtype=np.int64)
+    nz = m > 0
+    mz = m[nz]
+    with np.errstate(divide="ignore"):
+        e = np.ceil(np.log2(mz / 6.0))
+    e = np.clip(e, -128, 129).astype(np.int64)
+    for _ in range(4):
+        too_small = mz > np.ldexp(6.0, e)                    # definition violated: raise E
+        e = np.where(too_small & (e < 129), e + 1, e)
+        not_least = (e > -128) & (mz <= np.ldexp(6.0, e - 1))  # a smaller E also works
+        e = np.where(not_least, e - 1, e)
+    out[nz] = np.clip(e, -127, 127)
+    return out
+
+
+# --------------------------------------------------------------------------
+# FP4 E2M1 codes ([review] §3.1 table "Code grid", §6.5; readings R4, R5)
+# --------------------------------------------------------------------------
+E2M1_LEVELS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])  # magnitude codes 0..7
+
+
+def _nearest_even(a: np.ndarray, table: np.ndarray) -> np.ndarray:
+    """Index of the entry of the increasing ``table`` nearest to a >= 0, ties to the
+    even index; values above the last entry map to the last index (saturation)."""
+    a = np.asarray(a, dtype=np.float64)
+    i = np.searchsorted(table, a, side="right") - 1          # table[i] <= a
+    i = np.clip(i, 0, len(table) - 1)
+    top = i == len(table) - 1
+    j = np.minimum(i + 1, len(table) - 1)
+    below = a - table[i]                                     # distance to the lower neighbour
+    above = table[j] - a                                     # distance to the upper neighbour
+    pick_up = (above < below) | ((above == below) & (i % 2 == 1))
+    res = np.where(pick_up & ~top, j, i)
+    return res.astype(np.int64)
+
+
+def e2m1_encode(r) -> np.ndarray:
+    """FP4 E2M1 code of a value already divided by its group scale.
+
+    Bit 3 is the sign of r (signbit, so -0.0 and small negatives give 8); bits
+    0..2 index the nearest level, ties to the even code; |r| > 6 saturates to 6.
+    """
+    r = np.asarray(r, dtype=np.float64)
+    mag = _nearest_even(np.abs(r), E2M1_LEVELS)
+    return (mag | (np.signbit(r).astype(np.int64) << 3)).astype(np.uint8)
+
+
+def e2m1_decode(code) -> np.ndarray:
+    code = np.asarray(code, dtype=np.int64)
+    mag = E2M1_LEVELS[code & 7]
+    return np.where(code & 8, -mag, mag)
+
+
+def quantize_fp4(x):
+    """Quantize rotated rows x[..., d] per 32-channel group.
+
+    Returns (codes [..., d] uint8 in 0..15, scale bytes [..., d/32] uint8).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    g = x.reshape(x.shape[:-1] + (d // GROUP, GROUP))
+    m = np.max(np.abs(g), axis=-1)                    # group absmax
+    e = scale_exponent(m)
+    r = np.ldexp(g, -e[..., None])                    # exact division by 2**E
+    codes = e2m1_encode(r).reshape(x.shape)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def dequantize_fp4(codes, scale_bytes) -> np.ndarray:
+    """value = code * 2**(byte - 127) ([review] §3.2; [commentary] footnote 2)."""
+    codes = np.asarray(codes)
+    d = codes.shape[-1]
+    v = e2m1_decode(codes).reshape(codes.shape[:-1] + (d // GROUP, GROUP))
+    e = np.asarray(scale_bytes, dtype=np.int64) - 127
+    return np.ldexp(v, e[..., None]).reshape(codes.shape)
+
+
+def pack_nibbles(codes) -> np.ndarray:
+    """Two codes per byte: element 2j in the low nibble, 2j+1 in the high nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(b) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 15
+    out[..., 1::2] = b >> 4
+    return out
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3 (OCP) for the query ([review] §3.2, §4.2) and the FP8 baseline; R6
+# --------------------------------------------------------------------------
+def e4m3_decode(b) -> np.ndarray:
+    """OCP E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is
+    subnormal (m/8 * 2**-6); S.1111.111 is NaN; no infinities."""
+    b = np.asarray(b, dtype=np.int64)
+    s = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    val = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    val = np.where((e == 15) & ((b & 7) == 7), np.nan, val)
+    return s * val
+
+
+_E4M3_POS = e4m3_decode(np.arange(0x7F))      # codes 0x00..0x7E, increasing, max 448
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Round float64 to OCP E4M3: nearest, ties to even code, |v| > 448 saturates
+    to 448 (0x7E / 0xFE), sign bit copied (so -0.0 gives 0x80).  Inputs are finite."""
+    v = np.asarray(v, dtype=np.float64)
+    mag = _nearest_even(np.abs(v), _E4M3_POS)
+    return (mag | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) to float64, exactly."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def f32_to_f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def bf16_round_bits(x32) -> np.ndarray:
+    """float32 values to bf16 bits, round to nearest, ties to even (finite inputs):
+    choose the nearer of the two bf16 neighbours of x."""
+    x = np.asarray(x32, dtype=np.float32)
+    u = x.view(np.uint32)
+    lo_bits = (u >> 16).astype(np.uint32)                     # truncation toward zero
+    lo = bf16_bits_to_f64(lo_bits.astype(np.uint16))
+    hi = bf16_bits_to_f64((lo_bits + 1).astype(np.uint16))    # next bf16 away from zero
+    a = np.abs(x.astype(np.float64))
+    d_lo, d_hi = a - np.abs(lo), np.abs(hi) - a
+    up = (d_hi < d_lo) | ((d_hi == d_lo) & (lo_bits & 1 == 1))
+    return np.where(up, lo_bits + 1, lo_bits).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# Paged cache layout (reading R8).  Pools are uint8 [num_pages][H_kv][block].
+#   FP4 K block: codes[16 tok][d/2] (token-major) then scales[16 tok][d/32]
+#   FP4 V block: codes[d/2 channel pairs][16 tok] then scales[d/32 groups][16 tok]
+#   FP8 K block: [16 tok][d] bytes;  FP8 V block: [d][16 tok] bytes
+#   BF16 K block: [16 tok][d] bf16;  BF16 V block: [d][16 tok] bf16 (little endian)
+# --------------------------------------------------------------------------
+def head_block_bytes(fmt: int, d: int) -> int:
+    if fmt == FMT_FP4:
+        return PAGE_SIZE * (d // 2) + PAGE_SIZE * (d // GROUP)   # 17 bytes per 32 elements
+    if fmt == FMT_FP8:
+        return PAGE_SIZE * d
+    if fmt == FMT_BF16:
+        return PAGE_SIZE * d * 2
+    raise ValueError(fmt)
+
+
+def page_bytes(fmt: int, num_kv_heads: int, d: int) -> int:
+    return num_kv_heads * head_block_bytes(fmt, d)
+
+
+def new_pool(fmt: int, num_pages: int, num_kv_heads: int, d: int) -> np.ndarray:
+    return np.zeros((num_pages, num_kv_heads, head_block_bytes(fmt, d)), dtype=np.uint8)
+
+
+def fp4_k_code_offset(tok, byte, d):
+    return tok * (d // 2) + byte
+
+
+def fp4_k_scale_offset(tok, group, d):
+    return PAGE_SIZE * (d // 2) + tok * (d // GROUP) + group
+
+
+def fp4_v_code_offset(tok, pair, d):
+    return pair * PAGE_SIZE + tok
+
+
+def fp4_v_scale_offset(tok, group, d):
+    return PAGE_SIZE * (d // 2) + group * PAGE_SIZE + tok
+
+
+def fp8_k_offset(tok, ch, d):
+    return tok * d + ch
+
+
+def fp8_v_offset(tok, ch, d):
+    return ch * PAGE_SIZE + tok
+
+
+def bf16_k_index(tok, ch, d):      # index into the block viewed as uint16
+    return tok * d + ch
+
+
+def bf16_v_index(tok, ch, d):
+    return ch * PAGE_SIZE + tok
+
+
+def append(fmt, k_pool, v_pool, k_new, v_new, slot_mapping, in_dtype="bf16"):
+    """Write new tokens into the paged pools in place.
+
+    k_new, v_new: [T][H_kv][d] as bf16 bits (uint16, in_dtype "bf16") or float32
+    (in_dtype "f32").  slot_mapping[t] = page * 16 + offset; a negative slot skips
+    the token.  FP4 rotates and quantizes ([review] §3.1); FP8 rounds each value to
+    E4M3 with scale 1; BF16 stores the value (float32 input rounded to bf16).
+    """
+    k_new = np.asarray(k_new)
+    T, H, d = k_new.shape
+    to64 = bf16_bits_to_f64 if in_dtype == "bf16" else f32_to_f64
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    keep = np.nonzero(slots >= 0)[0]
+    page, off = slots[keep] // PAGE_SIZE, slots[keep] % PAGE_SIZE
+    for pool, src, is_v in ((k_pool, k_new, False), (v_pool, np.asarray(v_new), True)):
+        flat = pool.reshape(pool.shape[0], H, -1)
+        x = to64(src[keep])                                   # [n][H][d] exact
+        if fmt == FMT_FP4:
+            codes, sbytes = quantize_fp4(wht(x))              # [n][H][d], [n][H][d/32]
+            packed = pack_nibbles(codes)                      # [n][H][d/2]
+            j = np.arange(d // 2)
+            g = np.arange(d // GROUP)
+            for h in range(H):
+                if is_v:
+                    flat[page[:, None], h, fp4_v_code_offset(off[:, None], j[None, :], d)] = packed[:, h]
+                    flat[page[:, None], h, fp4_v_scale_offset(off[:, None], g[None, :], d)] = sbytes[:, h]
+                else:
+                    flat[page[:, None], h, fp4_k_code_offset(off[:, None], j[None, :], d)] = packed[:, h]
+                    flat[page[:, None], h, fp4_k_scale_offset(off[:, None], g[None, :], d)] = sbytes[:, h]
+        elif fmt == FMT_FP8:
+            b = e4m3_encode(x)
+            c = np.arange(d)
+            fn = fp8_v_offset if is_v else fp8_k_offset
+            for h in range(H):
+                flat[page[:, None], h, fn(off[:, None], c[None, :], d)] = b[:, h]
+        elif fmt == FMT_BF16:
+            bits = src[keep].astype(np.uint16) if in_dtype == "bf16" else bf16_round_bits(src[keep])
+            c = np.arange(d)
+            fn = bf16_v_index if is_v else bf16_k_index
+            f16 = flat.view(np.uint16)
+            for h in range(H):
+                f16[page[:, None], h, fn(off[:, None], c[None, :], d)] = bits[:, h]
+        else:
+            raise ValueError(fmt)
+
+
+def gather_dequant(fmt, pool, page_row, seq_len, head, d, is_v) -> np.ndarray:
+    """Dequantized [seq_len][d] rows of one KV head of one sequence: token t lives
+    in page page_row[t // 16] at offset t % 16."""
+    t = np.arange(seq_len)
+    page = np.asarray(page_row, dtype=np.int64)[t // PAGE_SIZE][:, None]
+    off = (t % PAGE_SIZE)[:, None]
+    H = pool.shape[1]
+    flat = pool.reshape(pool.shape[0], H, -1)
+    if fmt == FMT_FP4:
+        j = np.arange(d // 2)[None, :]
+        g = np.arange(d // GROUP)[None, :]
+        if is_v:
+            packed = flat[page, head, fp4_v_code_offset(off, j, d)]
+            sb = flat[page, head, fp4_v_scale_offset(off, g, d)]
+        else:
+            packed = flat[page, head, fp4_k_code_offset(off, j, d)]
+            sb = flat[page, head, fp4_k_scale_offset(off, g, d)]
+        return dequantize_fp4(unpack_nibbles(packed), sb)
+    c = np.arange(d)[None, :]
+    if fmt == FMT_FP8:
+        fn = fp8_v_offset if is_v else fp8_k_offset
+        return e4m3_decode(flat[page, head, fn(off, c, d)])
+    if fmt == FMT_BF16:
+        fn = bf16_v_index if is_v else bf16_k_index
+        return bf16_bits_to_f64(flat.view(np.uint16)[page, head, fn(off, c, d)])
+    raise ValueError(fmt)
+
+
+def rotate_quantize_query(q, in_dtype="bf16") -> np.ndarray:
+    """E4M3 bytes of the rotated query ([review] §3.2: the query is rotated into the
+    key basis and rounded to FP8 E4M3), rounded directly from float64 (R5)."""
+    to64 = bf16_bits_to_f64 if in_dtype == "bf16" else f32_to_f64
+    return e4m3_encode(wht(to64(q)))
+
+
+def attention(qhat, k, v, sm_scale) -> np.ndarray:
+    """softmax(sm_scale * qhat k^T) v in float64 for one KV head: qhat [G][d],
+    k, v [L][d] -> [G][d]."""
+    s = sm_scale * (qhat @ k.T)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=1, keepdims=True)
+    return p @ v
+
+
+def decode_attention_rows(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table, seq_lens,
+                          sm_scale, rows, in_dtype="bf16") -> np.ndarray:
+    """Output rows for the (sequence, query head) pairs in ``rows`` ([n][2]).
+
+    FP4: q rotated and rounded to E4M3, output rotated back with the same
+    normalized WHT (self-inverse); FP8: q rounded to E4M3, no rotation; BF16: q
+    as given.  A sequence of length 0 gives a zero row.
+    """
+    q = np.asarray(q)
+    Hq = q.shape[1]
+    group = Hq // num_kv_heads
+    to64 = bf16_bits_to_f64 if in_dtype == "bf16" else f32_to_f64
+    out = np.zeros((len(rows), d))
+    cache = {}
+    for n, (b, h) in enumerate(rows):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        hk = h // group
+        key = (b, hk)
+        if key not in cache:
+            cache = {key: (gather_dequant(fmt, k_pool, page_table[b], L, hk, d, False),
+                           gather_dequant(fmt, v_pool, page_table[b], L, hk, d, True))}
+        K, V = cache[key]
+        if fmt == FMT_FP4:
+            qhat = e4m3_decode(rotate_quantize_query(q[b, h], in_dtype))
+        elif fmt == FMT_FP8:
+            qhat = e4m3_decode(e4m3_encode(to64(q[b, h])))
+        else:
+            qhat = to64(q[b, h])
+        o = attention(qhat[None, :], K, V, float(sm_scale))[0]
+        out[n] = wht(o) if fmt == FMT_FP4 else o
+    return out
+
+
+def decode_attention(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table, seq_lens,
+                     sm_scale, in_dtype="bf16") -> np.ndarray:
+    """All output rows [B][H_q][d] (float64)."""
+    q = np.asarray(q)
+    B, Hq = q.shape[0], q.shape[1]
+    rows = [(b, h) for b in range(B) for h in range(Hq)]
+    out = decode_attention_rows(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table,
+                                seq_lens, sm_scale, rows, in_dtype)
+    return out.reshape(B, Hq, d)

@@ -1,0 +1,401 @@
+"""Pins for the CPU oracle against facts the pages and mathematics fix.
+
+[review]     "[arXiv 2606.20474] UltraQuant: 컨텍스트가 긴 에이전트를 위한 4비트 KV 캐싱"
+[commentary] pheeree.github.io "kv-cache-4bit-serving-residency-collapse"
+[tq-guide]   "TurboQuant 완전 정리 - 이론 최적에 근접한 KV 캐시·벡터 검색 양자화와 vLLM 실측"
+
+Each pin uses an independent route (exact rational arithmetic, a library
+routine, a closed form, an invariant or a printed value), never a re-typing of
+the oracle's own formula.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle as O
+from bit_kv_cache_wht_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- rotation
+@pytest.mark.parametrize("d", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_hadamard_orthogonal(d):
+    h = O.sylvester_hadamard(d)
+    assert np.array_equal(h @ h.T, d * np.eye(d, dtype=np.int64))      # H H^T = d I
+    assert np.array_equal(h, h.T)
+
+
+@pytest.mark.parametrize("d", [2, 8, 64, 128])
+def test_hadamard_is_library_sylvester(d):
+    assert np.array_equal(O.sylvester_hadamard(d), scipy.linalg.hadamard(d))
+
+
+def test_wht_scale_is_correctly_rounded_sqrt():
+    assert O.wht_scale(64) == 0.125
+    c = O.wht_scale(128)
+    half_ulp = Fraction(math.ulp(c)) / 2
+    lo, hi = Fraction(c) - half_ulp, Fraction(c) + half_ulp
+    assert lo * lo < Fraction(1, 128) < hi * hi            # c is the nearest double to sqrt(1/128)
+
+
+def test_wht_orthogonality_invariants():
+    rng = np.random.default_rng(0)
+    x, y = rng.standard_normal((2, 50, 128))
+    wx, wy = O.wht(x), O.wht(y)
+    np.testing.assert_allclose(O.wht(wx), x, rtol=0, atol=1e-13)                # self-inverse
+    np.testing.assert_allclose(np.linalg.norm(wx, axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+    # [tq-guide] "직교성을 이용한 내적 보존": <Mx, My> = <x, y>
+    np.testing.assert_allclose((wx * wy).sum(1), (x * y).sum(1), rtol=1e-12, atol=1e-12)
+    e0 = np.zeros(128); e0[0] = 1.0
+    np.testing.assert_allclose(O.wht(e0), np.full(128, O.wht_scale(128)), rtol=0, atol=0)
+    np.testing.assert_allclose(O.wht(np.ones(128)), np.sqrt(128.0) * e0, rtol=1e-15, atol=1e-15)
+
+
+def _exact_hadamard_row(vals):
+    """H v in exact rational arithmetic (fast transform over Fractions)."""
+    v = [Fraction(float(t)) for t in vals]
+    h = 1
+    while h < len(v):
+        for i in range(0, len(v), 2 * h):
+            for j in range(i, i + h):
+                a, b = v[j], v[j + h]
+                v[j], v[j + h] = a + b, a - b
+        h *= 2
+    return v
+
+
+def test_wht_float64_sums_are_exact_on_bf16_rows():
+    # The oracle and the GPU sum in different orders; both are exact when the
+    # row's exponent span allows it.  Check against exact rationals.
+    wl = W.make_workload("pin", 1, 8, 8, 128, [24], [24], seed=42)
+    x = O.bf16_bits_to_f64(wl.k.reshape(-1, 128))
+    c = O.wht_scale(128)
+    got = O.wht(x)
+    for r in range(x.shape[0]):
+        exact = _exact_hadamard_row(x[r])
+        assert all(float(e) == e for e in exact)            # every sum representable
+        assert np.array_equal(got[r], np.array([float(e) * c for e in exact]))
+
+
+# ---------------------------------------------------------------- UE8M0 exponent
+def _least_exponent(m: float) -> int:
+    """Brute force: smallest integer E with m <= 6 * 2**E, exact rationals."""
+    fm = Fraction(m)
+    e = math.floor(math.log2(m)) - 4 if m > 0 else -2000
+    while Fraction(6) * Fraction(2) ** e < fm:
+        e += 1
+    while Fraction(6) * Fraction(2) ** (e - 1) >= fm:
+        e -= 1
+    return e
+
+
+def test_scale_exponent_against_brute_force():
+    vals = [0.0, 5e-324, 1e-310, 2.0 ** -1022, 1e-40, 6 * 2.0 ** -127, 6 * 2.0 ** -128, 1e-3, 0.5,
+            1.0, 1.5, 3.0, 5.999999999, 6.0, 6.000000001, 7.5, 12.0, 1e30, 6 * 2.0 ** 127,
+            6 * 2.0 ** 127 * (1 + 2 ** -52), 1e300]
+    for k in range(-140, 140, 7):
+        b = 6.0 * 2.0 ** k
+        vals += [b, np.nextafter(b, 0), np.nextafter(b, np.inf)]
+        f = 1.5 * 2.0 ** k                      # boundary of the closed form at fraction 1.5
+        vals += [f, np.nextafter(f, 0), np.nextafter(f, np.inf)]
+    rng = np.random.default_rng(1)
+    vals += list(np.exp(rng.uniform(-100, 100, 500)))
+    vals = np.array(vals)
+    got = O.scale_exponent(vals)
+    for m, e in zip(vals, got):
+        want = -127 if m == 0 else min(127, max(-127, _least_exponent(float(m))))
+        assert e == want, (m, e, want)
+
+
+def test_scale_exponent_never_clips_in_range():
+    rng = np.random.default_rng(2)
+    m = np.exp(rng.uniform(-60, 60, 10000))
+    e = O.scale_exponent(m)
+    assert np.all(m <= np.ldexp(6.0, e)) and np.all(m > np.ldexp(6.0, e - 1))
+
+
+# ---------------------------------------------------------------- E2M1
+def _e2m1_from_bits(code):
+    """Value of an E2M1 bit pattern from the format: 1 sign, 2 exponent (bias 1),
+    1 mantissa bit; exponent 0 is subnormal."""
+    s = -1.0 if code & 8 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    return s * (m * 0.5 if e == 0 else (1 + m / 2) * 2.0 ** (e - 1))
+
+
+def test_e2m1_levels_follow_bit_format():
+    for c in range(16):
+        assert O.e2m1_decode(c) == _e2m1_from_bits(c)
+        assert np.signbit(O.e2m1_decode(c)) == bool(c & 8)
+
+
+def test_e2m1_round_to_nearest_even_exhaustive():
+    levels = [_e2m1_from_bits(c) for c in range(8)]
+    for c, lv in enumerate(levels):
+        assert O.e2m1_encode(lv) == c and O.e2m1_encode(-lv) == c | 8
+    for c in range(7):
+        lo, hi = levels[c], levels[c + 1]
+        mid = (lo + hi) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert O.e2m1_encode(mid) == even
+        assert O.e2m1_encode(-mid) == even | 8
+        assert O.e2m1_encode(np.nextafter(mid, 0)) == c
+        assert O.e2m1_encode(np.nextafter(mid, 10)) == c + 1
+    assert O.e2m1_encode(6.5) == 7 and O.e2m1_encode(1e9) == 7 and O.e2m1_encode(-7.0) == 15
+    assert O.e2m1_encode(-0.0) == 8 and O.e2m1_encode(-0.1) == 8 and O.e2m1_encode(0.0) == 0
+
+
+def test_fp4_roundtrip_on_grid():
+    # North-star pin: values already on the E2M1 x 2^k grid come back exactly.
+    rng = np.random.default_rng(3)
+    mags = np.array([_e2m1_from_bits(c) for c in range(8)])
+    k = rng.integers(-20, 20, size=(2000, 1))
+    x = rng.choice(mags, size=(2000, 32)) * rng.choice([-1.0, 1.0], size=(2000, 32))
+    x = np.ldexp(x, k)
+    codes, sb = O.quantize_fp4(x)
+    assert np.array_equal(O.dequantize_fp4(codes, sb), x)
+
+
+def test_fp4_quantizer_distortion_vs_published_bounds():
+    # [tq-guide] 이론적 보장: D_mse >= 1/4^b; FP4 plus one scale byte per 32 is
+    # 4.25 bits per element.  The fixed grid sits above TurboQuant's 4-bit value.
+    g = golden("tq_distortion.json")
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((20000, 128))
+    x /= np.linalg.norm(x, axis=1, keepdims=True)
+    y = O.wht(x)
+    codes, sb = O.quantize_fp4(y)
+    mse = np.mean(np.sum((O.dequantize_fp4(codes, sb) - y) ** 2, axis=1))
+    assert mse >= 4.0 ** -4.25
+    assert mse >= g["lower_bound"][3] and mse >= g["turboquant_mse"][3]
+    assert mse < 0.03
+
+
+# ---------------------------------------------------------------- packing / format
+def test_pack_unpack_identity_all_bytes():
+    b = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    assert np.array_equal(O.pack_nibbles(O.unpack_nibbles(b)), b)
+    assert np.array_equal(O.unpack_nibbles(np.array([0x21], np.uint8)), [1, 2])  # low nibble first
+
+
+def test_format_facts_printed_on_pages():
+    f = golden("format_facts.json")
+    d = 128
+    blk = O.head_block_bytes(O.FMT_FP4, d)
+    groups = O.PAGE_SIZE * d // f["group_channels"]
+    assert blk == groups * f["bytes_per_group"]
+    assert 8 * blk / (O.PAGE_SIZE * d) == f["bits_per_element"]
+    assert 1 - f["code_bits"] / f["bits_per_element"] < f["within_fraction_of_ideal_4bit"]
+    T, H = 65536, 8
+    assert T // O.PAGE_SIZE * O.page_bytes(O.FMT_FP4, H, d) == T * H * d * 17 // 32
+    assert O.head_block_bytes(O.FMT_FP8, d) * 2 == O.head_block_bytes(O.FMT_BF16, d)
+
+
+@pytest.mark.parametrize("fmt", [O.FMT_FP4, O.FMT_FP8, O.FMT_BF16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_page_layout_is_a_bijection(fmt, d):
+    """Writing all 16 slots of a page touches every byte of each head block exactly
+    once, for K and for V: the offset helpers tile the block."""
+    counts = {}
+    for is_v in (False, True):
+        cnt = np.zeros(O.head_block_bytes(fmt, d), np.int64)
+        tok = np.arange(16)[:, None]
+        if fmt == O.FMT_FP4:
+            code = (O.fp4_v_code_offset if is_v else O.fp4_k_code_offset)(tok, np.arange(d // 2)[None], d)
+            sc = (O.fp4_v_scale_offset if is_v else O.fp4_k_scale_offset)(tok, np.arange(d // 32)[None], d)
+            np.add.at(cnt, code.ravel(), 1)
+            np.add.at(cnt, sc.ravel(), 1)
+        elif fmt == O.FMT_FP8:
+            off = (O.fp8_v_offset if is_v else O.fp8_k_offset)(tok, np.arange(d)[None], d)
+            np.add.at(cnt, off.ravel(), 1)
+        else:
+            idx = (O.bf16_v_index if is_v else O.bf16_k_index)(tok, np.arange(d)[None], d)
+            np.add.at(cnt, (2 * idx).ravel(), 1)
+            np.add.at(cnt, (2 * idx + 1).ravel(), 1)
+        counts[is_v] = cnt
+        assert np.all(cnt == 1)
+
+
+# ---------------------------------------------------------------- E4M3 / bf16
+def test_e4m3_decode_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_decode(codes)
+    nan = (codes & 0x7F) == 0x7F
+    assert np.all(np.isnan(got[nan])) and np.all(np.isnan(ref[nan]))
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+def test_e4m3_encode_roundtrip_and_ties():
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(finite)), finite)
+    pos = O.e4m3_decode(np.arange(0x7F))
+    mids = (pos[:-1] + pos[1:]) / 2
+    enc = O.e4m3_encode(mids)
+    lower = np.arange(0x7E)
+    assert np.array_equal(enc, np.where(lower % 2 == 0, lower, lower + 1))    # ties to even
+    assert O.e4m3_encode(449.0) == 0x7E and O.e4m3_encode(1e6) == 0x7E and O.e4m3_encode(-1e6) == 0xFE
+    assert O.e4m3_encode(-0.0) == 0x80
+
+
+def test_e4m3_encode_matches_torch_cast():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * np.float32(10.0) ** rng.integers(-4, 3, 200000),
+        (O.e4m3_decode(np.arange(0x7E)) + O.e4m3_decode(np.arange(1, 0x7F))) / 2,   # midpoints
+    ]).astype(np.float32)
+    x = np.concatenate([x, -x])
+    x = x[np.abs(x) < 464]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x.astype(np.float64)), ref)
+
+
+def test_bf16_round_matches_torch_cast():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal(100000).astype(np.float32)
+    ties = ((x.view(np.uint32) & 0xFFFF0000) | 0x8000).view(np.float32)     # exact halfway cases
+    x = np.concatenate([x, ties, -ties])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_round_bits(x), ref)
+
+
+# ---------------------------------------------------------------- cache write / read
+def _grid_workload(d=64, T=48, H=2, seed=7):
+    """Inputs whose rotation lands exactly on the FP4 grid (d = 64: c_d = 1/8 makes
+    the WHT exactly invertible), so the whole write path must be lossless."""
+    rng = np.random.default_rng(seed)
+    mags = np.array([_e2m1_from_bits(c) for c in range(8)])
+    y = rng.choice(mags, size=(T, H, d)) * rng.choice([-1.0, 1.0], size=(T, H, d))
+    y = np.ldexp(y.reshape(T, H, d // 32, 32), rng.integers(-3, 3, size=(T, H, d // 32, 1))).reshape(T, H, d)
+    x = O.wht(y)                                       # exact: y dyadic, c = 1/8
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    assert np.array_equal(O.wht(x), y)
+    return x.astype(np.float32), y
+
+
+def test_append_fp4_end_to_end_exact_on_d64():
+    x, y = _grid_workload()
+    T, H, d = x.shape
+    rng = np.random.default_rng(8)
+    pages = rng.permutation(8)
+    slots = (pages[np.arange(T) // 16] * 16 + np.arange(T) % 16).astype(np.int32)
+    kp, vp = O.new_pool(O.FMT_FP4, 8, H, d), O.new_pool(O.FMT_FP4, 8, H, d)
+    O.append(O.FMT_FP4, kp, vp, x, x, slots, in_dtype="f32")
+    table = pages[:3]
+    for h in range(H):
+        for is_v, pool in ((False, kp), (True, vp)):
+            assert np.array_equal(O.gather_dequant(O.FMT_FP4, pool, table, T, h, d, is_v), y[:, h])
+
+
+def test_append_skips_negative_slots_and_writes_nothing_else():
+    x, _ = _grid_workload(T=16, H=1)
+    kp, vp = O.new_pool(O.FMT_FP4, 2, 1, 64), O.new_pool(O.FMT_FP4, 2, 1, 64)
+    slots = np.full(16, -1, np.int32)
+    slots[3] = 16 + 5
+    O.append(O.FMT_FP4, kp, vp, x, x, slots, in_dtype="f32")
+    assert not kp[0].any() and not vp[0].any()
+    blk = kp[1, 0]
+    touched = np.concatenate([O.fp4_k_code_offset(5, np.arange(32), 64), O.fp4_k_scale_offset(5, np.arange(2), 64)])
+    mask = np.zeros(blk.size, bool); mask[touched] = True
+    assert not blk[~mask].any()
+
+
+# ---------------------------------------------------------------- attention
+def _brute_attention(q, K, V, scale):
+    """Plain loops in Python floats: softmax(scale q.k) weighted sum of v."""
+    s = [scale * sum(a * b for a, b in zip(q, k)) for k in K]
+    mx = max(s)
+    w = [math.exp(t - mx) for t in s]
+    tot = sum(w)
+    return [sum(w[j] * V[j][c] for j in range(len(V))) / tot for c in range(len(q))]
+
+
+def test_fp4_decode_equals_plain_attention_on_exact_inputs():
+    # Quantizer bypassed in effect: inputs are exact on the FP4 / E4M3 grids, so the
+    # rotated-and-unrotated FP4 path must equal attention on the original vectors.
+    d, T, H, G = 64, 40, 2, 3
+    x_k, _ = _grid_workload(d=d, T=T, H=H, seed=9)
+    x_v, _ = _grid_workload(d=d, T=T, H=H, seed=10)
+    rng = np.random.default_rng(11)
+    q_rot = rng.choice([0.0, 0.5, 1.0, -1.0, 2.0, -1.5, 0.25, -3.0], size=(2, H * G, d))
+    q = O.wht(q_rot).astype(np.float32)
+    assert np.array_equal(O.wht(q.astype(np.float64)), q_rot)
+    lens = np.array([T, 17])
+    pages = rng.permutation(6)
+    table = np.stack([pages[:3], pages[3:6]])
+    kp, vp = O.new_pool(O.FMT_FP4, 6, H, d), O.new_pool(O.FMT_FP4, 6, H, d)
+    for b in range(2):
+        L = lens[b]
+        slots = table[b][np.arange(L) // 16] * 16 + np.arange(L) % 16
+        O.append(O.FMT_FP4, kp, vp, x_k[:L], x_v[:L], slots, in_dtype="f32")
+    scale = 1 / math.sqrt(d)
+    out = O.decode_attention(O.FMT_FP4, kp, vp, H, d, q, table, lens, scale, in_dtype="f32")
+    for b in range(2):
+        for h in range(H * G):
+            ref = _brute_attention(q[b, h].astype(np.float64), x_k[:lens[b], h // G].astype(np.float64),
+                                   x_v[:lens[b], h // G].astype(np.float64), scale)
+            np.testing.assert_allclose(out[b, h], ref, rtol=0, atol=1e-12)
+
+
+def _small_pools(fmt, seed=12, B=3, H=2, G=4, d=128, lens=(1, 33, 70)):
+    wl = W.make_workload("attn", B, H * G, H, d, list(lens), list(lens), seed=seed)
+    kp, vp = O.new_pool(fmt, wl.num_pages, H, d), O.new_pool(fmt, wl.num_pages, H, d)
+    O.append(fmt, kp, vp, wl.k, wl.v, wl.slot_mapping)
+    return wl, kp, vp
+
+
+@pytest.mark.parametrize("fmt", [O.FMT_FP4, O.FMT_FP8, O.FMT_BF16])
+def test_attention_special_cases(fmt):
+    wl, kp, vp = _small_pools(fmt)
+    d, H = wl.head_dim, wl.num_kv_heads
+    scale = 1 / math.sqrt(d)
+    out = O.decode_attention(fmt, kp, vp, H, d, wl.q, wl.page_table, wl.seq_lens, scale)
+    unrot = O.wht if fmt == O.FMT_FP4 else (lambda v: v)
+    G = wl.num_q_heads // H
+    for h in range(wl.num_q_heads):     # seq_len 1: output is that token's value row
+        v0 = O.gather_dequant(fmt, vp, wl.page_table[0], 1, h // G, d, True)[0]
+        np.testing.assert_allclose(out[0, h], unrot(v0), rtol=0, atol=1e-12)
+    # q = 0: equal logits, output is the mean of the value rows
+    q0 = np.zeros_like(wl.q)
+    out0 = O.decode_attention(fmt, kp, vp, H, d, q0, wl.page_table, wl.seq_lens, scale)
+    for b in range(wl.batch):
+        V = O.gather_dequant(fmt, vp, wl.page_table[b], wl.seq_lens[b], 0, d, True)
+        np.testing.assert_allclose(out0[b, 0], unrot(V.mean(0)), rtol=0, atol=1e-12)
+    # empty sequence gives a zero row
+    lens0 = wl.seq_lens.copy(); lens0[1] = 0
+    oz = O.decode_attention(fmt, kp, vp, H, d, wl.q, wl.page_table, lens0, scale)
+    assert not oz[1].any()
+
+
+def test_attention_weights_sum_to_one_and_gqa_mapping():
+    wl, kp, vp = _small_pools(O.FMT_FP4, seed=13)
+    d, H, G = wl.head_dim, wl.num_kv_heads, wl.num_q_heads // wl.num_kv_heads
+    # softmax weights sum to 1: with every value row equal to ones the output is ones
+    K = np.random.default_rng(0).standard_normal((50, d))
+    qh = np.random.default_rng(1).standard_normal((3, d))
+    np.testing.assert_allclose(O.attention(qh, K, np.ones((50, d)), 0.3), 1.0, rtol=1e-14)
+    # duplicated query heads give identical rows; GQA equals MHA with repeated KV
+    q = wl.q.copy()
+    q[:, 1] = q[:, 0]
+    out = O.decode_attention(O.FMT_FP4, kp, vp, H, d, q, wl.page_table, wl.seq_lens, 0.1)
+    assert np.array_equal(out[:, 0], out[:, 1])
+    b = 2
+    for h in range(wl.num_q_heads):
+        qhat = O.e4m3_decode(O.rotate_quantize_query(q[b, h]))
+        K = O.gather_dequant(O.FMT_FP4, kp, wl.page_table[b], wl.seq_lens[b], h // G, d, False)
+        V = O.gather_dequant(O.FMT_FP4, vp, wl.page_table[b], wl.seq_lens[b], h // G, d, True)
+        np.testing.assert_allclose(out[b, h], O.wht(O.attention(qhat[None], K, V, 0.1)[0]), rtol=0, atol=1e-14)
