@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Bench: FP4-KV decode step on one MI355X, against the FP8/BF16 KV baselines and
+the CPU oracle.
+
+One step is one pass of the hot path over a batch: append the new token of every
+sequence to the paged cache (rotate + quantize + pack for FP4) and run decode
+attention over the whole context (query rotation to E4M3, split-K attention,
+merge + inverse rotation).  Default workload: 64 sequences x 8,192 context,
+64 query heads / 8 KV heads, head_dim 128, 16-token pages randomly permuted.
+
+Prints one JSON line.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+METRIC = "FP4-KV decode-attn us/step & HBM GB/s (% peak), 64 seq x 8K ctx GQA"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_gqa", choices=["decode_gqa", "long", "ragged", "tiny"])
+    ap.add_argument("--no-baselines", action="store_true", help="skip the FP8/BF16 KV kernels")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle sample")
+    return ap.parse_args()
+
+
+def make_workload(name):
+    from bit_kv_cache_wht_amd import workloads as W
+    if name == "decode_gqa":
+        return W.decode_gqa(new=1)
+    if name == "long":
+        return W.long_context(new=1)
+    if name == "ragged":
+        return W.ragged()
+    return W.tiny()
+
+
+def fp4_kv_bytes_per_token_head(d):
+    return 2 * (d // 2 + d // 32)            # K + V, 17 bytes per 32 elements each
+
+
+KV_BYTES = {"fp4": lambda d: fp4_kv_bytes_per_token_head(d), "fp8": lambda d: 2 * d, "bf16": lambda d: 4 * d}
+
+
+class HipEvents:
+    """hipEvent_t pairs created and read through the HIP runtime, so that events
+    recorded inside libuq (on the kernel's stream) can be timed."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0 and self.hip.hipEventCreate(ctypes.byref(b)) == 0
+            self.pairs.append((a.value, b.value))
+
+    def elapsed_ms(self, i):
+        ms = self.ct.c_float()
+        st = self.hip.hipEventElapsedTime(self.ct.byref(ms), self.pairs[i][0], self.pairs[i][1])
+        assert st == 0, f"hipEventElapsedTime failed ({st})"
+        return ms.value
+
+    def close(self):
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+
+
+class Runner:
+    """Holds device buffers for one format and runs steps through the C ABI."""
+
+    def __init__(self, fmt, wl):
+        import torch
+        import bit_kv_cache_wht_amd as uq
+        self.fmt, self.wl, self.uq, self.torch = fmt, wl, uq, torch
+        fid = {"fp4": uq.UQ_KV_FP4, "fp8": uq.UQ_KV_FP8, "bf16": uq.UQ_KV_BF16}[fmt]
+        self.append = {"fp4": uq.uq_quantize_append, "fp8": uq.uq_append_fp8, "bf16": uq.uq_append_bf16}[fmt]
+        self.decode = {"fp4": uq.uq_decode_attention, "fp8": uq.uq_decode_attention_fp8,
+                       "bf16": uq.uq_decode_attention_bf16}[fmt]
+        d = wl.head_dim
+        self.cache = uq.KvCache.allocate(fid, wl.num_pages, wl.num_kv_heads, d)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        kv = (lambda a: dev(a.view(np.int16)).view(torch.bfloat16)) if wl.in_dtype == "bf16" else dev
+        new = wl.new_token_index()
+        pre = wl.prefix_token_index()
+        # untimed prefill of the prefix, in chunks to bound host->device staging
+        for i in range(0, len(pre), 1 << 18):
+            idx = pre[i:i + (1 << 18)]
+            self.append(self.cache, kv(wl.k[idx]), kv(wl.v[idx]), dev(wl.slot_mapping[idx]))
+        self.k_new, self.v_new = kv(wl.k[new]), kv(wl.v[new])
+        self.slots_new = dev(wl.slot_mapping[new])
+        self.q = kv(wl.q)
+        self.page_table = dev(wl.page_table)
+        self.seq_lens = dev(wl.seq_lens)
+        self.out = torch.empty((wl.batch, wl.num_q_heads, d), dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(uq.uq_decode_workspace_bytes(self.cache, wl.batch, wl.num_q_heads,
+                                                           wl.page_table.shape[1]), dtype=torch.uint8, device="cuda")
+        self.sm_scale = float(np.float32(1.0 / np.sqrt(d)))
+        torch.cuda.synchronize()
+
+    def step(self, ev=None):
+        self.append(self.cache, self.k_new, self.v_new, self.slots_new)
+        if ev is not None:
+            self.uq.uq_profile_next_decode(ev[0], ev[1])
+        self.decode(self.cache, self.q, self.page_table, self.seq_lens, self.sm_scale, self.out, self.ws)
+
+    def run(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        evs = HipEvents(steps)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        t0.record()
+        for i in range(steps):
+            self.step(evs.pairs[i])
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms_step = t0.elapsed_time(t1) / steps
+        k_ms = [evs.elapsed_ms(i) for i in range(steps)]
+        evs.close()
+        return dict(ms_per_step=ms_step, wall_ms_per_step=1e3 * wall / steps,
+                    decode_kernel_ms=float(np.mean(k_ms)), decode_kernel_ms_p10=float(np.percentile(k_ms, 10)),
+                    decode_kernel_ms_p90=float(np.percentile(k_ms, 90)))
+
+    def kernel_bytes(self):
+        """Algorithmic bytes of one launch of the split-K attention kernel: every
+        cached K/V byte of every context token once, the query operand and the
+        page-table entries; split partials are overhead and not counted."""
+        wl = self.wl
+        d = wl.head_dim
+        tok_heads = int(np.sum(wl.seq_lens.astype(np.int64))) * wl.num_kv_heads
+        kv = tok_heads * KV_BYTES[self.fmt](d)
+        q = wl.batch * wl.num_q_heads * d * (2 if self.fmt == "bf16" else 1)
+        pt = int(np.sum((wl.seq_lens.astype(np.int64) + 15) // 16)) * 4
+        return kv + q + pt, kv
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle as it stands, on a bounded sample of the same step: decode rows of
+    whole (sequence, KV head) pairs plus the appends of their new tokens, scaled to
+    one full step.  BLAS is pinned to one thread, so the oracle uses one core."""
+    import threadpoolctl
+    import oracle as O
+    G = wl.num_q_heads // wl.num_kv_heads
+    d = wl.head_dim
+    with threadpoolctl.threadpool_limits(1):
+        pairs = 0
+        elapsed_pairs = 0.0
+        t_start = time.perf_counter()
+        rng = np.random.default_rng(0)
+        order = rng.permutation(wl.batch * wl.num_kv_heads)
+        for pair in order:
+            b, hk = divmod(int(pair), wl.num_kv_heads)
+            L = int(wl.seq_lens[b])
+            npg = (L + 15) // 16
+            t0 = wl.tok_offsets[b]
+            kp, vp = O.new_pool(O.FMT_FP4, npg, 1, d), O.new_pool(O.FMT_FP4, npg, 1, d)
+            # cache holds the prefix already; the step appends the new token(s) and decodes
+            n_new = int(wl.new_lens[b])
+            pre = np.arange(L - n_new, dtype=np.int32)
+            O.append(O.FMT_FP4, kp, vp, wl.k[t0:t0 + L - n_new, hk:hk + 1], wl.v[t0:t0 + L - n_new, hk:hk + 1], pre,
+                     in_dtype=wl.in_dtype)
+            t_pair = time.perf_counter()
+            O.append(O.FMT_FP4, kp, vp, wl.k[t0 + L - n_new:t0 + L, hk:hk + 1], wl.v[t0 + L - n_new:t0 + L, hk:hk + 1],
+                     np.arange(L - n_new, L, dtype=np.int32), in_dtype=wl.in_dtype)
+            rows = [(0, g) for g in range(G)]
+            O.decode_attention_rows(O.FMT_FP4, kp, vp, 1, d, wl.q[b:b + 1, hk * G:(hk + 1) * G], np.arange(npg)[None],
+                                    np.array([L]), float(np.float32(1 / np.sqrt(d))), rows, in_dtype=wl.in_dtype)
+            elapsed_pairs += time.perf_counter() - t_pair
+            pairs += 1
+            if time.perf_counter() - t_start > budget_s:
+                break
+    per_pair = elapsed_pairs / pairs
+    total_pairs = wl.batch * wl.num_kv_heads
+    return {"value": per_pair * total_pairs * 1e6, "unit": "us/step", "cores": 1, "kind": "oracle",
+            "sample": f"{pairs} of {total_pairs} (sequence, KV head) pairs: append of the new token + decode of "
+                      f"its {G} query heads over the full context, float64 numpy; scaled to the whole step "
+                      f"(prefix quantization untimed)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this hot path needs no "
+              f"collectives and is benchmarked at N=1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    log(f"generating workload {args.workload}")
+    t = time.perf_counter()
+    wl = make_workload(args.workload)
+    log(f"workload ready in {time.perf_counter() - t:.1f}s: B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
+        f"d={wl.head_dim} tokens={wl.total_tokens}")
+    results = {}
+    fmts = ["fp4"] if args.no_baselines else ["fp4", "fp8", "bf16"]
+    for fmt in fmts:
+        log(f"{fmt}: prefill + timing")
+        r = Runner(fmt, wl)
+        res = r.run(args.steps, args.warmup)
+        algo, kv = r.kernel_bytes()
+        res["kernel_gbs"] = algo / (res["decode_kernel_ms"] * 1e-3) / 1e9
+        res["kernel_algo_bytes"] = algo
+        res["kv_bytes"] = kv
+        results[fmt] = res
+        log(f"{fmt}: {1e3 * res['ms_per_step']:.1f} us/step, decode kernel {1e3 * res['decode_kernel_ms']:.1f} us "
+            f"= {res['kernel_gbs']:.0f} GB/s")
+        del r
+        torch.cuda.empty_cache()
+
+    fp4 = results["fp4"]
+    line = {
+        "metric": METRIC,
+        "value": round(fp4["ms_per_step"] * 1e3, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(fp4["ms_per_step"], 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4_e2m1xfp8_e4m3->f32 (f16 PV)",
+        "data": "synthetic (seeded Gaussian K/V with outlier channels, permuted pages)",
+        "config": {"workload": f"{wl.name}: {wl.batch} seq x {int(wl.seq_lens.max())} ctx, {wl.num_q_heads} q heads / "
+                               f"{wl.num_kv_heads} kv heads, head_dim {wl.head_dim}, 16-token pages permuted; step = "
+                               f"FP4 append of 1 new token per seq + decode",
+                   "global_batch": wl.batch, "seq_len": int(wl.seq_lens.max()), "parallelism": "none (1 GPU)"},
+        "kv_gbs_per_step": round(fp4["kv_bytes"] / (fp4["ms_per_step"] * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(fp4["kernel_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(fp4["kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel<Fp4Pol<128>>", "kernel_us": round(fp4["decode_kernel_ms"] * 1e3, 2),
+                     "kernel_us_p10_p90": [round(fp4["decode_kernel_ms_p10"] * 1e3, 2),
+                                           round(fp4["decode_kernel_ms_p90"] * 1e3, 2)],
+                     "algo_bytes_per_launch": fp4["kernel_algo_bytes"]},
+        "baselines": {f: {"us_per_step": round(results[f]["ms_per_step"] * 1e3, 2),
+                          "decode_kernel_us": round(results[f]["decode_kernel_ms"] * 1e3, 2),
+                          "kernel_gbs": round(results[f]["kernel_gbs"], 1),
+                          "frac_hbm_peak": round(results[f]["kernel_gbs"] / HBM_PEAK_GBS, 4)}
+                      for f in results if f != "fp4"},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle sample)")
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,32 @@
-"""UltraQuant FP4 KV-cache hot path for MI355X (gfx950): Python binding."""
+"""UltraQuant FP4 KV-cache hot path for MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libuq.so`` (declared in include/uq.h):
+every function here only marshals torch tensors into pointers and sizes; all
+computation runs in the HIP kernels.  Importing the package does not load the
+library; the first call does, and raises if ``libuq.so`` is missing (build it
+with ``python -m bit_kv_cache_wht_amd.build``).
+"""
+from ._binding import (  # noqa: F401
+    UQ_FLAG_OUT_ROTATED,
+    UQ_IN_BF16,
+    UQ_IN_F32,
+    UQ_KV_BF16,
+    UQ_KV_FP4,
+    UQ_KV_FP8,
+    KvCache,
+    UqError,
+    lib,
+    uq_append_bf16,
+    uq_append_fp8,
+    uq_decode_attention,
+    uq_decode_attention_bf16,
+    uq_decode_attention_fp8,
+    uq_decode_workspace_bytes,
+    uq_head_block_bytes,
+    uq_last_hip_error,
+    uq_page_bytes,
+    uq_profile_next_decode,
+    uq_quantize_append,
+    uq_rotate_quantize_query,
+    uq_status_string,
+)

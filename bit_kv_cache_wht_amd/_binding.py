@@ -1,0 +1,212 @@
+"""ctypes binding of libuq (include/uq.h).  Argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+UQ_OK, UQ_ERR_INVALID_ARG, UQ_ERR_UNSUPPORTED, UQ_ERR_WORKSPACE, UQ_ERR_HIP = 0, -1, -2, -3, -4
+UQ_KV_FP4, UQ_KV_FP8, UQ_KV_BF16 = 0, 1, 2
+UQ_IN_BF16, UQ_IN_F32 = 0, 1
+UQ_PAGE_SIZE = 16
+UQ_FLAG_OUT_ROTATED = 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libuq.so")
+
+
+class UqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        detail = ""
+        if status == UQ_ERR_HIP:
+            detail = f" (hipError {uq_last_hip_error()})"
+        super().__init__(f"{fn} failed: {uq_status_string(status)} [{status}]{detail}")
+        self.status = status
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_U = ctypes.c_uint32
+_SZ = ctypes.c_size_t
+_CP = ctypes.POINTER(_Cache)
+
+_SIGS = {
+    "uq_head_block_bytes": (_SZ, [_I, _I]),
+    "uq_page_bytes": (_SZ, [_CP]),
+    "uq_quantize_append": (ctypes.c_int, [_CP, _P, _P, _I, _P, _I, _U, _P]),
+    "uq_append_fp8": (ctypes.c_int, [_CP, _P, _P, _I, _P, _I, _U, _P]),
+    "uq_append_bf16": (ctypes.c_int, [_CP, _P, _P, _I, _P, _I, _U, _P]),
+    "uq_rotate_quantize_query": (ctypes.c_int, [_P, _I, _P, _I, _I, _P]),
+    "uq_decode_workspace_bytes": (_SZ, [_CP, _I, _I, _I]),
+    "uq_decode_attention": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
+    "uq_decode_attention_fp8": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
+    "uq_decode_attention_bf16": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
+    "uq_profile_next_decode": (ctypes.c_int, [_P, _P]),
+    "uq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "uq_last_hip_error": (ctypes.c_int, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libuq.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_kv_cache_wht_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype, f.argtypes = res, args
+        _lib = h
+    return _lib
+
+
+@dataclass
+class KvCache:
+    """Descriptor of a paged K/V cache; pools are caller-owned uint8 device tensors
+    of shape [num_pages][num_kv_heads][head block bytes]."""
+    format: int
+    num_pages: int
+    num_kv_heads: int
+    head_dim: int
+    k_pool: object
+    v_pool: object
+
+    @classmethod
+    def allocate(cls, fmt: int, num_pages: int, num_kv_heads: int, head_dim: int, device="cuda", zero=True):
+        import torch
+        blk = uq_head_block_bytes(fmt, head_dim)
+        if blk == 0:
+            raise UqError("uq_head_block_bytes", UQ_ERR_UNSUPPORTED)
+        alloc = torch.zeros if zero else torch.empty
+        k = alloc((num_pages, num_kv_heads, blk), dtype=torch.uint8, device=device)
+        v = alloc((num_pages, num_kv_heads, blk), dtype=torch.uint8, device=device)
+        return cls(fmt, num_pages, num_kv_heads, head_dim, k, v)
+
+    def c(self) -> _Cache:
+        return _Cache(self.format, self.num_pages, UQ_PAGE_SIZE, self.num_kv_heads, self.head_dim,
+                      _ptr(self.k_pool), _ptr(self.v_pool))
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return UQ_IN_BF16
+    if t.dtype == torch.float32:
+        return UQ_IN_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or float32)")
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors passed to libuq must be contiguous")
+
+
+def _check(fn: str, status: int) -> None:
+    if status != UQ_OK:
+        raise UqError(fn, status)
+
+
+def uq_status_string(status: int) -> str:
+    return lib().uq_status_string(status).decode()
+
+
+def uq_last_hip_error() -> int:
+    return lib().uq_last_hip_error()
+
+
+def uq_head_block_bytes(fmt: int, head_dim: int) -> int:
+    return lib().uq_head_block_bytes(fmt, head_dim)
+
+
+def uq_page_bytes(cache: KvCache) -> int:
+    c = cache.c()
+    return lib().uq_page_bytes(ctypes.byref(c))
+
+
+def _append(name, cache, k_new, v_new, slot_mapping, flags, stream):
+    _contig(k_new, v_new, slot_mapping)
+    c = cache.c()
+    n = int(k_new.shape[0])
+    st = getattr(lib(), name)(ctypes.byref(c), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(slot_mapping), n,
+                              flags, _stream(stream))
+    _check(name, st)
+
+
+def uq_quantize_append(cache: KvCache, k_new, v_new, slot_mapping, flags: int = 0, stream=None) -> None:
+    """FP4 write path; k_new, v_new [T][H_kv][d] bf16/f32, slot_mapping int32 [T]."""
+    _append("uq_quantize_append", cache, k_new, v_new, slot_mapping, flags, stream)
+
+
+def uq_append_fp8(cache: KvCache, k_new, v_new, slot_mapping, flags: int = 0, stream=None) -> None:
+    _append("uq_append_fp8", cache, k_new, v_new, slot_mapping, flags, stream)
+
+
+def uq_append_bf16(cache: KvCache, k_new, v_new, slot_mapping, flags: int = 0, stream=None) -> None:
+    _append("uq_append_bf16", cache, k_new, v_new, slot_mapping, flags, stream)
+
+
+def uq_rotate_quantize_query(q, q_fp8, stream=None) -> None:
+    """q [rows][d] bf16/f32 -> q_fp8 uint8 [rows][d] (E4M3 of the rotated query)."""
+    _contig(q, q_fp8)
+    rows, d = int(q.shape[0]), int(q.shape[-1])
+    st = lib().uq_rotate_quantize_query(_ptr(q), _dtype_code(q), _ptr(q_fp8), rows, d, _stream(stream))
+    _check("uq_rotate_quantize_query", st)
+
+
+def uq_decode_workspace_bytes(cache: KvCache, num_seqs: int, num_q_heads: int, max_pages_per_seq: int) -> int:
+    c = cache.c()
+    return lib().uq_decode_workspace_bytes(ctypes.byref(c), num_seqs, num_q_heads, max_pages_per_seq)
+
+
+def _decode(name, cache, q, page_table, seq_lens, sm_scale, out, workspace, flags, stream):
+    _contig(q, page_table, seq_lens, out, workspace)
+    c = cache.c()
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = getattr(lib(), name)(ctypes.byref(c), _ptr(q), _dtype_code(q), _ptr(page_table), int(page_table.shape[1]),
+                              _ptr(seq_lens), B, Hq, float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, flags,
+                              _stream(stream))
+    _check(name, st)
+
+
+def uq_decode_attention(cache, q, page_table, seq_lens, sm_scale, out, workspace, flags=0, stream=None) -> None:
+    """FP4 decode: q [B][H_q][d], page_table int32 [B][max_pages], seq_lens int32 [B],
+    out float32 [B][H_q][d], workspace uint8 >= uq_decode_workspace_bytes."""
+    _decode("uq_decode_attention", cache, q, page_table, seq_lens, sm_scale, out, workspace, flags, stream)
+
+
+def uq_decode_attention_fp8(cache, q, page_table, seq_lens, sm_scale, out, workspace, flags=0, stream=None) -> None:
+    _decode("uq_decode_attention_fp8", cache, q, page_table, seq_lens, sm_scale, out, workspace, flags, stream)
+
+
+def uq_decode_attention_bf16(cache, q, page_table, seq_lens, sm_scale, out, workspace, flags=0, stream=None) -> None:
+    _decode("uq_decode_attention_bf16", cache, q, page_table, seq_lens, sm_scale, out, workspace, flags, stream)
+
+
+def uq_profile_next_decode(start_event, stop_event) -> None:
+    """Record two hipEvent_t handles (ints) around the next decode call's main kernel."""
+    _check("uq_profile_next_decode", lib().uq_profile_next_decode(start_event, stop_event))

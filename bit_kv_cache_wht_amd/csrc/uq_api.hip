@@ -1,0 +1,197 @@
+// extern "C" entry points of libuq: argument validation (host only, before any
+// HIP call) and kernel launches.  Declarations and semantics: include/uq.h.
+#include <hip/hip_runtime.h>
+
+#include "uq_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return UQ_OK;
+  g_last_hip_error = (int)e;
+  return UQ_ERR_HIP;
+}
+
+bool dim_ok(int d) { return d == 64 || d == 128; }
+
+// Cache descriptor checks shared by every entry point.
+int check_cache(const uq_kv_cache* c, int want_format) {
+  if (c == nullptr) return UQ_ERR_INVALID_ARG;
+  if (c->format != want_format) return UQ_ERR_INVALID_ARG;
+  if (c->page_size != UQ_PAGE_SIZE) return UQ_ERR_UNSUPPORTED;
+  if (!dim_ok(c->head_dim)) return UQ_ERR_UNSUPPORTED;
+  if (c->num_kv_heads < 1 || c->num_pages < 1) return UQ_ERR_INVALID_ARG;
+  if (c->k_pool == nullptr || c->v_pool == nullptr) return UQ_ERR_INVALID_ARG;
+  return UQ_OK;
+}
+
+typedef hipError_t (*append_launcher)(const uq::AppendArgs&, int, int, hipStream_t);
+
+int append_common(const uq_kv_cache* cache, int format, const void* k_new, const void* v_new, int32_t in_dtype,
+                  const int32_t* slot_mapping, int32_t num_tokens, uint32_t flags, uq_stream_t stream,
+                  append_launcher launch) {
+  int st = check_cache(cache, format);
+  if (st != UQ_OK) return st;
+  if (flags != 0u) return UQ_ERR_INVALID_ARG;
+  if (in_dtype != UQ_IN_BF16 && in_dtype != UQ_IN_F32) return UQ_ERR_INVALID_ARG;
+  if (num_tokens < 0) return UQ_ERR_INVALID_ARG;
+  if (num_tokens == 0) return UQ_OK;
+  if (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr) return UQ_ERR_INVALID_ARG;
+  uq::AppendArgs a;
+  a.k = k_new;
+  a.v = v_new;
+  a.slot_mapping = slot_mapping;
+  a.k_pool = static_cast<uint8_t*>(cache->k_pool);
+  a.v_pool = static_cast<uint8_t*>(cache->v_pool);
+  a.page_bytes = (int64_t)uq_page_bytes(cache);
+  a.T = num_tokens;
+  a.H = cache->num_kv_heads;
+  return hip_status(launch(a, cache->head_dim, in_dtype, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q_dtype, const int32_t* page_table,
+                  int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                  float sm_scale, float* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                  uq_stream_t stream) {
+  int st = check_cache(cache, format);
+  if (st != UQ_OK) return st;
+  const uint32_t allowed = format == UQ_KV_FP4 ? UQ_FLAG_OUT_ROTATED : 0u;
+  if ((flags & ~allowed) != 0u) return UQ_ERR_INVALID_ARG;
+  if (q_dtype != UQ_IN_BF16 && q_dtype != UQ_IN_F32) return UQ_ERR_INVALID_ARG;
+  if (format == UQ_KV_BF16 && q_dtype != UQ_IN_BF16) return UQ_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || max_pages_per_seq < 1 || num_q_heads < 1) return UQ_ERR_INVALID_ARG;
+  if (num_q_heads % cache->num_kv_heads != 0) return UQ_ERR_UNSUPPORTED;
+  if (num_q_heads / cache->num_kv_heads > 16) return UQ_ERR_UNSUPPORTED;
+  if (!(sm_scale == sm_scale)) return UQ_ERR_INVALID_ARG;   // NaN
+  if (num_seqs == 0) return UQ_OK;
+  if (q == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr) return UQ_ERR_INVALID_ARG;
+  const size_t need = uq_decode_workspace_bytes(cache, num_seqs, num_q_heads, max_pages_per_seq);
+  if (workspace == nullptr || workspace_bytes < need) return UQ_ERR_WORKSPACE;
+  uq::DecodeArgs a;
+  a.format = format;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.k_pool = static_cast<const uint8_t*>(cache->k_pool);
+  a.v_pool = static_cast<const uint8_t*>(cache->v_pool);
+  a.page_bytes = (int64_t)uq_page_bytes(cache);
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_seq;
+  a.seq_lens = seq_lens;
+  a.B = num_seqs;
+  a.Hq = num_q_heads;
+  a.Hkv = cache->num_kv_heads;
+  a.D = cache->head_dim;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.ws = static_cast<uint8_t*>(workspace);
+  a.lay = uq::decode_layout(format, num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim);
+  a.unrotate = format == UQ_KV_FP4 && !(flags & UQ_FLAG_OUT_ROTATED);
+  a.ev_start = g_prof_start;
+  a.ev_stop = g_prof_stop;
+  g_prof_start = g_prof_stop = nullptr;
+  return hip_status(uq::launch_decode(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t uq_head_block_bytes(int32_t format, int32_t head_dim) {
+  if (!dim_ok(head_dim)) return 0;
+  switch (format) {
+    case UQ_KV_FP4: return (size_t)UQ_PAGE_SIZE * head_dim / 2 + (size_t)UQ_PAGE_SIZE * head_dim / UQ_GROUP;
+    case UQ_KV_FP8: return (size_t)UQ_PAGE_SIZE * head_dim;
+    case UQ_KV_BF16: return (size_t)UQ_PAGE_SIZE * head_dim * 2;
+    default: return 0;
+  }
+}
+
+size_t uq_page_bytes(const uq_kv_cache* c) {
+  if (c == nullptr || c->num_kv_heads < 1 || c->page_size != UQ_PAGE_SIZE) return 0;
+  return (size_t)c->num_kv_heads * uq_head_block_bytes(c->format, c->head_dim);
+}
+
+int uq_quantize_append(const uq_kv_cache* cache, const void* k_new, const void* v_new, int32_t in_dtype,
+                       const int32_t* slot_mapping, int32_t num_tokens, uint32_t flags, uq_stream_t stream) {
+  return append_common(cache, UQ_KV_FP4, k_new, v_new, in_dtype, slot_mapping, num_tokens, flags, stream,
+                       uq::launch_append_fp4);
+}
+
+int uq_append_fp8(const uq_kv_cache* cache, const void* k_new, const void* v_new, int32_t in_dtype,
+                  const int32_t* slot_mapping, int32_t num_tokens, uint32_t flags, uq_stream_t stream) {
+  return append_common(cache, UQ_KV_FP8, k_new, v_new, in_dtype, slot_mapping, num_tokens, flags, stream,
+                       uq::launch_append_fp8);
+}
+
+int uq_append_bf16(const uq_kv_cache* cache, const void* k_new, const void* v_new, int32_t in_dtype,
+                   const int32_t* slot_mapping, int32_t num_tokens, uint32_t flags, uq_stream_t stream) {
+  return append_common(cache, UQ_KV_BF16, k_new, v_new, in_dtype, slot_mapping, num_tokens, flags, stream,
+                       uq::launch_append_bf16);
+}
+
+int uq_rotate_quantize_query(const void* q, int32_t in_dtype, uint8_t* q_fp8, int32_t rows, int32_t head_dim,
+                             uq_stream_t stream) {
+  if (in_dtype != UQ_IN_BF16 && in_dtype != UQ_IN_F32) return UQ_ERR_INVALID_ARG;
+  if (!dim_ok(head_dim)) return UQ_ERR_UNSUPPORTED;
+  if (rows < 0) return UQ_ERR_INVALID_ARG;
+  if (rows == 0) return UQ_OK;
+  if (q == nullptr || q_fp8 == nullptr) return UQ_ERR_INVALID_ARG;
+  return hip_status(uq::launch_query(q, in_dtype, q_fp8, rows, head_dim, true, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t uq_decode_workspace_bytes(const uq_kv_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_pages_per_seq) {
+  if (cache == nullptr || !dim_ok(cache->head_dim) || cache->num_kv_heads < 1) return 0;
+  if (cache->format < UQ_KV_FP4 || cache->format > UQ_KV_BF16) return 0;
+  if (num_seqs < 0 || num_q_heads < 1 || max_pages_per_seq < 1) return 0;
+  return uq::decode_layout(cache->format, num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim).total;
+}
+
+int uq_decode_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtype, const int32_t* page_table,
+                        int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                        float sm_scale, float* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                        uq_stream_t stream) {
+  return decode_common(cache, UQ_KV_FP4, q, q_dtype, page_table, max_pages_per_seq, seq_lens, num_seqs, num_q_heads,
+                       sm_scale, out, workspace, workspace_bytes, flags, stream);
+}
+
+int uq_decode_attention_fp8(const uq_kv_cache* cache, const void* q, int32_t q_dtype, const int32_t* page_table,
+                            int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                            float sm_scale, float* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                            uq_stream_t stream) {
+  return decode_common(cache, UQ_KV_FP8, q, q_dtype, page_table, max_pages_per_seq, seq_lens, num_seqs, num_q_heads,
+                       sm_scale, out, workspace, workspace_bytes, flags, stream);
+}
+
+int uq_decode_attention_bf16(const uq_kv_cache* cache, const void* q, int32_t q_dtype, const int32_t* page_table,
+                             int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                             float sm_scale, float* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                             uq_stream_t stream) {
+  return decode_common(cache, UQ_KV_BF16, q, q_dtype, page_table, max_pages_per_seq, seq_lens, num_seqs, num_q_heads,
+                       sm_scale, out, workspace, workspace_bytes, flags, stream);
+}
+
+int uq_profile_next_decode(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return UQ_ERR_INVALID_ARG;
+  g_prof_start = static_cast<hipEvent_t>(start_event);
+  g_prof_stop = static_cast<hipEvent_t>(stop_event);
+  return UQ_OK;
+}
+
+const char* uq_status_string(int status) {
+  switch (status) {
+    case UQ_OK: return "ok";
+    case UQ_ERR_INVALID_ARG: return "invalid argument";
+    case UQ_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case UQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case UQ_ERR_HIP: return "HIP error (see uq_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int uq_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,227 @@
+// Cache write kernels: FP4 (rotate + quantize + pack), FP8 and BF16 baselines,
+// and the query rotation to FP8.
+//
+// [review] = "[arXiv 2606.20474] UltraQuant: 컨텍스트가 긴 에이전트를 위한 4비트 KV 캐싱"
+//            (manon006.tistory.com/395)
+// [commentary] = pheeree.github.io "kv-cache-4bit-serving-residency-collapse"
+//
+// FP4 work mapping: a row is one (token, KV head) vector of K or of V.  D/32
+// consecutive lanes share a row, lane part p owning channels 32p..32p+31; after
+// the butterfly the same lane owns output group p, so group absmax, scale,
+// rounding and packing stay in registers.  A wave covers 64 / (D/32) rows.
+#include "uq_device.h"
+#include "uq_internal.h"
+
+namespace uq {
+
+template <int IN> __device__ __forceinline__ void load_row32(const void* base, int64_t elem, double (&x)[32]) {
+  if constexpr (IN == UQ_IN_BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint4 u = p[w];
+      const uint32_t d[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[8 * w + 2 * i] = bf16_bits_to_f64(d[i] & 0xFFFFu);
+        x[8 * w + 2 * i + 1] = bf16_bits_to_f64(d[i] >> 16);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const float4 f = p[w];
+      x[4 * w] = f.x; x[4 * w + 1] = f.y; x[4 * w + 2] = f.z; x[4 * w + 3] = f.w;
+    }
+  }
+}
+
+// FP4 write path ([review] §3.1; [commentary] footnote 2): WHT, group absmax,
+// UE8M0 scale byte, E2M1 codes, two codes per byte, paged store.
+template <int D, int IN>
+__global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
+  constexpr int LPR = D / 32;
+  constexpr int RPW = 64 / LPR;
+  constexpr int BLK = Fp4Block<D>::kBytes;
+  constexpr int CODE = Fp4Block<D>::kCodeBytes;
+  const int lane = threadIdx.x & 63;
+  const int p = lane % LPR;
+  const int64_t nrows = 2LL * a.T * a.H;
+  const int64_t row0 = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * RPW;
+  if (row0 >= nrows) return;                       // whole wave idle (no barriers used)
+  const int64_t row = row0 + lane / LPR;
+  const bool in_range = row < nrows;
+  const int64_t r = in_range ? row : 0;            // idle lanes read row 0 (in bounds)
+  const int64_t kv_rows = (int64_t)a.T * a.H;
+  const bool is_v = r >= kv_rows;
+  const int64_t tr = is_v ? r - kv_rows : r;       // token * H + head
+  const int t = (int)(tr / a.H), h = (int)(tr - (int64_t)t * a.H);
+  const int slot = a.slot_mapping[t];
+
+  double x[32];
+  load_row32<IN>(is_v ? a.v : a.k, tr * D + 32 * p, x);
+  wht_row<D>(x, lane);
+
+  double m = 0.0;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) m = fmax(m, fabs(x[e]));
+  const int E = scale_exponent(m);
+
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc |= e2m1_code(ldexp(x[8 * q + i], -E)) << (4 * i);
+    w[q] = acc;
+  }
+  if (!in_range || slot < 0) return;
+  const int page = slot >> 4, off = slot & 15;
+  const uint8_t scale_byte = (uint8_t)(E + 127);
+  if (!is_v) {
+    uint8_t* blk = a.k_pool + (int64_t)page * a.page_bytes + (int64_t)h * BLK;
+    *reinterpret_cast<uint4*>(blk + off * (D / 2) + 16 * p) = make_uint4(w[0], w[1], w[2], w[3]);
+    blk[CODE + off * (D / 32) + p] = scale_byte;
+  } else {
+    uint8_t* blk = a.v_pool + (int64_t)page * a.page_bytes + (int64_t)h * BLK;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) blk[(16 * p + i) * kPage + off] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+    blk[CODE + p * kPage + off] = scale_byte;
+  }
+}
+
+// Baseline writes: one thread per 8 channels of a (token, head, K|V) row.
+template <int D, int IN, int FMT>
+__global__ __launch_bounds__(256) void append_plain_kernel(AppendArgs a) {
+  constexpr int TPR = D / 8;                      // threads per row
+  constexpr int ESZ = FMT == UQ_KV_FP8 ? 1 : 2;   // stored bytes per element
+  constexpr int BLK = kPage * D * ESZ;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t kv_rows = (int64_t)a.T * a.H;
+  const int64_t row = gid / TPR;
+  if (row >= 2 * kv_rows) return;
+  const int c0 = (int)(gid - row * TPR) * 8;
+  const bool is_v = row >= kv_rows;
+  const int64_t tr = is_v ? row - kv_rows : row;
+  const int t = (int)(tr / a.H), h = (int)(tr - (int64_t)t * a.H);
+  const int slot = a.slot_mapping[t];
+  if (slot < 0) return;
+  const int page = slot >> 4, off = slot & 15;
+  const void* src = is_v ? a.v : a.k;
+  float f[8];
+  uint32_t bits[8];
+  if constexpr (IN == UQ_IN_BF16) {
+    const uint4 u = load16(static_cast<const uint16_t*>(src) + tr * D + c0);
+    const uint32_t d[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bits[2 * i] = d[i] & 0xFFFFu;
+      bits[2 * i + 1] = d[i] >> 16;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(bits[i] << 16);
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + tr * D + c0);
+    const float4 f0 = p[0], f1 = p[1];
+    f[0] = f0.x; f[1] = f0.y; f[2] = f0.z; f[3] = f0.w; f[4] = f1.x; f[5] = f1.y; f[6] = f1.z; f[7] = f1.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bits[i] = f32_to_bf16_bits(f[i]);
+  }
+  uint8_t* blk = (is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes + (int64_t)h * BLK;
+  if constexpr (FMT == UQ_KV_FP8) {
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = e4m3_from_f64((double)f[i]);
+    if (!is_v) {
+      *reinterpret_cast<uint2*>(blk + off * D + c0) =
+          make_uint2(b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24, b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) blk[(c0 + i) * kPage + off] = (uint8_t)b[i];
+    }
+  } else {
+    uint16_t* blk16 = reinterpret_cast<uint16_t*>(blk);
+    if (!is_v) {
+      *reinterpret_cast<uint4*>(blk16 + off * D + c0) =
+          make_uint4(bits[0] | bits[1] << 16, bits[2] | bits[3] << 16, bits[4] | bits[5] << 16, bits[6] | bits[7] << 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) blk16[(c0 + i) * kPage + off] = (uint16_t)bits[i];
+    }
+  }
+}
+
+// Query rotation ([review] §3.2): q_fp8 = E4M3(c_d * H_d q) from float64.
+// Same row mapping as the FP4 write path; ROT = false gives the unrotated
+// E4M3 query of the FP8 baseline.
+template <int D, int IN, bool ROT>
+__global__ __launch_bounds__(256) void query_kernel(const void* q, uint8_t* out, int rows) {
+  constexpr int LPR = D / 32;
+  constexpr int RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63;
+  const int p = lane % LPR;
+  const int64_t row0 = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * RPW;
+  if (row0 >= rows) return;
+  const int64_t row = row0 + lane / LPR;
+  const bool in_range = row < rows;
+  const int64_t r = in_range ? row : 0;
+  double x[32];
+  load_row32<IN>(q, r * D + 32 * p, x);
+  if constexpr (ROT) wht_row<D>(x, lane);
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    w[i] = e4m3_from_f64(x[4 * i]) | e4m3_from_f64(x[4 * i + 1]) << 8 | e4m3_from_f64(x[4 * i + 2]) << 16 |
+           e4m3_from_f64(x[4 * i + 3]) << 24;
+  if (!in_range) return;
+  uint4* o = reinterpret_cast<uint4*>(out + r * D + 32 * p);
+  o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+static unsigned grid_rows(int64_t rows, int rows_per_wave) {
+  const int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave;
+  return (unsigned)((waves + 3) / 4);
+}
+
+hipError_t launch_append_fp4(const AppendArgs& a, int D, int in, hipStream_t s) {
+  const int64_t rows = 2LL * a.T * a.H;
+  const int rpw = 64 / (D / 32);
+  const dim3 grid(grid_rows(rows, rpw)), block(256);
+  if (D == 128 && in == UQ_IN_BF16) hipLaunchKernelGGL((append_fp4_kernel<128, UQ_IN_BF16>), grid, block, 0, s, a);
+  else if (D == 128) hipLaunchKernelGGL((append_fp4_kernel<128, UQ_IN_F32>), grid, block, 0, s, a);
+  else if (in == UQ_IN_BF16) hipLaunchKernelGGL((append_fp4_kernel<64, UQ_IN_BF16>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((append_fp4_kernel<64, UQ_IN_F32>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_plain(const AppendArgs& a, int D, int in, hipStream_t s) {
+  const int64_t threads = 2LL * a.T * a.H * (D / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  if (D == 128 && in == UQ_IN_BF16) hipLaunchKernelGGL((append_plain_kernel<128, UQ_IN_BF16, FMT>), grid, block, 0, s, a);
+  else if (D == 128) hipLaunchKernelGGL((append_plain_kernel<128, UQ_IN_F32, FMT>), grid, block, 0, s, a);
+  else if (in == UQ_IN_BF16) hipLaunchKernelGGL((append_plain_kernel<64, UQ_IN_BF16, FMT>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((append_plain_kernel<64, UQ_IN_F32, FMT>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_fp8(const AppendArgs& a, int D, int in, hipStream_t s) { return launch_plain<UQ_KV_FP8>(a, D, in, s); }
+hipError_t launch_append_bf16(const AppendArgs& a, int D, int in, hipStream_t s) { return launch_plain<UQ_KV_BF16>(a, D, in, s); }
+
+hipError_t launch_query(const void* q, int in, uint8_t* out, int rows, int D, bool rot, hipStream_t s) {
+  const dim3 grid(grid_rows(rows, 64 / (D / 32))), block(256);
+#define UQ_Q(DD, II, RR) hipLaunchKernelGGL((query_kernel<DD, II, RR>), grid, block, 0, s, q, out, rows)
+  if (D == 128) {
+    if (in == UQ_IN_BF16) { if (rot) UQ_Q(128, UQ_IN_BF16, true); else UQ_Q(128, UQ_IN_BF16, false); }
+    else { if (rot) UQ_Q(128, UQ_IN_F32, true); else UQ_Q(128, UQ_IN_F32, false); }
+  } else {
+    if (in == UQ_IN_BF16) { if (rot) UQ_Q(64, UQ_IN_BF16, true); else UQ_Q(64, UQ_IN_BF16, false); }
+    else { if (rot) UQ_Q(64, UQ_IN_F32, true); else UQ_Q(64, UQ_IN_F32, false); }
+  }
+#undef UQ_Q
+  return hipGetLastError();
+}
+
+}  // namespace uq

@@ -1,0 +1,141 @@
+// Device-side building blocks for libuq (gfx950, wave64).
+//
+// [review] = "[arXiv 2606.20474] UltraQuant: 컨텍스트가 긴 에이전트를 위한 4비트 KV 캐싱"
+//            (manon006.tistory.com/395)
+//
+// Rounding decisions of the write path are taken in float64 on the exact rotated
+// value: the Walsh-Hadamard butterfly of bf16/f32 inputs is exact in float64 for
+// any row whose nonzero exponents span at most 38 (bf16) / 22 (f32) binades, so
+// its result does not depend on the order of the additions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace uq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+constexpr int kPage = 16;    // tokens per page
+constexpr int kGroup = 32;   // channels per scale group ([review] §3.1)
+
+// sqrt(1/d) as the nearest double (0x1.6a09e667f3bcdp-4 is sqrt(2)/16 rounded once).
+template <int D> __device__ __forceinline__ double wht_c() { return D == 64 ? 0.125 : 0x1.6a09e667f3bcdp-4; }
+template <int D> __device__ __forceinline__ float wht_cf() { return D == 64 ? 0.125f : 0x1.6a09e6p-4f; }
+
+template <int D> struct Fp4Block {
+  static constexpr int kCodeBytes = kPage * D / 2;          // codes of 16 slots
+  static constexpr int kBytes = kCodeBytes + kPage * D / 32; // + one scale byte per group
+};
+
+__device__ __forceinline__ double bf16_bits_to_f64(uint32_t b16) {
+  return (double)__uint_as_float(b16 << 16);
+}
+
+// Value of `v` held by lane ^ XOR (XOR = 1 or 2, inside a quad) via DPP quad_perm.
+template <int XOR> __device__ __forceinline__ double quad_swap(double v) {
+  constexpr int ctrl = XOR == 1 ? 0xB1 /* [1,0,3,2] */ : 0x4E /* [2,3,0,1] */;
+  int lo = __double2loint(v), hi = __double2hiint(v);
+  lo = __builtin_amdgcn_update_dpp(0, lo, ctrl, 0xF, 0xF, false);
+  hi = __builtin_amdgcn_update_dpp(0, hi, ctrl, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
+// Sylvester butterfly over the 32 values a lane holds (stages h = 1..16).
+__device__ __forceinline__ void wht32_inlane(double (&x)[32]) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 32; i += 2 * h)
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const double a = x[j], b = x[j + h];
+        x[j] = a + b;
+        x[j + h] = a - b;
+      }
+}
+
+// One butterfly stage whose partner element sits in lane ^ XOR: the lane with the
+// XOR bit clear keeps a + b, the other b' = a - b, each a single rounded add
+// (fma with an exact +-1 product).
+template <int XOR> __device__ __forceinline__ void wht_cross_stage(double (&x)[32], int lane) {
+  const double sgn = (lane & XOR) ? -1.0 : 1.0;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const double other = quad_swap<XOR>(x[e]);
+    x[e] = __builtin_fma(x[e], sgn, other);
+  }
+}
+
+// Normalized WHT of a row of D = 32 * LPR channels spread over LPR = D/32
+// consecutive lanes, lane part p holding channels 32p..32p+31.  On return the
+// lane holds output channels 32p..32p+31, i.e. one quantization group.
+template <int D> __device__ __forceinline__ void wht_row(double (&x)[32], int lane) {
+  wht32_inlane(x);
+  wht_cross_stage<1>(x, lane);                 // h = 32
+  if constexpr (D == 128) wht_cross_stage<2>(x, lane);   // h = 64
+  const double c = wht_c<D>();
+#pragma unroll
+  for (int e = 0; e < 32; ++e) x[e] *= c;
+}
+
+// Least integer E with m <= 6 * 2^E, clamped to [-127, 127] (m == 0 -> -127).
+// With m = f * 2^ex, f in [0.5, 1): 6 * 2^(ex-3) = 0.75 * 2^ex, so E = ex - 3
+// when f <= 0.75 and ex - 2 otherwise.
+__device__ __forceinline__ int scale_exponent(double m) {
+  if (!(m > 0.0)) return -127;
+  int ex;
+  const double f = frexp(m, &ex);
+  int e = ex - 3 + (f > 0.75 ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// FP4 E2M1 code of r = x / 2^E: magnitude rounded to nearest of
+// {0,.5,1,1.5,2,3,4,6}, ties to the even code, |r| > 6 saturating; sign bit from r.
+// The grid has quantum 0.5 on [0,2), 1 on [2,4), 2 on [4,6]: scale into integer
+// steps, round half to even, and offset into the code range.
+__device__ __forceinline__ uint32_t e2m1_code(double r) {
+  const double a = fmin(fabs(r), 6.0);
+  double s;
+  int off;
+  if (a < 2.0) { s = 2.0; off = 0; }
+  else if (a < 4.0) { s = 1.0; off = 2; }
+  else { s = 0.5; off = 4; }
+  const int n = (int)__builtin_rint(a * s);
+  const uint32_t sign = ((uint32_t)__double2hiint(r)) >> 31;
+  return (uint32_t)(n + off) | (sign << 3);
+}
+
+// OCP E4M3 byte of a float64: nearest, ties to even, |v| > 448 -> 448, sign
+// copied (also for zero).  Subnormals have quantum 2^-9.
+__device__ __forceinline__ uint32_t e4m3_from_f64(double v) {
+  const double a = fabs(v);
+  const uint32_t sign = ((uint32_t)__double2hiint(v)) >> 31;
+  uint32_t code;
+  if (a > 448.0) {
+    code = 0x7E;
+  } else if (a < 0x1p-6) {
+    code = (uint32_t)__builtin_rint(a * 512.0);             // 0..8 (8 = 2^-6)
+  } else {
+    int ex;
+    (void)frexp(a, &ex);                                     // a in [2^(ex-1), 2^ex)
+    const int e = ex - 1;                                    // -6..8
+    const int n = (int)__builtin_rint(ldexp(a, 3 - e));     // 8..16 (16 carries)
+    code = (uint32_t)((e + 7) * 8 + n - 8);
+  }
+  return code | (sign << 7);
+}
+
+// bf16 bits of a float, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+}  // namespace uq

@@ -1,0 +1,62 @@
+// Host-side declarations shared by the libuq translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/uq.h"
+
+namespace uq {
+
+struct AppendArgs {
+  const void* k;              // [T][H][D] bf16 or f32
+  const void* v;
+  const int32_t* slot_mapping;
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  int64_t page_bytes;         // bytes of one page of one pool
+  int32_t T, H;
+};
+
+// Launchers return the hipError_t of the launch.
+hipError_t launch_append_fp4(const AppendArgs& a, int head_dim, int in_dtype, hipStream_t s);
+hipError_t launch_append_fp8(const AppendArgs& a, int head_dim, int in_dtype, hipStream_t s);
+hipError_t launch_append_bf16(const AppendArgs& a, int head_dim, int in_dtype, hipStream_t s);
+hipError_t launch_query(const void* q, int in_dtype, uint8_t* q_fp8, int rows, int head_dim,
+                        bool rotate, hipStream_t s);
+
+// Decode work split: one item is (sequence, split of pps pages, group of up to
+// kWavesPerWG KV heads); one wave runs one KV head of an item.
+constexpr int kWavesPerWG = 4;
+
+struct DecodeLayout {
+  size_t hdr, base, items, qbuf, ml, po, total;
+  int32_t target_bs;   // target number of (sequence, split) pairs
+  int32_t max_bs;      // bound on (sequence, split) pairs: target_bs + num_seqs
+};
+
+DecodeLayout decode_layout(int format, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim);
+
+struct DecodeArgs {
+  int format;
+  const void* q;             // caller's query (bf16 / f32)
+  int q_dtype;
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  int64_t page_bytes;
+  const int32_t* page_table;
+  int32_t max_pages;
+  const int32_t* seq_lens;
+  int32_t B, Hq, Hkv, D;
+  float sm_scale;
+  float* out;
+  uint8_t* ws;
+  DecodeLayout lay;
+  bool unrotate;
+  hipEvent_t ev_start, ev_stop;   // optional, recorded around the main kernel
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace uq

@@ -9,11 +9,14 @@ tests, the bench and the CPU oracle's callers.
 [review] = "[arXiv 2606.20474] UltraQuant: 컨텍스트가 긴 에이전트를 위한 4비트 KV 캐싱"
 (manon006.tistory.com/395).
 
-Draw order for a seed (numpy PCG64): context lengths (ragged workload only),
-outlier channels for K then V (per KV head, without replacement), K values,
-V values, q values, page permutation.  K/V/q are float32 standard normals,
-multiplied by the outlier factor on the chosen channels and, for bf16 inputs,
-rounded to bf16 with torch's CPU cast.
+Draw order for a seed (numpy PCG64 main stream): context lengths (ragged
+workload only), outlier channels for K then V (per KV head, without
+replacement), q values, page permutation.  K and V values come from separate
+streams, one per block of 65,536 tokens, seeded with SeedSequence(seed,
+spawn_key=(1 for K / 2 for V, block)), so that large workloads can be drawn in
+parallel.  All values are float32 standard normals, multiplied by the outlier
+factor on the chosen channels and, for bf16 inputs, rounded to the nearest
+bf16 (ties to even).
 """
 from __future__ import annotations
 
@@ -59,22 +62,40 @@ class Workload:
         return np.concatenate(idx) if idx else np.zeros(0, np.int64)
 
 
+CHUNK = 1 << 16     # tokens per K/V random stream
+
+
 def _to_bf16_bits(x32: np.ndarray) -> np.ndarray:
-    import torch
-    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16)
-    return t.view(torch.int16).numpy().view(np.uint16)
+    """Nearest bf16 (ties to even) of finite float32 values, as uint16 bits."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
 
 
-def _draw_kv(rng, T, H, d, outlier_ch, factor, in_dtype, chunk=1 << 16):
-    """[T][H][d] values, drawn in token chunks (same stream as one big draw)."""
+def _draw_kv(seed, which, T, H, d, outlier_ch, factor, in_dtype):
+    """[T][H][d] values; token block c comes from its own stream (seed, which, c)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import os
     out = np.empty((T, H, d), dtype=np.uint16 if in_dtype == "bf16" else np.float32)
     mult = np.ones((H, d), dtype=np.float32)
     for h in range(H):
         mult[h, outlier_ch[h]] = factor
-    for t0 in range(0, T, chunk):
-        n = min(chunk, T - t0)
-        x = rng.standard_normal((n, H, d), dtype=np.float32) * mult
+
+    def block(c):
+        t0 = c * CHUNK
+        n = min(CHUNK, T - t0)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(which, c))))
+        x = rng.standard_normal((n, H, d), dtype=np.float32)
+        x *= mult
         out[t0:t0 + n] = _to_bf16_bits(x) if in_dtype == "bf16" else x
+
+    nblocks = (T + CHUNK - 1) // CHUNK
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), nblocks))
+    if workers == 1:
+        for c in range(nblocks):
+            block(c)
+    else:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(block, range(nblocks)))
     return out
 
 
@@ -93,8 +114,8 @@ def make_workload(name, batch, num_q_heads, num_kv_heads, head_dim, seq_lens, ne
     out_v = [rng.choice(d, size=n_outliers, replace=False) for _ in range(H)]
     tok_offsets = np.concatenate([[0], np.cumsum(seq_lens)]).astype(np.int64)
     T = int(tok_offsets[-1])
-    k = _draw_kv(rng, T, H, d, out_k, outlier_factor, in_dtype)
-    v = _draw_kv(rng, T, H, d, out_v, outlier_factor, in_dtype)
+    k = _draw_kv(seed, 1, T, H, d, out_k, outlier_factor, in_dtype)
+    v = _draw_kv(seed, 2, T, H, d, out_v, outlier_factor, in_dtype)
     q32 = rng.standard_normal((batch, num_q_heads, d), dtype=np.float32)
     q = _to_bf16_bits(q32) if in_dtype == "bf16" else q32
     pages_per_seq = (seq_lens + PAGE_SIZE - 1) // PAGE_SIZE
@@ -127,8 +148,8 @@ def _ragged_lengths(batch, lo, hi, chunk):
     return draw
 
 
-# The five named workloads.  ``scale`` < 1 shrinks lengths/batch for tests that
-# the oracle must finish in seconds while keeping heads, head_dim and structure.
+# The five named workloads (full sizes); tests build smaller ones of the same
+# structure with make_workload.
 def tiny(seed=1001):
     """1 sequence, 1 query head / 1 KV head, head_dim 64, context 256, fp32 inputs,
     2 outlier channels x20 on K and V."""

@@ -1,0 +1,201 @@
+/*
+ * uq.h -- C ABI of libuq: UltraQuant-style FP4 KV cache for AMD MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [review]     "[arXiv 2606.20474] UltraQuant: 컨텍스트가 긴 에이전트를 위한 4비트 KV 캐싱"
+ *                (manon006.tistory.com/395)
+ *   [commentary] "kv-cache-4bit-serving-residency-collapse" (pheeree.github.io, 2026-09-01),
+ *                whose footnotes quote the paper in English
+ *
+ * The write path ([review] §3.1) rotates each new key and value head vector with
+ * a normalized Walsh-Hadamard transform, takes the absolute maximum of every
+ * 32-channel group, stores the group scale as a UE8M0 byte (scale = byte - 127)
+ * and rounds each channel to the FP4 E2M1 grid; 32 codes (16 B) plus the scale
+ * byte make 17 B per group, 4.25 bits per element ([commentary] footnote 2).
+ * Dequantization is value = code * 2^(byte - 127) ([review] §3.2).  The decode
+ * side rotates the query into the key basis, rounds it to FP8 E4M3 once, outside
+ * the key loop ([review] §3.2, §4.2), and runs attention over the paged cache.
+ * BF16 and FP8 E4M3 caches on the same paged layout are the baselines
+ * ([review] §4.3).
+ *
+ * Conventions where the pages are silent:
+ *   - the WHT is the Sylvester Hadamard matrix in natural order scaled by
+ *     sqrt(1/head_dim), applied to K and to V; the attention output is rotated
+ *     back, so `out` is in the original basis;
+ *   - the scale exponent E is the least integer with absmax <= 6 * 2^E, clamped
+ *     to [-127, 127] (never clips); rounding is to nearest, ties to even code;
+ *     the sign bit is the sign of the value; every rounding decision is taken in
+ *     float64 on the exact rotated value;
+ *   - FP8 is OCP E4M3 (bias 7, max 448), round to nearest even, saturating.
+ *
+ * Memory and ownership
+ *   All pointers named *pool, k_new, v_new, q, q_fp8, out, slot_mapping,
+ *   page_table, seq_lens and workspace are DEVICE pointers owned by the caller.
+ *   The library allocates nothing and keeps no state between calls apart from
+ *   the loaded code object and a thread-local error code; calls are reentrant.
+ *   Every call enqueues its kernels on `stream` (NULL = the default stream) and
+ *   returns without synchronizing.  Arguments are validated on the host before
+ *   any launch; device-resident contents (page ids, slots, lengths) are trusted:
+ *   an out-of-range value there is undefined behaviour.
+ *
+ * Paged layout (part of the ABI).  A pool is [num_pages][num_kv_heads][block];
+ * token position t of a sequence lives in page page_table[t / 16] at slot t % 16.
+ * Head-block layouts (d = head_dim, 16 slots):
+ *   FP4  K: codes [16 slot][d/2 B] (byte j: channel 2j low nibble, 2j+1 high),
+ *           then scales [16 slot][d/32 B]                      = 17*d/2 bytes
+ *   FP4  V: codes [d/2 channel pair][16 slot] (byte: channel 2c low nibble,
+ *           2c+1 high nibble), then scales [d/32 group][16 slot] = 17*d/2 bytes
+ *   FP8  K: [16 slot][d] E4M3 bytes;   FP8  V: [d][16 slot] E4M3 bytes
+ *   BF16 K: [16 slot][d] bf16;         BF16 V: [d][16 slot] bf16
+ * K is slot-major because the QK product contracts over channels; V is
+ * channel-major because the PV product contracts over tokens.
+ */
+#ifndef UQ_H
+#define UQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* uq_stream_t;   /* a hipStream_t; NULL = default stream */
+
+enum uq_status {
+  UQ_OK = 0,
+  UQ_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad enum, inconsistent sizes   */
+  UQ_ERR_UNSUPPORTED = -2,   /* head_dim not 64/128, page_size not 16, H_q/H_kv not 1..16  */
+  UQ_ERR_WORKSPACE = -3,     /* workspace null or smaller than uq_decode_workspace_bytes  */
+  UQ_ERR_HIP = -4            /* a HIP call failed; uq_last_hip_error() has the hipError_t */
+};
+
+enum uq_kv_format { UQ_KV_FP4 = 0, UQ_KV_FP8 = 1, UQ_KV_BF16 = 2 };
+enum uq_in_dtype { UQ_IN_BF16 = 0, UQ_IN_F32 = 1 };
+
+#define UQ_PAGE_SIZE 16
+#define UQ_GROUP 32
+#define UQ_FLAG_OUT_ROTATED 1u   /* FP4 decode: leave `out` in the rotated (WHT) basis */
+
+/* Cache descriptor; read at call time, never retained. */
+typedef struct uq_kv_cache {
+  int32_t format;        /* enum uq_kv_format                                   */
+  int32_t num_pages;     /* pages in each pool                                  */
+  int32_t page_size;     /* tokens per page; must be 16                          */
+  int32_t num_kv_heads;  /* >= 1                                                 */
+  int32_t head_dim;      /* 64 or 128                                            */
+  void* k_pool;          /* device, [num_pages][num_kv_heads][block], 256-B aligned */
+  void* v_pool;          /* device, same shape                                    */
+} uq_kv_cache;
+
+/* Bytes of one head-block (one KV head of one page): FP4 17*d/2, FP8 16*d,
+ * BF16 32*d; 0 for an unknown format or head_dim.  Host only. */
+size_t uq_head_block_bytes(int32_t format, int32_t head_dim);
+
+/* Bytes of one page of one pool (num_kv_heads head-blocks); 0 if invalid. */
+size_t uq_page_bytes(const uq_kv_cache* cache);
+
+/*
+ * FP4 write path ([review] §3.1; [commentary] footnote 2): for each token
+ * t < num_tokens with slot = slot_mapping[t] >= 0, rotate k_new[t][h] and
+ * v_new[t][h] (h < num_kv_heads) with the normalized WHT in float64, quantize
+ * every 32-channel group to E2M1 codes plus a UE8M0 scale byte and store them at
+ * page slot/16, slot slot%16 of k_pool / v_pool.  slot < 0 skips the token.
+ *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim], bf16 or f32
+ *                 (in_dtype), contiguous
+ *   slot_mapping  device int32 [num_tokens]
+ *   flags         must be 0
+ * cache->format must be UQ_KV_FP4.  Two tokens mapped to the same slot in one
+ * call race.  num_tokens == 0 is a no-op.
+ */
+int uq_quantize_append(const uq_kv_cache* cache, const void* k_new, const void* v_new,
+                       int32_t in_dtype, const int32_t* slot_mapping, int32_t num_tokens,
+                       uint32_t flags, uq_stream_t stream);
+
+/* FP8 baseline write ([review] §4.3 "hardware FP8 KV"): each value rounded to
+ * OCP E4M3 (nearest even, saturating at 448), scale 1, no rotation.  Same
+ * arguments as uq_quantize_append; cache->format must be UQ_KV_FP8. */
+int uq_append_fp8(const uq_kv_cache* cache, const void* k_new, const void* v_new,
+                  int32_t in_dtype, const int32_t* slot_mapping, int32_t num_tokens,
+                  uint32_t flags, uq_stream_t stream);
+
+/* BF16 baseline write ([review] §4.3 "BF16"): plain copy (f32 input rounded to
+ * nearest even bf16).  cache->format must be UQ_KV_BF16. */
+int uq_append_bf16(const uq_kv_cache* cache, const void* k_new, const void* v_new,
+                   int32_t in_dtype, const int32_t* slot_mapping, int32_t num_tokens,
+                   uint32_t flags, uq_stream_t stream);
+
+/*
+ * Query rotation ([review] §3.2, §4.2): q_fp8[r][c] = E4M3(c_d * (H_d q[r])[c]),
+ * rounded directly from the float64 rotated value.
+ *   q      device [rows][head_dim], bf16 or f32 (in_dtype)
+ *   q_fp8  device uint8 [rows][head_dim]
+ * head_dim must be 64 or 128.
+ */
+int uq_rotate_quantize_query(const void* q, int32_t in_dtype, uint8_t* q_fp8, int32_t rows,
+                             int32_t head_dim, uq_stream_t stream);
+
+/* Workspace bytes needed by the decode entry points for this shape (an upper
+ * bound valid for every seq_lens content).  0 if the arguments are invalid. */
+size_t uq_decode_workspace_bytes(const uq_kv_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_pages_per_seq);
+
+/*
+ * FP4 decode attention ([review] §3.2, §4.2, §6.3): for each sequence b and
+ * query head h, out[b][h] = sum_j p_j * V[j] with p = softmax_j(sm_scale *
+ * qhat . K[j]) over tokens j < seq_lens[b], where qhat is the rotated E4M3
+ * query and K, V are the dequantized rotated cache rows of KV head
+ * h / (num_q_heads / num_kv_heads); the result is rotated back with the same
+ * normalized WHT unless UQ_FLAG_OUT_ROTATED is set.
+ *   q           device [num_seqs][num_q_heads][head_dim], bf16 or f32 (q_dtype)
+ *   page_table  device int32 [num_seqs][max_pages_per_seq]; entries past
+ *               ceil(seq_lens[b] / 16) are not read
+ *   seq_lens    device int32 [num_seqs], each in [0, 16 * max_pages_per_seq]
+ *   out         device float [num_seqs][num_q_heads][head_dim]; must not alias
+ *               any input; a sequence of length 0 gives a zero row
+ *   workspace   device, >= uq_decode_workspace_bytes(...) bytes, 256-B aligned
+ * num_q_heads must be a multiple of num_kv_heads with a ratio of 1..16.
+ * Accuracy: codes and scales enter exactly; logits and the softmax are float32,
+ * probabilities and dequantized values enter the PV product as float16, so V
+ * groups must have E <= 13 (|v| <= 49152) to stay finite in float16.
+ */
+int uq_decode_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtype,
+                        const int32_t* page_table, int32_t max_pages_per_seq,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                        float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                        uint32_t flags, uq_stream_t stream);
+
+/* FP8 baseline decode: same arguments; cache->format must be UQ_KV_FP8; the
+ * query is rounded to E4M3 without rotation and `out` needs no unrotation
+ * (flags must be 0). */
+int uq_decode_attention_fp8(const uq_kv_cache* cache, const void* q, int32_t q_dtype,
+                            const int32_t* page_table, int32_t max_pages_per_seq,
+                            const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                            float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                            uint32_t flags, uq_stream_t stream);
+
+/* BF16 baseline decode: same arguments; cache->format must be UQ_KV_BF16 and
+ * q_dtype must be UQ_IN_BF16 (flags must be 0). */
+int uq_decode_attention_bf16(const uq_kv_cache* cache, const void* q, int32_t q_dtype,
+                             const int32_t* page_table, int32_t max_pages_per_seq,
+                             const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                             float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                             uint32_t flags, uq_stream_t stream);
+
+/* Instrumentation: the next decode call on this thread (any format) records
+ * `start` immediately before and `stop` immediately after its main split-K
+ * attention kernel, on that call's stream, then forgets both.  The events are
+ * caller-owned hipEvent_t handles (created with timing enabled); passing NULL
+ * for both cancels a pending request.  Nothing is skipped or reordered. */
+int uq_profile_next_decode(void* start_event, void* stop_event);
+
+/* Static description of a status code. */
+const char* uq_status_string(int status);
+
+/* hipError_t of the last UQ_ERR_HIP returned on this thread (0 if none). */
+int uq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* UQ_H */

@@ -1,0 +1,147 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol that
+include/uq.h declares, and its host-side validation returns the documented
+status before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_kv_cache_wht_amd as uq
+from bit_kv_cache_wht_amd import _binding as B
+import oracle as O
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "uq.h")
+FAKE = 0x10000          # non-null placeholder; validation fails before any use
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(uq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 13, names
+    h = uq.lib()
+    for n in names:
+        assert hasattr(h, n), n
+    assert set(names) == set(B._SIGS)
+
+
+def cache(fmt=B.UQ_KV_FP4, pages=4, heads=2, d=128, page_size=16, k=FAKE, v=FAKE):
+    return B._Cache(fmt, pages, page_size, heads, d, k, v)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("d", [64, 128])
+def test_block_sizes_match_oracle_layout(fmt, d):
+    assert uq.uq_head_block_bytes(fmt, d) == O.head_block_bytes(fmt, d)
+    c = cache(fmt, heads=8, d=d)
+    assert uq.lib().uq_page_bytes(ctypes.byref(c)) == O.page_bytes(fmt, 8, d)
+
+
+def test_block_sizes_invalid():
+    assert uq.uq_head_block_bytes(0, 96) == 0
+    assert uq.uq_head_block_bytes(7, 128) == 0
+    c = cache(page_size=32)
+    assert uq.lib().uq_page_bytes(ctypes.byref(c)) == 0
+    assert uq.lib().uq_page_bytes(None) == 0
+
+
+APPENDS = [("uq_quantize_append", B.UQ_KV_FP4), ("uq_append_fp8", B.UQ_KV_FP8), ("uq_append_bf16", B.UQ_KV_BF16)]
+
+
+@pytest.mark.parametrize("name,fmt", APPENDS)
+def test_append_validation(name, fmt):
+    f = getattr(uq.lib(), name)
+    ok = cache(fmt)
+    call = lambda c=ok, k=FAKE, v=FAKE, dt=0, s=FAKE, n=4, fl=0: f(ctypes.byref(c) if c is not None else None,
+                                                                    k, v, dt, s, n, fl, None)
+    assert call(c=None) == B.UQ_ERR_INVALID_ARG
+    other = (fmt + 1) % 3
+    assert call(c=cache(other)) == B.UQ_ERR_INVALID_ARG          # format mismatch
+    assert call(c=cache(fmt, page_size=8)) == B.UQ_ERR_UNSUPPORTED
+    assert call(c=cache(fmt, d=96)) == B.UQ_ERR_UNSUPPORTED
+    assert call(c=cache(fmt, heads=0)) == B.UQ_ERR_INVALID_ARG
+    assert call(c=cache(fmt, k=None)) == B.UQ_ERR_INVALID_ARG
+    assert call(k=None) == B.UQ_ERR_INVALID_ARG
+    assert call(v=None) == B.UQ_ERR_INVALID_ARG
+    assert call(s=None) == B.UQ_ERR_INVALID_ARG
+    assert call(dt=5) == B.UQ_ERR_INVALID_ARG
+    assert call(n=-1) == B.UQ_ERR_INVALID_ARG
+    assert call(fl=1) == B.UQ_ERR_INVALID_ARG
+    assert call(n=0, k=None, v=None, s=None) == B.UQ_OK            # empty append is a no-op
+
+
+def test_query_validation():
+    f = uq.lib().uq_rotate_quantize_query
+    assert f(FAKE, 3, FAKE, 4, 128, None) == B.UQ_ERR_INVALID_ARG
+    assert f(FAKE, 0, FAKE, 4, 96, None) == B.UQ_ERR_UNSUPPORTED
+    assert f(None, 0, FAKE, 4, 128, None) == B.UQ_ERR_INVALID_ARG
+    assert f(FAKE, 0, None, 4, 128, None) == B.UQ_ERR_INVALID_ARG
+    assert f(FAKE, 0, FAKE, -1, 128, None) == B.UQ_ERR_INVALID_ARG
+    assert f(None, 0, None, 0, 128, None) == B.UQ_OK
+
+
+DECODES = [("uq_decode_attention", B.UQ_KV_FP4), ("uq_decode_attention_fp8", B.UQ_KV_FP8),
+           ("uq_decode_attention_bf16", B.UQ_KV_BF16)]
+
+
+@pytest.mark.parametrize("name,fmt", DECODES)
+def test_decode_validation(name, fmt):
+    f = getattr(uq.lib(), name)
+    ok = cache(fmt, heads=2)
+    ws = uq.lib().uq_decode_workspace_bytes(ctypes.byref(ok), 3, 16, 8)
+    assert ws > 0
+
+    def call(c=ok, q=FAKE, qd=0, pt=FAKE, mp=8, sl=FAKE, B_=3, Hq=16, scale=0.1, out=FAKE, w=FAKE, wb=ws, fl=0):
+        return f(ctypes.byref(c) if c is not None else None, q, qd, pt, mp, sl, B_, Hq, scale, out, w, wb, fl, None)
+
+    assert call(c=None) == B.UQ_ERR_INVALID_ARG
+    assert call(c=cache((fmt + 1) % 3, heads=2)) == B.UQ_ERR_INVALID_ARG
+    assert call(c=cache(fmt, heads=2, d=256)) == B.UQ_ERR_UNSUPPORTED
+    assert call(Hq=15) == B.UQ_ERR_UNSUPPORTED                   # H_q % H_kv != 0
+    assert call(Hq=34) == B.UQ_ERR_UNSUPPORTED                   # group of 17 > 16
+    assert call(B_=-1) == B.UQ_ERR_INVALID_ARG
+    assert call(mp=0) == B.UQ_ERR_INVALID_ARG
+    assert call(q=None) == B.UQ_ERR_INVALID_ARG
+    assert call(pt=None) == B.UQ_ERR_INVALID_ARG
+    assert call(sl=None) == B.UQ_ERR_INVALID_ARG
+    assert call(out=None) == B.UQ_ERR_INVALID_ARG
+    assert call(qd=9) == B.UQ_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == B.UQ_ERR_INVALID_ARG
+    assert call(w=None) == B.UQ_ERR_WORKSPACE
+    assert call(wb=ws - 1) == B.UQ_ERR_WORKSPACE
+    assert call(fl=2) == B.UQ_ERR_INVALID_ARG
+    if fmt == B.UQ_KV_FP4:
+        assert call(fl=B.UQ_FLAG_OUT_ROTATED, w=None) == B.UQ_ERR_WORKSPACE     # flag accepted
+    else:
+        assert call(fl=B.UQ_FLAG_OUT_ROTATED) == B.UQ_ERR_INVALID_ARG
+    if fmt == B.UQ_KV_BF16:
+        assert call(qd=B.UQ_IN_F32) == B.UQ_ERR_UNSUPPORTED
+    assert call(B_=0, q=None, pt=None, sl=None, out=None, w=None) == B.UQ_OK
+
+
+def test_workspace_bytes_grow_with_shape():
+    c = cache(B.UQ_KV_FP4, heads=8)
+    w1 = uq.lib().uq_decode_workspace_bytes(ctypes.byref(c), 64, 64, 512)
+    w2 = uq.lib().uq_decode_workspace_bytes(ctypes.byref(c), 128, 64, 512)
+    assert 0 < w1 < w2 and w1 % 256 == 0
+    assert uq.lib().uq_decode_workspace_bytes(None, 1, 1, 1) == 0
+    assert uq.lib().uq_decode_workspace_bytes(ctypes.byref(c), 1, 0, 1) == 0
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert uq.uq_status_string(s) != "unknown status"
+    assert uq.uq_status_string(99) == "unknown status"
+    assert uq.uq_last_hip_error() == 0
+
+
+def test_profile_events_validation():
+    f = uq.lib().uq_profile_next_decode
+    assert f(FAKE, None) == B.UQ_ERR_INVALID_ARG
+    assert f(None, FAKE) == B.UQ_ERR_INVALID_ARG
+    assert f(None, None) == B.UQ_OK

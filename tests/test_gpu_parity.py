@@ -1,0 +1,156 @@
+"""GPU parity: libuq (through its C ABI) against the CPU oracle on the same seeded
+inputs.  Cache bytes (FP4 codes, UE8M0 scale bytes, FP8 and BF16 values) and
+E4M3 query bytes must be bit-exact; attention outputs must be within relative
+L2 1e-3 and max-abs 5e-3 of the oracle's float64 result computed from the
+identical quantized cache.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle as O
+from bit_kv_cache_wht_amd import workloads as W
+
+from gpu_util import (FORMATS, announce, assert_close, dev, gpu_append, gpu_cache, gpu_decode, oracle_append,
+                      oracle_decode, pools_np, torch_mod, uq)
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(name):
+    """Small workloads that still span several 4-page steps and ragged tails."""
+    if name == "tiny":
+        return W.tiny()
+    specs = {
+        "edge_lens": dict(batch=4, num_q_heads=64, num_kv_heads=8, head_dim=128, seq_lens=[1, 15, 16, 17]),
+        "gqa_ragged": dict(batch=3, num_q_heads=32, num_kv_heads=4, head_dim=128, seq_lens=[300, 1000, 77]),
+        "mha_5heads": dict(batch=2, num_q_heads=5, num_kv_heads=5, head_dim=128, seq_lens=[129, 40]),
+        "group16_d64": dict(batch=2, num_q_heads=16, num_kv_heads=1, head_dim=64, seq_lens=[200, 33]),
+        "empty_seqs": dict(batch=5, num_q_heads=8, num_kv_heads=2, head_dim=128, seq_lens=[0, 5, 0, 64, 65]),
+        "one_long": dict(batch=1, num_q_heads=8, num_kv_heads=1, head_dim=128, seq_lens=[5000]),
+        "d64_bf16": dict(batch=3, num_q_heads=12, num_kv_heads=3, head_dim=64, seq_lens=[90, 64, 250]),
+    }
+    s = specs[name]
+    return W.make_workload(name, s["batch"], s["num_q_heads"], s["num_kv_heads"], s["head_dim"], s["seq_lens"],
+                           s["seq_lens"], seed=zlib.crc32(name.encode()) % 1000 + 7)
+
+
+SMALL = ["tiny", "edge_lens", "gqa_ragged", "mha_5heads", "group16_d64", "empty_seqs", "one_long", "d64_bf16"]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("name", SMALL)
+def test_append_bit_exact(fmt, name):
+    wl = _wl(name)
+    announce(f"append {fmt} {name} T={wl.total_tokens} H={wl.num_kv_heads} d={wl.head_dim}")
+    got = pools_np(gpu_append(fmt, wl))
+    want = oracle_append(fmt, wl)
+    for g, w, kv in zip(got, want, "KV"):
+        bad = np.nonzero(g != w)
+        assert bad[0].size == 0, f"{kv} pool: {bad[0].size} bytes differ, first at {[int(x[0]) for x in bad]}"
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_append_skips_negative_slots_and_partial_calls(fmt):
+    wl = _wl("gqa_ragged")
+    announce(f"append {fmt} with skipped slots")
+    rng = np.random.default_rng(0)
+    slots = wl.slot_mapping.copy()
+    slots[rng.random(slots.size) < 0.3] = -1
+    cache = gpu_cache(fmt, wl)
+    half = wl.total_tokens // 2
+    gpu_append(fmt, wl, cache, idx=np.arange(half), slots=slots[:half])          # two calls
+    gpu_append(fmt, wl, cache, idx=np.arange(half, wl.total_tokens), slots=slots[half:])
+    want = oracle_append(fmt, wl, slots=slots)
+    for g, w in zip(pools_np(cache), want):
+        assert np.array_equal(g, w)
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_query_rotation_bytes(in_dtype, d):
+    torch = torch_mod()
+    rng = np.random.default_rng(d)
+    rows = 333
+    x = (rng.standard_normal((rows, d)) * 10.0 ** rng.integers(-6, 3, (rows, 1))).astype(np.float32)
+    x[0] = 0.0
+    x[1] = 1e4                                   # saturates after rotation
+    x[2, :] = 0; x[2, 0] = -3e-3                 # subnormal E4M3 range, negative
+    if in_dtype == "bf16":
+        arr = W._to_bf16_bits(x)
+    else:
+        arr = x
+    announce(f"query rotation {in_dtype} d={d} rows={rows}")
+    out = torch.empty((rows, d), dtype=torch.uint8, device="cuda")
+    uq().uq_rotate_quantize_query(dev(arr, in_dtype), out)
+    torch.cuda.synchronize()
+    want = O.rotate_quantize_query(arr, in_dtype=in_dtype)
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("name", SMALL)
+def test_decode_on_oracle_cache(fmt, name):
+    wl = _wl(name)
+    if fmt == "bf16" and wl.in_dtype != "bf16":
+        pytest.skip("the BF16 baseline takes a bf16 query")
+    pools = oracle_append(fmt, wl)
+    announce(f"decode {fmt} {name} B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} lens={list(wl.seq_lens)}")
+    got = gpu_decode(fmt, wl, gpu_cache(fmt, wl, pools))
+    want = oracle_decode(fmt, wl, pools)
+    assert_close(got, want, f"{fmt} {name}")
+    for b in np.nonzero(wl.seq_lens == 0)[0]:
+        assert not got[b].any()
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("name", ["tiny", "gqa_ragged", "one_long"])
+def test_end_to_end(fmt, name):
+    wl = _wl(name)
+    if fmt == "bf16" and wl.in_dtype != "bf16":
+        pytest.skip("the BF16 baseline takes a bf16 query")
+    announce(f"end-to-end {fmt} {name}")
+    got = gpu_decode(fmt, wl, gpu_append(fmt, wl))
+    want = oracle_decode(fmt, wl, oracle_append(fmt, wl))
+    assert_close(got, want, f"e2e {fmt} {name}")
+
+
+def test_fp4_out_rotated_flag():
+    wl = _wl("gqa_ragged")
+    pools = oracle_append("fp4", wl)
+    announce("decode fp4 OUT_ROTATED")
+    got = gpu_decode("fp4", wl, gpu_cache("fp4", wl, pools), flags=uq().UQ_FLAG_OUT_ROTATED)
+    want = O.wht(oracle_decode("fp4", wl, pools))        # normalized WHT is self-inverse
+    assert_close(got, want, "out rotated")
+
+
+def test_decode_repeatable_and_stream_ordered():
+    # the same call twice gives identical bits (no atomics, fixed split plan)
+    wl = _wl("one_long")
+    cache = gpu_append("fp4", wl)
+    announce("decode fp4 repeat")
+    a = gpu_decode("fp4", wl, cache)
+    b = gpu_decode("fp4", wl, cache)
+    assert np.array_equal(a, b)
+
+
+def test_fp4_decode_with_disparate_group_scales():
+    # Rows whose rotated groups differ by 2^20 in magnitude: the scaled MFMA must
+    # keep the small group's contribution (its UE8M0 block scale differs per lane).
+    rng = np.random.default_rng(11)
+    T, H, d = 96, 1, 64
+    y = rng.standard_normal((T, H, d))
+    y[..., :32] *= 2.0 ** 10
+    y[..., 32:] *= 2.0 ** -10
+    x = O.wht(y).astype(np.float32)
+    wl = W.make_workload("wide", 1, 4, 1, d, [T], [T], in_dtype="f32", seed=3)
+    wl.k[:] = x
+    wl.v[:] = x[::-1]
+    wl.q[:] = (rng.standard_normal((1, 4, d)) * 2.0 ** -8).astype(np.float32)
+    pools = oracle_append("fp4", wl)
+    announce("decode fp4 with group scales 2^10 / 2^-10")
+    got = gpu_decode("fp4", wl, gpu_cache("fp4", wl, pools))
+    want = oracle_decode("fp4", wl, pools)
+    # compare per output element relative to that row's scale
+    assert_close(got / np.abs(want).max(), want / np.abs(want).max(), "fp4 wide scales (normalized)")
