@@ -175,6 +175,7 @@ template <int D> __device__ __forceinline__ v8i load_q_fp8(const uint8_t* qrow, 
 }
 
 template <int D> struct Fp4Pol {
+  static constexpr int kStages = 4;
   static constexpr int kBlk = Fp4Block<D>::kBytes;
   static constexpr int kCode = Fp4Block<D>::kCodeBytes;
   static constexpr int kGroups = D / 32;
@@ -265,6 +266,7 @@ template <int D> struct Fp4Pol {
 // small products when large ones are present in the same instruction, which
 // with unrotated outlier channels moves logits by ~1e-4 relative.
 template <int D> struct Fp8Pol {
+  static constexpr int kStages = 3;
   static constexpr int kBlk = kPage * D;
   static constexpr int kTiles = D / 16;
   static constexpr int kLanesK = D / 32;   // lane groups holding 32 channels of a row
@@ -340,6 +342,7 @@ template <int D> struct Fp8Pol {
 };
 
 template <int D> struct Bf16Pol {
+  static constexpr int kStages = 2;
   static constexpr int kBlk = kPage * D * 2;
   static constexpr int kTiles = D / 16;
   static constexpr int kK = D / 32;     // 16x16x32 MFMAs per token row
@@ -417,7 +420,9 @@ struct KArgs {
 };
 
 template <class Pol, int D>
-__global__ __launch_bounds__(256, 1) void decode_kernel(const KArgs a) {
+__global__ __launch_bounds__(256, 1) void decode_kernel(const KArgs a, const int32_t* __restrict__ page_table,
+                                                        const int2* __restrict__ items,
+                                                        const int32_t* __restrict__ seq_lens) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15, j4 = lane >> 4;
@@ -427,14 +432,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const KArgs a) {
     const int bs = item / a.n_hg;
     const int hk = (item - bs * a.n_hg) * kWavesPerWG + wave;
     if (hk >= a.Hkv) continue;
-    const int2 it2 = a.items[bs];
+    const int2 it2 = items[bs];
     const int b = it2.x;
-    const int L = a.seq_lens[b];
+    const int L = seq_lens[b];
     const int pages = (L + kPage - 1) / kPage;
     const int p_begin = it2.y * pps;
     const int p_end = min(p_begin + pps, pages);
     const int n_step = (p_end - p_begin + 3) >> 2;
-    const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
+    const int32_t* pt = page_table + (int64_t)b * a.max_pages;
     const int hq0 = hk * a.G;
 
     typename Pol::QOp qo;
@@ -446,11 +451,23 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const KArgs a) {
     for (int t = 0; t < Pol::kTiles; ++t) O[t] = v4f{0, 0, 0, 0};
 
     const int64_t head_off = (int64_t)hk * Pol::kBlk;
-    auto load_step = [&](typename Pol::Step& st, int s) {
+    // The four page ids of a step are wave-uniform: scalar loads fetch them one
+    // step ahead of the data loads that use them.  A vector load here would sit
+    // at the back of the in-order vector-memory counter, and waiting for it
+    // would also wait for every prefetch issued before it.
+    struct Ids { int v[4]; };
+    auto fetch_ids = [&](int s) {
+      Ids r;
       const int pg = p_begin + 4 * s;
-      const int pk = pg + (r16 >> 2), pv = pg + j4;
-      const int idk = pt[pk < p_end ? pk : p_begin];
-      const int idv = pt[pv < p_end ? pv : p_begin];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) r.v[x] = pt[min(pg + x, p_end - 1)];
+      return r;
+    };
+    auto pick = [](const Ids& ids, int x) {
+      return x == 0 ? ids.v[0] : x == 1 ? ids.v[1] : x == 2 ? ids.v[2] : ids.v[3];
+    };
+    auto load_step = [&](typename Pol::Step& st, const Ids& ids) {
+      const int idk = pick(ids, r16 >> 2), idv = pick(ids, j4);
       Pol::load(st, a.k_pool + (int64_t)idk * a.page_bytes + head_off, a.v_pool + (int64_t)idv * a.page_bytes + head_off,
                 r16, j4);
     };
@@ -511,16 +528,30 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const KArgs a) {
       }
     };
 
-    typename Pol::Step A, Bst;
-    if (n_step > 0) load_step(A, 0);
-    for (int s = 0; s < n_step; s += 2) {
-      if (s + 1 < n_step) load_step(Bst, s + 1);
-      compute_step(A, s);
-      if (s + 1 < n_step) {
-        if (s + 2 < n_step) load_step(A, s + 2);
-        compute_step(Bst, s + 1);
+    // Software pipeline: kStages register buffers, kStages - 1 steps of loads in
+    // flight while one step computes (latency x bandwidth needs ~100 KB in
+    // flight per CU).  Buffer indices are compile-time after unrolling.
+    // Prefetches are issued unconditionally, clamped to the last step (those
+    // addresses were just loaded, so the repeats hit in L2), which keeps the
+    // number of outstanding loads the same on every path and lets each step
+    // wait only for its own data.
+    constexpr int P = Pol::kStages;
+    typename Pol::Step st[P];
+    const int last = n_step - 1;
+#pragma unroll
+    for (int i = 0; i < P - 1; ++i) load_step(st[i], fetch_ids(min(i, last)));
+    Ids next = fetch_ids(min(P - 1, last));
+    for (int s0 = 0;; s0 += P) {
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int cur = s0 + i;
+        if (cur > last) goto steps_done;
+        load_step(st[(i + P - 1) % P], next);
+        next = fetch_ids(min(cur + P, last));
+        compute_step(st[i], cur);
       }
     }
+  steps_done:
 
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
@@ -550,16 +581,47 @@ __global__ __launch_bounds__(256) void reduce_kernel(const PlanHdr* hdr, const i
 #pragma unroll
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
   if (ns > 0) {
+    // split headers: lane s holds (m, l) of split s (64 splits per pass)
     float mmax = -INFINITY;
-    for (int s = 0; s < ns; ++s) mmax = fmaxf(mmax, ml[(int64_t)(s0 + s) * Hq + h].x);
-    float l = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const int64_t prow = (int64_t)(s0 + s) * Hq + h;
-      const float2 v = ml[prow];
-      const float w = __builtin_amdgcn_exp2f(v.x - mmax);
-      l += w * v.y;
+    for (int c = 0; c < ns; c += 64) {
+      const float m = c + lane < ns ? ml[(int64_t)(s0 + c + lane) * Hq + h].x : -INFINITY;
+      mmax = fmaxf(mmax, m);
+    }
 #pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] += w * po[prow * D + lane + 64 * k];
+    for (int x = 32; x >= 1; x >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, x));
+    float l = 0.f;
+    for (int c = 0; c < ns; c += 64) {
+      const int n = min(64, ns - c);
+      float w = 0.f, lw = 0.f;
+      if (lane < n) {
+        const float2 v = ml[(int64_t)(s0 + c + lane) * Hq + h];
+        w = __builtin_amdgcn_exp2f(v.x - mmax);
+        lw = w * v.y;
+      }
+#pragma unroll
+      for (int x = 32; x >= 1; x >>= 1) lw += __shfl_xor(lw, x);
+      l += lw;
+      const float* src = po + ((int64_t)(s0 + c) * Hq + h) * D + lane;
+      const int64_t stride = (int64_t)Hq * D;
+      int s = 0;
+      for (; s + 4 <= n; s += 4) {               // four independent split rows in flight
+        float v[4][PER];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int k = 0; k < PER; ++k) v[u][k] = src[(s + u) * stride + 64 * k];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float wu = __shfl(w, s + u);
+#pragma unroll
+          for (int k = 0; k < PER; ++k) o[k] += wu * v[u][k];
+        }
+      }
+      for (; s < n; ++s) {
+        const float ws = __shfl(w, s);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) o[k] += ws * src[s * stride + 64 * k];
+      }
     }
     const float inv = 1.f / l;
 #pragma unroll
@@ -634,9 +696,11 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
     e = hipEventRecord(a.ev_start, s);
     if (e != hipSuccess) return e;
   }
-  if (a.format == UQ_KV_FP4) hipLaunchKernelGGL((decode_kernel<Fp4Pol<D>, D>), g2, blk, 0, s, k);
-  else if (a.format == UQ_KV_FP8) hipLaunchKernelGGL((decode_kernel<Fp8Pol<D>, D>), g2, blk, 0, s, k);
-  else hipLaunchKernelGGL((decode_kernel<Bf16Pol<D>, D>), g2, blk, 0, s, k);
+  if (a.format == UQ_KV_FP4)
+    hipLaunchKernelGGL((decode_kernel<Fp4Pol<D>, D>), g2, blk, 0, s, k, a.page_table, items, a.seq_lens);
+  else if (a.format == UQ_KV_FP8)
+    hipLaunchKernelGGL((decode_kernel<Fp8Pol<D>, D>), g2, blk, 0, s, k, a.page_table, items, a.seq_lens);
+  else hipLaunchKernelGGL((decode_kernel<Bf16Pol<D>, D>), g2, blk, 0, s, k, a.page_table, items, a.seq_lens);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.ev_stop != nullptr) {
