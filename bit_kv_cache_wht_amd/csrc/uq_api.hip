@@ -65,7 +65,7 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   if (num_seqs < 0 || max_pages_per_seq < 1 || num_q_heads < 1) return UQ_ERR_INVALID_ARG;
   if (num_q_heads % cache->num_kv_heads != 0) return UQ_ERR_UNSUPPORTED;
   if (num_q_heads / cache->num_kv_heads > 16) return UQ_ERR_UNSUPPORTED;
-  if (!(sm_scale == sm_scale)) return UQ_ERR_INVALID_ARG;   // NaN
+  if (!(sm_scale > 0.f) || sm_scale > 3.0e38f) return UQ_ERR_INVALID_ARG;   // NaN, <= 0, inf
   if (num_seqs == 0) return UQ_OK;
   if (q == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr) return UQ_ERR_INVALID_ARG;
   const size_t need = uq_decode_workspace_bytes(cache, num_seqs, num_q_heads, max_pages_per_seq);

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
   if (!is_v) {
     uint8_t* blk = a.k_pool + (int64_t)page * a.page_bytes + (int64_t)h * BLK;
     *reinterpret_cast<uint4*>(blk + off * (D / 2) + 16 * p) = make_uint4(w[0], w[1], w[2], w[3]);
-    blk[CODE + off * (D / 32) + p] = scale_byte;
+    blk[CODE + 4 * ((off & 3) * (D / 32) + p) + (off >> 2)] = scale_byte;   // [slot%4][group][slot/4]
   } else {
     uint8_t* blk = a.v_pool + (int64_t)page * a.page_bytes + (int64_t)h * BLK;
 #pragma unroll

@@ -28,15 +28,18 @@
 // first) and an FP8 operand k = 16(l/16)..+15 and 64+16(l/16)..+15; lane i+16b
 // supplies the scale of row i, k-block b.  For 16x16x32 f16, lane l holds
 // k = 8(l/16)..+7; results land in lane l as column l%16, rows 4(l/16)..+3.
+#include <type_traits>
+
 #include "uq_device.h"
 #include "uq_internal.h"
+
 
 namespace uq {
 
 namespace {
 
 constexpr int kTargetItems = 1024;   // decode items per launch the plan aims for
-constexpr int kDecodeWGs = 256;      // persistent decode workgroups (1 per CU)
+constexpr int kCUs = 256;            // MI355X compute units; one 4-wave workgroup per SIMD wave slot
 
 struct PlanHdr {
   int32_t n_bs;   // (sequence, split) pairs
@@ -174,73 +177,74 @@ template <int D> __device__ __forceinline__ v8i load_q_fp8(const uint8_t* qrow, 
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
+// FP4.  Lane (r, j) of the PV product owns channel pairs CPL*r .. CPL*r + CPL-1
+// (CPL = D/32, i.e. channels 2*CPL*r .. 2*CPL*r + 2*CPL - 1, all in group
+// r*CPL/16), so one scale per token serves all of its conversions.
 template <int D> struct Fp4Pol {
-  static constexpr int kStages = 4;
+  static constexpr int kOcc = 2;        // waves per SIMD (256 registers each)
+  static constexpr int kStages = 2;
   static constexpr int kBlk = Fp4Block<D>::kBytes;
   static constexpr int kCode = Fp4Block<D>::kCodeBytes;
   static constexpr int kGroups = D / 32;
+  static constexpr int kCPL = D / 32;             // channel pairs per lane
   static constexpr int kTiles = D / 16;
   struct Step {
     uint4 kc[4];          // K codes, MFMA m: token slot 4m + (lane%16)%4, group lane/16
-    uint32_t ks[4];       // K scale byte for the same (token, group)
-    uint4 vc[kGroups];    // V codes of channel pair 16g + lane%16, slots 0..15
-    uint4 vs[kGroups];    // V scale bytes of group g, slots 0..15
+    uint32_t ks;          // K scale bytes of those 4 tokens (byte m)
+    uint4 vc[kCPL];       // V codes of channel pair kCPL*(lane%16) + q, slots 0..15
+    uint4 vs;             // V scale bytes of that group, slots 0..15
   };
   struct QOp { v8i b; };
   __device__ static void load_q(QOp& qo, const uint8_t* qrow, bool valid, int j4) {
     qo.b = load_q_fp8<D>(qrow, valid, j4);
   }
   __device__ static void load(Step& st, const uint8_t* kb, const uint8_t* vb, int r16, int j4) {
+    if (j4 < kGroups) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int slot = 4 * m + (r16 & 3);
-      if (j4 < kGroups) {
-        st.kc[m] = load16(kb + slot * (D / 2) + 16 * j4);
-        st.ks[m] = kb[kCode + slot * (D / 32) + j4];
-      } else {
-        st.kc[m] = make_uint4(0, 0, 0, 0);
-        st.ks[m] = 127;
-      }
+      for (int m = 0; m < 4; ++m) st.kc[m] = load16(kb + (4 * m + (r16 & 3)) * (D / 2) + 16 * j4);
+      // scale bytes are stored [slot % 4][group][slot / 4]: one dword per lane
+      st.ks = *reinterpret_cast<const uint32_t*>(kb + kCode + 4 * ((r16 & 3) * kGroups + j4));
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) st.kc[m] = make_uint4(0, 0, 0, 0);
+      st.ks = 0x7F7F7F7Fu;
     }
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      st.vc[g] = load16(vb + (16 * g + r16) * kPage);
-      st.vs[g] = load16(vb + kCode + 16 * g);
-    }
+    for (int q = 0; q < kCPL; ++q) st.vc[q] = load16(vb + (kCPL * r16 + q) * kPage);
+    st.vs = load16(vb + kCode + kPage * ((kCPL * r16) / 16));
+  }
+  template <int M> __device__ static v4f qk1(const Step& st, const QOp& qo) {
+    const v8i a = v8i{(int)st.kc[M].x, (int)st.kc[M].y, (int)st.kc[M].z, (int)st.kc[M].w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qo.b, v4f{0, 0, 0, 0}, 4 /*A fp4*/, 0 /*B fp8*/,
+                                                           M /*byte M of ks*/, (int)st.ks, 0, 127);
   }
   __device__ static void qk(const Step& st, const QOp& qo, v4f (&S)[4]) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const v8i a = v8i{(int)st.kc[m].x, (int)st.kc[m].y, (int)st.kc[m].z, (int)st.kc[m].w, 0, 0, 0, 0};
-      S[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qo.b, v4f{0, 0, 0, 0}, 4 /*A fp4*/, 0 /*B fp8*/,
-                                                             0, (int)st.ks[m], 0, 127);
-    }
+    S[0] = qk1<0>(st, qo);
+    S[1] = qk1<1>(st, qo);
+    S[2] = qk1<2>(st, qo);
+    S[3] = qk1<3>(st, qo);
   }
-  // Converts group g's 16 slots to f16: X[t] = (channel 2c, channel 2c+1) of slot t,
-  // scaled by 2^(byte - 127) in the conversion.
-  __device__ static void convert_group(const Step& st, int g, uint32_t (&X)[16]) {
-    const uint32_t c[4] = {st.vc[g].x, st.vc[g].y, st.vc[g].z, st.vc[g].w};
-    const uint32_t s[4] = {st.vs[g].x, st.vs[g].y, st.vs[g].z, st.vs[g].w};
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const float scale = __uint_as_float(((s[t >> 2] >> (8 * (t & 3))) & 0xFFu) << 23);
-      v2h h;
-      switch (t & 3) {
-        case 0: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], scale, 0); break;
-        case 1: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], scale, 1); break;
-        case 2: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], scale, 2); break;
-        default: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], scale, 3); break;
-      }
-      X[t] = __builtin_bit_cast(uint32_t, h);
-    }
-  }
-  // Accumulates the PV product of one step into O.
   template <class MaskFn>
   __device__ static void pv(const Step& st, const v8h (&P)[2][2], v4f (&O)[kTiles], MaskFn mask) {
+    const uint32_t s[4] = {st.vs.x, st.vs.y, st.vs.z, st.vs.w};
+    float sc[16];
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      uint32_t X[16];
-      convert_group(st, g, X);
+    for (int t = 0; t < 16; ++t) sc[t] = __uint_as_float(((s[t >> 2] >> (8 * (t & 3))) & 0xFFu) << 23);
+#pragma unroll
+    for (int q = 0; q < kCPL; ++q) {
+      const uint32_t c[4] = {st.vc[q].x, st.vc[q].y, st.vc[q].z, st.vc[q].w};
+      uint32_t X[16];      // slot t: (channel 2cp, channel 2cp + 1) scaled by 2^(byte_t - 127)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        v2h h;
+        switch (t & 3) {
+          case 0: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 0); break;
+          case 1: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 1); break;
+          case 2: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 2); break;
+          default: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 3); break;
+        }
+        X[t] = __builtin_bit_cast(uint32_t, h);
+      }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         uint32_t ev[4], od[4];
@@ -252,13 +256,13 @@ template <int D> struct Fp4Pol {
         }
         const v8h ae = __builtin_bit_cast(v8h, make_uint4(ev[0], ev[1], ev[2], ev[3]));
         const v8h ao = __builtin_bit_cast(v8h, make_uint4(od[0], od[1], od[2], od[3]));
-        O[2 * g] = mma2(ae, P[half], O[2 * g]);
-        O[2 * g + 1] = mma2(ao, P[half], O[2 * g + 1]);
+        O[2 * q] = mma2(ae, P[half], O[2 * q]);
+        O[2 * q + 1] = mma2(ao, P[half], O[2 * q + 1]);
       }
     }
   }
-  // Tile 2g holds even channels 2(16g + row), tile 2g+1 the odd ones.
-  __device__ static int channel(int tile, int j4, int v) { return 2 * (16 * (tile >> 1) + 4 * j4 + v) + (tile & 1); }
+  // Tile 2q + par, row 4j + v: channel pair kCPL * (4j + v) + q, channel 2 * pair + par.
+  __device__ static int channel(int tile, int j4, int v) { return 2 * (kCPL * (4 * j4 + v) + (tile >> 1)) + (tile & 1); }
 };
 
 // FP8 baseline.  QK runs on f16 MFMAs after an exact E4M3 -> f16 conversion:
@@ -266,6 +270,7 @@ template <int D> struct Fp4Pol {
 // small products when large ones are present in the same instruction, which
 // with unrotated outlier channels moves logits by ~1e-4 relative.
 template <int D> struct Fp8Pol {
+  static constexpr int kOcc = 1;
   static constexpr int kStages = 3;
   static constexpr int kBlk = kPage * D;
   static constexpr int kTiles = D / 16;
@@ -342,6 +347,7 @@ template <int D> struct Fp8Pol {
 };
 
 template <int D> struct Bf16Pol {
+  static constexpr int kOcc = 1;
   static constexpr int kStages = 2;
   static constexpr int kBlk = kPage * D * 2;
   static constexpr int kTiles = D / 16;
@@ -420,7 +426,7 @@ struct KArgs {
 };
 
 template <class Pol, int D>
-__global__ __launch_bounds__(256, 1) void decode_kernel(const KArgs a, const int32_t* __restrict__ page_table,
+__global__ __launch_bounds__(256, Pol::kOcc) void decode_kernel(const KArgs a, const int32_t* __restrict__ page_table,
                                                         const int2* __restrict__ items,
                                                         const int32_t* __restrict__ seq_lens) {
   const int lane = threadIdx.x & 63;
@@ -446,6 +452,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const KArgs a, const int
     Pol::load_q(qo, a.q + (int64_t)(b * a.Hq + hq0 + r16) * a.q_row_bytes, r16 < a.G, j4);
 
     float m_run = -INFINITY, l_run = 0.f;
+    const float m_slack = 8.0f / a.scale_log2;     // 2^8 headroom in raw logit units
     v4f O[Pol::kTiles];
 #pragma unroll
     for (int t = 0; t < Pol::kTiles; ++t) O[t] = v4f{0, 0, 0, 0};
@@ -471,41 +478,52 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const KArgs a, const int
       Pol::load(st, a.k_pool + (int64_t)idk * a.page_bytes + head_off, a.v_pool + (int64_t)idv * a.page_bytes + head_off,
                 r16, j4);
     };
-    auto compute_step = [&](const typename Pol::Step& st, int s) {
+    // One step: QK, online softmax, PV.  MASKED handles a partial last step
+    // (pages past the split, slots past the sequence); every other step is full.
+    auto compute_step = [&](const typename Pol::Step& st, int s, auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
       const int pg = p_begin + 4 * s;
       v4f S[4];
       Pol::qk(st, qo, S);
       // tokens of page pg + j4 held by this lane: slots 4m + v
-      const int tok0 = (pg + j4) * kPage;
-      const int nvalid = (pg + j4 < p_end) ? min(kPage, L - tok0) : 0;   // valid slots of page j4
-      const bool full = (pg + 4 <= p_end) && ((pg + 4) * kPage <= L);
+      int nvalid = kPage;
       float t[16];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float x = S[m][v] * a.scale_log2;
-          t[4 * m + v] = (full || 4 * m + v < nvalid) ? x : -INFINITY;
-        }
-      float mx = t[0];
+        for (int v = 0; v < 4; ++v) t[4 * m + v] = S[m][v];
+      if constexpr (MASKED) {
+        const int tok0 = (pg + j4) * kPage;
+        nvalid = (pg + j4 < p_end) ? min(kPage, L - tok0) : 0;
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, t[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        for (int i = 0; i < 16; ++i) t[i] = i < nvalid ? t[i] : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+#pragma unroll
+      for (int i = 4; i < 16; i += 2) mx = fmaxf(mx, fmaxf(t[i], t[i + 1]));
+      // Conditional rescaling: exponents are taken against the running reference
+      // m_run as long as no logit exceeds it by more than 8 / scale_log2 (so
+      // p <= 2^8, well inside float16); only then is the reference raised,
+      // which needs the cross-lane maximum and a rescale of l and O.
+      if (__any(mx > m_run + m_slack)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2);
+        l_run *= alpha;
+#pragma unroll
+        for (int tt = 0; tt < Pol::kTiles; ++tt) O[tt] *= alpha;
+        m_run = m_new;
+      }
+      const float neg_mc = -m_run * a.scale_log2;
       float psum = 0.f;
       float pf[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        pf[i] = __builtin_amdgcn_exp2f(t[i] - m_use);
+        pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
         psum += pf[i];
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int tt = 0; tt < Pol::kTiles; ++tt) O[tt] *= alpha;
+      l_run += psum;
       v8h P[2][2];
 #pragma unroll
       for (int half = 0; half < 2; ++half)
@@ -513,9 +531,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const KArgs a, const int
         for (int i = 0; i < 8; ++i) {
           const _Float16 hi = (_Float16)pf[8 * half + i];
           P[half][0][i] = hi;
-          P[half][1][i] = (_Float16)(pf[8 * half + i] - (float)hi);
+          P[half][1][i] = (_Float16)__builtin_fmaf((float)hi, -1.0f, pf[8 * half + i]);   // exact p - hi
         }
-      if (full) {
+      if constexpr (!MASKED) {
         Pol::pv(st, P, O, [](int, int, uint32_t x) { return x; });
       } else {
         // zero V of slots past the valid ones so garbage in unwritten slots cannot
@@ -538,6 +556,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const KArgs a, const int
     constexpr int P = Pol::kStages;
     typename Pol::Step st[P];
     const int last = n_step - 1;
+    // the last step is full when its 4 pages exist and hold 64 valid tokens
+    const bool last_full = (p_begin + 4 * n_step <= p_end) && ((p_begin + 4 * n_step) * kPage <= L);
 #pragma unroll
     for (int i = 0; i < P - 1; ++i) load_step(st[i], fetch_ids(min(i, last)));
     Ids next = fetch_ids(min(P - 1, last));
@@ -548,7 +568,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const KArgs a, const int
         if (cur > last) goto steps_done;
         load_step(st[(i + P - 1) % P], next);
         next = fetch_ids(min(cur + P, last));
-        compute_step(st[i], cur);
+        if (cur < last || last_full) compute_step(st[i], cur, std::false_type{});
+        else compute_step(st[i], cur, std::true_type{});
       }
     }
   steps_done:
@@ -562,7 +583,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const KArgs a, const int
       for (int tt = 0; tt < Pol::kTiles; ++tt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) o[Pol::channel(tt, j4, v)] = O[tt][v];
-      if (j4 == 0) a.ml[prow] = make_float2(m_run, l_tot);
+      if (j4 == 0) a.ml[prow] = make_float2(m_run * a.scale_log2, l_tot);
     }
   }
 }
@@ -691,7 +712,9 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   k.ml = ml;
   k.po = po;
   const int max_items = L.max_bs * k.n_hg;
-  const dim3 g2((unsigned)(max_items < kDecodeWGs ? max_items : kDecodeWGs));
+  const int occ = a.format == UQ_KV_FP4 ? Fp4Pol<D>::kOcc : 1;
+  const int wgs = kCUs * occ;
+  const dim3 g2((unsigned)(max_items < wgs ? max_items : wgs));
   if (a.ev_start != nullptr) {
     e = hipEventRecord(a.ev_start, s);
     if (e != hipSuccess) return e;

@@ -244,7 +244,7 @@ def bf16_round_bits(x32) -> np.ndarray:
 
 # --------------------------------------------------------------------------
 # Paged cache layout (reading R8).  Pools are uint8 [num_pages][H_kv][block].
-#   FP4 K block: codes[16 tok][d/2] (token-major) then scales[16 tok][d/32]
+#   FP4 K block: codes[16 tok][d/2] (token-major) then scales[tok % 4][d/32][tok // 4]
 #   FP4 V block: codes[d/2 channel pairs][16 tok] then scales[d/32 groups][16 tok]
 #   FP8 K block: [16 tok][d] bytes;  FP8 V block: [d][16 tok] bytes
 #   BF16 K block: [16 tok][d] bf16;  BF16 V block: [d][16 tok] bf16 (little endian)
@@ -272,7 +272,8 @@ def fp4_k_code_offset(tok, byte, d):
 
 
 def fp4_k_scale_offset(tok, group, d):
-    return PAGE_SIZE * (d // 2) + tok * (d // GROUP) + group
+    # scale bytes ordered [slot % 4][group][slot // 4]
+    return PAGE_SIZE * (d // 2) + ((tok % 4) * (d // GROUP) + group) * 4 + tok // 4
 
 
 def fp4_v_code_offset(tok, pair, d):

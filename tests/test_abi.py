@@ -112,6 +112,9 @@ def test_decode_validation(name, fmt):
     assert call(out=None) == B.UQ_ERR_INVALID_ARG
     assert call(qd=9) == B.UQ_ERR_INVALID_ARG
     assert call(scale=float("nan")) == B.UQ_ERR_INVALID_ARG
+    assert call(scale=0.0) == B.UQ_ERR_INVALID_ARG
+    assert call(scale=-0.1) == B.UQ_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == B.UQ_ERR_INVALID_ARG
     assert call(w=None) == B.UQ_ERR_WORKSPACE
     assert call(wb=ws - 1) == B.UQ_ERR_WORKSPACE
     assert call(fl=2) == B.UQ_ERR_INVALID_ARG
