@@ -117,7 +117,7 @@ class Runner:
         self.page_table = dev(wl.page_table)
         self.seq_lens = dev(wl.seq_lens)
         self.out = torch.empty((wl.batch, wl.num_q_heads, d), dtype=torch.float32, device="cuda")
-        self.ws = torch.empty(uq.uq_decode_workspace_bytes(self.cache, wl.batch, wl.num_q_heads,
+        self.ws = torch.zeros(uq.uq_decode_workspace_bytes(self.cache, wl.batch, wl.num_q_heads,
                                                            wl.page_table.shape[1]), dtype=torch.uint8, device="cuda")
         self.sm_scale = float(np.float32(1.0 / np.sqrt(d)))
         torch.cuda.synchronize()

@@ -14,29 +14,6 @@
 
 namespace uq {
 
-template <int IN> __device__ __forceinline__ void load_row32(const void* base, int64_t elem, double (&x)[32]) {
-  if constexpr (IN == UQ_IN_BF16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint4 u = p[w];
-      const uint32_t d[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[8 * w + 2 * i] = bf16_bits_to_f64(d[i] & 0xFFFFu);
-        x[8 * w + 2 * i + 1] = bf16_bits_to_f64(d[i] >> 16);
-      }
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const float4 f = p[w];
-      x[4 * w] = f.x; x[4 * w + 1] = f.y; x[4 * w + 2] = f.z; x[4 * w + 3] = f.w;
-    }
-  }
-}
-
 // FP4 write path ([review] §3.1; [commentary] footnote 2): WHT, group absmax,
 // UE8M0 scale byte, E2M1 codes, two codes per byte, paged store.
 template <int D, int IN>
@@ -86,7 +63,11 @@ __global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
   } else {
     uint8_t* blk = a.v_pool + (int64_t)page * a.page_bytes + (int64_t)h * BLK;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) blk[(16 * p + i) * kPage + off] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+    for (int i = 0; i < 16; ++i) {          // channel pair c = 16p + i, row 16 (c % CPL) + c / CPL
+      constexpr int CPL = D / 32;
+      const int c = 16 * p + i;
+      blk[(16 * (c % CPL) + c / CPL) * kPage + off] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+    }
     blk[CODE + p * kPage + off] = scale_byte;
   }
 }

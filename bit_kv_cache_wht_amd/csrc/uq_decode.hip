@@ -1,16 +1,14 @@
-// Split-K GQA decode attention over the paged FP4 / FP8 / BF16 cache.
+// Split-K GQA decode attention over the paged FP4 / FP8 / BF16 cache, one kernel.
 //
 // [review] = "[arXiv 2606.20474] UltraQuant: 컨텍스트가 긴 에이전트를 위한 4비트 KV 캐싱"
 //            (manon006.tistory.com/395)
 //
-// Launch sequence on one stream:
-//   1. query + plan: the query is rotated and rounded to E4M3 once, outside the
-//      key loop ([review] §4.2; skipped for BF16); one extra workgroup turns
-//      seq_lens into the list of (sequence, split) pairs.
-//   2. decode: persistent workgroups of 4 waves walk the item list; one wave
-//      streams the pages of one KV head of one split, four pages per step.
-//   3. reduce: merges the split partials (m, l, o), normalizes and, for FP4,
-//      rotates the output back with the normalized WHT.
+// One launch per call.  Each workgroup derives the split plan from seq_lens in
+// LDS, rotates and rounds its query rows to E4M3 once, outside the key loop
+// ([review] §4.2; BF16 keeps bf16), streams the pages of its (sequence, KV head,
+// split) item with its four waves, merges them in LDS and writes the output
+// rotated back with the normalized WHT.  Sequences split across workgroups are
+// merged by the last workgroup to finish.
 //
 // Per step a wave covers 4 pages (64 tokens) of one KV head and up to 16 query
 // heads (the GQA group, padded to the 16 MFMA columns):
@@ -38,113 +36,8 @@ namespace uq {
 
 namespace {
 
-constexpr int kTargetItems = 1024;   // decode items per launch the plan aims for
+constexpr int kTargetItems = 512;    // decode items per launch the plan aims for (one per workgroup)
 constexpr int kCUs = 256;            // MI355X compute units; one 4-wave workgroup per SIMD wave slot
-
-struct PlanHdr {
-  int32_t n_bs;   // (sequence, split) pairs
-  int32_t pps;    // pages per split, multiple of 4
-};
-
-// ------------------------------------------------------------------ plan
-__device__ void plan_block(const int32_t* seq_lens, int B, int target_bs, PlanHdr* hdr, int32_t* base,
-                           int2* items) {
-  __shared__ int32_t red[256];
-  __shared__ int32_t s_pps, s_carry;
-  const int tid = threadIdx.x;
-  int32_t tot = 0;
-  for (int b = tid; b < B; b += blockDim.x) tot += (seq_lens[b] + kPage - 1) / kPage;
-  red[tid] = tot;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  if (tid == 0) {
-    int pps = (red[0] + target_bs - 1) / target_bs;
-    pps = pps < 4 ? 4 : (pps + 3) & ~3;
-    s_pps = pps;
-    s_carry = 0;
-  }
-  __syncthreads();
-  const int pps = s_pps;
-  for (int b0 = 0; b0 < B; b0 += blockDim.x) {
-    const int b = b0 + tid;
-    const int pages = b < B ? (seq_lens[b] + kPage - 1) / kPage : 0;
-    const int ns = (pages + pps - 1) / pps;
-    red[tid] = ns;
-    __syncthreads();
-    for (int s = 1; s < 256; s <<= 1) {       // inclusive Hillis-Steele scan
-      const int v = tid >= s ? red[tid - s] : 0;
-      __syncthreads();
-      red[tid] += v;
-      __syncthreads();
-    }
-    const int start = s_carry + red[tid] - ns;
-    if (b < B) {
-      base[b] = start;
-      for (int s = 0; s < ns; ++s) items[start + s] = make_int2(b, s);
-    }
-    __syncthreads();
-    if (tid == blockDim.x - 1) s_carry += red[tid];
-    __syncthreads();
-  }
-  if (tid == 0) {
-    base[B] = s_carry;
-    hdr->n_bs = s_carry;
-    hdr->pps = pps;
-  }
-}
-
-template <int D, int IN, bool ROT>
-__global__ __launch_bounds__(256) void query_plan_kernel(const void* q, uint8_t* qbuf, int rows, const int32_t* seq_lens,
-                                                         int B, int target_bs, PlanHdr* hdr, int32_t* base, int2* items) {
-  if (blockIdx.x == gridDim.x - 1) {
-    plan_block(seq_lens, B, target_bs, hdr, base, items);
-    return;
-  }
-  if (qbuf == nullptr) return;
-  constexpr int LPR = D / 32;
-  constexpr int RPW = 64 / LPR;
-  const int lane = threadIdx.x & 63;
-  const int p = lane % LPR;
-  const int64_t row0 = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * RPW;
-  if (row0 >= rows) return;
-  const int64_t row = row0 + lane / LPR;
-  const bool in_range = row < rows;
-  const int64_t r = in_range ? row : 0;
-  double x[32];
-  if constexpr (IN == UQ_IN_BF16) {
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + r * D + 32 * p);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint4 u = src[w];
-      const uint32_t d[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[8 * w + 2 * i] = bf16_bits_to_f64(d[i] & 0xFFFFu);
-        x[8 * w + 2 * i + 1] = bf16_bits_to_f64(d[i] >> 16);
-      }
-    }
-  } else {
-    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(q) + r * D + 32 * p);
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const float4 f = src[w];
-      x[4 * w] = f.x; x[4 * w + 1] = f.y; x[4 * w + 2] = f.z; x[4 * w + 3] = f.w;
-    }
-  }
-  if constexpr (ROT) wht_row<D>(x, lane);
-  uint32_t w[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    w[i] = e4m3_from_f64(x[4 * i]) | e4m3_from_f64(x[4 * i + 1]) << 8 | e4m3_from_f64(x[4 * i + 2]) << 16 |
-           e4m3_from_f64(x[4 * i + 3]) << 24;
-  if (!in_range) return;
-  uint4* o = reinterpret_cast<uint4*>(qbuf + r * D + 32 * p);
-  o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-  o[1] = make_uint4(w[4], w[5], w[6], w[7]);
-}
 
 // ------------------------------------------------------------------ formats
 // Each policy loads one step (4 pages) into registers and provides:
@@ -191,7 +84,7 @@ template <int D> struct Fp4Pol {
   struct Step {
     uint4 kc[4];          // K codes, MFMA m: token slot 4m + (lane%16)%4, group lane/16
     uint32_t ks;          // K scale bytes of those 4 tokens (byte m)
-    uint4 vc[kCPL];       // V codes of channel pair kCPL*(lane%16) + q, slots 0..15
+    uint4 vc[kCPL];       // V codes of channel pair kCPL*(lane%16) + q (row 16q + lane%16), slots 0..15
     uint4 vs;             // V scale bytes of that group, slots 0..15
   };
   struct QOp { v8i b; };
@@ -210,7 +103,7 @@ template <int D> struct Fp4Pol {
       st.ks = 0x7F7F7F7Fu;
     }
 #pragma unroll
-    for (int q = 0; q < kCPL; ++q) st.vc[q] = load16(vb + (kCPL * r16 + q) * kPage);
+    for (int q = 0; q < kCPL; ++q) st.vc[q] = load16(vb + (16 * q + r16) * kPage);   // pair kCPL*r16 + q
     st.vs = load16(vb + kCode + kPage * ((kCPL * r16) / 16));
   }
   template <int M> __device__ static v4f qk1(const Step& st, const QOp& qo) {
@@ -407,61 +300,187 @@ template <int D> struct Bf16Pol {
   __device__ static int channel(int tile, int j4, int v) { return 16 * tile + 4 * j4 + v; }
 };
 
+// ------------------------------------------------------------------ plan
+// Every workgroup derives the split plan from seq_lens in LDS: pages per split
+// pps (a multiple of 4, sized so that the (sequence, split) pairs number about
+// target_bs) and base[b] = first pair of sequence b, base[B] = number of pairs.
+// A sequence of length 0 still gets one (empty) pair so that its output row is
+// written.
+__device__ void wg_plan(const int32_t* __restrict__ seq_lens, int B, int target_bs, int32_t* base, int32_t* red,
+                        int32_t& pps_out) {
+  const int tid = threadIdx.x;
+  int32_t tot = 0;
+  for (int b = tid; b < B; b += 256) tot += (seq_lens[b] + kPage - 1) / kPage;
+  red[tid] = tot;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) red[tid] += red[tid + st];
+    __syncthreads();
+  }
+  int pps = (red[0] + target_bs - 1) / target_bs;
+  pps = pps < 4 ? 4 : (pps + 3) & ~3;
+  __syncthreads();
+  int32_t carry = 0;
+  for (int b0 = 0; b0 < B; b0 += 256) {
+    const int b = b0 + tid;
+    const int pages = b < B ? (seq_lens[b] + kPage - 1) / kPage : 0;
+    const int ns = b < B ? max(1, (pages + pps - 1) / pps) : 0;
+    red[tid] = ns;
+    __syncthreads();
+    for (int st = 1; st < 256; st <<= 1) {      // inclusive Hillis-Steele scan
+      const int v = tid >= st ? red[tid - st] : 0;
+      __syncthreads();
+      red[tid] += v;
+      __syncthreads();
+    }
+    if (b < B) base[b] = carry + red[tid] - ns;
+    carry += red[255];
+    __syncthreads();
+  }
+  if (tid == 0) base[B] = carry;
+  __syncthreads();
+  pps_out = pps;
+}
+
+// Query rows of one workgroup into LDS: E4M3 bytes of the (FP4: rotated) rows
+// row0 .. row0 + n - 1 of q, zero rows up to 16; BF16 keeps the bf16 values.
+// Run by one wave; D/32 lanes per row as in the write path.
+template <int D, int IN, int FMT>
+__device__ void query_rows(const void* q, int64_t row0, int n, uint8_t* qs, int lane) {
+  if constexpr (FMT == UQ_KV_BF16) {
+    // 16 rows x D bf16; 16 bytes per lane per pass
+    constexpr int kChunks = 16 * D * 2 / 16;
+    for (int c = lane; c < kChunks; c += 64) {
+      const int r = c / (D / 8), k = c - r * (D / 8);
+      const uint4 v = r < n ? load16(static_cast<const uint16_t*>(q) + (row0 + r) * D + 8 * k) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(qs + 16 * c) = v;
+    }
+  } else {
+    constexpr int LPR = D / 32;
+    const int rr = lane / LPR, p = lane % LPR;
+    if (rr >= 16) return;                          // whole quads drop out together
+    double x[32];
+    if (rr < n) {
+      load_row32<IN>(q, (row0 + rr) * D + 32 * p, x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) x[e] = 0.0;
+    }
+    if constexpr (FMT == UQ_KV_FP4) wht_row<D>(x, lane);
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i] = e4m3_from_f64(x[4 * i]) | e4m3_from_f64(x[4 * i + 1]) << 8 | e4m3_from_f64(x[4 * i + 2]) << 16 |
+             e4m3_from_f64(x[4 * i + 3]) << 24;
+    uint4* o = reinterpret_cast<uint4*>(qs + rr * D + 32 * p);
+    o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+// Normalizes one merged output row held as channels lane + 64k and, for FP4,
+// rotates it back with the normalized WHT (stage h = 64 inside the lane, the
+// others across lanes), then stores it.
+template <int D, bool UNROT>
+__device__ void store_row(float (&o)[D / 64], float l, float* dst, int lane) {
+  constexpr int PER = D / 64;
+  const float inv = l > 0.f ? 1.f / l : 0.f;      // l == 0 only for empty sequences
+#pragma unroll
+  for (int k = 0; k < PER; ++k) o[k] *= inv;
+  if constexpr (UNROT) {
+    if constexpr (PER == 2) {
+      const float x0 = o[0], x1 = o[1];
+      o[0] = x0 + x1;
+      o[1] = x0 - x1;
+    }
+#pragma unroll
+    for (int hh = 32; hh >= 1; hh >>= 1)
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const float other = __shfl_xor(o[k], hh);
+        o[k] = (lane & hh) ? other - o[k] : o[k] + other;
+      }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] *= wht_cf<D>();
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) dst[lane + 64 * k] = o[k];
+}
+
 // ------------------------------------------------------------------ decode
 struct KArgs {
   const uint8_t* k_pool;
   const uint8_t* v_pool;
   int64_t page_bytes;
-  const int32_t* page_table;
   int32_t max_pages;
-  const int32_t* seq_lens;
-  const uint8_t* q;          // E4M3 query (FP4/FP8) or the caller's bf16 query
-  int64_t q_row_bytes;
-  int32_t Hq, Hkv, G, n_hg;
+  const void* q;             // caller's query [B][Hq][D], bf16 or f32
+  int32_t B, Hq, Hkv, G;
+  int32_t target_bs;
   float scale_log2;          // sm_scale * log2(e)
-  const PlanHdr* hdr;
-  const int2* items;
-  float2* ml;                // [bs][Hq] (m in log2 units, l)
+  float* out;                // [B][Hq][D]
+  float2* ml;                // [bs][Hq] (m in log2 units, l) of multi-split sequences
   float* po;                 // [bs][Hq][D]
+  int32_t* cnt;              // [B][Hkv] arrival counters, zero between calls
 };
 
-template <class Pol, int D>
+// LDS carve-up of one workgroup (bytes): query rows, four per-wave partial
+// results (m, l, O for 16 heads), the plan scratch and base[B + 1].
+template <int D, int FMT> struct Smem {
+  static constexpr int kQ = 16 * D * (FMT == UQ_KV_BF16 ? 2 : 1);
+  static constexpr int kO = kQ;                                // [4][16][D] float
+  static constexpr int kM = kO + 4 * 16 * D * 4;               // [4][16] float
+  static constexpr int kL = kM + 4 * 16 * 4;                   // [4][16] float
+  static constexpr int kFlag = kL + 4 * 16 * 4;
+  static constexpr int kRed = kFlag + 16;                      // [256] int
+  static constexpr int kBase = kRed + 256 * 4;                 // [B + 1] int
+  static size_t bytes(int B) { return (size_t)kBase + 4 * (size_t)(B + 1); }
+};
+
+// One workgroup per item (sequence b, KV head hk, split s of pps pages); its
+// four waves take consecutive quarters of the split's 4-page steps and merge in
+// LDS.  A sequence with one split writes its output directly; otherwise each
+// split writes a partial and the last one to arrive (device-scope counter)
+// merges them.
+template <class Pol, int D, int IN, int FMT, bool UNROT>
 __global__ __launch_bounds__(256, Pol::kOcc) void decode_kernel(const KArgs a, const int32_t* __restrict__ page_table,
-                                                        const int2* __restrict__ items,
-                                                        const int32_t* __restrict__ seq_lens) {
+                                                                const int32_t* __restrict__ seq_lens) {
+  using SM = Smem<D, FMT>;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* qs = smem;
+  float* mo = reinterpret_cast<float*>(smem + SM::kO);
+  float* mm = reinterpret_cast<float*>(smem + SM::kM);
+  float* mlw = reinterpret_cast<float*>(smem + SM::kL);
+  int32_t* flag = reinterpret_cast<int32_t*>(smem + SM::kFlag);
+  int32_t* red = reinterpret_cast<int32_t*>(smem + SM::kRed);
+  int32_t* base = reinterpret_cast<int32_t*>(smem + SM::kBase);
+
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15, j4 = lane >> 4;
-  const int n_items = a.hdr->n_bs * a.n_hg;
-  const int pps = a.hdr->pps;
+  int pps;
+  wg_plan(seq_lens, a.B, a.target_bs, base, red, pps);
+  const int n_items = base[a.B] * a.Hkv;
+
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int bs = item / a.n_hg;
-    const int hk = (item - bs * a.n_hg) * kWavesPerWG + wave;
-    if (hk >= a.Hkv) continue;
-    const int2 it2 = items[bs];
-    const int b = it2.x;
+    const int bs = item / a.Hkv;
+    const int hk = item - bs * a.Hkv;
+    int lo = 0, hi = a.B;                        // b: last index with base[b] <= bs
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (base[mid] <= bs) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int n_split = base[b + 1] - base[b];
     const int L = seq_lens[b];
     const int pages = (L + kPage - 1) / kPage;
-    const int p_begin = it2.y * pps;
+    const int p_begin = (bs - base[b]) * pps;
     const int p_end = min(p_begin + pps, pages);
-    const int n_step = (p_end - p_begin + 3) >> 2;
+    const int n_step = p_end > p_begin ? (p_end - p_begin + 3) >> 2 : 0;
+    const int s_lo = wave * n_step / 4, s_hi = (wave + 1) * n_step / 4;   // this wave's steps
     const int32_t* pt = page_table + (int64_t)b * a.max_pages;
     const int hq0 = hk * a.G;
-
-    typename Pol::QOp qo;
-    Pol::load_q(qo, a.q + (int64_t)(b * a.Hq + hq0 + r16) * a.q_row_bytes, r16 < a.G, j4);
-
-    float m_run = -INFINITY, l_run = 0.f;
-    const float m_slack = 8.0f / a.scale_log2;     // 2^8 headroom in raw logit units
-    v4f O[Pol::kTiles];
-#pragma unroll
-    for (int t = 0; t < Pol::kTiles; ++t) O[t] = v4f{0, 0, 0, 0};
-
     const int64_t head_off = (int64_t)hk * Pol::kBlk;
-    // The four page ids of a step are wave-uniform: scalar loads fetch them one
-    // step ahead of the data loads that use them.  A vector load here would sit
-    // at the back of the in-order vector-memory counter, and waiting for it
-    // would also wait for every prefetch issued before it.
+
     struct Ids { int v[4]; };
     auto fetch_ids = [&](int s) {
       Ids r;
@@ -478,15 +497,33 @@ __global__ __launch_bounds__(256, Pol::kOcc) void decode_kernel(const KArgs a, c
       Pol::load(st, a.k_pool + (int64_t)idk * a.page_bytes + head_off, a.v_pool + (int64_t)idv * a.page_bytes + head_off,
                 r16, j4);
     };
-    // One step: QK, online softmax, PV.  MASKED handles a partial last step
-    // (pages past the split, slots past the sequence); every other step is full.
+
+    constexpr int P = Pol::kStages;
+    typename Pol::Step st[P];
+    const int last = s_hi - 1;
+    if (s_hi > s_lo) {
+#pragma unroll
+      for (int i = 0; i < P - 1; ++i) load_step(st[i], fetch_ids(min(s_lo + i, last)));
+    }
+    if (wave == 0) query_rows<D, IN, FMT>(a.q, (int64_t)b * a.Hq + hq0, a.G, qs, lane);
+    __syncthreads();
+    typename Pol::QOp qo;
+    Pol::load_q(qo, qs + r16 * D * (FMT == UQ_KV_BF16 ? 2 : 1), r16 < a.G, j4);
+
+    float m_run = -INFINITY, l_run = 0.f;
+    const float m_slack = 8.0f / a.scale_log2;     // 2^8 headroom in raw logit units
+    v4f O[Pol::kTiles];
+#pragma unroll
+    for (int t = 0; t < Pol::kTiles; ++t) O[t] = v4f{0, 0, 0, 0};
+
+    // One step: QK, online softmax, PV.  MASKED handles the split's partial last
+    // step (pages past the split, slots past the sequence).
     auto compute_step = [&](const typename Pol::Step& st, int s, auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value;
       const int pg = p_begin + 4 * s;
       v4f S[4];
       Pol::qk(st, qo, S);
-      // tokens of page pg + j4 held by this lane: slots 4m + v
-      int nvalid = kPage;
+      int nvalid = kPage;                          // valid slots of page pg + j4
       float t[16];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
@@ -503,8 +540,8 @@ __global__ __launch_bounds__(256, Pol::kOcc) void decode_kernel(const KArgs a, c
       for (int i = 4; i < 16; i += 2) mx = fmaxf(mx, fmaxf(t[i], t[i + 1]));
       // Conditional rescaling: exponents are taken against the running reference
       // m_run as long as no logit exceeds it by more than 8 / scale_log2 (so
-      // p <= 2^8, well inside float16); only then is the reference raised,
-      // which needs the cross-lane maximum and a rescale of l and O.
+      // p <= 2^8, well inside float16); only then is the reference raised, which
+      // needs the cross-lane maximum and a rescale of l and O.
       if (__any(mx > m_run + m_slack)) {
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -524,21 +561,21 @@ __global__ __launch_bounds__(256, Pol::kOcc) void decode_kernel(const KArgs a, c
         psum += pf[i];
       }
       l_run += psum;
-      v8h P[2][2];
+      v8h Pm[2][2];
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const _Float16 hi = (_Float16)pf[8 * half + i];
-          P[half][0][i] = hi;
-          P[half][1][i] = (_Float16)__builtin_fmaf((float)hi, -1.0f, pf[8 * half + i]);   // exact p - hi
+          const _Float16 hi16 = (_Float16)pf[8 * half + i];
+          Pm[half][0][i] = hi16;
+          Pm[half][1][i] = (_Float16)__builtin_fmaf((float)hi16, -1.0f, pf[8 * half + i]);   // exact p - hi
         }
       if constexpr (!MASKED) {
-        Pol::pv(st, P, O, [](int, int, uint32_t x) { return x; });
+        Pol::pv(st, Pm, O, [](int, int, uint32_t x) { return x; });
       } else {
         // zero V of slots past the valid ones so garbage in unwritten slots cannot
         // turn 0 * inf into NaN; dword i of half h holds slots 8h + 2i, 8h + 2i + 1
-        Pol::pv(st, P, O, [nvalid](int half, int i, uint32_t x) {
+        Pol::pv(st, Pm, O, [nvalid](int half, int i, uint32_t x) {
           const int s0 = 8 * half + 2 * i;
           const uint32_t keep = (s0 < nvalid ? 0xFFFFu : 0u) | (s0 + 1 < nvalid ? 0xFFFF0000u : 0u);
           return x & keep;
@@ -546,213 +583,196 @@ __global__ __launch_bounds__(256, Pol::kOcc) void decode_kernel(const KArgs a, c
       }
     };
 
-    // Software pipeline: kStages register buffers, kStages - 1 steps of loads in
-    // flight while one step computes (latency x bandwidth needs ~100 KB in
-    // flight per CU).  Buffer indices are compile-time after unrolling.
-    // Prefetches are issued unconditionally, clamped to the last step (those
-    // addresses were just loaded, so the repeats hit in L2), which keeps the
-    // number of outstanding loads the same on every path and lets each step
-    // wait only for its own data.
-    constexpr int P = Pol::kStages;
-    typename Pol::Step st[P];
-    const int last = n_step - 1;
-    // the last step is full when its 4 pages exist and hold 64 valid tokens
-    const bool last_full = (p_begin + 4 * n_step <= p_end) && ((p_begin + 4 * n_step) * kPage <= L);
+    if (s_hi > s_lo) {
+      // Software pipeline over this wave's steps: P register buffers, P - 1 steps
+      // of loads in flight.  Prefetches are issued unconditionally (clamped to the
+      // wave's last step, whose addresses then hit in L2) so the number of
+      // outstanding loads is the same on every path and each step waits only
+      // for its own data.  Page ids are wave-uniform: scalar loads fetch them one
+      // step ahead, outside the in-order vector-memory counter.
+      const bool last_full = (p_begin + 4 * n_step <= p_end) && ((p_begin + 4 * n_step) * kPage <= L);
+      const int split_last = n_step - 1;
+      Ids next = fetch_ids(min(s_lo + P - 1, last));
+      for (int s0 = s_lo;; s0 += P) {
 #pragma unroll
-    for (int i = 0; i < P - 1; ++i) load_step(st[i], fetch_ids(min(i, last)));
-    Ids next = fetch_ids(min(P - 1, last));
-    for (int s0 = 0;; s0 += P) {
-#pragma unroll
-      for (int i = 0; i < P; ++i) {
-        const int cur = s0 + i;
-        if (cur > last) goto steps_done;
-        load_step(st[(i + P - 1) % P], next);
-        next = fetch_ids(min(cur + P, last));
-        if (cur < last || last_full) compute_step(st[i], cur, std::false_type{});
-        else compute_step(st[i], cur, std::true_type{});
+        for (int i = 0; i < P; ++i) {
+          const int cur = s0 + i;
+          if (cur > last) goto steps_done;
+          load_step(st[(i + P - 1) % P], next);
+          next = fetch_ids(min(cur + P, last));
+          if (cur < split_last || last_full) compute_step(st[i], cur, std::false_type{});
+          else compute_step(st[i], cur, std::true_type{});
+        }
       }
+    steps_done:;
     }
-  steps_done:
 
+    // per-wave result -> LDS: m (log2 units), l (summed over the 4 lane groups), O
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
     if (r16 < a.G) {
-      const int64_t prow = (int64_t)bs * a.Hq + hq0 + r16;
-      float* o = a.po + prow * D;
+      float* o = mo + (wave * 16 + r16) * D;
 #pragma unroll
       for (int tt = 0; tt < Pol::kTiles; ++tt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) o[Pol::channel(tt, j4, v)] = O[tt][v];
-      if (j4 == 0) a.ml[prow] = make_float2(m_run * a.scale_log2, l_tot);
+      if (j4 == 0) {
+        mm[wave * 16 + r16] = m_run * a.scale_log2;
+        mlw[wave * 16 + r16] = l_tot;
+      }
     }
-  }
-}
+    __syncthreads();
 
-// ------------------------------------------------------------------ reduce
-template <int D, bool UNROT>
-__global__ __launch_bounds__(256) void reduce_kernel(const PlanHdr* hdr, const int32_t* base, const float2* ml,
-                                                     const float* po, float* out, int rows, int Hq) {
-  constexpr int PER = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int b = row / Hq, h = row - b * Hq;
-  const int s0 = base[b], ns = base[b + 1] - s0;
-  float o[PER];
+    // merge the 4 waves; wave w handles heads w, w + 4, ...
+    constexpr int PER = D / 64;
+    for (int h = wave; h < a.G; h += 4) {
+      float m = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  if (ns > 0) {
-    // split headers: lane s holds (m, l) of split s (64 splits per pass)
-    float mmax = -INFINITY;
-    for (int c = 0; c < ns; c += 64) {
-      const float m = c + lane < ns ? ml[(int64_t)(s0 + c + lane) * Hq + h].x : -INFINITY;
-      mmax = fmaxf(mmax, m);
-    }
+      for (int w = 0; w < 4; ++w) m = fmaxf(m, mm[w * 16 + h]);
+      float o[PER], l = 0.f;
 #pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, x));
-    float l = 0.f;
-    for (int c = 0; c < ns; c += 64) {
-      const int n = min(64, ns - c);
-      float w = 0.f, lw = 0.f;
-      if (lane < n) {
-        const float2 v = ml[(int64_t)(s0 + c + lane) * Hq + h];
-        w = __builtin_amdgcn_exp2f(v.x - mmax);
-        lw = w * v.y;
-      }
+      for (int k = 0; k < PER; ++k) o[k] = 0.f;
+      if (m > -INFINITY) {
 #pragma unroll
-      for (int x = 32; x >= 1; x >>= 1) lw += __shfl_xor(lw, x);
-      l += lw;
-      const float* src = po + ((int64_t)(s0 + c) * Hq + h) * D + lane;
-      const int64_t stride = (int64_t)Hq * D;
-      int s = 0;
-      for (; s + 4 <= n; s += 4) {               // four independent split rows in flight
-        float v[4][PER];
+        for (int w = 0; w < 4; ++w) {
+          const float wt = __builtin_amdgcn_exp2f(mm[w * 16 + h] - m);
+          l += wt * mlw[w * 16 + h];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int k = 0; k < PER; ++k) v[u][k] = src[(s + u) * stride + 64 * k];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float wu = __shfl(w, s + u);
-#pragma unroll
-          for (int k = 0; k < PER; ++k) o[k] += wu * v[u][k];
+          for (int k = 0; k < PER; ++k) o[k] += wt * mo[(w * 16 + h) * D + lane + 64 * k];
         }
       }
-      for (; s < n; ++s) {
-        const float ws = __shfl(w, s);
+      const int64_t row = (int64_t)b * a.Hq + hq0 + h;
+      if (n_split == 1) {
+        store_row<D, UNROT>(o, l, a.out + row * D, lane);
+      } else {
+        const int64_t prow = (int64_t)bs * a.Hq + hq0 + h;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) o[k] += ws * src[s * stride + 64 * k];
+        for (int k = 0; k < PER; ++k) a.po[prow * D + lane + 64 * k] = o[k];
+        if (lane == 0) a.ml[prow] = make_float2(m, l);
       }
     }
-    const float inv = 1.f / l;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] *= inv;
-    if constexpr (UNROT) {
-      if constexpr (PER == 2) {           // stage h = 64 is inside the lane
-        const float x0 = o[0], x1 = o[1];
-        o[0] = x0 + x1;
-        o[1] = x0 - x1;
+
+    if (n_split > 1) {
+      // publish the partial; the last split to arrive merges all of them
+      __threadfence();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        int32_t* c = a.cnt + (int64_t)b * a.Hkv + hk;
+        const int old = __hip_atomic_fetch_add(c, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int is_last = old == n_split - 1;
+        if (is_last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = is_last;
       }
+      __syncthreads();
+      if (*flag) {
+        __threadfence();
+        const int bs0 = base[b];
+        for (int h = wave; h < a.G; h += 4) {
+          const int64_t col = hq0 + h;
+          float m = -INFINITY;
+          for (int c0 = 0; c0 < n_split; c0 += 64) {
+            const float mv = c0 + lane < n_split ? a.ml[(int64_t)(bs0 + c0 + lane) * a.Hq + col].x : -INFINITY;
+            m = fmaxf(m, mv);
+          }
 #pragma unroll
-      for (int hh = 32; hh >= 1; hh >>= 1) {
+          for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
+          float o[PER], l = 0.f;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          const float other = __shfl_xor(o[k], hh);
-          o[k] = (lane & hh) ? other - o[k] : o[k] + other;
+          for (int k = 0; k < PER; ++k) o[k] = 0.f;
+          for (int c0 = 0; c0 < n_split; c0 += 64) {
+            const int n = min(64, n_split - c0);
+            float wt = 0.f, lw = 0.f;
+            if (lane < n) {
+              const float2 v = a.ml[(int64_t)(bs0 + c0 + lane) * a.Hq + col];
+              wt = v.x > -INFINITY ? __builtin_amdgcn_exp2f(v.x - m) : 0.f;
+              lw = wt * v.y;
+            }
+#pragma unroll
+            for (int x = 32; x >= 1; x >>= 1) lw += __shfl_xor(lw, x);
+            l += lw;
+            for (int sidx = 0; sidx < n; ++sidx) {
+              const float ws = __shfl(wt, sidx);
+              const float* src = a.po + ((int64_t)(bs0 + c0 + sidx) * a.Hq + col) * D + lane;
+#pragma unroll
+              for (int k = 0; k < PER; ++k) o[k] += ws * src[64 * k];
+            }
+          }
+          store_row<D, UNROT>(o, l, a.out + ((int64_t)b * a.Hq + col) * D, lane);
         }
       }
-#pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] *= wht_cf<D>();
     }
+    __syncthreads();                               // LDS is reused by the next item
   }
-#pragma unroll
-  for (int k = 0; k < PER; ++k) out[(int64_t)row * D + lane + 64 * k] = o[k];
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+template <int D, int IN, int FMT, bool UNROT, class Pol>
+hipError_t launch_one(const DecodeArgs& a, const KArgs& k, hipStream_t s) {
+  const size_t lds = Smem<D, FMT>::bytes(a.B);
+  const int max_items = a.lay.max_bs * a.Hkv;
+  const int wgs = kCUs * Pol::kOcc;
+  const dim3 grid((unsigned)(max_items < wgs ? max_items : wgs)), blk(256);
+  hipLaunchKernelGGL((decode_kernel<Pol, D, IN, FMT, UNROT>), grid, blk, lds, s, k, a.page_table, a.seq_lens);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   const DecodeLayout& L = a.lay;
-  PlanHdr* hdr = reinterpret_cast<PlanHdr*>(a.ws + L.hdr);
-  int32_t* base = reinterpret_cast<int32_t*>(a.ws + L.base);
-  int2* items = reinterpret_cast<int2*>(a.ws + L.items);
-  uint8_t* qbuf = a.ws + L.qbuf;
-  float2* ml = reinterpret_cast<float2*>(a.ws + L.ml);
-  float* po = reinterpret_cast<float*>(a.ws + L.po);
-  const int rows = a.B * a.Hq;
-  const bool want_q = a.format != UQ_KV_BF16;
-  const bool rot = a.format == UQ_KV_FP4;
-  const unsigned qblocks = want_q ? (unsigned)(((rows + 64 / (D / 32) - 1) / (64 / (D / 32)) + 3) / 4) : 0;
-  const dim3 g1(qblocks + 1), blk(256);
-#define UQ_QP(II, RR) hipLaunchKernelGGL((query_plan_kernel<D, II, RR>), g1, blk, 0, s, a.q, want_q ? qbuf : nullptr, \
-                                         rows, a.seq_lens, a.B, L.target_bs, hdr, base, items)
-  if (a.q_dtype == UQ_IN_BF16) { if (rot) UQ_QP(UQ_IN_BF16, true); else UQ_QP(UQ_IN_BF16, false); }
-  else { if (rot) UQ_QP(UQ_IN_F32, true); else UQ_QP(UQ_IN_F32, false); }
-#undef UQ_QP
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
   KArgs k;
   k.k_pool = a.k_pool;
   k.v_pool = a.v_pool;
   k.page_bytes = a.page_bytes;
-  k.page_table = a.page_table;
   k.max_pages = a.max_pages;
-  k.seq_lens = a.seq_lens;
-  k.q = want_q ? qbuf : static_cast<const uint8_t*>(a.q);
-  k.q_row_bytes = want_q ? D : 2 * D;
+  k.q = a.q;
+  k.B = a.B;
   k.Hq = a.Hq;
   k.Hkv = a.Hkv;
   k.G = a.Hq / a.Hkv;
-  k.n_hg = (a.Hkv + kWavesPerWG - 1) / kWavesPerWG;
+  k.target_bs = L.target_bs;
   k.scale_log2 = a.sm_scale * 1.4426950408889634f;
-  k.hdr = hdr;
-  k.items = items;
-  k.ml = ml;
-  k.po = po;
-  const int max_items = L.max_bs * k.n_hg;
-  const int occ = a.format == UQ_KV_FP4 ? Fp4Pol<D>::kOcc : 1;
-  const int wgs = kCUs * occ;
-  const dim3 g2((unsigned)(max_items < wgs ? max_items : wgs));
-  if (a.ev_start != nullptr) {
-    e = hipEventRecord(a.ev_start, s);
-    if (e != hipSuccess) return e;
+  k.out = a.out;
+  k.ml = reinterpret_cast<float2*>(a.ws + L.ml);
+  k.po = reinterpret_cast<float*>(a.ws + L.po);
+  k.cnt = reinterpret_cast<int32_t*>(a.ws + L.cnt);
+  hipError_t e;
+  if (a.ev_start != nullptr && (e = hipEventRecord(a.ev_start, s)) != hipSuccess) return e;
+  const bool bf = a.q_dtype == UQ_IN_BF16;
+  if (a.format == UQ_KV_FP4) {
+    if (a.unrotate) e = bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP4, true, Fp4Pol<D>>(a, k, s)
+                           : launch_one<D, UQ_IN_F32, UQ_KV_FP4, true, Fp4Pol<D>>(a, k, s);
+    else e = bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP4, false, Fp4Pol<D>>(a, k, s)
+                : launch_one<D, UQ_IN_F32, UQ_KV_FP4, false, Fp4Pol<D>>(a, k, s);
+  } else if (a.format == UQ_KV_FP8) {
+    e = bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP8, false, Fp8Pol<D>>(a, k, s)
+           : launch_one<D, UQ_IN_F32, UQ_KV_FP8, false, Fp8Pol<D>>(a, k, s);
+  } else {
+    e = launch_one<D, UQ_IN_BF16, UQ_KV_BF16, false, Bf16Pol<D>>(a, k, s);
   }
-  if (a.format == UQ_KV_FP4)
-    hipLaunchKernelGGL((decode_kernel<Fp4Pol<D>, D>), g2, blk, 0, s, k, a.page_table, items, a.seq_lens);
-  else if (a.format == UQ_KV_FP8)
-    hipLaunchKernelGGL((decode_kernel<Fp8Pol<D>, D>), g2, blk, 0, s, k, a.page_table, items, a.seq_lens);
-  else hipLaunchKernelGGL((decode_kernel<Bf16Pol<D>, D>), g2, blk, 0, s, k, a.page_table, items, a.seq_lens);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.ev_stop != nullptr) {
-    e = hipEventRecord(a.ev_stop, s);
-    if (e != hipSuccess) return e;
-  }
-
-  const dim3 g3((unsigned)((rows + 3) / 4));
-  if (a.unrotate) hipLaunchKernelGGL((reduce_kernel<D, true>), g3, blk, 0, s, hdr, base, ml, po, a.out, rows, a.Hq);
-  else hipLaunchKernelGGL((reduce_kernel<D, false>), g3, blk, 0, s, hdr, base, ml, po, a.out, rows, a.Hq);
-  return hipGetLastError();
+  if (a.ev_stop != nullptr && (e = hipEventRecord(a.ev_stop, s)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 }  // namespace
 
 DecodeLayout decode_layout(int format, int B, int Hq, int Hkv, int D) {
+  (void)format;
   DecodeLayout L;
-  const int n_hg = (Hkv + kWavesPerWG - 1) / kWavesPerWG;
-  L.target_bs = (kTargetItems + n_hg - 1) / n_hg;
+  L.target_bs = (kTargetItems + Hkv - 1) / Hkv;
   L.max_bs = L.target_bs + B;
   size_t off = 0;
-  L.hdr = off; off = align256(off + sizeof(PlanHdr));
-  L.base = off; off = align256(off + sizeof(int32_t) * (size_t)(B + 1));
-  L.items = off; off = align256(off + sizeof(int2) * (size_t)L.max_bs);
-  L.qbuf = off; off = align256(off + (format == UQ_KV_BF16 ? 0 : (size_t)B * Hq * D));
+  L.cnt = off; off = align256(off + sizeof(int32_t) * (size_t)B * Hkv);
   L.ml = off; off = align256(off + sizeof(float2) * (size_t)L.max_bs * Hq);
   L.po = off; off = align256(off + sizeof(float) * (size_t)L.max_bs * Hq * D);
   L.total = off;
   return L;
+}
+
+size_t decode_lds_bytes(int format, int B, int D) {
+  if (format == UQ_KV_BF16) return D == 128 ? Smem<128, UQ_KV_BF16>::bytes(B) : Smem<64, UQ_KV_BF16>::bytes(B);
+  return D == 128 ? Smem<128, UQ_KV_FP4>::bytes(B) : Smem<64, UQ_KV_FP4>::bytes(B);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/uq.h"
+
 namespace uq {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -137,5 +139,30 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// 32 consecutive input values (bf16 bits or f32) starting at element `elem`, as float64.
+template <int IN> __device__ __forceinline__ void load_row32(const void* base, int64_t elem, double (&x)[32]) {
+  if constexpr (IN == UQ_IN_BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint4 u = p[w];
+      const uint32_t d[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[8 * w + 2 * i] = bf16_bits_to_f64(d[i] & 0xFFFFu);
+        x[8 * w + 2 * i + 1] = bf16_bits_to_f64(d[i] >> 16);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const float4 f = p[w];
+      x[4 * w] = f.x; x[4 * w + 1] = f.y; x[4 * w + 2] = f.z; x[4 * w + 3] = f.w;
+    }
+  }
+}
+
 
 }  // namespace uq

@@ -26,15 +26,16 @@ hipError_t launch_append_bf16(const AppendArgs& a, int head_dim, int in_dtype, h
 hipError_t launch_query(const void* q, int in_dtype, uint8_t* q_fp8, int rows, int head_dim,
                         bool rotate, hipStream_t s);
 
-// Decode work split: one item is (sequence, split of pps pages, group of up to
-// kWavesPerWG KV heads); one wave runs one KV head of an item.
-constexpr int kWavesPerWG = 4;
 
 struct DecodeLayout {
-  size_t hdr, base, items, qbuf, ml, po, total;
-  int32_t target_bs;   // target number of (sequence, split) pairs
-  int32_t max_bs;      // bound on (sequence, split) pairs: target_bs + num_seqs
+  size_t cnt, ml, po, total;   // byte offsets into the workspace
+  int32_t target_bs;           // target number of (sequence, split) pairs
+  int32_t max_bs;              // bound on (sequence, split) pairs: target_bs + num_seqs
 };
+
+// LDS bytes one decode workgroup needs for num_seqs sequences.
+size_t decode_lds_bytes(int format, int num_seqs, int head_dim);
+constexpr int kMaxDecodeSeqs = 8192;   // per-workgroup plan lives in LDS
 
 DecodeLayout decode_layout(int format, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim);
 

@@ -43,8 +43,9 @@
  * Head-block layouts (d = head_dim, 16 slots):
  *   FP4  K: codes [16 slot][d/2 B] (byte j: channel 2j low nibble, 2j+1 high),
  *           then scales [slot % 4][d/32 group][slot / 4]       = 17*d/2 bytes
- *   FP4  V: codes [d/2 channel pair][16 slot] (byte: channel 2c low nibble,
- *           2c+1 high nibble), then scales [d/32 group][16 slot] = 17*d/2 bytes
+ *   FP4  V: codes [d/2 row][16 slot] (byte: channel 2c low nibble, 2c+1 high
+ *           nibble of channel pair c, stored in row 16*(c % (d/32)) + c/(d/32)),
+ *           then scales [d/32 group][16 slot]                  = 17*d/2 bytes
  *   FP8  K: [16 slot][d] E4M3 bytes;   FP8  V: [d][16 slot] E4M3 bytes
  *   BF16 K: [16 slot][d] bf16;         BF16 V: [d][16 slot] bf16
  * K is slot-major because the QK product contracts over channels; V is
@@ -153,9 +154,12 @@ size_t uq_decode_workspace_bytes(const uq_kv_cache* cache, int32_t num_seqs, int
  *   seq_lens    device int32 [num_seqs], each in [0, 16 * max_pages_per_seq]
  *   out         device float [num_seqs][num_q_heads][head_dim]; must not alias
  *               any input; a sequence of length 0 gives a zero row
- *   workspace   device, >= uq_decode_workspace_bytes(...) bytes, 256-B aligned
- * num_q_heads must be a multiple of num_kv_heads with a ratio of 1..16, and
- * sm_scale must be positive and finite.
+ *   workspace   device, >= uq_decode_workspace_bytes(...) bytes, 256-B aligned,
+ *               zero-filled before its first use; every call leaves it ready for
+ *               the next one (no clearing needed).  Calls that overlap in time
+ *               must not share a workspace.
+ * num_q_heads must be a multiple of num_kv_heads with a ratio of 1..16,
+ * num_seqs at most 4096, and sm_scale positive and finite.
  * Accuracy: codes and scales enter exactly; logits and the softmax are float32,
  * probabilities and dequantized values enter the PV product as float16, so V
  * groups must have E <= 13 (|v| <= 49152) to stay finite in float16.

@@ -245,7 +245,8 @@ def bf16_round_bits(x32) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Paged cache layout (reading R8).  Pools are uint8 [num_pages][H_kv][block].
 #   FP4 K block: codes[16 tok][d/2] (token-major) then scales[tok % 4][d/32][tok // 4]
-#   FP4 V block: codes[d/2 channel pairs][16 tok] then scales[d/32 groups][16 tok]
+#   FP4 V block: codes[d/2 rows][16 tok] (channel pair c in row 16*(c % (d/32)) + c // (d/32))
+#                then scales[d/32 groups][16 tok]
 #   FP8 K block: [16 tok][d] bytes;  FP8 V block: [d][16 tok] bytes
 #   BF16 K block: [16 tok][d] bf16;  BF16 V block: [d][16 tok] bf16 (little endian)
 # --------------------------------------------------------------------------
@@ -277,7 +278,10 @@ def fp4_k_scale_offset(tok, group, d):
 
 
 def fp4_v_code_offset(tok, pair, d):
-    return pair * PAGE_SIZE + tok
+    # 16-byte rows (one per channel pair, byte = slot); channel pair c sits in
+    # row 16 * (c % (d/32)) + c // (d/32)
+    cpl = d // GROUP
+    return ((pair % cpl) * 16 + pair // cpl) * PAGE_SIZE + tok
 
 
 def fp4_v_scale_offset(tok, group, d):

@@ -91,7 +91,7 @@ def gpu_decode(fmt, wl, cache, flags=0, seq_lens=None, q=None):
     pt = dev(np.ascontiguousarray(wl.page_table, dtype=np.int32))
     sl = dev(np.ascontiguousarray(wl.seq_lens if seq_lens is None else seq_lens, dtype=np.int32))
     out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(m.uq_decode_workspace_bytes(cache, B, Hq, wl.page_table.shape[1]), dtype=torch.uint8,
+    ws = torch.zeros(m.uq_decode_workspace_bytes(cache, B, Hq, wl.page_table.shape[1]), dtype=torch.uint8,
                      device="cuda")
     decode_fn(fmt)(cache, ql, pt, sl, 1.0 / np.sqrt(d), out, ws, flags=flags)
     torch.cuda.synchronize()
