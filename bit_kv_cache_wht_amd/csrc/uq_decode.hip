@@ -26,6 +26,7 @@
 // first) and an FP8 operand k = 16(l/16)..+15 and 64+16(l/16)..+15; lane i+16b
 // supplies the scale of row i, k-block b.  For 16x16x32 f16, lane l holds
 // k = 8(l/16)..+7; results land in lane l as column l%16, rows 4(l/16)..+3.
+#include <atomic>
 #include <type_traits>
 
 #include "uq_device.h"
@@ -36,8 +37,8 @@ namespace uq {
 
 namespace {
 
-constexpr int kTargetItems = 512;    // decode items per launch the plan aims for (one per workgroup)
-constexpr int kCUs = 256;            // MI355X compute units; one 4-wave workgroup per SIMD wave slot
+constexpr int kTargetItems = 512;    // decode items per launch the plan aims for
+constexpr int kMaxR = 8;             // items per round of a workgroup, at most
 
 // ------------------------------------------------------------------ formats
 // Each policy loads one step (4 pages) into registers and provides:
@@ -51,12 +52,31 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
+// Keep-masks for the slots of one page that are valid (slot < nvalid): bytes
+// (slot t = byte t of 16) and 16-bit halves (slot t = half t of 16).
+__device__ __forceinline__ uint32_t slot_bytes_kept(int nvalid, int first) {
+  const int n = nvalid - first;                   // valid slots among first .. first + 3
+  return n >= 4 ? 0xFFFFFFFFu : n <= 0 ? 0u : (1u << (8 * n)) - 1u;
+}
+__device__ __forceinline__ uint32_t slot_halves_kept(int nvalid, int first) {
+  const int n = nvalid - first;                   // valid slots among first, first + 1
+  return n >= 2 ? 0xFFFFFFFFu : n <= 0 ? 0u : 0xFFFFu;
+}
+
 // PV product with P = hi + lo split into two float16 parts: float16 alone keeps
 // 11 bits of each probability, which against value channels of magnitude ~50
 // leaves errors near 1e-2; the split carries ~22 bits.
 __device__ __forceinline__ v4f mma2(const v8h& a, const v8h (&p)[2], v4f c) {
   c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, p[0], c, 0, 0, 0);
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, p[1], c, 0, 0, 0);
+}
+
+// p0, p1 ~= hi + lo as packed float16 pairs: hi = f16(p), lo = f16(p - hi), the
+// difference taken in float32 by v_fma_mix straight from the packed hi halves.
+__device__ __forceinline__ void split_f16x2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, v2h{(_Float16)p0, (_Float16)p1});
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(hi), "v"(p0));
+  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(lo) : "v"(hi), "v"(p1));
 }
 
 // E4M3 query as the FP8 B operand: lane (h, j) holds k = 16j..16j+15 and
@@ -75,15 +95,17 @@ template <int D> __device__ __forceinline__ v8i load_q_fp8(const uint8_t* qrow, 
 // r*CPL/16), so one scale per token serves all of its conversions.
 template <int D> struct Fp4Pol {
   static constexpr int kOcc = 2;        // waves per SIMD (256 registers each)
-  static constexpr int kStages = 2;
+  static constexpr int kBuf = 2;        // K and V register buffers (steps of prefetch)
   static constexpr int kBlk = Fp4Block<D>::kBytes;
   static constexpr int kCode = Fp4Block<D>::kCodeBytes;
   static constexpr int kGroups = D / 32;
   static constexpr int kCPL = D / 32;             // channel pairs per lane
   static constexpr int kTiles = D / 16;
-  struct Step {
+  struct KStep {
     uint4 kc[4];          // K codes, MFMA m: token slot 4m + (lane%16)%4, group lane/16
     uint32_t ks;          // K scale bytes of those 4 tokens (byte m)
+  };
+  struct VStep {
     uint4 vc[kCPL];       // V codes of channel pair kCPL*(lane%16) + q (row 16q + lane%16), slots 0..15
     uint4 vs;             // V scale bytes of that group, slots 0..15
   };
@@ -91,7 +113,7 @@ template <int D> struct Fp4Pol {
   __device__ static void load_q(QOp& qo, const uint8_t* qrow, bool valid, int j4) {
     qo.b = load_q_fp8<D>(qrow, valid, j4);
   }
-  __device__ static void load(Step& st, const uint8_t* kb, const uint8_t* vb, int r16, int j4) {
+  __device__ static void load_k(KStep& st, const uint8_t* kb, int r16, int j4) {
     if (j4 < kGroups) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) st.kc[m] = load16(kb + (4 * m + (r16 & 3)) * (D / 2) + 16 * j4);
@@ -102,27 +124,48 @@ template <int D> struct Fp4Pol {
       for (int m = 0; m < 4; ++m) st.kc[m] = make_uint4(0, 0, 0, 0);
       st.ks = 0x7F7F7F7Fu;
     }
+  }
+  __device__ static void load_v(VStep& st, const uint8_t* vb, int r16, int j4) {
 #pragma unroll
     for (int q = 0; q < kCPL; ++q) st.vc[q] = load16(vb + (16 * q + r16) * kPage);   // pair kCPL*r16 + q
     st.vs = load16(vb + kCode + kPage * ((kCPL * r16) / 16));
   }
-  template <int M> __device__ static v4f qk1(const Step& st, const QOp& qo) {
+  template <int M> __device__ static v4f qk1(const KStep& st, const QOp& qo) {
     const v8i a = v8i{(int)st.kc[M].x, (int)st.kc[M].y, (int)st.kc[M].z, (int)st.kc[M].w, 0, 0, 0, 0};
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qo.b, v4f{0, 0, 0, 0}, 4 /*A fp4*/, 0 /*B fp8*/,
                                                            M /*byte M of ks*/, (int)st.ks, 0, 127);
   }
-  __device__ static void qk(const Step& st, const QOp& qo, v4f (&S)[4]) {
+  __device__ static void qk(const KStep& st, const QOp& qo, v4f (&S)[4]) {
     S[0] = qk1<0>(st, qo);
     S[1] = qk1<1>(st, qo);
     S[2] = qk1<2>(st, qo);
     S[3] = qk1<3>(st, qo);
   }
-  template <class MaskFn>
-  __device__ static void pv(const Step& st, const v8h (&P)[2][2], v4f (&O)[kTiles], MaskFn mask) {
+  // Clears the value codes of slots past nvalid and gives them scale byte 127
+  // (2^0), so that whatever an unwritten slot holds converts to zero.
+  __device__ static void mask_v(VStep& st, int nvalid) {
+    const uint32_t k0 = slot_bytes_kept(nvalid, 0), k1 = slot_bytes_kept(nvalid, 4),
+                   k2 = slot_bytes_kept(nvalid, 8), k3 = slot_bytes_kept(nvalid, 12);
+#pragma unroll
+    for (int q = 0; q < kCPL; ++q) {
+      st.vc[q].x &= k0; st.vc[q].y &= k1; st.vc[q].z &= k2; st.vc[q].w &= k3;
+    }
+    st.vs.x = (st.vs.x & k0) | (~k0 & 0x7F7F7F7Fu);
+    st.vs.y = (st.vs.y & k1) | (~k1 & 0x7F7F7F7Fu);
+    st.vs.z = (st.vs.z & k2) | (~k2 & 0x7F7F7F7Fu);
+    st.vs.w = (st.vs.w & k3) | (~k3 & 0x7F7F7F7Fu);
+  }
+  __device__ static void pv(const VStep& st, const v8h (&P)[2][2], v4f (&O)[kTiles]) {
     const uint32_t s[4] = {st.vs.x, st.vs.y, st.vs.z, st.vs.w};
+    // The conversion reads only the exponent field of its float scale, so byte k
+    // of a scale word only has to be shifted into bits 23..30; the bits around it
+    // land in the sign and mantissa and are ignored.
     float sc[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) sc[t] = __uint_as_float(((s[t >> 2] >> (8 * (t & 3))) & 0xFFu) << 23);
+    for (int t = 0; t < 16; ++t) {
+      const int k = t & 3;
+      sc[t] = __uint_as_float(k == 3 ? s[t >> 2] >> 1 : s[t >> 2] << (23 - 8 * k));
+    }
 #pragma unroll
     for (int q = 0; q < kCPL; ++q) {
       const uint32_t c[4] = {st.vc[q].x, st.vc[q].y, st.vc[q].z, st.vc[q].w};
@@ -144,8 +187,8 @@ template <int D> struct Fp4Pol {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t x0 = X[8 * half + 2 * i], x1 = X[8 * half + 2 * i + 1];
-          ev[i] = mask(half, i, __builtin_amdgcn_perm(x1, x0, 0x05040100u));   // low halves: even channel
-          od[i] = mask(half, i, __builtin_amdgcn_perm(x1, x0, 0x07060302u));   // high halves: odd channel
+          ev[i] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);   // low halves: even channel
+          od[i] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);   // high halves: odd channel
         }
         const v8h ae = __builtin_bit_cast(v8h, make_uint4(ev[0], ev[1], ev[2], ev[3]));
         const v8h ao = __builtin_bit_cast(v8h, make_uint4(od[0], od[1], od[2], od[3]));
@@ -164,14 +207,12 @@ template <int D> struct Fp4Pol {
 // with unrotated outlier channels moves logits by ~1e-4 relative.
 template <int D> struct Fp8Pol {
   static constexpr int kOcc = 1;
-  static constexpr int kStages = 3;
+  static constexpr int kBuf = 3;
   static constexpr int kBlk = kPage * D;
   static constexpr int kTiles = D / 16;
   static constexpr int kLanesK = D / 32;   // lane groups holding 32 channels of a row
-  struct Step {
-    uint4 k[4][2];          // K bytes 32j..32j+31 of token slot 4m + (lane%16)%4
-    uint4 vc[kTiles];       // V bytes of channel 16t + lane%16, slots 0..15
-  };
+  struct KStep { uint4 k[4][2]; };     // K bytes 32j..32j+31 of token slot 4m + (lane%16)%4
+  struct VStep { uint4 vc[kTiles]; };  // V bytes of channel 16t + lane%16, slots 0..15
   // q as f16 B operands: MFMA kk pairs k-block j with channels 32j + 8kk..+7
   struct QOp { v8h b[4]; };
   __device__ static v8h cvt8(uint32_t w0, uint32_t w1) {
@@ -192,7 +233,7 @@ template <int D> struct Fp8Pol {
     qo.b[2] = cvt8(hi.x, hi.y);
     qo.b[3] = cvt8(hi.z, hi.w);
   }
-  __device__ static void load(Step& st, const uint8_t* kb, const uint8_t* vb, int r16, int j4) {
+  __device__ static void load_k(KStep& st, const uint8_t* kb, int r16, int j4) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int slot = 4 * m + (r16 & 3);
@@ -203,10 +244,12 @@ template <int D> struct Fp8Pol {
         st.k[m][0] = st.k[m][1] = make_uint4(0, 0, 0, 0);
       }
     }
+  }
+  __device__ static void load_v(VStep& st, const uint8_t* vb, int r16, int j4) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) st.vc[t] = load16(vb + (16 * t + r16) * kPage);
   }
-  __device__ static void qk(const Step& st, const QOp& qo, v4f (&S)[4]) {
+  __device__ static void qk(const KStep& st, const QOp& qo, v4f (&S)[4]) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       v4f acc = {0, 0, 0, 0};
@@ -217,8 +260,16 @@ template <int D> struct Fp8Pol {
       S[m] = acc;
     }
   }
-  template <class MaskFn>
-  __device__ static void pv(const Step& st, const v8h (&P)[2][2], v4f (&O)[kTiles], MaskFn mask) {
+  // Clears the value bytes of slots past nvalid.
+  __device__ static void mask_v(VStep& st, int nvalid) {
+    const uint32_t k0 = slot_bytes_kept(nvalid, 0), k1 = slot_bytes_kept(nvalid, 4),
+                   k2 = slot_bytes_kept(nvalid, 8), k3 = slot_bytes_kept(nvalid, 12);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      st.vc[t].x &= k0; st.vc[t].y &= k1; st.vc[t].z &= k2; st.vc[t].w &= k3;
+    }
+  }
+  __device__ static void pv(const VStep& st, const v8h (&P)[2][2], v4f (&O)[kTiles]) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       const uint32_t c[4] = {st.vc[t].x, st.vc[t].y, st.vc[t].z, st.vc[t].w};
@@ -230,7 +281,7 @@ template <int D> struct Fp8Pol {
           const uint32_t word = c[2 * half + (i >> 1)];
           const v2h h = (i & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true)
                                 : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false);
-          a[i] = mask(half, i, __builtin_bit_cast(uint32_t, h));
+          a[i] = __builtin_bit_cast(uint32_t, h);
         }
         O[t] = mma2(__builtin_bit_cast(v8h, make_uint4(a[0], a[1], a[2], a[3])), P[half], O[t]);
       }
@@ -241,14 +292,12 @@ template <int D> struct Fp8Pol {
 
 template <int D> struct Bf16Pol {
   static constexpr int kOcc = 1;
-  static constexpr int kStages = 2;
+  static constexpr int kBuf = 2;
   static constexpr int kBlk = kPage * D * 2;
   static constexpr int kTiles = D / 16;
   static constexpr int kK = D / 32;     // 16x16x32 MFMAs per token row
-  struct Step {
-    uint4 k[4][kK];        // K bf16 channels 32kk + 8j..+7 of token slot 4m + (lane%16)%4
-    uint4 v[kTiles][2];    // V bf16 of channel 16t + lane%16, slots 0..7 and 8..15
-  };
+  struct KStep { uint4 k[4][kK]; };      // K bf16 channels 32kk + 8j..+7 of token slot 4m + (lane%16)%4
+  struct VStep { uint4 v[kTiles][2]; };  // V bf16 of channel 16t + lane%16, slots 0..7 and 8..15
   struct QOp { v8bf b[kK]; };
   __device__ static void load_q(QOp& qo, const uint8_t* qrow, bool valid, int j4) {
 #pragma unroll
@@ -257,20 +306,22 @@ template <int D> struct Bf16Pol {
       qo.b[kk] = __builtin_bit_cast(v8bf, u);
     }
   }
-  __device__ static void load(Step& st, const uint8_t* kb, const uint8_t* vb, int r16, int j4) {
+  __device__ static void load_k(KStep& st, const uint8_t* kb, int r16, int j4) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int slot = 4 * m + (r16 & 3);
 #pragma unroll
       for (int kk = 0; kk < kK; ++kk) st.k[m][kk] = load16(kb + 2 * (slot * D + 32 * kk + 8 * j4));
     }
+  }
+  __device__ static void load_v(VStep& st, const uint8_t* vb, int r16, int j4) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       st.v[t][0] = load16(vb + 2 * ((16 * t + r16) * kPage));
       st.v[t][1] = load16(vb + 2 * ((16 * t + r16) * kPage + 8));
     }
   }
-  __device__ static void qk(const Step& st, const QOp& qo, v4f (&S)[4]) {
+  __device__ static void qk(const KStep& st, const QOp& qo, v4f (&S)[4]) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       v4f acc = {0, 0, 0, 0};
@@ -280,8 +331,20 @@ template <int D> struct Bf16Pol {
       S[m] = acc;
     }
   }
-  template <class MaskFn>
-  __device__ static void pv(const Step& st, const v8h (&P)[2][2], v4f (&O)[kTiles], MaskFn mask) {
+  // Clears the values of slots past nvalid.
+  __device__ static void mask_v(VStep& st, int nvalid) {
+    uint32_t k[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) k[i] = slot_halves_kept(nvalid, 2 * i);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        st.v[t][half].x &= k[4 * half]; st.v[t][half].y &= k[4 * half + 1];
+        st.v[t][half].z &= k[4 * half + 2]; st.v[t][half].w &= k[4 * half + 3];
+      }
+  }
+  __device__ static void pv(const VStep& st, const v8h (&P)[2][2], v4f (&O)[kTiles]) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
 #pragma unroll
@@ -291,7 +354,7 @@ template <int D> struct Bf16Pol {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float lo = __uint_as_float(c[i] << 16), hi = __uint_as_float(c[i] & 0xFFFF0000u);
-          a[i] = mask(half, i, pack_h2((_Float16)lo, (_Float16)hi));
+          a[i] = pack_h2((_Float16)lo, (_Float16)hi);
         }
         O[t] = mma2(__builtin_bit_cast(v8h, make_uint4(a[0], a[1], a[2], a[3])), P[half], O[t]);
       }
@@ -306,77 +369,134 @@ template <int D> struct Bf16Pol {
 // target_bs) and base[b] = first pair of sequence b, base[B] = number of pairs.
 // A sequence of length 0 still gets one (empty) pair so that its output row is
 // written.
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// Run by all 64 * NW threads; red: 2 * NW ints of scratch.
+template <int NW>
 __device__ void wg_plan(const int32_t* __restrict__ seq_lens, int B, int target_bs, int32_t* base, int32_t* red,
                         int32_t& pps_out) {
-  const int tid = threadIdx.x;
+  constexpr int NT = 64 * NW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t tot = 0;
-  for (int b = tid; b < B; b += 256) tot += (seq_lens[b] + kPage - 1) / kPage;
-  red[tid] = tot;
+  for (int b = tid; b < B; b += NT) tot += (seq_lens[b] + kPage - 1) / kPage;
+  tot = wave_sum(tot);
+  if (lane == 0) red[wave] = tot;
   __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) red[tid] += red[tid + st];
-    __syncthreads();
-  }
-  int pps = (red[0] + target_bs - 1) / target_bs;
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) total += red[w];
+  int pps = (total + target_bs - 1) / target_bs;
   pps = pps < 4 ? 4 : (pps + 3) & ~3;
-  __syncthreads();
   int32_t carry = 0;
-  for (int b0 = 0; b0 < B; b0 += 256) {
+  for (int b0 = 0; b0 < B; b0 += NT) {
     const int b = b0 + tid;
     const int pages = b < B ? (seq_lens[b] + kPage - 1) / kPage : 0;
     const int ns = b < B ? max(1, (pages + pps - 1) / pps) : 0;
-    red[tid] = ns;
+    const int incl = wave_incl_scan(ns, lane);
+    if (lane == 63) red[NW + wave] = incl;
     __syncthreads();
-    for (int st = 1; st < 256; st <<= 1) {      // inclusive Hillis-Steele scan
-      const int v = tid >= st ? red[tid - st] : 0;
-      __syncthreads();
-      red[tid] += v;
-      __syncthreads();
+    int woff = 0, chunk = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      woff += w < wave ? red[NW + w] : 0;
+      chunk += red[NW + w];
     }
-    if (b < B) base[b] = carry + red[tid] - ns;
-    carry += red[255];
-    __syncthreads();
+    if (b < B) base[b] = carry + woff + incl - ns;
+    carry += chunk;
+    __syncthreads();                               // red[NW..] is rewritten by the next chunk
   }
   if (tid == 0) base[B] = carry;
   __syncthreads();
   pps_out = pps;
 }
 
-// Query rows of one workgroup into LDS: E4M3 bytes of the (FP4: rotated) rows
-// row0 .. row0 + n - 1 of q, zero rows up to 16; BF16 keeps the bf16 values.
-// Run by one wave; D/32 lanes per row as in the write path.
-template <int D, int IN, int FMT>
-__device__ void query_rows(const void* q, int64_t row0, int n, uint8_t* qs, int lane) {
-  if constexpr (FMT == UQ_KV_BF16) {
-    // 16 rows x D bf16; 16 bytes per lane per pass
-    constexpr int kChunks = 16 * D * 2 / 16;
-    for (int c = lane; c < kChunks; c += 64) {
-      const int r = c / (D / 8), k = c - r * (D / 8);
-      const uint4 v = r < n ? load16(static_cast<const uint16_t*>(q) + (row0 + r) * D + 8 * k) : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(qs + 16 * c) = v;
+// Query rows into LDS: E4M3 bytes of the (FP4: rotated) rows; BF16 keeps the
+// bf16 values.  Each row is handled by 16 consecutive threads, part p holding
+// channels E*p .. E*p + E - 1 (E = D/16).  load() only issues the global loads,
+// so that they go out ahead of the first key/value loads (the vector-memory
+// counter retires in order); finish() rotates, rounds and stores.  The
+// normalized WHT is the Sylvester butterfly: stages h < E inside the thread,
+// stages h >= E between parts p and p ^ (h/E), taken in float64 where every sum
+// of bf16/f32 inputs is exact, so the E4M3 rounding sees the exact rotated value.
+template <int D, int IN, int FMT> struct QueryRows {
+  static constexpr int E = D / 16;
+  static constexpr int kBytes = E * (IN == UQ_IN_BF16 ? 2 : 4);   // 8, 16 or 32
+  uint4 w[2];
+
+  // Channels E*p .. E*p + E - 1 of query row qrow (zeros when !valid).
+  __device__ void load(const void* q, int64_t qrow, bool valid, int p) {
+    w[0] = w[1] = make_uint4(0, 0, 0, 0);
+    if (valid) {
+      const uint8_t* src = static_cast<const uint8_t*>(q) + (qrow * D + E * p) * (IN == UQ_IN_BF16 ? 2 : 4);
+      if constexpr (kBytes == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        w[0] = make_uint4(v.x, v.y, 0, 0);
+      } else {
+        w[0] = load16(src);
+        if constexpr (kBytes == 32) w[1] = load16(src + 16);
+      }
     }
-  } else {
-    constexpr int LPR = D / 32;
-    const int rr = lane / LPR, p = lane % LPR;
-    if (rr >= 16) return;                          // whole quads drop out together
-    double x[32];
-    if (rr < n) {
-      load_row32<IN>(q, (row0 + rr) * D + 32 * p, x);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 32; ++e) x[e] = 0.0;
-    }
-    if constexpr (FMT == UQ_KV_FP4) wht_row<D>(x, lane);
-    uint32_t w[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      w[i] = e4m3_from_f64(x[4 * i]) | e4m3_from_f64(x[4 * i + 1]) << 8 | e4m3_from_f64(x[4 * i + 2]) << 16 |
-             e4m3_from_f64(x[4 * i + 3]) << 24;
-    uint4* o = reinterpret_cast<uint4*>(qs + rr * D + 32 * p);
-    o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    o[1] = make_uint4(w[4], w[5], w[6], w[7]);
   }
-}
+
+  // Converts and stores the part into the LDS row dst (the 16 threads of a row
+  // must call it together).
+  __device__ void finish(uint8_t* dst_row, int p) const {
+    if constexpr (FMT == UQ_KV_BF16) {
+      uint8_t* dst = dst_row + 2 * E * p;
+      if constexpr (kBytes == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0].x, w[0].y);
+      else *reinterpret_cast<uint4*>(dst) = w[0];
+    } else {
+      const uint32_t u[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+      double x[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if constexpr (IN == UQ_IN_BF16) x[e] = bf16_bits_to_f64((u[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        else x[e] = (double)__uint_as_float(u[e]);
+      }
+      if constexpr (FMT == UQ_KV_FP4) {
+#pragma unroll
+        for (int h = 1; h < E; h <<= 1)
+#pragma unroll
+          for (int i = 0; i < E; i += 2 * h)
+#pragma unroll
+            for (int j = i; j < i + h; ++j) {
+              const double a0 = x[j], a1 = x[j + h];
+              x[j] = a0 + a1;
+              x[j + h] = a0 - a1;
+            }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {       // partner thread t ^ m holds the other half
+          const double sgn = (p & m) ? -1.0 : 1.0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) x[e] = __builtin_fma(x[e], sgn, __shfl_xor(x[e], m));
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] *= wht_c<D>();
+      }
+      uint32_t b[E / 4];
+#pragma unroll
+      for (int i = 0; i < E / 4; ++i)
+        b[i] = e4m3_from_f64(x[4 * i]) | e4m3_from_f64(x[4 * i + 1]) << 8 | e4m3_from_f64(x[4 * i + 2]) << 16 |
+               e4m3_from_f64(x[4 * i + 3]) << 24;
+      uint8_t* dst = dst_row + E * p;
+      if constexpr (E == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(b[0], b[1]);
+      else *reinterpret_cast<uint32_t*>(dst) = b[0];
+    }
+  }
+};
 
 // Normalizes one merged output row held as channels lane + 64k and, for FP4,
 // rotates it back with the normalized WHT (stage h = 64 inside the lane, the
@@ -418,131 +538,293 @@ struct KArgs {
   int32_t target_bs;
   float scale_log2;          // sm_scale * log2(e)
   float* out;                // [B][Hq][D]
-  float2* ml;                // [bs][Hq] (m in log2 units, l) of multi-split sequences
+  float* ml;                 // [bs][Hq][2] (m in log2 units, l) of multi-split sequences
   float* po;                 // [bs][Hq][D]
   int32_t* cnt;              // [B][Hkv] arrival counters, zero between calls
+  int32_t R;                 // items per round of a workgroup
 };
 
-// LDS carve-up of one workgroup (bytes): query rows, four per-wave partial
-// results (m, l, O for 16 heads), the plan scratch and base[B + 1].
-template <int D, int FMT> struct Smem {
-  static constexpr int kQ = 16 * D * (FMT == UQ_KV_BF16 ? 2 : 1);
-  static constexpr int kO = kQ;                                // [4][16][D] float
-  static constexpr int kM = kO + 4 * 16 * D * 4;               // [4][16] float
-  static constexpr int kL = kM + 4 * 16 * 4;                   // [4][16] float
-  static constexpr int kFlag = kL + 4 * 16 * 4;
-  static constexpr int kRed = kFlag + 16;                      // [256] int
-  static constexpr int kBase = kRed + 256 * 4;                 // [B + 1] int
-  static size_t bytes(int B) { return (size_t)kBase + 4 * (size_t)(B + 1); }
+// Split partials cross workgroups that may sit on different compute dies,
+// whose L2 caches are not coherent with each other.  Rather than ordinary
+// accesses bracketed by device-scope fences (each of which writes back and
+// invalidates the whole L2 of the die, stalling every wave on it), the partials
+// are written and read with relaxed device-scope atomic accesses, which write
+// through and re-fetch past the L2 by themselves.  The one ordering needed,
+// that all partial stores of a workgroup are complete before its arrival is
+// counted, comes from waiting on the vector-memory counter before the barrier.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// LDS carve-up (bytes) of one workgroup of NW waves working on rounds of up to R
+// items, each with G query heads:
+//   qs     [R][G][D]       query rows (E4M3 bytes; BF16: bf16)
+//   so     [R][NW][G][D]   per-wave partial O of each item (float)
+//   sm, sl [R][NW][G]      per-wave partial m (log2 units) and l (float)
+//   rec    [R][8]          item records (int)
+//   misc   [32]            step counter, per-item flags, plan scratch (int)
+//   base   [B + 1]         plan (int)
+struct Lds {
+  int qs, so, sm, sl, rec, misc, base, total;
+  __host__ __device__ static int up16(int x) { return (x + 15) & ~15; }
+  __host__ __device__ Lds(int R, int NW, int G, int D, int esz, int B) {
+    qs = 0;
+    so = up16(qs + R * G * D * esz);
+    sm = up16(so + R * NW * G * D * 4);
+    sl = up16(sm + R * NW * G * 4);
+    rec = up16(sl + R * NW * G * 4);
+    misc = up16(rec + R * 8 * 4);
+    base = up16(misc + 32 * 4);
+    total = up16(base + (B + 1) * 4);
+  }
 };
 
-// One workgroup per item (sequence b, KV head hk, split s of pps pages); its
-// four waves take consecutive quarters of the split's 4-page steps and merge in
-// LDS.  A sequence with one split writes its output directly; otherwise each
-// split writes a partial and the last one to arrive (device-scope counter)
-// merges them.
+// Item record fields.
+enum { kRecB = 0, kRecPBegin, kRecNpg, kRecHk, kRecLRel, kRecNStep, kRecBs, kRecNSplit };
+
+// One persistent workgroup per compute unit, NW = 4 * kOcc waves (so two waves
+// share a SIMD when kOcc = 2).  The workgroup takes its items in rounds of up to
+// R (item = sequence b, KV head hk, split of pps pages): the steps (4 pages) of
+// all items of a round form one list from which the waves claim steps one at a
+// time through an LDS counter.  Waves that share a SIMD therefore end within a
+// step of each other whatever the issue arbitration between them, and the
+// prefetch runs on across item boundaries.  A wave keeps one running softmax
+// state and parks it in its LDS slot for the item when its next step belongs to
+// another item; at the end of the round the slots of each item are merged.  A
+// sequence with one split writes its output directly; otherwise each split
+// writes a partial and the last one to arrive (device-scope counter) merges
+// them.
 template <class Pol, int D, int IN, int FMT, bool UNROT>
-__global__ __launch_bounds__(256, Pol::kOcc) void decode_kernel(const KArgs a, const int32_t* __restrict__ page_table,
-                                                                const int32_t* __restrict__ seq_lens) {
-  using SM = Smem<D, FMT>;
+__global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs a,
+                                                                   const int32_t* __restrict__ page_table,
+                                                                   const int32_t* __restrict__ seq_lens) {
+  constexpr int NW = 4 * Pol::kOcc;
+  constexpr int NT = 64 * NW;
+  constexpr int ESZ = FMT == UQ_KV_BF16 ? 2 : 1;
+  constexpr int N = Pol::kBuf;
+  constexpr int PER = D / 64;
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* qs = smem;
-  float* mo = reinterpret_cast<float*>(smem + SM::kO);
-  float* mm = reinterpret_cast<float*>(smem + SM::kM);
-  float* mlw = reinterpret_cast<float*>(smem + SM::kL);
-  int32_t* flag = reinterpret_cast<int32_t*>(smem + SM::kFlag);
-  int32_t* red = reinterpret_cast<int32_t*>(smem + SM::kRed);
-  int32_t* base = reinterpret_cast<int32_t*>(smem + SM::kBase);
+  const int G = a.G;
+  const Lds lay(a.R, NW, G, D, ESZ, a.B);
+  uint8_t* qs = smem + lay.qs;
+  float* so = reinterpret_cast<float*>(smem + lay.so);
+  float* smx = reinterpret_cast<float*>(smem + lay.sm);
+  float* slx = reinterpret_cast<float*>(smem + lay.sl);
+  int32_t* rec = reinterpret_cast<int32_t*>(smem + lay.rec);
+  int32_t* misc = reinterpret_cast<int32_t*>(smem + lay.misc);
+  int32_t* base = reinterpret_cast<int32_t*>(smem + lay.base);
+  int32_t* ctr = misc;            // step counter of the round
+  int32_t* flags = misc + 1;      // [kMaxR] last-split flags
+  int32_t* red = misc + 16;       // [2 * NW] plan scratch
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, j4 = lane >> 4;
   int pps;
-  wg_plan(seq_lens, a.B, a.target_bs, base, red, pps);
+  wg_plan<NW>(seq_lens, a.B, a.target_bs, base, red, pps);
   const int n_items = base[a.B] * a.Hkv;
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int bs = item / a.Hkv;
-    const int hk = item - bs * a.Hkv;
-    int lo = 0, hi = a.B;                        // b: last index with base[b] <= bs
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (base[mid] <= bs) lo = mid; else hi = mid;
-    }
-    const int b = lo;
-    const int n_split = base[b + 1] - base[b];
-    const int L = seq_lens[b];
-    const int pages = (L + kPage - 1) / kPage;
-    const int p_begin = (bs - base[b]) * pps;
-    const int p_end = min(p_begin + pps, pages);
-    const int n_step = p_end > p_begin ? (p_end - p_begin + 3) >> 2 : 0;
-    const int s_lo = wave * n_step / 4, s_hi = (wave + 1) * n_step / 4;   // this wave's steps
-    const int32_t* pt = page_table + (int64_t)b * a.max_pages;
-    const int hq0 = hk * a.G;
-    const int64_t head_off = (int64_t)hk * Pol::kBlk;
+  for (int r0 = blockIdx.x; r0 < n_items; r0 += gridDim.x * a.R) {
+    const int nR = min(a.R, (n_items - r0 + (int)gridDim.x - 1) / (int)gridDim.x);
 
-    struct Ids { int v[4]; };
-    auto fetch_ids = [&](int s) {
-      Ids r;
-      const int pg = p_begin + 4 * s;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) r.v[x] = pt[min(pg + x, p_end - 1)];
-      return r;
-    };
-    auto pick = [](const Ids& ids, int x) {
-      return x == 0 ? ids.v[0] : x == 1 ? ids.v[1] : x == 2 ? ids.v[2] : ids.v[3];
-    };
-    auto load_step = [&](typename Pol::Step& st, const Ids& ids) {
-      const int idk = pick(ids, r16 >> 2), idv = pick(ids, j4);
-      Pol::load(st, a.k_pool + (int64_t)idk * a.page_bytes + head_off, a.v_pool + (int64_t)idv * a.page_bytes + head_off,
-                r16, j4);
-    };
-
-    constexpr int P = Pol::kStages;
-    typename Pol::Step st[P];
-    const int last = s_hi - 1;
-    if (s_hi > s_lo) {
-#pragma unroll
-      for (int i = 0; i < P - 1; ++i) load_step(st[i], fetch_ids(min(s_lo + i, last)));
+    // ---- round set-up: item records, empty slots, step counter
+    if (tid < nR) {
+      const int item = r0 + tid * gridDim.x;
+      const int bs = item / a.Hkv;
+      const int hk = item - bs * a.Hkv;
+      int lo = 0, hi = a.B;                      // b: last index with base[b] <= bs
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (base[mid] <= bs) lo = mid; else hi = mid;
+      }
+      const int b = lo;
+      const int L = seq_lens[b];
+      const int pages = (L + kPage - 1) / kPage;
+      const int p_begin = (bs - base[b]) * pps;
+      const int npg = max(min(p_begin + pps, pages) - p_begin, 0);
+      int32_t* r = rec + 8 * tid;
+      r[kRecB] = b;
+      r[kRecPBegin] = p_begin;
+      r[kRecNpg] = npg;
+      r[kRecHk] = hk;
+      r[kRecLRel] = L - p_begin * kPage;
+      r[kRecNStep] = (npg + 3) >> 2;
+      r[kRecBs] = bs;
+      r[kRecNSplit] = base[b + 1] - base[b];
     }
-    if (wave == 0) query_rows<D, IN, FMT>(a.q, (int64_t)b * a.Hq + hq0, a.G, qs, lane);
+    for (int i = tid; i < nR * NW * G; i += NT) smx[i] = -INFINITY;
+    if (tid == 0) *ctr = 0;
     __syncthreads();
-    typename Pol::QOp qo;
-    Pol::load_q(qo, qs + r16 * D * (FMT == UQ_KV_BF16 ? 2 : 1), r16 < a.G, j4);
 
-    float m_run = -INFINITY, l_run = 0.f;
-    const float m_slack = 8.0f / a.scale_log2;     // 2^8 headroom in raw logit units
-    v4f O[Pol::kTiles];
+    // first step of each item of the round (ps[k] = T for k >= nR)
+    int ps[kMaxR + 1];
+    {
+      int acc = 0;
 #pragma unroll
-    for (int t = 0; t < Pol::kTiles; ++t) O[t] = v4f{0, 0, 0, 0};
+      for (int k = 0; k < kMaxR; ++k) {
+        ps[k] = acc;
+        if (k < nR) acc += __builtin_amdgcn_readfirstlane(rec[8 * k + kRecNStep]);
+      }
+      ps[kMaxR] = acc;
+    }
+    const int T = ps[kMaxR];
 
-    // One step: QK, online softmax, PV.  MASKED handles the split's partial last
-    // step (pages past the split, slots past the sequence).
-    auto compute_step = [&](const typename Pol::Step& st, int s, auto masked_tag) {
-      constexpr bool MASKED = decltype(masked_tag)::value;
-      const int pg = p_begin + 4 * s;
-      v4f S[4];
-      Pol::qk(st, qo, S);
-      int nvalid = kPage;                          // valid slots of page pg + j4
+    // query rows of the round, row r = k * G + h; the first pass's loads go out
+    // ahead of the key/value prologue
+    const int nrows = nR * G;
+    auto qrow_of = [&](int r) -> int64_t {
+      const int k = r / G, h = r - k * G;
+      return (int64_t)rec[8 * k + kRecB] * a.Hq + (int64_t)rec[8 * k + kRecHk] * G + h;
+    };
+    const int qr0 = tid >> 4, qp = tid & 15;
+    QueryRows<D, IN, FMT> qrows;
+    qrows.load(a.q, qr0 < nrows ? qrow_of(qr0) : 0, qr0 < nrows, qp);
+
+    // ---- step claims
+    struct Claim {
+      int meta;          // < 0: no step; else full << 28 | item << 20 | step
+      int hk;
+      int ids[4];        // page ids of the step's 4 pages (page 0 of the pool when none)
+    };
+    auto claim = [&]() {
+      Claim c;
+      int g = 0;
+      if (lane == 0) g = atomicAdd(ctr, 1);
+      g = __builtin_amdgcn_readlane(g, 0);
+      if (g >= T) {
+        c.meta = -1;
+        c.hk = 0;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) c.ids[x] = 0;
+        return c;
+      }
+      int k = 0, pk = 0;
+#pragma unroll
+      for (int j = 1; j < kMaxR; ++j) k += g >= ps[j] ? 1 : 0;
+#pragma unroll
+      for (int j = 0; j < kMaxR; ++j) pk = j == k ? ps[j] : pk;
+      const int s = g - pk;
+      const int32_t* r = rec + 8 * k;
+      const int b = __builtin_amdgcn_readfirstlane(r[kRecB]);
+      const int p_begin = __builtin_amdgcn_readfirstlane(r[kRecPBegin]);
+      const int npg = __builtin_amdgcn_readfirstlane(r[kRecNpg]);
+      const int lrel = __builtin_amdgcn_readfirstlane(r[kRecLRel]);
+      c.hk = __builtin_amdgcn_readfirstlane(r[kRecHk]);
+      // wave-uniform page-table reads: scalar loads, outside the in-order
+      // vector-memory counter of the key/value loads
+      const int32_t* pt = page_table + (int64_t)b * a.max_pages + p_begin;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) c.ids[x] = pt[min(4 * s + x, npg - 1)];
+      const bool full = (4 * s + 4 <= npg) && ((4 * s + 4) * kPage <= lrel);
+      c.meta = (full ? 1 << 28 : 0) | (k << 20) | s;
+      return c;
+    };
+    auto pick = [](const Claim& c, int x) {
+      return x == 0 ? c.ids[0] : x == 1 ? c.ids[1] : x == 2 ? c.ids[2] : c.ids[3];
+    };
+    auto load_k = [&](typename Pol::KStep& st, const Claim& c) {
+      Pol::load_k(st, a.k_pool + (int64_t)pick(c, r16 >> 2) * a.page_bytes + (int64_t)c.hk * Pol::kBlk, r16, j4);
+    };
+    auto load_v = [&](typename Pol::VStep& st, const Claim& c) {
+      Pol::load_v(st, a.v_pool + (int64_t)pick(c, j4) * a.page_bytes + (int64_t)c.hk * Pol::kBlk, r16, j4);
+    };
+
+    // ---- prologue: N K and N - 1 V buffers.  K is consumed by the QK at the
+    // start of a step, so its buffer is refilled for step s + N right after; V is
+    // used at the end of a step and its buffer is refilled for step s + N - 1 at
+    // the start of the next.  Loads of claims past the end read page 0 of the
+    // pool (always present) so that every path issues the same loads.
+    typename Pol::KStep kst[N];
+    typename Pol::VStep vst[N];
+    int meta[N + 1];               // meta[j]: step j after the current one
+    Claim cv, ck;                  // next V load (step + N - 1) and next K load (step + N)
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const Claim c = claim();
+      meta[i] = c.meta;
+      load_k(kst[i], c);
+      if (i < N - 1) load_v(vst[i], c);
+      if (i == N - 1) cv = c;
+    }
+    ck = claim();
+    meta[N] = ck.meta;
+
+    if (qr0 < nrows) qrows.finish(qs + qr0 * D * ESZ, qp);
+    for (int r = qr0 + NT / 16; r < nrows; r += NT / 16) {
+      QueryRows<D, IN, FMT> more;
+      more.load(a.q, qrow_of(r), true, qp);
+      more.finish(qs + r * D * ESZ, qp);
+    }
+    __syncthreads();
+
+    // ---- running state of the item the wave is on
+    typename Pol::QOp qo;
+    float m_run = -INFINITY, l_run = 0.f;
+    v4f O[Pol::kTiles];
+    int acc_k = -1;
+
+    auto park = [&]() {            // running state -> LDS slot (acc_k, wave)
+      float l_tot = l_run + __shfl_xor(l_run, 16);
+      l_tot += __shfl_xor(l_tot, 32);
+      if (r16 < G) {
+        const int slot = (acc_k * NW + wave) * G + r16;
+        float* o = so + slot * D;
+#pragma unroll
+        for (int tt = 0; tt < Pol::kTiles; ++tt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[Pol::channel(tt, j4, v)] = O[tt][v];
+        if (j4 == 0) {
+          smx[slot] = m_run * a.scale_log2;
+          slx[slot] = l_tot;
+        }
+      }
+    };
+    auto begin_item = [&](int k) {
+      m_run = -INFINITY;
+      l_run = 0.f;
+#pragma unroll
+      for (int t = 0; t < Pol::kTiles; ++t) O[t] = v4f{0, 0, 0, 0};
+      Pol::load_q(qo, qs + (k * G + r16) * D * ESZ, r16 < G, j4);
+      acc_k = k;
+    };
+
+    // Softmax and PV of step s of the current item given its logits S.  Slots
+    // past the item (pages past its split, tokens past the sequence) get logit
+    // -inf and value zero; the masking is applied on every step (all slots valid
+    // on full ones), which costs a few ALU operations but keeps a single copy of
+    // the step code and its register allocation.
+    auto finish_step = [&](v4f (&S)[4], typename Pol::VStep& st, int s, bool full) {
+      int nvalid = kPage;                          // valid slots of page 4s + j4 of the item
+      if (!full) {
+        const int npg = rec[8 * acc_k + kRecNpg], lrel = rec[8 * acc_k + kRecLRel];
+        const int pj = 4 * s + j4;
+        nvalid = pj < npg ? min(kPage, lrel - pj * kPage) : 0;
+      }
       float t[16];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) t[4 * m + v] = S[m][v];
-      if constexpr (MASKED) {
-        const int tok0 = (pg + j4) * kPage;
-        nvalid = (pg + j4 < p_end) ? min(kPage, L - tok0) : 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) t[i] = i < nvalid ? t[i] : -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
-#pragma unroll
-      for (int i = 4; i < 16; i += 2) mx = fmaxf(mx, fmaxf(t[i], t[i + 1]));
+        for (int v = 0; v < 4; ++v) t[4 * m + v] = 4 * m + v < nvalid ? S[m][v] : -INFINITY;
       // Conditional rescaling: exponents are taken against the running reference
-      // m_run as long as no logit exceeds it by more than 8 / scale_log2 (so
-      // p <= 2^8, well inside float16); only then is the reference raised, which
-      // needs the cross-lane maximum and a rescale of l and O.
-      if (__any(mx > m_run + m_slack)) {
+      // m_run as long as every lane's 16 probabilities sum to at most 2^8 (so each
+      // p <= 2^8, well inside float16).  Otherwise (a logit above the reference by
+      // more than 8 binades, the first step, or a NaN from -inf - -inf) the
+      // reference is raised to the row maximum across the 4 lanes of the row, l
+      // and O are rescaled and the probabilities recomputed.
+      float neg_mc = -m_run * a.scale_log2;
+      float pf[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
+      float psum = pf[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) psum += pf[i];
+      if (__any(!(psum <= 256.f))) {
+        float mx = t[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, t[i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
@@ -551,169 +833,194 @@ __global__ __launch_bounds__(256, Pol::kOcc) void decode_kernel(const KArgs a, c
 #pragma unroll
         for (int tt = 0; tt < Pol::kTiles; ++tt) O[tt] *= alpha;
         m_run = m_new;
-      }
-      const float neg_mc = -m_run * a.scale_log2;
-      float psum = 0.f;
-      float pf[16];
+        neg_mc = -m_run * a.scale_log2;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
-        psum += pf[i];
+        for (int i = 0; i < 16; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
+        psum = pf[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) psum += pf[i];
       }
       l_run += psum;
       v8h Pm[2][2];
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
+      for (int half = 0; half < 2; ++half) {
+        uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const _Float16 hi16 = (_Float16)pf[8 * half + i];
-          Pm[half][0][i] = hi16;
-          Pm[half][1][i] = (_Float16)__builtin_fmaf((float)hi16, -1.0f, pf[8 * half + i]);   // exact p - hi
-        }
-      if constexpr (!MASKED) {
-        Pol::pv(st, Pm, O, [](int, int, uint32_t x) { return x; });
-      } else {
-        // zero V of slots past the valid ones so garbage in unwritten slots cannot
-        // turn 0 * inf into NaN; dword i of half h holds slots 8h + 2i, 8h + 2i + 1
-        Pol::pv(st, Pm, O, [nvalid](int half, int i, uint32_t x) {
-          const int s0 = 8 * half + 2 * i;
-          const uint32_t keep = (s0 < nvalid ? 0xFFFFu : 0u) | (s0 + 1 < nvalid ? 0xFFFF0000u : 0u);
-          return x & keep;
-        });
+        for (int i = 0; i < 4; ++i) split_f16x2(pf[8 * half + 2 * i], pf[8 * half + 2 * i + 1], hw[i], lw[i]);
+        Pm[half][0] = __builtin_bit_cast(v8h, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        Pm[half][1] = __builtin_bit_cast(v8h, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
+      Pol::mask_v(st, nvalid);
+      Pol::pv(st, Pm, O);
     };
 
-    if (s_hi > s_lo) {
-      // Software pipeline over this wave's steps: P register buffers, P - 1 steps
-      // of loads in flight.  Prefetches are issued unconditionally (clamped to the
-      // wave's last step, whose addresses then hit in L2) so the number of
-      // outstanding loads is the same on every path and each step waits only
-      // for its own data.  Page ids are wave-uniform: scalar loads fetch them one
-      // step ahead, outside the in-order vector-memory counter.
-      const bool last_full = (p_begin + 4 * n_step <= p_end) && ((p_begin + 4 * n_step) * kPage <= L);
-      const int split_last = n_step - 1;
-      Ids next = fetch_ids(min(s_lo + P - 1, last));
-      for (int s0 = s_lo;; s0 += P) {
+    for (;;) {
 #pragma unroll
-        for (int i = 0; i < P; ++i) {
-          const int cur = s0 + i;
-          if (cur > last) goto steps_done;
-          load_step(st[(i + P - 1) % P], next);
-          next = fetch_ids(min(cur + P, last));
-          if (cur < split_last || last_full) compute_step(st[i], cur, std::false_type{});
-          else compute_step(st[i], cur, std::true_type{});
+      for (int i = 0; i < N; ++i) {
+        const int mc = meta[0];
+        if (mc < 0) goto steps_done;
+        const int kc = (mc >> 20) & 0xFF, sc = mc & 0xFFFFF;
+        if (kc != acc_k) {
+          if (acc_k >= 0) park();
+          begin_item(kc);
         }
-      }
-    steps_done:;
-    }
-
-    // per-wave result -> LDS: m (log2 units), l (summed over the 4 lane groups), O
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    if (r16 < a.G) {
-      float* o = mo + (wave * 16 + r16) * D;
+        load_v(vst[(i + N - 1) % N], cv);        // V of step + N - 1
+        v4f S[4];
+        Pol::qk(kst[i], qo, S);
+        load_k(kst[i], ck);                      // K of step + N
+        cv = ck;
 #pragma unroll
-      for (int tt = 0; tt < Pol::kTiles; ++tt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) o[Pol::channel(tt, j4, v)] = O[tt][v];
-      if (j4 == 0) {
-        mm[wave * 16 + r16] = m_run * a.scale_log2;
-        mlw[wave * 16 + r16] = l_tot;
+        for (int j = 0; j < N; ++j) meta[j] = meta[j + 1];
+        ck = claim();
+        meta[N] = ck.meta;
+        finish_step(S, vst[i], sc, (mc >> 28) & 1);
       }
     }
+  steps_done:
+    if (acc_k >= 0) park();
     __syncthreads();
 
-    // merge the 4 waves; wave w handles heads w, w + 4, ...
-    constexpr int PER = D / 64;
-    for (int h = wave; h < a.G; h += 4) {
+    // ---- merge the wave slots of each item; wave w takes rows w, w + NW, ...
+    for (int row = wave; row < nrows; row += NW) {
+      const int k = row / G, h = row - k * G;
+      const int slot0 = k * NW * G + h;          // slot of wave w: slot0 + w * G
       float m = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) m = fmaxf(m, mm[w * 16 + h]);
+      for (int w = 0; w < NW; ++w) m = fmaxf(m, smx[slot0 + w * G]);
       float o[PER], l = 0.f;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) o[k] = 0.f;
+      for (int kk = 0; kk < PER; ++kk) o[kk] = 0.f;
       if (m > -INFINITY) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float wt = __builtin_amdgcn_exp2f(mm[w * 16 + h] - m);
-          l += wt * mlw[w * 16 + h];
+        for (int w = 0; w < NW; ++w) {
+          const float mw = smx[slot0 + w * G];
+          if (mw > -INFINITY) {                  // slots of waves that took no step are stale
+            const float wt = __builtin_amdgcn_exp2f(mw - m);
+            l += wt * slx[slot0 + w * G];
 #pragma unroll
-          for (int k = 0; k < PER; ++k) o[k] += wt * mo[(w * 16 + h) * D + lane + 64 * k];
+            for (int kk = 0; kk < PER; ++kk) o[kk] += wt * so[(slot0 + w * G) * D + lane + 64 * kk];
+          }
         }
       }
-      const int64_t row = (int64_t)b * a.Hq + hq0 + h;
-      if (n_split == 1) {
-        store_row<D, UNROT>(o, l, a.out + row * D, lane);
+      const int32_t* r = rec + 8 * k;
+      const int64_t col = (int64_t)r[kRecHk] * G + h;
+      if (r[kRecNSplit] == 1) {
+        store_row<D, UNROT>(o, l, a.out + ((int64_t)r[kRecB] * a.Hq + col) * D, lane);
       } else {
-        const int64_t prow = (int64_t)bs * a.Hq + hq0 + h;
+        const int64_t prow = (int64_t)r[kRecBs] * a.Hq + col;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) a.po[prow * D + lane + 64 * k] = o[k];
-        if (lane == 0) a.ml[prow] = make_float2(m, l);
+        for (int kk = 0; kk < PER; ++kk) st_dev(a.po + prow * D + lane + 64 * kk, o[kk]);
+        if (lane == 0) {
+          st_dev(a.ml + 2 * prow, m);
+          st_dev(a.ml + 2 * prow + 1, l);
+        }
       }
     }
 
-    if (n_split > 1) {
-      // publish the partial; the last split to arrive merges all of them
-      __threadfence();
+    bool any_split = false;
+#pragma unroll
+    for (int k = 0; k < kMaxR; ++k) any_split |= k < nR && rec[8 * k + kRecNSplit] > 1;
+    if (any_split) {
+      // publish the partials; the last split of a sequence to arrive merges them
+      wait_vmem();
       __syncthreads();
-      if (threadIdx.x == 0) {
-        int32_t* c = a.cnt + (int64_t)b * a.Hkv + hk;
-        const int old = __hip_atomic_fetch_add(c, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        const int is_last = old == n_split - 1;
-        if (is_last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *flag = is_last;
+      if (tid < nR) {
+        const int32_t* r = rec + 8 * tid;
+        int is_last = 0;
+        if (r[kRecNSplit] > 1) {
+          int32_t* c = a.cnt + (int64_t)r[kRecB] * a.Hkv + r[kRecHk];
+          const int old = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          is_last = old == r[kRecNSplit] - 1;
+          if (is_last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        flags[tid] = is_last;
       }
       __syncthreads();
-      if (*flag) {
-        __threadfence();
+      for (int row = wave; row < nrows; row += NW) {
+        const int k = row / G, h = row - k * G;
+        if (!flags[k]) continue;
+        const int32_t* r = rec + 8 * k;
+        const int b = r[kRecB], n_split = r[kRecNSplit];
         const int bs0 = base[b];
-        for (int h = wave; h < a.G; h += 4) {
-          const int64_t col = hq0 + h;
-          float m = -INFINITY;
-          for (int c0 = 0; c0 < n_split; c0 += 64) {
-            const float mv = c0 + lane < n_split ? a.ml[(int64_t)(bs0 + c0 + lane) * a.Hq + col].x : -INFINITY;
-            m = fmaxf(m, mv);
-          }
-#pragma unroll
-          for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
-          float o[PER], l = 0.f;
-#pragma unroll
-          for (int k = 0; k < PER; ++k) o[k] = 0.f;
-          for (int c0 = 0; c0 < n_split; c0 += 64) {
-            const int n = min(64, n_split - c0);
-            float wt = 0.f, lw = 0.f;
-            if (lane < n) {
-              const float2 v = a.ml[(int64_t)(bs0 + c0 + lane) * a.Hq + col];
-              wt = v.x > -INFINITY ? __builtin_amdgcn_exp2f(v.x - m) : 0.f;
-              lw = wt * v.y;
-            }
-#pragma unroll
-            for (int x = 32; x >= 1; x >>= 1) lw += __shfl_xor(lw, x);
-            l += lw;
-            for (int sidx = 0; sidx < n; ++sidx) {
-              const float ws = __shfl(wt, sidx);
-              const float* src = a.po + ((int64_t)(bs0 + c0 + sidx) * a.Hq + col) * D + lane;
-#pragma unroll
-              for (int k = 0; k < PER; ++k) o[k] += ws * src[64 * k];
-            }
-          }
-          store_row<D, UNROT>(o, l, a.out + ((int64_t)b * a.Hq + col) * D, lane);
+        const int64_t col = (int64_t)r[kRecHk] * G + h;
+        float m = -INFINITY;
+        for (int c0 = 0; c0 < n_split; c0 += 64) {
+          const float mv = c0 + lane < n_split ? ld_dev(a.ml + 2 * ((int64_t)(bs0 + c0 + lane) * a.Hq + col)) : -INFINITY;
+          m = fmaxf(m, mv);
         }
+#pragma unroll
+        for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
+        float o[PER], l = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < PER; ++kk) o[kk] = 0.f;
+        for (int c0 = 0; c0 < n_split; c0 += 64) {
+          const int n = min(64, n_split - c0);
+          float wt = 0.f, lw = 0.f;
+          if (lane < n) {
+            const float* v = a.ml + 2 * ((int64_t)(bs0 + c0 + lane) * a.Hq + col);
+            const float vm = ld_dev(v), vl = ld_dev(v + 1);
+            wt = vm > -INFINITY ? __builtin_amdgcn_exp2f(vm - m) : 0.f;
+            lw = wt * vl;
+          }
+#pragma unroll
+          for (int x = 32; x >= 1; x >>= 1) lw += __shfl_xor(lw, x);
+          l += lw;
+          for (int sidx = 0; sidx < n; ++sidx) {
+            const float ws = __shfl(wt, sidx);
+            const float* src = a.po + ((int64_t)(bs0 + c0 + sidx) * a.Hq + col) * D + lane;
+#pragma unroll
+            for (int kk = 0; kk < PER; ++kk) o[kk] += ws * ld_dev(src + 64 * kk);
+          }
+        }
+        store_row<D, UNROT>(o, l, a.out + ((int64_t)b * a.Hq + col) * D, lane);
       }
     }
-    __syncthreads();                               // LDS is reused by the next item
+    __syncthreads();                               // LDS is reused by the next round
   }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Compute units and LDS bytes per workgroup of the current device, cached.
+struct DeviceLimits { int cus, lds; };
+DeviceLimits device_limits() {
+  static std::atomic<int> cache_cus[64], cache_lds[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int cus = cache_cus[dev].load(std::memory_order_relaxed), lds = cache_lds[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lds <= 0)
+      lds = 64 * 1024;
+    cache_lds[dev].store(lds, std::memory_order_relaxed);
+    cache_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  return {cus, lds};
+}
+
 template <int D, int IN, int FMT, bool UNROT, class Pol>
-hipError_t launch_one(const DecodeArgs& a, const KArgs& k, hipStream_t s) {
-  const size_t lds = Smem<D, FMT>::bytes(a.B);
+hipError_t launch_one(const DecodeArgs& a, const KArgs& k0, hipStream_t s) {
+  constexpr int NW = 4 * Pol::kOcc;
+  constexpr int ESZ = FMT == UQ_KV_BF16 ? 2 : 1;
+  const DeviceLimits dl = device_limits();
+  const int G = a.Hq / a.Hkv;
   const int max_items = a.lay.max_bs * a.Hkv;
-  const int wgs = kCUs * Pol::kOcc;
-  const dim3 grid((unsigned)(max_items < wgs ? max_items : wgs)), blk(256);
-  hipLaunchKernelGGL((decode_kernel<Pol, D, IN, FMT, UNROT>), grid, blk, lds, s, k, a.page_table, a.seq_lens);
+  const int grid = max_items < dl.cus ? max_items : dl.cus;
+  // items per round: enough for every item to fall in one round, within LDS
+  int R = (max_items + grid - 1) / grid;
+  R = R < kMaxR ? R : kMaxR;
+  while (R > 1 && Lds(R, NW, G, D, ESZ, a.B).total > dl.lds) --R;
+  const int lds = Lds(R, NW, G, D, ESZ, a.B).total;
+  if (lds > dl.lds) return hipErrorInvalidConfiguration;
+  auto kern = decode_kernel<Pol, D, IN, FMT, UNROT>;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
+  KArgs k = k0;
+  k.R = R;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NW), (size_t)lds, s, k, a.page_table, a.seq_lens);
   return hipGetLastError();
 }
 
@@ -733,7 +1040,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   k.target_bs = L.target_bs;
   k.scale_log2 = a.sm_scale * 1.4426950408889634f;
   k.out = a.out;
-  k.ml = reinterpret_cast<float2*>(a.ws + L.ml);
+  k.ml = reinterpret_cast<float*>(a.ws + L.ml);
   k.po = reinterpret_cast<float*>(a.ws + L.po);
   k.cnt = reinterpret_cast<int32_t*>(a.ws + L.cnt);
   hipError_t e;
@@ -770,10 +1077,6 @@ DecodeLayout decode_layout(int format, int B, int Hq, int Hkv, int D) {
   return L;
 }
 
-size_t decode_lds_bytes(int format, int B, int D) {
-  if (format == UQ_KV_BF16) return D == 128 ? Smem<128, UQ_KV_BF16>::bytes(B) : Smem<64, UQ_KV_BF16>::bytes(B);
-  return D == 128 ? Smem<128, UQ_KV_FP4>::bytes(B) : Smem<64, UQ_KV_FP4>::bytes(B);
-}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   return a.D == 128 ? launch_decode_d<128>(a, s) : launch_decode_d<64>(a, s);

@@ -33,8 +33,6 @@ struct DecodeLayout {
   int32_t max_bs;              // bound on (sequence, split) pairs: target_bs + num_seqs
 };
 
-// LDS bytes one decode workgroup needs for num_seqs sequences.
-size_t decode_lds_bytes(int format, int num_seqs, int head_dim);
 constexpr int kMaxDecodeSeqs = 8192;   // per-workgroup plan lives in LDS
 
 DecodeLayout decode_layout(int format, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim);
