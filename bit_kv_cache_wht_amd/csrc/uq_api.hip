@@ -64,6 +64,10 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   if (format == UQ_KV_BF16 && q_dtype != UQ_IN_BF16) return UQ_ERR_UNSUPPORTED;
   if (num_seqs < 0 || max_pages_per_seq < 1 || num_q_heads < 1) return UQ_ERR_INVALID_ARG;
   if (num_seqs > uq::kMaxDecodeSeqs) return UQ_ERR_UNSUPPORTED;
+  // the step list (4 pages per step, all sequences and KV heads) is indexed in 31 bits
+  if (max_pages_per_seq > (1 << 26) ||
+      (int64_t)num_seqs * ((max_pages_per_seq + 3) / 4) * cache->num_kv_heads > INT32_MAX)
+    return UQ_ERR_UNSUPPORTED;
   if (num_q_heads % cache->num_kv_heads != 0) return UQ_ERR_UNSUPPORTED;
   if (num_q_heads / cache->num_kv_heads > 16) return UQ_ERR_UNSUPPORTED;
   if (!(sm_scale > 0.f) || sm_scale > 3.0e38f) return UQ_ERR_INVALID_ARG;   // NaN, <= 0, inf

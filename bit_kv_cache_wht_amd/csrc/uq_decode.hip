@@ -37,7 +37,7 @@ namespace uq {
 
 namespace {
 
-constexpr int kTargetItems = 512;    // decode items per launch the plan aims for
+constexpr int kMaxGrid = 1024;       // workgroups per launch, at most (one per compute unit)
 constexpr int kMaxR = 8;             // items per round of a workgroup, at most
 
 // ------------------------------------------------------------------ formats
@@ -364,17 +364,12 @@ template <int D> struct Bf16Pol {
 };
 
 // ------------------------------------------------------------------ plan
-// Every workgroup derives the split plan from seq_lens in LDS: pages per split
-// pps (a multiple of 4, sized so that the (sequence, split) pairs number about
-// target_bs) and base[b] = first pair of sequence b, base[B] = number of pairs.
-// A sequence of length 0 still gets one (empty) pair so that its output row is
-// written.
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
-
+// The work of a call is the list of steps (4 pages) of all (sequence b, KV head
+// hk) items, items in the order b * Hkv + hk.  Every workgroup derives in LDS
+// sbase[b] = first step of item (b, 0), each item of sequence b having
+// steps(b) = ceil(pages(b) / 4) steps, and sbase[B] = T, the total.  Workgroup w
+// then takes steps [w T / grid, (w + 1) T / grid): equal shares whatever the
+// mix of lengths, items cut at share boundaries being merged across workgroups.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -384,43 +379,38 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// Run by all 64 * NW threads; red: 2 * NW ints of scratch.
+// Sequence length as used: clamped to [0, max_pages * 16] so that a length
+// beyond its page-table row can never index past the row.
+__device__ __forceinline__ int clamp_len(int L, int max_pages) {
+  return L < 0 ? 0 : (L > max_pages * kPage ? max_pages * kPage : L);
+}
+__device__ __forceinline__ int seq_steps(int L) { return ((L + kPage - 1) / kPage + 3) >> 2; }
+
+// Run by all 64 * NW threads; red: NW ints of scratch.
 template <int NW>
-__device__ void wg_plan(const int32_t* __restrict__ seq_lens, int B, int target_bs, int32_t* base, int32_t* red,
-                        int32_t& pps_out) {
+__device__ void wg_plan(const int32_t* __restrict__ seq_lens, int B, int Hkv, int max_pages, int32_t* sbase,
+                        int32_t* red) {
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int32_t tot = 0;
-  for (int b = tid; b < B; b += NT) tot += (seq_lens[b] + kPage - 1) / kPage;
-  tot = wave_sum(tot);
-  if (lane == 0) red[wave] = tot;
-  __syncthreads();
-  int total = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) total += red[w];
-  int pps = (total + target_bs - 1) / target_bs;
-  pps = pps < 4 ? 4 : (pps + 3) & ~3;
   int32_t carry = 0;
   for (int b0 = 0; b0 < B; b0 += NT) {
     const int b = b0 + tid;
-    const int pages = b < B ? (seq_lens[b] + kPage - 1) / kPage : 0;
-    const int ns = b < B ? max(1, (pages + pps - 1) / pps) : 0;
+    const int ns = b < B ? seq_steps(clamp_len(seq_lens[b], max_pages)) * Hkv : 0;
     const int incl = wave_incl_scan(ns, lane);
-    if (lane == 63) red[NW + wave] = incl;
+    if (lane == 63) red[wave] = incl;
     __syncthreads();
     int woff = 0, chunk = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      woff += w < wave ? red[NW + w] : 0;
-      chunk += red[NW + w];
+      woff += w < wave ? red[w] : 0;
+      chunk += red[w];
     }
-    if (b < B) base[b] = carry + woff + incl - ns;
+    if (b < B) sbase[b] = carry + woff + incl - ns;
     carry += chunk;
-    __syncthreads();                               // red[NW..] is rewritten by the next chunk
+    __syncthreads();                               // red is rewritten by the next chunk
   }
-  if (tid == 0) base[B] = carry;
+  if (tid == 0) sbase[B] = carry;
   __syncthreads();
-  pps_out = pps;
 }
 
 // Query rows into LDS: E4M3 bytes of the (FP4: rotated) rows; BF16 keeps the
@@ -535,11 +525,10 @@ struct KArgs {
   int32_t max_pages;
   const void* q;             // caller's query [B][Hq][D], bf16 or f32
   int32_t B, Hq, Hkv, G;
-  int32_t target_bs;
   float scale_log2;          // sm_scale * log2(e)
   float* out;                // [B][Hq][D]
-  float* ml;                 // [bs][Hq][2] (m in log2 units, l) of multi-split sequences
-  float* po;                 // [bs][Hq][D]
+  float* ml;                 // [2 * grid][G][2] partial (m in log2 units, l) of cut items
+  float* po;                 // [2 * grid][G][D] partial O of cut items
   int32_t* cnt;              // [B][Hkv] arrival counters, zero between calls
   int32_t R;                 // items per round of a workgroup
 };
@@ -584,20 +573,21 @@ struct Lds {
 };
 
 // Item record fields.
-enum { kRecB = 0, kRecPBegin, kRecNpg, kRecHk, kRecLRel, kRecNStep, kRecBs, kRecNSplit };
+enum { kRecB = 0, kRecPBegin, kRecNpg, kRecHk, kRecLRel, kRecNStep, kRecSlot, kRecNContrib };
 
 // One persistent workgroup per compute unit, NW = 4 * kOcc waves (so two waves
-// share a SIMD when kOcc = 2).  The workgroup takes its items in rounds of up to
-// R (item = sequence b, KV head hk, split of pps pages): the steps (4 pages) of
-// all items of a round form one list from which the waves claim steps one at a
-// time through an LDS counter.  Waves that share a SIMD therefore end within a
-// step of each other whatever the issue arbitration between them, and the
-// prefetch runs on across item boundaries.  A wave keeps one running softmax
-// state and parks it in its LDS slot for the item when its next step belongs to
-// another item; at the end of the round the slots of each item are merged.  A
-// sequence with one split writes its output directly; otherwise each split
-// writes a partial and the last one to arrive (device-scope counter) merges
-// them.
+// share a SIMD when kOcc = 2), each taking an equal share of the steps of the
+// call (see wg_plan).  A share is walked in rounds of up to R segments (the part
+// of one item inside the share): the steps of a round form one list from which
+// the waves claim steps one at a time through an LDS counter.  Waves that share
+// a SIMD therefore end within a step of each other whatever the issue
+// arbitration between them, and the prefetch runs on across segment boundaries.
+// A wave keeps one running softmax state and parks it in its LDS slot for the
+// segment when its next step belongs to another segment; at the end of the
+// round the slots of each segment are merged.  A segment that is a whole item
+// writes its output rows; otherwise the workgroup writes a partial (slot 2w for
+// the first segment of its share, 2w + 1 for the last) and the last of the
+// item's workgroups to arrive (device-scope counter) merges the partials.
 template <class Pol, int D, int IN, int FMT, bool UNROT>
 __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs a,
                                                                    const int32_t* __restrict__ page_table,
@@ -623,37 +613,57 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, j4 = lane >> 4;
-  int pps;
-  wg_plan<NW>(seq_lens, a.B, a.target_bs, base, red, pps);
-  const int n_items = base[a.B] * a.Hkv;
+  wg_plan<NW>(seq_lens, a.B, a.Hkv, a.max_pages, base, red);
+  const int64_t T = base[a.B];
+  // shares go to the first min(gridDim.x, T) workgroups, so that none is empty
+  // and the workgroups holding steps of an item are consecutive
+  const int grid = (int)(T < (int64_t)gridDim.x ? T : (int64_t)gridDim.x), wg = blockIdx.x;
+  auto share_begin = [&](int w) -> int64_t { return (int64_t)w * T / grid; };
+  auto owner = [&](int64_t g) -> int { return (int)(((g + 1) * grid - 1) / T); };   // w with g in its share
+  const int64_t g_hi = wg < grid ? share_begin(wg + 1) : 0;
 
-  for (int r0 = blockIdx.x; r0 < n_items; r0 += gridDim.x * a.R) {
-    const int nR = min(a.R, (n_items - r0 + (int)gridDim.x - 1) / (int)gridDim.x);
-
-    // ---- round set-up: item records, empty slots, step counter
-    if (tid < nR) {
-      const int item = r0 + tid * gridDim.x;
-      const int bs = item / a.Hkv;
-      const int hk = item - bs * a.Hkv;
-      int lo = 0, hi = a.B;                      // b: last index with base[b] <= bs
+  for (int64_t g_cur = wg < grid ? share_begin(wg) : 0; g_cur < g_hi;) {
+    // ---- round set-up: segments k = 0 .. nR-1 are items f0 + k clipped to the share
+    int f0;
+    {
+      int lo = 0, hi = a.B;                      // b: last index with sbase[b] <= g_cur (non-empty)
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (base[mid] <= bs) lo = mid; else hi = mid;
+        if (base[mid] <= g_cur) lo = mid; else hi = mid;
       }
-      const int b = lo;
-      const int L = seq_lens[b];
+      const int steps = (base[lo + 1] - base[lo]) / a.Hkv;
+      f0 = lo * a.Hkv + (int)((g_cur - base[lo]) / steps);
+    }
+    auto item_start = [&](int f) -> int64_t {
+      const int b = f / a.Hkv;
+      return base[b] + (int64_t)(f - b * a.Hkv) * ((base[b + 1] - base[b]) / a.Hkv);
+    };
+    int nR = 1;
+    while (nR < a.R && f0 + nR < a.B * a.Hkv && item_start(f0 + nR) < g_hi) ++nR;
+    if (tid < nR) {
+      const int f = f0 + tid;
+      const int b = f / a.Hkv;
+      const int hk = f - b * a.Hkv;
+      const int steps = (base[b + 1] - base[b]) / a.Hkv;
+      const int64_t start = item_start(f), end = start + steps;
+      const int64_t s_lo = start > g_cur ? start : g_cur, s_hi = end < g_hi ? end : g_hi;
+      const int L = clamp_len(seq_lens[b], a.max_pages);
       const int pages = (L + kPage - 1) / kPage;
-      const int p_begin = (bs - base[b]) * pps;
-      const int npg = max(min(p_begin + pps, pages) - p_begin, 0);
+      const int p_begin = 4 * (int)(s_lo - start);
       int32_t* r = rec + 8 * tid;
       r[kRecB] = b;
       r[kRecPBegin] = p_begin;
-      r[kRecNpg] = npg;
+      r[kRecNpg] = max(min(pages - p_begin, 4 * (int)(s_hi - s_lo)), 0);
       r[kRecHk] = hk;
       r[kRecLRel] = L - p_begin * kPage;
-      r[kRecNStep] = (npg + 3) >> 2;
-      r[kRecBs] = bs;
-      r[kRecNSplit] = base[b + 1] - base[b];
+      r[kRecNStep] = (int)max(s_hi - s_lo, (int64_t)0);
+      const bool partial = s_lo > start || s_hi < end;
+      r[kRecSlot] = partial ? 2 * wg + (share_begin(wg) >= start ? 0 : 1) : -1;
+      r[kRecNContrib] = partial ? owner(end - 1) - owner(start) + 1 : 1;
+    }
+    {
+      const int64_t e = item_start(f0 + nR - 1) + (base[(f0 + nR - 1) / a.Hkv + 1] - base[(f0 + nR - 1) / a.Hkv]) / a.Hkv;
+      g_cur = e < g_hi ? e : g_hi;               // next round starts after the last segment
     }
     for (int i = tid; i < nR * NW * G; i += NT) smx[i] = -INFINITY;
     if (tid == 0) *ctr = 0;
@@ -880,9 +890,11 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     if (acc_k >= 0) park();
     __syncthreads();
 
-    // ---- merge the wave slots of each item; wave w takes rows w, w + NW, ...
+    // ---- merge the wave slots of each segment; wave w takes rows w, w + NW, ...
     for (int row = wave; row < nrows; row += NW) {
       const int k = row / G, h = row - k * G;
+      const int32_t* r = rec + 8 * k;
+      if (r[kRecNStep] == 0) continue;           // empty sequences are written below
       const int slot0 = k * NW * G + h;          // slot of wave w: slot0 + w * G
       float m = -INFINITY;
 #pragma unroll
@@ -902,12 +914,11 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
           }
         }
       }
-      const int32_t* r = rec + 8 * k;
-      const int64_t col = (int64_t)r[kRecHk] * G + h;
-      if (r[kRecNSplit] == 1) {
-        store_row<D, UNROT>(o, l, a.out + ((int64_t)r[kRecB] * a.Hq + col) * D, lane);
+      const int slot = r[kRecSlot];
+      if (slot < 0) {
+        store_row<D, UNROT>(o, l, a.out + ((int64_t)r[kRecB] * a.Hq + (int64_t)r[kRecHk] * G + h) * D, lane);
       } else {
-        const int64_t prow = (int64_t)r[kRecBs] * a.Hq + col;
+        const int64_t prow = (int64_t)slot * G + h;
 #pragma unroll
         for (int kk = 0; kk < PER; ++kk) st_dev(a.po + prow * D + lane + 64 * kk, o[kk]);
         if (lane == 0) {
@@ -917,20 +928,20 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
       }
     }
 
-    bool any_split = false;
+    bool any_partial = false;
 #pragma unroll
-    for (int k = 0; k < kMaxR; ++k) any_split |= k < nR && rec[8 * k + kRecNSplit] > 1;
-    if (any_split) {
-      // publish the partials; the last split of a sequence to arrive merges them
+    for (int k = 0; k < kMaxR; ++k) any_partial |= k < nR && rec[8 * k + kRecSlot] >= 0;
+    if (any_partial) {
+      // publish the partials; the last workgroup of an item to arrive merges them
       wait_vmem();
       __syncthreads();
       if (tid < nR) {
         const int32_t* r = rec + 8 * tid;
         int is_last = 0;
-        if (r[kRecNSplit] > 1) {
+        if (r[kRecSlot] >= 0) {
           int32_t* c = a.cnt + (int64_t)r[kRecB] * a.Hkv + r[kRecHk];
           const int old = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          is_last = old == r[kRecNSplit] - 1;
+          is_last = old == r[kRecNContrib] - 1;
           if (is_last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         flags[tid] = is_last;
@@ -940,12 +951,18 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         const int k = row / G, h = row - k * G;
         if (!flags[k]) continue;
         const int32_t* r = rec + 8 * k;
-        const int b = r[kRecB], n_split = r[kRecNSplit];
-        const int bs0 = base[b];
-        const int64_t col = (int64_t)r[kRecHk] * G + h;
+        const int b = r[kRecB], hk = r[kRecHk];
+        const int steps = (base[b + 1] - base[b]) / a.Hkv;
+        const int64_t start = base[b] + (int64_t)hk * steps;
+        const int w0 = owner(start), n = r[kRecNContrib];
+        // partial of contributor w0 + i: slot 2w if the item begins its share, else 2w + 1
+        auto prow_of = [&](int i) -> int64_t {
+          const int w = w0 + i;
+          return (int64_t)(2 * w + (share_begin(w) >= start ? 0 : 1)) * G + h;
+        };
         float m = -INFINITY;
-        for (int c0 = 0; c0 < n_split; c0 += 64) {
-          const float mv = c0 + lane < n_split ? ld_dev(a.ml + 2 * ((int64_t)(bs0 + c0 + lane) * a.Hq + col)) : -INFINITY;
+        for (int c0 = 0; c0 < n; c0 += 64) {
+          const float mv = c0 + lane < n ? ld_dev(a.ml + 2 * prow_of(c0 + lane)) : -INFINITY;
           m = fmaxf(m, mv);
         }
 #pragma unroll
@@ -953,11 +970,11 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         float o[PER], l = 0.f;
 #pragma unroll
         for (int kk = 0; kk < PER; ++kk) o[kk] = 0.f;
-        for (int c0 = 0; c0 < n_split; c0 += 64) {
-          const int n = min(64, n_split - c0);
+        for (int c0 = 0; c0 < n; c0 += 64) {
+          const int nc = min(64, n - c0);
           float wt = 0.f, lw = 0.f;
-          if (lane < n) {
-            const float* v = a.ml + 2 * ((int64_t)(bs0 + c0 + lane) * a.Hq + col);
+          if (lane < nc) {
+            const float* v = a.ml + 2 * prow_of(c0 + lane);
             const float vm = ld_dev(v), vl = ld_dev(v + 1);
             wt = vm > -INFINITY ? __builtin_amdgcn_exp2f(vm - m) : 0.f;
             lw = wt * vl;
@@ -965,17 +982,23 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
 #pragma unroll
           for (int x = 32; x >= 1; x >>= 1) lw += __shfl_xor(lw, x);
           l += lw;
-          for (int sidx = 0; sidx < n; ++sidx) {
-            const float ws = __shfl(wt, sidx);
-            const float* src = a.po + ((int64_t)(bs0 + c0 + sidx) * a.Hq + col) * D + lane;
+          for (int i = 0; i < nc; ++i) {
+            const float ws = __shfl(wt, i);
+            const float* src = a.po + prow_of(c0 + i) * D + lane;
 #pragma unroll
             for (int kk = 0; kk < PER; ++kk) o[kk] += ws * ld_dev(src + 64 * kk);
           }
         }
-        store_row<D, UNROT>(o, l, a.out + ((int64_t)b * a.Hq + col) * D, lane);
+        store_row<D, UNROT>(o, l, a.out + ((int64_t)b * a.Hq + (int64_t)hk * G + h) * D, lane);
       }
     }
     __syncthreads();                               // LDS is reused by the next round
+  }
+
+  // rows of empty sequences are zero
+  for (int b = wg; b < a.B; b += gridDim.x) {
+    if (clamp_len(seq_lens[b], a.max_pages) > 0) continue;
+    for (int i = tid; i < a.Hq * D; i += NT) a.out[(int64_t)b * a.Hq * D + i] = 0.f;
   }
 }
 
@@ -1004,11 +1027,10 @@ hipError_t launch_one(const DecodeArgs& a, const KArgs& k0, hipStream_t s) {
   constexpr int ESZ = FMT == UQ_KV_BF16 ? 2 : 1;
   const DeviceLimits dl = device_limits();
   const int G = a.Hq / a.Hkv;
-  const int max_items = a.lay.max_bs * a.Hkv;
-  const int grid = max_items < dl.cus ? max_items : dl.cus;
-  // items per round: enough for every item to fall in one round, within LDS
-  int R = (max_items + grid - 1) / grid;
-  R = R < kMaxR ? R : kMaxR;
+  const int grid = dl.cus < kMaxGrid ? dl.cus : kMaxGrid;
+  // segments per round: as many as fit in LDS (the share of a workgroup usually
+  // spans a few items)
+  int R = kMaxR;
   while (R > 1 && Lds(R, NW, G, D, ESZ, a.B).total > dl.lds) --R;
   const int lds = Lds(R, NW, G, D, ESZ, a.B).total;
   if (lds > dl.lds) return hipErrorInvalidConfiguration;
@@ -1037,7 +1059,6 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   k.Hq = a.Hq;
   k.Hkv = a.Hkv;
   k.G = a.Hq / a.Hkv;
-  k.target_bs = L.target_bs;
   k.scale_log2 = a.sm_scale * 1.4426950408889634f;
   k.out = a.out;
   k.ml = reinterpret_cast<float*>(a.ws + L.ml);
@@ -1066,17 +1087,15 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
 
 DecodeLayout decode_layout(int format, int B, int Hq, int Hkv, int D) {
   (void)format;
+  const size_t G = (size_t)(Hq / Hkv);
   DecodeLayout L;
-  L.target_bs = (kTargetItems + Hkv - 1) / Hkv;
-  L.max_bs = L.target_bs + B;
   size_t off = 0;
   L.cnt = off; off = align256(off + sizeof(int32_t) * (size_t)B * Hkv);
-  L.ml = off; off = align256(off + sizeof(float2) * (size_t)L.max_bs * Hq);
-  L.po = off; off = align256(off + sizeof(float) * (size_t)L.max_bs * Hq * D);
+  L.ml = off; off = align256(off + sizeof(float) * 2 * (2 * (size_t)kMaxGrid) * G);
+  L.po = off; off = align256(off + sizeof(float) * (2 * (size_t)kMaxGrid) * G * D);
   L.total = off;
   return L;
 }
-
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   return a.D == 128 ? launch_decode_d<128>(a, s) : launch_decode_d<64>(a, s);

@@ -29,8 +29,6 @@ hipError_t launch_query(const void* q, int in_dtype, uint8_t* q_fp8, int rows, i
 
 struct DecodeLayout {
   size_t cnt, ml, po, total;   // byte offsets into the workspace
-  int32_t target_bs;           // target number of (sequence, split) pairs
-  int32_t max_bs;              // bound on (sequence, split) pairs: target_bs + num_seqs
 };
 
 constexpr int kMaxDecodeSeqs = 8192;   // per-workgroup plan lives in LDS

@@ -152,6 +152,7 @@ size_t uq_decode_workspace_bytes(const uq_kv_cache* cache, int32_t num_seqs, int
  *   page_table  device int32 [num_seqs][max_pages_per_seq]; entries past
  *               ceil(seq_lens[b] / 16) are not read
  *   seq_lens    device int32 [num_seqs], each in [0, 16 * max_pages_per_seq]
+ *               (values outside are clamped to that range)
  *   out         device float [num_seqs][num_q_heads][head_dim]; must not alias
  *               any input; a sequence of length 0 gives a zero row
  *   workspace   device, >= uq_decode_workspace_bytes(...) bytes, 256-B aligned,
@@ -159,7 +160,9 @@ size_t uq_decode_workspace_bytes(const uq_kv_cache* cache, int32_t num_seqs, int
  *               the next one (no clearing needed).  Calls that overlap in time
  *               must not share a workspace.
  * num_q_heads must be a multiple of num_kv_heads with a ratio of 1..16,
- * num_seqs at most 4096, and sm_scale positive and finite.
+ * num_seqs at most 8192, max_pages_per_seq at most 2^26 and
+ * num_seqs * ceil(max_pages_per_seq / 4) * num_kv_heads below 2^31 (else
+ * UQ_ERR_UNSUPPORTED), and sm_scale positive and finite.
  * Accuracy: codes and scales enter exactly; logits and the softmax are float32,
  * probabilities and dequantized values enter the PV product as float16, so V
  * groups must have E <= 13 (|v| <= 49152) to stay finite in float16.
