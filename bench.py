@@ -40,6 +40,12 @@ def parse():
     ap.add_argument("--no-baselines", action="store_true", help="skip the FP8/BF16 KV kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle sample")
+    ap.add_argument("--scrub-mb", type=int, default=0,
+                    help="read a buffer of this size between the event-timed steps (evicts the last-level cache)")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="run FP4 steps and a 1 GiB device copy only (for rocprofv3 --pmc runs)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM-traffic summary from two rocprofv3 counter_collection.csv files")
     return ap.parse_args()
 
 
@@ -52,6 +58,108 @@ def make_workload(name):
     if name == "ragged":
         return W.ragged()
     return W.tiny()
+
+
+DECODE_SOURCES = ["bit_kv_cache_wht_amd/csrc/uq_decode.hip", "bit_kv_cache_wht_amd/csrc/uq_device.h",
+                  "bit_kv_cache_wht_amd/csrc/uq_internal.h"]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_fp4_64x8192_hbm_traffic.md")
+COPY_BYTES = 1 << 30
+
+
+def decode_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the FP4 decode kernel from the committed counter
+    summary, or None if it is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith(("source_sha256:", "traffic_bytes_per_launch:")))
+    if fields.get("source_sha256", "").strip() != decode_source_sha():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_pmc(fetch_csv, write_csv, workload):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the FP4 decode kernel, each
+    scaled by what the same counter reads for a device copy of COPY_BYTES."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return vals
+
+    out = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = per_kernel(path, name)
+        dec = [v for k, v in vals.items() if "decode_kernel" in k and "Fp4Pol" in k]
+        cpy = [v for k, v in vals.items() if "copyBuffer" in k]
+        if not dec or not cpy:
+            raise SystemExit(f"{path}: no FP4 decode or copy dispatches for {name}")
+        dec = dec[0]
+        cpy = max(cpy, key=lambda v: max(v))
+        cpy_kib = max(cpy)
+        out[name] = dict(dispatches=len(dec), kib=float(np.mean(dec)), copy_kib=cpy_kib,
+                         factor=COPY_BYTES / (cpy_kib * 1024.0))
+    f, w = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    traffic = int(round(f["kib"] * 1024 * f["factor"] + w["kib"] * 1024 * w["factor"]))
+    lines = [
+        f"# HBM traffic of decode_kernel<Fp4Pol<128>> on {workload}",
+        "",
+        "Counters from two rocprofv3 runs of the same program (one counter each), then",
+        "`python3 bench.py --summarize-pmc <fetch csv> <write csv>`:",
+        "",
+        "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- python3 bench.py --pmc-pass",
+        "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o write -- python3 bench.py --pmc-pass",
+        "",
+        f"Calibration: the largest dispatch of the runtime's copy kernel moves {COPY_BYTES} bytes each way.",
+        "",
+        "| counter | decode dispatches | decode KiB/dispatch | copy KiB | scale factor | decode bytes |",
+        "|---|---|---|---|---|---|",
+    ]
+    for name, r in out.items():
+        lines.append(f"| {name} | {r['dispatches']} | {r['kib']:.0f} | {r['copy_kib']:.0f} | {r['factor']:.4f} | "
+                     f"{r['kib'] * 1024 * r['factor']:.4g} |")
+    lines += ["", f"source_sha256: {decode_source_sha()}", f"traffic_bytes_per_launch: {traffic}", ""]
+    with open(TRAFFIC_SUMMARY, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def pmc_pass(args):
+    """FP4 steps on the workload, then a plain device copy of known size."""
+    import torch
+    torch.cuda.set_device(0)
+    wl = make_workload(args.workload)
+    r = Runner("fp4", wl)
+    for _ in range(args.warmup + args.steps):
+        r.step()
+    torch.cuda.synchronize()
+    del r
+    torch.cuda.empty_cache()
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("pmc pass done")
 
 
 def fp4_kv_bytes_per_token_head(d):
@@ -128,22 +236,32 @@ class Runner:
             self.uq.uq_profile_next_decode(ev[0], ev[1])
         self.decode(self.cache, self.q, self.page_table, self.seq_lens, self.sm_scale, self.out, self.ws)
 
-    def run(self, steps, warmup):
+    def run(self, steps, warmup, scrub=None):
+        """Pass 1 times `steps` whole steps back to back with nothing else in the
+        timed region.  Pass 2 repeats them with HIP events that the library records
+        around its decode kernel, on the kernel's own stream; with `scrub` (a device
+        tensor) a read of it between steps, outside the events, evicts the
+        last-level cache first."""
         torch = self.torch
         for _ in range(warmup):
             self.step()
-        evs = HipEvents(steps)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         wall0 = time.perf_counter()
         t0.record()
-        for i in range(steps):
-            self.step(evs.pairs[i])
+        for _ in range(steps):
+            self.step()
         t1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
         ms_step = t0.elapsed_time(t1) / steps
+        evs = HipEvents(steps)
+        for i in range(steps):
+            if scrub is not None:
+                scrub.max()                        # a read: evicts without leaving dirty lines
+            self.step(evs.pairs[i])
+        torch.cuda.synchronize()
         k_ms = [evs.elapsed_ms(i) for i in range(steps)]
         evs.close()
         return dict(ms_per_step=ms_step, wall_ms_per_step=1e3 * wall / steps,
@@ -208,10 +326,16 @@ def cpu_baseline(wl, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this hot path needs no "
               f"collectives and is benchmarked at N=1", file=sys.stderr)
         sys.exit(2)
+    if args.pmc_pass:
+        pmc_pass(args)
+        return
     import torch
     torch.cuda.set_device(0)
     log(f"generating workload {args.workload}")
@@ -224,7 +348,9 @@ def main():
     for fmt in fmts:
         log(f"{fmt}: prefill + timing")
         r = Runner(fmt, wl)
-        res = r.run(args.steps, args.warmup)
+        scrub = torch.ones((args.scrub_mb << 20) // 4, dtype=torch.int32, device="cuda") if args.scrub_mb else None
+        res = r.run(args.steps, args.warmup, scrub)
+        del scrub
         algo, kv = r.kernel_bytes()
         res["kernel_gbs"] = algo / (res["decode_kernel_ms"] * 1e-3) / 1e9
         res["kernel_algo_bytes"] = algo
@@ -255,8 +381,11 @@ def main():
                    "global_batch": wl.batch, "seq_len": int(wl.seq_lens.max()), "parallelism": "none (1 GPU)"},
         "kv_gbs_per_step": round(fp4["kv_bytes"] / (fp4["ms_per_step"] * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(fp4["kernel_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(fp4["kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(fp4["kernel_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic() if args.workload == "decode_gqa" else None,
                      "kernel": "decode_kernel<Fp4Pol<128>>", "kernel_us": round(fp4["decode_kernel_ms"] * 1e3, 2),
+                     "timing": "HIP events around each launch on its stream"
+                               + (f", {args.scrub_mb} MB scrub between steps" if args.scrub_mb else ", steps back to back"),
                      "kernel_us_p10_p90": [round(fp4["decode_kernel_ms_p10"] * 1e3, 2),
                                            round(fp4["decode_kernel_ms_p90"] * 1e3, 2)],
                      "algo_bytes_per_launch": fp4["kernel_algo_bytes"]},
