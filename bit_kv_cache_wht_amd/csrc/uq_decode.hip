@@ -298,13 +298,20 @@ template <int D> struct Bf16Pol {
   static constexpr int kK = D / 32;     // 16x16x32 MFMAs per token row
   struct KStep { uint4 k[4][kK]; };      // K bf16 channels 32kk + 8j..+7 of token slot 4m + (lane%16)%4
   struct VStep { uint4 v[kTiles][2]; };  // V bf16 of channel 16t + lane%16, slots 0..7 and 8..15
-  struct QOp { v8bf b[kK]; };
+  // q as f16 B operands: MFMA kk, lane (h, j) holds channels 32kk + 8j..+7 of head h
+  struct QOp { v8h b[kK]; };
+  // bf16 pairs -> f16 pairs (exact for |x| >= 2^-14; smaller values lose bits as
+  // f16 subnormals, far below the output tolerance)
+  __device__ static uint32_t bf2h(uint32_t w) {
+    return pack_h2((_Float16)__uint_as_float(w << 16), (_Float16)__uint_as_float(w & 0xFFFF0000u));
+  }
+  __device__ static v8h bf2h8(const uint4& u) {
+    return __builtin_bit_cast(v8h, make_uint4(bf2h(u.x), bf2h(u.y), bf2h(u.z), bf2h(u.w)));
+  }
   __device__ static void load_q(QOp& qo, const uint8_t* qrow, bool valid, int j4) {
 #pragma unroll
-    for (int kk = 0; kk < kK; ++kk) {
-      const uint4 u = valid ? load16(qrow + 2 * (32 * kk + 8 * j4)) : make_uint4(0, 0, 0, 0);
-      qo.b[kk] = __builtin_bit_cast(v8bf, u);
-    }
+    for (int kk = 0; kk < kK; ++kk)
+      qo.b[kk] = bf2h8(valid ? load16(qrow + 2 * (32 * kk + 8 * j4)) : make_uint4(0, 0, 0, 0));
   }
   __device__ static void load_k(KStep& st, const uint8_t* kb, int r16, int j4) {
 #pragma unroll
@@ -321,13 +328,16 @@ template <int D> struct Bf16Pol {
       st.v[t][1] = load16(vb + 2 * ((16 * t + r16) * kPage + 8));
     }
   }
+  // QK on f16 MFMAs after widening K: feeding the loaded bf16 registers straight
+  // to bf16 MFMAs gave wrong logits on a wave's later steps (reproduced by the
+  // multi-step parity cases), while the widened form is exact and correct.
   __device__ static void qk(const KStep& st, const QOp& qo, v4f (&S)[4]) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       v4f acc = {0, 0, 0, 0};
 #pragma unroll
       for (int kk = 0; kk < kK; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, st.k[m][kk]), qo.b[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf2h8(st.k[m][kk]), qo.b[kk], acc, 0, 0, 0);
       S[m] = acc;
     }
   }
@@ -350,13 +360,7 @@ template <int D> struct Bf16Pol {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const uint32_t c[4] = {st.v[t][half].x, st.v[t][half].y, st.v[t][half].z, st.v[t][half].w};
-        uint32_t a[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float lo = __uint_as_float(c[i] << 16), hi = __uint_as_float(c[i] & 0xFFFF0000u);
-          a[i] = pack_h2((_Float16)lo, (_Float16)hi);
-        }
-        O[t] = mma2(__builtin_bit_cast(v8h, make_uint4(a[0], a[1], a[2], a[3])), P[half], O[t]);
+        O[t] = mma2(__builtin_bit_cast(v8h, make_uint4(bf2h(c[0]), bf2h(c[1]), bf2h(c[2]), bf2h(c[3]))), P[half], O[t]);
       }
     }
   }

@@ -30,13 +30,20 @@ def _wl(name):
         "empty_seqs": dict(batch=5, num_q_heads=8, num_kv_heads=2, head_dim=128, seq_lens=[0, 5, 0, 64, 65]),
         "one_long": dict(batch=1, num_q_heads=8, num_kv_heads=1, head_dim=128, seq_lens=[5000]),
         "d64_bf16": dict(batch=3, num_q_heads=12, num_kv_heads=3, head_dim=64, seq_lens=[90, 64, 250]),
+        # enough steps that every wave of every workgroup takes several, crossing
+        # item boundaries inside a workgroup's share
+        "multi_step": dict(batch=8, num_q_heads=64, num_kv_heads=8, head_dim=128, seq_lens=[2048] * 8),
+        # mixed lengths: shares cut items between workgroups after several steps each
+        "multi_ragged": dict(batch=6, num_q_heads=32, num_kv_heads=4, head_dim=128,
+                             seq_lens=[3000, 1500, 7000, 64, 2500, 5000]),
     }
     s = specs[name]
     return W.make_workload(name, s["batch"], s["num_q_heads"], s["num_kv_heads"], s["head_dim"], s["seq_lens"],
                            s["seq_lens"], seed=zlib.crc32(name.encode()) % 1000 + 7)
 
 
-SMALL = ["tiny", "edge_lens", "gqa_ragged", "mha_5heads", "group16_d64", "empty_seqs", "one_long", "d64_bf16"]
+SMALL = ["tiny", "edge_lens", "gqa_ragged", "mha_5heads", "group16_d64", "empty_seqs", "one_long", "d64_bf16",
+         "multi_step", "multi_ragged"]
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
