@@ -5,10 +5,10 @@
 //            (manon006.tistory.com/395)
 // [commentary] = pheeree.github.io "kv-cache-4bit-serving-residency-collapse"
 //
-// FP4 work mapping: a row is one (token, KV head) vector of K or of V.  D/32
-// consecutive lanes share a row, lane part p owning channels 32p..32p+31; after
-// the butterfly the same lane owns output group p, so group absmax, scale,
-// rounding and packing stay in registers.  A wave covers 64 / (D/32) rows.
+// FP4 work mapping: a row is one (token, KV head) vector of K or of V, spread
+// over LPR consecutive lanes (see append_fp4_kernel); after the butterfly each
+// lane owns the same channels of the rotated row, so group absmax, scale,
+// rounding and packing need at most a max across the lanes of a group.
 #include "uq_device.h"
 #include "uq_internal.h"
 
@@ -16,12 +16,34 @@ namespace uq {
 
 // FP4 write path ([review] §3.1; [commentary] footnote 2): WHT, group absmax,
 // UE8M0 scale byte, E2M1 codes, two codes per byte, paged store.
-template <int D, int IN>
+//
+// LPR lanes share a row, lane part p holding E = D / LPR consecutive channels
+// E*p .. E*p + E - 1.  LPR = D / 32 (E = 32: one quantization group per lane) for
+// large batches; LPR = D / 8 (E = 8, four lanes per group) when few rows are written,
+// which cuts the float64 work each lane does on its own.  Butterfly stages h < E
+// run inside the lane, stages h >= E between lanes p and p ^ (h / E); every sum
+// is exact in float64, so the results do not depend on the split.
+
+// Partner value of lane ^ M (M < 16, within the row's lane group).
+template <int M> __device__ __forceinline__ double lane_xor(double v) {
+  if constexpr (M == 1 || M == 2) return quad_swap<M>(v);
+  else return __shfl_xor(v, M);
+}
+
+template <int E, int M> __device__ __forceinline__ void cross_stage(double (&x)[E], int p) {
+  const double sgn = (p & M) ? -1.0 : 1.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = __builtin_fma(x[e], sgn, lane_xor<M>(x[e]));
+}
+
+template <int D, int IN, int LPR>
 __global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
-  constexpr int LPR = D / 32;
+  constexpr int E = D / LPR;                       // channels per lane
+  constexpr int LPG = 32 / E;                      // lanes per quantization group
   constexpr int RPW = 64 / LPR;
   constexpr int BLK = Fp4Block<D>::kBytes;
   constexpr int CODE = Fp4Block<D>::kCodeBytes;
+  constexpr int CPL = D / 32;                      // V: channel pairs per PV lane row group
   const int lane = threadIdx.x & 63;
   const int p = lane % LPR;
   const int64_t nrows = 2LL * a.T * a.H;
@@ -36,39 +58,78 @@ __global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
   const int t = (int)(tr / a.H), h = (int)(tr - (int64_t)t * a.H);
   const int slot = a.slot_mapping[t];
 
-  double x[32];
-  load_row32<IN>(is_v ? a.v : a.k, tr * D + 32 * p, x);
-  wht_row<D>(x, lane);
+  double x[E];
+  {
+    const void* base = is_v ? a.v : a.k;
+    const int64_t elem = tr * D + E * p;
+    if constexpr (E == 32) {
+      load_row32<IN>(base, elem, x);
+    } else if constexpr (IN == UQ_IN_BF16) {
+      const uint4 u = load16(static_cast<const uint16_t*>(base) + elem);
+      const uint32_t d[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_bits_to_f64(d[i] & 0xFFFFu);
+        x[2 * i + 1] = bf16_bits_to_f64(d[i] >> 16);
+      }
+    } else {
+      const float4* q4 = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+      const float4 f0 = q4[0], f1 = q4[1];
+      x[0] = f0.x; x[1] = f0.y; x[2] = f0.z; x[3] = f0.w; x[4] = f1.x; x[5] = f1.y; x[6] = f1.z; x[7] = f1.w;
+    }
+  }
+  // normalized Sylvester WHT
+#pragma unroll
+  for (int hh = 1; hh < E; hh <<= 1)
+#pragma unroll
+    for (int i = 0; i < E; i += 2 * hh)
+#pragma unroll
+      for (int j = i; j < i + hh; ++j) {
+        const double a0 = x[j], a1 = x[j + hh];
+        x[j] = a0 + a1;
+        x[j + hh] = a0 - a1;
+      }
+  if constexpr (LPR > 1) cross_stage<E, 1>(x, p);
+  if constexpr (LPR > 2) cross_stage<E, 2>(x, p);
+  if constexpr (LPR > 4) cross_stage<E, 4>(x, p);
+  if constexpr (LPR > 8) cross_stage<E, 8>(x, p);
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] *= wht_c<D>();
 
+  // group absmax -> scale exponent (identical in every lane of the group)
   double m = 0.0;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) m = fmax(m, fabs(x[e]));
-  const int E = scale_exponent(m);
+  for (int e = 0; e < E; ++e) m = fmax(m, fabs(x[e]));
+  if constexpr (LPG > 1) m = fmax(m, quad_swap<1>(m));
+  if constexpr (LPG > 2) m = fmax(m, quad_swap<2>(m));
+  const int Ex = scale_exponent(m);
 
-  uint32_t w[4];
+  uint32_t w[E / 8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < E / 8; ++q) {
     uint32_t acc = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc |= e2m1_code(ldexp(x[8 * q + i], -E)) << (4 * i);
+    for (int i = 0; i < 8; ++i) acc |= e2m1_code(ldexp(x[8 * q + i], -Ex)) << (4 * i);
     w[q] = acc;
   }
   if (!in_range || slot < 0) return;
   const int page = slot >> 4, off = slot & 15;
-  const uint8_t scale_byte = (uint8_t)(E + 127);
+  const int g = p / LPG;                           // quantization group of this lane
+  const bool writes_scale = (p % LPG) == 0;
+  const uint8_t scale_byte = (uint8_t)(Ex + 127);
   if (!is_v) {
     uint8_t* blk = a.k_pool + (int64_t)page * a.page_bytes + (int64_t)h * BLK;
-    *reinterpret_cast<uint4*>(blk + off * (D / 2) + 16 * p) = make_uint4(w[0], w[1], w[2], w[3]);
-    blk[CODE + 4 * ((off & 3) * (D / 32) + p) + (off >> 2)] = scale_byte;   // [slot%4][group][slot/4]
+    if constexpr (E == 32) *reinterpret_cast<uint4*>(blk + off * (D / 2) + 16 * p) = make_uint4(w[0], w[1], w[2], w[3]);
+    else *reinterpret_cast<uint32_t*>(blk + off * (D / 2) + 4 * p) = w[0];
+    if (writes_scale) blk[CODE + 4 * ((off & 3) * (D / 32) + g) + (off >> 2)] = scale_byte;   // [slot%4][group][slot/4]
   } else {
     uint8_t* blk = a.v_pool + (int64_t)page * a.page_bytes + (int64_t)h * BLK;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {          // channel pair c = 16p + i, row 16 (c % CPL) + c / CPL
-      constexpr int CPL = D / 32;
-      const int c = 16 * p + i;
+    for (int i = 0; i < E / 2; ++i) {              // channel pair c = (E/2) p + i, row 16 (c % CPL) + c / CPL
+      const int c = (E / 2) * p + i;
       blk[(16 * (c % CPL) + c / CPL) * kPage + off] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
     }
-    blk[CODE + p * kPage + off] = scale_byte;
+    if (writes_scale) blk[CODE + g * kPage + off] = scale_byte;
   }
 }
 
@@ -166,14 +227,24 @@ static unsigned grid_rows(int64_t rows, int rows_per_wave) {
   return (unsigned)((waves + 3) / 4);
 }
 
+template <int D, int IN>
+static void launch_fp4_rows(const AppendArgs& a, int64_t rows, hipStream_t s) {
+  // D/8 lanes per row (8 channels each) while the rows fill less than about two
+  // waves per SIMD at D/32 lanes per row; D/32 lanes per row beyond that
+  constexpr int kFewRows = 256 * 4 * 2 * (64 / (D / 32));
+  if (rows < kFewRows) {
+    hipLaunchKernelGGL((append_fp4_kernel<D, IN, D / 8>), dim3(grid_rows(rows, 64 / (D / 8))), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((append_fp4_kernel<D, IN, D / 32>), dim3(grid_rows(rows, 64 / (D / 32))), dim3(256), 0, s, a);
+  }
+}
+
 hipError_t launch_append_fp4(const AppendArgs& a, int D, int in, hipStream_t s) {
   const int64_t rows = 2LL * a.T * a.H;
-  const int rpw = 64 / (D / 32);
-  const dim3 grid(grid_rows(rows, rpw)), block(256);
-  if (D == 128 && in == UQ_IN_BF16) hipLaunchKernelGGL((append_fp4_kernel<128, UQ_IN_BF16>), grid, block, 0, s, a);
-  else if (D == 128) hipLaunchKernelGGL((append_fp4_kernel<128, UQ_IN_F32>), grid, block, 0, s, a);
-  else if (in == UQ_IN_BF16) hipLaunchKernelGGL((append_fp4_kernel<64, UQ_IN_BF16>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((append_fp4_kernel<64, UQ_IN_F32>), grid, block, 0, s, a);
+  if (D == 128 && in == UQ_IN_BF16) launch_fp4_rows<128, UQ_IN_BF16>(a, rows, s);
+  else if (D == 128) launch_fp4_rows<128, UQ_IN_F32>(a, rows, s);
+  else if (in == UQ_IN_BF16) launch_fp4_rows<64, UQ_IN_BF16>(a, rows, s);
+  else launch_fp4_rows<64, UQ_IN_F32>(a, rows, s);
   return hipGetLastError();
 }
 
