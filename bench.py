@@ -109,7 +109,7 @@ def summarize_pmc(fetch_csv, write_csv, workload):
     out = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         vals = per_kernel(path, name)
-        dec = [v for k, v in vals.items() if "decode_kernel" in k and "Fp4Pol" in k]
+        dec = [v for k, v in vals.items() if "decode_kernel" in k and ("Fp4Pol" in k or "Fp4PairPol" in k)]
         cpy = [v for k, v in vals.items() if "copyBuffer" in k]
         if not dec or not cpy:
             raise SystemExit(f"{path}: no FP4 decode or copy dispatches for {name}")
@@ -121,7 +121,7 @@ def summarize_pmc(fetch_csv, write_csv, workload):
     f, w = out["FETCH_SIZE"], out["WRITE_SIZE"]
     traffic = int(round(f["kib"] * 1024 * f["factor"] + w["kib"] * 1024 * w["factor"]))
     lines = [
-        f"# HBM traffic of decode_kernel<Fp4Pol<128>> on {workload}",
+        f"# HBM traffic of the FP4 decode kernel on {workload}",
         "",
         "Counters from two rocprofv3 runs of the same program (one counter each), then",
         "`python3 bench.py --summarize-pmc <fetch csv> <write csv>`:",
@@ -383,7 +383,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(fp4["kernel_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(fp4["kernel_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic() if args.workload == "decode_gqa" else None,
-                     "kernel": "decode_kernel<Fp4Pol<128>>", "kernel_us": round(fp4["decode_kernel_ms"] * 1e3, 2),
+                     "kernel": "decode_kernel<Fp4PairPol<128>> (KV-head pairs)", "kernel_us": round(fp4["decode_kernel_ms"] * 1e3, 2),
                      "timing": "HIP events around each launch on its stream"
                                + (f", {args.scrub_mb} MB scrub between steps" if args.scrub_mb else ", steps back to back"),
                      "kernel_us_p10_p90": [round(fp4["decode_kernel_ms_p10"] * 1e3, 2),

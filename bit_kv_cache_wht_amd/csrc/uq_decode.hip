@@ -52,6 +52,11 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
+// One of a step's page ids (wave-uniform values) by a lane-dependent index.
+__device__ __forceinline__ int pick_id(const int (&ids)[4], int x) {
+  return x == 0 ? ids[0] : x == 1 ? ids[1] : x == 2 ? ids[2] : ids[3];
+}
+
 // Keep-masks for the slots of one page that are valid (slot < nvalid): bytes
 // (slot t = byte t of 16) and 16-bit halves (slot t = half t of 16).
 __device__ __forceinline__ uint32_t slot_bytes_kept(int nvalid, int first) {
@@ -96,6 +101,10 @@ template <int D> __device__ __forceinline__ v8i load_q_fp8(const uint8_t* qrow, 
 template <int D> struct Fp4Pol {
   static constexpr int kOcc = 2;        // waves per SIMD (256 registers each)
   static constexpr int kBuf = 2;        // K and V register buffers (steps of prefetch)
+  // one KV head per item; a step is 4 pages; lane (r, j) holds the 16 slots of page j
+  static constexpr int kNH = 1, kNP = 4, kTok = 16;
+  __device__ static int lane_page(int j4) { return j4; }
+  __device__ static int lane_slot0(int) { return 0; }
   static constexpr int kBlk = Fp4Block<D>::kBytes;
   static constexpr int kCode = Fp4Block<D>::kCodeBytes;
   static constexpr int kGroups = D / 32;
@@ -110,10 +119,12 @@ template <int D> struct Fp4Pol {
     uint4 vs;             // V scale bytes of that group, slots 0..15
   };
   struct QOp { v8i b; };
-  __device__ static void load_q(QOp& qo, const uint8_t* qrow, bool valid, int j4) {
+  __device__ static void load_q(QOp& qo, const uint8_t* qrow, bool valid, int j4, int) {
     qo.b = load_q_fp8<D>(qrow, valid, j4);
   }
-  __device__ static void load_k(KStep& st, const uint8_t* kb, int r16, int j4) {
+  __device__ static void load_k(KStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
+                                int64_t head_off, int r16, int j4) {
+    const uint8_t* kb = pool + (int64_t)pick_id(ids, r16 >> 2) * page_bytes + head_off;
     if (j4 < kGroups) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) st.kc[m] = load16(kb + (4 * m + (r16 & 3)) * (D / 2) + 16 * j4);
@@ -125,7 +136,9 @@ template <int D> struct Fp4Pol {
       st.ks = 0x7F7F7F7Fu;
     }
   }
-  __device__ static void load_v(VStep& st, const uint8_t* vb, int r16, int j4) {
+  __device__ static void load_v(VStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
+                                int64_t head_off, int r16, int j4) {
+    const uint8_t* vb = pool + (int64_t)pick_id(ids, j4) * page_bytes + head_off;
 #pragma unroll
     for (int q = 0; q < kCPL; ++q) st.vc[q] = load16(vb + (16 * q + r16) * kPage);   // pair kCPL*r16 + q
     st.vs = load16(vb + kCode + kPage * ((kCPL * r16) / 16));
@@ -155,7 +168,7 @@ template <int D> struct Fp4Pol {
     st.vs.z = (st.vs.z & k2) | (~k2 & 0x7F7F7F7Fu);
     st.vs.w = (st.vs.w & k3) | (~k3 & 0x7F7F7F7Fu);
   }
-  __device__ static void pv(const VStep& st, const v8h (&P)[2][2], v4f (&O)[kTiles]) {
+  __device__ static void pv(const VStep& st, const v8h (&P)[2][2], v4f (&O)[kTiles], int) {
     const uint32_t s[4] = {st.vs.x, st.vs.y, st.vs.z, st.vs.w};
     // The conversion reads only the exponent field of its float scale, so byte k
     // of a scale word only has to be shifted into bits 23..30; the bits around it
@@ -201,6 +214,143 @@ template <int D> struct Fp4Pol {
   __device__ static int channel(int tile, int j4, int v) { return 2 * (kCPL * (4 * j4 + v) + (tile >> 1)) + (tile & 1); }
 };
 
+// FP4 with two KV heads per item (GQA groups of up to 8 query heads, an even
+// number of KV heads).  A step is 2 pages of both heads, the same bytes as a
+// 4-page step of one head, and the 16 MFMA columns hold the query heads of both
+// KV heads (head X in columns X*G .. X*G + G - 1) instead of 8 real columns and 8
+// of padding: the softmax work per step halves, and the two heads' adjacent
+// head-blocks (2 x 17*d/2 bytes, whole cache lines for d = 128) are fetched by
+// the same wave at the same time.
+//   QK: for each of the step's two token rows-of-16 (mm), head 0's product with
+//       the query operand masked to head 0's columns plus head 1's masked to
+//       head 1's, in one accumulator: 4 scaled MFMAs.  Token row i of MFMA mm is
+//       page i >> 3, slot 8((i >> 2) & 1) + 4mm + (i & 3), so lane (h, j) of the
+//       result holds slots 8(j & 1) .. 8(j & 1) + 7 of page j >> 1.
+//   PV: per head and tile one f16 product pair over the step's 32 tokens, P
+//       masked to that head's columns.
+template <int D> struct Fp4PairPol {
+  static constexpr int kOcc = 2;
+  static constexpr int kBuf = 2;
+  static constexpr int kNH = 2, kNP = 2, kTok = 8;
+  __device__ static int lane_page(int j4) { return j4 >> 1; }
+  __device__ static int lane_slot0(int j4) { return 8 * (j4 & 1); }
+  static constexpr int kBlk = Fp4Block<D>::kBytes;
+  static constexpr int kCode = Fp4Block<D>::kCodeBytes;
+  static constexpr int kGroups = D / 32;
+  static constexpr int kCPL = D / 32;             // channel pairs per lane
+  static constexpr int kTiles = D / 16;
+  struct KStep {
+    uint4 kc[4];          // MFMA 2X + mm: head X, token row lane%16, group lane/16
+    uint32_t ks;          // byte 2X + mm: the scale of that row and group
+  };
+  struct VStep {
+    uint2 vc[2][kCPL];    // head X, channel pair kCPL*(lane%16) + q: slots 8(j&1)..+7 of page j>>1
+    uint2 vs[2];          // head X, scale bytes of that group, same slots
+  };
+  struct QOp { v8i b[2]; };   // the lane's query row if its column belongs to head X, else zero
+  __device__ static void load_q(QOp& qo, const uint8_t* qrow, bool valid, int j4, int lane_head) {
+    const v8i q = load_q_fp8<D>(qrow, valid, j4);
+    const v8i z = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    qo.b[0] = lane_head == 0 ? q : z;
+    qo.b[1] = lane_head == 1 ? q : z;
+  }
+  __device__ static void load_k(KStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
+                                int64_t head_off, int r16, int j4) {
+    const uint8_t* pg = pool + (int64_t)pick_id(ids, r16 >> 3) * page_bytes + head_off;
+    const int slot0 = 8 * ((r16 >> 2) & 1) + (r16 & 3);
+    if (j4 < kGroups) {
+      uint32_t d[2];
+#pragma unroll
+      for (int X = 0; X < 2; ++X) {
+        const uint8_t* kb = pg + X * kBlk;
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) st.kc[2 * X + mm] = load16(kb + (slot0 + 4 * mm) * (D / 2) + 16 * j4);
+        // scales are [slot % 4][group][slot / 4]; this lane needs slot / 4 = 2((r16 >> 2) & 1) + mm
+        d[X] = *reinterpret_cast<const uint32_t*>(kb + kCode + 4 * ((r16 & 3) * kGroups + j4));
+      }
+      st.ks = __builtin_amdgcn_perm(d[1], d[0], ((r16 >> 2) & 1) ? 0x07060302u : 0x05040100u);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) st.kc[m] = make_uint4(0, 0, 0, 0);
+      st.ks = 0x7F7F7F7Fu;
+    }
+  }
+  __device__ static void load_v(VStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
+                                int64_t head_off, int r16, int j4) {
+    const uint8_t* pg = pool + (int64_t)pick_id(ids, j4 >> 1) * page_bytes + head_off + 8 * (j4 & 1);
+#pragma unroll
+    for (int X = 0; X < 2; ++X) {
+      const uint8_t* vb = pg + X * kBlk;
+#pragma unroll
+      for (int q = 0; q < kCPL; ++q) st.vc[X][q] = *reinterpret_cast<const uint2*>(vb + (16 * q + r16) * kPage);
+      st.vs[X] = *reinterpret_cast<const uint2*>(vb + kCode + kPage * ((kCPL * r16) / 16));
+    }
+  }
+  template <int M> __device__ static v4f qk1(const KStep& st, const v8i& b, v4f c) {
+    const v8i a = v8i{(int)st.kc[M].x, (int)st.kc[M].y, (int)st.kc[M].z, (int)st.kc[M].w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4 /*A fp4*/, 0 /*B fp8*/, M, (int)st.ks, 0, 127);
+  }
+  __device__ static void qk(const KStep& st, const QOp& qo, v4f (&S)[2]) {
+    S[0] = qk1<2>(st, qo.b[1], qk1<0>(st, qo.b[0], v4f{0, 0, 0, 0}));
+    S[1] = qk1<3>(st, qo.b[1], qk1<1>(st, qo.b[0], v4f{0, 0, 0, 0}));
+  }
+  // Clears the value codes of slots past nvalid (of this lane's 8) and gives them
+  // scale byte 127.
+  __device__ static void mask_v(VStep& st, int nvalid) {
+    const uint32_t k0 = slot_bytes_kept(nvalid, 0), k1 = slot_bytes_kept(nvalid, 4);
+#pragma unroll
+    for (int X = 0; X < 2; ++X) {
+#pragma unroll
+      for (int q = 0; q < kCPL; ++q) {
+        st.vc[X][q].x &= k0;
+        st.vc[X][q].y &= k1;
+      }
+      st.vs[X].x = (st.vs[X].x & k0) | (~k0 & 0x7F7F7F7Fu);
+      st.vs[X].y = (st.vs[X].y & k1) | (~k1 & 0x7F7F7F7Fu);
+    }
+  }
+  __device__ static void pv(const VStep& st, const v8h (&P)[1][2], v4f (&O)[kTiles], int lane_head) {
+    const v8h z = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int X = 0; X < 2; ++X) {
+      const v8h PX[2] = {lane_head == X ? P[0][0] : z, lane_head == X ? P[0][1] : z};
+      // the conversion reads only the exponent field of its float scale
+      const uint32_t s2[2] = {st.vs[X].x, st.vs[X].y};
+      float sc[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int k = t & 3;
+        sc[t] = __uint_as_float(k == 3 ? s2[t >> 2] >> 1 : s2[t >> 2] << (23 - 8 * k));
+      }
+#pragma unroll
+      for (int q = 0; q < kCPL; ++q) {
+        const uint32_t c[2] = {st.vc[X][q].x, st.vc[X][q].y};
+        uint32_t Xv[8];   // slot t: (channel 2cp, channel 2cp + 1) scaled by 2^(byte_t - 127)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          v2h h;
+          switch (t & 3) {
+            case 0: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 0); break;
+            case 1: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 1); break;
+            case 2: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 2); break;
+            default: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 3); break;
+          }
+          Xv[t] = __builtin_bit_cast(uint32_t, h);
+        }
+        uint32_t ev[4], od[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ev[i] = __builtin_amdgcn_perm(Xv[2 * i + 1], Xv[2 * i], 0x05040100u);   // low halves: even channel
+          od[i] = __builtin_amdgcn_perm(Xv[2 * i + 1], Xv[2 * i], 0x07060302u);   // high halves: odd channel
+        }
+        O[2 * q] = mma2(__builtin_bit_cast(v8h, make_uint4(ev[0], ev[1], ev[2], ev[3])), PX, O[2 * q]);
+        O[2 * q + 1] = mma2(__builtin_bit_cast(v8h, make_uint4(od[0], od[1], od[2], od[3])), PX, O[2 * q + 1]);
+      }
+    }
+  }
+  __device__ static int channel(int tile, int j4, int v) { return 2 * (kCPL * (4 * j4 + v) + (tile >> 1)) + (tile & 1); }
+};
+
 // FP8 baseline.  QK runs on f16 MFMAs after an exact E4M3 -> f16 conversion:
 // the FP8 x FP8 MFMAs (16x16x128 scaled and 16x16x32) drop low-order bits of
 // small products when large ones are present in the same instruction, which
@@ -208,6 +358,10 @@ template <int D> struct Fp4Pol {
 template <int D> struct Fp8Pol {
   static constexpr int kOcc = 1;
   static constexpr int kBuf = 3;
+  // one KV head per item; a step is 4 pages; lane (r, j) holds the 16 slots of page j
+  static constexpr int kNH = 1, kNP = 4, kTok = 16;
+  __device__ static int lane_page(int j4) { return j4; }
+  __device__ static int lane_slot0(int) { return 0; }
   static constexpr int kBlk = kPage * D;
   static constexpr int kTiles = D / 16;
   static constexpr int kLanesK = D / 32;   // lane groups holding 32 channels of a row
@@ -222,7 +376,7 @@ template <int D> struct Fp8Pol {
     const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
     return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   }
-  __device__ static void load_q(QOp& qo, const uint8_t* qrow, bool valid, int j4) {
+  __device__ static void load_q(QOp& qo, const uint8_t* qrow, bool valid, int j4, int) {
     uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
     if (valid && j4 < kLanesK) {
       lo = load16(qrow + 32 * j4);
@@ -233,7 +387,9 @@ template <int D> struct Fp8Pol {
     qo.b[2] = cvt8(hi.x, hi.y);
     qo.b[3] = cvt8(hi.z, hi.w);
   }
-  __device__ static void load_k(KStep& st, const uint8_t* kb, int r16, int j4) {
+  __device__ static void load_k(KStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
+                                int64_t head_off, int r16, int j4) {
+    const uint8_t* kb = pool + (int64_t)pick_id(ids, r16 >> 2) * page_bytes + head_off;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int slot = 4 * m + (r16 & 3);
@@ -245,7 +401,9 @@ template <int D> struct Fp8Pol {
       }
     }
   }
-  __device__ static void load_v(VStep& st, const uint8_t* vb, int r16, int j4) {
+  __device__ static void load_v(VStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
+                                int64_t head_off, int r16, int j4) {
+    const uint8_t* vb = pool + (int64_t)pick_id(ids, j4) * page_bytes + head_off;
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) st.vc[t] = load16(vb + (16 * t + r16) * kPage);
   }
@@ -269,7 +427,7 @@ template <int D> struct Fp8Pol {
       st.vc[t].x &= k0; st.vc[t].y &= k1; st.vc[t].z &= k2; st.vc[t].w &= k3;
     }
   }
-  __device__ static void pv(const VStep& st, const v8h (&P)[2][2], v4f (&O)[kTiles]) {
+  __device__ static void pv(const VStep& st, const v8h (&P)[2][2], v4f (&O)[kTiles], int) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       const uint32_t c[4] = {st.vc[t].x, st.vc[t].y, st.vc[t].z, st.vc[t].w};
@@ -293,6 +451,10 @@ template <int D> struct Fp8Pol {
 template <int D> struct Bf16Pol {
   static constexpr int kOcc = 1;
   static constexpr int kBuf = 2;
+  // one KV head per item; a step is 4 pages; lane (r, j) holds the 16 slots of page j
+  static constexpr int kNH = 1, kNP = 4, kTok = 16;
+  __device__ static int lane_page(int j4) { return j4; }
+  __device__ static int lane_slot0(int) { return 0; }
   static constexpr int kBlk = kPage * D * 2;
   static constexpr int kTiles = D / 16;
   static constexpr int kK = D / 32;     // 16x16x32 MFMAs per token row
@@ -308,12 +470,14 @@ template <int D> struct Bf16Pol {
   __device__ static v8h bf2h8(const uint4& u) {
     return __builtin_bit_cast(v8h, make_uint4(bf2h(u.x), bf2h(u.y), bf2h(u.z), bf2h(u.w)));
   }
-  __device__ static void load_q(QOp& qo, const uint8_t* qrow, bool valid, int j4) {
+  __device__ static void load_q(QOp& qo, const uint8_t* qrow, bool valid, int j4, int) {
 #pragma unroll
     for (int kk = 0; kk < kK; ++kk)
       qo.b[kk] = bf2h8(valid ? load16(qrow + 2 * (32 * kk + 8 * j4)) : make_uint4(0, 0, 0, 0));
   }
-  __device__ static void load_k(KStep& st, const uint8_t* kb, int r16, int j4) {
+  __device__ static void load_k(KStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
+                                int64_t head_off, int r16, int j4) {
+    const uint8_t* kb = pool + (int64_t)pick_id(ids, r16 >> 2) * page_bytes + head_off;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int slot = 4 * m + (r16 & 3);
@@ -321,7 +485,9 @@ template <int D> struct Bf16Pol {
       for (int kk = 0; kk < kK; ++kk) st.k[m][kk] = load16(kb + 2 * (slot * D + 32 * kk + 8 * j4));
     }
   }
-  __device__ static void load_v(VStep& st, const uint8_t* vb, int r16, int j4) {
+  __device__ static void load_v(VStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
+                                int64_t head_off, int r16, int j4) {
+    const uint8_t* vb = pool + (int64_t)pick_id(ids, j4) * page_bytes + head_off;
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       st.v[t][0] = load16(vb + 2 * ((16 * t + r16) * kPage));
@@ -354,7 +520,7 @@ template <int D> struct Bf16Pol {
         st.v[t][half].z &= k[4 * half + 2]; st.v[t][half].w &= k[4 * half + 3];
       }
   }
-  __device__ static void pv(const VStep& st, const v8h (&P)[2][2], v4f (&O)[kTiles]) {
+  __device__ static void pv(const VStep& st, const v8h (&P)[2][2], v4f (&O)[kTiles], int) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
 #pragma unroll
@@ -371,7 +537,8 @@ template <int D> struct Bf16Pol {
 // The work of a call is the list of steps (4 pages) of all (sequence b, KV head
 // hk) items, items in the order b * Hkv + hk.  Every workgroup derives in LDS
 // sbase[b] = first step of item (b, 0), each item of sequence b having
-// steps(b) = ceil(pages(b) / 4) steps, and sbase[B] = T, the total.  Workgroup w
+// steps(b) = ceil(pages(b) / NP) steps (NP = 4, or 2 for KV-head pairs), and
+// sbase[B] = T, the total.  Workgroup w
 // then takes steps [w T / grid, (w + 1) T / grid): equal shares whatever the
 // mix of lengths, items cut at share boundaries being merged across workgroups.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -388,18 +555,19 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 __device__ __forceinline__ int clamp_len(int L, int max_pages) {
   return L < 0 ? 0 : (L > max_pages * kPage ? max_pages * kPage : L);
 }
-__device__ __forceinline__ int seq_steps(int L) { return ((L + kPage - 1) / kPage + 3) >> 2; }
+template <int NP> __device__ __forceinline__ int seq_steps(int L) { return ((L + kPage - 1) / kPage + NP - 1) / NP; }
 
-// Run by all 64 * NW threads; red: NW ints of scratch.
-template <int NW>
-__device__ void wg_plan(const int32_t* __restrict__ seq_lens, int B, int Hkv, int max_pages, int32_t* sbase,
+// Run by all 64 * NW threads; red: NW ints of scratch.  Steps are NP pages;
+// each sequence has Hi items (KV heads, or KV-head pairs).
+template <int NW, int NP>
+__device__ void wg_plan(const int32_t* __restrict__ seq_lens, int B, int Hi, int max_pages, int32_t* sbase,
                         int32_t* red) {
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t carry = 0;
   for (int b0 = 0; b0 < B; b0 += NT) {
     const int b = b0 + tid;
-    const int ns = b < B ? seq_steps(clamp_len(seq_lens[b], max_pages)) * Hkv : 0;
+    const int ns = b < B ? seq_steps<NP>(clamp_len(seq_lens[b], max_pages)) * Hi : 0;
     const int incl = wave_incl_scan(ns, lane);
     if (lane == 63) red[wave] = incl;
     __syncthreads();
@@ -531,8 +699,8 @@ struct KArgs {
   int32_t B, Hq, Hkv, G;
   float scale_log2;          // sm_scale * log2(e)
   float* out;                // [B][Hq][D]
-  float* ml;                 // [2 * grid][G][2] partial (m in log2 units, l) of cut items
-  float* po;                 // [2 * grid][G][D] partial O of cut items
+  float* ml;                 // [2 * grid][16][2] partial (m in log2 units, l) of cut items
+  float* po;                 // [2 * grid][16][D] partial O of cut items
   int32_t* cnt;              // [B][Hkv] arrival counters, zero between calls
   int32_t R;                 // items per round of a workgroup
 };
@@ -602,7 +770,9 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
   constexpr int N = Pol::kBuf;
   constexpr int PER = D / 64;
   extern __shared__ __align__(16) uint8_t smem[];
-  const int G = a.G;
+  constexpr int NP = Pol::kNP, TOK = Pol::kTok;
+  const int G = a.G * Pol::kNH;      // query rows (MFMA columns) of an item
+  const int Hi = a.Hkv / Pol::kNH;   // items per sequence
   const Lds lay(a.R, NW, G, D, ESZ, a.B);
   uint8_t* qs = smem + lay.qs;
   float* so = reinterpret_cast<float*>(smem + lay.so);
@@ -617,7 +787,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, j4 = lane >> 4;
-  wg_plan<NW>(seq_lens, a.B, a.Hkv, a.max_pages, base, red);
+  wg_plan<NW, NP>(seq_lens, a.B, Hi, a.max_pages, base, red);
   const int64_t T = base[a.B];
   // shares go to the first min(gridDim.x, T) workgroups, so that none is empty
   // and the workgroups holding steps of an item are consecutive
@@ -635,29 +805,29 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         const int mid = (lo + hi) >> 1;
         if (base[mid] <= g_cur) lo = mid; else hi = mid;
       }
-      const int steps = (base[lo + 1] - base[lo]) / a.Hkv;
-      f0 = lo * a.Hkv + (int)((g_cur - base[lo]) / steps);
+      const int steps = (base[lo + 1] - base[lo]) / Hi;
+      f0 = lo * Hi + (int)((g_cur - base[lo]) / steps);
     }
     auto item_start = [&](int f) -> int64_t {
-      const int b = f / a.Hkv;
-      return base[b] + (int64_t)(f - b * a.Hkv) * ((base[b + 1] - base[b]) / a.Hkv);
+      const int b = f / Hi;
+      return base[b] + (int64_t)(f - b * Hi) * ((base[b + 1] - base[b]) / Hi);
     };
     int nR = 1;
-    while (nR < a.R && f0 + nR < a.B * a.Hkv && item_start(f0 + nR) < g_hi) ++nR;
+    while (nR < a.R && f0 + nR < a.B * Hi && item_start(f0 + nR) < g_hi) ++nR;
     if (tid < nR) {
       const int f = f0 + tid;
-      const int b = f / a.Hkv;
-      const int hk = f - b * a.Hkv;
-      const int steps = (base[b + 1] - base[b]) / a.Hkv;
+      const int b = f / Hi;
+      const int hk = f - b * Hi;
+      const int steps = (base[b + 1] - base[b]) / Hi;
       const int64_t start = item_start(f), end = start + steps;
       const int64_t s_lo = start > g_cur ? start : g_cur, s_hi = end < g_hi ? end : g_hi;
       const int L = clamp_len(seq_lens[b], a.max_pages);
       const int pages = (L + kPage - 1) / kPage;
-      const int p_begin = 4 * (int)(s_lo - start);
+      const int p_begin = NP * (int)(s_lo - start);
       int32_t* r = rec + 8 * tid;
       r[kRecB] = b;
       r[kRecPBegin] = p_begin;
-      r[kRecNpg] = max(min(pages - p_begin, 4 * (int)(s_hi - s_lo)), 0);
+      r[kRecNpg] = max(min(pages - p_begin, NP * (int)(s_hi - s_lo)), 0);
       r[kRecHk] = hk;
       r[kRecLRel] = L - p_begin * kPage;
       r[kRecNStep] = (int)max(s_hi - s_lo, (int64_t)0);
@@ -666,7 +836,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
       r[kRecNContrib] = partial ? owner(end - 1) - owner(start) + 1 : 1;
     }
     {
-      const int64_t e = item_start(f0 + nR - 1) + (base[(f0 + nR - 1) / a.Hkv + 1] - base[(f0 + nR - 1) / a.Hkv]) / a.Hkv;
+      const int64_t e = item_start(f0 + nR - 1) + (base[(f0 + nR - 1) / Hi + 1] - base[(f0 + nR - 1) / Hi]) / Hi;
       g_cur = e < g_hi ? e : g_hi;               // next round starts after the last segment
     }
     for (int i = tid; i < nR * NW * G; i += NT) smx[i] = -INFINITY;
@@ -731,19 +901,16 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
       // vector-memory counter of the key/value loads
       const int32_t* pt = page_table + (int64_t)b * a.max_pages + p_begin;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) c.ids[x] = pt[min(4 * s + x, npg - 1)];
-      const bool full = (4 * s + 4 <= npg) && ((4 * s + 4) * kPage <= lrel);
+      for (int x = 0; x < 4; ++x) c.ids[x] = x < NP ? pt[min(NP * s + x, npg - 1)] : 0;
+      const bool full = (NP * s + NP <= npg) && ((NP * s + NP) * kPage <= lrel);
       c.meta = (full ? 1 << 28 : 0) | (k << 20) | s;
       return c;
     };
-    auto pick = [](const Claim& c, int x) {
-      return x == 0 ? c.ids[0] : x == 1 ? c.ids[1] : x == 2 ? c.ids[2] : c.ids[3];
-    };
     auto load_k = [&](typename Pol::KStep& st, const Claim& c) {
-      Pol::load_k(st, a.k_pool + (int64_t)pick(c, r16 >> 2) * a.page_bytes + (int64_t)c.hk * Pol::kBlk, r16, j4);
+      Pol::load_k(st, a.k_pool, c.ids, a.page_bytes, (int64_t)c.hk * (Pol::kNH * Pol::kBlk), r16, j4);
     };
     auto load_v = [&](typename Pol::VStep& st, const Claim& c) {
-      Pol::load_v(st, a.v_pool + (int64_t)pick(c, j4) * a.page_bytes + (int64_t)c.hk * Pol::kBlk, r16, j4);
+      Pol::load_v(st, a.v_pool, c.ids, a.page_bytes, (int64_t)c.hk * (Pol::kNH * Pol::kBlk), r16, j4);
     };
 
     // ---- prologue: N K and N - 1 V buffers.  K is consumed by the QK at the
@@ -776,6 +943,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
 
     // ---- running state of the item the wave is on
     typename Pol::QOp qo;
+    const int lane_head = r16 / a.G;   // which KV head of the item this lane's column belongs to
     float m_run = -INFINITY, l_run = 0.f;
     v4f O[Pol::kTiles];
     int acc_k = -1;
@@ -801,7 +969,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
       l_run = 0.f;
 #pragma unroll
       for (int t = 0; t < Pol::kTiles; ++t) O[t] = v4f{0, 0, 0, 0};
-      Pol::load_q(qo, qs + (k * G + r16) * D * ESZ, r16 < G, j4);
+      Pol::load_q(qo, qs + (k * G + r16) * D * ESZ, r16 < G, j4, lane_head);
       acc_k = k;
     };
 
@@ -810,35 +978,36 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     // -inf and value zero; the masking is applied on every step (all slots valid
     // on full ones), which costs a few ALU operations but keeps a single copy of
     // the step code and its register allocation.
-    auto finish_step = [&](v4f (&S)[4], typename Pol::VStep& st, int s, bool full) {
-      int nvalid = kPage;                          // valid slots of page 4s + j4 of the item
+    auto finish_step = [&](v4f (&S)[TOK / 4], typename Pol::VStep& st, int s, bool full) {
+      int nvalid = TOK;                            // valid ones among this lane's TOK slots
       if (!full) {
         const int npg = rec[8 * acc_k + kRecNpg], lrel = rec[8 * acc_k + kRecLRel];
-        const int pj = 4 * s + j4;
-        nvalid = pj < npg ? min(kPage, lrel - pj * kPage) : 0;
+        const int pj = NP * s + Pol::lane_page(j4);
+        const int in_page = pj < npg ? min(kPage, lrel - pj * kPage) : 0;
+        nvalid = min(max(in_page - Pol::lane_slot0(j4), 0), TOK);
       }
-      float t[16];
+      float t[TOK];
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < TOK / 4; ++m)
 #pragma unroll
         for (int v = 0; v < 4; ++v) t[4 * m + v] = 4 * m + v < nvalid ? S[m][v] : -INFINITY;
       // Conditional rescaling: exponents are taken against the running reference
-      // m_run as long as every lane's 16 probabilities sum to at most 2^8 (so each
+      // m_run as long as every lane's probabilities sum to at most 2^8 (so each
       // p <= 2^8, well inside float16).  Otherwise (a logit above the reference by
       // more than 8 binades, the first step, or a NaN from -inf - -inf) the
       // reference is raised to the row maximum across the 4 lanes of the row, l
       // and O are rescaled and the probabilities recomputed.
       float neg_mc = -m_run * a.scale_log2;
-      float pf[16];
+      float pf[TOK];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
+      for (int i = 0; i < TOK; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
       float psum = pf[0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) psum += pf[i];
+      for (int i = 1; i < TOK; ++i) psum += pf[i];
       if (__any(!(psum <= 256.f))) {
         float mx = t[0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, t[i]);
+        for (int i = 1; i < TOK; ++i) mx = fmaxf(mx, t[i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
@@ -849,15 +1018,15 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         m_run = m_new;
         neg_mc = -m_run * a.scale_log2;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
+        for (int i = 0; i < TOK; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
         psum = pf[0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) psum += pf[i];
+        for (int i = 1; i < TOK; ++i) psum += pf[i];
       }
       l_run += psum;
-      v8h Pm[2][2];
+      v8h Pm[TOK / 8][2];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      for (int half = 0; half < TOK / 8; ++half) {
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) split_f16x2(pf[8 * half + 2 * i], pf[8 * half + 2 * i + 1], hw[i], lw[i]);
@@ -865,7 +1034,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         Pm[half][1] = __builtin_bit_cast(v8h, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
       Pol::mask_v(st, nvalid);
-      Pol::pv(st, Pm, O);
+      Pol::pv(st, Pm, O, lane_head);
     };
 
     for (;;) {
@@ -879,7 +1048,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
           begin_item(kc);
         }
         load_v(vst[(i + N - 1) % N], cv);        // V of step + N - 1
-        v4f S[4];
+        v4f S[TOK / 4];
         Pol::qk(kst[i], qo, S);
         load_k(kst[i], ck);                      // K of step + N
         cv = ck;
@@ -943,7 +1112,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         const int32_t* r = rec + 8 * tid;
         int is_last = 0;
         if (r[kRecSlot] >= 0) {
-          int32_t* c = a.cnt + (int64_t)r[kRecB] * a.Hkv + r[kRecHk];
+          int32_t* c = a.cnt + (int64_t)r[kRecB] * Hi + r[kRecHk];
           const int old = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           is_last = old == r[kRecNContrib] - 1;
           if (is_last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -956,7 +1125,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         if (!flags[k]) continue;
         const int32_t* r = rec + 8 * k;
         const int b = r[kRecB], hk = r[kRecHk];
-        const int steps = (base[b + 1] - base[b]) / a.Hkv;
+        const int steps = (base[b + 1] - base[b]) / Hi;
         const int64_t start = base[b] + (int64_t)hk * steps;
         const int w0 = owner(start), n = r[kRecNContrib];
         // partial of contributor w0 + i: slot 2w if the item begins its share, else 2w + 1
@@ -1030,7 +1199,7 @@ hipError_t launch_one(const DecodeArgs& a, const KArgs& k0, hipStream_t s) {
   constexpr int NW = 4 * Pol::kOcc;
   constexpr int ESZ = FMT == UQ_KV_BF16 ? 2 : 1;
   const DeviceLimits dl = device_limits();
-  const int G = a.Hq / a.Hkv;
+  const int G = a.Hq / a.Hkv * Pol::kNH;   // rows of an item
   const int grid = dl.cus < kMaxGrid ? dl.cus : kMaxGrid;
   // segments per round: as many as fit in LDS (the share of a workgroup usually
   // spans a few items)
@@ -1071,7 +1240,13 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   hipError_t e;
   if (a.ev_start != nullptr && (e = hipEventRecord(a.ev_start, s)) != hipSuccess) return e;
   const bool bf = a.q_dtype == UQ_IN_BF16;
-  if (a.format == UQ_KV_FP4) {
+  if (a.format == UQ_KV_FP4 && k.G <= 8 && a.Hkv % 2 == 0) {
+    // KV-head pairs fill the 16 MFMA columns
+    if (a.unrotate) e = bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP4, true, Fp4PairPol<D>>(a, k, s)
+                           : launch_one<D, UQ_IN_F32, UQ_KV_FP4, true, Fp4PairPol<D>>(a, k, s);
+    else e = bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP4, false, Fp4PairPol<D>>(a, k, s)
+                : launch_one<D, UQ_IN_F32, UQ_KV_FP4, false, Fp4PairPol<D>>(a, k, s);
+  } else if (a.format == UQ_KV_FP4) {
     if (a.unrotate) e = bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP4, true, Fp4Pol<D>>(a, k, s)
                            : launch_one<D, UQ_IN_F32, UQ_KV_FP4, true, Fp4Pol<D>>(a, k, s);
     else e = bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP4, false, Fp4Pol<D>>(a, k, s)
@@ -1091,7 +1266,8 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
 
 DecodeLayout decode_layout(int format, int B, int Hq, int Hkv, int D) {
   (void)format;
-  const size_t G = (size_t)(Hq / Hkv);
+  (void)Hq;
+  const size_t G = 16;   // rows of an item, at most (query heads per KV head, or per KV-head pair)
   DecodeLayout L;
   size_t off = 0;
   L.cnt = off; off = align256(off + sizeof(int32_t) * (size_t)B * Hkv);
