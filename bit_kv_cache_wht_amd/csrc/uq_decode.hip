@@ -561,13 +561,15 @@ template <int NP> __device__ __forceinline__ int seq_steps(int L) { return ((L +
 // each sequence has Hi items (KV heads, or KV-head pairs).
 template <int NW, int NP>
 __device__ void wg_plan(const int32_t* __restrict__ seq_lens, int B, int Hi, int max_pages, int32_t* sbase,
-                        int32_t* red) {
+                        int32_t* lens, int32_t* red) {
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t carry = 0;
   for (int b0 = 0; b0 < B; b0 += NT) {
     const int b = b0 + tid;
-    const int ns = b < B ? seq_steps<NP>(clamp_len(seq_lens[b], max_pages)) * Hi : 0;
+    const int L = b < B ? clamp_len(seq_lens[b], max_pages) : 0;
+    if (b < B) lens[b] = L;
+    const int ns = b < B ? seq_steps<NP>(L) * Hi : 0;
     const int incl = wave_incl_scan(ns, lane);
     if (lane == 63) red[wave] = incl;
     __syncthreads();
@@ -729,8 +731,9 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 //   rec    [R][8]          item records (int)
 //   misc   [32]            step counter, per-item flags, plan scratch (int)
 //   base   [B + 1]         plan (int)
+//   lens   [B]             sequence lengths as used (int)
 struct Lds {
-  int qs, so, sm, sl, rec, misc, base, total;
+  int qs, so, sm, sl, rec, misc, base, lens, total;
   __host__ __device__ static int up16(int x) { return (x + 15) & ~15; }
   __host__ __device__ Lds(int R, int NW, int G, int D, int esz, int B) {
     qs = 0;
@@ -740,7 +743,8 @@ struct Lds {
     rec = up16(sl + R * NW * G * 4);
     misc = up16(rec + R * 8 * 4);
     base = up16(misc + 32 * 4);
-    total = up16(base + (B + 1) * 4);
+    lens = up16(base + (B + 1) * 4);
+    total = up16(lens + B * 4);
   }
 };
 
@@ -781,87 +785,105 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
   int32_t* rec = reinterpret_cast<int32_t*>(smem + lay.rec);
   int32_t* misc = reinterpret_cast<int32_t*>(smem + lay.misc);
   int32_t* base = reinterpret_cast<int32_t*>(smem + lay.base);
+  int32_t* lens = reinterpret_cast<int32_t*>(smem + lay.lens);
   int32_t* ctr = misc;            // step counter of the round
   int32_t* flags = misc + 1;      // [kMaxR] last-split flags
   int32_t* red = misc + 16;       // [2 * NW] plan scratch
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, j4 = lane >> 4;
-  wg_plan<NW, NP>(seq_lens, a.B, Hi, a.max_pages, base, red);
-  const int64_t T = base[a.B];
+  if (tid == 0) *ctr = 0;                          // ordered before the first claim by the plan's barriers
+  wg_plan<NW, NP>(seq_lens, a.B, Hi, a.max_pages, base, lens, red);
+  const int T = base[a.B];                       // < 2^31: the host bounds the step count
   // shares go to the first min(gridDim.x, T) workgroups, so that none is empty
   // and the workgroups holding steps of an item are consecutive
-  const int grid = (int)(T < (int64_t)gridDim.x ? T : (int64_t)gridDim.x), wg = blockIdx.x;
-  auto share_begin = [&](int w) -> int64_t { return (int64_t)w * T / grid; };
-  auto owner = [&](int64_t g) -> int { return (int)(((g + 1) * grid - 1) / T); };   // w with g in its share
-  const int64_t g_hi = wg < grid ? share_begin(wg + 1) : 0;
+  const int grid = T < (int)gridDim.x ? T : (int)gridDim.x, wg = blockIdx.x;
+  // share_begin(w) = floor(w T / grid), from T = sq * grid + sr (w * sr < 2^20)
+  const int sq = grid > 0 ? T / grid : 0, sr = T - sq * grid;
+  auto share_begin = [&](int w) -> int { return w * sq + (w * sr) / grid; };
+  auto owner = [&](int g) -> int {              // the w whose share holds step g
+    int w = (int)((float)g * ((float)grid / (float)T));   // off by at most a few
+    w = w < 0 ? 0 : (w >= grid ? grid - 1 : w);
+    while (share_begin(w) > g) --w;
+    while (w + 1 < grid && share_begin(w + 1) <= g) ++w;
+    return w;
+  };
+  const int g_hi = wg < grid ? share_begin(wg + 1) : 0;
 
-  for (int64_t g_cur = wg < grid ? share_begin(wg) : 0; g_cur < g_hi;) {
-    // ---- round set-up: segments k = 0 .. nR-1 are items f0 + k clipped to the share
+  for (int g_cur = wg < grid ? share_begin(wg) : 0; g_cur < g_hi;) {
+    // ---- round set-up: segments k = 0 .. nR-1 are items f0 + k clipped to the
+    // share.  Every wave derives them itself, segment k in its lane k, so no
+    // barrier is needed before the claims; wave 0 also stores them in LDS for the
+    // masked steps and the merge (read after the barriers below).
     int f0;
     {
-      int lo = 0, hi = a.B;                      // b: last index with sbase[b] <= g_cur (non-empty)
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (base[mid] <= g_cur) lo = mid; else hi = mid;
+      // b: the last index with sbase[b] <= g_cur (a non-empty sequence), found
+      // 64 candidates at a time with a ballot
+      int lo = 0, n = a.B;                       // candidates lo .. lo + n - 1
+      while (n > 1) {
+        const int stride = (n + 63) / 64;
+        const int c = lo + lane * stride;
+        const int cnt = __builtin_popcountll(__ballot(lane * stride < n && base[c] <= g_cur));
+        lo += (cnt - 1) * stride;
+        n = min(stride, n - (cnt - 1) * stride);
       }
       const int steps = (base[lo + 1] - base[lo]) / Hi;
-      f0 = lo * Hi + (int)((g_cur - base[lo]) / steps);
+      f0 = lo * Hi + (g_cur - base[lo]) / steps;
     }
-    auto item_start = [&](int f) -> int64_t {
-      const int b = f / Hi;
-      return base[b] + (int64_t)(f - b * Hi) * ((base[b + 1] - base[b]) / Hi);
-    };
-    int nR = 1;
-    while (nR < a.R && f0 + nR < a.B * Hi && item_start(f0 + nR) < g_hi) ++nR;
-    if (tid < nR) {
-      const int f = f0 + tid;
-      const int b = f / Hi;
-      const int hk = f - b * Hi;
-      const int steps = (base[b + 1] - base[b]) / Hi;
-      const int64_t start = item_start(f), end = start + steps;
-      const int64_t s_lo = start > g_cur ? start : g_cur, s_hi = end < g_hi ? end : g_hi;
-      const int L = clamp_len(seq_lens[b], a.max_pages);
-      const int pages = (L + kPage - 1) / kPage;
-      const int p_begin = NP * (int)(s_lo - start);
-      int32_t* r = rec + 8 * tid;
-      r[kRecB] = b;
-      r[kRecPBegin] = p_begin;
-      r[kRecNpg] = max(min(pages - p_begin, NP * (int)(s_hi - s_lo)), 0);
-      r[kRecHk] = hk;
-      r[kRecLRel] = L - p_begin * kPage;
-      r[kRecNStep] = (int)max(s_hi - s_lo, (int64_t)0);
-      const bool partial = s_lo > start || s_hi < end;
-      r[kRecSlot] = partial ? 2 * wg + (share_begin(wg) >= start ? 0 : 1) : -1;
-      r[kRecNContrib] = partial ? owner(end - 1) - owner(start) + 1 : 1;
+    int sg_b = 0, sg_hk = 0, sg_pbeg = 0, sg_npg = 0, sg_lrel = 0, sg_nstep = 0, sg_slot = -1, sg_ncontrib = 1;
+    int sg_end = 0;
+    bool sg_ok = false;
+    {
+      const int f = f0 + lane;
+      if (lane < a.R && f < a.B * Hi) {
+        const int b = f / Hi;
+        const int hk = f - b * Hi;
+        const int steps = (base[b + 1] - base[b]) / Hi;
+        const int start = base[b] + hk * steps, end = start + steps;
+        sg_ok = lane == 0 || start < g_hi;
+        const int s_lo = start > g_cur ? start : g_cur, s_hi = end < g_hi ? end : g_hi;
+        const int L = lens[b];
+        const int pages = (L + kPage - 1) / kPage;
+        sg_b = b;
+        sg_hk = hk;
+        sg_pbeg = NP * (s_lo - start);
+        sg_npg = max(min(pages - sg_pbeg, NP * (s_hi - s_lo)), 0);
+        sg_lrel = L - sg_pbeg * kPage;
+        sg_nstep = max(s_hi - s_lo, 0);
+        const bool partial = s_lo > start || s_hi < end;
+        sg_slot = partial ? 2 * wg + (share_begin(wg) >= start ? 0 : 1) : -1;
+        sg_ncontrib = partial ? owner(end - 1) - owner(start) + 1 : 1;
+        sg_end = end;
+      }
+    }
+    const int nR = __builtin_popcountll(__ballot(sg_ok));   // valid segments are lanes 0 .. nR-1
+    if (lane >= nR) sg_nstep = 0;
+    const int sg_incl = wave_incl_scan(sg_nstep, lane);
+    const int sg_first = sg_incl - sg_nstep;                 // first step of segment `lane` in the round
+    const int T = __builtin_amdgcn_readlane(sg_incl, nR - 1);
+    if (wave == 0 && lane < nR) {
+      int32_t* r = rec + 8 * lane;
+      r[kRecB] = sg_b;
+      r[kRecPBegin] = sg_pbeg;
+      r[kRecNpg] = sg_npg;
+      r[kRecHk] = sg_hk;
+      r[kRecLRel] = sg_lrel;
+      r[kRecNStep] = sg_nstep;
+      r[kRecSlot] = sg_slot;
+      r[kRecNContrib] = sg_ncontrib;
     }
     {
-      const int64_t e = item_start(f0 + nR - 1) + (base[(f0 + nR - 1) / Hi + 1] - base[(f0 + nR - 1) / Hi]) / Hi;
+      const int e = __builtin_amdgcn_readlane(sg_end, nR - 1);
       g_cur = e < g_hi ? e : g_hi;               // next round starts after the last segment
     }
-    for (int i = tid; i < nR * NW * G; i += NT) smx[i] = -INFINITY;
-    if (tid == 0) *ctr = 0;
-    __syncthreads();
-
-    // first step of each item of the round (ps[k] = T for k >= nR)
-    int ps[kMaxR + 1];
-    {
-      int acc = 0;
-#pragma unroll
-      for (int k = 0; k < kMaxR; ++k) {
-        ps[k] = acc;
-        if (k < nR) acc += __builtin_amdgcn_readfirstlane(rec[8 * k + kRecNStep]);
-      }
-      ps[kMaxR] = acc;
-    }
-    const int T = ps[kMaxR];
+    for (int i = tid; i < nR * NW * G; i += NT) smx[i] = -INFINITY;   // parks come after the barrier below
 
     // query rows of the round, row r = k * G + h; the first pass's loads go out
     // ahead of the key/value prologue
     const int nrows = nR * G;
-    auto qrow_of = [&](int r) -> int64_t {
+    auto qrow_of = [&](int r) -> int64_t {       // r < nrows; segment r / G's record from its lane
       const int k = r / G, h = r - k * G;
-      return (int64_t)rec[8 * k + kRecB] * a.Hq + (int64_t)rec[8 * k + kRecHk] * G + h;
+      return (int64_t)__shfl(sg_b, k) * a.Hq + (int64_t)__shfl(sg_hk, k) * G + h;
     };
     const int qr0 = tid >> 4, qp = tid & 15;
     QueryRows<D, IN, FMT> qrows;
@@ -873,11 +895,17 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
       int hk;
       int ids[4];        // page ids of the step's 4 pages (page 0 of the pool when none)
     };
-    auto claim = [&]() {
-      Claim c;
+    // A claim takes the next step index from the LDS counter, then reads the
+    // step's page ids.  The prologue takes all its indices first: LDS and
+    // scalar-memory results share one completion counter, so an index taken
+    // after a page-table read would wait for that read.
+    auto take = [&]() {
       int g = 0;
       if (lane == 0) g = atomicAdd(ctr, 1);
-      g = __builtin_amdgcn_readlane(g, 0);
+      return __builtin_amdgcn_readlane(g, 0);
+    };
+    auto claim_at = [&](int g) {
+      Claim c;
       if (g >= T) {
         c.meta = -1;
         c.hk = 0;
@@ -885,18 +913,14 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         for (int x = 0; x < 4; ++x) c.ids[x] = 0;
         return c;
       }
-      int k = 0, pk = 0;
-#pragma unroll
-      for (int j = 1; j < kMaxR; ++j) k += g >= ps[j] ? 1 : 0;
-#pragma unroll
-      for (int j = 0; j < kMaxR; ++j) pk = j == k ? ps[j] : pk;
-      const int s = g - pk;
-      const int32_t* r = rec + 8 * k;
-      const int b = __builtin_amdgcn_readfirstlane(r[kRecB]);
-      const int p_begin = __builtin_amdgcn_readfirstlane(r[kRecPBegin]);
-      const int npg = __builtin_amdgcn_readfirstlane(r[kRecNpg]);
-      const int lrel = __builtin_amdgcn_readfirstlane(r[kRecLRel]);
-      c.hk = __builtin_amdgcn_readfirstlane(r[kRecHk]);
+      // segment k: the last one whose first step is <= g
+      const int k = __builtin_popcountll(__ballot(lane >= 1 && lane < nR && sg_first <= g));
+      const int s = g - __builtin_amdgcn_readlane(sg_first, k);
+      const int b = __builtin_amdgcn_readlane(sg_b, k);
+      const int p_begin = __builtin_amdgcn_readlane(sg_pbeg, k);
+      const int npg = __builtin_amdgcn_readlane(sg_npg, k);
+      const int lrel = __builtin_amdgcn_readlane(sg_lrel, k);
+      c.hk = __builtin_amdgcn_readlane(sg_hk, k);
       // wave-uniform page-table reads: scalar loads, outside the in-order
       // vector-memory counter of the key/value loads
       const int32_t* pt = page_table + (int64_t)b * a.max_pages + p_begin;
@@ -906,6 +930,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
       c.meta = (full ? 1 << 28 : 0) | (k << 20) | s;
       return c;
     };
+    auto claim = [&]() { return claim_at(take()); };
     auto load_k = [&](typename Pol::KStep& st, const Claim& c) {
       Pol::load_k(st, a.k_pool, c.ids, a.page_bytes, (int64_t)c.hk * (Pol::kNH * Pol::kBlk), r16, j4);
     };
@@ -922,16 +947,23 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     typename Pol::VStep vst[N];
     int meta[N + 1];               // meta[j]: step j after the current one
     Claim cv, ck;                  // next V load (step + N - 1) and next K load (step + N)
+    Claim c0[N];                   // all page-table reads go out before the first key/value load
+    int g0[N + 1];
+#pragma unroll
+    for (int i = 0; i <= N; ++i) g0[i] = take();
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const Claim c = claim();
-      meta[i] = c.meta;
-      load_k(kst[i], c);
-      if (i < N - 1) load_v(vst[i], c);
-      if (i == N - 1) cv = c;
+      c0[i] = claim_at(g0[i]);
+      meta[i] = c0[i].meta;
     }
-    ck = claim();
+    ck = claim_at(g0[N]);
     meta[N] = ck.meta;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      load_k(kst[i], c0[i]);
+      if (i < N - 1) load_v(vst[i], c0[i]);
+    }
+    cv = c0[N - 1];
 
     if (qr0 < nrows) qrows.finish(qs + qr0 * D * ESZ, qp);
     for (int r = qr0 + NT / 16; r < nrows; r += NT / 16) {
@@ -1126,7 +1158,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         const int32_t* r = rec + 8 * k;
         const int b = r[kRecB], hk = r[kRecHk];
         const int steps = (base[b + 1] - base[b]) / Hi;
-        const int64_t start = base[b] + (int64_t)hk * steps;
+        const int start = base[b] + hk * steps;
         const int w0 = owner(start), n = r[kRecNContrib];
         // partial of contributor w0 + i: slot 2w if the item begins its share, else 2w + 1
         auto prow_of = [&](int i) -> int64_t {
@@ -1165,6 +1197,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         store_row<D, UNROT>(o, l, a.out + ((int64_t)b * a.Hq + (int64_t)hk * G + h) * D, lane);
       }
     }
+    if (tid == 0) *ctr = 0;                        // every claim of this round is done (barrier above)
     __syncthreads();                               // LDS is reused by the next round
   }
 
