@@ -5,7 +5,10 @@ the CPU oracle.
 One step is one pass of the hot path over a batch: append the new token of every
 sequence to the paged cache (rotate + quantize + pack for FP4) and run decode
 attention over the whole context (query rotation to E4M3, split-K attention,
-merge + inverse rotation).  Default workload: 64 sequences x 8,192 context,
+merge + inverse rotation).  The FP4 step is one launch of the fused entry point
+(uq_append_decode_attention) when every sequence adds one token; the FP8 / BF16
+baselines (append kernel, then decode kernel) are reported beside it, and with
+--unfused the FP4 step as two launches as well.  Default workload: 64 sequences x 8,192 context,
 64 query heads / 8 KV heads, head_dim 128, 16-token pages randomly permuted.
 
 Prints one JSON line.  Progress goes to stderr.
@@ -39,6 +42,8 @@ def parse():
     ap.add_argument("--workload", default="decode_gqa", choices=["decode_gqa", "long", "ragged", "tiny"])
     ap.add_argument("--no-baselines", action="store_true", help="skip the FP8/BF16 KV kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="also time the FP4 step as two launches (append kernel, then decode kernel)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle sample")
     ap.add_argument("--scrub-mb", type=int, default=0,
                     help="read a buffer of this size between the event-timed steps (evicts the last-level cache)")
@@ -61,7 +66,7 @@ def make_workload(name):
 
 
 DECODE_SOURCES = ["bit_kv_cache_wht_amd/csrc/uq_decode.hip", "bit_kv_cache_wht_amd/csrc/uq_device.h",
-                  "bit_kv_cache_wht_amd/csrc/uq_internal.h"]
+                  "bit_kv_cache_wht_amd/csrc/uq_fp4_row.h", "bit_kv_cache_wht_amd/csrc/uq_internal.h"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_fp4_64x8192_hbm_traffic.md")
 COPY_BYTES = 1 << 30
 
@@ -121,7 +126,7 @@ def summarize_pmc(fetch_csv, write_csv, workload):
     f, w = out["FETCH_SIZE"], out["WRITE_SIZE"]
     traffic = int(round(f["kib"] * 1024 * f["factor"] + w["kib"] * 1024 * w["factor"]))
     lines = [
-        f"# HBM traffic of the FP4 decode kernel on {workload}",
+        f"# HBM traffic of the FP4 decode kernel (fused step) on {workload}",
         "",
         "Counters from two rocprofv3 runs of the same program (one counter each), then",
         "`python3 bench.py --summarize-pmc <fetch csv> <write csv>`:",
@@ -148,7 +153,7 @@ def pmc_pass(args):
     import torch
     torch.cuda.set_device(0)
     wl = make_workload(args.workload)
-    r = Runner("fp4", wl)
+    r = Runner("fp4", wl, fused=True)
     for _ in range(args.warmup + args.steps):
         r.step()
     torch.cuda.synchronize()
@@ -201,7 +206,7 @@ class HipEvents:
 class Runner:
     """Holds device buffers for one format and runs steps through the C ABI."""
 
-    def __init__(self, fmt, wl):
+    def __init__(self, fmt, wl, fused=False):
         import torch
         import bit_kv_cache_wht_amd as uq
         self.fmt, self.wl, self.uq, self.torch = fmt, wl, uq, torch
@@ -228,9 +233,20 @@ class Runner:
         self.ws = torch.zeros(uq.uq_decode_workspace_bytes(self.cache, wl.batch, wl.num_q_heads,
                                                            wl.page_table.shape[1]), dtype=torch.uint8, device="cuda")
         self.sm_scale = float(np.float32(1.0 / np.sqrt(d)))
+        # the fused step writes one token per sequence, at position seq_lens[b] - 1
+        self.fused = fused and fmt == "fp4" and bool(np.all(wl.new_lens == 1))
+        if self.fused:
+            self.k_new = self.k_new.reshape(wl.batch, wl.num_kv_heads, d)
+            self.v_new = self.v_new.reshape(wl.batch, wl.num_kv_heads, d)
         torch.cuda.synchronize()
 
     def step(self, ev=None):
+        if self.fused:
+            if ev is not None:
+                self.uq.uq_profile_next_decode(ev[0], ev[1])
+            self.uq.uq_append_decode_attention(self.cache, self.k_new, self.v_new, self.q, self.page_table,
+                                               self.seq_lens, self.sm_scale, self.out, self.ws)
+            return
         self.append(self.cache, self.k_new, self.v_new, self.slots_new)
         if ev is not None:
             self.uq.uq_profile_next_decode(ev[0], ev[1])
@@ -271,13 +287,18 @@ class Runner:
     def kernel_bytes(self):
         """Algorithmic bytes of one launch of the split-K attention kernel: every
         cached K/V byte of every context token once, the query operand and the
-        page-table entries; split partials are overhead and not counted."""
+        page-table entries, and for the fused step the new tokens' K/V rows read
+        and their cache bytes written; split partials are overhead and not
+        counted."""
         wl = self.wl
         d = wl.head_dim
         tok_heads = int(np.sum(wl.seq_lens.astype(np.int64))) * wl.num_kv_heads
         kv = tok_heads * KV_BYTES[self.fmt](d)
         q = wl.batch * wl.num_q_heads * d * (2 if self.fmt == "bf16" else 1)
         pt = int(np.sum((wl.seq_lens.astype(np.int64) + 15) // 16)) * 4
+        if self.fused:
+            in_bytes = 2 if wl.in_dtype == "bf16" else 4
+            pt += wl.batch * wl.num_kv_heads * (2 * d * in_bytes + KV_BYTES["fp4"](d))
         return kv + q + pt, kv
 
 
@@ -344,10 +365,10 @@ def main():
     log(f"workload ready in {time.perf_counter() - t:.1f}s: B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
         f"d={wl.head_dim} tokens={wl.total_tokens}")
     results = {}
-    fmts = ["fp4"] if args.no_baselines else ["fp4", "fp8", "bf16"]
+    fmts = ["fp4"] + ([] if args.no_baselines else ["fp8", "bf16"]) + (["fp4_unfused"] if args.unfused else [])
     for fmt in fmts:
         log(f"{fmt}: prefill + timing")
-        r = Runner(fmt, wl)
+        r = Runner(fmt.split("_")[0], wl, fused=fmt == "fp4")
         scrub = torch.ones((args.scrub_mb << 20) // 4, dtype=torch.int32, device="cuda") if args.scrub_mb else None
         res = r.run(args.steps, args.warmup, scrub)
         del scrub
@@ -355,6 +376,7 @@ def main():
         res["kernel_gbs"] = algo / (res["decode_kernel_ms"] * 1e-3) / 1e9
         res["kernel_algo_bytes"] = algo
         res["kv_bytes"] = kv
+        res["fused"] = r.fused
         results[fmt] = res
         log(f"{fmt}: {1e3 * res['ms_per_step']:.1f} us/step, decode kernel {1e3 * res['decode_kernel_ms']:.1f} us "
             f"= {res['kernel_gbs']:.0f} GB/s")
@@ -362,6 +384,7 @@ def main():
         torch.cuda.empty_cache()
 
     fp4 = results["fp4"]
+    fused_fp4 = fp4["fused"]
     line = {
         "metric": METRIC,
         "value": round(fp4["ms_per_step"] * 1e3, 2),
@@ -377,13 +400,15 @@ def main():
         "data": "synthetic (seeded Gaussian K/V with outlier channels, permuted pages)",
         "config": {"workload": f"{wl.name}: {wl.batch} seq x {int(wl.seq_lens.max())} ctx, {wl.num_q_heads} q heads / "
                                f"{wl.num_kv_heads} kv heads, head_dim {wl.head_dim}, 16-token pages permuted; step = "
-                               f"FP4 append of 1 new token per seq + decode",
+                               f"FP4 append of the new token(s) of every seq + decode"
+                               + (" in one fused launch" if fused_fp4 else ""),
                    "global_batch": wl.batch, "seq_len": int(wl.seq_lens.max()), "parallelism": "none (1 GPU)"},
         "kv_gbs_per_step": round(fp4["kv_bytes"] / (fp4["ms_per_step"] * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(fp4["kernel_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(fp4["kernel_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic() if args.workload == "decode_gqa" else None,
-                     "kernel": "decode_kernel<Fp4PairPol<128>> (KV-head pairs)", "kernel_us": round(fp4["decode_kernel_ms"] * 1e3, 2),
+                     "kernel": "decode_kernel<Fp4PairPol<128>> (KV-head pairs" + (", fused append)" if fused_fp4 else ")"),
+                     "kernel_us": round(fp4["decode_kernel_ms"] * 1e3, 2),
                      "timing": "HIP events around each launch on its stream"
                                + (f", {args.scrub_mb} MB scrub between steps" if args.scrub_mb else ", steps back to back"),
                      "kernel_us_p10_p90": [round(fp4["decode_kernel_ms_p10"] * 1e3, 2),

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     lib,
     uq_append_bf16,
     uq_append_fp8,
+    uq_append_decode_attention,
     uq_decode_attention,
     uq_decode_attention_bf16,
     uq_decode_attention_fp8,

@@ -44,6 +44,8 @@ _SIGS = {
     "uq_rotate_quantize_query": (ctypes.c_int, [_P, _I, _P, _I, _I, _P]),
     "uq_decode_workspace_bytes": (_SZ, [_CP, _I, _I, _I]),
     "uq_decode_attention": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
+    "uq_append_decode_attention": (ctypes.c_int, [_CP, _P, _P, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ,
+                                                  _U, _P]),
     "uq_decode_attention_fp8": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
     "uq_decode_attention_bf16": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
     "uq_profile_next_decode": (ctypes.c_int, [_P, _P]),
@@ -197,6 +199,23 @@ def uq_decode_attention(cache, q, page_table, seq_lens, sm_scale, out, workspace
     """FP4 decode: q [B][H_q][d], page_table int32 [B][max_pages], seq_lens int32 [B],
     out float32 [B][H_q][d], workspace uint8 >= uq_decode_workspace_bytes."""
     _decode("uq_decode_attention", cache, q, page_table, seq_lens, sm_scale, out, workspace, flags, stream)
+
+
+def uq_append_decode_attention(cache, k_new, v_new, q, page_table, seq_lens, sm_scale, out, workspace, flags=0,
+                               stream=None) -> None:
+    """Fused FP4 step: writes k_new / v_new [B][H_kv][d] (the dtype of q) at position
+    seq_lens[b] - 1 of each sequence, then decodes as uq_decode_attention."""
+    _contig(k_new, v_new, q, page_table, seq_lens, out, workspace)
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise TypeError("uq_append_decode_attention: k_new, v_new and q must share one dtype")
+    c = cache.c()
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().uq_append_decode_attention(ctypes.byref(c), _ptr(k_new), _ptr(v_new), _ptr(q), _dtype_code(q),
+                                          _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens), B, Hq,
+                                          float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, flags,
+                                          _stream(stream))
+    _check("uq_append_decode_attention", st)
 
 
 def uq_decode_attention_fp8(cache, q, page_table, seq_lens, sm_scale, out, workspace, flags=0, stream=None) -> None:

@@ -55,7 +55,7 @@ int append_common(const uq_kv_cache* cache, int format, const void* k_new, const
 int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q_dtype, const int32_t* page_table,
                   int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
                   float sm_scale, float* out, void* workspace, size_t workspace_bytes, uint32_t flags,
-                  uq_stream_t stream) {
+                  uq_stream_t stream, const void* k_new = nullptr, const void* v_new = nullptr) {
   int st = check_cache(cache, format);
   if (st != UQ_OK) return st;
   const uint32_t allowed = format == UQ_KV_FP4 ? UQ_FLAG_OUT_ROTATED : 0u;
@@ -73,6 +73,7 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   if (!(sm_scale > 0.f) || sm_scale > 3.0e38f) return UQ_ERR_INVALID_ARG;   // NaN, <= 0, inf
   if (num_seqs == 0) return UQ_OK;
   if (q == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr) return UQ_ERR_INVALID_ARG;
+  if ((k_new == nullptr) != (v_new == nullptr)) return UQ_ERR_INVALID_ARG;
   const size_t need = uq_decode_workspace_bytes(cache, num_seqs, num_q_heads, max_pages_per_seq);
   if (workspace == nullptr || workspace_bytes < need) return UQ_ERR_WORKSPACE;
   uq::DecodeArgs a;
@@ -94,6 +95,8 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   a.ws = static_cast<uint8_t*>(workspace);
   a.lay = uq::decode_layout(format, num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim);
   a.unrotate = format == UQ_KV_FP4 && !(flags & UQ_FLAG_OUT_ROTATED);
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.ev_start = g_prof_start;
   a.ev_stop = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
@@ -161,6 +164,16 @@ int uq_decode_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtype
                         uq_stream_t stream) {
   return decode_common(cache, UQ_KV_FP4, q, q_dtype, page_table, max_pages_per_seq, seq_lens, num_seqs, num_q_heads,
                        sm_scale, out, workspace, workspace_bytes, flags, stream);
+}
+
+int uq_append_decode_attention(const uq_kv_cache* cache, const void* k_new, const void* v_new, const void* q,
+                               int32_t in_dtype, const int32_t* page_table, int32_t max_pages_per_seq,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, float sm_scale,
+                               float* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                               uq_stream_t stream) {
+  if (num_seqs > 0 && (k_new == nullptr || v_new == nullptr)) return UQ_ERR_INVALID_ARG;
+  return decode_common(cache, UQ_KV_FP4, q, in_dtype, page_table, max_pages_per_seq, seq_lens, num_seqs, num_q_heads,
+                       sm_scale, out, workspace, workspace_bytes, flags, stream, k_new, v_new);
 }
 
 int uq_decode_attention_fp8(const uq_kv_cache* cache, const void* q, int32_t q_dtype, const int32_t* page_table,

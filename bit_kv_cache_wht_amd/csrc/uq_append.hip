@@ -10,40 +10,21 @@
 // lane owns the same channels of the rotated row, so group absmax, scale,
 // rounding and packing need at most a max across the lanes of a group.
 #include "uq_device.h"
+#include "uq_fp4_row.h"
 #include "uq_internal.h"
 
 namespace uq {
 
 // FP4 write path ([review] §3.1; [commentary] footnote 2): WHT, group absmax,
-// UE8M0 scale byte, E2M1 codes, two codes per byte, paged store.
+// UE8M0 scale byte, E2M1 codes, two codes per byte, paged store (Fp4Row).
 //
-// LPR lanes share a row, lane part p holding E = D / LPR consecutive channels
-// E*p .. E*p + E - 1.  LPR = D / 32 (E = 32: one quantization group per lane) for
-// large batches; LPR = D / 8 (E = 8, four lanes per group) when few rows are written,
-// which cuts the float64 work each lane does on its own.  Butterfly stages h < E
-// run inside the lane, stages h >= E between lanes p and p ^ (h / E); every sum
-// is exact in float64, so the results do not depend on the split.
-
-// Partner value of lane ^ M (M < 16, within the row's lane group).
-template <int M> __device__ __forceinline__ double lane_xor(double v) {
-  if constexpr (M == 1 || M == 2) return quad_swap<M>(v);
-  else return __shfl_xor(v, M);
-}
-
-template <int E, int M> __device__ __forceinline__ void cross_stage(double (&x)[E], int p) {
-  const double sgn = (p & M) ? -1.0 : 1.0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) x[e] = __builtin_fma(x[e], sgn, lane_xor<M>(x[e]));
-}
-
+// LPR = D / 32 lanes per row (E = 32: one quantization group per lane) for large
+// batches; LPR = D / 8 (E = 8, four lanes per group) when few rows are written,
+// which cuts the float64 work each lane does on its own.
 template <int D, int IN, int LPR>
 __global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
-  constexpr int E = D / LPR;                       // channels per lane
-  constexpr int LPG = 32 / E;                      // lanes per quantization group
+  using Row = Fp4Row<D, IN, LPR>;
   constexpr int RPW = 64 / LPR;
-  constexpr int BLK = Fp4Block<D>::kBytes;
-  constexpr int CODE = Fp4Block<D>::kCodeBytes;
-  constexpr int CPL = D / 32;                      // V: channel pairs per PV lane row group
   const int lane = threadIdx.x & 63;
   const int p = lane % LPR;
   const int64_t nrows = 2LL * a.T * a.H;
@@ -58,79 +39,14 @@ __global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
   const int t = (int)(tr / a.H), h = (int)(tr - (int64_t)t * a.H);
   const int slot = a.slot_mapping[t];
 
-  double x[E];
-  {
-    const void* base = is_v ? a.v : a.k;
-    const int64_t elem = tr * D + E * p;
-    if constexpr (E == 32) {
-      load_row32<IN>(base, elem, x);
-    } else if constexpr (IN == UQ_IN_BF16) {
-      const uint4 u = load16(static_cast<const uint16_t*>(base) + elem);
-      const uint32_t d[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16_bits_to_f64(d[i] & 0xFFFFu);
-        x[2 * i + 1] = bf16_bits_to_f64(d[i] >> 16);
-      }
-    } else {
-      const float4* q4 = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
-      const float4 f0 = q4[0], f1 = q4[1];
-      x[0] = f0.x; x[1] = f0.y; x[2] = f0.z; x[3] = f0.w; x[4] = f1.x; x[5] = f1.y; x[6] = f1.z; x[7] = f1.w;
-    }
-  }
-  // normalized Sylvester WHT
-#pragma unroll
-  for (int hh = 1; hh < E; hh <<= 1)
-#pragma unroll
-    for (int i = 0; i < E; i += 2 * hh)
-#pragma unroll
-      for (int j = i; j < i + hh; ++j) {
-        const double a0 = x[j], a1 = x[j + hh];
-        x[j] = a0 + a1;
-        x[j + hh] = a0 - a1;
-      }
-  if constexpr (LPR > 1) cross_stage<E, 1>(x, p);
-  if constexpr (LPR > 2) cross_stage<E, 2>(x, p);
-  if constexpr (LPR > 4) cross_stage<E, 4>(x, p);
-  if constexpr (LPR > 8) cross_stage<E, 8>(x, p);
-#pragma unroll
-  for (int e = 0; e < E; ++e) x[e] *= wht_c<D>();
-
-  // group absmax -> scale exponent (identical in every lane of the group)
-  double m = 0.0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) m = fmax(m, fabs(x[e]));
-  if constexpr (LPG > 1) m = fmax(m, quad_swap<1>(m));
-  if constexpr (LPG > 2) m = fmax(m, quad_swap<2>(m));
-  const int Ex = scale_exponent(m);
-
-  uint32_t w[E / 8];
-#pragma unroll
-  for (int q = 0; q < E / 8; ++q) {
-    uint32_t acc = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc |= e2m1_code(ldexp(x[8 * q + i], -Ex)) << (4 * i);
-    w[q] = acc;
-  }
+  Row x;
+  x.load(is_v ? a.v : a.k, tr, p);
+  x.quantize(p);
   if (!in_range || slot < 0) return;
   const int page = slot >> 4, off = slot & 15;
-  const int g = p / LPG;                           // quantization group of this lane
-  const bool writes_scale = (p % LPG) == 0;
-  const uint8_t scale_byte = (uint8_t)(Ex + 127);
-  if (!is_v) {
-    uint8_t* blk = a.k_pool + (int64_t)page * a.page_bytes + (int64_t)h * BLK;
-    if constexpr (E == 32) *reinterpret_cast<uint4*>(blk + off * (D / 2) + 16 * p) = make_uint4(w[0], w[1], w[2], w[3]);
-    else *reinterpret_cast<uint32_t*>(blk + off * (D / 2) + 4 * p) = w[0];
-    if (writes_scale) blk[CODE + 4 * ((off & 3) * (D / 32) + g) + (off >> 2)] = scale_byte;   // [slot%4][group][slot/4]
-  } else {
-    uint8_t* blk = a.v_pool + (int64_t)page * a.page_bytes + (int64_t)h * BLK;
-#pragma unroll
-    for (int i = 0; i < E / 2; ++i) {              // channel pair c = (E/2) p + i, row 16 (c % CPL) + c / CPL
-      const int c = (E / 2) * p + i;
-      blk[(16 * (c % CPL) + c / CPL) * kPage + off] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
-    }
-    if (writes_scale) blk[CODE + g * kPage + off] = scale_byte;
-  }
+  uint8_t* blk = (is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes + (int64_t)h * Row::BLK;
+  if (!is_v) x.store_k(blk, off, p);
+  else x.store_v(blk, off, p);
 }
 
 // Baseline writes: one thread per 8 channels of a (token, head, K|V) row.

@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "uq_device.h"
+#include "uq_fp4_row.h"
 #include "uq_internal.h"
 
 
@@ -691,6 +692,16 @@ __device__ void store_row(float (&o)[D / 64], float l, float* dst, int lane) {
   for (int k = 0; k < PER; ++k) dst[lane + 64 * k] = o[k];
 }
 
+// Quantizes and stores a row of the fused step's newest token.
+template <class Row>
+__device__ __forceinline__ void write_new(Row& row, uint8_t* blk, int off, bool live, bool is_v, int p) {
+  row.quantize(p);
+  if (live) {
+    if (is_v) row.store_v(blk, off, p);
+    else row.store_k(blk, off, p);
+  }
+}
+
 // ------------------------------------------------------------------ decode
 struct KArgs {
   const uint8_t* k_pool;
@@ -705,6 +716,8 @@ struct KArgs {
   float* po;                 // [2 * grid][16][D] partial O of cut items
   int32_t* cnt;              // [B][Hkv] arrival counters, zero between calls
   int32_t R;                 // items per round of a workgroup
+  const void* k_new;         // fused step (FP4): the newest token's K and V, [B][Hkv][D]
+  const void* v_new;         // in the query's dtype; null: attention only
 };
 
 // Split partials cross workgroups that may sit on different compute dies,
@@ -832,7 +845,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     }
     int sg_b = 0, sg_hk = 0, sg_pbeg = 0, sg_npg = 0, sg_lrel = 0, sg_nstep = 0, sg_slot = -1, sg_ncontrib = 1;
     int sg_end = 0;
-    bool sg_ok = false;
+    bool sg_ok = false, sg_new = false;
     {
       const int f = f0 + lane;
       if (lane < a.R && f < a.B * Hi) {
@@ -854,10 +867,11 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         sg_slot = partial ? 2 * wg + (share_begin(wg) >= start ? 0 : 1) : -1;
         sg_ncontrib = partial ? owner(end - 1) - owner(start) + 1 : 1;
         sg_end = end;
+        sg_new = s_hi == end && L > 0;           // the item's last step, holding its newest token
       }
     }
     const int nR = __builtin_popcountll(__ballot(sg_ok));   // valid segments are lanes 0 .. nR-1
-    if (lane >= nR) sg_nstep = 0;
+    if (lane >= nR) sg_nstep = 0, sg_new = false;
     const int sg_incl = wave_incl_scan(sg_nstep, lane);
     const int sg_first = sg_incl - sg_nstep;                 // first step of segment `lane` in the round
     const int T = __builtin_amdgcn_readlane(sg_incl, nR - 1);
@@ -888,6 +902,51 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     const int qr0 = tid >> 4, qp = tid & 15;
     QueryRows<D, IN, FMT> qrows;
     qrows.load(a.q, qr0 < nrows ? qrow_of(qr0) : 0, qr0 < nrows, qp);
+
+    // ---- fused step: the newest token of each item whose last step is in this
+    // round is written here, by wave k for segment k (rows: the item's kNH K
+    // heads, then its V heads, D/8 lanes per row).  Only the wave that claims
+    // that last step reads the page slot, and the claim comes after one of the
+    // barriers below: the one before the main loop when the step's index in the
+    // round is past the NW * (N + 1) indices taken in the prologue, else one
+    // right after the write, before any claim.
+    using NewRow = Fp4Row<D, IN, D / 8>;
+    NewRow nrow;
+    uint8_t* nblk = nullptr;
+    int noff = 0;
+    bool nwrite = false;               // this wave has a row to write (row lanes: nlive)
+    int np = 0;                        // lane part of the lane's row
+    bool nlive = false, nv = false;    // the lane's row exists / is a V row
+    if constexpr (FMT == UQ_KV_FP4) {
+      static_assert(kMaxR <= NW, "segment k of a round is written by wave k");
+      if (a.k_new != nullptr) {
+        const uint64_t nm = __ballot(sg_new);
+        if ((nm >> wave) & 1) {
+          nwrite = true;
+          int ln = lane;                   // opaque: the lane-dependent addresses are formed here, not
+          asm volatile("" : "+v"(ln));     // kept in registers across rounds
+          const int nr = ln / (D / 8);
+          np = ln % (D / 8);
+          nlive = nr < 2 * Pol::kNH;
+          nv = nr >= Pol::kNH;
+          const int b = __builtin_amdgcn_readlane(sg_b, wave), it = __builtin_amdgcn_readlane(sg_hk, wave);
+          const int t = lens[b] - 1;
+          const int page = page_table[(int64_t)b * a.max_pages + (t >> 4)];
+          const int head = Pol::kNH * it + (nlive ? nr % Pol::kNH : 0);
+          nrow.load(nv && nlive ? a.v_new : a.k_new, (int64_t)b * a.Hkv + head, np);
+          nblk = const_cast<uint8_t*>(nv && nlive ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes +
+                 (int64_t)head * NewRow::BLK;
+          noff = t & 15;
+        }
+        if (__ballot(sg_new && sg_first + sg_nstep <= NW * (N + 1)) != 0) {
+          if (nwrite) {
+            write_new(nrow, nblk, noff, nlive, nv, np);
+            nwrite = false;
+          }
+          __syncthreads();
+        }
+      }
+    }
 
     // ---- step claims
     struct Claim {
@@ -958,6 +1017,9 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     }
     ck = claim_at(g0[N]);
     meta[N] = ck.meta;
+    if constexpr (FMT == UQ_KV_FP4) {
+      if (nwrite) write_new(nrow, nblk, noff, nlive, nv, np);   // ordered before the main loop's claims by its barrier
+    }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       load_k(kst[i], c0[i]);
@@ -1270,6 +1332,8 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   k.ml = reinterpret_cast<float*>(a.ws + L.ml);
   k.po = reinterpret_cast<float*>(a.ws + L.po);
   k.cnt = reinterpret_cast<int32_t*>(a.ws + L.cnt);
+  k.k_new = a.k_new;
+  k.v_new = a.v_new;
   hipError_t e;
   if (a.ev_start != nullptr && (e = hipEventRecord(a.ev_start, s)) != hipSuccess) return e;
   const bool bf = a.q_dtype == UQ_IN_BF16;

@@ -1,0 +1,120 @@
+// FP4 write of one (token, KV head) row of K or of V ([review] §3.1;
+// [commentary] footnote 2), spread over LPR consecutive lanes of a wave: lane
+// part p holds channels E*p .. E*p + E - 1 (E = D / LPR).  The append kernel and
+// the fused decode step both write through this code, so a token gets the same
+// bytes whichever entry point stores it.
+//
+// [review] = "[arXiv 2606.20474] UltraQuant: 컨텍스트가 긴 에이전트를 위한 4비트 KV 캐싱"
+//            (manon006.tistory.com/395)
+// [commentary] = pheeree.github.io "kv-cache-4bit-serving-residency-collapse"
+//
+// Butterfly stages h < E run inside the lane, stages h >= E between lanes p and
+// p ^ (h / E); every sum is exact in float64, so the result does not depend on
+// the split.  After the butterfly each lane owns the same channels of the rotated
+// row, so group absmax, scale, rounding and packing need at most a max across the
+// LPG = 32 / E lanes of a group.
+#pragma once
+#include "uq_device.h"
+
+namespace uq {
+
+// Partner value of lane ^ M (M < 16, within the row's lane group).
+template <int M> __device__ __forceinline__ double lane_xor(double v) {
+  if constexpr (M == 1 || M == 2) return quad_swap<M>(v);
+  else return __shfl_xor(v, M);
+}
+
+template <int E, int M> __device__ __forceinline__ void cross_stage(double (&x)[E], int p) {
+  const double sgn = (p & M) ? -1.0 : 1.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = __builtin_fma(x[e], sgn, lane_xor<M>(x[e]));
+}
+
+template <int D, int IN, int LPR> struct Fp4Row {
+  static constexpr int E = D / LPR;                       // channels per lane
+  static constexpr int LPG = 32 / E;                      // lanes per quantization group
+  static constexpr int BLK = Fp4Block<D>::kBytes;
+  static constexpr int CODE = Fp4Block<D>::kCodeBytes;
+  static constexpr int CPL = D / 32;                      // V: channel pairs per PV lane row group
+  static constexpr int NU = E * (IN == UQ_IN_BF16 ? 2 : 4) / 16;
+  uint4 raw[NU];                                          // the lane's input bits
+  uint32_t w[E / 8];                                      // packed codes, channel E*p + i in nibble i
+  int ex;                                                 // scale exponent of the lane's group
+
+  // Input channels E*p .. of row `row` of a [rows][D] array (bf16 bits or f32).
+  __device__ __forceinline__ void load(const void* src, int64_t row, int p) {
+    const uint8_t* b = static_cast<const uint8_t*>(src) + (row * D + E * p) * (IN == UQ_IN_BF16 ? 2 : 4);
+#pragma unroll
+    for (int i = 0; i < NU; ++i) raw[i] = load16(b + 16 * i);
+  }
+
+  // Normalized WHT, group absmax, UE8M0 exponent and E2M1 codes (all lanes of
+  // the row call it together).
+  __device__ __forceinline__ void quantize(int p) {
+    double x[E];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const uint32_t d[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (IN == UQ_IN_BF16) {
+          x[8 * i + 2 * j] = bf16_bits_to_f64(d[j] & 0xFFFFu);
+          x[8 * i + 2 * j + 1] = bf16_bits_to_f64(d[j] >> 16);
+        } else {
+          x[4 * i + j] = (double)__uint_as_float(d[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 1; hh < E; hh <<= 1)
+#pragma unroll
+      for (int i = 0; i < E; i += 2 * hh)
+#pragma unroll
+        for (int j = i; j < i + hh; ++j) {
+          const double a0 = x[j], a1 = x[j + hh];
+          x[j] = a0 + a1;
+          x[j + hh] = a0 - a1;
+        }
+    if constexpr (LPR > 1) cross_stage<E, 1>(x, p);
+    if constexpr (LPR > 2) cross_stage<E, 2>(x, p);
+    if constexpr (LPR > 4) cross_stage<E, 4>(x, p);
+    if constexpr (LPR > 8) cross_stage<E, 8>(x, p);
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] *= wht_c<D>();
+
+    double m = 0.0;                                       // group absmax, the same in every lane of the group
+#pragma unroll
+    for (int e = 0; e < E; ++e) m = fmax(m, fabs(x[e]));
+    if constexpr (LPG > 1) m = fmax(m, quad_swap<1>(m));
+    if constexpr (LPG > 2) m = fmax(m, quad_swap<2>(m));
+    ex = scale_exponent(m);
+#pragma unroll
+    for (int q = 0; q < E / 8; ++q) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc |= e2m1_code(ldexp(x[8 * q + i], -ex)) << (4 * i);
+      w[q] = acc;
+    }
+  }
+
+  // Stores into the K head block `blk` at page slot `off`: codes [slot][D/2],
+  // scales [slot % 4][group][slot / 4].
+  __device__ __forceinline__ void store_k(uint8_t* blk, int off, int p) const {
+    if constexpr (E == 32) *reinterpret_cast<uint4*>(blk + off * (D / 2) + 16 * p) = make_uint4(w[0], w[1], w[2], w[3]);
+    else *reinterpret_cast<uint32_t*>(blk + off * (D / 2) + 4 * p) = w[0];
+    if (p % LPG == 0) blk[CODE + 4 * ((off & 3) * (D / 32) + p / LPG) + (off >> 2)] = (uint8_t)(ex + 127);
+  }
+
+  // Stores into the V head block `blk` at page slot `off`: channel pair c in
+  // code row 16 (c % CPL) + c / CPL, column `off`; scales [group][slot].
+  __device__ __forceinline__ void store_v(uint8_t* blk, int off, int p) const {
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
+      const int c = (E / 2) * p + i;
+      blk[(16 * (c % CPL) + c / CPL) * kPage + off] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+    }
+    if (p % LPG == 0) blk[CODE + (p / LPG) * kPage + off] = (uint8_t)(ex + 127);
+  }
+};
+
+}  // namespace uq

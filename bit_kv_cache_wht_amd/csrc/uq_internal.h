@@ -51,6 +51,8 @@ struct DecodeArgs {
   uint8_t* ws;
   DecodeLayout lay;
   bool unrotate;
+  const void* k_new;         // fused FP4 step: newest token's K/V [B][Hkv][D] (q_dtype), or null
+  const void* v_new;
   hipEvent_t ev_start, ev_stop;   // optional, recorded around the main kernel
 };
 

@@ -173,6 +173,28 @@ int uq_decode_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtype
                         float sm_scale, float* out, void* workspace, size_t workspace_bytes,
                         uint32_t flags, uq_stream_t stream);
 
+/*
+ * One FP4 decode step in a single launch ([review] §3.1 write path followed by
+ * the §3.2 decode): for every sequence b with L = seq_lens[b] > 0, writes the
+ * step's newest token -- k_new[b][h] and v_new[b][h] for every KV head h -- at
+ * position L - 1 (page page_table[b][(L-1)/16], slot (L-1) % 16) with exactly
+ * the bytes uq_quantize_append would store there, then computes
+ * uq_decode_attention over positions 0 .. L-1, the new token included.  The
+ * result equals uq_quantize_append with slot_mapping[b] = that slot followed by
+ * uq_decode_attention.
+ *   k_new, v_new  device [num_seqs][num_kv_heads][head_dim], in_dtype
+ *   q             device [num_seqs][num_q_heads][head_dim], in_dtype
+ *   other arguments and limits as uq_decode_attention; cache->format must be
+ *   UQ_KV_FP4.  Sequences of length 0 write nothing.  The written slot must not
+ *   be shared with another sequence's range (it never is when page tables do
+ *   not share pages).
+ */
+int uq_append_decode_attention(const uq_kv_cache* cache, const void* k_new, const void* v_new, const void* q,
+                               int32_t in_dtype, const int32_t* page_table, int32_t max_pages_per_seq,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, float sm_scale,
+                               float* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                               uq_stream_t stream);
+
 /* FP8 baseline decode: same arguments; cache->format must be UQ_KV_FP8; the
  * query is rounded to E4M3 without rotation and `out` needs no unrotation
  * (flags must be 0). */

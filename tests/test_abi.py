@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     h = uq.lib()
     for n in names:
         assert hasattr(h, n), n
@@ -125,6 +125,29 @@ def test_decode_validation(name, fmt):
     if fmt == B.UQ_KV_BF16:
         assert call(qd=B.UQ_IN_F32) == B.UQ_ERR_UNSUPPORTED
     assert call(B_=0, q=None, pt=None, sl=None, out=None, w=None) == B.UQ_OK
+
+
+def test_fused_step_validation():
+    f = uq.lib().uq_append_decode_attention
+    ok = cache(B.UQ_KV_FP4, heads=2)
+    ws = uq.lib().uq_decode_workspace_bytes(ctypes.byref(ok), 3, 16, 8)
+
+    def call(c=ok, k=FAKE, v=FAKE, q=FAKE, dt=0, pt=FAKE, mp=8, sl=FAKE, B_=3, Hq=16, scale=0.1, out=FAKE, w=FAKE,
+             wb=ws, fl=0):
+        return f(ctypes.byref(c) if c is not None else None, k, v, q, dt, pt, mp, sl, B_, Hq, scale, out, w, wb, fl,
+                 None)
+
+    assert call(c=None) == B.UQ_ERR_INVALID_ARG
+    assert call(c=cache(B.UQ_KV_FP8, heads=2)) == B.UQ_ERR_INVALID_ARG    # FP4 caches only
+    assert call(k=None) == B.UQ_ERR_INVALID_ARG
+    assert call(v=None) == B.UQ_ERR_INVALID_ARG
+    assert call(q=None) == B.UQ_ERR_INVALID_ARG
+    assert call(dt=4) == B.UQ_ERR_INVALID_ARG
+    assert call(Hq=15) == B.UQ_ERR_UNSUPPORTED
+    assert call(w=None) == B.UQ_ERR_WORKSPACE
+    assert call(fl=2) == B.UQ_ERR_INVALID_ARG
+    assert call(fl=B.UQ_FLAG_OUT_ROTATED, w=None) == B.UQ_ERR_WORKSPACE
+    assert call(B_=0, k=None, v=None, q=None, pt=None, sl=None, out=None, w=None) == B.UQ_OK
 
 
 def test_workspace_bytes_grow_with_shape():

@@ -133,13 +133,21 @@ def test_fp4_out_rotated_flag():
 
 
 def test_decode_repeatable_and_stream_ordered():
-    # the same call twice gives identical bits (no atomics, fixed split plan)
+    # One step per workgroup here, so the same call twice gives identical bits.
+    # With several steps per workgroup the waves claim steps dynamically, and
+    # which wave's running sums a step joins changes between calls: the results
+    # then differ at float32 rounding level only.
     wl = _wl("one_long")
     cache = gpu_append("fp4", wl)
     announce("decode fp4 repeat")
     a = gpu_decode("fp4", wl, cache)
     b = gpu_decode("fp4", wl, cache)
     assert np.array_equal(a, b)
+    wl = _wl("multi_step")
+    cache = gpu_append("fp4", wl)
+    a = gpu_decode("fp4", wl, cache)
+    b = gpu_decode("fp4", wl, cache)
+    assert np.linalg.norm(a - b) <= 1e-6 * np.linalg.norm(a)
 
 
 def test_fp4_decode_with_disparate_group_scales():
