@@ -151,6 +151,43 @@ def summarize_pmc(fetch_csv, write_csv, workload):
     print("\n".join(lines))
 
 
+def append_throughput(steps, warmup, settle_s):
+    """The FP4 write path alone on the append workload (65,536 tokens x 8 KV heads x
+    head_dim 128, bf16, permuted pages): quantized tokens/s and HBM GB/s of one
+    uq_quantize_append call (HIP events around the K timed calls, one launch each)."""
+    import torch
+    import bit_kv_cache_wht_amd as uq
+    from bit_kv_cache_wht_amd import workloads as W
+    wl = W.append_only()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    k = dev(wl.k.view(np.int16)).view(torch.bfloat16)
+    v = dev(wl.v.view(np.int16)).view(torch.bfloat16)
+    slots = dev(wl.slot_mapping)
+    cache = uq.KvCache.allocate(uq.UQ_KV_FP4, wl.num_pages, wl.num_kv_heads, wl.head_dim)
+    call = lambda: uq.uq_quantize_append(cache, k, v, slots)
+    t = time.perf_counter()
+    while time.perf_counter() - t < settle_s:
+        for _ in range(20):
+            call()
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    T, H, d = wl.total_tokens, wl.num_kv_heads, wl.head_dim
+    algo = T * H * 2 * (2 * d + fp4_kv_bytes_per_token_head(d) // 2) + T * 4   # bf16 K/V in, codes+scales out, slots
+    return {"workload": f"{wl.name}: {T} tokens x {H} kv heads x head_dim {d}, bf16, permuted pages",
+            "us_per_call": round(us, 2), "quantized_tokens_per_s": round(T / (us * 1e-6)),
+            "token_heads_per_s": round(T * H / (us * 1e-6)), "gbs": round(algo / (us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "algo_bytes_per_call": algo}
+
+
 def pmc_pass(args):
     """FP4 steps on the workload, then a plain device copy of known size."""
     import torch
@@ -438,6 +475,12 @@ def main():
                           "frac_hbm_peak": round(results[f]["kernel_gbs"] / HBM_PEAK_GBS, 4)}
                       for f in results if f != "fp4"},
     }
+    if not args.no_baselines:
+        log("append throughput (FP4 write path alone)")
+        line["append"] = append_throughput(args.steps, args.warmup, args.settle_ms * 1e-3)
+        log(f"append: {line['append']['us_per_call']} us per call, "
+            f"{line['append']['quantized_tokens_per_s'] / 1e6:.1f} M tokens/s, {line['append']['gbs']} GB/s")
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -9,6 +9,8 @@
 // over LPR consecutive lanes (see append_fp4_kernel); after the butterfly each
 // lane owns the same channels of the rotated row, so group absmax, scale,
 // rounding and packing need at most a max across the lanes of a group.
+#include <algorithm>
+
 #include "uq_device.h"
 #include "uq_fp4_row.h"
 #include "uq_internal.h"
@@ -47,6 +49,55 @@ __global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
   uint8_t* blk = (is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes + (int64_t)h * Row::BLK;
   if (!is_v) x.store_k(blk, off, p);
   else x.store_v(blk, off, p);
+}
+
+// Large writes: a persistent grid-stride loop over groups of RPW rows per wave,
+// each wave fetching its next group's inputs (and slots) before working on the
+// current one, so that the float64 work of one group hides the memory latency
+// of the next.  Rows r < 2T H are indexed in 32 bits (the host bounds T H).
+template <int D, int IN, int LPR>
+__global__ __launch_bounds__(256) void append_fp4_stream_kernel(AppendArgs a) {
+  using Row = Fp4Row<D, IN, LPR>;
+  constexpr int RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63;
+  const int p = lane % LPR;
+  const int kv_rows = a.T * a.H, nrows = 2 * kv_rows;
+  const int groups = (nrows + RPW - 1) / RPW;
+  const int nwaves = gridDim.x * (blockDim.x >> 6);
+  int g = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (g >= groups) return;                         // whole wave idle (no barriers used)
+  struct In {
+    Row x;
+    int slot, tr;
+    bool is_v, live;
+  };
+  auto fetch = [&](In& in, int grp) {
+    const int row = grp * RPW + lane / LPR;
+    in.live = row < nrows;
+    const int r = in.live ? row : 0;               // idle lanes read row 0 (in bounds)
+    in.is_v = r >= kv_rows;
+    in.tr = in.is_v ? r - kv_rows : r;             // token * H + head
+    in.slot = a.slot_mapping[in.tr / a.H];
+    in.x.load(in.is_v ? a.v : a.k, in.tr, p);
+  };
+  In cur, nxt;
+  fetch(cur, g);
+  for (;;) {
+    const int gn = g + nwaves;
+    const bool more = gn < groups;                 // wave-uniform
+    if (more) fetch(nxt, gn);
+    cur.x.quantize(p);
+    if (cur.live && cur.slot >= 0) {
+      const int h = cur.tr % a.H;
+      const int page = cur.slot >> 4, off = cur.slot & 15;
+      uint8_t* blk = (cur.is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes + (int64_t)h * Row::BLK;
+      if (!cur.is_v) cur.x.store_k(blk, off, p);
+      else cur.x.store_v(blk, off, p);
+    }
+    if (!more) break;
+    cur = nxt;
+    g = gn;
+  }
 }
 
 // Baseline writes: one thread per 8 channels of a (token, head, K|V) row.
@@ -138,6 +189,24 @@ __global__ __launch_bounds__(256) void query_kernel(const void* q, uint8_t* out,
   o[1] = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
+#ifndef APPEND_LPR
+#define APPEND_LPR(D) ((D) / 32)
+#endif
+#ifndef APPEND_BPC
+#define APPEND_BPC 4
+#endif
+static int append_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
 static unsigned grid_rows(int64_t rows, int rows_per_wave) {
   const int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave;
   return (unsigned)((waves + 3) / 4);
@@ -151,7 +220,9 @@ static void launch_fp4_rows(const AppendArgs& a, int64_t rows, hipStream_t s) {
   if (rows < kFewRows) {
     hipLaunchKernelGGL((append_fp4_kernel<D, IN, D / 8>), dim3(grid_rows(rows, 64 / (D / 8))), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((append_fp4_kernel<D, IN, D / 32>), dim3(grid_rows(rows, 64 / (D / 32))), dim3(256), 0, s, a);
+    constexpr int LPR = APPEND_LPR(D);
+    const unsigned blocks = (unsigned)std::min<int64_t>(grid_rows(rows, 64 / LPR), (int64_t)append_cus() * APPEND_BPC);
+    hipLaunchKernelGGL((append_fp4_stream_kernel<D, IN, LPR>), dim3(blocks), dim3(256), 0, s, a);
   }
 }
 

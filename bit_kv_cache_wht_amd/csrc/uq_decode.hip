@@ -649,7 +649,7 @@ template <int D, int IN, int FMT> struct QueryRows {
           for (int e = 0; e < E; ++e) x[e] = __builtin_fma(x[e], sgn, __shfl_xor(x[e], m));
         }
 #pragma unroll
-        for (int e = 0; e < E; ++e) x[e] *= wht_c<D>();
+        for (int e = 0; e < E; ++e) x[e] = __builtin_fma(x[e], wht_c<D>(), 0.0);   // + 0: an exact zero is +0
       }
       uint32_t b[E / 4];
 #pragma unroll

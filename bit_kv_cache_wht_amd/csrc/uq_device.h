@@ -82,7 +82,7 @@ template <int D> __device__ __forceinline__ void wht_row(double (&x)[32], int la
   if constexpr (D == 128) wht_cross_stage<2>(x, lane);   // h = 64
   const double c = wht_c<D>();
 #pragma unroll
-  for (int e = 0; e < 32; ++e) x[e] *= c;
+  for (int e = 0; e < 32; ++e) x[e] = __builtin_fma(x[e], c, 0.0);   // + 0: an exact zero is +0
 }
 
 // Least integer E with m <= 6 * 2^E, clamped to [-127, 127] (m == 0 -> -127).
@@ -110,6 +110,25 @@ __device__ __forceinline__ uint32_t e2m1_code(double r) {
   const int n = (int)__builtin_rint(a * s);
   const uint32_t sign = ((uint32_t)__double2hiint(r)) >> 31;
   return (uint32_t)(n + off) | (sign << 3);
+}
+
+// r rounded to float32 by round-to-odd (truncate, then set the last bit if any
+// dropped bit was set).  Rounding that result to a format with at least two
+// fewer significant bits (here E2M1 x 2^E, 2 bits, whose decision points are all
+// even floats) gives the same result as rounding r itself, so the float32
+// hardware converter can take the decision that is defined on the float64
+// value.  Valid for |r| < 2^128; below 2^-120 it returns a float of r's sign and
+// magnitude below 2^-119 (callers only need that such values round to zero).
+// Integer form: the magnitude, floored at 2^-120 so that its float64 exponent
+// lies in [903, 1150], has the float32 exponent 896 below it; its low nine
+// exponent bits and the top 23 mantissa bits, shifted right by 29, minus 384 in
+// the exponent field, are the truncated float32 magnitude.
+__device__ __forceinline__ float f32_round_to_odd(double r) {
+  const double a = fmax(fabs(r), 0x1p-120);
+  const uint32_t ahi = (uint32_t)__double2hiint(a), alo = (uint32_t)__double2loint(a);
+  const uint32_t mag = __builtin_amdgcn_alignbit(ahi, alo, 29) - (384u << 23);
+  const uint32_t sticky = min(alo << 3, 1u);
+  return __uint_as_float(((uint32_t)__double2hiint(r) & 0x80000000u) | mag | sticky);
 }
 
 // OCP E4M3 byte of a float64: nearest, ties to even, |v| > 448 -> 448, sign

@@ -79,29 +79,49 @@ template <int D, int IN, int LPR> struct Fp4Row {
     if constexpr (LPR > 2) cross_stage<E, 2>(x, p);
     if constexpr (LPR > 4) cross_stage<E, 4>(x, p);
     if constexpr (LPR > 8) cross_stage<E, 8>(x, p);
-#pragma unroll
-    for (int e = 0; e < E; ++e) x[e] *= wht_c<D>();
 
-    double m = 0.0;                                       // group absmax, the same in every lane of the group
+    // The normalized channel is RN(c_d x + 0) (one float64 rounding; the + 0
+    // makes an exact zero +0 whatever the butterfly's signed zeros).  Rounding is
+    // monotone, so the group absmax of those is RN(c_d max |x|).
+    const double c = wht_c<D>();
+    double m = 0.0;                                       // the same in every lane of the group
 #pragma unroll
     for (int e = 0; e < E; ++e) m = fmax(m, fabs(x[e]));
     if constexpr (LPG > 1) m = fmax(m, quad_swap<1>(m));
     if constexpr (LPG > 2) m = fmax(m, quad_swap<2>(m));
-    ex = scale_exponent(m);
+    ex = scale_exponent(m * c);
+    if (ex >= -100 && ex <= 100) {
+      // hardware E2M1 rounding (nearest even, saturating, sign kept) of the
+      // round-to-odd float32 value, divided by the scale 2^ex
+      const float sc = __uint_as_float((uint32_t)(ex + 127) << 23);
 #pragma unroll
-    for (int q = 0; q < E / 8; ++q) {
-      uint32_t acc = 0;
+      for (int q = 0; q < E / 8; ++q) {
+        float f[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc |= e2m1_code(ldexp(x[8 * q + i], -ex)) << (4 * i);
-      w[q] = acc;
+        for (int i = 0; i < 8; ++i) f[i] = f32_round_to_odd(__builtin_fma(x[8 * q + i], c, 0.0));
+        uint32_t acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0], f[1], sc, 0);
+        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[2], f[3], sc, 1);
+        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[4], f[5], sc, 2);
+        w[q] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[6], f[7], sc, 3);
+      }
+    } else {                                              // scales beyond the float32 range: float64 rounding
+#pragma unroll
+      for (int q = 0; q < E / 8; ++q) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc |= e2m1_code(ldexp(__builtin_fma(x[8 * q + i], c, 0.0), -ex)) << (4 * i);
+        w[q] = acc;
+      }
     }
   }
 
   // Stores into the K head block `blk` at page slot `off`: codes [slot][D/2],
   // scales [slot % 4][group][slot / 4].
   __device__ __forceinline__ void store_k(uint8_t* blk, int off, int p) const {
-    if constexpr (E == 32) *reinterpret_cast<uint4*>(blk + off * (D / 2) + 16 * p) = make_uint4(w[0], w[1], w[2], w[3]);
-    else *reinterpret_cast<uint32_t*>(blk + off * (D / 2) + 4 * p) = w[0];
+    uint8_t* dst = blk + off * (D / 2) + (E / 2) * p;
+    if constexpr (E == 32) *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    else if constexpr (E == 16) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    else *reinterpret_cast<uint32_t*>(dst) = w[0];
     if (p % LPG == 0) blk[CODE + 4 * ((off & 3) * (D / 32) + p / LPG) + (off >> 2)] = (uint8_t)(ex + 127);
   }
 

@@ -23,7 +23,9 @@ What the method computes ([review] §3.1, §3.2; [commentary] footnote 2):
 Readings where the pages are silent (each listed with its reason in the design doc):
   R1  K and V are both rotated; the attention output is rotated back.
   R2  WHT = Sylvester Hadamard in natural order, scaled by c_d = sqrt(1/d),
-      over the whole head_dim, no random signs.
+      over the whole head_dim, no random signs.  A rotated value whose exact
+      sum is zero is +0: the exact transform has no signed zeros, and the sign
+      float64 summation leaves on a zero depends on the order of the sums.
   R3  E = the least integer with m <= 6 * 2**E (never clips), clamped to
       [-127, 127]; an all-zero group gets E = -127.
   R4  E2M1 rounding is to nearest, ties to the even code; the sign bit is the
@@ -82,12 +84,13 @@ def wht(x) -> np.ndarray:
 
     The sum is taken first and multiplied by c_d once.  For bf16 input rows whose
     nonzero exponents span at most 38 binades (fp32: 22) every partial sum is an
-    exact float64, so any summation order gives the same result.
+    exact float64, so any summation order gives the same result; adding +0 after
+    the scaling turns a zero of either sign into +0 (reading R2).
     """
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     h = sylvester_hadamard(d).astype(np.float64)
-    return (x @ h) * wht_scale(d)      # H symmetric: (H x)^T = x^T H
+    return (x @ h) * wht_scale(d) + 0.0      # H symmetric: (H x)^T = x^T H
 
 
 # --------------------------------------------------------------------------

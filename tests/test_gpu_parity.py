@@ -58,6 +58,58 @@ def test_append_bit_exact(fmt, name):
         assert bad[0].size == 0, f"{kv} pool: {bad[0].size} bytes differ, first at {[int(x[0]) for x in bad]}"
 
 
+def _extreme_rows(d, rng):
+    """float32 K/V rows that reach every rounding regime of the FP4 write: group
+    scales from 2^-127 to 2^127 (including the ends the float32 hardware
+    rounding does not cover), float32 subnormal inputs, zero and negative-zero
+    groups, and rows whose rotated values sit within float32 rounding of E2M1
+    decision points (the inverse rotation of grid midpoints, rounded to
+    float32; for d = 64, c_d = 1/8 and some land exactly on them)."""
+    from scipy.linalg import hadamard
+    Hn = hadamard(d).astype(np.float64) / np.sqrt(d)
+    rows = []
+    for k in (-149, -140, -130, -125, -120, -110, -102, -101, -100, -99, -60, 0, 60, 99, 100, 101, 102, 110, 120, 125):
+        rows.append(rng.standard_normal(d) * 2.0 ** k)
+    z = np.zeros(d); z[: d // 2] = -0.0; rows.append(z)
+    z = rng.standard_normal(d); z[32:64] = 0.0; rows.append(z)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
+    for e in (-90, -30, -3, 0, 7, 40, 95):
+        for _ in range(3):
+            y = rng.choice(mids, d) * rng.choice([-1.0, 1.0], d) * 2.0 ** e
+            y[::32] = 6.0 * 2.0 ** e                       # fixes each group's scale at e
+            rows.append(Hn @ y)
+    x = np.clip(np.array(rows, dtype=np.float64), -3.0e38, 3.0e38).astype(np.float32)
+    # keep each row inside the exact-sum domain of the rotation (nonzero float32
+    # exponents within 22 binades): entries below 2^-20 of the row's maximum are 0
+    big = np.abs(x).max(axis=1, keepdims=True)
+    x[np.abs(x) < big * np.float32(2.0 ** -20)] = 0.0
+    return x
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("many", [False, True])
+def test_append_extreme_scales_and_near_ties(d, many):
+    # `many` repeats the rows past the small-batch threshold so that the large-
+    # batch kernel runs too
+    rng = np.random.default_rng(d + (7 if many else 0))
+    base = _extreme_rows(d, rng)
+    reps = 1600 if many else 1
+    H = 2
+    xs = np.tile(base, (reps, 1))
+    T = xs.shape[0] // H
+    k = xs[: T * H].reshape(T, H, d)
+    v = -xs[::-1][: T * H].reshape(T, H, d)
+    wl = W.make_workload("extreme", 1, H, H, d, [T], [T], in_dtype="f32", seed=9)
+    wl.k = np.ascontiguousarray(k)
+    wl.v = np.ascontiguousarray(v)
+    announce(f"append fp4 extreme scales d={d} T={T} H={H}")
+    got = pools_np(gpu_append("fp4", wl))
+    want = oracle_append("fp4", wl)
+    for g, w, kv in zip(got, want, "KV"):
+        bad = np.nonzero(g != w)
+        assert bad[0].size == 0, f"{kv} pool: {bad[0].size} bytes differ, first at {[int(x[0]) for x in bad]}"
+
+
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_append_skips_negative_slots_and_partial_calls(fmt):
     wl = _wl("gqa_ragged")

@@ -89,6 +89,25 @@ def test_wht_float64_sums_are_exact_on_bf16_rows():
         assert np.array_equal(got[r], np.array([float(e) * c for e in exact]))
 
 
+def test_wht_exact_zero_outputs_are_positive_zero():
+    # Reading R2: an output whose exact sum is zero carries no sign.  Rows of
+    # signed zeros, and rows whose Hadamard sums cancel exactly, give +0 there.
+    d = 64
+    z = np.zeros((3, d))
+    z[0] = -0.0
+    z[1, ::2] = -0.0
+    z[2, 0], z[2, 1] = 1.5, -1.5                 # H row k sums to 0 where H[0,k] == H[1,k]
+    got = O.wht(z)
+    h = O.sylvester_hadamard(d)
+    zero = np.zeros_like(got, dtype=bool)
+    zero[:2] = True
+    zero[2] = h[0] == h[1]
+    assert np.all(got[zero] == 0.0) and not np.any(np.signbit(got[zero]))
+    assert np.all(np.abs(got[2][~zero[2]]) == 3.0 * O.wht_scale(d))
+    codes, _ = O.quantize_fp4(got)
+    assert not np.any(codes[zero])                  # code 0, not the negative-zero code 8
+
+
 # ---------------------------------------------------------------- UE8M0 exponent
 def _least_exponent(m: float) -> int:
     """Brute force: smallest integer E with m <= 6 * 2**E, exact rationals."""
