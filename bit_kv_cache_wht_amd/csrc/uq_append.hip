@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void query_kernel(const void* q, uint8_t* out,
 #define APPEND_LPR(D) ((D) / 32)
 #endif
 #ifndef APPEND_BPC
-#define APPEND_BPC 4
+#define APPEND_BPC 16
 #endif
 static int append_cus() {
   static int cus = 0;

@@ -41,9 +41,9 @@ __device__ __forceinline__ double bf16_bits_to_f64(uint32_t b16) {
 // Value of `v` held by lane ^ XOR (XOR = 1 or 2, inside a quad) via DPP quad_perm.
 template <int XOR> __device__ __forceinline__ double quad_swap(double v) {
   constexpr int ctrl = XOR == 1 ? 0xB1 /* [1,0,3,2] */ : 0x4E /* [2,3,0,1] */;
-  int lo = __double2loint(v), hi = __double2hiint(v);
-  lo = __builtin_amdgcn_update_dpp(0, lo, ctrl, 0xF, 0xF, false);
-  hi = __builtin_amdgcn_update_dpp(0, hi, ctrl, 0xF, 0xF, false);
+  // a quad permutation reads a lane of every quad, so no lane needs an old value
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), ctrl, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), ctrl, 0xF, 0xF, true);
   return __hiloint2double(hi, lo);
 }
 
@@ -127,7 +127,8 @@ __device__ __forceinline__ float f32_round_to_odd(double r) {
   const double a = fmax(fabs(r), 0x1p-120);
   const uint32_t ahi = (uint32_t)__double2hiint(a), alo = (uint32_t)__double2loint(a);
   const uint32_t mag = __builtin_amdgcn_alignbit(ahi, alo, 29) - (384u << 23);
-  const uint32_t sticky = min(alo << 3, 1u);
+  uint32_t sticky;                       // min(alo << 3, 1) in one instruction
+  asm("v_min_u32 %0, %1, 1" : "=v"(sticky) : "v"(alo << 3));
   return __uint_as_float(((uint32_t)__double2hiint(r) & 0x80000000u) | mag | sticky);
 }
 

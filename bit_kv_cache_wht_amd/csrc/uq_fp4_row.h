@@ -32,14 +32,15 @@ template <int E, int M> __device__ __forceinline__ void cross_stage(double (&x)[
 
 template <int D, int IN, int LPR> struct Fp4Row {
   static constexpr int E = D / LPR;                       // channels per lane
-  static constexpr int LPG = 32 / E;                      // lanes per quantization group
+  static constexpr int LPG = E < 32 ? 32 / E : 1;         // lanes per quantization group
+  static constexpr int GPL = E > 32 ? E / 32 : 1;         // quantization groups per lane
   static constexpr int BLK = Fp4Block<D>::kBytes;
   static constexpr int CODE = Fp4Block<D>::kCodeBytes;
   static constexpr int CPL = D / 32;                      // V: channel pairs per PV lane row group
   static constexpr int NU = E * (IN == UQ_IN_BF16 ? 2 : 4) / 16;
   uint4 raw[NU];                                          // the lane's input bits
   uint32_t w[E / 8];                                      // packed codes, channel E*p + i in nibble i
-  int ex;                                                 // scale exponent of the lane's group
+  int ex[GPL];                                            // scale exponents of the lane's groups
 
   // Input channels E*p .. of row `row` of a [rows][D] array (bf16 bits or f32).
   __device__ __forceinline__ void load(const void* src, int64_t row, int p) {
@@ -84,33 +85,38 @@ template <int D, int IN, int LPR> struct Fp4Row {
     // makes an exact zero +0 whatever the butterfly's signed zeros).  Rounding is
     // monotone, so the group absmax of those is RN(c_d max |x|).
     const double c = wht_c<D>();
-    double m = 0.0;                                       // the same in every lane of the group
+    constexpr int EG = E / GPL;                           // channels of one group held by the lane
 #pragma unroll
-    for (int e = 0; e < E; ++e) m = fmax(m, fabs(x[e]));
-    if constexpr (LPG > 1) m = fmax(m, quad_swap<1>(m));
-    if constexpr (LPG > 2) m = fmax(m, quad_swap<2>(m));
-    ex = scale_exponent(m * c);
-    if (ex >= -100 && ex <= 100) {
-      // hardware E2M1 rounding (nearest even, saturating, sign kept) of the
-      // round-to-odd float32 value, divided by the scale 2^ex
-      const float sc = __uint_as_float((uint32_t)(ex + 127) << 23);
+    for (int g = 0; g < GPL; ++g) {
+      double m = 0.0;                                     // the same in every lane of the group
 #pragma unroll
-      for (int q = 0; q < E / 8; ++q) {
-        float f[8];
+      for (int e = 0; e < EG; ++e) m = fmax(m, fabs(x[EG * g + e]));
+      if constexpr (LPG > 1) m = fmax(m, quad_swap<1>(m));
+      if constexpr (LPG > 2) m = fmax(m, quad_swap<2>(m));
+      const int xg = scale_exponent(m * c);
+      ex[g] = xg;
+      if (xg >= -100 && xg <= 100) {
+        // hardware E2M1 rounding (nearest even, saturating, sign kept) of the
+        // round-to-odd float32 value, divided by the scale 2^xg
+        const float sc = __uint_as_float((uint32_t)(xg + 127) << 23);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = f32_round_to_odd(__builtin_fma(x[8 * q + i], c, 0.0));
-        uint32_t acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0], f[1], sc, 0);
-        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[2], f[3], sc, 1);
-        acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[4], f[5], sc, 2);
-        w[q] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[6], f[7], sc, 3);
-      }
-    } else {                                              // scales beyond the float32 range: float64 rounding
+        for (int q = EG / 8 * g; q < EG / 8 * (g + 1); ++q) {
+          float f[8];
 #pragma unroll
-      for (int q = 0; q < E / 8; ++q) {
-        uint32_t acc = 0;
+          for (int i = 0; i < 8; ++i) f[i] = f32_round_to_odd(__builtin_fma(x[8 * q + i], c, 0.0));
+          uint32_t acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0], f[1], sc, 0);
+          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[2], f[3], sc, 1);
+          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[4], f[5], sc, 2);
+          w[q] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[6], f[7], sc, 3);
+        }
+      } else {                                            // scales beyond the float32 range: float64 rounding
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc |= e2m1_code(ldexp(__builtin_fma(x[8 * q + i], c, 0.0), -ex)) << (4 * i);
-        w[q] = acc;
+        for (int q = EG / 8 * g; q < EG / 8 * (g + 1); ++q) {
+          uint32_t acc = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc |= e2m1_code(ldexp(__builtin_fma(x[8 * q + i], c, 0.0), -xg)) << (4 * i);
+          w[q] = acc;
+        }
       }
     }
   }
@@ -119,10 +125,20 @@ template <int D, int IN, int LPR> struct Fp4Row {
   // scales [slot % 4][group][slot / 4].
   __device__ __forceinline__ void store_k(uint8_t* blk, int off, int p) const {
     uint8_t* dst = blk + off * (D / 2) + (E / 2) * p;
-    if constexpr (E == 32) *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-    else if constexpr (E == 16) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-    else *reinterpret_cast<uint32_t*>(dst) = w[0];
-    if (p % LPG == 0) blk[CODE + 4 * ((off & 3) * (D / 32) + p / LPG) + (off >> 2)] = (uint8_t)(ex + 127);
+    if constexpr (E >= 32) {
+#pragma unroll
+      for (int u = 0; u < E / 32; ++u)
+        reinterpret_cast<uint4*>(dst)[u] = make_uint4(w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3]);
+    } else if constexpr (E == 16) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    } else {
+      *reinterpret_cast<uint32_t*>(dst) = w[0];
+    }
+    if (p % LPG == 0) {
+#pragma unroll
+      for (int g = 0; g < GPL; ++g)
+        blk[CODE + 4 * ((off & 3) * (D / 32) + p / LPG * GPL + g) + (off >> 2)] = (uint8_t)(ex[g] + 127);
+    }
   }
 
   // Stores into the V head block `blk` at page slot `off`: channel pair c in
@@ -133,7 +149,10 @@ template <int D, int IN, int LPR> struct Fp4Row {
       const int c = (E / 2) * p + i;
       blk[(16 * (c % CPL) + c / CPL) * kPage + off] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
     }
-    if (p % LPG == 0) blk[CODE + (p / LPG) * kPage + off] = (uint8_t)(ex + 127);
+    if (p % LPG == 0) {
+#pragma unroll
+      for (int g = 0; g < GPL; ++g) blk[CODE + (p / LPG * GPL + g) * kPage + off] = (uint8_t)(ex[g] + 127);
+    }
   }
 };
 
