@@ -1227,33 +1227,47 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
           const int w = w0 + i;
           return (int64_t)(2 * w + (share_begin(w) >= start ? 0 : 1)) * G + h;
         };
-        float m = -INFINITY;
-        for (int c0 = 0; c0 < n; c0 += 64) {
-          const float mv = c0 + lane < n ? ld_dev(a.ml + 2 * prow_of(c0 + lane)) : -INFINITY;
-          m = fmaxf(m, mv);
-        }
-#pragma unroll
-        for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
-        float o[PER], l = 0.f;
+        // Contributors 64 at a time, lane i holding contributor c0 + i's (m, l);
+        // their O rows are read 8 contributors per batch, all loads of a batch
+        // in flight together (each read goes past the L2 to the device level).
+        float m = -INFINITY, l = 0.f, o[PER];
 #pragma unroll
         for (int kk = 0; kk < PER; ++kk) o[kk] = 0.f;
         for (int c0 = 0; c0 < n; c0 += 64) {
           const int nc = min(64, n - c0);
-          float wt = 0.f, lw = 0.f;
+          float vm = -INFINITY, vl = 0.f;
           if (lane < nc) {
             const float* v = a.ml + 2 * prow_of(c0 + lane);
-            const float vm = ld_dev(v), vl = ld_dev(v + 1);
-            wt = vm > -INFINITY ? __builtin_amdgcn_exp2f(vm - m) : 0.f;
-            lw = wt * vl;
+            vm = ld_dev(v);
+            vl = ld_dev(v + 1);
           }
+          float mc = vm;
+#pragma unroll
+          for (int x = 32; x >= 1; x >>= 1) mc = fmaxf(mc, __shfl_xor(mc, x));
+          const float mn = fmaxf(m, mc);
+          const float keep = m > -INFINITY ? __builtin_amdgcn_exp2f(m - mn) : 0.f;   // rescale of earlier chunks
+          const float wt = vm > -INFINITY ? __builtin_amdgcn_exp2f(vm - mn) : 0.f;
+          float lw = wt * vl;
 #pragma unroll
           for (int x = 32; x >= 1; x >>= 1) lw += __shfl_xor(lw, x);
-          l += lw;
-          for (int i = 0; i < nc; ++i) {
-            const float ws = __shfl(wt, i);
-            const float* src = a.po + prow_of(c0 + i) * D + lane;
+          l = l * keep + lw;
 #pragma unroll
-            for (int kk = 0; kk < PER; ++kk) o[kk] += ws * ld_dev(src + 64 * kk);
+          for (int kk = 0; kk < PER; ++kk) o[kk] *= keep;
+          m = mn;
+          for (int i0 = 0; i0 < nc; i0 += 8) {
+            float buf[8][PER];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float* src = a.po + prow_of(c0 + min(i0 + j, nc - 1)) * D + lane;   // past nc: weight 0
+#pragma unroll
+              for (int kk = 0; kk < PER; ++kk) buf[j][kk] = ld_dev(src + 64 * kk);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float ws = __shfl(wt, i0 + j);             // i0 + j < 64; 0 past nc (lane >= nc)
+#pragma unroll
+              for (int kk = 0; kk < PER; ++kk) o[kk] += ws * buf[j][kk];
+            }
           }
         }
         store_row<D, UNROT>(o, l, a.out + ((int64_t)b * a.Hq + (int64_t)hk * G + h) * D, lane);
