@@ -739,21 +739,23 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // LDS carve-up (bytes) of one workgroup of NW waves working on rounds of up to R
 // items, each with G query heads:
 //   qs     [R][G][D]       query rows (E4M3 bytes; BF16: bf16)
-//   so     [R][NW][G][D]   per-wave partial O of each item (float)
-//   sm, sl [R][NW][G]      per-wave partial m (log2 units) and l (float)
+//   so     [R][NW][16][D]  per-wave partial O of each item (float), 16 >= G
+//                          rows per slot so that slot offsets are constants
+//   sm, sl [R][NW][16]     per-wave partial m (log2 units) and l (float)
 //   rec    [R][8]          item records (int)
 //   misc   [32]            step counter, per-item flags, plan scratch (int)
 //   base   [B + 1]         plan (int)
 //   lens   [B]             sequence lengths as used (int)
+constexpr int kSR = 16;   // rows of a wave slot in LDS (the 16 MFMA columns; an item has G <= 16)
 struct Lds {
   int qs, so, sm, sl, rec, misc, base, lens, total;
   __host__ __device__ static int up16(int x) { return (x + 15) & ~15; }
   __host__ __device__ Lds(int R, int NW, int G, int D, int esz, int B) {
     qs = 0;
     so = up16(qs + R * G * D * esz);
-    sm = up16(so + R * NW * G * D * 4);
-    sl = up16(sm + R * NW * G * 4);
-    rec = up16(sl + R * NW * G * 4);
+    sm = up16(so + R * NW * kSR * D * 4);
+    sl = up16(sm + R * NW * kSR * 4);
+    rec = up16(sl + R * NW * kSR * 4);
     misc = up16(rec + R * 8 * 4);
     base = up16(misc + 32 * 4);
     lens = up16(base + (B + 1) * 4);
@@ -890,7 +892,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
       const int e = __builtin_amdgcn_readlane(sg_end, nR - 1);
       g_cur = e < g_hi ? e : g_hi;               // next round starts after the last segment
     }
-    for (int i = tid; i < nR * NW * G; i += NT) smx[i] = -INFINITY;   // parks come after the barrier below
+    for (int i = tid; i < nR * NW * kSR; i += NT) smx[i] = -INFINITY;   // parks come after the barrier below
 
     // query rows of the round, row r = k * G + h; the first pass's loads go out
     // ahead of the key/value prologue
@@ -1046,7 +1048,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
       float l_tot = l_run + __shfl_xor(l_run, 16);
       l_tot += __shfl_xor(l_tot, 32);
       if (r16 < G) {
-        const int slot = (acc_k * NW + wave) * G + r16;
+        const int slot = (acc_k * NW + wave) * kSR + r16;
         float* o = so + slot * D;
 #pragma unroll
         for (int tt = 0; tt < Pol::kTiles; ++tt)
@@ -1158,28 +1160,35 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     __syncthreads();
 
     // ---- merge the wave slots of each segment; wave w takes rows w, w + NW, ...
-    for (int row = wave; row < nrows; row += NW) {
+    // (row indices held as wave-uniform scalars, so the slot addressing is scalar)
+    for (int row = __builtin_amdgcn_readfirstlane(wave); row < nrows; row += NW) {
       const int k = row / G, h = row - k * G;
       const int32_t* r = rec + 8 * k;
       if (r[kRecNStep] == 0) continue;           // empty sequences are written below
-      const int slot0 = k * NW * G + h;          // slot of wave w: slot0 + w * G
+      const int slot0 = k * NW * kSR + h;        // slot of wave w: slot0 + w * kSR
+      // all slot reads first, then the weighted sum without branches; a slot of
+      // a wave that took no step has m = -inf and stale l and O, masked out
+      float ms[NW], ls[NW], os[NW][PER];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        ms[w] = smx[slot0 + w * kSR];
+        ls[w] = slx[slot0 + w * kSR];
+#pragma unroll
+        for (int kk = 0; kk < PER; ++kk) os[w][kk] = so[(slot0 + w * kSR) * D + lane + 64 * kk];
+      }
       float m = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) m = fmaxf(m, smx[slot0 + w * G]);
+      for (int w = 0; w < NW; ++w) m = fmaxf(m, ms[w]);
       float o[PER], l = 0.f;
 #pragma unroll
       for (int kk = 0; kk < PER; ++kk) o[kk] = 0.f;
-      if (m > -INFINITY) {
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          const float mw = smx[slot0 + w * G];
-          if (mw > -INFINITY) {                  // slots of waves that took no step are stale
-            const float wt = __builtin_amdgcn_exp2f(mw - m);
-            l += wt * slx[slot0 + w * G];
+      for (int w = 0; w < NW; ++w) {
+        const bool live = ms[w] > -INFINITY;
+        const float wt = live ? __builtin_amdgcn_exp2f(ms[w] - m) : 0.f;
+        l = live ? fmaf(wt, ls[w], l) : l;
 #pragma unroll
-            for (int kk = 0; kk < PER; ++kk) o[kk] += wt * so[(slot0 + w * G) * D + lane + 64 * kk];
-          }
-        }
+        for (int kk = 0; kk < PER; ++kk) o[kk] = live ? fmaf(wt, os[w][kk], o[kk]) : o[kk];
       }
       const int slot = r[kRecSlot];
       if (slot < 0) {
