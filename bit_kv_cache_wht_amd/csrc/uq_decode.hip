@@ -692,6 +692,62 @@ __device__ void store_row(float (&o)[D / 64], float l, float* dst, int lane) {
   for (int k = 0; k < PER; ++k) dst[lane + 64 * k] = o[k];
 }
 
+// Value held by lane ^ M within each 32-lane half of the wave (M = 1 .. 16):
+// DPP quad permutations for 1 and 2, row shifts for 4, a row rotation for 8,
+// a swizzle for 16 -- none goes through the LDS crossbar's address path.
+template <int M> __device__ __forceinline__ float xor32(float v, int lane) {
+  const int x = __float_as_int(v);
+  if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));
+  else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+  else if constexpr (M == 4) {
+    const int up = __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0xF, true);   // row_shl:4, lane i <- i + 4
+    const int dn = __builtin_amdgcn_mov_dpp(x, 0x114, 0xF, 0xF, true);   // row_shr:4, lane i <- i - 4
+    return __int_as_float((lane & 4) ? dn : up);
+  } else if constexpr (M == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true));   // row_ror:8
+  else return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x401F));    // and 31, xor 16
+}
+
+// As store_row for a row held by one 32-lane half of the wave, channel
+// (lane % 32) + 32 c in o[c]: the butterfly stages 32 and 64 run inside the
+// lane, stages 1 .. 16 across lanes of the half.
+template <int D, bool UNROT>
+__device__ void store_row32(float (&o)[D / 32], float l, float* dst, bool live, int lane) {
+  constexpr int PC = D / 32;
+  const float inv = l > 0.f ? 1.f / l : 0.f;      // l == 0 only for empty sequences
+#pragma unroll
+  for (int c = 0; c < PC; ++c) o[c] *= inv;
+  if constexpr (UNROT) {
+#pragma unroll
+    for (int h = 1; h < PC; h <<= 1)
+#pragma unroll
+      for (int c = 0; c < PC; ++c)
+        if (!(c & h)) {
+          const float x0 = o[c], x1 = o[c + h];
+          o[c] = x0 + x1;
+          o[c + h] = x0 - x1;
+        }
+    auto stage = [&](auto mtag) {
+      constexpr int M = decltype(mtag)::value;
+#pragma unroll
+      for (int c = 0; c < PC; ++c) {
+        const float other = xor32<M>(o[c], lane);
+        o[c] = (lane & M) ? other - o[c] : o[c] + other;
+      }
+    };
+    stage(std::integral_constant<int, 16>{});
+    stage(std::integral_constant<int, 8>{});
+    stage(std::integral_constant<int, 4>{});
+    stage(std::integral_constant<int, 2>{});
+    stage(std::integral_constant<int, 1>{});
+#pragma unroll
+    for (int c = 0; c < PC; ++c) o[c] *= wht_cf<D>();
+  }
+  if (live) {
+#pragma unroll
+    for (int c = 0; c < PC; ++c) dst[(lane & 31) + 32 * c] = o[c];
+  }
+}
+
 // Quantizes and stores a row of the fused step's newest token.
 template <class Row>
 __device__ __forceinline__ void write_new(Row& row, uint8_t* blk, int off, bool live, bool is_v, int p) {
@@ -1159,48 +1215,59 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     if (acc_k >= 0) park();
     __syncthreads();
 
-    // ---- merge the wave slots of each segment; wave w takes rows w, w + NW, ...
-    // (row indices held as wave-uniform scalars, so the slot addressing is scalar)
-    for (int row = __builtin_amdgcn_readfirstlane(wave); row < nrows; row += NW) {
-      const int k = row / G, h = row - k * G;
-      const int32_t* r = rec + 8 * k;
-      if (r[kRecNStep] == 0) continue;           // empty sequences are written below
-      const int slot0 = k * NW * kSR + h;        // slot of wave w: slot0 + w * kSR
-      // all slot reads first, then the weighted sum without branches; a slot of
-      // a wave that took no step has m = -inf and stale l and O, masked out
-      float ms[NW], ls[NW], os[NW][PER];
+    // ---- merge the wave slots of each segment: a wave takes two rows at a time,
+    // lanes 0-31 the first and 32-63 the second, channels (lane % 32) + 32 c
+    // (row pairs indexed by wave-uniform scalars; the rows differ per half)
+    {
+      constexpr int PC = D / 32;
+      int ln = lane;                             // opaque: the lane-derived values are formed here,
+      asm volatile("" : "+v"(ln));               // not held in registers from the kernel's start
+      const int half = ln >> 5, l32 = ln & 31;
+      for (int row0 = 2 * __builtin_amdgcn_readfirstlane(wave); row0 < nrows; row0 += 2 * NW) {
+        const int row = row0 + half;
+        const bool have = row < nrows;
+        const int rr = have ? row : row0;
+        const int k = rr / G, h = rr - k * G;
+        const int32_t* r = rec + 8 * k;
+        const int slot0 = k * NW * kSR + h;      // slot of wave w: slot0 + w * kSR
+        // all slot reads first, then the weighted sum without branches; a slot of
+        // a wave that took no step has m = -inf and stale l and O, masked out
+        float ms[NW], ls[NW], os[NW][PC];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        ms[w] = smx[slot0 + w * kSR];
-        ls[w] = slx[slot0 + w * kSR];
+        for (int w = 0; w < NW; ++w) {
+          ms[w] = smx[slot0 + w * kSR];
+          ls[w] = slx[slot0 + w * kSR];
 #pragma unroll
-        for (int kk = 0; kk < PER; ++kk) os[w][kk] = so[(slot0 + w * kSR) * D + lane + 64 * kk];
-      }
-      float m = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) m = fmaxf(m, ms[w]);
-      float o[PER], l = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < PER; ++kk) o[kk] = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const bool live = ms[w] > -INFINITY;
-        const float wt = live ? __builtin_amdgcn_exp2f(ms[w] - m) : 0.f;
-        l = live ? fmaf(wt, ls[w], l) : l;
-#pragma unroll
-        for (int kk = 0; kk < PER; ++kk) o[kk] = live ? fmaf(wt, os[w][kk], o[kk]) : o[kk];
-      }
-      const int slot = r[kRecSlot];
-      if (slot < 0) {
-        store_row<D, UNROT>(o, l, a.out + ((int64_t)r[kRecB] * a.Hq + (int64_t)r[kRecHk] * G + h) * D, lane);
-      } else {
-        const int64_t prow = (int64_t)slot * G + h;
-#pragma unroll
-        for (int kk = 0; kk < PER; ++kk) st_dev(a.po + prow * D + lane + 64 * kk, o[kk]);
-        if (lane == 0) {
-          st_dev(a.ml + 2 * prow, m);
-          st_dev(a.ml + 2 * prow + 1, l);
+          for (int c = 0; c < PC; ++c) os[w][c] = so[(slot0 + w * kSR) * D + l32 + 32 * c];
         }
+        float m = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) m = fmaxf(m, ms[w]);
+        float o[PC], l = 0.f;
+#pragma unroll
+        for (int c = 0; c < PC; ++c) o[c] = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const bool live = ms[w] > -INFINITY;
+          const float wt = live ? __builtin_amdgcn_exp2f(ms[w] - m) : 0.f;
+          l = live ? fmaf(wt, ls[w], l) : l;
+#pragma unroll
+          for (int c = 0; c < PC; ++c) o[c] = live ? fmaf(wt, os[w][c], o[c]) : o[c];
+        }
+        const int nstep = r[kRecNStep], slot = r[kRecSlot];   // nstep == 0: empty sequence, written below
+        const bool whole = have && nstep > 0 && slot < 0;
+        if (have && nstep > 0 && slot >= 0) {
+          const int64_t prow = (int64_t)slot * G + h;
+#pragma unroll
+          for (int c = 0; c < PC; ++c) st_dev(a.po + prow * D + l32 + 32 * c, o[c]);
+          if (l32 == 0) {
+            st_dev(a.ml + 2 * prow, m);
+            st_dev(a.ml + 2 * prow + 1, l);
+          }
+        }
+        if (__any(whole))                        // the whole wave runs the butterflies
+          store_row32<D, UNROT>(o, l, a.out + ((int64_t)r[kRecB] * a.Hq + (int64_t)r[kRecHk] * G + h) * D, whole,
+                                ln);
       }
     }
 
