@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle sample")
     ap.add_argument("--scrub-mb", type=int, default=0,
                     help="read a buffer of this size between the event-timed steps (evicts the last-level cache)")
+    ap.add_argument("--cold-mb", type=int, default=1024,
+                    help="after the warm passes, time the decode kernel again with a read of a buffer of this "
+                         "size before every step (0: skip); reported as the cold kernel time")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run FP4 steps and a 1 GiB device copy only (for rocprofv3 --pmc runs)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -149,6 +152,32 @@ def summarize_pmc(fetch_csv, write_csv, workload):
     with open(TRAFFIC_SUMMARY, "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
+
+
+def stream_read_gbs(reps=20):
+    """Read bandwidth of the library's plain streaming-read kernel (uq_stream_read)
+    in the same process: a 2 GiB buffer, each byte loaded once, HIP events around
+    `reps` back-to-back launches after 5 untimed ones; also the same for torch's
+    max over that buffer (another read-only kernel, for comparison)."""
+    import torch
+    import bit_kv_cache_wht_amd as uq
+    x = torch.ones((2 << 30) // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fn in (("uq_stream_read", lambda: uq.uq_stream_read(x, sink)), ("torch_max", lambda: x.max())):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = x.numel() * 4 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    del x, sink
+    torch.cuda.empty_cache()
+    return res
 
 
 def append_throughput(steps, warmup, settle_s):
@@ -292,13 +321,14 @@ class Runner:
             self.uq.uq_profile_next_decode(ev[0], ev[1])
         self.decode(self.cache, self.q, self.page_table, self.seq_lens, self.sm_scale, self.out, self.ws)
 
-    def run(self, steps, warmup, scrub=None, settle_s=0.0):
+    def run(self, steps, warmup, scrub=None, settle_s=0.0, cold=None):
         """After `settle_s` seconds of untimed steps and `warmup` more, pass 1
         times `steps` whole steps back to back with nothing else in the timed
         region.  Pass 2 repeats them with HIP events that the library records
         around its decode kernel, on the kernel's own stream; with `scrub` (a device
         tensor) a read of it between steps, outside the events, evicts the
-        last-level cache first."""
+        last-level cache first.  With `cold` (a device tensor) pass 3 does the
+        same with that read between every two steps."""
         torch = self.torch
         t_settle = time.perf_counter()
         while time.perf_counter() - t_settle < settle_s:
@@ -325,10 +355,17 @@ class Runner:
             self.step(evs.pairs[i])
         torch.cuda.synchronize()
         k_ms = [evs.elapsed_ms(i) for i in range(steps)]
+        res = dict(ms_per_step=ms_step, wall_ms_per_step=1e3 * wall / steps,
+                   decode_kernel_ms=float(np.mean(k_ms)), decode_kernel_ms_p10=float(np.percentile(k_ms, 10)),
+                   decode_kernel_ms_p90=float(np.percentile(k_ms, 90)))
+        if cold is not None:
+            for i in range(steps):
+                cold.max()                         # a read of >= 1 GiB: the 256 MB last-level cache holds none of the pages
+                self.step(evs.pairs[i])
+            torch.cuda.synchronize()
+            res["decode_kernel_ms_cold"] = float(np.mean([evs.elapsed_ms(i) for i in range(steps)]))
         evs.close()
-        return dict(ms_per_step=ms_step, wall_ms_per_step=1e3 * wall / steps,
-                    decode_kernel_ms=float(np.mean(k_ms)), decode_kernel_ms_p10=float(np.percentile(k_ms, 10)),
-                    decode_kernel_ms_p90=float(np.percentile(k_ms, 90)))
+        return res
 
     def kernel_bytes(self):
         """Algorithmic bytes of one launch of the split-K attention kernel: every
@@ -416,7 +453,8 @@ def main():
         log(f"{fmt}: prefill + timing")
         r = Runner(fmt.split("_")[0], wl, fused=fmt == "fp4")
         scrub = torch.ones((args.scrub_mb << 20) // 4, dtype=torch.int32, device="cuda") if args.scrub_mb else None
-        res = r.run(args.steps, args.warmup, scrub, settle_s=args.settle_ms * 1e-3)
+        cold = torch.ones((args.cold_mb << 20) // 4, dtype=torch.int32, device="cuda") if args.cold_mb else None
+        res = r.run(args.steps, args.warmup, scrub, settle_s=args.settle_ms * 1e-3, cold=cold)
         algo, kv = r.kernel_bytes()
         # A fused step is exactly one launch of the decode kernel, so HIP events
         # around the K back-to-back steps time K launches (gaps included); event
@@ -431,7 +469,7 @@ def main():
         results[fmt] = res
         log(f"{fmt}: {1e3 * res['ms_per_step']:.1f} us/step, decode kernel {1e3 * res['kernel_ms']:.1f} us "
             f"= {res['kernel_gbs']:.0f} GB/s (event pairs {1e3 * res['decode_kernel_ms']:.1f} us)")
-        del r, scrub
+        del r, scrub, cold
         torch.cuda.empty_cache()
 
     fp4 = results["fp4"]
@@ -466,15 +504,25 @@ def main():
                                 "HIP events around each launch on its stream"
                                 + (f", {args.scrub_mb} MB scrub between steps" if args.scrub_mb else "")),
                      "kernel_us_event_pairs": round(fp4["decode_kernel_ms"] * 1e3, 2),
+                     "kernel_us_event_pairs_cold": (round(fp4["decode_kernel_ms_cold"] * 1e3, 2)
+                                                    if "decode_kernel_ms_cold" in fp4 else None),
                      "kernel_us_event_pairs_p10_p90": [round(fp4["decode_kernel_ms_p10"] * 1e3, 2),
                                                        round(fp4["decode_kernel_ms_p90"] * 1e3, 2)],
                      "algo_bytes_per_launch": fp4["kernel_algo_bytes"]},
         "baselines": {f: {"us_per_step": round(results[f]["ms_per_step"] * 1e3, 2),
                           "decode_kernel_us": round(results[f]["kernel_ms"] * 1e3, 2),
+                          "decode_kernel_us_event_pairs_cold": (round(results[f]["decode_kernel_ms_cold"] * 1e3, 2)
+                                                                if "decode_kernel_ms_cold" in results[f] else None),
                           "kernel_gbs": round(results[f]["kernel_gbs"], 1),
                           "frac_hbm_peak": round(results[f]["kernel_gbs"] / HBM_PEAK_GBS, 4)}
                       for f in results if f != "fp4"},
     }
+    sr = stream_read_gbs()
+    line["roofline"]["stream_read_gbs"] = round(sr["uq_stream_read"], 1)
+    line["roofline"]["torch_max_read_gbs"] = round(sr["torch_max"], 1)
+    line["roofline"]["frac_of_stream_read"] = round(fp4["kernel_gbs"] / sr["uq_stream_read"], 4)
+    log(f"streaming read reference: {sr['uq_stream_read']:.0f} GB/s (torch max {sr['torch_max']:.0f}); "
+        f"FP4 decode at {fp4['kernel_gbs'] / sr['uq_stream_read']:.2%} of it")
     if not args.no_baselines:
         log("append throughput (FP4 write path alone)")
         line["append"] = append_throughput(args.steps, args.warmup, args.settle_ms * 1e-3)

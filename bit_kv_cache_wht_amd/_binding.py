@@ -49,6 +49,7 @@ _SIGS = {
     "uq_decode_attention_fp8": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
     "uq_decode_attention_bf16": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
     "uq_profile_next_decode": (ctypes.c_int, [_P, _P]),
+    "uq_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
     "uq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "uq_last_hip_error": (ctypes.c_int, []),
 }
@@ -229,3 +230,10 @@ def uq_decode_attention_bf16(cache, q, page_table, seq_lens, sm_scale, out, work
 def uq_profile_next_decode(start_event, stop_event) -> None:
     """Record two hipEvent_t handles (ints) around the next decode call's main kernel."""
     _check("uq_profile_next_decode", lib().uq_profile_next_decode(start_event, stop_event))
+
+
+def uq_stream_read(src, sink, stream=None) -> None:
+    """Streaming read of the whole tensor `src` (bandwidth reference); XORs the XOR
+    of its 32-bit words into the int32 tensor `sink` (one element)."""
+    nbytes = src.numel() * src.element_size()
+    _check("uq_stream_read", lib().uq_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)))

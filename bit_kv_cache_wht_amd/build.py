@@ -9,7 +9,7 @@ import subprocess
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["csrc/uq_api.hip", "csrc/uq_append.hip", "csrc/uq_decode.hip"]
+SOURCES = ["csrc/uq_api.hip", "csrc/uq_append.hip", "csrc/uq_decode.hip", "csrc/uq_stream.hip"]
 LIB = os.path.join(PKG, "libuq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

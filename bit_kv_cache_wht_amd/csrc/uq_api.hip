@@ -199,6 +199,14 @@ int uq_profile_next_decode(void* start_event, void* stop_event) {
   return UQ_OK;
 }
 
+int uq_stream_read(const void* src, size_t bytes, uint32_t* sink, uq_stream_t stream) {
+  if (bytes == 0) return UQ_OK;
+  if (src == nullptr || sink == nullptr) return UQ_ERR_INVALID_ARG;
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+    return UQ_ERR_INVALID_ARG;
+  return hip_status(uq::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 const char* uq_status_string(int status) {
   switch (status) {
     case UQ_OK: return "ok";

@@ -219,6 +219,15 @@ int uq_decode_attention_bf16(const uq_kv_cache* cache, const void* q, int32_t q_
  * for both cancels a pending request.  Nothing is skipped or reordered. */
 int uq_profile_next_decode(void* start_event, void* stop_event);
 
+/* Instrumentation: a plain streaming read of `bytes` bytes of device memory at
+ * `src`, the reference rate for a kernel bound by HBM reads (each byte loaded
+ * once, coalesced; nothing written but one 32-bit word).  The XOR of all the
+ * buffer's little-endian 32-bit words is XORed into *sink (device memory,
+ * caller-owned; zero it first to read the XOR itself).  `src` must be 16-byte
+ * aligned and `bytes` a multiple of 16 (else UQ_ERR_INVALID_ARG); bytes == 0
+ * launches nothing.  Asynchronous on `stream`. */
+int uq_stream_read(const void* src, size_t bytes, uint32_t* sink, uq_stream_t stream);
+
 /* Static description of a status code. */
 const char* uq_status_string(int status);
 

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     h = uq.lib()
     for n in names:
         assert hasattr(h, n), n
@@ -171,3 +171,13 @@ def test_profile_events_validation():
     assert f(FAKE, None) == B.UQ_ERR_INVALID_ARG
     assert f(None, FAKE) == B.UQ_ERR_INVALID_ARG
     assert f(None, None) == B.UQ_OK
+
+
+def test_stream_read_validation():
+    f = uq.lib().uq_stream_read
+    assert f(None, 0, None, None) == B.UQ_OK                  # nothing to read: no launch
+    assert f(None, 16, FAKE, None) == B.UQ_ERR_INVALID_ARG
+    assert f(FAKE, 16, None, None) == B.UQ_ERR_INVALID_ARG
+    assert f(FAKE + 4, 16, FAKE, None) == B.UQ_ERR_INVALID_ARG   # src not 16-byte aligned
+    assert f(FAKE, 20, FAKE, None) == B.UQ_ERR_INVALID_ARG       # not a multiple of 16 bytes
+    assert f(FAKE, 16, FAKE + 2, None) == B.UQ_ERR_INVALID_ARG   # sink not 4-byte aligned
