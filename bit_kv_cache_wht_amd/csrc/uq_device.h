@@ -160,6 +160,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Loads of cache pages, which a decode launch reads once: nontemporal, so the
+// lines stream through the caches instead of being kept in them (on MI355X a
+// plain streaming read runs at ~6.3 TB/s this way against ~7.0 TB/s).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load8_stream(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(static_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t load4_stream(const void* p) {
+  return __builtin_nontemporal_load(static_cast<const uint32_t*>(p));
+}
+
 // 32 consecutive input values (bf16 bits or f32) starting at element `elem`, as float64.
 template <int IN> __device__ __forceinline__ void load_row32(const void* base, int64_t elem, double (&x)[32]) {
   if constexpr (IN == UQ_IN_BF16) {

@@ -1,12 +1,14 @@
 // A plain streaming read of device memory: the bandwidth reference against which
 // the decode kernel's HBM rate is read.  Every 16-byte word is loaded once,
-// coalesced, eight loads in flight per lane; the XOR of all 32-bit words leaves
-// the kernel through one atomic per wave, so no load can be dropped and the
-// result can be checked.
+// coalesced, eight nontemporal loads in flight per lane (the fastest plain read
+// measured on MI355X: ~7.0 TB/s, against ~6.3 TB/s with ordinary loads); the XOR
+// of all 32-bit words leaves the kernel through one atomic per wave, so no load
+// can be dropped and the result can be checked.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 
+#include "uq_device.h"
 #include "uq_internal.h"
 
 namespace uq {
@@ -25,13 +27,13 @@ __global__ __launch_bounds__(kSrThreads) void stream_read_kernel(const uint4* __
     const uint4* p = src + c * kChunk + threadIdx.x;        // < (c + 1) * kChunk <= n16
     uint4 v[kSrUnroll];
 #pragma unroll
-    for (int u = 0; u < kSrUnroll; ++u) v[u] = p[u * kSrThreads];
+    for (int u = 0; u < kSrUnroll; ++u) v[u] = load16_stream(p + u * kSrThreads);
 #pragma unroll
     for (int u = 0; u < kSrUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (int64_t i = nchunks * kChunk + (int64_t)blockIdx.x * kSrThreads + threadIdx.x; i < n16;
        i += (int64_t)gridDim.x * kSrThreads) {
-    const uint4 v = src[i];
+    const uint4 v = load16_stream(src + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
 #pragma unroll

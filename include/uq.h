@@ -221,7 +221,8 @@ int uq_profile_next_decode(void* start_event, void* stop_event);
 
 /* Instrumentation: a plain streaming read of `bytes` bytes of device memory at
  * `src`, the reference rate for a kernel bound by HBM reads (each byte loaded
- * once, coalesced; nothing written but one 32-bit word).  The XOR of all the
+ * once, coalesced, with nontemporal loads; nothing written but one 32-bit
+ * word).  The XOR of all the
  * buffer's little-endian 32-bit words is XORed into *sink (device memory,
  * caller-owned; zero it first to read the XOR itself).  `src` must be 16-byte
  * aligned and `bytes` a multiple of 16 (else UQ_ERR_INVALID_ARG); bytes == 0
