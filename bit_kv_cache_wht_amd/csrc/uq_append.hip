@@ -139,15 +139,12 @@ __global__ __launch_bounds__(256) void append_plain_kernel(AppendArgs a) {
   }
   uint8_t* blk = (is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes + (int64_t)h * BLK;
   if constexpr (FMT == UQ_KV_FP8) {
-    uint32_t b[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b[i] = e4m3_from_f64((double)f[i]);
+    const uint32_t b0 = e4m3x4_f32(f[0], f[1], f[2], f[3]), b1 = e4m3x4_f32(f[4], f[5], f[6], f[7]);
     if (!is_v) {
-      *reinterpret_cast<uint2*>(blk + off * D + c0) =
-          make_uint2(b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24, b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24);
+      *reinterpret_cast<uint2*>(blk + off * D + c0) = make_uint2(b0, b1);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) blk[(c0 + i) * kPage + off] = (uint8_t)b[i];
+      for (int i = 0; i < 8; ++i) blk[(c0 + i) * kPage + off] = (uint8_t)((i < 4 ? b0 : b1) >> (8 * (i & 3)));
     }
   } else {
     uint16_t* blk16 = reinterpret_cast<uint16_t*>(blk);
@@ -180,9 +177,7 @@ __global__ __launch_bounds__(256) void query_kernel(const void* q, uint8_t* out,
   if constexpr (ROT) wht_row<D>(x, lane);
   uint32_t w[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    w[i] = e4m3_from_f64(x[4 * i]) | e4m3_from_f64(x[4 * i + 1]) << 8 | e4m3_from_f64(x[4 * i + 2]) << 16 |
-           e4m3_from_f64(x[4 * i + 3]) << 24;
+  for (int i = 0; i < 8; ++i) w[i] = e4m3x4_f64(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
   if (!in_range) return;
   uint4* o = reinterpret_cast<uint4*>(out + r * D + 32 * p);
   o[0] = make_uint4(w[0], w[1], w[2], w[3]);

@@ -544,13 +544,30 @@ template <int D> struct Bf16Pol {
 // sbase[B] = T, the total.  Workgroup w
 // then takes steps [w T / grid, (w + 1) T / grid): equal shares whatever the
 // mix of lengths, items cut at share boundaries being merged across workgroups.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(v, d);
-    if (lane >= d) v += t;
-  }
+// Inclusive sum over the 64 lanes: Hillis-Steele inside each 16-lane row
+// (DPP row shifts, lanes past the row start adding 0), then the row totals
+// broadcast into the later rows (row_bcast:15 into rows 1 and 3, row_bcast:31
+// into rows 2 and 3).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
   return v;
+}
+
+// floor(n / d) for 0 <= n < 2^31, d >= 1 and a quotient below 2^20, from rd =
+// the hardware reciprocal of d (1 ulp): the float estimate is then within 0.2
+// of n / d, so its truncation is off by at most one, fixed in exact integer
+// arithmetic (q * d <= n + d < 2^32).
+__device__ __forceinline__ int div_q20(int n, int d, float rd) {
+  uint32_t q = (uint32_t)((float)n * rd);
+  const int r = (int)((uint32_t)n - q * (uint32_t)d);
+  q += r >= d ? 1u : 0u;
+  q -= r < 0 ? 1u : 0u;
+  return (int)q;
 }
 
 // Sequence length as used: clamped to [0, max_pages * 16] so that a length
@@ -573,7 +590,7 @@ __device__ void wg_plan(const int32_t* __restrict__ seq_lens, int B, int Hi, int
     const int L = b < B ? clamp_len(seq_lens[b], max_pages) : 0;
     if (b < B) lens[b] = L;
     const int ns = b < B ? seq_steps<NP>(L) * Hi : 0;
-    const int incl = wave_incl_scan(ns, lane);
+    const int incl = wave_incl_scan(ns);
     if (lane == 63) red[wave] = incl;
     __syncthreads();
     int woff = 0, chunk = 0;
@@ -618,6 +635,12 @@ template <int D, int IN, int FMT> struct QueryRows {
     }
   }
 
+  template <int M> __device__ static void cross(double (&x)[E], int p) {
+    const double sgn = (p & M) ? -1.0 : 1.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = __builtin_fma(x[e], sgn, lane_xor16<M>(x[e], p));
+  }
+
   // Converts and stores the part into the LDS row dst (the 16 threads of a row
   // must call it together).
   __device__ void finish(uint8_t* dst_row, int p) const {
@@ -644,20 +667,18 @@ template <int D, int IN, int FMT> struct QueryRows {
               x[j] = a0 + a1;
               x[j + h] = a0 - a1;
             }
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) {       // partner thread t ^ m holds the other half
-          const double sgn = (p & m) ? -1.0 : 1.0;
-#pragma unroll
-          for (int e = 0; e < E; ++e) x[e] = __builtin_fma(x[e], sgn, __shfl_xor(x[e], m));
-        }
+        // partner thread t ^ m holds the other half (the row's 16 threads are a
+        // 16-lane row of the wave)
+        cross<1>(x, p);
+        cross<2>(x, p);
+        cross<4>(x, p);
+        cross<8>(x, p);
 #pragma unroll
         for (int e = 0; e < E; ++e) x[e] = __builtin_fma(x[e], wht_c<D>(), 0.0);   // + 0: an exact zero is +0
       }
       uint32_t b[E / 4];
 #pragma unroll
-      for (int i = 0; i < E / 4; ++i)
-        b[i] = e4m3_from_f64(x[4 * i]) | e4m3_from_f64(x[4 * i + 1]) << 8 | e4m3_from_f64(x[4 * i + 2]) << 16 |
-               e4m3_from_f64(x[4 * i + 3]) << 24;
+      for (int i = 0; i < E / 4; ++i) b[i] = e4m3x4_f64(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
       uint8_t* dst = dst_row + E * p;
       if constexpr (E == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(b[0], b[1]);
       else *reinterpret_cast<uint32_t*>(dst) = b[0];
@@ -873,17 +894,19 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
   const int grid = T < (int)gridDim.x ? T : (int)gridDim.x, wg = blockIdx.x;
   // share_begin(w) = floor(w T / grid), from T = sq * grid + sr (w * sr < 2^20)
   const int sq = grid > 0 ? T / grid : 0, sr = T - sq * grid;
-  auto share_begin = [&](int w) -> int { return w * sq + (w * sr) / grid; };
+  const float r_grid = __builtin_amdgcn_rcpf((float)grid), r_hi = __builtin_amdgcn_rcpf((float)Hi);
+  const float grid_per_step = (float)grid * __builtin_amdgcn_rcpf((float)T);
+  auto share_begin = [&](int w) -> int { return w * sq + div_q20(w * sr, grid, r_grid); };
   auto owner = [&](int g) -> int {              // the w whose share holds step g
-    int w = (int)((float)g * ((float)grid / (float)T));   // off by at most a few
+    int w = (int)((float)g * grid_per_step);    // off by at most a few
     w = w < 0 ? 0 : (w >= grid ? grid - 1 : w);
     while (share_begin(w) > g) --w;
     while (w + 1 < grid && share_begin(w + 1) <= g) ++w;
     return w;
   };
-  const int g_hi = wg < grid ? share_begin(wg + 1) : 0;
+  const int g_lo = wg < grid ? share_begin(wg) : 0, g_hi = wg < grid ? share_begin(wg + 1) : 0;
 
-  for (int g_cur = wg < grid ? share_begin(wg) : 0; g_cur < g_hi;) {
+  for (int g_cur = g_lo; g_cur < g_hi;) {
     // ---- round set-up: segments k = 0 .. nR-1 are items f0 + k clipped to the
     // share.  Every wave derives them itself, segment k in its lane k, so no
     // barrier is needed before the claims; wave 0 also stores them in LDS for the
@@ -900,8 +923,8 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         lo += (cnt - 1) * stride;
         n = min(stride, n - (cnt - 1) * stride);
       }
-      const int steps = (base[lo + 1] - base[lo]) / Hi;
-      f0 = lo * Hi + (g_cur - base[lo]) / steps;
+      const int steps = seq_steps<NP>(lens[lo]);   // per item of sequence lo (> 0: base[lo] <= g_cur < base[lo + 1])
+      f0 = lo * Hi + div_q20(g_cur - base[lo], steps, __builtin_amdgcn_rcpf((float)steps));
     }
     int sg_b = 0, sg_hk = 0, sg_pbeg = 0, sg_npg = 0, sg_lrel = 0, sg_nstep = 0, sg_slot = -1, sg_ncontrib = 1;
     int sg_end = 0;
@@ -909,9 +932,9 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     {
       const int f = f0 + lane;
       if (lane < a.R && f < a.B * Hi) {
-        const int b = f / Hi;
+        const int b = div_q20(f, Hi, r_hi);
         const int hk = f - b * Hi;
-        const int steps = (base[b + 1] - base[b]) / Hi;
+        const int steps = seq_steps<NP>(lens[b]);
         const int start = base[b] + hk * steps, end = start + steps;
         sg_ok = lane == 0 || start < g_hi;
         const int s_lo = start > g_cur ? start : g_cur, s_hi = end < g_hi ? end : g_hi;
@@ -924,7 +947,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         sg_lrel = L - sg_pbeg * kPage;
         sg_nstep = max(s_hi - s_lo, 0);
         const bool partial = s_lo > start || s_hi < end;
-        sg_slot = partial ? 2 * wg + (share_begin(wg) >= start ? 0 : 1) : -1;
+        sg_slot = partial ? 2 * wg + (g_lo >= start ? 0 : 1) : -1;
         sg_ncontrib = partial ? owner(end - 1) - owner(start) + 1 : 1;
         sg_end = end;
         sg_new = s_hi == end && L > 0;           // the item's last step, holding its newest token
@@ -932,7 +955,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     }
     const int nR = __builtin_popcountll(__ballot(sg_ok));   // valid segments are lanes 0 .. nR-1
     if (lane >= nR) sg_nstep = 0, sg_new = false;
-    const int sg_incl = wave_incl_scan(sg_nstep, lane);
+    const int sg_incl = wave_incl_scan(sg_nstep);
     const int sg_first = sg_incl - sg_nstep;                 // first step of segment `lane` in the round
     const int T = __builtin_amdgcn_readlane(sg_incl, nR - 1);
     if (wave == 0 && lane < nR) {
@@ -1297,7 +1320,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         if (!flags[k]) continue;
         const int32_t* r = rec + 8 * k;
         const int b = r[kRecB], hk = r[kRecHk];
-        const int steps = (base[b + 1] - base[b]) / Hi;
+        const int steps = seq_steps<NP>(lens[b]);
         const int start = base[b] + hk * steps;
         const int w0 = owner(start), n = r[kRecNContrib];
         // partial of contributor w0 + i: slot 2w if the item begins its share, else 2w + 1

@@ -47,6 +47,27 @@ template <int XOR> __device__ __forceinline__ double quad_swap(double v) {
   return __hiloint2double(hi, lo);
 }
 
+// Value of `v` held by lane ^ M (M = 1, 2, 4 or 8, inside the lane's 16-lane
+// row) via DPP; p = the lane index modulo 16.  M = 4 takes lane + 4 (row_shl:4)
+// where bit 2 of p is clear and lane - 4 (row_shr:4) where it is set; M = 8 is
+// row_ror:8.
+template <int M> __device__ __forceinline__ double lane_xor16(double v, int p) {
+  if constexpr (M == 1 || M == 2) {
+    return quad_swap<M>(v);
+  } else {
+    constexpr int c0 = M == 4 ? 0x104 : 0x128;
+    const int lo0 = __builtin_amdgcn_mov_dpp(__double2loint(v), c0, 0xF, 0xF, true);
+    const int hi0 = __builtin_amdgcn_mov_dpp(__double2hiint(v), c0, 0xF, 0xF, true);
+    if constexpr (M == 8) {
+      return __hiloint2double(hi0, lo0);
+    } else {
+      const int lo1 = __builtin_amdgcn_mov_dpp(__double2loint(v), 0x114, 0xF, 0xF, true);
+      const int hi1 = __builtin_amdgcn_mov_dpp(__double2hiint(v), 0x114, 0xF, 0xF, true);
+      return (p & 4) ? __hiloint2double(hi1, lo1) : __hiloint2double(hi0, lo0);
+    }
+  }
+}
+
 // Sylvester butterfly over the 32 values a lane holds (stages h = 1..16).
 __device__ __forceinline__ void wht32_inlane(double (&x)[32]) {
 #pragma unroll
@@ -132,24 +153,26 @@ __device__ __forceinline__ float f32_round_to_odd(double r) {
   return __uint_as_float(((uint32_t)__double2hiint(r) & 0x80000000u) | mag | sticky);
 }
 
-// OCP E4M3 byte of a float64: nearest, ties to even, |v| > 448 -> 448, sign
-// copied (also for zero).  Subnormals have quantum 2^-9.
-__device__ __forceinline__ uint32_t e4m3_from_f64(double v) {
-  const double a = fabs(v);
-  const uint32_t sign = ((uint32_t)__double2hiint(v)) >> 31;
-  uint32_t code;
-  if (a > 448.0) {
-    code = 0x7E;
-  } else if (a < 0x1p-6) {
-    code = (uint32_t)__builtin_rint(a * 512.0);             // 0..8 (8 = 2^-6)
-  } else {
-    int ex;
-    (void)frexp(a, &ex);                                     // a in [2^(ex-1), 2^ex)
-    const int e = ex - 1;                                    // -6..8
-    const int n = (int)__builtin_rint(ldexp(a, 3 - e));     // 8..16 (16 carries)
-    code = (uint32_t)((e + 7) * 8 + n - 8);
-  }
-  return code | (sign << 7);
+// OCP E4M3 bytes (nearest, ties to even, |v| > 448 -> 448, sign copied, also
+// for zero; subnormal quantum 2^-9) of four values, byte i from the i-th.  The
+// hardware converter v_cvt_pk_fp8_f32 (probed on gfx950 over every E4M3 value,
+// the midpoints and one ulp either side, subnormals and signed zeros: nearest
+// even, OCP encoding) takes float32 inputs within +-448.
+__device__ __forceinline__ uint32_t e4m3x4_f32(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -448.f, 448.f);
+  b = __builtin_amdgcn_fmed3f(b, -448.f, 448.f);
+  c = __builtin_amdgcn_fmed3f(c, -448.f, 448.f);
+  d = __builtin_amdgcn_fmed3f(d, -448.f, 448.f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+// The same for float64 values: clamped to +-448 in float64, then rounded to
+// float32 by round to odd, which keeps the nearest-even decision onto the
+// 4-bit significand (and the sign of zero).
+__device__ __forceinline__ uint32_t e4m3x4_f64(double a, double b, double c, double d) {
+  auto f = [](double v) { return f32_round_to_odd(fmin(fmax(v, -448.0), 448.0)); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f(a), f(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f(c), f(d), lo, true);
 }
 
 // bf16 bits of a float, round to nearest even (finite inputs).

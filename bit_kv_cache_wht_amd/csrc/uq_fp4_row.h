@@ -18,16 +18,12 @@
 
 namespace uq {
 
-// Partner value of lane ^ M (M < 16, within the row's lane group).
-template <int M> __device__ __forceinline__ double lane_xor(double v) {
-  if constexpr (M == 1 || M == 2) return quad_swap<M>(v);
-  else return __shfl_xor(v, M);
-}
-
+// Butterfly stage between lane parts p and p ^ M (the row's lanes are aligned
+// to their count, so p ^ M is lane ^ M).
 template <int E, int M> __device__ __forceinline__ void cross_stage(double (&x)[E], int p) {
   const double sgn = (p & M) ? -1.0 : 1.0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) x[e] = __builtin_fma(x[e], sgn, lane_xor<M>(x[e]));
+  for (int e = 0; e < E; ++e) x[e] = __builtin_fma(x[e], sgn, lane_xor16<M>(x[e], p));
 }
 
 template <int D, int IN, int LPR> struct Fp4Row {
