@@ -74,7 +74,8 @@ def lib() -> ctypes.CDLL:
 @dataclass
 class KvCache:
     """Descriptor of a paged K/V cache; pools are caller-owned uint8 device tensors
-    of shape [num_pages][num_kv_heads][head block bytes]."""
+    of shape [num_pages][uq_page_bytes]; head h's block of a page starts at byte
+    h * head block bytes (``blocks`` views them as [num_pages][num_kv_heads][block])."""
     format: int
     num_pages: int
     num_kv_heads: int
@@ -88,10 +89,17 @@ class KvCache:
         blk = uq_head_block_bytes(fmt, head_dim)
         if blk == 0:
             raise UqError("uq_head_block_bytes", UQ_ERR_UNSUPPORTED)
+        pb = lib().uq_page_bytes(ctypes.byref(_Cache(fmt, num_pages, UQ_PAGE_SIZE, num_kv_heads, head_dim,
+                                                      None, None)))
         alloc = torch.zeros if zero else torch.empty
-        k = alloc((num_pages, num_kv_heads, blk), dtype=torch.uint8, device=device)
-        v = alloc((num_pages, num_kv_heads, blk), dtype=torch.uint8, device=device)
+        k = alloc((num_pages, pb), dtype=torch.uint8, device=device)
+        v = alloc((num_pages, pb), dtype=torch.uint8, device=device)
         return cls(fmt, num_pages, num_kv_heads, head_dim, k, v)
+
+    def blocks(self, pool):
+        """[num_pages][num_kv_heads][head block bytes] view of a pool (no copy)."""
+        blk = uq_head_block_bytes(self.format, self.head_dim)
+        return pool.as_strided((self.num_pages, self.num_kv_heads, blk), (pool.stride(0), blk, 1))
 
     def c(self) -> _Cache:
         return _Cache(self.format, self.num_pages, UQ_PAGE_SIZE, self.num_kv_heads, self.head_dim,

@@ -119,7 +119,15 @@ size_t uq_head_block_bytes(int32_t format, int32_t head_dim) {
 
 size_t uq_page_bytes(const uq_kv_cache* c) {
   if (c == nullptr || c->num_kv_heads < 1 || c->page_size != UQ_PAGE_SIZE) return 0;
-  return (size_t)c->num_kv_heads * uq_head_block_bytes(c->format, c->head_dim);
+  size_t b = (size_t)c->num_kv_heads * uq_head_block_bytes(c->format, c->head_dim);
+  // FP4 head blocks are 8.5 (d = 128) or 4.25 (d = 64) lines of 128 B, so the
+  // blocks of a page start at different offsets modulo 512 B; when a page is a
+  // whole number of 512-B units, every page would repeat the same offsets and
+  // the heads whose blocks start at the slower offsets would always stream
+  // slower.  One extra line makes consecutive pages start at all four 128-B
+  // offsets modulo 512.
+  if (c->format == UQ_KV_FP4 && b != 0 && b % 512 == 0) b += 128;
+  return b;
 }
 
 int uq_quantize_append(const uq_kv_cache* cache, const void* k_new, const void* v_new, int32_t in_dtype,

@@ -38,8 +38,10 @@
  *   any launch; device-resident contents (page ids, slots, lengths) are trusted:
  *   an out-of-range value there is undefined behaviour.
  *
- * Paged layout (part of the ABI).  A pool is [num_pages][num_kv_heads][block];
- * token position t of a sequence lives in page page_table[t / 16] at slot t % 16.
+ * Paged layout (part of the ABI).  A pool is [num_pages][uq_page_bytes]; a page
+ * holds the num_kv_heads head-blocks back to back from its first byte (FP4
+ * pages may end in 128 unused bytes, see uq_page_bytes); token position t of a
+ * sequence lives in page page_table[t / 16] at slot t % 16.
  * Head-block layouts (d = head_dim, 16 slots):
  *   FP4  K: codes [16 slot][d/2 B] (byte j: channel 2j low nibble, 2j+1 high),
  *           then scales [slot % 4][d/32 group][slot / 4]       = 17*d/2 bytes
@@ -85,7 +87,8 @@ typedef struct uq_kv_cache {
   int32_t page_size;     /* tokens per page; must be 16                          */
   int32_t num_kv_heads;  /* >= 1                                                 */
   int32_t head_dim;      /* 64 or 128                                            */
-  void* k_pool;          /* device, [num_pages][num_kv_heads][block], 256-B aligned */
+  void* k_pool;          /* device, [num_pages][uq_page_bytes], 256-B aligned; head h's
+                            block of a page starts at byte h * uq_head_block_bytes */
   void* v_pool;          /* device, same shape                                    */
 } uq_kv_cache;
 
@@ -93,7 +96,11 @@ typedef struct uq_kv_cache {
  * BF16 32*d; 0 for an unknown format or head_dim.  Host only. */
 size_t uq_head_block_bytes(int32_t format, int32_t head_dim);
 
-/* Bytes of one page of one pool (num_kv_heads head-blocks); 0 if invalid. */
+/* Bytes of one page of one pool: num_kv_heads head-blocks, plus, for FP4 when
+ * those fill a whole number of 512-B units, one 128-B line that nothing reads or
+ * writes (so that consecutive pages begin at different offsets modulo 512 B: on
+ * MI355X, 8.5-line head-block pairs that always start at the same such offset
+ * stream up to ~5% slower than others).  0 if invalid. */
 size_t uq_page_bytes(const uq_kv_cache* cache);
 
 /*

@@ -53,8 +53,8 @@ def gpu_cache(fmt, wl, pools=None):
     m = uq()
     c = m.KvCache.allocate(FMT_ID[fmt], wl.num_pages, wl.num_kv_heads, wl.head_dim)
     if pools is not None:
-        c.k_pool.copy_(dev(pools[0]))
-        c.v_pool.copy_(dev(pools[1]))
+        c.blocks(c.k_pool).copy_(dev(pools[0]))
+        c.blocks(c.v_pool).copy_(dev(pools[1]))
     return c
 
 
@@ -79,8 +79,21 @@ def oracle_append(fmt, wl, idx=None, slots=None):
     return kp, vp
 
 
+def page_blocks_np(cache, pool, idx=None):
+    """Pages `idx` (default all) of a device pool as numpy [n][H][block], after
+    checking that the bytes past the head blocks of each page (the FP4 page
+    padding) are still zero."""
+    torch = torch_mod()
+    rows = pool if idx is None else pool.index_select(0, torch.from_numpy(np.asarray(idx, np.int64)).cuda())
+    a = rows.cpu().numpy()
+    blk = uq().uq_head_block_bytes(cache.format, cache.head_dim)
+    used = cache.num_kv_heads * blk
+    assert not a[:, used:].any(), "bytes past the head blocks of a page were written"
+    return np.ascontiguousarray(a[:, :used]).reshape(a.shape[0], cache.num_kv_heads, blk)
+
+
 def pools_np(cache):
-    return cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
+    return page_blocks_np(cache, cache.k_pool), page_blocks_np(cache, cache.v_pool)
 
 
 def gpu_decode(fmt, wl, cache, flags=0, seq_lens=None, q=None):

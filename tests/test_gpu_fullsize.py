@@ -19,7 +19,7 @@ import oracle as O
 from bit_kv_cache_wht_amd import workloads as W
 
 from gpu_util import FMT_ID, announce, assert_close, gpu_append, gpu_decode, oracle_decode_rows_from_inputs, \
-    torch_mod
+    page_blocks_np, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,6 @@ def _free():
 def _check_pages(fmt, wl, cache, n_pages, seed):
     """Sampled whole pages of the GPU pools against the oracle's pages holding the
     same tokens (remapped to a compact pool)."""
-    torch = torch_mod()
     rng = np.random.default_rng(seed)
     page_of = wl.slot_mapping // 16
     used = np.unique(page_of)
@@ -43,9 +42,8 @@ def _check_pages(fmt, wl, cache, n_pages, seed):
     kp, vp = O.new_pool(FMT_ID[fmt], pages.size, wl.num_kv_heads, wl.head_dim), \
         O.new_pool(FMT_ID[fmt], pages.size, wl.num_kv_heads, wl.head_dim)
     O.append(FMT_ID[fmt], kp, vp, wl.k[tok], wl.v[tok], remap.astype(np.int32), in_dtype=wl.in_dtype)
-    idx = torch.from_numpy(pages.astype(np.int64)).cuda()
-    got_k = cache.k_pool.index_select(0, idx).cpu().numpy().reshape(kp.shape)
-    got_v = cache.v_pool.index_select(0, idx).cpu().numpy().reshape(vp.shape)
+    got_k = page_blocks_np(cache, cache.k_pool, pages)
+    got_v = page_blocks_np(cache, cache.v_pool, pages)
     announce(f"{fmt} {wl.name}: {pages.size} sampled pages, {tok.size} tokens")
     assert np.array_equal(got_k, kp), f"{fmt} {wl.name}: K pages differ from the oracle"
     assert np.array_equal(got_v, vp), f"{fmt} {wl.name}: V pages differ from the oracle"

@@ -24,7 +24,7 @@ import oracle as O
 from bit_kv_cache_wht_amd import workloads as W
 
 from gpu_util import (FMT_ID, announce, assert_close, dev, gpu_append, gpu_cache, gpu_decode, oracle_append,
-                      oracle_decode, oracle_decode_rows_from_inputs, pools_np, torch_mod, uq)
+                      oracle_decode, oracle_decode_rows_from_inputs, page_blocks_np, pools_np, torch_mod, uq)
 from test_gpu_parity import SMALL, _wl
 
 pytestmark = pytest.mark.gpu
@@ -115,7 +115,6 @@ def test_fused_step_small(name):
 def _check_new_pages(wl, cache, seqs, extra, seed):
     """Pages holding the new tokens of `seqs` plus `extra` random pages, whole,
     against the oracle's pages built from the tokens that live in them."""
-    torch = torch_mod()
     rng = np.random.default_rng(seed)
     lens = wl.seq_lens.astype(np.int64)
     page_of = wl.slot_mapping // 16
@@ -126,9 +125,8 @@ def _check_new_pages(wl, cache, seqs, extra, seed):
     kp = O.new_pool(FMT_ID["fp4"], pages.size, wl.num_kv_heads, wl.head_dim)
     vp = O.new_pool(FMT_ID["fp4"], pages.size, wl.num_kv_heads, wl.head_dim)
     O.append(FMT_ID["fp4"], kp, vp, wl.k[tok], wl.v[tok], remap.astype(np.int32), in_dtype=wl.in_dtype)
-    idx = torch.from_numpy(pages.astype(np.int64)).cuda()
-    got_k = cache.k_pool.index_select(0, idx).cpu().numpy().reshape(kp.shape)
-    got_v = cache.v_pool.index_select(0, idx).cpu().numpy().reshape(vp.shape)
+    got_k = page_blocks_np(cache, cache.k_pool, pages)
+    got_v = page_blocks_np(cache, cache.v_pool, pages)
     announce(f"fused {wl.name}: {pages.size} sampled pages ({len(seqs)} with new tokens)")
     assert np.array_equal(got_k, kp), "K pages differ from the oracle"
     assert np.array_equal(got_v, vp), "V pages differ from the oracle"
