@@ -120,13 +120,19 @@ size_t uq_head_block_bytes(int32_t format, int32_t head_dim) {
 size_t uq_page_bytes(const uq_kv_cache* c) {
   if (c == nullptr || c->num_kv_heads < 1 || c->page_size != UQ_PAGE_SIZE) return 0;
   size_t b = (size_t)c->num_kv_heads * uq_head_block_bytes(c->format, c->head_dim);
-  // FP4 head blocks are 8.5 (d = 128) or 4.25 (d = 64) lines of 128 B, so the
-  // blocks of a page start at different offsets modulo 512 B; when a page is a
-  // whole number of 512-B units, every page would repeat the same offsets and
-  // the heads whose blocks start at the slower offsets would always stream
-  // slower.  One extra line makes consecutive pages start at all four 128-B
-  // offsets modulo 512.
-  if (c->format == UQ_KV_FP4 && b != 0 && b % 512 == 0) b += 128;
+  // Pages that are a whole number of 512-B units would put every page's head
+  // blocks at the same address offsets, and on MI355X some offsets stream
+  // slower.  FP4 head blocks are 8.5 (d = 128) or 4.25 (d = 64) lines of 128 B,
+  // so a page's pairs start at different 128-B offsets modulo 512 B and the pair
+  // at the slowest one set the launch time: one extra line makes consecutive
+  // pages start at all four.  FP8 pages (16 KB for 8 heads of d = 128) decoded
+  // at 254 us with 2-KB-aligned pools against 167-170 us at other alignments:
+  // 256 extra bytes make it 169 us whatever the pool's alignment.  BF16 pages
+  // showed no such effect and are not padded.
+  if (b != 0 && b % 512 == 0) {
+    if (c->format == UQ_KV_FP4) b += 128;
+    else if (c->format == UQ_KV_FP8) b += 256;
+  }
   return b;
 }
 

@@ -39,8 +39,8 @@
  *   an out-of-range value there is undefined behaviour.
  *
  * Paged layout (part of the ABI).  A pool is [num_pages][uq_page_bytes]; a page
- * holds the num_kv_heads head-blocks back to back from its first byte (FP4
- * pages may end in 128 unused bytes, see uq_page_bytes); token position t of a
+ * holds the num_kv_heads head-blocks back to back from its first byte (FP4 and
+ * FP8 pages may end in unused bytes, see uq_page_bytes); token position t of a
  * sequence lives in page page_table[t / 16] at slot t % 16.
  * Head-block layouts (d = head_dim, 16 slots):
  *   FP4  K: codes [16 slot][d/2 B] (byte j: channel 2j low nibble, 2j+1 high),
@@ -96,11 +96,12 @@ typedef struct uq_kv_cache {
  * BF16 32*d; 0 for an unknown format or head_dim.  Host only. */
 size_t uq_head_block_bytes(int32_t format, int32_t head_dim);
 
-/* Bytes of one page of one pool: num_kv_heads head-blocks, plus, for FP4 when
- * those fill a whole number of 512-B units, one 128-B line that nothing reads or
- * writes (so that consecutive pages begin at different offsets modulo 512 B: on
- * MI355X, 8.5-line head-block pairs that always start at the same such offset
- * stream up to ~5% slower than others).  0 if invalid. */
+/* Bytes of one page of one pool: num_kv_heads head-blocks, plus, when those fill
+ * a whole number of 512-B units, bytes that nothing reads or writes: 128 for FP4
+ * (so that consecutive pages begin at different offsets modulo 512 B: on MI355X,
+ * 8.5-line head-block pairs that always start at the same such offset stream up
+ * to ~5% slower than others), 256 for FP8 (16-KB pages read up to 1.5x slower
+ * at some pool alignments), none for BF16.  0 if invalid. */
 size_t uq_page_bytes(const uq_kv_cache* cache);
 
 /*

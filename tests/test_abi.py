@@ -39,9 +39,11 @@ def cache(fmt=B.UQ_KV_FP4, pages=4, heads=2, d=128, page_size=16, k=FAKE, v=FAKE
 def test_block_sizes_match_oracle_layout(fmt, d):
     assert uq.uq_head_block_bytes(fmt, d) == O.head_block_bytes(fmt, d)
     c = cache(fmt, heads=8, d=d)
-    # FP4 pages whose head blocks fill whole 512-B units get one more 128-B line
+    # pages whose head blocks fill whole 512-B units get 128 (FP4) or 256 (FP8)
+    # more bytes
     want = O.page_bytes(fmt, 8, d)
-    want += 128 if fmt == uq.UQ_KV_FP4 and want % 512 == 0 else 0
+    if want % 512 == 0:
+        want += {uq.UQ_KV_FP4: 128, uq.UQ_KV_FP8: 256}.get(fmt, 0)
     assert uq.lib().uq_page_bytes(ctypes.byref(c)) == want
 
 
