@@ -36,6 +36,12 @@ Readings where the pages are silent (each listed with its reason in the design doc):
   R7  sm_scale multiplies the logits; GQA maps query head h to KV head
       h // (H_q / H_kv).
   R8  Cache page layout: see ``head_block_bytes`` and the ``*_offset`` helpers.
+  R9  constOpt scale mode (``scale_mode="constopt"``): s = c * m rounded once to
+      float64 (c = 0.156 by default), E = the integer nearest to log2(s) (the
+      log domain: the pages' "power-of-two-optimal" constant 0.195 is the
+      optimum of that rule on rotated unit vectors, where linear-domain rounding
+      would put it near 0.207), clamped to [-127, 127], m == 0 giving -127;
+      codes then saturate at +-6 as in R4.
 
 Parity pins: tests/test_oracle_pins.py (no function here is "parity unpinned").
 """
@@ -46,7 +52,8 @@ import numpy as np
 __all__ = [
     "PAGE_SIZE", "GROUP", "FMT_FP4", "FMT_FP8", "FMT_BF16",
     "sylvester_hadamard", "wht_scale", "wht",
-    "scale_exponent", "E2M1_LEVELS", "e2m1_encode", "e2m1_decode",
+    "scale_exponent", "CONSTOPT_C", "SQRT2_UP", "scale_exponent_constopt",
+    "E2M1_LEVELS", "e2m1_encode", "e2m1_decode",
     "quantize_fp4", "dequantize_fp4", "pack_nibbles", "unpack_nibbles",
     "e4m3_decode", "e4m3_encode", "bf16_bits_to_f64", "f32_to_f64", "bf16_round_bits",
     "head_block_bytes", "page_bytes", "new_pool",
@@ -120,6 +127,33 @@ def scale_exponent(m) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# constOpt group scale ([review] §3.1 and §3.3 "constant-optimized scaling": the
+# absmax times a global constant c, stored as the nearest power of two, c = 0.156
+# from offline calibration; §6.2 ablation of c; [commentary] footnote 13; R9)
+# --------------------------------------------------------------------------
+CONSTOPT_C = 0.156
+SQRT2_UP = float.fromhex("0x1.6a09e667f3bcdp+0")     # the least double above sqrt(2)
+
+
+def scale_exponent_constopt(m, c=CONSTOPT_C) -> np.ndarray:
+    """The integer nearest to log2(s), s = c * m rounded once to float64, clamped to
+    [-127, 127]; m == 0 gives -127.
+
+    With s = M * 2**e, M in [1, 2): E = e + 1 when M > sqrt(2), else e.  sqrt(2)
+    is irrational, so no double equals it (no ties) and M > sqrt(2) exactly when
+    M >= SQRT2_UP.
+    """
+    m = np.asarray(m, dtype=np.float64)
+    s = np.float64(c) * m
+    out = np.full(m.shape, -127, dtype=np.int64)
+    nz = s > 0
+    frac, ex = np.frexp(s[nz])                               # s = frac * 2**ex, frac in [0.5, 1)
+    e = (ex - 1).astype(np.int64) + (2.0 * frac >= SQRT2_UP)
+    out[nz] = np.clip(e, -127, 127)
+    return out
+
+
+# --------------------------------------------------------------------------
 # FP4 E2M1 codes ([review] §3.1 table "Code grid", §6.5; readings R4, R5)
 # --------------------------------------------------------------------------
 E2M1_LEVELS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])  # magnitude codes 0..7
@@ -157,8 +191,9 @@ def e2m1_decode(code) -> np.ndarray:
     return np.where(code & 8, -mag, mag)
 
 
-def quantize_fp4(x):
-    """Quantize rotated rows x[..., d] per 32-channel group.
+def quantize_fp4(x, scale_mode="absmax", c=CONSTOPT_C):
+    """Quantize rotated rows x[..., d] per 32-channel group; the scale exponent is
+    R3's (``scale_mode="absmax"``) or R9's (``"constopt"``, constant c).
 
     Returns (codes [..., d] uint8 in 0..15, scale bytes [..., d/32] uint8).
     """
@@ -166,7 +201,12 @@ def quantize_fp4(x):
     d = x.shape[-1]
     g = x.reshape(x.shape[:-1] + (d // GROUP, GROUP))
     m = np.max(np.abs(g), axis=-1)                    # group absmax
-    e = scale_exponent(m)
+    if scale_mode == "absmax":
+        e = scale_exponent(m)
+    elif scale_mode == "constopt":
+        e = scale_exponent_constopt(m, c)
+    else:
+        raise ValueError(scale_mode)
     r = np.ldexp(g, -e[..., None])                    # exact division by 2**E
     codes = e2m1_encode(r).reshape(x.shape)
     return codes, (e + 127).astype(np.uint8)
@@ -307,12 +347,13 @@ def bf16_v_index(tok, ch, d):
     return ch * PAGE_SIZE + tok
 
 
-def append(fmt, k_pool, v_pool, k_new, v_new, slot_mapping, in_dtype="bf16"):
+def append(fmt, k_pool, v_pool, k_new, v_new, slot_mapping, in_dtype="bf16", scale_mode="absmax"):
     """Write new tokens into the paged pools in place.
 
     k_new, v_new: [T][H_kv][d] as bf16 bits (uint16, in_dtype "bf16") or float32
     (in_dtype "f32").  slot_mapping[t] = page * 16 + offset; a negative slot skips
-    the token.  FP4 rotates and quantizes ([review] §3.1); FP8 rounds each value to
+    the token.  FP4 rotates and quantizes ([review] §3.1; ``scale_mode`` as in
+    ``quantize_fp4``, constOpt with c = 0.156); FP8 rounds each value to
     E4M3 with scale 1; BF16 stores the value (float32 input rounded to bf16).
     """
     k_new = np.asarray(k_new)
@@ -325,7 +366,7 @@ def append(fmt, k_pool, v_pool, k_new, v_new, slot_mapping, in_dtype="bf16"):
         flat = pool.reshape(pool.shape[0], H, -1)
         x = to64(src[keep])                                   # [n][H][d] exact
         if fmt == FMT_FP4:
-            codes, sbytes = quantize_fp4(wht(x))              # [n][H][d], [n][H][d/32]
+            codes, sbytes = quantize_fp4(wht(x), scale_mode)  # [n][H][d], [n][H][d/32]
             packed = pack_nibbles(codes)                      # [n][H][d/2]
             j = np.arange(d // 2)
             g = np.arange(d // GROUP)

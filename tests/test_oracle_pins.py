@@ -145,6 +145,86 @@ def test_scale_exponent_never_clips_in_range():
     assert np.all(m <= np.ldexp(6.0, e)) and np.all(m > np.ldexp(6.0, e - 1))
 
 
+# ---------------------------------------------------------------- constOpt scale (R9)
+def test_sqrt2_up_brackets_sqrt2():
+    # SQRT2_UP is the least double above sqrt(2): its square exceeds 2 and the
+    # previous double's square is below 2 (exact rational arithmetic)
+    up = Fraction(O.SQRT2_UP)
+    below = Fraction(float(np.nextafter(O.SQRT2_UP, 0.0)))
+    assert up * up > 2 > below * below
+
+
+def _nearest_log2(s: float) -> int:
+    """The integer nearest to log2(s) for a double s > 0, by exact comparison of
+    s^2 with 2^(2k+1) (sqrt(2) is irrational, so there are no ties)."""
+    q = Fraction(s)
+    k = math.floor(math.log2(s))
+    while Fraction(2) ** k > q:
+        k -= 1
+    while Fraction(2) ** (k + 1) <= q:
+        k += 1
+    return k + 1 if q * q > Fraction(2) ** (2 * k + 1) else k
+
+
+def test_constopt_exponent_against_exact_log2_rounding():
+    rng = np.random.default_rng(11)
+    for c in (O.CONSTOPT_C, 0.195, 1.0):
+        m = list(np.exp(rng.uniform(-80, 80, 400)))
+        for k in range(-130, 130, 9):        # products just either side of sqrt(2) * 2^k
+            t = O.SQRT2_UP * 2.0 ** k / c
+            m += [t, np.nextafter(t, 0), np.nextafter(t, np.inf), 2.0 ** k / c]
+        m = np.array(m)
+        got = O.scale_exponent_constopt(m, c)
+        for mi, e in zip(m, got):
+            s = float(np.float64(c) * mi)
+            want = -127 if s == 0 else min(127, max(-127, _nearest_log2(s)))
+            assert e == want, (c, mi, s, e, want)
+
+
+def test_constopt_worked_values_log_domain():
+    # c = 1: s = m.  0.72 is nearer 1 than 0.5 in log2 (-0.47) though nearer 0.5
+    # on the line; 0.70 is nearer 0.5 in both.  1.4 -> 2^0, 1.5 -> 2^1.
+    e = O.scale_exponent_constopt(np.array([0.72, 0.70, 1.0, 1.4, 1.5, 0.0, 1e300, 1e-300]), 1.0)
+    assert list(e) == [0, -1, 0, 0, 1, -127, 127, -127]
+
+
+def test_constopt_codes_saturate_at_six():
+    # absmax m = 1 / 0.156 gives s = c m = 1 (E = 0): the absmax element
+    # (6.41 before scaling) saturates to the top code, 6.0
+    m = 1.0 / O.CONSTOPT_C
+    x = np.zeros((1, 32))
+    x[0, 0], x[0, 1], x[0, 2] = m, -m, 1.25
+    codes, sb = O.quantize_fp4(x, "constopt")
+    assert sb[0, 0] == 127
+    assert codes[0, 0] == 7 and codes[0, 1] == 15 and codes[0, 2] == 2     # 1.25 -> 1.0 (tie to even)
+    assert O.dequantize_fp4(codes, sb)[0, 0] == 6.0
+    # the absmax rule never clips: the same group gets E = 1 (6.41 <= 12)
+    codes2, sb2 = O.quantize_fp4(x)
+    assert sb2[0, 0] == 128 and codes2[0, 0] == 5                            # 6.41 / 2 = 3.2 -> 3.0 (code 5)
+
+
+def test_constopt_power_of_two_optimum_matches_pages():
+    # [review] §3.3 / §6.2, [commentary] footnote 13: c = 0.195 is the optimum of
+    # the power-of-two rule (0.156 being the optimum of an unconstrained scale).
+    # On rotated unit vectors the quantizer's MSE under R9 is least at 0.195; the
+    # paper's default 0.156 and raw absmax (c = 1) are worse under the same rule.
+    g = golden("constopt_constants.json")
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((2000, 128))
+    y = O.wht(x / np.linalg.norm(x, axis=1, keepdims=True))
+
+    def mse(c):
+        codes, sb = O.quantize_fp4(y, "constopt", c)
+        return np.mean(np.sum((O.dequantize_fp4(codes, sb) - y) ** 2, axis=1))
+
+    cs = np.round(np.arange(0.180, 0.2101, 0.005), 3)
+    errs = [mse(c) for c in cs]
+    best = cs[int(np.argmin(errs))]
+    assert abs(best - g["c_power_of_two_optimal"]) <= 0.005, (best, errs)
+    assert mse(g["c_default_mse_optimal"]) > min(errs)
+    assert mse(g["c_raw_absmax"]) > mse(g["c_default_mse_optimal"])
+
+
 # ---------------------------------------------------------------- E2M1
 def _e2m1_from_bits(code):
     """Value of an E2M1 bit pattern from the format: 1 sign, 2 exponent (bias 1),
