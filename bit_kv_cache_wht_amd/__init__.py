@@ -8,6 +8,7 @@ with ``python -m bit_kv_cache_wht_amd.build``).
 """
 from ._binding import (  # noqa: F401
     UQ_FLAG_OUT_ROTATED,
+    UQ_FLAG_SCALE_CONSTOPT,
     UQ_IN_BF16,
     UQ_IN_F32,
     UQ_KV_BF16,

@@ -10,6 +10,7 @@ UQ_KV_FP4, UQ_KV_FP8, UQ_KV_BF16 = 0, 1, 2
 UQ_IN_BF16, UQ_IN_F32 = 0, 1
 UQ_PAGE_SIZE = 16
 UQ_FLAG_OUT_ROTATED = 1
+UQ_FLAG_SCALE_CONSTOPT = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libuq.so")
 

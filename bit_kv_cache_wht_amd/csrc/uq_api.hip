@@ -35,7 +35,8 @@ int append_common(const uq_kv_cache* cache, int format, const void* k_new, const
                   append_launcher launch) {
   int st = check_cache(cache, format);
   if (st != UQ_OK) return st;
-  if (flags != 0u) return UQ_ERR_INVALID_ARG;
+  const uint32_t allowed = format == UQ_KV_FP4 ? UQ_FLAG_SCALE_CONSTOPT : 0u;
+  if ((flags & ~allowed) != 0u) return UQ_ERR_INVALID_ARG;
   if (in_dtype != UQ_IN_BF16 && in_dtype != UQ_IN_F32) return UQ_ERR_INVALID_ARG;
   if (num_tokens < 0) return UQ_ERR_INVALID_ARG;
   if (num_tokens == 0) return UQ_OK;
@@ -49,6 +50,7 @@ int append_common(const uq_kv_cache* cache, int format, const void* k_new, const
   a.page_bytes = (int64_t)uq_page_bytes(cache);
   a.T = num_tokens;
   a.H = cache->num_kv_heads;
+  a.constopt = (flags & UQ_FLAG_SCALE_CONSTOPT) ? 1 : 0;
   return hip_status(launch(a, cache->head_dim, in_dtype, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -58,7 +60,9 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
                   uq_stream_t stream, const void* k_new = nullptr, const void* v_new = nullptr) {
   int st = check_cache(cache, format);
   if (st != UQ_OK) return st;
-  const uint32_t allowed = format == UQ_KV_FP4 ? UQ_FLAG_OUT_ROTATED : 0u;
+  // the constOpt bit selects the scale rule of the fused step's write
+  const uint32_t allowed = format != UQ_KV_FP4 ? 0u
+                           : UQ_FLAG_OUT_ROTATED | (k_new != nullptr ? UQ_FLAG_SCALE_CONSTOPT : 0u);
   if ((flags & ~allowed) != 0u) return UQ_ERR_INVALID_ARG;
   if (q_dtype != UQ_IN_BF16 && q_dtype != UQ_IN_F32) return UQ_ERR_INVALID_ARG;
   if (format == UQ_KV_BF16 && q_dtype != UQ_IN_BF16) return UQ_ERR_UNSUPPORTED;
@@ -95,6 +99,7 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   a.ws = static_cast<uint8_t*>(workspace);
   a.lay = uq::decode_layout(format, num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim);
   a.unrotate = format == UQ_KV_FP4 && !(flags & UQ_FLAG_OUT_ROTATED);
+  a.constopt = (flags & UQ_FLAG_SCALE_CONSTOPT) != 0u;
   a.k_new = k_new;
   a.v_new = v_new;
   a.ev_start = g_prof_start;

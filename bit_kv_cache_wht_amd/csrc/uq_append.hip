@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
 
   Row x;
   x.load(is_v ? a.v : a.k, tr, p);
-  x.quantize(p);
+  x.quantize(p, a.constopt != 0);
   if (!in_range || slot < 0) return;
   const int page = slot >> 4, off = slot & 15;
   uint8_t* blk = (is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes + (int64_t)h * Row::BLK;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void append_fp4_stream_kernel(AppendArgs a) {
     const int gn = g + nwaves;
     const bool more = gn < groups;                 // wave-uniform
     if (more) fetch(nxt, gn);
-    cur.x.quantize(p);
+    cur.x.quantize(p, a.constopt != 0);
     if (cur.live && cur.slot >= 0) {
       const int h = cur.tr % a.H;
       const int page = cur.slot >> 4, off = cur.slot & 15;

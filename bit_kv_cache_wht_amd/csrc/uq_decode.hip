@@ -773,8 +773,9 @@ __device__ void store_row32(float (&o)[D / 32], float l, float* dst, bool live, 
 
 // Quantizes and stores a row of the fused step's newest token.
 template <class Row>
-__device__ __forceinline__ void write_new(Row& row, uint8_t* blk, int off, bool live, bool is_v, int p) {
-  row.quantize(p);
+__device__ __forceinline__ void write_new(Row& row, uint8_t* blk, int off, bool live, bool is_v, int p,
+                                          bool constopt) {
+  row.quantize(p, constopt);
   if (live) {
     if (is_v) row.store_v(blk, off, p);
     else row.store_k(blk, off, p);
@@ -797,6 +798,7 @@ struct KArgs {
   int32_t R;                 // items per round of a workgroup
   const void* k_new;         // fused step (FP4): the newest token's K and V, [B][Hkv][D]
   const void* v_new;         // in the query's dtype; null: attention only
+  int32_t constopt;          // fused step: constOpt group scales for the written token
 };
 
 // Split partials cross workgroups that may sit on different compute dies,
@@ -1023,7 +1025,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         }
         if (__ballot(sg_new && sg_first + sg_nstep <= NW * (N + 1)) != 0) {
           if (nwrite) {
-            write_new(nrow, nblk, noff, nlive, nv, np);
+            write_new(nrow, nblk, noff, nlive, nv, np, a.constopt != 0);
             nwrite = false;
           }
           __syncthreads();
@@ -1101,7 +1103,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     ck = claim_at(g0[N]);
     meta[N] = ck.meta;
     if constexpr (FMT == UQ_KV_FP4) {
-      if (nwrite) write_new(nrow, nblk, noff, nlive, nv, np);   // ordered before the main loop's claims by its barrier
+      if (nwrite) write_new(nrow, nblk, noff, nlive, nv, np, a.constopt != 0);   // ordered before the main loop's claims by its barrier
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -1449,6 +1451,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   k.cnt = reinterpret_cast<int32_t*>(a.ws + L.cnt);
   k.k_new = a.k_new;
   k.v_new = a.v_new;
+  k.constopt = a.constopt ? 1 : 0;
   hipError_t e;
   if (a.ev_start != nullptr && (e = hipEventRecord(a.ev_start, s)) != hipSuccess) return e;
   const bool bf = a.q_dtype == UQ_IN_BF16;

@@ -117,6 +117,21 @@ __device__ __forceinline__ int scale_exponent(double m) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// constOpt scale exponent ([review] §3.3 "constant-optimized scaling", c = 0.156;
+// §6.2): the integer nearest to log2(s), s = c m rounded once to float64,
+// clamped to [-127, 127] (m = 0 gives -127).  With s = M 2^e, M in [1, 2), the
+// exponent rounds up when M > sqrt(2); no double equals sqrt(2), and the least
+// double above it has significand bits 0x6A09E667F3BCD, so the test is a
+// comparison of the significand bits.
+__device__ __forceinline__ int constopt_exponent(double m) {
+  const double s = 0.156 * m;
+  if (!(s >= 0x1p-128)) return -127;                 // zero, or below the clamp
+  const uint64_t b = (uint64_t)__double_as_longlong(s);
+  const int e = (int)(b >> 52) - 1023;               // s is normal and positive here
+  const int E = e + ((b & 0xFFFFFFFFFFFFFull) >= 0x6A09E667F3BCDull ? 1 : 0);
+  return E > 127 ? 127 : E;
+}
+
 // FP4 E2M1 code of r = x / 2^E: magnitude rounded to nearest of
 // {0,.5,1,1.5,2,3,4,6}, ties to the even code, |r| > 6 saturating; sign bit from r.
 // The grid has quantum 0.5 on [0,2), 1 on [2,4), 2 on [4,6]: scale into integer

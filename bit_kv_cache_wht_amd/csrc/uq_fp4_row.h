@@ -45,9 +45,9 @@ template <int D, int IN, int LPR> struct Fp4Row {
     for (int i = 0; i < NU; ++i) raw[i] = load16(b + 16 * i);
   }
 
-  // Normalized WHT, group absmax, UE8M0 exponent and E2M1 codes (all lanes of
-  // the row call it together).
-  __device__ __forceinline__ void quantize(int p) {
+  // Normalized WHT, group absmax, UE8M0 exponent (the absmax rule, or constOpt
+  // when `constopt`) and E2M1 codes (all lanes of the row call it together).
+  __device__ __forceinline__ void quantize(int p, bool constopt) {
     double x[E];
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
@@ -89,11 +89,11 @@ template <int D, int IN, int LPR> struct Fp4Row {
       for (int e = 0; e < EG; ++e) m = fmax(m, fabs(x[EG * g + e]));
       if constexpr (LPG > 1) m = fmax(m, quad_swap<1>(m));
       if constexpr (LPG > 2) m = fmax(m, quad_swap<2>(m));
-      const int xg = scale_exponent(m * c);
+      const int xg = constopt ? constopt_exponent(m * c) : scale_exponent(m * c);
       ex[g] = xg;
       if (xg >= -100 && xg <= 100) {
-        // hardware E2M1 rounding (nearest even, saturating, sign kept) of the
-        // round-to-odd float32 value, divided by the scale 2^xg
+        // hardware E2M1 rounding (nearest even, saturating at 6, sign kept) of
+        // the round-to-odd float32 value, divided by the scale 2^xg
         const float sc = __uint_as_float((uint32_t)(xg + 127) << 23);
 #pragma unroll
         for (int q = EG / 8 * g; q < EG / 8 * (g + 1); ++q) {

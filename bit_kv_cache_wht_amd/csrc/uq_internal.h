@@ -17,6 +17,7 @@ struct AppendArgs {
   uint8_t* v_pool;
   int64_t page_bytes;         // bytes of one page of one pool
   int32_t T, H;
+  int32_t constopt;           // FP4: constOpt group scales (UQ_FLAG_SCALE_CONSTOPT)
 };
 
 // Launchers return the hipError_t of the launch.
@@ -52,6 +53,7 @@ struct DecodeArgs {
   uint8_t* ws;
   DecodeLayout lay;
   bool unrotate;
+  bool constopt;             // fused FP4 step: constOpt scales for the written token
   const void* k_new;         // fused FP4 step: newest token's K/V [B][Hkv][D] (q_dtype), or null
   const void* v_new;
   hipEvent_t ev_start, ev_stop;   // optional, recorded around the main kernel

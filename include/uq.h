@@ -79,6 +79,12 @@ enum uq_in_dtype { UQ_IN_BF16 = 0, UQ_IN_F32 = 1 };
 #define UQ_PAGE_SIZE 16
 #define UQ_GROUP 32
 #define UQ_FLAG_OUT_ROTATED 1u   /* FP4 decode: leave `out` in the rotated (WHT) basis */
+/* FP4 write (uq_quantize_append, the fused step): constOpt group scales
+ * ([review] §3.3 "constant-optimized scaling", §6.2): E = the integer nearest
+ * to log2(RN(0.156 * m)) (m = group absmax of the rotated row, rounding in the
+ * log domain), clamped to [-127, 127], m = 0 giving -127; codes x / 2^E then
+ * saturate at +-6.  Without it E is the least integer with m <= 6 * 2^E. */
+#define UQ_FLAG_SCALE_CONSTOPT 2u
 
 /* Cache descriptor; read at call time, never retained. */
 typedef struct uq_kv_cache {
@@ -113,7 +119,7 @@ size_t uq_page_bytes(const uq_kv_cache* cache);
  *   k_new, v_new  device [num_tokens][num_kv_heads][head_dim], bf16 or f32
  *                 (in_dtype), contiguous
  *   slot_mapping  device int32 [num_tokens]
- *   flags         must be 0
+ *   flags         0 or UQ_FLAG_SCALE_CONSTOPT (else UQ_ERR_INVALID_ARG)
  * cache->format must be UQ_KV_FP4.  Two tokens mapped to the same slot in one
  * call race.  num_tokens == 0 is a no-op.
  */
@@ -192,6 +198,8 @@ int uq_decode_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtype
  * uq_decode_attention.
  *   k_new, v_new  device [num_seqs][num_kv_heads][head_dim], in_dtype
  *   q             device [num_seqs][num_q_heads][head_dim], in_dtype
+ *   flags         UQ_FLAG_OUT_ROTATED as for uq_decode_attention, and
+ *                 UQ_FLAG_SCALE_CONSTOPT for the write as for uq_quantize_append
  *   other arguments and limits as uq_decode_attention; cache->format must be
  *   UQ_KV_FP4.  Sequences of length 0 write nothing.  The written slot must not
  *   be shared with another sequence's range (it never is when page tables do

@@ -58,24 +58,24 @@ def gpu_cache(fmt, wl, pools=None):
     return c
 
 
-def gpu_append(fmt, wl, cache=None, idx=None, slots=None):
+def gpu_append(fmt, wl, cache=None, idx=None, slots=None, flags=0):
     """Writes tokens ``idx`` (default all) with their slots through the C ABI."""
     torch = torch_mod()
     cache = cache if cache is not None else gpu_cache(fmt, wl)
     idx = np.arange(wl.total_tokens) if idx is None else np.asarray(idx)
     sl = wl.slot_mapping[idx] if slots is None else np.asarray(slots, np.int32)
     k, v = dev(wl.k[idx], wl.in_dtype), dev(wl.v[idx], wl.in_dtype)
-    append_fn(fmt)(cache, k, v, dev(np.ascontiguousarray(sl, dtype=np.int32)))
+    append_fn(fmt)(cache, k, v, dev(np.ascontiguousarray(sl, dtype=np.int32)), flags)
     torch.cuda.synchronize()
     return cache
 
 
-def oracle_append(fmt, wl, idx=None, slots=None):
+def oracle_append(fmt, wl, idx=None, slots=None, scale_mode="absmax"):
     kp, vp = O.new_pool(FMT_ID[fmt], wl.num_pages, wl.num_kv_heads, wl.head_dim), \
         O.new_pool(FMT_ID[fmt], wl.num_pages, wl.num_kv_heads, wl.head_dim)
     idx = np.arange(wl.total_tokens) if idx is None else np.asarray(idx)
     sl = wl.slot_mapping[idx] if slots is None else np.asarray(slots, np.int32)
-    O.append(FMT_ID[fmt], kp, vp, wl.k[idx], wl.v[idx], sl, in_dtype=wl.in_dtype)
+    O.append(FMT_ID[fmt], kp, vp, wl.k[idx], wl.v[idx], sl, in_dtype=wl.in_dtype, scale_mode=scale_mode)
     return kp, vp
 
 

@@ -77,6 +77,12 @@ def test_append_validation(name, fmt):
     assert call(dt=5) == B.UQ_ERR_INVALID_ARG
     assert call(n=-1) == B.UQ_ERR_INVALID_ARG
     assert call(fl=1) == B.UQ_ERR_INVALID_ARG
+    assert call(fl=4) == B.UQ_ERR_INVALID_ARG
+    if fmt == B.UQ_KV_FP4:                                          # constOpt accepted for FP4 writes only
+        assert call(fl=B.UQ_FLAG_SCALE_CONSTOPT, k=None) == B.UQ_ERR_INVALID_ARG
+        assert call(fl=B.UQ_FLAG_SCALE_CONSTOPT, n=0, k=None, v=None, s=None) == B.UQ_OK
+    else:
+        assert call(fl=B.UQ_FLAG_SCALE_CONSTOPT, n=0, k=None, v=None, s=None) == B.UQ_ERR_INVALID_ARG
     assert call(n=0, k=None, v=None, s=None) == B.UQ_OK            # empty append is a no-op
 
 
@@ -150,8 +156,9 @@ def test_fused_step_validation():
     assert call(dt=4) == B.UQ_ERR_INVALID_ARG
     assert call(Hq=15) == B.UQ_ERR_UNSUPPORTED
     assert call(w=None) == B.UQ_ERR_WORKSPACE
-    assert call(fl=2) == B.UQ_ERR_INVALID_ARG
+    assert call(fl=4) == B.UQ_ERR_INVALID_ARG
     assert call(fl=B.UQ_FLAG_OUT_ROTATED, w=None) == B.UQ_ERR_WORKSPACE
+    assert call(fl=B.UQ_FLAG_SCALE_CONSTOPT | B.UQ_FLAG_OUT_ROTATED, w=None) == B.UQ_ERR_WORKSPACE
     assert call(B_=0, k=None, v=None, q=None, pt=None, sl=None, out=None, w=None) == B.UQ_OK
 
 
