@@ -99,7 +99,11 @@ template <int D> __device__ __forceinline__ v8i load_q_fp8(const uint8_t* qrow, 
 // FP4.  Lane (r, j) of the PV product owns channel pairs CPL*r .. CPL*r + CPL-1
 // (CPL = D/32, i.e. channels 2*CPL*r .. 2*CPL*r + 2*CPL - 1, all in group
 // r*CPL/16), so one scale per token serves all of its conversions.
+// kShareAlpha: the cost, in steps, charged to each item when the steps of a call
+// are divided between workgroups (the per-item share of a round's set-up,
+// prologue latency, drain and merge; see share_plan).
 template <int D> struct Fp4Pol {
+  static constexpr int kShareAlpha = 12;
   static constexpr int kOcc = 2;        // waves per SIMD (256 registers each)
   static constexpr int kBuf = 2;        // K and V register buffers (steps of prefetch)
   // one KV head per item; a step is 4 pages; lane (r, j) holds the 16 slots of page j
@@ -230,6 +234,7 @@ template <int D> struct Fp4Pol {
 //   PV: per head and tile one f16 product pair over the step's 32 tokens, P
 //       masked to that head's columns.
 template <int D> struct Fp4PairPol {
+  static constexpr int kShareAlpha = 12;
   static constexpr int kOcc = 2;
   static constexpr int kBuf = 2;
   static constexpr int kNH = 2, kNP = 2, kTok = 8;
@@ -357,6 +362,7 @@ template <int D> struct Fp4PairPol {
 // small products when large ones are present in the same instruction, which
 // with unrotated outlier channels moves logits by ~1e-4 relative.
 template <int D> struct Fp8Pol {
+  static constexpr int kShareAlpha = 6;
   static constexpr int kOcc = 1;
   static constexpr int kBuf = 3;
   // one KV head per item; a step is 4 pages; lane (r, j) holds the 16 slots of page j
@@ -450,6 +456,7 @@ template <int D> struct Fp8Pol {
 };
 
 template <int D> struct Bf16Pol {
+  static constexpr int kShareAlpha = 3;
   static constexpr int kOcc = 1;
   static constexpr int kBuf = 2;
   // one KV head per item; a step is 4 pages; lane (r, j) holds the 16 slots of page j
@@ -577,33 +584,85 @@ __device__ __forceinline__ int clamp_len(int L, int max_pages) {
 }
 template <int NP> __device__ __forceinline__ int seq_steps(int L) { return ((L + kPage - 1) / kPage + NP - 1) / NP; }
 
-// Run by all 64 * NW threads; red: NW ints of scratch.  Steps are NP pages;
-// each sequence has Hi items (KV heads, or KV-head pairs).
+// Run by all 64 * NW threads; red: 2 NW ints of scratch.  Steps are NP pages;
+// each sequence has Hi items (KV heads, or KV-head pairs).  Returns, in every
+// thread, bit 0 set when the sequences' step counts differ and bit 1 when one of
+// them has none.
 template <int NW, int NP>
-__device__ void wg_plan(const int32_t* __restrict__ seq_lens, int B, int Hi, int max_pages, int32_t* sbase,
-                        int32_t* lens, int32_t* red) {
+__device__ int wg_plan(const int32_t* __restrict__ seq_lens, int B, int Hi, int max_pages, int32_t* sbase,
+                       int32_t* lens, int32_t* red) {
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s0 = B > 0 ? seq_steps<NP>(clamp_len(seq_lens[0], max_pages)) : 0;
   int32_t carry = 0;
+  int bits = 0;
   for (int b0 = 0; b0 < B; b0 += NT) {
     const int b = b0 + tid;
     const int L = b < B ? clamp_len(seq_lens[b], max_pages) : 0;
     if (b < B) lens[b] = L;
-    const int ns = b < B ? seq_steps<NP>(L) * Hi : 0;
+    const int s = seq_steps<NP>(L);
+    const int ns = b < B ? s * Hi : 0;
     const int incl = wave_incl_scan(ns);
-    if (lane == 63) red[wave] = incl;
+    const int wbits = (__any(b < B && s != s0) ? 1 : 0) | (__any(b < B && s == 0) ? 2 : 0);
+    if (lane == 63) {
+      red[wave] = incl;
+      red[NW + wave] = wbits;
+    }
     __syncthreads();
     int woff = 0, chunk = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       woff += w < wave ? red[w] : 0;
       chunk += red[w];
+      bits |= red[NW + w];
     }
     if (b < B) sbase[b] = carry + woff + incl - ns;
     carry += chunk;
     __syncthreads();                               // red is rewritten by the next chunk
   }
   if (tid == 0) sbase[B] = carry;
+  __syncthreads();
+  return bits;
+}
+
+// Cost-balanced share boundaries sb[0 .. grid] (run by all 64 * NW threads;
+// one barrier): workgroup w takes steps [sb[w], sb[w + 1]).  Each item is
+// charged its steps plus `alpha` > 0, and the cost line is cut into grid equal
+// parts, so that a share spanning many short items (several rounds, each with
+// its own set-up, prologue latency, drain and merge) gets fewer steps.  Item
+// f = b Hi + hk costs alpha and then its steps, so cost c maps to step
+// base[b] + hk steps(b) + clamp(c - start of f - alpha, 0, steps(b)).  The
+// caller keeps alpha <= (T / grid) / 2 and gives every sequence a step, so
+// consecutive cuts lie more than alpha apart in cost and no share is empty.
+template <int NW, int NP>
+__device__ void share_plan(const int32_t* base, const int32_t* lens, int B, int Hi, int T, int grid, int alpha,
+                           int32_t* sb) {
+  constexpr int NT = 64 * NW;
+  const int64_t C = (int64_t)T + (int64_t)alpha * B * Hi;   // < 2^53
+  for (int w = threadIdx.x; w <= grid; w += NT) {
+    int g = T;
+    if (w < grid) {
+      // t = floor(w C / grid); w C < 2^53 is exact in float64, and a quotient
+      // that is not an integer is at least 1/grid from one, so the floor of the
+      // rounded quotient is exact
+      const int64_t t = (int64_t)floor((double)((int64_t)w * C) / (double)grid);
+      // the last sequence b with cbase(b) = base[b] + alpha Hi b <= t
+      int lo = 0, hi = B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)base[mid] + (int64_t)alpha * Hi * mid <= t) lo = mid;
+        else hi = mid - 1;
+      }
+      const int sq = seq_steps<NP>(lens[lo]), per = sq + alpha;
+      const uint32_t r = (uint32_t)(t - ((int64_t)base[lo] + (int64_t)alpha * Hi * lo));   // < Hi per < 2^32
+      int hk = (int)(r / (uint32_t)per);
+      hk = hk < Hi - 1 ? hk : Hi - 1;
+      int64_t o = (int64_t)r - (int64_t)hk * per - alpha;
+      o = o < 0 ? 0 : (o > sq ? sq : o);
+      g = base[lo] + hk * sq + (int)o;
+    }
+    sb[w] = g;
+  }
   __syncthreads();
 }
 
@@ -827,9 +886,10 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 //   misc   [32]            step counter, per-item flags, plan scratch (int)
 //   base   [B + 1]         plan (int)
 //   lens   [B]             sequence lengths as used (int)
+//   sb     [kMaxGrid + 1]  share boundaries (int)
 constexpr int kSR = 16;   // rows of a wave slot in LDS (the 16 MFMA columns; an item has G <= 16)
 struct Lds {
-  int qs, so, sm, sl, rec, misc, base, lens, total;
+  int qs, so, sm, sl, rec, misc, base, lens, sb, total;
   __host__ __device__ static int up16(int x) { return (x + 15) & ~15; }
   __host__ __device__ Lds(int R, int NW, int G, int D, int esz, int B) {
     qs = 0;
@@ -840,7 +900,8 @@ struct Lds {
     misc = up16(rec + R * 8 * 4);
     base = up16(misc + 32 * 4);
     lens = up16(base + (B + 1) * 4);
-    total = up16(lens + B * 4);
+    sb = up16(lens + B * 4);
+    total = up16(sb + (kMaxGrid + 1) * 4);
   }
 };
 
@@ -889,20 +950,36 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, j4 = lane >> 4;
   if (tid == 0) *ctr = 0;                          // ordered before the first claim by the plan's barriers
-  wg_plan<NW, NP>(seq_lens, a.B, Hi, a.max_pages, base, lens, red);
+  const int plan_bits = wg_plan<NW, NP>(seq_lens, a.B, Hi, a.max_pages, base, lens, red);
   const int T = base[a.B];                       // < 2^31: the host bounds the step count
   // shares go to the first min(gridDim.x, T) workgroups, so that none is empty
   // and the workgroups holding steps of an item are consecutive
   const int grid = T < (int)gridDim.x ? T : (int)gridDim.x, wg = blockIdx.x;
-  // share_begin(w) = floor(w T / grid), from T = sq * grid + sr (w * sr < 2^20)
-  const int sq = grid > 0 ? T / grid : 0, sr = T - sq * grid;
-  const float r_grid = __builtin_amdgcn_rcpf((float)grid), r_hi = __builtin_amdgcn_rcpf((float)Hi);
-  const float grid_per_step = (float)grid * __builtin_amdgcn_rcpf((float)T);
-  auto share_begin = [&](int w) -> int { return w * sq + div_q20(w * sr, grid, r_grid); };
-  auto owner = [&](int g) -> int {              // the w whose share holds step g
-    int w = (int)((float)g * grid_per_step);    // off by at most a few
+  // Sequences of unequal lengths (none empty) get cost-balanced shares from an
+  // LDS table; otherwise share_begin(w) = floor(w T / grid) in closed form, from
+  // T = sq * grid + sr (w * sr < 2^20).
+  int alpha = Pol::kShareAlpha;
+  if (grid > 0 && 2 * alpha > T / grid) alpha = (T / grid) / 2;
+  if (plan_bits != 1 || grid < 1) alpha = 0;
+  int32_t* sb = reinterpret_cast<int32_t*>(smem + lay.sb);
+  if (alpha > 0) {
+    share_plan<NW, NP>(base, lens, a.B, Hi, T, grid, alpha, sb);
+  } else {
+    const int sq = grid > 0 ? T / grid : 0, sr = T - sq * grid;
+    const float r_grid = __builtin_amdgcn_rcpf((float)grid);
+    for (int w = tid; w <= grid; w += NT) sb[w] = w * sq + div_q20(w * sr, grid, r_grid);
+    __syncthreads();
+  }
+  const float r_hi = __builtin_amdgcn_rcpf((float)Hi);
+  const float grid_per_cost = (float)grid * __builtin_amdgcn_rcpf((float)T + (float)alpha * (float)(a.B * Hi));
+  const float falpha = (float)alpha;
+  auto share_begin = [&](int w) -> int { return sb[w]; };
+  // the w whose share holds step g of item f: estimated from the cost of g
+  // (g + alpha (f + 1)), then walked to the exact share
+  auto owner = [&](int g, int f) -> int {
+    int w = (int)(((float)g + falpha * (float)(f + 1)) * grid_per_cost);
     w = w < 0 ? 0 : (w >= grid ? grid - 1 : w);
-    while (share_begin(w) > g) --w;
+    while (w > 0 && share_begin(w) > g) --w;
     while (w + 1 < grid && share_begin(w + 1) <= g) ++w;
     return w;
   };
@@ -950,7 +1027,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         sg_nstep = max(s_hi - s_lo, 0);
         const bool partial = s_lo > start || s_hi < end;
         sg_slot = partial ? 2 * wg + (g_lo >= start ? 0 : 1) : -1;
-        sg_ncontrib = partial ? owner(end - 1) - owner(start) + 1 : 1;
+        sg_ncontrib = partial ? owner(end - 1, f) - owner(start, f) + 1 : 1;
         sg_end = end;
         sg_new = s_hi == end && L > 0;           // the item's last step, holding its newest token
       }
@@ -1324,7 +1401,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         const int b = r[kRecB], hk = r[kRecHk];
         const int steps = seq_steps<NP>(lens[b]);
         const int start = base[b] + hk * steps;
-        const int w0 = owner(start), n = r[kRecNContrib];
+        const int w0 = owner(start, b * Hi + hk), n = r[kRecNContrib];
         // partial of contributor w0 + i: slot 2w if the item begins its share, else 2w + 1
         auto prow_of = [&](int i) -> int64_t {
           const int w = w0 + i;

@@ -163,6 +163,26 @@ def test_decode_on_oracle_cache(fmt, name):
         assert not got[b].any()
 
 
+def _many_short():
+    """240 sequences, mostly short with a few long ones (about 65K tokens): with
+    unequal lengths the decode charges each item a fixed cost when it divides the
+    steps between workgroups, so shares here hold many items (several rounds)
+    and cut items at uneven step counts."""
+    rng = np.random.default_rng(77)
+    lens = rng.choice([17, 40, 90, 130, 300, 600], size=240)
+    lens[::37] = 2048 + rng.integers(0, 1500, size=lens[::37].size)
+    return W.make_workload("many_short", 240, 32, 4, 128, list(lens), list(lens), seed=78)
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])     # 8- and 4-wave workgroups
+def test_decode_many_short_sequences(fmt):
+    wl = _many_short()
+    pools = oracle_append(fmt, wl)
+    announce(f"decode {fmt} many_short B={wl.batch} tokens={wl.total_tokens}")
+    got = gpu_decode(fmt, wl, gpu_cache(fmt, wl, pools))
+    assert_close(got, oracle_decode(fmt, wl, pools), f"{fmt} many_short")
+
+
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("name", ["tiny", "gqa_ragged", "one_long"])
 def test_end_to_end(fmt, name):
