@@ -37,7 +37,7 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="before the warm-up steps, run steps for this long so that the GPU clocks reach their "
@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="also time the FP4 step as two launches (append kernel, then decode kernel)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time each oracle worker may spend building its pairs' caches before the timed step")
     ap.add_argument("--scrub-mb", type=int, default=0,
                     help="read a buffer of this size between the event-timed steps (evicts the last-level cache)")
     ap.add_argument("--cold-mb", type=int, default=1024,
@@ -356,7 +357,8 @@ class Runner:
         torch.cuda.synchronize()
         k_ms = [evs.elapsed_ms(i) for i in range(steps)]
         res = dict(ms_per_step=ms_step, wall_ms_per_step=1e3 * wall / steps,
-                   decode_kernel_ms=float(np.mean(k_ms)), decode_kernel_ms_p10=float(np.percentile(k_ms, 10)),
+                   decode_kernel_ms=float(np.mean(k_ms)), decode_kernel_ms_median=float(np.median(k_ms)),
+                   decode_kernel_ms_p10=float(np.percentile(k_ms, 10)),
                    decode_kernel_ms_p90=float(np.percentile(k_ms, 90)))
         if cold is not None:
             for i in range(steps):
@@ -385,47 +387,91 @@ class Runner:
         return kv + q + pt, kv
 
 
-def cpu_baseline(wl, budget_s):
-    """The oracle as it stands, on a bounded sample of the same step: decode rows of
-    whole (sequence, KV head) pairs plus the appends of their new tokens, scaled to
-    one full step.  BLAS is pinned to one thread, so the oracle uses one core."""
-    import threadpoolctl
+def _oracle_pair_prepare(wl, pair):
+    """Oracle cache of one (sequence, KV head) pair holding the prefix (untimed)."""
     import oracle as O
-    G = wl.num_q_heads // wl.num_kv_heads
-    d = wl.head_dim
+    b, hk = divmod(int(pair), wl.num_kv_heads)
+    L, d = int(wl.seq_lens[b]), wl.head_dim
+    npg = (L + 15) // 16
+    t0, n_new = int(wl.tok_offsets[b]), int(wl.new_lens[b])
+    kp, vp = O.new_pool(O.FMT_FP4, npg, 1, d), O.new_pool(O.FMT_FP4, npg, 1, d)
+    O.append(O.FMT_FP4, kp, vp, wl.k[t0:t0 + L - n_new, hk:hk + 1], wl.v[t0:t0 + L - n_new, hk:hk + 1],
+             np.arange(L - n_new, dtype=np.int32), in_dtype=wl.in_dtype)
+    return b, hk, kp, vp
+
+
+def _oracle_pair_step(wl, prepared):
+    """The step for one pair: append of its new token(s), decode of its query heads."""
+    import oracle as O
+    b, hk, kp, vp = prepared
+    G, d = wl.num_q_heads // wl.num_kv_heads, wl.head_dim
+    L, t0, n_new = int(wl.seq_lens[b]), int(wl.tok_offsets[b]), int(wl.new_lens[b])
+    O.append(O.FMT_FP4, kp, vp, wl.k[t0 + L - n_new:t0 + L, hk:hk + 1], wl.v[t0 + L - n_new:t0 + L, hk:hk + 1],
+             np.arange(L - n_new, L, dtype=np.int32), in_dtype=wl.in_dtype)
+    O.decode_attention_rows(O.FMT_FP4, kp, vp, 1, d, wl.q[b:b + 1, hk * G:(hk + 1) * G],
+                            np.arange((L + 15) // 16)[None], np.array([L]), float(np.float32(1 / np.sqrt(d))),
+                            [(0, g) for g in range(G)], in_dtype=wl.in_dtype)
+
+
+def _oracle_worker(wl, pairs, budget_s, barrier, out):
+    import threadpoolctl
     with threadpoolctl.threadpool_limits(1):
-        pairs = 0
-        elapsed_pairs = 0.0
-        t_start = time.perf_counter()
-        rng = np.random.default_rng(0)
-        order = rng.permutation(wl.batch * wl.num_kv_heads)
-        for pair in order:
-            b, hk = divmod(int(pair), wl.num_kv_heads)
-            L = int(wl.seq_lens[b])
-            npg = (L + 15) // 16
-            t0 = wl.tok_offsets[b]
-            kp, vp = O.new_pool(O.FMT_FP4, npg, 1, d), O.new_pool(O.FMT_FP4, npg, 1, d)
-            # cache holds the prefix already; the step appends the new token(s) and decodes
-            n_new = int(wl.new_lens[b])
-            pre = np.arange(L - n_new, dtype=np.int32)
-            O.append(O.FMT_FP4, kp, vp, wl.k[t0:t0 + L - n_new, hk:hk + 1], wl.v[t0:t0 + L - n_new, hk:hk + 1], pre,
-                     in_dtype=wl.in_dtype)
-            t_pair = time.perf_counter()
-            O.append(O.FMT_FP4, kp, vp, wl.k[t0 + L - n_new:t0 + L, hk:hk + 1], wl.v[t0 + L - n_new:t0 + L, hk:hk + 1],
-                     np.arange(L - n_new, L, dtype=np.int32), in_dtype=wl.in_dtype)
-            rows = [(0, g) for g in range(G)]
-            O.decode_attention_rows(O.FMT_FP4, kp, vp, 1, d, wl.q[b:b + 1, hk * G:(hk + 1) * G], np.arange(npg)[None],
-                                    np.array([L]), float(np.float32(1 / np.sqrt(d))), rows, in_dtype=wl.in_dtype)
-            elapsed_pairs += time.perf_counter() - t_pair
-            pairs += 1
-            if time.perf_counter() - t_start > budget_s:
+        t = time.perf_counter()
+        prepared = []
+        for pair in pairs:
+            prepared.append(_oracle_pair_prepare(wl, pair))
+            if time.perf_counter() - t > budget_s:
                 break
-    per_pair = elapsed_pairs / pairs
+        barrier.wait()
+        t0 = time.perf_counter()
+        for p in prepared:
+            _oracle_pair_step(wl, p)
+        t1 = time.perf_counter()
+    out.put((len(prepared), t0, t1))
+
+
+def oracle_cores():
+    """Host cores for the oracle: those this process may run on, at most 16 (a
+    one-GPU share of a GPU host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle as it stands, on the host cores this process may use: one forked
+    worker per core, each with BLAS pinned to one thread, takes (sequence, KV
+    head) pairs in a seeded random order and builds their caches with the prefix
+    (untimed, within the budget); then all workers run the step on their pairs
+    at once (append of the new token(s), decode of the pair's query heads).  The
+    wall time of that phase, scaled by all pairs / pairs run, is the value.  Runs
+    before this process touches the GPU (the workers are forks)."""
+    import multiprocessing as mp
+    import platform
+    cores = oracle_cores()
     total_pairs = wl.batch * wl.num_kv_heads
-    return {"value": per_pair * total_pairs * 1e6, "unit": "us/step", "cores": 1, "kind": "oracle",
-            "sample": f"{pairs} of {total_pairs} (sequence, KV head) pairs: append of the new token + decode of "
-                      f"its {G} query heads over the full context, float64 numpy; scaled to the whole step "
-                      f"(prefix quantization untimed)"}
+    order = np.random.default_rng(0).permutation(total_pairs)
+    ctx = mp.get_context("fork")
+    barrier, out = ctx.Barrier(cores), ctx.Queue()
+    procs = [ctx.Process(target=_oracle_worker, args=(wl, order[w::cores], budget_s, barrier, out))
+             for w in range(cores)]
+    for p in procs:
+        p.start()
+    res = [out.get() for _ in procs]
+    for p in procs:
+        p.join()
+    done = sum(r[0] for r in res)
+    wall = max(r[2] for r in res) - min(r[1] for r in res)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        cpu = platform.processor() or cpu
+    G = wl.num_q_heads // wl.num_kv_heads
+    return {"value": wall * total_pairs / done * 1e6, "unit": "us/step", "cores": cores, "kind": "oracle",
+            "cpu": cpu,
+            "sample": f"{done} of {total_pairs} (sequence, KV head) pairs on {cores} worker processes at once: "
+                      f"append of the new token(s) + decode of its {G} query heads over the full context, "
+                      f"float64 numpy; wall time scaled to the whole step (prefix quantization untimed)"}
 
 
 def main():
@@ -441,12 +487,16 @@ def main():
         pmc_pass(args)
         return
     import torch
-    torch.cuda.set_device(0)
     log(f"generating workload {args.workload}")
     t = time.perf_counter()
     wl = make_workload(args.workload)
     log(f"workload ready in {time.perf_counter() - t:.1f}s: B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
         f"d={wl.head_dim} tokens={wl.total_tokens}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline (oracle on {oracle_cores()} host cores; before the GPU is touched)")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+    torch.cuda.set_device(0)
     results = {}
     fmts = ["fp4"] + ([] if args.no_baselines else ["fp8", "bf16"]) + (["fp4_unfused"] if args.unfused else [])
     for fmt in fmts:
@@ -506,6 +556,7 @@ def main():
                      "kernel_us_event_pairs": round(fp4["decode_kernel_ms"] * 1e3, 2),
                      "kernel_us_event_pairs_cold": (round(fp4["decode_kernel_ms_cold"] * 1e3, 2)
                                                     if "decode_kernel_ms_cold" in fp4 else None),
+                     "kernel_us_event_pairs_median": round(fp4["decode_kernel_ms_median"] * 1e3, 2),
                      "kernel_us_event_pairs_p10_p90": [round(fp4["decode_kernel_ms_p10"] * 1e3, 2),
                                                        round(fp4["decode_kernel_ms_p90"] * 1e3, 2)],
                      "algo_bytes_per_launch": fp4["kernel_algo_bytes"]},
@@ -529,9 +580,8 @@ def main():
         log(f"append: {line['append']['us_per_call']} us per call, "
             f"{line['append']['quantized_tokens_per_s'] / 1e6:.1f} M tokens/s, {line['append']['gbs']} GB/s")
         torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle sample)")
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
