@@ -36,6 +36,10 @@ Readings where the pages are silent (each listed with its reason in the design doc):
   R7  sm_scale multiplies the logits; GQA maps query head h to KV head
       h // (H_q / H_kv).
   R8  Cache page layout: see ``head_block_bytes`` and the ``*_offset`` helpers.
+  R10 Chunked prefill over the cache: a sequence's chunk of q_lens[b] query
+      tokens holds its last positions (the chunk is written to the cache
+      first); chunk token j at position P = seq_lens[b] - q_lens[b] + j attends
+      to positions 0 .. P, each row exactly as the decode over that prefix.
   R9  constOpt scale mode (``scale_mode="constopt"``): s = c * m rounded once to
       float64 (c = 0.156 by default), E = the integer nearest to log2(s) (the
       log domain: the pages' "power-of-two-optimal" constant 0.195 is the
@@ -56,7 +60,7 @@ __all__ = [
     "E2M1_LEVELS", "e2m1_encode", "e2m1_decode",
     "quantize_fp4", "dequantize_fp4", "pack_nibbles", "unpack_nibbles",
     "e4m3_decode", "e4m3_encode", "bf16_bits_to_f64", "f32_to_f64", "bf16_round_bits",
-    "head_block_bytes", "page_bytes", "new_pool",
+    "head_block_bytes", "page_bytes", "new_pool", "prefill_attention",
     "fp4_k_code_offset", "fp4_k_scale_offset", "fp4_v_code_offset", "fp4_v_scale_offset",
     "fp8_k_offset", "fp8_v_offset", "bf16_k_index", "bf16_v_index",
     "append", "gather_dequant", "rotate_quantize_query", "attention",
@@ -472,6 +476,23 @@ def decode_attention_rows(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table, s
         o = attention(qhat[None, :], K, V, float(sm_scale))[0]
         out[n] = wht(o) if fmt == FMT_FP4 else o
     return out
+
+
+def prefill_attention(fmt, k_pool, v_pool, num_kv_heads, d, q, q_lens, page_table, seq_lens,
+                      sm_scale, in_dtype="bf16") -> np.ndarray:
+    """Causal attention of chunks of query tokens over the cache ([review] §1 and
+    §5.4: a new turn's tokens read the resident prefix instead of re-prefilling
+    it; reading R10).  q [T_q][H_q][d] holds sequence 0's chunk, then sequence
+    1's, ...; the row of chunk token j of sequence b is the decode of that row
+    over positions 0 .. seq_lens[b] - q_lens[b] + j.  Returns [T_q][H_q][d]."""
+    q = np.asarray(q)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    b_of = np.repeat(np.arange(q_lens.size), q_lens)                   # sequence of each query token
+    j_of = np.arange(q.shape[0]) - np.repeat(np.cumsum(q_lens) - q_lens, q_lens)
+    prefix = seq_lens[b_of] - q_lens[b_of] + j_of + 1                  # positions 0 .. P
+    table = np.asarray(page_table)[b_of]
+    return decode_attention(fmt, k_pool, v_pool, num_kv_heads, d, q, table, prefix, sm_scale, in_dtype)
 
 
 def decode_attention(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table, seq_lens,

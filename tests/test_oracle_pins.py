@@ -450,6 +450,51 @@ def test_fp4_decode_equals_plain_attention_on_exact_inputs():
             np.testing.assert_allclose(out[b, h], ref, rtol=0, atol=1e-12)
 
 
+def test_fp4_prefill_equals_causal_attention_on_exact_inputs():
+    # R10 on inputs exact on the FP4 / E4M3 grids: every chunk row equals plain
+    # causal attention (a triangular mask over the chunk) on the original vectors.
+    d, T, H, G = 64, 40, 2, 3
+    x_k, _ = _grid_workload(d=d, T=T, H=H, seed=19)
+    x_v, _ = _grid_workload(d=d, T=T, H=H, seed=20)
+    rng = np.random.default_rng(21)
+    lens, chunks = np.array([T, 21]), np.array([7, 21])               # a chunk after a prefix; a whole prompt
+    q_rot = rng.choice([0.0, 0.5, 1.0, -1.0, 2.0, -1.5, 0.25, -3.0], size=(int(chunks.sum()), H * G, d))
+    q = O.wht(q_rot).astype(np.float32)
+    pages = rng.permutation(6)
+    table = np.stack([pages[:3], pages[3:6]])
+    kp, vp = O.new_pool(O.FMT_FP4, 6, H, d), O.new_pool(O.FMT_FP4, 6, H, d)
+    for b in range(2):
+        L = lens[b]
+        slots = table[b][np.arange(L) // 16] * 16 + np.arange(L) % 16
+        O.append(O.FMT_FP4, kp, vp, x_k[:L], x_v[:L], slots, in_dtype="f32")
+    scale = 1 / math.sqrt(d)
+    out = O.prefill_attention(O.FMT_FP4, kp, vp, H, d, q, chunks, table, lens, scale, in_dtype="f32")
+    row = 0
+    for b in range(2):
+        for j in range(chunks[b]):
+            P = lens[b] - chunks[b] + j                                 # the token's position
+            for h in range(H * G):
+                Kx = x_k[:P + 1, h // G].astype(np.float64)
+                Vx = x_v[:P + 1, h // G].astype(np.float64)
+                ref = _brute_attention(q[row, h].astype(np.float64), Kx, Vx, scale)
+                np.testing.assert_allclose(out[row, h], ref, rtol=0, atol=1e-12)
+            row += 1
+    # causality: changing keys and values after a token's position leaves its row alone
+    x_k2, x_v2 = x_k.copy(), x_v.copy()
+    x_k2[36:], x_v2[36:] = x_k[36:] * 2, -x_v[36:]
+    kp2, vp2 = O.new_pool(O.FMT_FP4, 6, H, d), O.new_pool(O.FMT_FP4, 6, H, d)
+    for b in range(2):
+        L = lens[b]
+        slots = table[b][np.arange(L) // 16] * 16 + np.arange(L) % 16
+        O.append(O.FMT_FP4, kp2, vp2, x_k2[:L], x_v2[:L], slots, in_dtype="f32")
+    out2 = O.prefill_attention(O.FMT_FP4, kp2, vp2, H, d, q, chunks, table, lens, scale, in_dtype="f32")
+    keep = 36 - (lens[0] - chunks[0])                                 # sequence 0's chunk tokens before position 36
+    assert keep == 3
+    assert np.array_equal(out2[:keep], out[:keep])                    # positions 33 .. 35
+    assert all(not np.array_equal(out2[r], out[r]) for r in range(keep, chunks[0]))
+    assert np.array_equal(out2[chunks[0]:], out[chunks[0]:])          # sequence 1 is 21 tokens long
+
+
 def _small_pools(fmt, seed=12, B=3, H=2, G=4, d=128, lens=(1, 33, 70)):
     wl = W.make_workload("attn", B, H * G, H, d, list(lens), list(lens), seed=seed)
     kp, vp = O.new_pool(fmt, wl.num_pages, H, d), O.new_pool(fmt, wl.num_pages, H, d)
