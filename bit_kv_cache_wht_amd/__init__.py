@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     uq_page_bytes,
     uq_profile_next_decode,
     uq_stream_read,
+    uq_prefill_attention,
     uq_quantize_append,
     uq_rotate_quantize_query,
     uq_status_string,

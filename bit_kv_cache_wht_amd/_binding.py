@@ -51,6 +51,7 @@ _SIGS = {
     "uq_decode_attention_bf16": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
     "uq_profile_next_decode": (ctypes.c_int, [_P, _P]),
     "uq_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
+    "uq_prefill_attention": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _U, _P]),
     "uq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "uq_last_hip_error": (ctypes.c_int, []),
 }
@@ -246,3 +247,15 @@ def uq_stream_read(src, sink, stream=None) -> None:
     of its 32-bit words into the int32 tensor `sink` (one element)."""
     nbytes = src.numel() * src.element_size()
     _check("uq_stream_read", lib().uq_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
+
+
+def uq_prefill_attention(cache, q, cu_seqlens_q, page_table, seq_lens, sm_scale, out, flags=0, stream=None) -> None:
+    """Chunked-prefill attention: q [T_q][H_q][d] (bf16/f32), cu_seqlens_q int32
+    [B + 1], out float32 [T_q][H_q][d]; each sequence's chunk is its last tokens."""
+    _contig(q, cu_seqlens_q, page_table, seq_lens, out)
+    c = cache.c()
+    st = lib().uq_prefill_attention(ctypes.byref(c), _ptr(q), _dtype_code(q), _ptr(cu_seqlens_q), int(q.shape[0]),
+                                    _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens),
+                                    int(seq_lens.shape[0]), int(q.shape[1]), float(sm_scale), _ptr(out), flags,
+                                    _stream(stream))
+    _check("uq_prefill_attention", st)

@@ -218,6 +218,41 @@ int uq_profile_next_decode(void* start_event, void* stop_event) {
   return UQ_OK;
 }
 
+int uq_prefill_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtype, const int32_t* cu_seqlens_q,
+                         int32_t total_q, const int32_t* page_table, int32_t max_pages_per_seq,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, float sm_scale, float* out,
+                         uint32_t flags, uq_stream_t stream) {
+  int st = check_cache(cache, UQ_KV_FP4);
+  if (st != UQ_OK) return st;
+  if (flags != 0u) return UQ_ERR_INVALID_ARG;
+  if (q_dtype != UQ_IN_BF16 && q_dtype != UQ_IN_F32) return UQ_ERR_INVALID_ARG;
+  if (num_seqs < 0 || total_q < 0 || max_pages_per_seq < 1 || num_q_heads < 1) return UQ_ERR_INVALID_ARG;
+  if (num_q_heads % cache->num_kv_heads != 0 || num_q_heads / cache->num_kv_heads > 128) return UQ_ERR_UNSUPPORTED;
+  if (num_seqs > uq::prefill_max_seqs() || max_pages_per_seq > (1 << 26)) return UQ_ERR_UNSUPPORTED;
+  if (!(sm_scale > 0.f) || !(sm_scale < INFINITY)) return UQ_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_q == 0) return UQ_OK;
+  if (q == nullptr || cu_seqlens_q == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
+    return UQ_ERR_INVALID_ARG;
+  uq::PrefillArgs a;
+  a.k_pool = static_cast<const uint8_t*>(cache->k_pool);
+  a.v_pool = static_cast<const uint8_t*>(cache->v_pool);
+  a.page_bytes = (int64_t)uq_page_bytes(cache);
+  a.max_pages = max_pages_per_seq;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.cu_q = cu_seqlens_q;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.B = num_seqs;
+  a.Hq = num_q_heads;
+  a.Hkv = cache->num_kv_heads;
+  a.D = cache->head_dim;
+  a.Tq = total_q;
+  a.sm_scale = sm_scale;
+  return hip_status(uq::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
 int uq_stream_read(const void* src, size_t bytes, uint32_t* sink, uq_stream_t stream) {
   if (bytes == 0) return UQ_OK;
   if (src == nullptr || sink == nullptr) return UQ_ERR_INVALID_ARG;

@@ -1569,6 +1569,287 @@ DecodeLayout decode_layout(int format, int B, int Hq, int Hkv, int D) {
   return L;
 }
 
+
+// ------------------------------------------------------------------ chunked prefill
+// Causal attention of chunks of query tokens over the FP4 cache ([review] §1 and
+// §5.4: a new turn's tokens read the resident prefix instead of re-prefilling it).
+// A workgroup takes kPfRows query rows, rows r = t G + h for QT = kPfRows / G
+// consecutive chunk tokens t of one sequence and the G query heads of one KV
+// head, and walks the cache from position 0 to its last token's position in
+// steps of 4 pages (64 keys), exactly as the FP4 decode steps: K/V double-
+// buffered in registers, scaled-MFMA QK, online softmax with lazy rescaling,
+// hi + lo float16 P in the PV.  Each of the 4 waves owns kPfNB 16-row column
+// blocks and reuses every loaded K/V step for all of them.  Logits past a row's
+// own position get -inf (causal), value slots past the sequence end are
+// cleared.  Rows are rotated back and stored like the decode's.
+namespace {
+constexpr int kPfWaves = 4;
+constexpr int kPfNB = 2;                                  // column blocks per wave
+constexpr int kPfRows = 16 * kPfNB * kPfWaves;            // query rows of a workgroup
+constexpr int kPfMaxSeqs = 4096;                          // plan in LDS
+
+struct PfArgs {
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  int64_t page_bytes;
+  int32_t max_pages;
+  const void* q;              // [Tq][Hq][D]
+  const int32_t* cu_q;        // [B + 1] first q row of each sequence's chunk
+  const int32_t* page_table;  // [B][max_pages]
+  const int32_t* seq_lens;    // [B]
+  float* out;                 // [Tq][Hq][D]
+  int32_t B, Hq, Hkv, G, QT;
+  float scale_log2;
+};
+
+template <int D>
+struct PfLds {
+  static constexpr int kQs = 0;                                   // [kPfRows][D] E4M3 query rows
+  static constexpr int kStage = kQs + kPfRows * D;                // [kPfWaves][16][D] float rows
+  static constexpr int kL = kStage + kPfWaves * 16 * D * 4;       // [kPfWaves][16] float l
+  static constexpr int kPlan = kL + kPfWaves * 16 * 4;            // [kPfMaxSeqs + 1] block prefix
+  static constexpr int kMisc = kPlan + (kPfMaxSeqs + 1) * 4;      // [2 * kPfWaves] scratch
+  static constexpr int kTotal = kMisc + 2 * kPfWaves * 4;
+};
+
+template <int D, int IN>
+__global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) {
+  using Pol = Fp4Pol<D>;
+  constexpr int NT = 64 * kPfWaves;
+  constexpr int TOK = Pol::kTok;                               // 16 slots of one page per lane
+  using L = PfLds<D>;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* qs = smem + L::kQs;
+  float* stage = reinterpret_cast<float*>(smem + L::kStage);
+  float* stage_l = reinterpret_cast<float*>(smem + L::kL);
+  int32_t* bb = reinterpret_cast<int32_t*>(smem + L::kPlan);
+  int32_t* red = reinterpret_cast<int32_t*>(smem + L::kMisc);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, j4 = lane >> 4;
+  const int hk = blockIdx.y;
+
+  // ---- plan: bb[b] = first block of sequence b (blocks of QT chunk tokens)
+  int carry = 0;
+  for (int b0 = 0; b0 < a.B; b0 += NT) {
+    const int b = b0 + tid;
+    const int n = b < a.B ? (a.cu_q[b + 1] - a.cu_q[b] + a.QT - 1) / a.QT : 0;
+    const int incl = wave_incl_scan(n);
+    if (lane == 63) red[wave] = incl;
+    __syncthreads();
+    int woff = 0, chunk = 0;
+#pragma unroll
+    for (int w = 0; w < kPfWaves; ++w) {
+      woff += w < wave ? red[w] : 0;
+      chunk += red[w];
+    }
+    if (b < a.B) bb[b] = carry + woff + incl - n;
+    carry += chunk;
+    __syncthreads();
+  }
+  const int blk = blockIdx.x;
+  if (blk >= carry) return;                                    // past the last block: idle
+  int lo = 0, hi = a.B - 1;                                    // the last b with bb[b] <= blk
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (bb[mid] <= blk) lo = mid;
+    else hi = mid - 1;
+  }
+  const int b = lo;
+  const int q0 = a.cu_q[b], qlen = a.cu_q[b + 1] - q0;
+  const int t0 = (blk - bb[b]) * a.QT;                          // first chunk token of the block
+  const int nt = min(a.QT, qlen - t0);                          // its tokens
+  const int Ls = clamp_len(a.seq_lens[b], a.max_pages);
+  const int pos0 = Ls - qlen + t0;                              // position of token t0
+  const int nrows = nt * a.G;
+  const int npages = (Ls + kPage - 1) / kPage;
+  // position of row r (padding rows attend to position 0 and are not stored)
+  auto row_pos = [&](int r) -> int {
+    const int p = r < nrows ? pos0 + r / a.G : 0;
+    return p < 0 ? 0 : p;
+  };
+  const int last_pos = row_pos(nrows - 1);
+  const int steps = last_pos / (4 * kPage) + 1;                 // 64 keys per step
+
+  // ---- query rows: rotate, round to E4M3, into LDS
+  for (int r = tid >> 4; r < kPfRows; r += NT / 16) {
+    const int p = tid & 15;
+    QueryRows<D, IN, UQ_KV_FP4> qr;
+    const bool valid = r < nrows;
+    const int64_t qrow = (int64_t)(q0 + t0 + (valid ? r / a.G : 0)) * a.Hq + (int64_t)hk * a.G + (valid ? r % a.G : 0);
+    qr.load(a.q, qrow, valid, p);
+    qr.finish(qs + r * D, p);
+  }
+  __syncthreads();
+
+  typename Pol::QOp qo[kPfNB];
+  int rpos[kPfNB];                                             // position of this lane's row in block c
+  float m_run[kPfNB], l_run[kPfNB];
+  v4f O[kPfNB][Pol::kTiles];
+#pragma unroll
+  for (int c = 0; c < kPfNB; ++c) {
+    const int row = (wave * kPfNB + c) * 16 + r16;
+    Pol::load_q(qo[c], qs + row * D, true, j4, 0);
+    rpos[c] = row_pos(row);
+    m_run[c] = -INFINITY;
+    l_run[c] = 0.f;
+#pragma unroll
+    for (int t = 0; t < Pol::kTiles; ++t) O[c][t] = v4f{0, 0, 0, 0};
+  }
+
+  const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
+  const int64_t head_off = (int64_t)hk * Pol::kBlk;
+  auto ids_of = [&](int s, int (&ids)[4]) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) ids[x] = pt[max(min(4 * s + x, npages - 1), 0)];   // within the row
+  };
+  // K/V buffers alternate between two named pairs (the step loop is unrolled by
+  // two, so that no buffer is indexed at run time and all stay in registers)
+  typename Pol::KStep k0, k1;
+  typename Pol::VStep v0, v1;
+  {
+    int ids[4];
+    ids_of(0, ids);
+    Pol::load_k(k0, a.k_pool, ids, a.page_bytes, head_off, r16, j4);
+    Pol::load_v(v0, a.v_pool, ids, a.page_bytes, head_off, r16, j4);
+  }
+  auto step = [&](int s, typename Pol::KStep& kc, typename Pol::VStep& vc, typename Pol::KStep& kn,
+                  typename Pol::VStep& vn) {
+    if (s + 1 < steps) {                                       // prefetch the next step
+      int ids[4];
+      ids_of(s + 1, ids);
+      Pol::load_k(kn, a.k_pool, ids, a.page_bytes, head_off, r16, j4);
+      Pol::load_v(vn, a.v_pool, ids, a.page_bytes, head_off, r16, j4);
+    }
+    const int key0 = 4 * kPage * s + kPage * j4;                // first key of this lane's page
+    Pol::mask_v(vc, min(max(Ls - key0, 0), TOK));              // value slots past the sequence end
+#pragma unroll
+    for (int c = 0; c < kPfNB; ++c) {
+      v4f S[TOK / 4];
+      Pol::qk(kc, qo[c], S);
+      const int nvalid = min(max(rpos[c] - key0 + 1, 0), TOK);  // causal: keys <= the row's position
+      float t[TOK];
+#pragma unroll
+      for (int m = 0; m < TOK / 4; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) t[4 * m + v] = 4 * m + v < nvalid ? S[m][v] : -INFINITY;
+      float neg_mc = -m_run[c] * a.scale_log2;
+      float pf[TOK];
+#pragma unroll
+      for (int i = 0; i < TOK; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
+      float psum = pf[0];
+#pragma unroll
+      for (int i = 1; i < TOK; ++i) psum += pf[i];
+      if (__any(!(psum <= 256.f))) {
+        float mx = t[0];
+#pragma unroll
+        for (int i = 1; i < TOK; ++i) mx = fmaxf(mx, t[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[c], mx);
+        // a row whose every key so far is masked keeps m = -inf and takes no rescale
+        const float alpha = m_new > -INFINITY ? __builtin_amdgcn_exp2f((m_run[c] - m_new) * a.scale_log2) : 1.f;
+        const float keep = m_run[c] > -INFINITY ? alpha : 0.f;
+        l_run[c] *= keep;
+#pragma unroll
+        for (int tt = 0; tt < Pol::kTiles; ++tt) O[c][tt] *= keep;
+        m_run[c] = m_new;
+        neg_mc = m_new > -INFINITY ? -m_new * a.scale_log2 : 0.f;
+#pragma unroll
+        for (int i = 0; i < TOK; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
+        psum = pf[0];
+#pragma unroll
+        for (int i = 1; i < TOK; ++i) psum += pf[i];
+      }
+      l_run[c] += psum;
+      v8h Pm[TOK / 8][2];
+#pragma unroll
+      for (int half = 0; half < TOK / 8; ++half) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split_f16x2(pf[8 * half + 2 * i], pf[8 * half + 2 * i + 1], hw[i], lw[i]);
+        Pm[half][0] = __builtin_bit_cast(v8h, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        Pm[half][1] = __builtin_bit_cast(v8h, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      }
+      Pol::pv(vc, Pm, O[c], 0);
+    }
+  };
+  for (int s = 0; s < steps; s += 2) {
+    step(s, k0, v0, k1, v1);
+    if (s + 1 < steps) step(s + 1, k1, v1, k0, v0);
+  }
+
+  // ---- rows out: block by block through the wave's LDS stage (16 rows), two
+  // rows at a time per wave (one per 32-lane half), normalized, rotated back
+  constexpr int PC = D / 32;
+  float* st = stage + wave * 16 * D;
+  float* stl = stage_l + wave * 16;
+  const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int c = 0; c < kPfNB; ++c) {
+    float l_tot = l_run[c] + __shfl_xor(l_run[c], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+#pragma unroll
+    for (int tt = 0; tt < Pol::kTiles; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) st[r16 * D + Pol::channel(tt, j4, v)] = O[c][tt][v];
+    if (j4 == 0) stl[r16] = l_tot;
+    __builtin_amdgcn_s_waitcnt(0xC07F);                         // lgkmcnt(0): the stage is written
+    __builtin_amdgcn_wave_barrier();
+    for (int rr = 0; rr < 16; rr += 2) {
+      const int rloc = rr + half;
+      const int row = (wave * kPfNB + c) * 16 + rloc;
+      float o[PC];
+#pragma unroll
+      for (int k = 0; k < PC; ++k) o[k] = st[rloc * D + l32 + 32 * k];
+      const float l = stl[rloc];
+      const bool live = row < nrows;
+      const int64_t orow = live ? (int64_t)(q0 + t0 + row / a.G) * a.Hq + (int64_t)hk * a.G + row % a.G : 0;
+      store_row32<D, true>(o, l, a.out + orow * D, live, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();                           // the stage is reused by the next block
+  }
+}
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& p, hipStream_t s) {
+  PfArgs a;
+  a.k_pool = p.k_pool;
+  a.v_pool = p.v_pool;
+  a.page_bytes = p.page_bytes;
+  a.max_pages = p.max_pages;
+  a.q = p.q;
+  a.cu_q = p.cu_q;
+  a.page_table = p.page_table;
+  a.seq_lens = p.seq_lens;
+  a.out = p.out;
+  a.B = p.B;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.G = p.Hq / p.Hkv;
+  a.QT = kPfRows / a.G;
+  a.scale_log2 = p.sm_scale * 1.4426950408889634f;
+  // blocks: at most ceil(Tq / QT) + B (each sequence ends at most one partial block)
+  const int64_t nblk = ((int64_t)p.Tq + a.QT - 1) / a.QT + p.B;
+  if (nblk > INT32_MAX / 2) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nblk, (unsigned)p.Hkv);
+  auto go = [&](auto kern, size_t lds) -> hipError_t {
+    if (lds > 64 * 1024) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(64 * kPfWaves), lds, s, a);
+    return hipGetLastError();
+  };
+  const bool bf = p.q_dtype == UQ_IN_BF16;
+  if (p.D == 128)
+    return bf ? go(prefill_kernel<128, UQ_IN_BF16>, PfLds<128>::kTotal) : go(prefill_kernel<128, UQ_IN_F32>, PfLds<128>::kTotal);
+  return bf ? go(prefill_kernel<64, UQ_IN_BF16>, PfLds<64>::kTotal) : go(prefill_kernel<64, UQ_IN_F32>, PfLds<64>::kTotal);
+}
+
+int prefill_max_seqs() { return kPfMaxSeqs; }
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   return a.D == 128 ? launch_decode_d<128>(a, s) : launch_decode_d<64>(a, s);
 }

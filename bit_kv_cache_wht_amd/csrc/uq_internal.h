@@ -61,4 +61,21 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+struct PrefillArgs {
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  int64_t page_bytes;
+  int32_t max_pages;
+  const void* q;               // [Tq][Hq][D]
+  int32_t q_dtype;
+  const int32_t* cu_q;         // [B + 1]
+  const int32_t* page_table;   // [B][max_pages]
+  const int32_t* seq_lens;     // [B]
+  float* out;                  // [Tq][Hq][D]
+  int32_t B, Hq, Hkv, D, Tq;
+  float sm_scale;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+int prefill_max_seqs();
+
 }  // namespace uq

@@ -180,3 +180,15 @@ def ragged(seed=1005, batch=128, lo=1024, hi=131072, chunk=256):
     head_dim 128, plus a 256-token chunk appended per sequence before each decode."""
     return make_workload(f"ragged_{batch}", batch, 32, 4, 128, [0] * batch, [0] * batch, seed=seed,
                          draw_lengths=_ragged_lengths(batch, lo, hi, chunk))
+
+
+def prefill_queries(wl: Workload, seed: int = 2001):
+    """Query rows for chunked prefill over the workload's cache: one row per new
+    token of every sequence (its new_lens[b] last positions), [T_q][H_q][d] in the
+    workload's input dtype, drawn N(0, 1) from their own stream, and the row
+    offsets cu_seqlens_q [B + 1] (int32)."""
+    q_lens = np.asarray(wl.new_lens, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    rng = np.random.Generator(np.random.PCG64([seed, 7]))
+    q32 = rng.standard_normal((int(cu[-1]), wl.num_q_heads, wl.head_dim), dtype=np.float32)
+    return (_to_bf16_bits(q32) if wl.in_dtype == "bf16" else q32), cu

@@ -211,6 +211,33 @@ int uq_append_decode_attention(const uq_kv_cache* cache, const void* k_new, cons
                                float* out, void* workspace, size_t workspace_bytes, uint32_t flags,
                                uq_stream_t stream);
 
+/*
+ * Chunked-prefill attention over an FP4 cache ([review] §1 and §5.4: the tokens
+ * of a new turn attend to the resident prefix instead of re-prefilling it).
+ * Sequence b's chunk -- q rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 -- holds
+ * its last q_len = cu_seqlens_q[b+1] - cu_seqlens_q[b] positions, already
+ * written to the cache; chunk token j, at position P = seq_lens[b] - q_len + j,
+ * attends to positions 0 .. P (causal).  Each output row equals the
+ * uq_decode_attention row of that query over a sequence of length P + 1: q is
+ * rotated and rounded to E4M3, the output is rotated back.
+ *   q             device [total_q][num_q_heads][head_dim], q_dtype (bf16 or f32)
+ *   cu_seqlens_q  device int32 [num_seqs + 1], non-decreasing, cu[0] = 0,
+ *                 cu[num_seqs] = total_q, each chunk no longer than its sequence
+ *   page_table, max_pages_per_seq, seq_lens, sm_scale as uq_decode_attention
+ *   out           device float32 [total_q][num_q_heads][head_dim]
+ *   flags         must be 0
+ * cache->format must be UQ_KV_FP4; num_q_heads a multiple of num_kv_heads with
+ * at most 128 query heads per KV head; num_seqs <= 4096 (else
+ * UQ_ERR_UNSUPPORTED).  No workspace.  total_q == 0 or num_seqs == 0 is a
+ * no-op.  Device-resident contents that break the rules above are undefined
+ * behaviour.
+ */
+int uq_prefill_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtype,
+                         const int32_t* cu_seqlens_q, int32_t total_q, const int32_t* page_table,
+                         int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                         int32_t num_q_heads, float sm_scale, float* out, uint32_t flags,
+                         uq_stream_t stream);
+
 /* FP8 baseline decode: same arguments; cache->format must be UQ_KV_FP8; the
  * query is rounded to E4M3 without rotation and `out` needs no unrotation
  * (flags must be 0). */

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     h = uq.lib()
     for n in names:
         assert hasattr(h, n), n
@@ -193,3 +193,28 @@ def test_stream_read_validation():
     assert f(FAKE + 4, 16, FAKE, None) == B.UQ_ERR_INVALID_ARG   # src not 16-byte aligned
     assert f(FAKE, 20, FAKE, None) == B.UQ_ERR_INVALID_ARG       # not a multiple of 16 bytes
     assert f(FAKE, 16, FAKE + 2, None) == B.UQ_ERR_INVALID_ARG   # sink not 4-byte aligned
+
+
+def test_prefill_validation():
+    f = uq.lib().uq_prefill_attention
+    ok = cache(B.UQ_KV_FP4, heads=2)
+
+    def call(c=ok, q=FAKE, dt=0, cu=FAKE, tq=10, pt=FAKE, mp=8, sl=FAKE, B_=3, Hq=16, scale=0.1, out=FAKE, fl=0):
+        return f(ctypes.byref(c) if c is not None else None, q, dt, cu, tq, pt, mp, sl, B_, Hq, scale, out, fl, None)
+
+    assert call(c=None) == B.UQ_ERR_INVALID_ARG
+    assert call(c=cache(B.UQ_KV_FP8, heads=2)) == B.UQ_ERR_INVALID_ARG     # FP4 caches only
+    assert call(fl=1) == B.UQ_ERR_INVALID_ARG
+    assert call(dt=3) == B.UQ_ERR_INVALID_ARG
+    assert call(B_=-1) == B.UQ_ERR_INVALID_ARG
+    assert call(tq=-1) == B.UQ_ERR_INVALID_ARG
+    assert call(mp=0) == B.UQ_ERR_INVALID_ARG
+    assert call(Hq=15) == B.UQ_ERR_UNSUPPORTED                  # not a multiple of the KV heads
+    assert call(Hq=2 * 129) == B.UQ_ERR_UNSUPPORTED             # more than 128 query heads per KV head
+    assert call(B_=4097) == B.UQ_ERR_UNSUPPORTED
+    assert call(scale=0.0) == B.UQ_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == B.UQ_ERR_INVALID_ARG
+    for name in ("q", "cu", "pt", "sl", "out"):
+        assert call(**{name: None}) == B.UQ_ERR_INVALID_ARG
+    assert call(tq=0, q=None, cu=None, pt=None, sl=None, out=None) == B.UQ_OK     # nothing to do
+    assert call(B_=0, q=None, cu=None, pt=None, sl=None, out=None) == B.UQ_OK
