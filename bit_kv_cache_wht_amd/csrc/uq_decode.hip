@@ -1584,7 +1584,7 @@ DecodeLayout decode_layout(int format, int B, int Hq, int Hkv, int D) {
 // cleared.  Rows are rotated back and stored like the decode's.
 namespace {
 constexpr int kPfWaves = 4;
-constexpr int kPfNB = 2;                                  // column blocks per wave
+constexpr int kPfNB = 4;                                  // column blocks per wave
 constexpr int kPfRows = 16 * kPfNB * kPfWaves;            // query rows of a workgroup
 constexpr int kPfMaxSeqs = 4096;                          // plan in LDS
 
@@ -1611,6 +1611,50 @@ struct PfLds {
   static constexpr int kMisc = kPlan + (kPfMaxSeqs + 1) * 4;      // [2 * kPfWaves] scratch
   static constexpr int kTotal = kMisc + 2 * kPfWaves * 4;
 };
+
+// The value step of Fp4Pol as f16 MFMA A operands, converted once and shared by
+// the wave's column blocks: VA[q][half][0 / 1] holds the even / odd channels of
+// channel pairs kCPL*(lane%16) + q for slots 8 half .. 8 half + 7 (the same
+// operands Fp4Pol::pv forms for its MMAs).
+template <int D>
+__device__ __forceinline__ void pf_convert_v(const typename Fp4Pol<D>::VStep& st, v8h (&VA)[D / 32][2][2]) {
+  constexpr int kCPL = D / 32;
+  const uint32_t s[4] = {st.vs.x, st.vs.y, st.vs.z, st.vs.w};
+  float sc[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int k = t & 3;
+    sc[t] = __uint_as_float(k == 3 ? s[t >> 2] >> 1 : s[t >> 2] << (23 - 8 * k));
+  }
+#pragma unroll
+  for (int q = 0; q < kCPL; ++q) {
+    const uint32_t c[4] = {st.vc[q].x, st.vc[q].y, st.vc[q].z, st.vc[q].w};
+    uint32_t X[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      v2h h;
+      switch (t & 3) {
+        case 0: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 0); break;
+        case 1: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 1); break;
+        case 2: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 2); break;
+        default: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 3); break;
+      }
+      X[t] = __builtin_bit_cast(uint32_t, h);
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t ev[4], od[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t x0 = X[8 * half + 2 * i], x1 = X[8 * half + 2 * i + 1];
+        ev[i] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+        od[i] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+      }
+      VA[q][half][0] = __builtin_bit_cast(v8h, make_uint4(ev[0], ev[1], ev[2], ev[3]));
+      VA[q][half][1] = __builtin_bit_cast(v8h, make_uint4(od[0], od[1], od[2], od[3]));
+    }
+  }
+}
 
 template <int D, int IN>
 __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) {
@@ -1722,6 +1766,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
     }
     const int key0 = 4 * kPage * s + kPage * j4;                // first key of this lane's page
     Pol::mask_v(vc, min(max(Ls - key0, 0), TOK));              // value slots past the sequence end
+    v8h VA[D / 32][2][2];
+    pf_convert_v<D>(vc, VA);
 #pragma unroll
     for (int c = 0; c < kPfNB; ++c) {
       v4f S[TOK / 4];
@@ -1770,7 +1816,13 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
         Pm[half][0] = __builtin_bit_cast(v8h, make_uint4(hw[0], hw[1], hw[2], hw[3]));
         Pm[half][1] = __builtin_bit_cast(v8h, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
-      Pol::pv(vc, Pm, O[c], 0);
+#pragma unroll
+      for (int q = 0; q < D / 32; ++q)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          O[c][2 * q] = mma2(VA[q][half][0], Pm[half], O[c][2 * q]);
+          O[c][2 * q + 1] = mma2(VA[q][half][1], Pm[half], O[c][2 * q + 1]);
+        }
     }
   };
   for (int s = 0; s < steps; s += 2) {
