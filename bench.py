@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix peak, vendor figure
 METRIC = "FP4-KV decode-attn us/step & HBM GB/s (% peak), 64 seq x 8K ctx GQA"
 
 
@@ -45,6 +46,7 @@ def parse():
     ap.add_argument("--workload", default="decode_gqa", choices=["decode_gqa", "long", "ragged", "tiny"])
     ap.add_argument("--no-baselines", action="store_true", help="skip the FP8/BF16 KV kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--unfused", action="store_true",
                     help="also time the FP4 step as two launches (append kernel, then decode kernel)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -216,6 +218,53 @@ def append_throughput(steps, warmup, settle_s):
             "us_per_call": round(us, 2), "quantized_tokens_per_s": round(T / (us * 1e-6)),
             "token_heads_per_s": round(T * H / (us * 1e-6)), "gbs": round(algo / (us * 1e-6) / 1e9, 1),
             "frac_hbm_peak": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "algo_bytes_per_call": algo}
+
+
+def prefill_throughput(reps, warmup):
+    """Chunked-prefill attention over the FP4 cache on the ragged workload (128
+    sequences of 1k..32k tokens, 32 q heads / 4 kv heads, head_dim 128, bf16; the
+    last 256 tokens of every sequence are the chunk): one uq_prefill_attention call
+    per rep, HIP events around the `reps` timed calls.  Useful flops count only the
+    causal (row, key) pairs: 4 * head_dim flops each (QK and PV)."""
+    import torch
+    import bit_kv_cache_wht_amd as uq
+    from bit_kv_cache_wht_amd import workloads as W
+    wl = W.ragged()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    bf = lambda a: dev(a.view(np.int16)).view(torch.bfloat16)
+    cache = uq.KvCache.allocate(uq.UQ_KV_FP4, wl.num_pages, wl.num_kv_heads, wl.head_dim)
+    for i in range(0, wl.total_tokens, 1 << 18):
+        j = np.arange(i, min(i + (1 << 18), wl.total_tokens))
+        uq.uq_quantize_append(cache, bf(wl.k[j]), bf(wl.v[j]), dev(wl.slot_mapping[j]))
+    q, cu = W.prefill_queries(wl)
+    qd, cud, pt, sl = bf(q), dev(cu), dev(wl.page_table), dev(wl.seq_lens)
+    out = torch.empty((q.shape[0], wl.num_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    scale = float(np.float32(1.0 / np.sqrt(wl.head_dim)))
+    call = lambda: uq.uq_prefill_attention(cache, qd, cud, pt, sl, scale, out)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    ql = np.diff(cu).astype(np.int64)
+    L = wl.seq_lens.astype(np.int64)
+    pairs = int(sum((L[b] - ql[b] + np.arange(1, ql[b] + 1)).sum() for b in range(wl.batch))) * wl.num_q_heads
+    tflops = 4 * wl.head_dim * pairs / (ms * 1e-3) / 1e12
+    del cache, qd, out
+    torch.cuda.empty_cache()
+    return {"workload": f"{wl.name}: {wl.batch} seq, {int(ql[0])}-token chunk after each prefix "
+                        f"({int(L.min())}..{int(L.max())} tokens), {wl.num_q_heads} q heads / {wl.num_kv_heads} kv heads, "
+                        f"head_dim {wl.head_dim}, bf16 queries, FP4 cache",
+            "ms_per_call": round(ms, 3), "query_tokens_per_s": round(int(cu[-1]) / (ms * 1e-3)),
+            "causal_pairs": pairs, "useful_tflops": round(tflops, 1),
+            "peak_tflops_f16_mfma": MFMA_F16_PEAK_TFLOPS,
+            "frac_f16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "note": "PV runs as two f16 products (P split hi/lo), so the MFMA work is 1.5x the useful flops"}
 
 
 def pmc_pass(args):
@@ -580,6 +629,10 @@ def main():
         log(f"append: {line['append']['us_per_call']} us per call, "
             f"{line['append']['quantized_tokens_per_s'] / 1e6:.1f} M tokens/s, {line['append']['gbs']} GB/s")
         torch.cuda.empty_cache()
+    if not args.no_prefill:
+        log("chunked prefill over the FP4 cache (ragged workload)")
+        line["prefill"] = prefill_throughput(max(5, args.steps // 10), 3)
+        log(f"prefill: {line['prefill']['ms_per_call']} ms per call, {line['prefill']['useful_tflops']} TFLOP/s useful")
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
