@@ -46,6 +46,16 @@ Readings where the pages are silent (each listed with its reason in the design doc):
       optimum of that rule on rotated unit vectors, where linear-domain rounding
       would put it near 0.207), clamped to [-127, 127], m == 0 giving -127;
       codes then saturate at +-6 as in R4.
+  R11 K-only rotation (``k_only=True``; [review] §3.1 table "Rotation": the
+      Walsh-Hadamard rotation is applied to K; [commentary] footnote 1:
+      "asymmetric K/V treatment"): K is rotated as in R1/R2, V is quantized in
+      its own basis (a zero channel stored as +0, like a rotated zero in R2),
+      and the attention output is not rotated back.
+  R12 Randomized-sign Hadamard (``signs``; [tq-guide] "알고리즘 원리", "랜덤 회전과
+      Beta 분포": a random +-1 diagonal times the Hadamard matrix): the rotation
+      is R = c_d H_d diag(s) with one caller-drawn s in {+1, -1}^d per cache,
+      applied to K, V and the query alike; the output goes back through
+      R^T = diag(s) c_d H_d.  Without signs R is the plain R2 transform.
 
 Parity pins: tests/test_oracle_pins.py (no function here is "parity unpinned").
 """
@@ -55,7 +65,7 @@ import numpy as np
 
 __all__ = [
     "PAGE_SIZE", "GROUP", "FMT_FP4", "FMT_FP8", "FMT_BF16",
-    "sylvester_hadamard", "wht_scale", "wht",
+    "sylvester_hadamard", "wht_scale", "wht", "rotate", "unrotate",
     "scale_exponent", "CONSTOPT_C", "SQRT2_UP", "scale_exponent_constopt",
     "E2M1_LEVELS", "e2m1_encode", "e2m1_decode",
     "quantize_fp4", "dequantize_fp4", "pack_nibbles", "unpack_nibbles",
@@ -102,6 +112,25 @@ def wht(x) -> np.ndarray:
     d = x.shape[-1]
     h = sylvester_hadamard(d).astype(np.float64)
     return (x @ h) * wht_scale(d) + 0.0      # H symmetric: (H x)^T = x^T H
+
+
+def rotate(x, signs=None) -> np.ndarray:
+    """R x over the last axis with R = c_d H_d diag(s) (reading R12): channel i
+    negated where signs[i] = -1, then the normalized WHT; signs None is R2's R."""
+    x = np.asarray(x, dtype=np.float64)
+    if signs is not None:
+        s = np.asarray(signs, dtype=np.float64)
+        if s.shape != (x.shape[-1],) or not np.all(np.abs(s) == 1.0):
+            raise ValueError("signs must be a +-1 vector of length head_dim")
+        x = x * s
+    return wht(x)
+
+
+def unrotate(y, signs=None) -> np.ndarray:
+    """R^T y = diag(s) c_d H_d y (the inverse of ``rotate``: c_d H_d is symmetric
+    and orthogonal, diag(s) its own inverse)."""
+    o = wht(y)
+    return o if signs is None else o * np.asarray(signs, dtype=np.float64)
 
 
 # --------------------------------------------------------------------------
@@ -351,15 +380,19 @@ def bf16_v_index(tok, ch, d):
     return ch * PAGE_SIZE + tok
 
 
-def append(fmt, k_pool, v_pool, k_new, v_new, slot_mapping, in_dtype="bf16", scale_mode="absmax"):
+def append(fmt, k_pool, v_pool, k_new, v_new, slot_mapping, in_dtype="bf16", scale_mode="absmax",
+           k_only=False, signs=None):
     """Write new tokens into the paged pools in place.
 
     k_new, v_new: [T][H_kv][d] as bf16 bits (uint16, in_dtype "bf16") or float32
     (in_dtype "f32").  slot_mapping[t] = page * 16 + offset; a negative slot skips
     the token.  FP4 rotates and quantizes ([review] §3.1; ``scale_mode`` as in
-    ``quantize_fp4``, constOpt with c = 0.156); FP8 rounds each value to
-    E4M3 with scale 1; BF16 stores the value (float32 input rounded to bf16).
+    ``quantize_fp4``, constOpt with c = 0.156; ``k_only`` leaves V unrotated, R11;
+    ``signs`` makes the rotation R12's); FP8 rounds each value to E4M3 with
+    scale 1; BF16 stores the value (float32 input rounded to bf16).
     """
+    if fmt != FMT_FP4 and (k_only or signs is not None):
+        raise ValueError("rotation variants apply to the FP4 cache only")
     k_new = np.asarray(k_new)
     T, H, d = k_new.shape
     to64 = bf16_bits_to_f64 if in_dtype == "bf16" else f32_to_f64
@@ -370,7 +403,8 @@ def append(fmt, k_pool, v_pool, k_new, v_new, slot_mapping, in_dtype="bf16", sca
         flat = pool.reshape(pool.shape[0], H, -1)
         x = to64(src[keep])                                   # [n][H][d] exact
         if fmt == FMT_FP4:
-            codes, sbytes = quantize_fp4(wht(x), scale_mode)  # [n][H][d], [n][H][d/32]
+            y = x + 0.0 if (is_v and k_only) else rotate(x, signs)
+            codes, sbytes = quantize_fp4(y, scale_mode)       # [n][H][d], [n][H][d/32]
             packed = pack_nibbles(codes)                      # [n][H][d/2]
             j = np.arange(d // 2)
             g = np.arange(d // GROUP)
@@ -426,11 +460,12 @@ def gather_dequant(fmt, pool, page_row, seq_len, head, d, is_v) -> np.ndarray:
     raise ValueError(fmt)
 
 
-def rotate_quantize_query(q, in_dtype="bf16") -> np.ndarray:
+def rotate_quantize_query(q, in_dtype="bf16", signs=None) -> np.ndarray:
     """E4M3 bytes of the rotated query ([review] §3.2: the query is rotated into the
-    key basis and rounded to FP8 E4M3), rounded directly from float64 (R5)."""
+    key basis and rounded to FP8 E4M3), rounded directly from float64 (R5); with
+    ``signs`` the rotation is R12's."""
     to64 = bf16_bits_to_f64 if in_dtype == "bf16" else f32_to_f64
-    return e4m3_encode(wht(to64(q)))
+    return e4m3_encode(rotate(to64(q), signs))
 
 
 def attention(qhat, k, v, sm_scale) -> np.ndarray:
@@ -444,13 +479,17 @@ def attention(qhat, k, v, sm_scale) -> np.ndarray:
 
 
 def decode_attention_rows(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table, seq_lens,
-                          sm_scale, rows, in_dtype="bf16") -> np.ndarray:
+                          sm_scale, rows, in_dtype="bf16", k_only=False, signs=None) -> np.ndarray:
     """Output rows for the (sequence, query head) pairs in ``rows`` ([n][2]).
 
-    FP4: q rotated and rounded to E4M3, output rotated back with the same
-    normalized WHT (self-inverse); FP8: q rounded to E4M3, no rotation; BF16: q
-    as given.  A sequence of length 0 gives a zero row.
+    FP4: q rotated and rounded to E4M3, output rotated back with the transpose of
+    the rotation (R2's normalized WHT is its own inverse); with ``k_only`` (R11)
+    the output stays as attended, V being unrotated; ``signs`` as in R12.  FP8:
+    q rounded to E4M3, no rotation; BF16: q as given.  A sequence of length 0
+    gives a zero row.
     """
+    if fmt != FMT_FP4 and (k_only or signs is not None):
+        raise ValueError("rotation variants apply to the FP4 cache only")
     q = np.asarray(q)
     Hq = q.shape[1]
     group = Hq // num_kv_heads
@@ -468,18 +507,18 @@ def decode_attention_rows(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table, s
                            gather_dequant(fmt, v_pool, page_table[b], L, hk, d, True))}
         K, V = cache[key]
         if fmt == FMT_FP4:
-            qhat = e4m3_decode(rotate_quantize_query(q[b, h], in_dtype))
+            qhat = e4m3_decode(rotate_quantize_query(q[b, h], in_dtype, signs))
         elif fmt == FMT_FP8:
             qhat = e4m3_decode(e4m3_encode(to64(q[b, h])))
         else:
             qhat = to64(q[b, h])
         o = attention(qhat[None, :], K, V, float(sm_scale))[0]
-        out[n] = wht(o) if fmt == FMT_FP4 else o
+        out[n] = unrotate(o, signs) if (fmt == FMT_FP4 and not k_only) else o
     return out
 
 
 def prefill_attention(fmt, k_pool, v_pool, num_kv_heads, d, q, q_lens, page_table, seq_lens,
-                      sm_scale, in_dtype="bf16") -> np.ndarray:
+                      sm_scale, in_dtype="bf16", k_only=False, signs=None) -> np.ndarray:
     """Causal attention of chunks of query tokens over the cache ([review] §1 and
     §5.4: a new turn's tokens read the resident prefix instead of re-prefilling
     it; reading R10).  q [T_q][H_q][d] holds sequence 0's chunk, then sequence
@@ -492,15 +531,16 @@ def prefill_attention(fmt, k_pool, v_pool, num_kv_heads, d, q, q_lens, page_tabl
     j_of = np.arange(q.shape[0]) - np.repeat(np.cumsum(q_lens) - q_lens, q_lens)
     prefix = seq_lens[b_of] - q_lens[b_of] + j_of + 1                  # positions 0 .. P
     table = np.asarray(page_table)[b_of]
-    return decode_attention(fmt, k_pool, v_pool, num_kv_heads, d, q, table, prefix, sm_scale, in_dtype)
+    return decode_attention(fmt, k_pool, v_pool, num_kv_heads, d, q, table, prefix, sm_scale, in_dtype,
+                            k_only, signs)
 
 
 def decode_attention(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table, seq_lens,
-                     sm_scale, in_dtype="bf16") -> np.ndarray:
+                     sm_scale, in_dtype="bf16", k_only=False, signs=None) -> np.ndarray:
     """All output rows [B][H_q][d] (float64)."""
     q = np.asarray(q)
     B, Hq = q.shape[0], q.shape[1]
     rows = [(b, h) for b in range(B) for h in range(Hq)]
     out = decode_attention_rows(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table,
-                                seq_lens, sm_scale, rows, in_dtype)
+                                seq_lens, sm_scale, rows, in_dtype, k_only, signs)
     return out.reshape(B, Hq, d)

@@ -495,6 +495,106 @@ def test_fp4_prefill_equals_causal_attention_on_exact_inputs():
     assert np.array_equal(out2[chunks[0]:], out[chunks[0]:])          # sequence 1 is 21 tokens long
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_signed_rotation_is_library_hadamard_times_sign_diagonal(d):
+    # R12: R = c_d H_d diag(s), built here from scipy's Hadamard matrix; R is
+    # orthogonal and unrotate is its transpose.
+    rng = np.random.default_rng(40 + d)
+    s = rng.choice([-1.0, 1.0], size=d)
+    R = scipy.linalg.hadamard(d).astype(np.float64) / math.sqrt(d) @ np.diag(s)
+    x = rng.standard_normal((5, d))
+    np.testing.assert_allclose(O.rotate(x, s), x @ R.T, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(O.unrotate(x, s), x @ R, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(O.unrotate(O.rotate(x, s), s), x, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(R.T @ R, np.eye(d), rtol=0, atol=1e-14)
+    assert np.array_equal(O.rotate(x, np.ones(d)), O.wht(x))
+    with pytest.raises(ValueError):
+        O.rotate(x, np.full(d, 0.5))
+
+
+def test_all_negative_signs_flip_every_nonzero_code():
+    # s = -1 everywhere makes R x = -(c_d H_d x): the same scale bytes, and every
+    # code's sign bit flipped except where the rotated value is exactly zero (+0
+    # in both, R2).  Rows: d = 64 grid rows scaled off the grid, so the codes
+    # include exact zeros, small values of both signs and saturated ones.
+    d = 64
+    x, _ = _grid_workload(d=d, T=16, H=2, seed=41)
+    x = (x.astype(np.float64) * 1.37).astype(np.float32)
+    zero = (x.astype(np.float64) @ scipy.linalg.hadamard(d).astype(np.float64)) == 0.0   # [16][2][d]
+    assert zero.any() and not zero.all()
+    slots = np.arange(16, dtype=np.int32)
+    pools = {}
+    for name, sg in (("plain", None), ("neg", -np.ones(d))):
+        kp, vp = O.new_pool(O.FMT_FP4, 1, 2, d), O.new_pool(O.FMT_FP4, 1, 2, d)
+        O.append(O.FMT_FP4, kp, vp, x, x, slots, in_dtype="f32", signs=sg)
+        pools[name] = (kp, vp)
+    cj = np.arange(d // 2)
+    for pool_i, is_v in ((0, False), (1, True)):
+        cf = O.fp4_v_code_offset if is_v else O.fp4_k_code_offset
+        sf = O.fp4_v_scale_offset if is_v else O.fp4_k_scale_offset
+        for h in range(2):
+            a = pools["plain"][pool_i].reshape(1, 2, -1)[0, h]
+            b = pools["neg"][pool_i].reshape(1, 2, -1)[0, h]
+            for t in range(16):
+                ca = O.unpack_nibbles(a[cf(t, cj, d)])
+                cb = O.unpack_nibbles(b[cf(t, cj, d)])
+                assert np.array_equal(np.where(zero[t, h], ca, ca ^ 8), cb)
+                assert np.array_equal(ca[zero[t, h]], np.zeros(int(zero[t, h].sum()), np.uint8))
+                assert np.array_equal(a[sf(t, np.arange(d // 32), d)], b[sf(t, np.arange(d // 32), d)])
+
+
+@pytest.mark.parametrize("variant", ["signs", "k_only", "k_only_signs"])
+def test_fp4_rotation_variants_equal_plain_attention_on_exact_inputs(variant):
+    # R11 / R12 on inputs exact on the FP4 / E4M3 grids after the variant's
+    # rotation (K and the query through R = c_d H_d diag(s), V through R or left
+    # as it is): decode and prefill must equal plain attention on the original
+    # vectors.  A sign left out anywhere, or V rotated under k_only, puts the
+    # rows off the grid and fails by the quantization error.
+    d, T, H, G = 64, 40, 2, 3
+    k_only = variant.startswith("k_only")
+    rng = np.random.default_rng(50 + len(variant))
+    s = rng.choice([-1.0, 1.0], size=d) if variant.endswith("signs") else None
+    sv = np.ones(d) if s is None else s
+    _, y_k = _grid_workload(d=d, T=T, H=H, seed=51)
+    _, y_v = _grid_workload(d=d, T=T, H=H, seed=52)
+    x_k = (sv * O.wht(y_k)).astype(np.float32)                  # R^T y: exact at d = 64
+    x_v = (y_v if k_only else sv * O.wht(y_v)).astype(np.float32)
+    assert np.array_equal(O.rotate(x_k.astype(np.float64), s), y_k)
+    q_rot = rng.choice([0.0, 0.5, 1.0, -1.0, 2.0, -1.5, 0.25, -3.0], size=(2, H * G, d))
+    q = (sv * O.wht(q_rot)).astype(np.float32)
+    lens = np.array([T, 17])
+    pages = rng.permutation(6)
+    table = np.stack([pages[:3], pages[3:6]])
+    kp, vp = O.new_pool(O.FMT_FP4, 6, H, d), O.new_pool(O.FMT_FP4, 6, H, d)
+    for b in range(2):
+        L = lens[b]
+        slots = table[b][np.arange(L) // 16] * 16 + np.arange(L) % 16
+        O.append(O.FMT_FP4, kp, vp, x_k[:L], x_v[:L], slots, in_dtype="f32", k_only=k_only, signs=s)
+    for h in range(H):
+        assert np.array_equal(O.gather_dequant(O.FMT_FP4, vp, table[0], T, h, d, True), y_v[:, h])
+    scale = 1 / math.sqrt(d)
+    out = O.decode_attention(O.FMT_FP4, kp, vp, H, d, q, table, lens, scale, in_dtype="f32", k_only=k_only,
+                             signs=s)
+    for b in range(2):
+        for h in range(H * G):
+            ref = _brute_attention(q[b, h].astype(np.float64), x_k[:lens[b], h // G].astype(np.float64),
+                                   x_v[:lens[b], h // G].astype(np.float64), scale)
+            np.testing.assert_allclose(out[b, h], ref, rtol=0, atol=1e-12)
+    # prefill: a 5-token chunk at the end of sequence 0
+    qc = np.repeat(q[:1], 5, axis=0)
+    pf = O.prefill_attention(O.FMT_FP4, kp, vp, H, d, qc, np.array([5, 0]), table, lens, scale, in_dtype="f32",
+                             k_only=k_only, signs=s)
+    for j in range(5):
+        P = T - 5 + j
+        for h in range(H * G):
+            ref = _brute_attention(qc[j, h].astype(np.float64), x_k[:P + 1, h // G].astype(np.float64),
+                                   x_v[:P + 1, h // G].astype(np.float64), scale)
+            np.testing.assert_allclose(pf[j, h], ref, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.append(O.FMT_FP8, O.new_pool(O.FMT_FP8, 6, H, d), O.new_pool(O.FMT_FP8, 6, H, d), x_k[:1], x_v[:1],
+                 np.zeros(1, np.int32), in_dtype="f32", k_only=True)
+
+
 def _small_pools(fmt, seed=12, B=3, H=2, G=4, d=128, lens=(1, 33, 70)):
     wl = W.make_workload("attn", B, H * G, H, d, list(lens), list(lens), seed=seed)
     kp, vp = O.new_pool(fmt, wl.num_pages, H, d), O.new_pool(fmt, wl.num_pages, H, d)
