@@ -14,9 +14,12 @@ from ._binding import (  # noqa: F401
     UQ_KV_BF16,
     UQ_KV_FP4,
     UQ_KV_FP8,
+    UQ_ROT_K_ONLY,
+    UQ_ROT_SIGNS,
     KvCache,
     UqError,
     lib,
+    sign_words,
     uq_append_bf16,
     uq_append_fp8,
     uq_append_decode_attention,

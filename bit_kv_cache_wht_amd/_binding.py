@@ -11,6 +11,8 @@ UQ_IN_BF16, UQ_IN_F32 = 0, 1
 UQ_PAGE_SIZE = 16
 UQ_FLAG_OUT_ROTATED = 1
 UQ_FLAG_SCALE_CONSTOPT = 2
+UQ_ROT_K_ONLY = 1
+UQ_ROT_SIGNS = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libuq.so")
 
@@ -27,7 +29,8 @@ class UqError(RuntimeError):
 class _Cache(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p)]
+                ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("rotation", ctypes.c_uint32), ("rotation_signs", ctypes.c_uint32 * 4)]
 
 
 _P = ctypes.c_void_p
@@ -84,9 +87,15 @@ class KvCache:
     head_dim: int
     k_pool: object
     v_pool: object
+    rotation: int = 0                        # UQ_ROT_* bits
+    rotation_signs: tuple = (0, 0, 0, 0)     # sign bits of s (UQ_ROT_SIGNS)
 
     @classmethod
-    def allocate(cls, fmt: int, num_pages: int, num_kv_heads: int, head_dim: int, device="cuda", zero=True):
+    def allocate(cls, fmt: int, num_pages: int, num_kv_heads: int, head_dim: int, device="cuda", zero=True,
+                 k_only=False, signs=None):
+        """Zeroed pools for a new cache.  FP4 only: ``k_only`` leaves V unrotated
+        (UQ_ROT_K_ONLY); ``signs`` (head_dim values of +1 / -1) makes the rotation
+        c_d H diag(signs) (UQ_ROT_SIGNS)."""
         import torch
         blk = uq_head_block_bytes(fmt, head_dim)
         if blk == 0:
@@ -96,7 +105,11 @@ class KvCache:
         alloc = torch.zeros if zero else torch.empty
         k = alloc((num_pages, pb), dtype=torch.uint8, device=device)
         v = alloc((num_pages, pb), dtype=torch.uint8, device=device)
-        return cls(fmt, num_pages, num_kv_heads, head_dim, k, v)
+        rot, words = (UQ_ROT_K_ONLY if k_only else 0), (0, 0, 0, 0)
+        if signs is not None:
+            rot |= UQ_ROT_SIGNS
+            words = sign_words(signs, head_dim)
+        return cls(fmt, num_pages, num_kv_heads, head_dim, k, v, rot, words)
 
     def blocks(self, pool):
         """[num_pages][num_kv_heads][head block bytes] view of a pool (no copy)."""
@@ -105,7 +118,20 @@ class KvCache:
 
     def c(self) -> _Cache:
         return _Cache(self.format, self.num_pages, UQ_PAGE_SIZE, self.num_kv_heads, self.head_dim,
-                      _ptr(self.k_pool), _ptr(self.v_pool))
+                      _ptr(self.k_pool), _ptr(self.v_pool), self.rotation, (ctypes.c_uint32 * 4)(*self.rotation_signs))
+
+
+def sign_words(signs, head_dim: int) -> tuple:
+    """The four rotation_signs words for a vector of head_dim signs (+1 / -1):
+    bit i % 32 of word i / 32 set where signs[i] is -1."""
+    import numpy as np
+    s = np.asarray(signs)
+    if s.shape != (head_dim,) or not np.all(np.abs(s) == 1):
+        raise ValueError("signs must hold head_dim values of +1 or -1")
+    words = [0, 0, 0, 0]
+    for i in np.nonzero(s < 0)[0]:
+        words[int(i) // 32] |= 1 << (int(i) % 32)
+    return tuple(words)
 
 
 def _ptr(t) -> int | None:

@@ -25,7 +25,22 @@ int check_cache(const uq_kv_cache* c, int want_format) {
   if (!dim_ok(c->head_dim)) return UQ_ERR_UNSUPPORTED;
   if (c->num_kv_heads < 1 || c->num_pages < 1) return UQ_ERR_INVALID_ARG;
   if (c->k_pool == nullptr || c->v_pool == nullptr) return UQ_ERR_INVALID_ARG;
+  // rotation variants: FP4 only; sign bits only with UQ_ROT_SIGNS and below head_dim
+  if ((c->rotation & ~(UQ_ROT_K_ONLY | UQ_ROT_SIGNS)) != 0u) return UQ_ERR_INVALID_ARG;
+  if (c->rotation != 0u && c->format != UQ_KV_FP4) return UQ_ERR_INVALID_ARG;
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t allowed = (c->rotation & UQ_ROT_SIGNS) && 32 * w < c->head_dim ? ~0u : 0u;
+    if ((c->rotation_signs[w] & ~allowed) != 0u) return UQ_ERR_INVALID_ARG;
+  }
   return UQ_OK;
+}
+
+// The rotation variant of a validated cache as the kernels take it.
+uq::Rot rot_of(const uq_kv_cache* c) {
+  uq::Rot r;
+  r.k_only = (c->rotation & UQ_ROT_K_ONLY) ? 1u : 0u;
+  for (int w = 0; w < 4; ++w) r.s[w] = (c->rotation & UQ_ROT_SIGNS) ? c->rotation_signs[w] : 0u;
+  return r;
 }
 
 typedef hipError_t (*append_launcher)(const uq::AppendArgs&, int, int, hipStream_t);
@@ -51,6 +66,7 @@ int append_common(const uq_kv_cache* cache, int format, const void* k_new, const
   a.T = num_tokens;
   a.H = cache->num_kv_heads;
   a.constopt = (flags & UQ_FLAG_SCALE_CONSTOPT) ? 1 : 0;
+  a.rot = rot_of(cache);
   return hip_status(launch(a, cache->head_dim, in_dtype, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -98,7 +114,8 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   a.out = out;
   a.ws = static_cast<uint8_t*>(workspace);
   a.lay = uq::decode_layout(format, num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim);
-  a.unrotate = format == UQ_KV_FP4 && !(flags & UQ_FLAG_OUT_ROTATED);
+  a.rot = rot_of(cache);
+  a.unrotate = format == UQ_KV_FP4 && !(flags & UQ_FLAG_OUT_ROTATED) && a.rot.k_only == 0u;
   a.constopt = (flags & UQ_FLAG_SCALE_CONSTOPT) != 0u;
   a.k_new = k_new;
   a.v_new = v_new;
@@ -250,6 +267,7 @@ int uq_prefill_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtyp
   a.D = cache->head_dim;
   a.Tq = total_q;
   a.sm_scale = sm_scale;
+  a.rot = rot_of(cache);
   return hip_status(uq::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -23,7 +23,7 @@ namespace uq {
 // LPR = D / 32 lanes per row (E = 32: one quantization group per lane) for large
 // batches; LPR = D / 8 (E = 8, four lanes per group) when few rows are written,
 // which cuts the float64 work each lane does on its own.
-template <int D, int IN, int LPR>
+template <int D, int IN, int LPR, bool RV>
 __global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
   using Row = Fp4Row<D, IN, LPR>;
   constexpr int RPW = 64 / LPR;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
 
   Row x;
   x.load(is_v ? a.v : a.k, tr, p);
-  x.quantize(p, a.constopt != 0);
+  x.template quantize<RV>(p, a.constopt != 0, a.rot, is_v);
   if (!in_range || slot < 0) return;
   const int page = slot >> 4, off = slot & 15;
   uint8_t* blk = (is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes + (int64_t)h * Row::BLK;
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
 // each wave fetching its next group's inputs (and slots) before working on the
 // current one, so that the float64 work of one group hides the memory latency
 // of the next.  Rows r < 2T H are indexed in 32 bits (the host bounds T H).
-template <int D, int IN, int LPR>
+template <int D, int IN, int LPR, bool RV>
 __global__ __launch_bounds__(256) void append_fp4_stream_kernel(AppendArgs a) {
   using Row = Fp4Row<D, IN, LPR>;
   constexpr int RPW = 64 / LPR;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void append_fp4_stream_kernel(AppendArgs a) {
     const int gn = g + nwaves;
     const bool more = gn < groups;                 // wave-uniform
     if (more) fetch(nxt, gn);
-    cur.x.quantize(p, a.constopt != 0);
+    cur.x.template quantize<RV>(p, a.constopt != 0, a.rot, cur.is_v);
     if (cur.live && cur.slot >= 0) {
       const int h = cur.tr % a.H;
       const int page = cur.slot >> 4, off = cur.slot & 15;
@@ -207,26 +207,36 @@ static unsigned grid_rows(int64_t rows, int rows_per_wave) {
   return (unsigned)((waves + 3) / 4);
 }
 
-template <int D, int IN>
+template <int D, int IN, bool RV>
 static void launch_fp4_rows(const AppendArgs& a, int64_t rows, hipStream_t s) {
   // D/8 lanes per row (8 channels each) while the rows fill less than about two
   // waves per SIMD at D/32 lanes per row; D/32 lanes per row beyond that
   constexpr int kFewRows = 256 * 4 * 2 * (64 / (D / 32));
   if (rows < kFewRows) {
-    hipLaunchKernelGGL((append_fp4_kernel<D, IN, D / 8>), dim3(grid_rows(rows, 64 / (D / 8))), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((append_fp4_kernel<D, IN, D / 8, RV>), dim3(grid_rows(rows, 64 / (D / 8))), dim3(256), 0, s,
+                       a);
   } else {
     constexpr int LPR = APPEND_LPR(D);
     const unsigned blocks = (unsigned)std::min<int64_t>(grid_rows(rows, 64 / LPR), (int64_t)append_cus() * APPEND_BPC);
-    hipLaunchKernelGGL((append_fp4_stream_kernel<D, IN, LPR>), dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((append_fp4_stream_kernel<D, IN, LPR, RV>), dim3(blocks), dim3(256), 0, s, a);
   }
+}
+
+template <bool RV>
+static void launch_fp4_dispatch(const AppendArgs& a, int D, int in, int64_t rows, hipStream_t s) {
+  if (D == 128 && in == UQ_IN_BF16) launch_fp4_rows<128, UQ_IN_BF16, RV>(a, rows, s);
+  else if (D == 128) launch_fp4_rows<128, UQ_IN_F32, RV>(a, rows, s);
+  else if (in == UQ_IN_BF16) launch_fp4_rows<64, UQ_IN_BF16, RV>(a, rows, s);
+  else launch_fp4_rows<64, UQ_IN_F32, RV>(a, rows, s);
 }
 
 hipError_t launch_append_fp4(const AppendArgs& a, int D, int in, hipStream_t s) {
   const int64_t rows = 2LL * a.T * a.H;
-  if (D == 128 && in == UQ_IN_BF16) launch_fp4_rows<128, UQ_IN_BF16>(a, rows, s);
-  else if (D == 128) launch_fp4_rows<128, UQ_IN_F32>(a, rows, s);
-  else if (in == UQ_IN_BF16) launch_fp4_rows<64, UQ_IN_BF16>(a, rows, s);
-  else launch_fp4_rows<64, UQ_IN_F32>(a, rows, s);
+  // caches with a rotation variant take their own instantiations, so the
+  // plain path carries none of the variant code
+  const bool rv = a.rot.k_only != 0u || (a.rot.s[0] | a.rot.s[1] | a.rot.s[2] | a.rot.s[3]) != 0u;
+  if (rv) launch_fp4_dispatch<true>(a, D, in, rows, s);
+  else launch_fp4_dispatch<false>(a, D, in, rows, s);
   return hipGetLastError();
 }
 

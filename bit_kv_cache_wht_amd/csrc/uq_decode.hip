@@ -701,8 +701,10 @@ template <int D, int IN, int FMT> struct QueryRows {
   }
 
   // Converts and stores the part into the LDS row dst (the 16 threads of a row
-  // must call it together).
-  __device__ void finish(uint8_t* dst_row, int p) const {
+  // must call it together); FP4 rotates by c_d H, or with RV by
+  // R = c_d H diag(s) with rot's signs.
+  template <bool RV>
+  __device__ __forceinline__ void finish(uint8_t* dst_row, int p, const Rot& rot) const {
     if constexpr (FMT == UQ_KV_BF16) {
       uint8_t* dst = dst_row + 2 * E * p;
       if constexpr (kBytes == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0].x, w[0].y);
@@ -716,6 +718,10 @@ template <int D, int IN, int FMT> struct QueryRows {
         else x[e] = (double)__uint_as_float(u[e]);
       }
       if constexpr (FMT == UQ_KV_FP4) {
+        if (RV && has_signs(rot)) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) x[e] = flip_sign(x[e], sign_mask(rot, E * p + e));
+        }
 #pragma unroll
         for (int h = 1; h < E; h <<= 1)
 #pragma unroll
@@ -746,10 +752,11 @@ template <int D, int IN, int FMT> struct QueryRows {
 };
 
 // Normalizes one merged output row held as channels lane + 64k and, for FP4,
-// rotates it back with the normalized WHT (stage h = 64 inside the lane, the
-// others across lanes), then stores it.
-template <int D, bool UNROT>
-__device__ void store_row(float (&o)[D / 64], float l, float* dst, int lane) {
+// rotates it back through R^T = diag(s) c_d H (the normalized WHT with stage
+// h = 64 inside the lane and the others across lanes, then the cache's signs),
+// then stores it.
+template <int D, bool UNROT, bool RV>
+__device__ __forceinline__ void store_row(float (&o)[D / 64], float l, float* dst, int lane, const Rot& rot) {
   constexpr int PER = D / 64;
   const float inv = l > 0.f ? 1.f / l : 0.f;      // l == 0 only for empty sequences
 #pragma unroll
@@ -769,6 +776,13 @@ __device__ void store_row(float (&o)[D / 64], float l, float* dst, int lane) {
       }
 #pragma unroll
     for (int k = 0; k < PER; ++k) o[k] *= wht_cf<D>();
+    if (RV && has_signs(rot)) {                 // channel lane + 64 k: bit lane % 32 of word 2 k + lane / 32
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const uint32_t w = (lane & 32) ? rot.s[2 * k + 1] : rot.s[2 * k];
+        o[k] = flip_sign(o[k], ((w >> (lane & 31)) & 1u) << 31);
+      }
+    }
   }
 #pragma unroll
   for (int k = 0; k < PER; ++k) dst[lane + 64 * k] = o[k];
@@ -792,8 +806,9 @@ template <int M> __device__ __forceinline__ float xor32(float v, int lane) {
 // As store_row for a row held by one 32-lane half of the wave, channel
 // (lane % 32) + 32 c in o[c]: the butterfly stages 32 and 64 run inside the
 // lane, stages 1 .. 16 across lanes of the half.
-template <int D, bool UNROT>
-__device__ void store_row32(float (&o)[D / 32], float l, float* dst, bool live, int lane) {
+template <int D, bool UNROT, bool RV>
+__device__ __forceinline__ void store_row32(float (&o)[D / 32], float l, float* dst, bool live, int lane,
+                                            const Rot& rot) {
   constexpr int PC = D / 32;
   const float inv = l > 0.f ? 1.f / l : 0.f;      // l == 0 only for empty sequences
 #pragma unroll
@@ -823,6 +838,10 @@ __device__ void store_row32(float (&o)[D / 32], float l, float* dst, bool live, 
     stage(std::integral_constant<int, 1>{});
 #pragma unroll
     for (int c = 0; c < PC; ++c) o[c] *= wht_cf<D>();
+    if (RV && has_signs(rot)) {                 // channel (lane % 32) + 32 c: bit lane % 32 of word c
+#pragma unroll
+      for (int c = 0; c < PC; ++c) o[c] = flip_sign(o[c], ((rot.s[c] >> (lane & 31)) & 1u) << 31);
+    }
   }
   if (live) {
 #pragma unroll
@@ -831,10 +850,10 @@ __device__ void store_row32(float (&o)[D / 32], float l, float* dst, bool live, 
 }
 
 // Quantizes and stores a row of the fused step's newest token.
-template <class Row>
+template <bool RV, class Row>
 __device__ __forceinline__ void write_new(Row& row, uint8_t* blk, int off, bool live, bool is_v, int p,
-                                          bool constopt) {
-  row.quantize(p, constopt);
+                                          bool constopt, const Rot& rot) {
+  row.template quantize<RV>(p, constopt, rot, is_v);
   if (live) {
     if (is_v) row.store_v(blk, off, p);
     else row.store_k(blk, off, p);
@@ -858,6 +877,7 @@ struct KArgs {
   const void* k_new;         // fused step (FP4): the newest token's K and V, [B][Hkv][D]
   const void* v_new;         // in the query's dtype; null: attention only
   int32_t constopt;          // fused step: constOpt group scales for the written token
+  Rot rot;                   // FP4: the cache's rotation variant
 };
 
 // Split partials cross workgroups that may sit on different compute dies,
@@ -921,7 +941,7 @@ enum { kRecB = 0, kRecPBegin, kRecNpg, kRecHk, kRecLRel, kRecNStep, kRecSlot, kR
 // writes its output rows; otherwise the workgroup writes a partial (slot 2w for
 // the first segment of its share, 2w + 1 for the last) and the last of the
 // item's workgroups to arrive (device-scope counter) merges the partials.
-template <class Pol, int D, int IN, int FMT, bool UNROT>
+template <class Pol, int D, int IN, int FMT, bool UNROT, bool RV>
 __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs a,
                                                                    const int32_t* __restrict__ page_table,
                                                                    const int32_t* __restrict__ seq_lens) {
@@ -1102,7 +1122,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         }
         if (__ballot(sg_new && sg_first + sg_nstep <= NW * (N + 1)) != 0) {
           if (nwrite) {
-            write_new(nrow, nblk, noff, nlive, nv, np, a.constopt != 0);
+            write_new<RV>(nrow, nblk, noff, nlive, nv, np, a.constopt != 0, a.rot);
             nwrite = false;
           }
           __syncthreads();
@@ -1180,7 +1200,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     ck = claim_at(g0[N]);
     meta[N] = ck.meta;
     if constexpr (FMT == UQ_KV_FP4) {
-      if (nwrite) write_new(nrow, nblk, noff, nlive, nv, np, a.constopt != 0);   // ordered before the main loop's claims by its barrier
+      if (nwrite) write_new<RV>(nrow, nblk, noff, nlive, nv, np, a.constopt != 0, a.rot);   // ordered before the main loop's claims by its barrier
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -1189,11 +1209,11 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     }
     cv = c0[N - 1];
 
-    if (qr0 < nrows) qrows.finish(qs + qr0 * D * ESZ, qp);
+    if (qr0 < nrows) qrows.template finish<RV>(qs + qr0 * D * ESZ, qp, a.rot);
     for (int r = qr0 + NT / 16; r < nrows; r += NT / 16) {
       QueryRows<D, IN, FMT> more;
       more.load(a.q, qrow_of(r), true, qp);
-      more.finish(qs + r * D * ESZ, qp);
+      more.template finish<RV>(qs + r * D * ESZ, qp, a.rot);
     }
     __syncthreads();
 
@@ -1370,8 +1390,8 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
           }
         }
         if (__any(whole))                        // the whole wave runs the butterflies
-          store_row32<D, UNROT>(o, l, a.out + ((int64_t)r[kRecB] * a.Hq + (int64_t)r[kRecHk] * G + h) * D, whole,
-                                ln);
+          store_row32<D, UNROT, RV>(o, l, a.out + ((int64_t)r[kRecB] * a.Hq + (int64_t)r[kRecHk] * G + h) * D, whole,
+                                ln, a.rot);
       }
     }
 
@@ -1450,7 +1470,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
             }
           }
         }
-        store_row<D, UNROT>(o, l, a.out + ((int64_t)b * a.Hq + (int64_t)hk * G + h) * D, lane);
+        store_row<D, UNROT, RV>(o, l, a.out + ((int64_t)b * a.Hq + (int64_t)hk * G + h) * D, lane, a.rot);
       }
     }
     if (tid == 0) *ctr = 0;                        // every claim of this round is done (barrier above)
@@ -1483,7 +1503,7 @@ DeviceLimits device_limits() {
   return {cus, lds};
 }
 
-template <int D, int IN, int FMT, bool UNROT, class Pol>
+template <int D, int IN, int FMT, bool UNROT, class Pol, bool RV = false>
 hipError_t launch_one(const DecodeArgs& a, const KArgs& k0, hipStream_t s) {
   constexpr int NW = 4 * Pol::kOcc;
   constexpr int ESZ = FMT == UQ_KV_BF16 ? 2 : 1;
@@ -1496,7 +1516,7 @@ hipError_t launch_one(const DecodeArgs& a, const KArgs& k0, hipStream_t s) {
   while (R > 1 && Lds(R, NW, G, D, ESZ, a.B).total > dl.lds) --R;
   const int lds = Lds(R, NW, G, D, ESZ, a.B).total;
   if (lds > dl.lds) return hipErrorInvalidConfiguration;
-  auto kern = decode_kernel<Pol, D, IN, FMT, UNROT>;
+  auto kern = decode_kernel<Pol, D, IN, FMT, UNROT, RV>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1507,6 +1527,10 @@ hipError_t launch_one(const DecodeArgs& a, const KArgs& k0, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NW), (size_t)lds, s, k, a.page_table, a.seq_lens);
   return hipGetLastError();
 }
+
+template <class T> struct PolTag {
+  using type = T;
+};
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
@@ -1529,20 +1553,26 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   k.k_new = a.k_new;
   k.v_new = a.v_new;
   k.constopt = a.constopt ? 1 : 0;
+  k.rot = a.rot;
   hipError_t e;
   if (a.ev_start != nullptr && (e = hipEventRecord(a.ev_start, s)) != hipSuccess) return e;
   const bool bf = a.q_dtype == UQ_IN_BF16;
+  // FP4 caches with a rotation variant take their own instantiations, so the
+  // plain path carries none of the variant code
+  auto fp4 = [&](auto pol, auto rv) -> hipError_t {
+    using P = typename decltype(pol)::type;
+    constexpr bool RV = decltype(rv)::value;
+    if (a.unrotate) return bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP4, true, P, RV>(a, k, s)
+                              : launch_one<D, UQ_IN_F32, UQ_KV_FP4, true, P, RV>(a, k, s);
+    return bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP4, false, P, RV>(a, k, s)
+              : launch_one<D, UQ_IN_F32, UQ_KV_FP4, false, P, RV>(a, k, s);
+  };
+  const bool rv = a.rot.k_only != 0u || (a.rot.s[0] | a.rot.s[1] | a.rot.s[2] | a.rot.s[3]) != 0u;
   if (a.format == UQ_KV_FP4 && k.G <= 8 && a.Hkv % 2 == 0) {
     // KV-head pairs fill the 16 MFMA columns
-    if (a.unrotate) e = bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP4, true, Fp4PairPol<D>>(a, k, s)
-                           : launch_one<D, UQ_IN_F32, UQ_KV_FP4, true, Fp4PairPol<D>>(a, k, s);
-    else e = bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP4, false, Fp4PairPol<D>>(a, k, s)
-                : launch_one<D, UQ_IN_F32, UQ_KV_FP4, false, Fp4PairPol<D>>(a, k, s);
+    e = rv ? fp4(PolTag<Fp4PairPol<D>>{}, std::true_type{}) : fp4(PolTag<Fp4PairPol<D>>{}, std::false_type{});
   } else if (a.format == UQ_KV_FP4) {
-    if (a.unrotate) e = bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP4, true, Fp4Pol<D>>(a, k, s)
-                           : launch_one<D, UQ_IN_F32, UQ_KV_FP4, true, Fp4Pol<D>>(a, k, s);
-    else e = bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP4, false, Fp4Pol<D>>(a, k, s)
-                : launch_one<D, UQ_IN_F32, UQ_KV_FP4, false, Fp4Pol<D>>(a, k, s);
+    e = rv ? fp4(PolTag<Fp4Pol<D>>{}, std::true_type{}) : fp4(PolTag<Fp4Pol<D>>{}, std::false_type{});
   } else if (a.format == UQ_KV_FP8) {
     e = bf ? launch_one<D, UQ_IN_BF16, UQ_KV_FP8, false, Fp8Pol<D>>(a, k, s)
            : launch_one<D, UQ_IN_F32, UQ_KV_FP8, false, Fp8Pol<D>>(a, k, s);
@@ -1600,6 +1630,8 @@ struct PfArgs {
   float* out;                 // [Tq][Hq][D]
   int32_t B, Hq, Hkv, G, QT;
   float scale_log2;
+  Rot rot;                    // the cache's rotation variant
+  int32_t unrot;              // rotate the output back (V rotated)
 };
 
 template <int D>
@@ -1721,7 +1753,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
     const bool valid = r < nrows;
     const int64_t qrow = (int64_t)(q0 + t0 + (valid ? r / a.G : 0)) * a.Hq + (int64_t)hk * a.G + (valid ? r % a.G : 0);
     qr.load(a.q, qrow, valid, p);
-    qr.finish(qs + r * D, p);
+    qr.template finish<true>(qs + r * D, p, a.rot);
   }
   __syncthreads();
 
@@ -1856,7 +1888,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
       const float l = stl[rloc];
       const bool live = row < nrows;
       const int64_t orow = live ? (int64_t)(q0 + t0 + row / a.G) * a.Hq + (int64_t)hk * a.G + row % a.G : 0;
-      store_row32<D, true>(o, l, a.out + orow * D, live, lane);
+      if (a.unrot) store_row32<D, true, true>(o, l, a.out + orow * D, live, lane, a.rot);
+      else store_row32<D, false, true>(o, l, a.out + orow * D, live, lane, a.rot);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_wave_barrier();                           // the stage is reused by the next block
@@ -1881,6 +1914,8 @@ hipError_t launch_prefill(const PrefillArgs& p, hipStream_t s) {
   a.G = p.Hq / p.Hkv;
   a.QT = kPfRows / a.G;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
+  a.rot = p.rot;
+  a.unrot = p.rot.k_only ? 0 : 1;
   // blocks: at most ceil(Tq / QT) + B (each sequence ends at most one partial block)
   const int64_t nblk = ((int64_t)p.Tq + a.QT - 1) / a.QT + p.B;
   if (nblk > INT32_MAX / 2) return hipErrorInvalidValue;

@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include "../../include/uq.h"
+#include "uq_internal.h"
 
 namespace uq {
 
@@ -28,6 +29,19 @@ constexpr int kGroup = 32;   // channels per scale group ([review] §3.1)
 // sqrt(1/d) as the nearest double (0x1.6a09e667f3bcdp-4 is sqrt(2)/16 rounded once).
 template <int D> __device__ __forceinline__ double wht_c() { return D == 64 ? 0.125 : 0x1.6a09e667f3bcdp-4; }
 template <int D> __device__ __forceinline__ float wht_cf() { return D == 64 ? 0.125f : 0x1.6a09e6p-4f; }
+
+// Sign bit (1u << 31, or 0) of channel ch in the rotation's sign diagonal.
+__device__ __forceinline__ uint32_t sign_mask(const Rot& r, int ch) {
+  const int w = ch >> 5;
+  const uint32_t word = w == 0 ? r.s[0] : w == 1 ? r.s[1] : w == 2 ? r.s[2] : r.s[3];
+  return ((word >> (ch & 31)) & 1u) << 31;
+}
+__device__ __forceinline__ bool has_signs(const Rot& r) { return (r.s[0] | r.s[1] | r.s[2] | r.s[3]) != 0u; }
+// x with its sign bit XORed by m (an exact negation when m is set).
+__device__ __forceinline__ double flip_sign(double x, uint32_t m) {
+  return __hiloint2double(__double2hiint(x) ^ (int)m, __double2loint(x));
+}
+__device__ __forceinline__ float flip_sign(float x, uint32_t m) { return __uint_as_float(__float_as_uint(x) ^ m); }
 
 template <int D> struct Fp4Block {
   static constexpr int kCodeBytes = kPage * D / 2;          // codes of 16 slots

@@ -47,7 +47,12 @@ template <int D, int IN, int LPR> struct Fp4Row {
 
   // Normalized WHT, group absmax, UE8M0 exponent (the absmax rule, or constOpt
   // when `constopt`) and E2M1 codes (all lanes of the row call it together).
-  __device__ __forceinline__ void quantize(int p, bool constopt) {
+  // RV: the cache's rotation variant applies -- R = c_d H diag(s) with its
+  // signs, and a V row of a K-only cache is quantized as it is; without RV the
+  // rotation is the plain c_d H.
+  template <bool RV = false>
+  __device__ __forceinline__ void quantize(int p, bool constopt, const Rot& rot, bool is_v) {
+    const bool rotate = !RV || !(is_v && rot.k_only != 0u);   // the same for all lanes of the row
     double x[E];
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
@@ -62,25 +67,33 @@ template <int D, int IN, int LPR> struct Fp4Row {
         }
       }
     }
+    if (rotate) {
+      if (RV && has_signs(rot)) {
 #pragma unroll
-    for (int hh = 1; hh < E; hh <<= 1)
+        for (int e = 0; e < E; ++e) x[e] = flip_sign(x[e], sign_mask(rot, E * p + e));
+      }
 #pragma unroll
-      for (int i = 0; i < E; i += 2 * hh)
+      for (int hh = 1; hh < E; hh <<= 1)
 #pragma unroll
-        for (int j = i; j < i + hh; ++j) {
-          const double a0 = x[j], a1 = x[j + hh];
-          x[j] = a0 + a1;
-          x[j + hh] = a0 - a1;
-        }
-    if constexpr (LPR > 1) cross_stage<E, 1>(x, p);
-    if constexpr (LPR > 2) cross_stage<E, 2>(x, p);
-    if constexpr (LPR > 4) cross_stage<E, 4>(x, p);
-    if constexpr (LPR > 8) cross_stage<E, 8>(x, p);
+        for (int i = 0; i < E; i += 2 * hh)
+#pragma unroll
+          for (int j = i; j < i + hh; ++j) {
+            const double a0 = x[j], a1 = x[j + hh];
+            x[j] = a0 + a1;
+            x[j + hh] = a0 - a1;
+          }
+      // the partner lanes of a cross stage belong to the same row
+      if constexpr (LPR > 1) cross_stage<E, 1>(x, p);
+      if constexpr (LPR > 2) cross_stage<E, 2>(x, p);
+      if constexpr (LPR > 4) cross_stage<E, 4>(x, p);
+      if constexpr (LPR > 8) cross_stage<E, 8>(x, p);
+    }
 
     // The normalized channel is RN(c_d x + 0) (one float64 rounding; the + 0
-    // makes an exact zero +0 whatever the butterfly's signed zeros).  Rounding is
-    // monotone, so the group absmax of those is RN(c_d max |x|).
-    const double c = wht_c<D>();
+    // makes an exact zero +0 whatever the butterfly's signed zeros; unrotated,
+    // c = 1 and x + 0 is x with a zero of either sign made +0).  Rounding is
+    // monotone, so the group absmax of those is RN(c max |x|).
+    const double c = rotate ? wht_c<D>() : 1.0;
     constexpr int EG = E / GPL;                           // channels of one group held by the lane
 #pragma unroll
     for (int g = 0; g < GPL; ++g) {

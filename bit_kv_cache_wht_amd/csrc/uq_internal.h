@@ -9,6 +9,14 @@
 
 namespace uq {
 
+// A cache's rotation variant as the FP4 kernels take it (by value): k_only = V
+// stored in its own basis; s = sign bits of R = c_d H_d diag(s), bit i % 32 of
+// s[i / 32] set for s_i = -1 (all zero for the plain transform).
+struct Rot {
+  uint32_t k_only;
+  uint32_t s[4];
+};
+
 struct AppendArgs {
   const void* k;              // [T][H][D] bf16 or f32
   const void* v;
@@ -18,6 +26,7 @@ struct AppendArgs {
   int64_t page_bytes;         // bytes of one page of one pool
   int32_t T, H;
   int32_t constopt;           // FP4: constOpt group scales (UQ_FLAG_SCALE_CONSTOPT)
+  Rot rot;                    // FP4: the cache's rotation variant
 };
 
 // Launchers return the hipError_t of the launch.
@@ -52,8 +61,9 @@ struct DecodeArgs {
   float* out;
   uint8_t* ws;
   DecodeLayout lay;
-  bool unrotate;
+  bool unrotate;             // FP4: rotate the output back (through R^T)
   bool constopt;             // fused FP4 step: constOpt scales for the written token
+  Rot rot;                   // FP4: the cache's rotation variant
   const void* k_new;         // fused FP4 step: newest token's K/V [B][Hkv][D] (q_dtype), or null
   const void* v_new;
   hipEvent_t ev_start, ev_stop;   // optional, recorded around the main kernel
@@ -74,6 +84,7 @@ struct PrefillArgs {
   float* out;                  // [Tq][Hq][D]
   int32_t B, Hq, Hkv, D, Tq;
   float sm_scale;
+  Rot rot;                     // the cache's rotation variant
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 int prefill_max_seqs();

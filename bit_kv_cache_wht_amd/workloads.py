@@ -192,3 +192,10 @@ def prefill_queries(wl: Workload, seed: int = 2001):
     rng = np.random.Generator(np.random.PCG64([seed, 7]))
     q32 = rng.standard_normal((int(cu[-1]), wl.num_q_heads, wl.head_dim), dtype=np.float32)
     return (_to_bf16_bits(q32) if wl.in_dtype == "bf16" else q32), cu
+
+
+def rotation_signs(head_dim: int, seed: int = 3001) -> np.ndarray:
+    """A sign vector for a randomized-sign Hadamard cache: head_dim values of +1.0
+    or -1.0, each -1 with probability 1/2, from their own seeded stream."""
+    rng = np.random.Generator(np.random.PCG64([seed, 11]))
+    return np.where(rng.integers(0, 2, size=head_dim) == 1, -1.0, 1.0)

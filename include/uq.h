@@ -6,6 +6,8 @@
  *                (manon006.tistory.com/395)
  *   [commentary] "kv-cache-4bit-serving-residency-collapse" (pheeree.github.io, 2026-09-01),
  *                whose footnotes quote the paper in English
+ *   [tq-guide]   "TurboQuant 완전 정리 - 이론 최적에 근접한 KV 캐시·벡터 검색 양자화와 vLLM 실측"
+ *                (juhoplayground.github.io)
  *
  * The write path ([review] §3.1) rotates each new key and value head vector with
  * a normalized Walsh-Hadamard transform, takes the absolute maximum of every
@@ -21,7 +23,8 @@
  * Conventions where the pages are silent:
  *   - the WHT is the Sylvester Hadamard matrix in natural order scaled by
  *     sqrt(1/head_dim), applied to K and to V; the attention output is rotated
- *     back, so `out` is in the original basis;
+ *     back, so `out` is in the original basis (K-only rotation and a random
+ *     sign diagonal are variants of a cache: UQ_ROT_*);
  *   - the scale exponent E is the least integer with absmax <= 6 * 2^E, clamped
  *     to [-127, 127] (never clips); rounding is to nearest, ties to even code;
  *     the sign bit is the sign of the value; every rounding decision is taken in
@@ -87,6 +90,27 @@ enum uq_in_dtype { UQ_IN_BF16 = 0, UQ_IN_F32 = 1 };
 #define UQ_FLAG_SCALE_CONSTOPT 2u
 
 /* Cache descriptor; read at call time, never retained. */
+/* Rotation variants of an FP4 cache (uq_kv_cache.rotation; 0 = K and V rotated
+ * by the normalized Walsh-Hadamard transform c_d H_d, the default).  Every call
+ * on one cache must use the same variant: it fixes how the stored bytes encode
+ * K and V.
+ *
+ * UQ_ROT_K_ONLY ([review] §3.1 table "Rotation": the rotation is applied to K;
+ * [commentary] footnote 1: "asymmetric K/V treatment"): V is quantized in its
+ * own basis (a zero channel stored as +0); K and the query are rotated as
+ * usual, and the attention output needs no rotating back (UQ_FLAG_OUT_ROTATED
+ * then changes nothing).
+ *
+ * UQ_ROT_SIGNS ([tq-guide] "알고리즘 원리", "랜덤 회전과 Beta 분포": a random sign
+ * diagonal times the Hadamard matrix): the rotation is R = c_d H_d diag(s),
+ * s_i = -1 where bit i % 32 of rotation_signs[i / 32] is set, else +1; K, V
+ * and the query go through R and the output back through R^T = diag(s) c_d H_d.
+ * The caller draws s, once per cache.  Bits at or above head_dim must be 0, and
+ * all four words must be 0 without this bit.  uq_rotate_quantize_query always
+ * applies the plain transform. */
+#define UQ_ROT_K_ONLY 1u
+#define UQ_ROT_SIGNS 2u
+
 typedef struct uq_kv_cache {
   int32_t format;        /* enum uq_kv_format                                   */
   int32_t num_pages;     /* pages in each pool                                  */
@@ -96,6 +120,8 @@ typedef struct uq_kv_cache {
   void* k_pool;          /* device, [num_pages][uq_page_bytes], 256-B aligned; head h's
                             block of a page starts at byte h * uq_head_block_bytes */
   void* v_pool;          /* device, same shape                                    */
+  uint32_t rotation;     /* UQ_ROT_* bits; FP4 only (0 for FP8 and BF16)           */
+  uint32_t rotation_signs[4];   /* with UQ_ROT_SIGNS: the sign bits of s          */
 } uq_kv_cache;
 
 /* Bytes of one head-block (one KV head of one page): FP4 17*d/2, FP8 16*d,

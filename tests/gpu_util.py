@@ -48,10 +48,11 @@ def decode_fn(fmt):
     return {"fp4": m.uq_decode_attention, "fp8": m.uq_decode_attention_fp8, "bf16": m.uq_decode_attention_bf16}[fmt]
 
 
-def gpu_cache(fmt, wl, pools=None):
-    """A zeroed GPU cache for the workload, or one holding the given numpy pools."""
+def gpu_cache(fmt, wl, pools=None, k_only=False, signs=None):
+    """A zeroed GPU cache for the workload, or one holding the given numpy pools;
+    ``k_only`` / ``signs`` select the FP4 rotation variant."""
     m = uq()
-    c = m.KvCache.allocate(FMT_ID[fmt], wl.num_pages, wl.num_kv_heads, wl.head_dim)
+    c = m.KvCache.allocate(FMT_ID[fmt], wl.num_pages, wl.num_kv_heads, wl.head_dim, k_only=k_only, signs=signs)
     if pools is not None:
         c.blocks(c.k_pool).copy_(dev(pools[0]))
         c.blocks(c.v_pool).copy_(dev(pools[1]))
@@ -70,12 +71,13 @@ def gpu_append(fmt, wl, cache=None, idx=None, slots=None, flags=0):
     return cache
 
 
-def oracle_append(fmt, wl, idx=None, slots=None, scale_mode="absmax"):
+def oracle_append(fmt, wl, idx=None, slots=None, scale_mode="absmax", k_only=False, signs=None):
     kp, vp = O.new_pool(FMT_ID[fmt], wl.num_pages, wl.num_kv_heads, wl.head_dim), \
         O.new_pool(FMT_ID[fmt], wl.num_pages, wl.num_kv_heads, wl.head_dim)
     idx = np.arange(wl.total_tokens) if idx is None else np.asarray(idx)
     sl = wl.slot_mapping[idx] if slots is None else np.asarray(slots, np.int32)
-    O.append(FMT_ID[fmt], kp, vp, wl.k[idx], wl.v[idx], sl, in_dtype=wl.in_dtype, scale_mode=scale_mode)
+    O.append(FMT_ID[fmt], kp, vp, wl.k[idx], wl.v[idx], sl, in_dtype=wl.in_dtype, scale_mode=scale_mode,
+             k_only=k_only, signs=signs)
     return kp, vp
 
 
@@ -115,13 +117,15 @@ def sm_scale(d):
     return float(np.float32(1.0 / np.sqrt(d)))
 
 
-def oracle_decode(fmt, wl, pools, rows=None, seq_lens=None):
+def oracle_decode(fmt, wl, pools, rows=None, seq_lens=None, k_only=False, signs=None):
     lens = wl.seq_lens if seq_lens is None else seq_lens
     if rows is None:
         return O.decode_attention(FMT_ID[fmt], pools[0], pools[1], wl.num_kv_heads, wl.head_dim, wl.q,
-                                  wl.page_table, lens, sm_scale(wl.head_dim), in_dtype=wl.in_dtype)
+                                  wl.page_table, lens, sm_scale(wl.head_dim), in_dtype=wl.in_dtype,
+                                  k_only=k_only, signs=signs)
     return O.decode_attention_rows(FMT_ID[fmt], pools[0], pools[1], wl.num_kv_heads, wl.head_dim, wl.q,
-                                   wl.page_table, lens, sm_scale(wl.head_dim), rows, in_dtype=wl.in_dtype)
+                                   wl.page_table, lens, sm_scale(wl.head_dim), rows, in_dtype=wl.in_dtype,
+                                   k_only=k_only, signs=signs)
 
 
 def oracle_decode_rows_from_inputs(fmt, wl, rows):

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import bit_kv_cache_wht_amd as uq
@@ -30,8 +31,58 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(B._SIGS)
 
 
-def cache(fmt=B.UQ_KV_FP4, pages=4, heads=2, d=128, page_size=16, k=FAKE, v=FAKE):
-    return B._Cache(fmt, pages, page_size, heads, d, k, v)
+def cache(fmt=B.UQ_KV_FP4, pages=4, heads=2, d=128, page_size=16, k=FAKE, v=FAKE, rot=0, signs=(0, 0, 0, 0)):
+    return B._Cache(fmt, pages, page_size, heads, d, k, v, rot, (ctypes.c_uint32 * 4)(*signs))
+
+
+def test_cache_struct_layout():
+    # uq_kv_cache: five int32, two pointers, the rotation word, four sign words
+    assert ctypes.sizeof(B._Cache) == 64
+    assert B._Cache.rotation.offset == 40 and B._Cache.rotation_signs.offset == 44
+
+
+def _rotation_cases(fmt, d):
+    """(cache, expected status of a call that would otherwise succeed)."""
+    out = [(cache(fmt, d=d, rot=4), B.UQ_ERR_INVALID_ARG),                         # unknown bit
+           (cache(fmt, d=d, signs=(1, 0, 0, 0)), B.UQ_ERR_INVALID_ARG)]            # signs without UQ_ROT_SIGNS
+    if fmt == B.UQ_KV_FP4:
+        out += [(cache(fmt, d=d, rot=B.UQ_ROT_K_ONLY), B.UQ_OK),
+                (cache(fmt, d=d, rot=B.UQ_ROT_SIGNS, signs=(0xFFFFFFFF, 1, 0, 0)), B.UQ_OK),
+                (cache(fmt, d=d, rot=3, signs=(0, 0x80000000, 0, 0)), B.UQ_OK),
+                (cache(fmt, d=d, rot=B.UQ_ROT_SIGNS, signs=(0, 0, 1 if d == 64 else 0, 1 if d == 64 else 0)),
+                 B.UQ_ERR_INVALID_ARG if d == 64 else B.UQ_OK)]                    # bits at or above head_dim
+    else:
+        out += [(cache(fmt, d=d, rot=B.UQ_ROT_K_ONLY), B.UQ_ERR_INVALID_ARG),       # FP4 caches only
+                (cache(fmt, d=d, rot=B.UQ_ROT_SIGNS, signs=(1, 0, 0, 0)), B.UQ_ERR_INVALID_ARG)]
+    return out
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("name,fmt", [("uq_quantize_append", 0), ("uq_append_fp8", 1), ("uq_append_bf16", 2)])
+def test_rotation_variant_validation(name, fmt, d):
+    f = getattr(uq.lib(), name)
+    for c, want in _rotation_cases(fmt, d):
+        # an empty append reaches the end of validation without a launch
+        assert f(ctypes.byref(c), None, None, 0, None, 0, 0, None) == want, (c.rotation, list(c.rotation_signs))
+    dec = {0: uq.lib().uq_decode_attention, 1: uq.lib().uq_decode_attention_fp8,
+           2: uq.lib().uq_decode_attention_bf16}[fmt]
+    for c, want in _rotation_cases(fmt, d):
+        assert dec(ctypes.byref(c), None, 0, None, 8, None, 0, 16, 0.1, None, None, 0, 0, None) == want
+    if fmt == 0:
+        pf = uq.lib().uq_prefill_attention
+        for c, want in _rotation_cases(fmt, d):
+            assert pf(ctypes.byref(c), None, 0, None, 0, None, 8, None, 3, 16, 0.1, None, 0, None) == want
+
+
+def test_sign_words_packing():
+    s = np.ones(128)
+    s[[0, 31, 32, 127]] = -1
+    assert uq.sign_words(s, 128) == (0x80000001, 1, 0, 0x80000000)
+    assert uq.sign_words(np.ones(64), 64) == (0, 0, 0, 0)
+    with pytest.raises(ValueError):
+        uq.sign_words(np.ones(64), 128)
+    with pytest.raises(ValueError):
+        uq.sign_words(np.zeros(64), 64)
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2])
