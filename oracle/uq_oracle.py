@@ -75,6 +75,7 @@ __all__ = [
     "fp8_k_offset", "fp8_v_offset", "bf16_k_index", "bf16_v_index",
     "append", "gather_dequant", "rotate_quantize_query", "attention",
     "decode_attention", "decode_attention_rows",
+    "pv_f16_hi_lo", "fold_p_fp8", "pv_fp8_scaled",
 ]
 
 PAGE_SIZE = 16          # tokens per page (vLLM-style paged cache; [review] §6.5.1)
@@ -476,6 +477,62 @@ def attention(qhat, k, v, sm_scale) -> np.ndarray:
     p = np.exp(s)
     p = p / p.sum(axis=1, keepdims=True)
     return p @ v
+
+
+# --------------------------------------------------------------------------
+# PV operand precision: the f16 hi + lo probabilities the kernels use, and the
+# fully scaled-MFMA alternative ([review] §3.2 and [commentary] footnote 2: FP4
+# value codes and UE8M0 scales fed to the scaled matrix instruction).  Models of
+# operand rounding only (products summed exactly), for measuring what each
+# choice costs against the float64 result.
+# --------------------------------------------------------------------------
+def _f16(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def pv_f16_hi_lo(p, v) -> np.ndarray:
+    """sum_t P[r, t] V[t, c] with P split into f16 hi = f16(p) and lo = f16(p - hi)
+    and V as f16 (exact for dequantized FP4 within the f16 range): p [R][T],
+    v [T][d] -> [R][d]."""
+    p = np.asarray(p, dtype=np.float64)
+    hi = _f16(p)
+    lo = _f16(p - hi)
+    v16 = _f16(v)
+    return hi @ v16 + lo @ v16
+
+
+def fold_p_fp8(p, exps, block=32) -> np.ndarray:
+    """The B operand of a scaled-MFMA PV for one 32-channel group: V's per-token
+    exponent E_t folded into the probabilities, normalized by the largest E of
+    each block of 32 tokens (that block's UE8M0 operand scale 2^M) and rounded
+    to E4M3.  p [R][T], exps [T] (V's group exponents) -> the rounded operand
+    times 2^M, [R][T] (so that sum_t result[r, t] * code[t] is the PV)."""
+    p = np.asarray(p, dtype=np.float64)
+    e = np.asarray(exps, dtype=np.int64)
+    T = e.size
+    out = np.zeros_like(p)
+    for b0 in range(0, T, block):
+        sl = slice(b0, min(b0 + block, T))
+        M = int(e[sl].max())
+        folded = np.ldexp(p[:, sl], (e[sl] - M)[None, :])
+        out[:, sl] = np.ldexp(e4m3_decode(e4m3_encode(folded)), M)
+    return out
+
+
+def pv_fp8_scaled(p, codes, scale_bytes) -> np.ndarray:
+    """sum_t P[r, t] V[t, c] computed as the scaled-MFMA PV would: FP4 codes as the
+    A operand (scale 1), and per 32-channel group g the probabilities folded with
+    V's exponents of that group (``fold_p_fp8``) as the FP8 B operand.
+    p [R][T], codes [T][d] (0..15), scale_bytes [T][d/32] -> [R][d]."""
+    codes = np.asarray(codes)
+    T, d = codes.shape
+    vals = e2m1_decode(codes)
+    e = np.asarray(scale_bytes, dtype=np.int64) - 127
+    out = np.zeros((np.asarray(p).shape[0], d))
+    for g in range(d // GROUP):
+        cs = slice(GROUP * g, GROUP * (g + 1))
+        out[:, cs] = fold_p_fp8(p, e[:, g]) @ vals[:, cs]
+    return out
 
 
 def decode_attention_rows(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table, seq_lens,

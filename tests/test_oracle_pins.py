@@ -643,3 +643,77 @@ def test_attention_weights_sum_to_one_and_gqa_mapping():
         K = O.gather_dequant(O.FMT_FP4, kp, wl.page_table[b], wl.seq_lens[b], h // G, d, False)
         V = O.gather_dequant(O.FMT_FP4, vp, wl.page_table[b], wl.seq_lens[b], h // G, d, True)
         np.testing.assert_allclose(out[b, h], O.wht(O.attention(qhat[None], K, V, 0.1)[0]), rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- PV operand precision
+def test_fold_p_fp8_exact_when_exponents_match_and_p_on_grid():
+    # Closed form: with one V exponent per 32-token block and p on the E4M3 grid,
+    # the folded FP8 operand is p itself and the scaled PV is the exact product.
+    rng = np.random.default_rng(60)
+    T, d = 96, 64
+    grid = np.array([1.0, 0.75, 0.5, 0.375, 0.25, 0.125, 0.0625, 0.015625])
+    p = rng.choice(grid, size=(3, T))
+    e_blk = rng.integers(-6, 6, size=(T // 32, d // 32))
+    sb = (np.repeat(e_blk, 32, axis=0) + 127).astype(np.uint8)          # [T][d/32]
+    codes = rng.integers(0, 16, size=(T, d)).astype(np.uint8)
+    for g in range(d // 32):
+        e = sb[:, g].astype(np.int64) - 127
+        assert np.array_equal(O.fold_p_fp8(p, e), np.ldexp(p, e[None, :]))        # p 2^E_t, unrounded
+    np.testing.assert_array_equal(O.pv_fp8_scaled(p, codes, sb), p @ O.dequantize_fp4(codes, sb))
+
+
+def test_fold_p_fp8_error_within_e4m3_half_ulp():
+    # E4M3 has 3 fraction bits: a folded value in the normal range [2^-6, 448]
+    # rounds within 2^-4 relative; below half the least subnormal (2^-10) to 0.
+    rng = np.random.default_rng(61)
+    p = rng.uniform(0.0, 1.0, size=(4, 128))
+    e = rng.integers(-20, 3, size=128)
+    out = O.fold_p_fp8(p, e)
+    M = np.repeat([e[i:i + 32].max() for i in range(0, 128, 32)], 32)
+    folded = np.ldexp(p, e - M)
+    normal = folded >= 2.0 ** -6
+    assert normal.any() and (~normal).any()
+    want = np.ldexp(p, e[None, :])                     # p 2^E_t
+    rel = np.abs(out - want) / want
+    assert np.all(rel[normal] <= 2.0 ** -4)
+    assert np.all(out[folded < 2.0 ** -10] == 0.0)
+
+
+def test_pv_f16_hi_lo_carries_22_bits():
+    rng = np.random.default_rng(62)
+    p = rng.uniform(2.0 ** -10, 1.0, size=(4, 200))
+    v = O.dequantize_fp4(rng.integers(0, 16, size=(200, 64)).astype(np.uint8),
+                         rng.integers(120, 133, size=(200, 2)).astype(np.uint8))
+    # hi + lo is p to 2^-22 relative, or to 2^-25 absolute where lo is an f16
+    # subnormal; V is exact in f16
+    bound = (2.0 ** -22 * p + 2.0 ** -25) @ np.abs(v)
+    err = np.abs(O.pv_f16_hi_lo(p, v) - p @ v)
+    assert np.all(err <= bound * (1 + 1e-9) + 1e-12)
+    hi_only = p.astype(np.float16).astype(np.float64) @ v
+    assert np.all(np.abs(hi_only - p @ v) <= 2.0 ** -11 * p @ np.abs(v) * (1 + 1e-9))
+
+
+def test_pv_precision_choice_on_decode_statistics():
+    # What the PV operand precision costs on decode statistics (8 query heads of
+    # one KV head, 8192 tokens, d = 128, K/V with outlier channels, rotated
+    # cache): f16 hi + lo P stays far inside the 1e-3 relative-L2 output
+    # tolerance; FP8 P with V's exponents folded in (the fully scaled-MFMA PV)
+    # does not.
+    wl = W.make_workload("pv_prec", 1, 8, 1, 128, [8192], [8192], seed=63)
+    k = O.bf16_bits_to_f64(wl.k[:, 0])
+    v = O.bf16_bits_to_f64(wl.v[:, 0])
+    kc, ksb = O.quantize_fp4(O.wht(k))
+    vc, vsb = O.quantize_fp4(O.wht(v))
+    K, V = O.dequantize_fp4(kc, ksb), O.dequantize_fp4(vc, vsb)
+    qhat = O.e4m3_decode(O.rotate_quantize_query(wl.q[0]))                # [8][128]
+    s = (qhat @ K.T) / math.sqrt(128)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    l = p.sum(axis=1, keepdims=True)
+    exact = O.wht(p @ V / l)
+    res = {}
+    for name, got in (("f16_hi_lo", O.pv_f16_hi_lo(p, V)), ("fp8_scaled", O.pv_fp8_scaled(p, vc, vsb))):
+        o = O.wht(got / l)
+        res[name] = (np.linalg.norm(o - exact) / np.linalg.norm(exact), np.abs(o - exact).max())
+    print("PV precision (rel-L2, max-abs):", res)
+    assert res["f16_hi_lo"][0] < 1e-5 and res["f16_hi_lo"][1] < 1e-4
+    assert res["fp8_scaled"][0] > 1e-3
