@@ -10,7 +10,8 @@ times (the library picks its launch configuration from the shapes alone).
 
 Sizes: append 65,536 tokens x 8 heads; decode 64 x 8,192 and 8 x 65,536 (64 / 8
 heads); ragged 128 sequences of 1,024..131,072 tokens (32 / 4 heads) with the
-longest and the shortest sequence always among the samples.
+longest and the shortest sequence always among the samples, decoded and (their
+last 256 tokens as the chunk) prefilled.
 """
 import numpy as np
 import pytest
@@ -19,7 +20,7 @@ import oracle as O
 from bit_kv_cache_wht_amd import workloads as W
 
 from gpu_util import FMT_ID, announce, assert_close, gpu_append, gpu_decode, oracle_decode_rows_from_inputs, \
-    page_blocks_np, torch_mod
+    page_blocks_np, sm_scale, torch_mod, uq
 
 pytestmark = pytest.mark.gpu
 
@@ -104,3 +105,41 @@ def test_ragged_128_fp4():
     _check_rows("fp4", wl, got, pairs)
     del cache
     _free()
+
+
+def test_prefill_ragged_128_fp4():
+    # The bench's prefill call: the last 256 tokens of each of the 128 ragged
+    # sequences attend causally to their cache.  Sampled chunk rows (first, middle
+    # and last token of the chunk; all query heads of one KV head) of the longest,
+    # the shortest and a median sequence against the oracle's decode of that row
+    # over its causal prefix, from a private cache of the pair's raw inputs.
+    torch = torch_mod()
+    wl = W.ragged()
+    q, cu = W.prefill_queries(wl)
+    lens = wl.seq_lens
+    announce(f"prefill fp4 {wl.name}: B={wl.batch} lens {int(lens.min())}..{int(lens.max())} Tq={q.shape[0]}")
+    cache = gpu_append("fp4", wl)
+    out = torch.full((q.shape[0], wl.num_q_heads, wl.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    qd = dv(q.view(np.int16)).view(torch.bfloat16)
+    uq().uq_prefill_attention(cache, qd, dv(cu), dv(wl.page_table), dv(wl.seq_lens), sm_scale(wl.head_dim), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    del cache, out, qd
+    _free()
+    assert np.isfinite(got).all()
+    G, d = wl.num_q_heads // wl.num_kv_heads, wl.head_dim
+    order = np.argsort(lens)
+    for b, hk in [(int(order[-1]), 3), (int(order[0]), 0), (int(order[len(order) // 2]), 2)]:
+        L, ql, t0 = int(lens[b]), int(cu[b + 1] - cu[b]), int(wl.tok_offsets[b])
+        npg = (L + 15) // 16
+        kp, vp = O.new_pool(O.FMT_FP4, npg, 1, d), O.new_pool(O.FMT_FP4, npg, 1, d)
+        O.append(O.FMT_FP4, kp, vp, wl.k[t0:t0 + L, hk:hk + 1], wl.v[t0:t0 + L, hk:hk + 1],
+                 np.arange(L, dtype=np.int32), in_dtype=wl.in_dtype)
+        for j in (0, ql // 2, ql - 1):
+            row = int(cu[b]) + j
+            qrows = q[row:row + 1, hk * G:(hk + 1) * G].reshape(1, G, d)
+            want = O.decode_attention_rows(O.FMT_FP4, kp, vp, 1, d, qrows, np.arange(npg)[None, :],
+                                           np.array([L - ql + j + 1]), sm_scale(d), [(0, g) for g in range(G)],
+                                           in_dtype=wl.in_dtype)
+            assert_close(got[row, hk * G:(hk + 1) * G], want, f"prefill ragged seq {b} (L={L}) token {j} kv {hk}")
