@@ -1797,7 +1797,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
       Pol::load_v(vn, a.v_pool, ids, a.page_bytes, head_off, r16, j4);
     }
     const int key0 = 4 * kPage * s + kPage * j4;                // first key of this lane's page
-    Pol::mask_v(vc, min(max(Ls - key0, 0), TOK));              // value slots past the sequence end
+    if (__any(Ls - key0 < TOK)) Pol::mask_v(vc, min(max(Ls - key0, 0), TOK));   // slots past the sequence end
     v8h VA[D / 32][2][2];
     pf_convert_v<D>(vc, VA);
 #pragma unroll
@@ -1806,10 +1806,17 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
       Pol::qk(kc, qo[c], S);
       const int nvalid = min(max(rpos[c] - key0 + 1, 0), TOK);  // causal: keys <= the row's position
       float t[TOK];
+      if (__all(nvalid == TOK)) {                                // steps wholly before the rows: no mask
 #pragma unroll
-      for (int m = 0; m < TOK / 4; ++m)
+        for (int m = 0; m < TOK / 4; ++m)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) t[4 * m + v] = 4 * m + v < nvalid ? S[m][v] : -INFINITY;
+          for (int v = 0; v < 4; ++v) t[4 * m + v] = S[m][v];
+      } else {
+#pragma unroll
+        for (int m = 0; m < TOK / 4; ++m)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) t[4 * m + v] = 4 * m + v < nvalid ? S[m][v] : -INFINITY;
+      }
       float neg_mc = -m_run[c] * a.scale_log2;
       float pf[TOK];
 #pragma unroll
