@@ -1800,6 +1800,19 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
     if (__any(Ls - key0 < TOK)) Pol::mask_v(vc, min(max(Ls - key0, 0), TOK));   // slots past the sequence end
     v8h VA[D / 32][2][2];
     pf_convert_v<D>(vc, VA);
+    // PV of block c (its probabilities as f16 hi + lo in Pprev) runs while block
+    // c + 1 takes its exponentials: the two are independent, and the scheduling
+    // barriers below alternate their MFMAs and VALU instructions
+    v8h Pprev[TOK / 8][2];
+    auto pv_block = [&](v4f (&Oc)[Pol::kTiles]) {
+#pragma unroll
+      for (int q = 0; q < D / 32; ++q)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          Oc[2 * q] = mma2(VA[q][half][0], Pprev[half], Oc[2 * q]);
+          Oc[2 * q + 1] = mma2(VA[q][half][1], Pprev[half], Oc[2 * q + 1]);
+        }
+    };
 #pragma unroll
     for (int c = 0; c < kPfNB; ++c) {
       v4f S[TOK / 4];
@@ -1824,6 +1837,14 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
       float psum = pf[0];
 #pragma unroll
       for (int i = 1; i < TOK; ++i) psum += pf[i];
+      if (c > 0) {
+        pv_block(O[c - 1]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU instructions
+        }
+      }
       if (__any(!(psum <= 256.f))) {
         float mx = t[0];
 #pragma unroll
@@ -1846,23 +1867,16 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
         for (int i = 1; i < TOK; ++i) psum += pf[i];
       }
       l_run[c] += psum;
-      v8h Pm[TOK / 8][2];
 #pragma unroll
       for (int half = 0; half < TOK / 8; ++half) {
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) split_f16x2(pf[8 * half + 2 * i], pf[8 * half + 2 * i + 1], hw[i], lw[i]);
-        Pm[half][0] = __builtin_bit_cast(v8h, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-        Pm[half][1] = __builtin_bit_cast(v8h, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        Pprev[half][0] = __builtin_bit_cast(v8h, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        Pprev[half][1] = __builtin_bit_cast(v8h, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
-#pragma unroll
-      for (int q = 0; q < D / 32; ++q)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          O[c][2 * q] = mma2(VA[q][half][0], Pm[half], O[c][2 * q]);
-          O[c][2 * q + 1] = mma2(VA[q][half][1], Pm[half], O[c][2 * q + 1]);
-        }
     }
+    pv_block(O[kPfNB - 1]);
   };
   for (int s = 0; s < steps; s += 2) {
     step(s, k0, v0, k1, v1);
