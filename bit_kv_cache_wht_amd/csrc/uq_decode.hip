@@ -1840,9 +1840,9 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
       if (c > 0) {
         pv_block(O[c - 1]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU instructions
+        for (int i = 0; i < 32; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU instructions
         }
       }
       if (__any(!(psum <= 256.f))) {
