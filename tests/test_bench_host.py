@@ -1,0 +1,67 @@
+"""Host logic of bench.py (no GPU): the one-GPU contract, the per-token byte
+count the roofline uses, and the HBM-traffic summary (counter arithmetic and the
+rule that a summary taken on other decode sources is not reported)."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_fp4_bytes_per_token_head():
+    # K and V, each 16 B of codes and 1 scale byte per 32 channels
+    assert bench.fp4_kv_bytes_per_token_head(128) == 2 * (64 + 4) == 136
+    assert bench.fp4_kv_bytes_per_token_head(64) == 68
+
+
+def _counter_csv(path, counter, decode_kib, copy_kib):
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for v in decode_kib:
+            w.writerow({"Kernel_Name": "void uq::decode_kernel<uq::Fp4PairPol<128>, 128, 0, 0, true, false>",
+                        "Counter_Name": counter, "Counter_Value": v})
+        for v in copy_kib:
+            w.writerow({"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": counter, "Counter_Value": v})
+        w.writerow({"Kernel_Name": "other", "Counter_Name": counter, "Counter_Value": 1e9})
+
+
+def test_traffic_summary_scales_by_the_copy(tmp_path, monkeypatch):
+    # a 1 GiB copy that reads as 2 GiB of fetch (factor 1/2) and 1 GiB of write
+    # (factor 1): decode 1000 KiB fetched -> 500 KiB, 10 KiB written -> 10 KiB
+    out = tmp_path / "traffic.md"
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(out))
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [1000.0, 1000.0], [2.0 * (1 << 20), 5.0])
+    _counter_csv(write, "WRITE_SIZE", [10.0, 10.0], [1.0 * (1 << 20)])
+    bench.summarize_pmc(str(fetch), str(write), "test workload")
+    text = out.read_text()
+    assert f"source_sha256: {bench.decode_source_sha()}" in text
+    assert "traffic_bytes_per_launch: 522240" in text                 # (500 + 10) KiB
+    assert bench.recorded_traffic() == 522240
+    # the same summary is not reported once the decode sources differ
+    monkeypatch.setattr(bench, "decode_source_sha", lambda: "0" * 16)
+    assert bench.recorded_traffic() is None
+
+
+def test_traffic_summary_needs_decode_and_copy_dispatches(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(tmp_path / "traffic.md"))
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [1000.0], [])
+    _counter_csv(write, "WRITE_SIZE", [10.0], [1.0 * (1 << 20)])
+    with pytest.raises(SystemExit):
+        bench.summarize_pmc(str(fetch), str(write), "test workload")
+    assert not (tmp_path / "traffic.md").exists()
