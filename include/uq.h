@@ -27,8 +27,18 @@
  *     sign diagonal are variants of a cache: UQ_ROT_*);
  *   - the scale exponent E is the least integer with absmax <= 6 * 2^E, clamped
  *     to [-127, 127] (never clips); rounding is to nearest, ties to even code;
- *     the sign bit is the sign of the value; every rounding decision is taken in
- *     float64 on the exact rotated value;
+ *     the sign bit is the sign of the value; every rounding decision (scale,
+ *     code, E4M3 query byte) is taken in float64 on the rotated value, which is
+ *     the exact Hadamard sum S times c_d (the double nearest sqrt(1/d)), rounded
+ *     once, plus +0;
+ *   - exact-sum domain: the rotation sums in float64 butterflies, which are exact
+ *     -- and the stored bytes therefore a function of the exact rotated values --
+ *     for every row (head_dim input values) that are all integer multiples of
+ *     2^u with sum |x_i| < 2^(u+53) for some integer u.  Every bf16 row whose
+ *     nonzero magnitudes span at most 38 binades (2^38) and every f32 row
+ *     spanning at most 22 is inside.  Outside it each rotated value can differ
+ *     from the exact one by at most (log2(d) + 2) * 2^-53 * c_d * sum |x_i|, and
+ *     the bytes are the rounding decisions of such a value;
  *   - FP8 is OCP E4M3 (bias 7, max 448), round to nearest even, saturating.
  *
  * Memory and ownership

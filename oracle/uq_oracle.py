@@ -23,9 +23,10 @@ What the method computes ([review] §3.1, §3.2; [commentary] footnote 2):
 Readings where the pages are silent (each listed with its reason in the design doc):
   R1  K and V are both rotated; the attention output is rotated back.
   R2  WHT = Sylvester Hadamard in natural order, scaled by c_d = sqrt(1/d),
-      over the whole head_dim, no random signs.  A rotated value whose exact
-      sum is zero is +0: the exact transform has no signed zeros, and the sign
-      float64 summation leaves on a zero depends on the order of the sums.
+      over the whole head_dim, no random signs.  Each rotated value is the
+      exact Hadamard sum times c_d (the double nearest sqrt(1/d)), rounded once
+      to float64.  A rotated value whose exact sum is zero is +0: the exact
+      transform has no signed zeros.
   R3  E = the least integer with m <= 6 * 2**E (never clips), clamped to
       [-127, 127]; an all-zero group gets E = -127.
   R4  E2M1 rounding is to nearest, ties to the even code; the sign bit is the
@@ -65,7 +66,7 @@ import numpy as np
 
 __all__ = [
     "PAGE_SIZE", "GROUP", "FMT_FP4", "FMT_FP8", "FMT_BF16",
-    "sylvester_hadamard", "wht_scale", "wht", "rotate", "unrotate",
+    "sylvester_hadamard", "wht_scale", "exact_sum_rows", "wht", "rotate", "unrotate",
     "scale_exponent", "CONSTOPT_C", "SQRT2_UP", "scale_exponent_constopt",
     "E2M1_LEVELS", "e2m1_encode", "e2m1_decode",
     "quantize_fp4", "dequantize_fp4", "pack_nibbles", "unpack_nibbles",
@@ -101,18 +102,64 @@ def wht_scale(d: int) -> float:
     return float(np.sqrt(1.0 / d))
 
 
-def wht(x) -> np.ndarray:
+def exact_sum_rows(x) -> np.ndarray:
+    """Per row of x (last axis): True when every partial sum of the values with
+    any signs is exactly representable in float64, so that a float64 sum of them
+    in any order and grouping is exact.
+
+    Criterion: all values are integer multiples of 2**u (u = the lowest set bit
+    of any of them) and sum |x_i| < 2**(u + 53); then every partial sum is such a
+    multiple below that bound.  For bf16 rows this holds when the nonzero
+    exponents span at most 38 binades, for float32 rows 22.  The float64 sum of
+    the |x_i| used for the test is itself exact below the bound and, rounding
+    being monotone, at or above it otherwise, so the test is exact.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    frac, ex = np.frexp(a)                                  # a = frac * 2**ex, frac in [0.5, 1)
+    mant = np.ldexp(frac, 53).astype(np.int64)              # 53-bit integer significand (0 for a = 0)
+    low = mant & -mant                                      # its lowest set bit
+    lowexp = np.where(a > 0, np.frexp(low.astype(np.float64))[1] - 1 + ex - 53, 1 << 20)
+    u = lowexp.min(axis=-1)                                 # 2**20: an all-zero row
+    bound = np.ldexp(1.0, np.minimum(u + 53, 1023))
+    return (a.sum(axis=-1) < bound) | (u == 1 << 20)
+
+
+def _wht_exact_row(row: np.ndarray, c: float) -> np.ndarray:
+    """RN(c * (H row)_k) + 0 for one row, the Hadamard sums in exact integer
+    arithmetic (every float64 is a dyadic rational) and rounded once."""
+    from fractions import Fraction
+    fr = [Fraction(float(t)) for t in row]
+    den = max(f.denominator for f in fr)                    # a power of two
+    n = np.array([int(f * den) for f in fr], dtype=object)
+    sums = sylvester_hadamard(row.size).astype(object) @ n  # exact Python integers
+    cf = Fraction(c)
+    return np.array([float(cf * int(s) / den) for s in sums], dtype=np.float64) + 0.0
+
+
+def wht(x, exact=True) -> np.ndarray:
     """Normalized Walsh-Hadamard transform over the last axis: x -> c_d * (H_d x).
 
-    The sum is taken first and multiplied by c_d once.  For bf16 input rows whose
-    nonzero exponents span at most 38 binades (fp32: 22) every partial sum is an
-    exact float64, so any summation order gives the same result; adding +0 after
-    the scaling turns a zero of either sign into +0 (reading R2).
+    exact=True (the write path and the query): each output is the exact sum
+    S = (H_d x)_k multiplied by c_d and rounded once to float64, plus +0 (an
+    exact zero is +0 whatever the signs of the inputs, reading R2).  Rows for
+    which ``exact_sum_rows`` holds take the float64 matrix product, whose sums
+    are then exact in any order; the other rows take exact integer arithmetic.
+
+    exact=False (outputs compared within a tolerance): the float64 matrix
+    product for every row, whose rounding errors are of order 2**-53 times the
+    row's L1 norm.
     """
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     h = sylvester_hadamard(d).astype(np.float64)
-    return (x @ h) * wht_scale(d) + 0.0      # H symmetric: (H x)^T = x^T H
+    c = wht_scale(d)
+    out = (x @ h) * c + 0.0                  # H symmetric: (H x)^T = x^T H
+    if exact:
+        flat_x, flat_o = x.reshape(-1, d), out.reshape(-1, d)
+        for r in np.nonzero(~exact_sum_rows(flat_x))[0]:
+            flat_o[r] = _wht_exact_row(flat_x[r], c)
+    return out
 
 
 def rotate(x, signs=None) -> np.ndarray:
@@ -130,7 +177,7 @@ def rotate(x, signs=None) -> np.ndarray:
 def unrotate(y, signs=None) -> np.ndarray:
     """R^T y = diag(s) c_d H_d y (the inverse of ``rotate``: c_d H_d is symmetric
     and orthogonal, diag(s) its own inverse)."""
-    o = wht(y)
+    o = wht(y, exact=False)
     return o if signs is None else o * np.asarray(signs, dtype=np.float64)
 
 

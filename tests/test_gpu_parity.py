@@ -58,20 +58,26 @@ def test_append_bit_exact(fmt, name):
         assert bad[0].size == 0, f"{kv} pool: {bad[0].size} bytes differ, first at {[int(x[0]) for x in bad]}"
 
 
-def _extreme_rows(d, rng):
+def _edge_rows(d, rng):
     """float32 K/V rows that reach every rounding regime of the FP4 write: group
     scales from 2^-127 to 2^127 (including the ends the float32 hardware
     rounding does not cover), float32 subnormal inputs, zero and negative-zero
     groups, and rows whose rotated values sit within float32 rounding of E2M1
     decision points (the inverse rotation of grid midpoints, rounded to
-    float32; for d = 64, c_d = 1/8 and some land exactly on them)."""
+    float32; for d = 64, c_d = 1/8 and some land exactly on them).
+
+    The scaled rows draw their magnitudes within 2^13 of each other, so they
+    lie inside the exact-sum domain stated in uq.h; the near-tie rows fall on
+    either side of it.  Returns (inside, outside), split by the oracle's
+    criterion."""
     from scipy.linalg import hadamard
     Hn = hadamard(d).astype(np.float64) / np.sqrt(d)
     rows = []
     for k in (-149, -140, -130, -125, -120, -110, -102, -101, -100, -99, -60, 0, 60, 99, 100, 101, 102, 110, 120, 125):
-        rows.append(rng.standard_normal(d) * 2.0 ** k)
+        mag = (1.0 + rng.random(d)) * 2.0 ** (k + rng.integers(-12, 1, d))
+        rows.append(mag * rng.choice([-1.0, 1.0], d))
     z = np.zeros(d); z[: d // 2] = -0.0; rows.append(z)
-    z = rng.standard_normal(d); z[32:64] = 0.0; rows.append(z)
+    z = rng.choice([-1.0, 1.0], d) * (1.0 + rng.random(d)); z[32:64] = 0.0; rows.append(z)
     mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
     for e in (-90, -30, -3, 0, 7, 40, 95):
         for _ in range(3):
@@ -79,35 +85,111 @@ def _extreme_rows(d, rng):
             y[::32] = 6.0 * 2.0 ** e                       # fixes each group's scale at e
             rows.append(Hn @ y)
     x = np.clip(np.array(rows, dtype=np.float64), -3.0e38, 3.0e38).astype(np.float32)
-    # keep each row inside the exact-sum domain of the rotation (nonzero float32
-    # exponents within 22 binades): entries below 2^-20 of the row's maximum are 0
-    big = np.abs(x).max(axis=1, keepdims=True)
-    x[np.abs(x) < big * np.float32(2.0 ** -20)] = 0.0
-    return x
+    inside = O.exact_sum_rows(x.astype(np.float64))
+    return x[inside], x[~inside]
+
+
+def _append_rows(d, xs, many, name):
+    """FP4-appends the rows (as K, and reversed and negated as V; `many` repeats
+    them past the small-batch threshold so that the large-batch kernel runs
+    too); returns the workload and the GPU pools."""
+    H = 2
+    xs = np.tile(xs, (1600 if many else 1, 1))
+    T = xs.shape[0] // H
+    wl = W.make_workload(name, 1, H, H, d, [T], [T], in_dtype="f32", seed=9)
+    wl.k = np.ascontiguousarray(xs[: T * H].reshape(T, H, d))
+    wl.v = np.ascontiguousarray(-xs[::-1][: T * H].reshape(T, H, d))
+    announce(f"append fp4 {name} d={d} T={T} H={H}")
+    return wl, pools_np(gpu_append("fp4", wl))
 
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("many", [False, True])
 def test_append_extreme_scales_and_near_ties(d, many):
-    # `many` repeats the rows past the small-batch threshold so that the large-
-    # batch kernel runs too
     rng = np.random.default_rng(d + (7 if many else 0))
-    base = _extreme_rows(d, rng)
-    reps = 1600 if many else 1
-    H = 2
-    xs = np.tile(base, (reps, 1))
-    T = xs.shape[0] // H
-    k = xs[: T * H].reshape(T, H, d)
-    v = -xs[::-1][: T * H].reshape(T, H, d)
-    wl = W.make_workload("extreme", 1, H, H, d, [T], [T], in_dtype="f32", seed=9)
-    wl.k = np.ascontiguousarray(k)
-    wl.v = np.ascontiguousarray(v)
-    announce(f"append fp4 extreme scales d={d} T={T} H={H}")
-    got = pools_np(gpu_append("fp4", wl))
+    inside, _ = _edge_rows(d, rng)
+    assert inside.shape[0] >= 30
+    wl, got = _append_rows(d, inside, many, "extreme")
     want = oracle_append("fp4", wl)
     for g, w, kv in zip(got, want, "KV"):
         bad = np.nonzero(g != w)
         assert bad[0].size == 0, f"{kv} pool: {bad[0].size} bytes differ, first at {[int(x[0]) for x in bad]}"
+
+
+def _stated_bound(x, d):
+    """uq.h's bound on how far a rotated value may be from the exact one outside
+    the exact-sum domain, per float32 row: (log2(d) + 2) 2^-53 c_d sum |x_i|."""
+    return (np.log2(d) + 2) * 2.0 ** -53 * O.wht_scale(d) * np.abs(x.astype(np.float64)).sum(-1)
+
+
+def check_fp4_within_stated_bound(wl, pools):
+    """Every group scale and every code of the workload's rows in the FP4 pools
+    are the rounding decisions of some values within the stated bound of the
+    exact rotated rows: the scale lies between the exponents of the group
+    absmax minus and plus the bound, and each dequantized value between the
+    roundings, at that scale, of the exact value minus and plus the bound."""
+    d, H = wl.head_dim, wl.num_kv_heads
+    T = wl.total_tokens
+    t = np.arange(T)
+    page = wl.page_table[0][t // 16]
+    for pool, src, is_v in ((pools[0], wl.k, False), (pools[1], wl.v, True)):
+        blk = pool.reshape(pool.shape[0], H, -1)
+        off = O.fp4_v_scale_offset if is_v else O.fp4_k_scale_offset
+        for h in range(H):
+            rows = src[:, h]
+            vals = O.gather_dequant(O.FMT_FP4, pool, wl.page_table[0], T, h, d, is_v)
+            E = blk[page[:, None], h, off((t % 16)[:, None], np.arange(d // 32)[None, :], d)].astype(np.int64) - 127
+            y = O.wht(rows.astype(np.float64))
+            delta = _stated_bound(rows, d)[:, None]
+            m = np.abs(y).reshape(T, d // 32, 32).max(2)
+            lo_e, hi_e = O.scale_exponent(np.maximum(m - delta, 0.0)), O.scale_exponent(m + delta)
+            assert np.all((E >= lo_e) & (E <= hi_e)), "a group scale outside the stated bound"
+            Ee = np.repeat(E, 32, axis=1)
+            q = lambda v: np.ldexp(O.e2m1_decode(O.e2m1_encode(np.ldexp(v, -Ee))), Ee)
+            assert np.all((vals >= q(y - delta)) & (vals <= q(y + delta))), "a code outside the stated bound"
+
+
+def outside_domain_rows(d, rng):
+    """The near-tie rows outside the exact-sum domain plus rows spanning up to
+    2^100 (one large channel beside full-precision float32 values, float32
+    subnormals beside normals); all outside the domain."""
+    _, outside = _edge_rows(d, rng)
+    extra = rng.standard_normal((40, d))
+    extra[:, 0] *= 2.0 ** rng.integers(30, 100, 40)
+    extra[10:20] *= 2.0 ** -100
+    extra[20:30, 1:] *= 2.0 ** -40
+    x = np.concatenate([outside, extra.astype(np.float32)])
+    return x[~O.exact_sum_rows(x.astype(np.float64))]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_append_outside_exact_sum_domain_within_stated_bound(d):
+    # uq.h: outside the exact-sum domain each rotated value is within
+    # (log2 d + 2) 2^-53 c_d sum|x| of the exact one, and the stored bytes are
+    # the rounding decisions of such a value.
+    x = outside_domain_rows(d, np.random.default_rng(300 + d))
+    assert x.shape[0] >= 40
+    wl, got = _append_rows(d, x, False, "outside_domain")
+    check_fp4_within_stated_bound(wl, got)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_query_rotation_outside_exact_sum_domain_within_stated_bound(d):
+    torch = torch_mod()
+    rng = np.random.default_rng(400 + d)
+    x = rng.standard_normal((64, d))
+    x[:, 0] *= 2.0 ** rng.integers(25, 60, 64)
+    x = x.astype(np.float32)
+    assert not O.exact_sum_rows(x.astype(np.float64)).any()
+    out = torch.empty((64, d), dtype=torch.uint8, device="cuda")
+    announce(f"query rotation outside the exact-sum domain d={d}")
+    uq().uq_rotate_quantize_query(dev(x, "f32"), out)
+    torch.cuda.synchronize()
+    got = O.e4m3_decode(out.cpu().numpy())
+    y = O.wht(x.astype(np.float64))
+    delta = _stated_bound(x, d)[:, None]
+    lo, hi = O.e4m3_decode(O.e4m3_encode(y - delta)), O.e4m3_decode(O.e4m3_encode(y + delta))
+    assert np.all((got >= lo) & (got <= hi))
 
 
 @pytest.mark.parametrize("fmt", FORMATS)

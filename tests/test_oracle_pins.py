@@ -89,6 +89,49 @@ def test_wht_float64_sums_are_exact_on_bf16_rows():
         assert np.array_equal(got[r], np.array([float(e) * c for e in exact]))
 
 
+def test_exact_sum_rows_boundary():
+    # The criterion at its edge, built from explicit values: multiples of 2^u
+    # whose magnitudes sum to 2^(u+53) - 2^u keep every partial sum exact; one
+    # more 2^u (a sum of 2^(u+53), where the spacing of doubles becomes 2^(u+1))
+    # does not.
+    for u in (-149, -30, 0, 40):
+        unit = 2.0 ** u
+        row = np.zeros(128)
+        row[0] = 2.0 ** (u + 52)
+        row[1] = 2.0 ** (u + 52) - 2 * unit
+        row[2] = unit
+        assert O.exact_sum_rows(row[None])[0]            # sum 2^(u+53) - 2^u
+        row[3] = unit
+        assert not O.exact_sum_rows(row[None])[0]        # sum 2^(u+53)
+    assert O.exact_sum_rows(np.zeros((1, 64)))[0]
+    # bf16 rows: exponent spans of 38 binades are inside, 39 and more may not be
+    r = np.zeros((2, 128))
+    r[:, :127] = 1.9921875                                # 0x3FFF: bf16 with all 8 significand bits
+    r[0, 127] = 1.9921875 * 2.0 ** -38
+    r[1, 127] = 1.9921875 * 2.0 ** -39
+    assert list(O.exact_sum_rows(r)) == [True, False]
+
+
+def test_wht_outside_the_exact_sum_domain_is_the_exact_sum_rounded_once():
+    # Rows with a span far beyond the domain: the oracle's value must be the
+    # exact Hadamard sum (here by the fast transform over Fractions) times c_d,
+    # rounded once, whatever the float64 matrix product gives.
+    rng = np.random.default_rng(77)
+    for d in (64, 128):
+        x = rng.standard_normal((6, d)).astype(np.float32).astype(np.float64)
+        x[:, 0] *= 2.0 ** 60
+        x[1, 1:] *= 2.0 ** -70
+        x[2, 1::3] = 0.0
+        x[3] *= 2.0 ** -100                                # float32 subnormals beside normals
+        assert not O.exact_sum_rows(x).any()
+        c = Fraction(O.wht_scale(d))
+        got = O.wht(x)
+        for r in range(x.shape[0]):
+            want = np.array([float(c * e) for e in _exact_hadamard_row(x[r])]) + 0.0
+            assert np.array_equal(got[r], want)
+        assert not np.array_equal(got, O.wht(x, exact=False))   # the float64 product rounds here
+
+
 def test_wht_exact_zero_outputs_are_positive_zero():
     # Reading R2: an output whose exact sum is zero carries no sign.  Rows of
     # signed zeros, and rows whose Hadamard sums cancel exactly, give +0 there.
@@ -623,6 +666,88 @@ def test_attention_special_cases(fmt):
     lens0 = wl.seq_lens.copy(); lens0[1] = 0
     oz = O.decode_attention(fmt, kp, vp, H, d, wl.q, wl.page_table, lens0, scale)
     assert not oz[1].any()
+
+
+def _baseline_pools(fmt, k, v, lens, H, d, in_dtype, seed):
+    rng = np.random.default_rng(seed)
+    npg = [(L + 15) // 16 for L in lens]
+    pages = rng.permutation(sum(npg))
+    table = np.zeros((len(lens), max(npg)), np.int64)
+    kp, vp = O.new_pool(fmt, sum(npg), H, d), O.new_pool(fmt, sum(npg), H, d)
+    off = 0
+    for b, L in enumerate(lens):
+        table[b, :npg[b]] = pages[off:off + npg[b]]
+        off += npg[b]
+        slots = table[b][np.arange(L) // 16] * 16 + np.arange(L) % 16
+        O.append(fmt, kp, vp, k[b, :L], v[b, :L], slots.astype(np.int32), in_dtype=in_dtype)
+    return kp, vp, table
+
+
+@pytest.mark.parametrize("fmt", [O.FMT_FP8, O.FMT_BF16])
+def test_baseline_decode_equals_plain_attention_on_grid_inputs(fmt):
+    # The FP8 / BF16 branch of the decode: q, K and V exactly on the format's
+    # grid (E4M3 values from torch's float8_e4m3fn, or bf16 values), so the
+    # oracle must equal plain attention on the given vectors, unrotated.
+    H, G, d, T = 2, 3, 64, 40
+    lens = [T, 23]
+    g = torch.Generator().manual_seed(31 + fmt)
+    if fmt == O.FMT_FP8:
+        def grid(*shape):
+            b = torch.randint(0, 256, shape, generator=g, dtype=torch.int32).to(torch.uint8)
+            b[(b & 0x7F) == 0x7F] = 0x3A                                  # no NaN codes
+            b &= 0xBF                                                       # exponent field < 8: |x| < 2
+            return b.view(torch.float8_e4m3fn).to(torch.float32).numpy()
+        k, v, q = grid(2, T, H, d), grid(2, T, H, d), grid(2, H * G, d)
+        args = dict(in_dtype="f32")
+        kx, vx, qx = k, v, q
+    else:
+        def grid(*shape):
+            t = torch.randn(*shape, generator=g).to(torch.bfloat16)
+            return t.view(torch.int16).numpy().view(np.uint16), t.to(torch.float64).numpy()
+        (k, kx), (v, vx), (q, qx) = grid(2, T, H, d), grid(2, T, H, d), grid(2, H * G, d)
+        args = dict(in_dtype="bf16")
+    kp, vp, table = _baseline_pools(fmt, k, v, lens, H, d, args["in_dtype"], seed=32)
+    scale = 1 / math.sqrt(d)
+    out = O.decode_attention(fmt, kp, vp, H, d, q, table, np.array(lens), scale, **args)
+    for b in range(2):
+        for h in range(H * G):
+            ref = _brute_attention(np.asarray(qx[b, h], np.float64), np.asarray(kx[b, :lens[b], h // G], np.float64),
+                                   np.asarray(vx[b, :lens[b], h // G], np.float64), scale)
+            np.testing.assert_allclose(out[b, h], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("fmt", [O.FMT_FP8, O.FMT_BF16])
+def test_baseline_decode_rounds_off_grid_inputs_like_torch(fmt):
+    # Off-grid inputs: the FP8 baseline rounds q, K and V to E4M3 (no rotation,
+    # no query scale), the BF16 baseline stores float32 K and V rounded to bf16
+    # and takes the bf16 query as it is; the expected values come from torch's
+    # float8_e4m3fn / bfloat16 casts and plain attention.
+    H, G, d, T = 2, 4, 128, 37
+    lens = [T, 9]
+    rng = np.random.default_rng(41 + fmt)
+    k = (rng.standard_normal((2, T, H, d)) * 3).astype(np.float32)
+    v = (rng.standard_normal((2, T, H, d)) * 3).astype(np.float32)
+    k[..., 5] *= 20                                           # outlier channel, still below 448
+    q32 = rng.standard_normal((2, H * G, d)).astype(np.float32)
+    kp, vp, table = _baseline_pools(fmt, k, v, lens, H, d, "f32", seed=42)
+    if fmt == O.FMT_FP8:
+        cast = lambda a: torch.from_numpy(a).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        q, args, qx = q32, dict(in_dtype="f32"), cast(q32)
+    else:
+        cast = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+        qt = torch.from_numpy(q32).to(torch.bfloat16)
+        q, args, qx = qt.view(torch.int16).numpy().view(np.uint16), dict(in_dtype="bf16"), qt.to(torch.float64).numpy()
+    kx, vx = cast(k), cast(v)
+    scale = 1 / math.sqrt(d)
+    out = O.decode_attention(fmt, kp, vp, H, d, q, table, np.array(lens), scale, **args)
+    for b in range(2):
+        for h in range(H * G):
+            ref = _brute_attention(qx[b, h], kx[b, :lens[b], h // G], vx[b, :lens[b], h // G], scale)
+            np.testing.assert_allclose(out[b, h], ref, rtol=0, atol=1e-11)
+    # a rotation anywhere in the branch would move the rows far from these values
+    rot = O.decode_attention(O.FMT_FP4, *_baseline_pools(O.FMT_FP4, k, v, lens, H, d, "f32", seed=42)[:2], H, d,
+                             q32, table, np.array(lens), scale, in_dtype="f32")
+    assert np.abs(rot - out).max() > 1e-3
 
 
 def test_attention_weights_sum_to_one_and_gqa_mapping():
