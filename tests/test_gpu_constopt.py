@@ -17,7 +17,7 @@ from bit_kv_cache_wht_amd import workloads as W
 from gpu_util import (announce, assert_close, dev, gpu_append, gpu_cache, oracle_append, oracle_decode, pools_np,
                       torch_mod, uq)
 from test_gpu_fused import _new_rows, _split
-from test_gpu_parity import SMALL, _extreme_rows, _wl
+from test_gpu_parity import SMALL, _edge_rows, _wl
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +56,7 @@ def _rows_wl(x, d, H=2):
 def test_constopt_append_extreme_scales(d, many):
     # `many` repeats the rows past the small-batch threshold (large-batch kernel)
     rng = np.random.default_rng(100 + d + (7 if many else 0))
-    x = np.tile(_extreme_rows(d, rng), (1600 if many else 1, 1))
+    x = np.tile(_edge_rows(d, rng)[0], (1600 if many else 1, 1))   # rows inside the exact-sum domain
     wl = _rows_wl(x, d)
     announce(f"append fp4 constOpt extreme scales d={d} T={wl.total_tokens}")
     _assert_pools_equal(pools_np(gpu_append("fp4", wl, flags=_flag())),
