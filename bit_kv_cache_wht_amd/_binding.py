@@ -158,10 +158,52 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bf16 or float32)")
 
 
+# Argument checks: every tensor the library reads or writes must have the shape
+# and dtype the C call assumes, since a mismatch there becomes an out-of-bounds
+# device access.  Shapes and dtypes are checked first and device placement last.
+def _need(cond: bool, msg: str, exc=ValueError) -> None:
+    if not cond:
+        raise exc(msg)
+
+
+def _shape(t, shape, name: str) -> None:
+    _need(tuple(t.shape) == tuple(shape), f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _int32(t, shape, name: str) -> None:
+    import torch
+    _need(t.dtype == torch.int32, f"{name}: dtype {t.dtype}, expected torch.int32", TypeError)
+    _shape(t, shape, name)
+
+
+def _float32(t, shape, name: str) -> None:
+    import torch
+    _need(t.dtype == torch.float32, f"{name}: dtype {t.dtype}, expected torch.float32", TypeError)
+    _shape(t, shape, name)
+
+
 def _contig(*ts):
     for t in ts:
         if t is not None and not t.is_contiguous():
             raise ValueError("tensors passed to libuq must be contiguous")
+
+
+def _on_device(**named) -> None:
+    for name, t in named.items():
+        if t is not None and not isinstance(t, int) and t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+
+
+def _cache_ok(cache) -> None:
+    """The pools of a cache hold num_pages pages of uq_page_bytes each."""
+    need = cache.num_pages * uq_page_bytes(cache)
+    _need(need > 0, "invalid cache descriptor")
+    pools = {name: getattr(cache, name) for name in ("k_pool", "v_pool")}
+    for name, t in pools.items():
+        if t is not None and not isinstance(t, int):
+            _need(t.numel() * t.element_size() >= need, f"{name}: {t.numel() * t.element_size()} bytes, "
+                  f"expected at least {need} (num_pages x uq_page_bytes)")
+    _on_device(**pools)
 
 
 def _check(fn: str, status: int) -> None:
@@ -188,9 +230,16 @@ def uq_page_bytes(cache: KvCache) -> int:
 
 def _append(name, cache, k_new, v_new, slot_mapping, flags, stream):
     _contig(k_new, v_new, slot_mapping)
-    c = cache.c()
     n = int(k_new.shape[0])
-    st = getattr(lib(), name)(ctypes.byref(c), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(slot_mapping), n,
+    code = _dtype_code(k_new)
+    _need(v_new.dtype == k_new.dtype, f"{name}: k_new is {k_new.dtype} but v_new is {v_new.dtype}", TypeError)
+    _shape(k_new, (n, cache.num_kv_heads, cache.head_dim), "k_new")
+    _shape(v_new, (n, cache.num_kv_heads, cache.head_dim), "v_new")
+    _int32(slot_mapping, (n,), "slot_mapping")
+    _cache_ok(cache)
+    _on_device(k_new=k_new, v_new=v_new, slot_mapping=slot_mapping)
+    c = cache.c()
+    st = getattr(lib(), name)(ctypes.byref(c), _ptr(k_new), _ptr(v_new), code, _ptr(slot_mapping), n,
                               flags, _stream(stream))
     _check(name, st)
 
@@ -210,9 +259,15 @@ def uq_append_bf16(cache: KvCache, k_new, v_new, slot_mapping, flags: int = 0, s
 
 def uq_rotate_quantize_query(q, q_fp8, stream=None) -> None:
     """q [rows][d] bf16/f32 -> q_fp8 uint8 [rows][d] (E4M3 of the rotated query)."""
+    import torch
     _contig(q, q_fp8)
+    code = _dtype_code(q)
+    _need(q.dim() == 2, f"q: {q.dim()} dimensions, expected [rows][head_dim]")
     rows, d = int(q.shape[0]), int(q.shape[-1])
-    st = lib().uq_rotate_quantize_query(_ptr(q), _dtype_code(q), _ptr(q_fp8), rows, d, _stream(stream))
+    _need(q_fp8.dtype == torch.uint8, f"q_fp8: dtype {q_fp8.dtype}, expected torch.uint8", TypeError)
+    _shape(q_fp8, (rows, d), "q_fp8")
+    _on_device(q=q, q_fp8=q_fp8)
+    st = lib().uq_rotate_quantize_query(_ptr(q), code, _ptr(q_fp8), rows, d, _stream(stream))
     _check("uq_rotate_quantize_query", st)
 
 
@@ -221,12 +276,32 @@ def uq_decode_workspace_bytes(cache: KvCache, num_seqs: int, num_q_heads: int, m
     return lib().uq_decode_workspace_bytes(ctypes.byref(c), num_seqs, num_q_heads, max_pages_per_seq)
 
 
-def _decode(name, cache, q, page_table, seq_lens, sm_scale, out, workspace, flags, stream):
-    _contig(q, page_table, seq_lens, out, workspace)
-    c = cache.c()
+def _decode_checks(name, cache, q, page_table, seq_lens, out, workspace, k_new=None, v_new=None):
+    """Shapes and dtypes of a decode call's tensors; returns (B, H_q)."""
+    _contig(q, page_table, seq_lens, out, workspace, k_new, v_new)
+    code = _dtype_code(q)
+    _need(q.dim() == 3 and int(q.shape[2]) == cache.head_dim,
+          f"{name}: q shape {tuple(q.shape)}, expected [num_seqs][num_q_heads][{cache.head_dim}]")
     B, Hq = int(q.shape[0]), int(q.shape[1])
+    _need(page_table.dim() == 2, f"page_table: {page_table.dim()} dimensions, expected [num_seqs][max_pages]")
+    _int32(page_table, (B, int(page_table.shape[1])), "page_table")
+    _int32(seq_lens, (B,), "seq_lens")
+    _float32(out, (B, Hq, cache.head_dim), "out")
+    for nm, t in (("k_new", k_new), ("v_new", v_new)):
+        if t is not None:
+            _need(t.dtype == q.dtype, f"{name}: {nm} is {t.dtype} but q is {q.dtype}", TypeError)
+            _shape(t, (B, cache.num_kv_heads, cache.head_dim), nm)
+    _cache_ok(cache)
+    _on_device(q=q, page_table=page_table, seq_lens=seq_lens, out=out, workspace=workspace, k_new=k_new,
+               v_new=v_new)
+    return code, B, Hq
+
+
+def _decode(name, cache, q, page_table, seq_lens, sm_scale, out, workspace, flags, stream):
+    code, B, Hq = _decode_checks(name, cache, q, page_table, seq_lens, out, workspace)
+    c = cache.c()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = getattr(lib(), name)(ctypes.byref(c), _ptr(q), _dtype_code(q), _ptr(page_table), int(page_table.shape[1]),
+    st = getattr(lib(), name)(ctypes.byref(c), _ptr(q), code, _ptr(page_table), int(page_table.shape[1]),
                               _ptr(seq_lens), B, Hq, float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, flags,
                               _stream(stream))
     _check(name, st)
@@ -242,13 +317,11 @@ def uq_append_decode_attention(cache, k_new, v_new, q, page_table, seq_lens, sm_
                                stream=None) -> None:
     """Fused FP4 step: writes k_new / v_new [B][H_kv][d] (the dtype of q) at position
     seq_lens[b] - 1 of each sequence, then decodes as uq_decode_attention."""
-    _contig(k_new, v_new, q, page_table, seq_lens, out, workspace)
-    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
-        raise TypeError("uq_append_decode_attention: k_new, v_new and q must share one dtype")
+    code, B, Hq = _decode_checks("uq_append_decode_attention", cache, q, page_table, seq_lens, out, workspace,
+                                 k_new, v_new)
     c = cache.c()
-    B, Hq = int(q.shape[0]), int(q.shape[1])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().uq_append_decode_attention(ctypes.byref(c), _ptr(k_new), _ptr(v_new), _ptr(q), _dtype_code(q),
+    st = lib().uq_append_decode_attention(ctypes.byref(c), _ptr(k_new), _ptr(v_new), _ptr(q), code,
                                           _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens), B, Hq,
                                           float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, flags,
                                           _stream(stream))
@@ -271,6 +344,9 @@ def uq_profile_next_decode(start_event, stop_event) -> None:
 def uq_stream_read(src, sink, stream=None) -> None:
     """Streaming read of the whole tensor `src` (bandwidth reference); XORs the XOR
     of its 32-bit words into the int32 tensor `sink` (one element)."""
+    _contig(src, sink)
+    _need(sink.numel() * sink.element_size() >= 4, "sink: at least one 32-bit word")
+    _on_device(src=src, sink=sink)
     nbytes = src.numel() * src.element_size()
     _check("uq_stream_read", lib().uq_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
 
@@ -279,9 +355,21 @@ def uq_prefill_attention(cache, q, cu_seqlens_q, page_table, seq_lens, sm_scale,
     """Chunked-prefill attention: q [T_q][H_q][d] (bf16/f32), cu_seqlens_q int32
     [B + 1], out float32 [T_q][H_q][d]; each sequence's chunk is its last tokens."""
     _contig(q, cu_seqlens_q, page_table, seq_lens, out)
+    code = _dtype_code(q)
+    _need(q.dim() == 3 and int(q.shape[2]) == cache.head_dim,
+          f"uq_prefill_attention: q shape {tuple(q.shape)}, expected [total_q][num_q_heads][{cache.head_dim}]")
+    Tq, Hq = int(q.shape[0]), int(q.shape[1])
+    _need(seq_lens.dim() == 1, "seq_lens: expected [num_seqs]")
+    B = int(seq_lens.shape[0])
+    _int32(seq_lens, (B,), "seq_lens")
+    _int32(cu_seqlens_q, (B + 1,), "cu_seqlens_q")
+    _need(page_table.dim() == 2, "page_table: expected [num_seqs][max_pages]")
+    _int32(page_table, (B, int(page_table.shape[1])), "page_table")
+    _float32(out, (Tq, Hq, cache.head_dim), "out")
+    _cache_ok(cache)
+    _on_device(q=q, cu_seqlens_q=cu_seqlens_q, page_table=page_table, seq_lens=seq_lens, out=out)
     c = cache.c()
-    st = lib().uq_prefill_attention(ctypes.byref(c), _ptr(q), _dtype_code(q), _ptr(cu_seqlens_q), int(q.shape[0]),
-                                    _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens),
-                                    int(seq_lens.shape[0]), int(q.shape[1]), float(sm_scale), _ptr(out), flags,
-                                    _stream(stream))
+    st = lib().uq_prefill_attention(ctypes.byref(c), _ptr(q), code, _ptr(cu_seqlens_q), Tq,
+                                    _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens), B, Hq,
+                                    float(sm_scale), _ptr(out), flags, _stream(stream))
     _check("uq_prefill_attention", st)

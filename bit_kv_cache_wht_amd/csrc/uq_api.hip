@@ -54,6 +54,8 @@ int append_common(const uq_kv_cache* cache, int format, const void* k_new, const
   if ((flags & ~allowed) != 0u) return UQ_ERR_INVALID_ARG;
   if (in_dtype != UQ_IN_BF16 && in_dtype != UQ_IN_F32) return UQ_ERR_INVALID_ARG;
   if (num_tokens < 0) return UQ_ERR_INVALID_ARG;
+  // the kernels index the 2 T H rows (K and V) in 32 bits
+  if ((int64_t)2 * num_tokens * cache->num_kv_heads > INT32_MAX) return UQ_ERR_UNSUPPORTED;
   if (num_tokens == 0) return UQ_OK;
   if (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr) return UQ_ERR_INVALID_ARG;
   uq::AppendArgs a;
@@ -84,8 +86,10 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   if (format == UQ_KV_BF16 && q_dtype != UQ_IN_BF16) return UQ_ERR_UNSUPPORTED;
   if (num_seqs < 0 || max_pages_per_seq < 1 || num_q_heads < 1) return UQ_ERR_INVALID_ARG;
   if (num_seqs > uq::kMaxDecodeSeqs) return UQ_ERR_UNSUPPORTED;
-  // the step list (4 pages per step, all sequences and KV heads) is indexed in 31 bits
-  if (max_pages_per_seq > (1 << 26) ||
+  // the step list (4 pages per step, all sequences and KV heads) is indexed in
+  // 31 bits, and a step's index inside its item in 20 bits (an item has at most
+  // ceil(max_pages_per_seq / 2) steps)
+  if (max_pages_per_seq > (1 << 21) ||
       (int64_t)num_seqs * ((max_pages_per_seq + 3) / 4) * cache->num_kv_heads > INT32_MAX)
     return UQ_ERR_UNSUPPORTED;
   if (num_q_heads % cache->num_kv_heads != 0) return UQ_ERR_UNSUPPORTED;

@@ -157,7 +157,9 @@ size_t uq_page_bytes(const uq_kv_cache* cache);
  *   slot_mapping  device int32 [num_tokens]
  *   flags         0 or UQ_FLAG_SCALE_CONSTOPT (else UQ_ERR_INVALID_ARG)
  * cache->format must be UQ_KV_FP4.  Two tokens mapped to the same slot in one
- * call race.  num_tokens == 0 is a no-op.
+ * call race.  num_tokens == 0 is a no-op; 2 * num_tokens * num_kv_heads above
+ * 2^31 - 1 is UQ_ERR_UNSUPPORTED (the same limit holds for uq_append_fp8 and
+ * uq_append_bf16).
  */
 int uq_quantize_append(const uq_kv_cache* cache, const void* k_new, const void* v_new,
                        int32_t in_dtype, const int32_t* slot_mapping, int32_t num_tokens,
@@ -210,7 +212,7 @@ size_t uq_decode_workspace_bytes(const uq_kv_cache* cache, int32_t num_seqs, int
  *               the next one (no clearing needed).  Calls that overlap in time
  *               must not share a workspace.
  * num_q_heads must be a multiple of num_kv_heads with a ratio of 1..16,
- * num_seqs at most 8192, max_pages_per_seq at most 2^26 and
+ * num_seqs at most 8192, max_pages_per_seq at most 2^21 and
  * num_seqs * ceil(max_pages_per_seq / 4) * num_kv_heads below 2^31 (else
  * UQ_ERR_UNSUPPORTED), and sm_scale positive and finite.
  * Accuracy: codes and scales enter exactly; logits and the softmax are float32,

@@ -135,6 +135,9 @@ def test_append_validation(name, fmt):
     else:
         assert call(fl=B.UQ_FLAG_SCALE_CONSTOPT, n=0, k=None, v=None, s=None) == B.UQ_ERR_INVALID_ARG
     assert call(n=0, k=None, v=None, s=None) == B.UQ_OK            # empty append is a no-op
+    # 2 T H rows are indexed in 32 bits
+    assert call(c=cache(fmt, heads=1), n=1 << 30) == B.UQ_ERR_UNSUPPORTED
+    assert call(c=cache(fmt, heads=4), n=(1 << 28) + 1) == B.UQ_ERR_UNSUPPORTED
 
 
 def test_query_validation():
@@ -187,6 +190,10 @@ def test_decode_validation(name, fmt):
     if fmt == B.UQ_KV_BF16:
         assert call(qd=B.UQ_IN_F32) == B.UQ_ERR_UNSUPPORTED
     assert call(B_=0, q=None, pt=None, sl=None, out=None, w=None) == B.UQ_OK
+    # a step's index inside its item is kept in 20 bits: at most 2^21 pages per sequence
+    assert call(B_=1, mp=(1 << 21) + 1) == B.UQ_ERR_UNSUPPORTED
+    wbig = uq.lib().uq_decode_workspace_bytes(ctypes.byref(ok), 1, 16, 1 << 21)
+    assert call(B_=1, mp=1 << 21, w=None, wb=wbig) == B.UQ_ERR_WORKSPACE      # the limit itself passes
 
 
 def test_fused_step_validation():
