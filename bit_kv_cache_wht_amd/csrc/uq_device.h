@@ -143,7 +143,7 @@ __device__ __forceinline__ int constopt_exponent(double m) {
   const uint64_t b = (uint64_t)__double_as_longlong(s);
   const int e = (int)(b >> 52) - 1023;               // s is normal and positive here
   const int E = e + ((b & 0xFFFFFFFFFFFFFull) >= 0x6A09E667F3BCDull ? 1 : 0);
-  return E > 127 ? 127 : E;
+  return E > 127 ? 127 : (E < -127 ? -127 : E);      // s in [2^-128, 2^-127.5) gives -128
 }
 
 // FP4 E2M1 code of r = x / 2^E: magnitude rounded to nearest of

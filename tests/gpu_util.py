@@ -81,6 +81,57 @@ def oracle_append(fmt, wl, idx=None, slots=None, scale_mode="absmax", k_only=Fal
     return kp, vp
 
 
+def oracle_threads() -> int:
+    """Host threads for the oracle: the cores this process may run on, at most 16
+    (a one-GPU share of a GPU host)."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _threaded(fn, items):
+    """fn over items on oracle_threads() threads with BLAS held to one thread
+    each (numpy releases the interpreter lock inside its array loops)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import threadpoolctl
+    with threadpoolctl.threadpool_limits(1):
+        with ThreadPoolExecutor(oracle_threads()) as ex:
+            return list(ex.map(fn, items))
+
+
+def oracle_append_all(fmt, wl, chunk=4096):
+    """The oracle's pools holding every token of the workload, from its raw
+    inputs.  Chunks of tokens are appended by separate threads into the same
+    pools: every byte of a pool belongs to one (slot, head), so the chunks
+    write disjoint bytes."""
+    kp, vp = O.new_pool(FMT_ID[fmt], wl.num_pages, wl.num_kv_heads, wl.head_dim), \
+        O.new_pool(FMT_ID[fmt], wl.num_pages, wl.num_kv_heads, wl.head_dim)
+
+    def one(t0):
+        sl = slice(t0, min(t0 + chunk, wl.total_tokens))
+        O.append(FMT_ID[fmt], kp, vp, wl.k[sl], wl.v[sl], wl.slot_mapping[sl], in_dtype=wl.in_dtype)
+
+    _threaded(one, range(0, wl.total_tokens, chunk))
+    return kp, vp
+
+
+def oracle_decode_all(fmt, wl, pools):
+    """Every output row [B][H_q][d] of the oracle's decode over its pools, the
+    (sequence, KV head) pairs on separate threads."""
+    B, Hq, d = wl.batch, wl.num_q_heads, wl.head_dim
+    G = Hq // wl.num_kv_heads
+    out = np.zeros((B, Hq, d))
+
+    def one(pair):
+        b, hk = divmod(pair, wl.num_kv_heads)
+        rows = [(b, hk * G + g) for g in range(G)]
+        out[b, hk * G:(hk + 1) * G] = O.decode_attention_rows(
+            FMT_ID[fmt], pools[0], pools[1], wl.num_kv_heads, d, wl.q, wl.page_table, wl.seq_lens, sm_scale(d),
+            rows, in_dtype=wl.in_dtype)
+
+    _threaded(one, range(B * wl.num_kv_heads))
+    return out
+
+
 def page_blocks_np(cache, pool, idx=None):
     """Pages `idx` (default all) of a device pool as numpy [n][H][block], after
     checking that the bytes past the head blocks of each page (the FP4 page
