@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     uq_decode_attention,
     uq_decode_attention_bf16,
     uq_decode_attention_fp8,
+    uq_decode_attention_noalloc,
     uq_decode_workspace_bytes,
     uq_head_block_bytes,
     uq_last_hip_error,

@@ -48,6 +48,7 @@ _SIGS = {
     "uq_rotate_quantize_query": (ctypes.c_int, [_P, _I, _P, _I, _I, _P]),
     "uq_decode_workspace_bytes": (_SZ, [_CP, _I, _I, _I]),
     "uq_decode_attention": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
+    "uq_decode_attention_noalloc": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _U, _P]),
     "uq_append_decode_attention": (ctypes.c_int, [_CP, _P, _P, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ,
                                                   _U, _P]),
     "uq_decode_attention_fp8": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
@@ -311,6 +312,17 @@ def uq_decode_attention(cache, q, page_table, seq_lens, sm_scale, out, workspace
     """FP4 decode: q [B][H_q][d], page_table int32 [B][max_pages], seq_lens int32 [B],
     out float32 [B][H_q][d], workspace uint8 >= uq_decode_workspace_bytes."""
     _decode("uq_decode_attention", cache, q, page_table, seq_lens, sm_scale, out, workspace, flags, stream)
+
+
+def uq_decode_attention_noalloc(cache, q, page_table, seq_lens, sm_scale, out, flags=0, stream=None) -> None:
+    """FP4 decode as uq_decode_attention, with the library's static scratch array as
+    its workspace (allocates nothing; calls overlapping in time on one GPU race)."""
+    code, B, Hq = _decode_checks("uq_decode_attention_noalloc", cache, q, page_table, seq_lens, out, None)
+    c = cache.c()
+    st = lib().uq_decode_attention_noalloc(ctypes.byref(c), _ptr(q), code, _ptr(page_table),
+                                           int(page_table.shape[1]), _ptr(seq_lens), B, Hq, float(sm_scale),
+                                           _ptr(out), flags, _stream(stream))
+    _check("uq_decode_attention_noalloc", st)
 
 
 def uq_append_decode_attention(cache, k_new, v_new, q, page_table, seq_lens, sm_scale, out, workspace, flags=0,

@@ -2,6 +2,8 @@
 // HIP call) and kernel launches.  Declarations and semantics: include/uq.h.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "uq_internal.h"
 
 namespace {
@@ -43,6 +45,63 @@ uq::Rot rot_of(const uq_kv_cache* c) {
   return r;
 }
 
+// ---- scratch of the no-allocation decode (uq_decode_attention_noalloc)
+// Its workspace is this static device array, one per GPU the library runs on.
+// The layout is fixed whatever the call's shape: the arrival counters (zero
+// when a call starts; every complete call leaves them zero) always occupy the
+// first kNoallocCounterBytes, so a later call with another shape never finds a
+// partial of an earlier call where it expects a counter.
+constexpr int kNoallocMaxItems = 65536;                        // num_seqs * num_kv_heads, at most
+constexpr size_t kNoallocCounterBytes = 4 * (size_t)kNoallocMaxItems;
+constexpr size_t kNoallocScratchBytes = 17301504;              // counters + partials for head_dim 128
+
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+uq::DecodeLayout noalloc_layout(int head_dim) {
+  const uq::DecodeLayout shaped = uq::decode_layout(UQ_KV_FP4, 1, 1, 1, head_dim);
+  uq::DecodeLayout L;
+  L.cnt = 0;
+  L.ml = kNoallocCounterBytes;                                  // a multiple of 256
+  L.po = L.ml + (shaped.po - shaped.ml);
+  L.total = L.po + (shaped.total - shaped.po);
+  return L;
+}
+
+__global__ void zero_words(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// The device address of `scratch` on the current device, taken once per device
+// with hipGetSymbolAddress (on the host the array's name is only a stand-in for
+// the symbol and must never be passed to a kernel).  The first call on a device
+// also clears the counter region, with a fill kernel on the call's stream ahead
+// of the call's own kernel.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return UQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (ptr == nullptr) return UQ_ERR_HIP;
+    const int n = (int)(kNoallocCounterBytes / 4);
+    hipLaunchKernelGGL(zero_words, dim3((n + 255) / 256), dim3(256), 0, stream, static_cast<uint32_t*>(ptr), n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return UQ_OK;
+}
+
 typedef hipError_t (*append_launcher)(const uq::AppendArgs&, int, int, hipStream_t);
 
 int append_common(const uq_kv_cache* cache, int format, const void* k_new, const void* v_new, int32_t in_dtype,
@@ -72,10 +131,13 @@ int append_common(const uq_kv_cache* cache, int format, const void* k_new, const
   return hip_status(launch(a, cache->head_dim, in_dtype, reinterpret_cast<hipStream_t>(stream)));
 }
 
+// Decode entry points.  `noalloc`: the workspace is the library's static
+// scratch array (fixed layout), set up after every argument check has passed.
 int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q_dtype, const int32_t* page_table,
                   int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
                   float sm_scale, float* out, void* workspace, size_t workspace_bytes, uint32_t flags,
-                  uq_stream_t stream, const void* k_new = nullptr, const void* v_new = nullptr) {
+                  uq_stream_t stream, const void* k_new = nullptr, const void* v_new = nullptr,
+                  bool noalloc = false) {
   int st = check_cache(cache, format);
   if (st != UQ_OK) return st;
   // the constOpt bit selects the scale rule of the fused step's write
@@ -98,8 +160,18 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   if (num_seqs == 0) return UQ_OK;
   if (q == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr) return UQ_ERR_INVALID_ARG;
   if ((k_new == nullptr) != (v_new == nullptr)) return UQ_ERR_INVALID_ARG;
-  const size_t need = uq_decode_workspace_bytes(cache, num_seqs, num_q_heads, max_pages_per_seq);
-  if (workspace == nullptr || workspace_bytes < need) return UQ_ERR_WORKSPACE;
+  uq::DecodeLayout lay;
+  if (noalloc) {
+    if ((int64_t)num_seqs * cache->num_kv_heads > kNoallocMaxItems) return UQ_ERR_WORKSPACE;
+    lay = noalloc_layout(cache->head_dim);
+    if (lay.total > kNoallocScratchBytes) return UQ_ERR_WORKSPACE;
+    const int sst = noalloc_scratch(reinterpret_cast<hipStream_t>(stream), &workspace);
+    if (sst != UQ_OK) return sst;
+  } else {
+    const size_t need = uq_decode_workspace_bytes(cache, num_seqs, num_q_heads, max_pages_per_seq);
+    if (workspace == nullptr || workspace_bytes < need) return UQ_ERR_WORKSPACE;
+    lay = uq::decode_layout(format, num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim);
+  }
   uq::DecodeArgs a;
   a.format = format;
   a.q = q;
@@ -117,7 +189,7 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   a.sm_scale = sm_scale;
   a.out = out;
   a.ws = static_cast<uint8_t*>(workspace);
-  a.lay = uq::decode_layout(format, num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim);
+  a.lay = lay;
   a.rot = rot_of(cache);
   a.unrotate = format == UQ_KV_FP4 && !(flags & UQ_FLAG_OUT_ROTATED) && a.rot.k_only == 0u;
   a.constopt = (flags & UQ_FLAG_SCALE_CONSTOPT) != 0u;
@@ -204,6 +276,13 @@ int uq_decode_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtype
                         uq_stream_t stream) {
   return decode_common(cache, UQ_KV_FP4, q, q_dtype, page_table, max_pages_per_seq, seq_lens, num_seqs, num_q_heads,
                        sm_scale, out, workspace, workspace_bytes, flags, stream);
+}
+
+int uq_decode_attention_noalloc(const uq_kv_cache* cache, const void* q, int32_t q_dtype, const int32_t* page_table,
+                                int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                                int32_t num_q_heads, float sm_scale, float* out, uint32_t flags, uq_stream_t stream) {
+  return decode_common(cache, UQ_KV_FP4, q, q_dtype, page_table, max_pages_per_seq, seq_lens, num_seqs, num_q_heads,
+                       sm_scale, out, nullptr, 0, flags, stream, nullptr, nullptr, true);
 }
 
 int uq_append_decode_attention(const uq_kv_cache* cache, const void* k_new, const void* v_new, const void* q,

@@ -226,6 +226,24 @@ int uq_decode_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtype
                         uint32_t flags, uq_stream_t stream);
 
 /*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the FP4 decode
+ * of uq_decode_attention without a workspace argument.  Its split partials and
+ * arrival counters live in a static device array of the library, 17,301,504
+ * bytes per GPU it runs on, held until the process ends; the call itself
+ * allocates nothing.  The first call on a device finds the array's address
+ * (hipGetSymbolAddress) and clears its counters with a fill kernel on `stream`.
+ * Arguments and results as uq_decode_attention; in addition num_seqs *
+ * num_kv_heads above 65,536 is UQ_ERR_WORKSPACE.  Every call on one GPU shares
+ * the array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must not be issued; calls in stream order are safe.
+ */
+int uq_decode_attention_noalloc(const uq_kv_cache* cache, const void* q, int32_t q_dtype,
+                                const int32_t* page_table, int32_t max_pages_per_seq,
+                                const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                float sm_scale, float* out, uint32_t flags, uq_stream_t stream);
+
+/*
  * One FP4 decode step in a single launch ([review] §3.1 write path followed by
  * the §3.2 decode): for every sequence b with L = seq_lens[b] > 0, writes the
  * step's newest token -- k_new[b][h] and v_new[b][h] for every KV head h -- at

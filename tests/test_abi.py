@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     h = uq.lib()
     for n in names:
         assert hasattr(h, n), n
@@ -218,6 +218,27 @@ def test_fused_step_validation():
     assert call(fl=B.UQ_FLAG_OUT_ROTATED, w=None) == B.UQ_ERR_WORKSPACE
     assert call(fl=B.UQ_FLAG_SCALE_CONSTOPT | B.UQ_FLAG_OUT_ROTATED, w=None) == B.UQ_ERR_WORKSPACE
     assert call(B_=0, k=None, v=None, q=None, pt=None, sl=None, out=None, w=None) == B.UQ_OK
+
+
+def test_noalloc_decode_validation():
+    # every argument check runs before the static scratch array is set up, so
+    # none of these reaches the device
+    f = uq.lib().uq_decode_attention_noalloc
+    ok = cache(B.UQ_KV_FP4, heads=2)
+
+    def call(c=ok, q=FAKE, qd=0, pt=FAKE, mp=8, sl=FAKE, B_=3, Hq=16, scale=0.1, out=FAKE, fl=0):
+        return f(ctypes.byref(c) if c is not None else None, q, qd, pt, mp, sl, B_, Hq, scale, out, fl, None)
+
+    assert call(c=None) == B.UQ_ERR_INVALID_ARG
+    assert call(c=cache(B.UQ_KV_FP8, heads=2)) == B.UQ_ERR_INVALID_ARG       # FP4 caches only
+    assert call(Hq=15) == B.UQ_ERR_UNSUPPORTED
+    assert call(q=None) == B.UQ_ERR_INVALID_ARG
+    assert call(scale=0.0) == B.UQ_ERR_INVALID_ARG
+    assert call(fl=2) == B.UQ_ERR_INVALID_ARG
+    assert call(mp=(1 << 21) + 1, B_=1) == B.UQ_ERR_UNSUPPORTED
+    # more (sequence, KV head) items than the static array's 65,536 counters
+    assert call(c=cache(B.UQ_KV_FP4, heads=9), B_=8000, Hq=9) == B.UQ_ERR_WORKSPACE
+    assert call(B_=0, q=None, pt=None, sl=None, out=None) == B.UQ_OK
 
 
 def test_workspace_bytes_grow_with_shape():
