@@ -80,8 +80,9 @@ def lib() -> ctypes.CDLL:
 @dataclass
 class KvCache:
     """Descriptor of a paged K/V cache; pools are caller-owned uint8 device tensors
-    of shape [num_pages][uq_page_bytes]; head h's block of a page starts at byte
-    h * head block bytes (``blocks`` views them as [num_pages][num_kv_heads][block])."""
+    of shape [num_pages][uq_page_bytes], a page being its head blocks back to back
+    (``blocks`` views them as [num_pages][block position][block]; FP4 pages hold
+    KV head h at position (h + 2 page) mod num_kv_heads, see include/uq.h)."""
     format: int
     num_pages: int
     num_kv_heads: int

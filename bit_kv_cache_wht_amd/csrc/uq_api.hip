@@ -126,6 +126,7 @@ int append_common(const uq_kv_cache* cache, int format, const void* k_new, const
   a.page_bytes = (int64_t)uq_page_bytes(cache);
   a.T = num_tokens;
   a.H = cache->num_kv_heads;
+  a.hmask = uq::pow2_mask(cache->num_kv_heads);
   a.constopt = (flags & UQ_FLAG_SCALE_CONSTOPT) ? 1 : 0;
   a.rot = rot_of(cache);
   return hip_status(launch(a, cache->head_dim, in_dtype, reinterpret_cast<hipStream_t>(stream)));
@@ -186,6 +187,7 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   a.Hq = num_q_heads;
   a.Hkv = cache->num_kv_heads;
   a.D = cache->head_dim;
+  a.hmask = uq::pow2_mask(cache->num_kv_heads);
   a.sm_scale = sm_scale;
   a.out = out;
   a.ws = static_cast<uint8_t*>(workspace);
@@ -217,21 +219,7 @@ size_t uq_head_block_bytes(int32_t format, int32_t head_dim) {
 
 size_t uq_page_bytes(const uq_kv_cache* c) {
   if (c == nullptr || c->num_kv_heads < 1 || c->page_size != UQ_PAGE_SIZE) return 0;
-  size_t b = (size_t)c->num_kv_heads * uq_head_block_bytes(c->format, c->head_dim);
-  // Pages that are a whole number of 512-B units would put every page's head
-  // blocks at the same address offsets, and on MI355X some offsets stream
-  // slower.  FP4 head blocks are 8.5 (d = 128) or 4.25 (d = 64) lines of 128 B,
-  // so a page's pairs start at different 128-B offsets modulo 512 B and the pair
-  // at the slowest one set the launch time: one extra line makes consecutive
-  // pages start at all four.  FP8 pages (16 KB for 8 heads of d = 128) decoded
-  // at 254 us with 2-KB-aligned pools against 167-170 us at other alignments:
-  // 256 extra bytes make it 169 us whatever the pool's alignment.  BF16 pages
-  // showed no such effect and are not padded.
-  if (b != 0 && b % 512 == 0) {
-    if (c->format == UQ_KV_FP4) b += 128;
-    else if (c->format == UQ_KV_FP8) b += 256;
-  }
-  return b;
+  return (size_t)c->num_kv_heads * uq_head_block_bytes(c->format, c->head_dim);
 }
 
 int uq_quantize_append(const uq_kv_cache* cache, const void* k_new, const void* v_new, int32_t in_dtype,
@@ -348,6 +336,7 @@ int uq_prefill_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtyp
   a.Hq = num_q_heads;
   a.Hkv = cache->num_kv_heads;
   a.D = cache->head_dim;
+  a.hmask = uq::pow2_mask(cache->num_kv_heads);
   a.Tq = total_q;
   a.sm_scale = sm_scale;
   a.rot = rot_of(cache);

@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
   x.template quantize<RV>(p, a.constopt != 0, a.rot, is_v);
   if (!in_range || slot < 0) return;
   const int page = slot >> 4, off = slot & 15;
-  uint8_t* blk = (is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes + (int64_t)h * Row::BLK;
+  uint8_t* blk = (is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes +
+                 (int64_t)fp4_block_pos(h, page, a.H, a.hmask) * Row::BLK;
   if (!is_v) x.store_k(blk, off, p);
   else x.store_v(blk, off, p);
 }
@@ -90,7 +91,8 @@ __global__ __launch_bounds__(256) void append_fp4_stream_kernel(AppendArgs a) {
     if (cur.live && cur.slot >= 0) {
       const int h = cur.tr % a.H;
       const int page = cur.slot >> 4, off = cur.slot & 15;
-      uint8_t* blk = (cur.is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes + (int64_t)h * Row::BLK;
+      uint8_t* blk = (cur.is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes +
+                     (int64_t)fp4_block_pos(h, page, a.H, a.hmask) * Row::BLK;
       if (!cur.is_v) cur.x.store_k(blk, off, p);
       else cur.x.store_v(blk, off, p);
     }

@@ -53,6 +53,15 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
+// Where an item's head blocks sit in a page: head0 = the item's first KV head
+// (FP4 blocks at position (h + 2 page) mod H, see fp4_block_pos; FP8 and BF16
+// blocks at position h).
+struct PageGeo {
+  int head0;
+  int H;
+  int mask;
+};
+
 // One of a step's page ids (wave-uniform values) by a lane-dependent index.
 __device__ __forceinline__ int pick_id(const int (&ids)[4], int x) {
   return x == 0 ? ids[0] : x == 1 ? ids[1] : x == 2 ? ids[2] : ids[3];
@@ -128,8 +137,9 @@ template <int D> struct Fp4Pol {
     qo.b = load_q_fp8<D>(qrow, valid, j4);
   }
   __device__ static void load_k(KStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
-                                int64_t head_off, int r16, int j4) {
-    const uint8_t* kb = pool + (int64_t)pick_id(ids, r16 >> 2) * page_bytes + head_off;
+                                const PageGeo& g, int r16, int j4) {
+    const int pid = pick_id(ids, r16 >> 2);
+    const uint8_t* kb = pool + (int64_t)pid * page_bytes + (int64_t)fp4_block_pos(g.head0, pid, g.H, g.mask) * kBlk;
     if (j4 < kGroups) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) st.kc[m] = load16_stream(kb + (4 * m + (r16 & 3)) * (D / 2) + 16 * j4);
@@ -142,8 +152,9 @@ template <int D> struct Fp4Pol {
     }
   }
   __device__ static void load_v(VStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
-                                int64_t head_off, int r16, int j4) {
-    const uint8_t* vb = pool + (int64_t)pick_id(ids, j4) * page_bytes + head_off;
+                                const PageGeo& g, int r16, int j4) {
+    const int pid = pick_id(ids, j4);
+    const uint8_t* vb = pool + (int64_t)pid * page_bytes + (int64_t)fp4_block_pos(g.head0, pid, g.H, g.mask) * kBlk;
 #pragma unroll
     for (int q = 0; q < kCPL; ++q) st.vc[q] = load16_stream(vb + (16 * q + r16) * kPage);   // pair kCPL*r16 + q
     st.vs = load16_stream(vb + kCode + kPage * ((kCPL * r16) / 16));
@@ -261,8 +272,10 @@ template <int D> struct Fp4PairPol {
     qo.b[1] = lane_head == 1 ? q : z;
   }
   __device__ static void load_k(KStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
-                                int64_t head_off, int r16, int j4) {
-    const uint8_t* pg = pool + (int64_t)pick_id(ids, r16 >> 3) * page_bytes + head_off;
+                                const PageGeo& g, int r16, int j4) {
+    // the pair's two blocks are adjacent (positions 2k, 2k + 1 of the page)
+    const int pid = pick_id(ids, r16 >> 3);
+    const uint8_t* pg = pool + (int64_t)pid * page_bytes + (int64_t)fp4_block_pos(g.head0, pid, g.H, g.mask) * kBlk;
     const int slot0 = 8 * ((r16 >> 2) & 1) + (r16 & 3);
     if (j4 < kGroups) {
       uint32_t d[2];
@@ -282,8 +295,10 @@ template <int D> struct Fp4PairPol {
     }
   }
   __device__ static void load_v(VStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
-                                int64_t head_off, int r16, int j4) {
-    const uint8_t* pg = pool + (int64_t)pick_id(ids, j4 >> 1) * page_bytes + head_off + 8 * (j4 & 1);
+                                const PageGeo& g, int r16, int j4) {
+    const int pid = pick_id(ids, j4 >> 1);
+    const uint8_t* pg = pool + (int64_t)pid * page_bytes + (int64_t)fp4_block_pos(g.head0, pid, g.H, g.mask) * kBlk +
+                        8 * (j4 & 1);
 #pragma unroll
     for (int X = 0; X < 2; ++X) {
       const uint8_t* vb = pg + X * kBlk;
@@ -395,8 +410,8 @@ template <int D> struct Fp8Pol {
     qo.b[3] = cvt8(hi.z, hi.w);
   }
   __device__ static void load_k(KStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
-                                int64_t head_off, int r16, int j4) {
-    const uint8_t* kb = pool + (int64_t)pick_id(ids, r16 >> 2) * page_bytes + head_off;
+                                const PageGeo& g, int r16, int j4) {
+    const uint8_t* kb = pool + (int64_t)pick_id(ids, r16 >> 2) * page_bytes + (int64_t)g.head0 * kBlk;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int slot = 4 * m + (r16 & 3);
@@ -409,8 +424,8 @@ template <int D> struct Fp8Pol {
     }
   }
   __device__ static void load_v(VStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
-                                int64_t head_off, int r16, int j4) {
-    const uint8_t* vb = pool + (int64_t)pick_id(ids, j4) * page_bytes + head_off;
+                                const PageGeo& g, int r16, int j4) {
+    const uint8_t* vb = pool + (int64_t)pick_id(ids, j4) * page_bytes + (int64_t)g.head0 * kBlk;
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) st.vc[t] = load16_stream(vb + (16 * t + r16) * kPage);
   }
@@ -486,8 +501,8 @@ template <int D> struct Bf16Pol {
       qo.b[kk] = bf2h8(valid ? load16(qrow + 2 * (32 * kk + 8 * j4)) : make_uint4(0, 0, 0, 0));
   }
   __device__ static void load_k(KStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
-                                int64_t head_off, int r16, int j4) {
-    const uint8_t* kb = pool + (int64_t)pick_id(ids, r16 >> 2) * page_bytes + head_off;
+                                const PageGeo& g, int r16, int j4) {
+    const uint8_t* kb = pool + (int64_t)pick_id(ids, r16 >> 2) * page_bytes + (int64_t)g.head0 * kBlk;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int slot = 4 * m + (r16 & 3);
@@ -496,8 +511,8 @@ template <int D> struct Bf16Pol {
     }
   }
   __device__ static void load_v(VStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
-                                int64_t head_off, int r16, int j4) {
-    const uint8_t* vb = pool + (int64_t)pick_id(ids, j4) * page_bytes + head_off;
+                                const PageGeo& g, int r16, int j4) {
+    const uint8_t* vb = pool + (int64_t)pick_id(ids, j4) * page_bytes + (int64_t)g.head0 * kBlk;
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       st.v[t][0] = load16(vb + 2 * ((16 * t + r16) * kPage));
@@ -868,6 +883,7 @@ struct KArgs {
   int32_t max_pages;
   const void* q;             // caller's query [B][Hq][D], bf16 or f32
   int32_t B, Hq, Hkv, G;
+  int32_t hmask;             // Hkv - 1 when Hkv is a power of two, else -1
   float scale_log2;          // sm_scale * log2(e)
   float* out;                // [B][Hq][D]
   float* ml;                 // [2 * grid][16][2] partial (m in log2 units, l) of cut items
@@ -1117,7 +1133,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
           const int head = Pol::kNH * it + (nlive ? nr % Pol::kNH : 0);
           nrow.load(nv && nlive ? a.v_new : a.k_new, (int64_t)b * a.Hkv + head, np);
           nblk = const_cast<uint8_t*>(nv && nlive ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes +
-                 (int64_t)head * NewRow::BLK;
+                 (int64_t)fp4_block_pos(head, page, a.Hkv, a.hmask) * NewRow::BLK;
           noff = t & 15;
         }
         if (__ballot(sg_new && sg_first + sg_nstep <= NW * (N + 1)) != 0) {
@@ -1173,10 +1189,10 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     };
     auto claim = [&]() { return claim_at(take()); };
     auto load_k = [&](typename Pol::KStep& st, const Claim& c) {
-      Pol::load_k(st, a.k_pool, c.ids, a.page_bytes, (int64_t)c.hk * (Pol::kNH * Pol::kBlk), r16, j4);
+      Pol::load_k(st, a.k_pool, c.ids, a.page_bytes, PageGeo{c.hk * Pol::kNH, a.Hkv, a.hmask}, r16, j4);
     };
     auto load_v = [&](typename Pol::VStep& st, const Claim& c) {
-      Pol::load_v(st, a.v_pool, c.ids, a.page_bytes, (int64_t)c.hk * (Pol::kNH * Pol::kBlk), r16, j4);
+      Pol::load_v(st, a.v_pool, c.ids, a.page_bytes, PageGeo{c.hk * Pol::kNH, a.Hkv, a.hmask}, r16, j4);
     };
 
     // ---- prologue: N K and N - 1 V buffers.  K is consumed by the QK at the
@@ -1544,6 +1560,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   k.B = a.B;
   k.Hq = a.Hq;
   k.Hkv = a.Hkv;
+  k.hmask = a.hmask;
   k.G = a.Hq / a.Hkv;
   k.scale_log2 = a.sm_scale * 1.4426950408889634f;
   k.out = a.out;
@@ -1629,6 +1646,7 @@ struct PfArgs {
   const int32_t* seq_lens;    // [B]
   float* out;                 // [Tq][Hq][D]
   int32_t B, Hq, Hkv, G, QT;
+  int32_t hmask;              // Hkv - 1 when Hkv is a power of two, else -1
   float scale_log2;
   Rot rot;                    // the cache's rotation variant
   int32_t unrot;              // rotate the output back (V rotated)
@@ -1773,7 +1791,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   }
 
   const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
-  const int64_t head_off = (int64_t)hk * Pol::kBlk;
+  const PageGeo geo{hk, a.Hkv, a.hmask};
   auto ids_of = [&](int s, int (&ids)[4]) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) ids[x] = pt[max(min(4 * s + x, npages - 1), 0)];   // within the row
@@ -1785,16 +1803,16 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   {
     int ids[4];
     ids_of(0, ids);
-    Pol::load_k(k0, a.k_pool, ids, a.page_bytes, head_off, r16, j4);
-    Pol::load_v(v0, a.v_pool, ids, a.page_bytes, head_off, r16, j4);
+    Pol::load_k(k0, a.k_pool, ids, a.page_bytes, geo, r16, j4);
+    Pol::load_v(v0, a.v_pool, ids, a.page_bytes, geo, r16, j4);
   }
   auto step = [&](int s, typename Pol::KStep& kc, typename Pol::VStep& vc, typename Pol::KStep& kn,
                   typename Pol::VStep& vn) {
     if (s + 1 < steps) {                                       // prefetch the next step
       int ids[4];
       ids_of(s + 1, ids);
-      Pol::load_k(kn, a.k_pool, ids, a.page_bytes, head_off, r16, j4);
-      Pol::load_v(vn, a.v_pool, ids, a.page_bytes, head_off, r16, j4);
+      Pol::load_k(kn, a.k_pool, ids, a.page_bytes, geo, r16, j4);
+      Pol::load_v(vn, a.v_pool, ids, a.page_bytes, geo, r16, j4);
     }
     const int key0 = 4 * kPage * s + kPage * j4;                // first key of this lane's page
     if (__any(Ls - key0 < TOK)) Pol::mask_v(vc, min(max(Ls - key0, 0), TOK));   // slots past the sequence end
@@ -1932,6 +1950,7 @@ hipError_t launch_prefill(const PrefillArgs& p, hipStream_t s) {
   a.B = p.B;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
+  a.hmask = p.hmask;
   a.G = p.Hq / p.Hkv;
   a.QT = kPfRows / a.G;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;

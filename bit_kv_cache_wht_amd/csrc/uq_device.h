@@ -43,6 +43,15 @@ __device__ __forceinline__ double flip_sign(double x, uint32_t m) {
 }
 __device__ __forceinline__ float flip_sign(float x, uint32_t m) { return __uint_as_float(__float_as_uint(x) ^ m); }
 
+// Position of KV head h's block inside FP4 page `page` of a cache with H KV
+// heads: (h + 2 page) mod H, so that for an even H a pair's two blocks stay
+// adjacent and pair p sits at pair position (p + page) mod (H / 2).  `mask` is
+// H - 1 when H is a power of two, else -1.  Page ids are non-negative.
+__device__ __forceinline__ int fp4_block_pos(int h, int page, int H, int mask) {
+  if (mask >= 0) return (int)(((uint32_t)h + 2u * (uint32_t)page) & (uint32_t)mask);
+  return (h + 2 * (page % H)) % H;
+}
+
 template <int D> struct Fp4Block {
   static constexpr int kCodeBytes = kPage * D / 2;          // codes of 16 slots
   static constexpr int kBytes = kCodeBytes + kPage * D / 32; // + one scale byte per group

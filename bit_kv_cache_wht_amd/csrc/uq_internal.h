@@ -25,6 +25,7 @@ struct AppendArgs {
   uint8_t* v_pool;
   int64_t page_bytes;         // bytes of one page of one pool
   int32_t T, H;
+  int32_t hmask;              // H - 1 when H is a power of two, else -1 (FP4 block positions)
   int32_t constopt;           // FP4: constOpt group scales (UQ_FLAG_SCALE_CONSTOPT)
   Rot rot;                    // FP4: the cache's rotation variant
 };
@@ -57,6 +58,7 @@ struct DecodeArgs {
   int32_t max_pages;
   const int32_t* seq_lens;
   int32_t B, Hq, Hkv, D;
+  int32_t hmask;             // Hkv - 1 when Hkv is a power of two, else -1
   float sm_scale;
   float* out;
   uint8_t* ws;
@@ -83,9 +85,13 @@ struct PrefillArgs {
   const int32_t* seq_lens;     // [B]
   float* out;                  // [Tq][Hq][D]
   int32_t B, Hq, Hkv, D, Tq;
+  int32_t hmask;               // Hkv - 1 when Hkv is a power of two, else -1
   float sm_scale;
   Rot rot;                     // the cache's rotation variant
 };
+
+// H - 1 when H is a power of two, else -1 (the FP4 block-position mask).
+inline int32_t pow2_mask(int32_t H) { return H > 0 && (H & (H - 1)) == 0 ? H - 1 : -1; }
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 int prefill_max_seqs();
 

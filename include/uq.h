@@ -52,9 +52,17 @@
  *   an out-of-range value there is undefined behaviour.
  *
  * Paged layout (part of the ABI).  A pool is [num_pages][uq_page_bytes]; a page
- * holds the num_kv_heads head-blocks back to back from its first byte (FP4 and
- * FP8 pages may end in unused bytes, see uq_page_bytes); token position t of a
- * sequence lives in page page_table[t / 16] at slot t % 16.
+ * holds the num_kv_heads head-blocks back to back, nothing else (FP4: exactly
+ * 17 bytes per 32 elements); token position t of a sequence lives in page
+ * page_table[t / 16] at slot t % 16.  The pages fix 17 B per group and paging,
+ * not the byte order inside a page; the order below serves the decode's
+ * operand loads, and FP4 pages rotate their KV-head pairs so that a pair's
+ * blocks start at different offsets modulo 512 B from page to page (on MI355X
+ * a pair that always starts at the same such offset can stream more slowly).
+ *   FP4: the block of KV head h in page P is at block position (h + 2P) mod
+ *        num_kv_heads (for an even head count, a pair's two blocks stay
+ *        adjacent and the pairs rotate by one pair position per page);
+ *   FP8, BF16: the block of KV head h is at position h.
  * Head-block layouts (d = head_dim, 16 slots):
  *   FP4  K: codes [16 slot][d/2 B] (byte j: channel 2j low nibble, 2j+1 high),
  *           then scales [slot % 4][d/32 group][slot / 4]       = 17*d/2 bytes
@@ -127,8 +135,8 @@ typedef struct uq_kv_cache {
   int32_t page_size;     /* tokens per page; must be 16                          */
   int32_t num_kv_heads;  /* >= 1                                                 */
   int32_t head_dim;      /* 64 or 128                                            */
-  void* k_pool;          /* device, [num_pages][uq_page_bytes], 256-B aligned; head h's
-                            block of a page starts at byte h * uq_head_block_bytes */
+  void* k_pool;          /* device, [num_pages][uq_page_bytes], 256-B aligned; see
+                            "Paged layout" for the block positions in a page     */
   void* v_pool;          /* device, same shape                                    */
   uint32_t rotation;     /* UQ_ROT_* bits; FP4 only (0 for FP8 and BF16)           */
   uint32_t rotation_signs[4];   /* with UQ_ROT_SIGNS: the sign bits of s          */
@@ -138,12 +146,9 @@ typedef struct uq_kv_cache {
  * BF16 32*d; 0 for an unknown format or head_dim.  Host only. */
 size_t uq_head_block_bytes(int32_t format, int32_t head_dim);
 
-/* Bytes of one page of one pool: num_kv_heads head-blocks, plus, when those fill
- * a whole number of 512-B units, bytes that nothing reads or writes: 128 for FP4
- * (so that consecutive pages begin at different offsets modulo 512 B: on MI355X,
- * 8.5-line head-block pairs that always start at the same such offset stream up
- * to ~5% slower than others), 256 for FP8 (16-KB pages read up to 1.5x slower
- * at some pool alignments), none for BF16.  0 if invalid. */
+/* Bytes of one page of one pool: num_kv_heads head-blocks (FP4: num_kv_heads *
+ * 17 * d / 2; FP8: num_kv_heads * 16 * d; BF16: num_kv_heads * 32 * d).  0 if
+ * the descriptor is invalid.  Host only. */
 size_t uq_page_bytes(const uq_kv_cache* cache);
 
 /*

@@ -72,7 +72,7 @@ __all__ = [
     "quantize_fp4", "dequantize_fp4", "pack_nibbles", "unpack_nibbles",
     "e4m3_decode", "e4m3_encode", "bf16_bits_to_f64", "f32_to_f64", "bf16_round_bits",
     "head_block_bytes", "page_bytes", "new_pool", "prefill_attention",
-    "fp4_k_code_offset", "fp4_k_scale_offset", "fp4_v_code_offset", "fp4_v_scale_offset",
+    "fp4_block_position", "fp4_k_code_offset", "fp4_k_scale_offset", "fp4_v_code_offset", "fp4_v_scale_offset",
     "fp8_k_offset", "fp8_v_offset", "bf16_k_index", "bf16_v_index",
     "append", "gather_dequant", "rotate_quantize_query", "attention",
     "decode_attention", "decode_attention_rows",
@@ -367,7 +367,13 @@ def bf16_round_bits(x32) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# Paged cache layout (reading R8).  Pools are uint8 [num_pages][H_kv][block].
+# Paged cache layout (reading R8).  Pools are uint8 [num_pages][H_kv][block]:
+# a page is H_kv blocks back to back, 17 bytes per 32 elements for FP4, with no
+# padding.  The order of bytes inside a page is not fixed by the pages; the
+# layout below serves the decode's operand loads, and the FP4 block positions
+# rotate with the page id, so that a KV-head pair's blocks start at different
+# offsets from page to page.
+#   FP4: KV head h's block at position (h + 2 page) mod H_kv of page `page`
 #   FP4 K block: codes[16 tok][d/2] (token-major) then scales[tok % 4][d/32][tok // 4]
 #   FP4 V block: codes[d/2 rows][16 tok] (channel pair c in row 16*(c % (d/32)) + c // (d/32))
 #                then scales[d/32 groups][16 tok]
@@ -390,6 +396,15 @@ def page_bytes(fmt: int, num_kv_heads: int, d: int) -> int:
 
 def new_pool(fmt: int, num_pages: int, num_kv_heads: int, d: int) -> np.ndarray:
     return np.zeros((num_pages, num_kv_heads, head_block_bytes(fmt, d)), dtype=np.uint8)
+
+
+def fp4_block_position(head, page, num_kv_heads):
+    """Position of KV head `head`'s block inside page `page` of an FP4 pool:
+    (head + 2 * page) mod H_kv.  For an even H_kv the two heads of a pair stay
+    adjacent and pair p sits at pair position (p + page) mod (H_kv / 2), so the
+    pairs' blocks start at different offsets from page to page (reading R8)."""
+    H = int(num_kv_heads)
+    return (np.asarray(head, np.int64) + 2 * (np.asarray(page, np.int64) % H)) % H
 
 
 def fp4_k_code_offset(tok, byte, d):
@@ -457,12 +472,13 @@ def append(fmt, k_pool, v_pool, k_new, v_new, slot_mapping, in_dtype="bf16", sca
             j = np.arange(d // 2)
             g = np.arange(d // GROUP)
             for h in range(H):
+                pos = fp4_block_position(h, page, H)[:, None]
                 if is_v:
-                    flat[page[:, None], h, fp4_v_code_offset(off[:, None], j[None, :], d)] = packed[:, h]
-                    flat[page[:, None], h, fp4_v_scale_offset(off[:, None], g[None, :], d)] = sbytes[:, h]
+                    flat[page[:, None], pos, fp4_v_code_offset(off[:, None], j[None, :], d)] = packed[:, h]
+                    flat[page[:, None], pos, fp4_v_scale_offset(off[:, None], g[None, :], d)] = sbytes[:, h]
                 else:
-                    flat[page[:, None], h, fp4_k_code_offset(off[:, None], j[None, :], d)] = packed[:, h]
-                    flat[page[:, None], h, fp4_k_scale_offset(off[:, None], g[None, :], d)] = sbytes[:, h]
+                    flat[page[:, None], pos, fp4_k_code_offset(off[:, None], j[None, :], d)] = packed[:, h]
+                    flat[page[:, None], pos, fp4_k_scale_offset(off[:, None], g[None, :], d)] = sbytes[:, h]
         elif fmt == FMT_FP8:
             b = e4m3_encode(x)
             c = np.arange(d)
@@ -491,12 +507,13 @@ def gather_dequant(fmt, pool, page_row, seq_len, head, d, is_v) -> np.ndarray:
     if fmt == FMT_FP4:
         j = np.arange(d // 2)[None, :]
         g = np.arange(d // GROUP)[None, :]
+        pos = fp4_block_position(head, page, H)
         if is_v:
-            packed = flat[page, head, fp4_v_code_offset(off, j, d)]
-            sb = flat[page, head, fp4_v_scale_offset(off, g, d)]
+            packed = flat[page, pos, fp4_v_code_offset(off, j, d)]
+            sb = flat[page, pos, fp4_v_scale_offset(off, g, d)]
         else:
-            packed = flat[page, head, fp4_k_code_offset(off, j, d)]
-            sb = flat[page, head, fp4_k_scale_offset(off, g, d)]
+            packed = flat[page, pos, fp4_k_code_offset(off, j, d)]
+            sb = flat[page, pos, fp4_k_scale_offset(off, g, d)]
         return dequantize_fp4(unpack_nibbles(packed), sb)
     c = np.arange(d)[None, :]
     if fmt == FMT_FP8:

@@ -89,13 +89,22 @@ def test_sign_words_packing():
 @pytest.mark.parametrize("d", [64, 128])
 def test_block_sizes_match_oracle_layout(fmt, d):
     assert uq.uq_head_block_bytes(fmt, d) == O.head_block_bytes(fmt, d)
-    c = cache(fmt, heads=8, d=d)
-    # pages whose head blocks fill whole 512-B units get 128 (FP4) or 256 (FP8)
-    # more bytes
-    want = O.page_bytes(fmt, 8, d)
-    if want % 512 == 0:
-        want += {uq.UQ_KV_FP4: 128, uq.UQ_KV_FP8: 256}.get(fmt, 0)
-    assert uq.lib().uq_page_bytes(ctypes.byref(c)) == want
+    for heads in (1, 3, 4, 8):
+        c = cache(fmt, heads=heads, d=d)
+        # a page is its head blocks back to back, nothing more
+        assert uq.lib().uq_page_bytes(ctypes.byref(c)) == O.page_bytes(fmt, heads, d) == heads * O.head_block_bytes(fmt, d)
+
+
+def test_page_bytes_at_the_benchmark_shapes():
+    # FP4: exactly 17/32 bytes per element (4.25 bits: [commentary] footnote 2;
+    # [review] §3.1 table "Stored footprint"); FP8 one byte; BF16 two.
+    for heads in (8, 4):
+        c = cache(B.UQ_KV_FP4, heads=heads, d=128)
+        assert uq.lib().uq_page_bytes(ctypes.byref(c)) == heads * 16 * (64 + 4) == heads * 16 * 128 * 17 // 32
+        assert uq.lib().uq_page_bytes(ctypes.byref(cache(B.UQ_KV_FP8, heads=heads, d=128))) == heads * 16 * 128
+        assert uq.lib().uq_page_bytes(ctypes.byref(cache(B.UQ_KV_BF16, heads=heads, d=128))) == heads * 16 * 128 * 2
+    c = cache(B.UQ_KV_FP4, heads=8, d=128)
+    assert uq.lib().uq_page_bytes(ctypes.byref(c)) == 8704
 
 
 def test_block_sizes_invalid():

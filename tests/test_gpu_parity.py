@@ -138,7 +138,8 @@ def check_fp4_within_stated_bound(wl, pools):
         for h in range(H):
             rows = src[:, h]
             vals = O.gather_dequant(O.FMT_FP4, pool, wl.page_table[0], T, h, d, is_v)
-            E = blk[page[:, None], h, off((t % 16)[:, None], np.arange(d // 32)[None, :], d)].astype(np.int64) - 127
+            pos = O.fp4_block_position(h, page, H)[:, None]
+            E = blk[page[:, None], pos, off((t % 16)[:, None], np.arange(d // 32)[None, :], d)].astype(np.int64) - 127
             y = O.wht(rows.astype(np.float64))
             delta = _stated_bound(rows, d)[:, None]
             m = np.abs(y).reshape(T, d // 32, 32).max(2)

@@ -370,6 +370,21 @@ def test_page_layout_is_a_bijection(fmt, d):
         assert np.all(cnt == 1)
 
 
+@pytest.mark.parametrize("H", [1, 2, 3, 4, 5, 8])
+def test_fp4_block_positions_permute_heads_and_rotate_pairs(H):
+    # Reading R8: in every page the heads' blocks take each position once; for
+    # an even H_kv the heads of a pair stay adjacent and the pairs rotate by one
+    # pair position from page to page, so over H_kv / 2 consecutive pages every
+    # pair starts at every pair position.
+    for page in list(range(12)) + [2 ** 30 + 3, 2 ** 31 - 1]:
+        pos = O.fp4_block_position(np.arange(H), page, H)
+        assert sorted(pos.tolist()) == list(range(H))
+        if H % 2 == 0:
+            assert np.all(pos[1::2] == pos[0::2] + 1) and np.all(pos[0::2] % 2 == 0)
+            assert np.array_equal(pos[0::2] // 2, (np.arange(H // 2) + page) % (H // 2))
+    assert O.fp4_block_position(3, 0, 8) == 3
+
+
 # ---------------------------------------------------------------- E4M3 / bf16
 def test_e4m3_decode_matches_torch_all_codes():
     codes = np.arange(256, dtype=np.uint8)
