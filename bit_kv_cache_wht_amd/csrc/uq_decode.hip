@@ -86,12 +86,16 @@ __device__ __forceinline__ v4f mma2(const v8h& a, const v8h (&p)[2], v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, p[1], c, 0, 0, 0);
 }
 
-// p0, p1 ~= hi + lo as packed float16 pairs: hi = f16(p), lo = f16(p - hi), the
-// difference taken in float32 by v_fma_mix straight from the packed hi halves.
+// p0, p1 ~= hi + lo as packed float16 pairs: hi = f16(p), lo = f16(p - hi) (the
+// float32 difference is exact: hi is within 2^-11 of p).  Written as plain code,
+// not inline asm: the packed operands feed an MFMA right away, and only
+// instructions the compiler sees get the wait states that a VALU write needs
+// before an MFMA reads the register (an inline-asm v_fma_mix here was followed
+// by the MFMA one cycle later, which then read the register's old high half).
 __device__ __forceinline__ void split_f16x2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
-  hi = __builtin_bit_cast(uint32_t, v2h{(_Float16)p0, (_Float16)p1});
-  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(hi), "v"(p0));
-  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(lo) : "v"(hi), "v"(p1));
+  const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
+  hi = __builtin_bit_cast(uint32_t, v2h{h0, h1});
+  lo = __builtin_bit_cast(uint32_t, v2h{(_Float16)(p0 - (float)h0), (_Float16)(p1 - (float)h1)});
 }
 
 // E4M3 query as the FP8 B operand: lane (h, j) holds k = 16j..16j+15 and

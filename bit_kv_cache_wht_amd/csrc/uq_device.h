@@ -186,8 +186,7 @@ __device__ __forceinline__ float f32_round_to_odd(double r) {
   const double a = fmax(fabs(r), 0x1p-120);
   const uint32_t ahi = (uint32_t)__double2hiint(a), alo = (uint32_t)__double2loint(a);
   const uint32_t mag = __builtin_amdgcn_alignbit(ahi, alo, 29) - (384u << 23);
-  uint32_t sticky;                       // min(alo << 3, 1) in one instruction
-  asm("v_min_u32 %0, %1, 1" : "=v"(sticky) : "v"(alo << 3));
+  const uint32_t sticky = min(alo << 3, 1u);   // 1 if any dropped low bit is set
   return __uint_as_float(((uint32_t)__double2hiint(r) & 0x80000000u) | mag | sticky);
 }
 
