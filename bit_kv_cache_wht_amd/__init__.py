@@ -7,6 +7,9 @@ library; the first call does, and raises if ``libuq.so`` is missing (build it
 with ``python -m bit_kv_cache_wht_amd.build``).
 """
 from ._binding import (  # noqa: F401
+    UQ_CHECK_BAD_LEN,
+    UQ_CHECK_BAD_PAGE,
+    UQ_FLAG_CHECK,
     UQ_FLAG_OUT_ROTATED,
     UQ_FLAG_SCALE_CONSTOPT,
     UQ_IN_BF16,
@@ -18,6 +21,7 @@ from ._binding import (  # noqa: F401
     UQ_ROT_SIGNS,
     KvCache,
     UqError,
+    decode_check_word,
     lib,
     sign_words,
     uq_append_bf16,

@@ -11,6 +11,8 @@ UQ_IN_BF16, UQ_IN_F32 = 0, 1
 UQ_PAGE_SIZE = 16
 UQ_FLAG_OUT_ROTATED = 1
 UQ_FLAG_SCALE_CONSTOPT = 2
+UQ_FLAG_CHECK = 4
+UQ_CHECK_BAD_LEN, UQ_CHECK_BAD_PAGE = 1, 2
 UQ_ROT_K_ONLY = 1
 UQ_ROT_SIGNS = 2
 
@@ -339,6 +341,13 @@ def uq_append_decode_attention(cache, k_new, v_new, q, page_table, seq_lens, sm_
                                           float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, flags,
                                           _stream(stream))
     _check("uq_append_decode_attention", st)
+
+
+def decode_check_word(workspace) -> int:
+    """The UQ_FLAG_CHECK error word (UQ_CHECK_* bits) held in the first 4 bytes of a
+    decode workspace (synchronizes with the device)."""
+    import torch
+    return int(workspace[:4].view(torch.int32).item()) & 0xFFFFFFFF
 
 
 def uq_decode_attention_fp8(cache, q, page_table, seq_lens, sm_scale, out, workspace, flags=0, stream=None) -> None:

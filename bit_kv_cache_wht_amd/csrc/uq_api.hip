@@ -26,6 +26,7 @@ int check_cache(const uq_kv_cache* c, int want_format) {
   if (c->page_size != UQ_PAGE_SIZE) return UQ_ERR_UNSUPPORTED;
   if (!dim_ok(c->head_dim)) return UQ_ERR_UNSUPPORTED;
   if (c->num_kv_heads < 1 || c->num_pages < 1) return UQ_ERR_INVALID_ARG;
+  if (c->num_kv_heads > 65536) return UQ_ERR_UNSUPPORTED;   // page offsets are 32-bit
   if (c->k_pool == nullptr || c->v_pool == nullptr) return UQ_ERR_INVALID_ARG;
   // rotation variants: FP4 only; sign bits only with UQ_ROT_SIGNS and below head_dim
   if ((c->rotation & ~(UQ_ROT_K_ONLY | UQ_ROT_SIGNS)) != 0u) return UQ_ERR_INVALID_ARG;
@@ -60,6 +61,7 @@ static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
 uq::DecodeLayout noalloc_layout(int head_dim) {
   const uq::DecodeLayout shaped = uq::decode_layout(UQ_KV_FP4, 1, 1, 1, head_dim);
   uq::DecodeLayout L;
+  L.err = 0;                                                    // unused: no UQ_FLAG_CHECK here
   L.cnt = 0;
   L.ml = kNoallocCounterBytes;                                  // a multiple of 256
   L.po = L.ml + (shaped.po - shaped.ml);
@@ -127,6 +129,8 @@ int append_common(const uq_kv_cache* cache, int format, const void* k_new, const
   a.T = num_tokens;
   a.H = cache->num_kv_heads;
   a.hmask = uq::pow2_mask(cache->num_kv_heads);
+  a.units = (int32_t)(a.page_bytes >> 8);
+  a.umask = uq::pow2_mask(a.units);
   a.constopt = (flags & UQ_FLAG_SCALE_CONSTOPT) ? 1 : 0;
   a.rot = rot_of(cache);
   return hip_status(launch(a, cache->head_dim, in_dtype, reinterpret_cast<hipStream_t>(stream)));
@@ -141,9 +145,11 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
                   bool noalloc = false) {
   int st = check_cache(cache, format);
   if (st != UQ_OK) return st;
-  // the constOpt bit selects the scale rule of the fused step's write
-  const uint32_t allowed = format != UQ_KV_FP4 ? 0u
-                           : UQ_FLAG_OUT_ROTATED | (k_new != nullptr ? UQ_FLAG_SCALE_CONSTOPT : 0u);
+  // the constOpt bit selects the scale rule of the fused step's write; the
+  // check reports into the workspace, which the no-allocation variant hides
+  const uint32_t allowed = (noalloc ? 0u : UQ_FLAG_CHECK) |
+                           (format != UQ_KV_FP4 ? 0u
+                            : UQ_FLAG_OUT_ROTATED | (k_new != nullptr ? UQ_FLAG_SCALE_CONSTOPT : 0u));
   if ((flags & ~allowed) != 0u) return UQ_ERR_INVALID_ARG;
   if (q_dtype != UQ_IN_BF16 && q_dtype != UQ_IN_F32) return UQ_ERR_INVALID_ARG;
   if (format == UQ_KV_BF16 && q_dtype != UQ_IN_BF16) return UQ_ERR_UNSUPPORTED;
@@ -192,6 +198,8 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   a.out = out;
   a.ws = static_cast<uint8_t*>(workspace);
   a.lay = lay;
+  a.check = (flags & UQ_FLAG_CHECK) != 0u;
+  a.num_pages = cache->num_pages;
   a.rot = rot_of(cache);
   a.unrotate = format == UQ_KV_FP4 && !(flags & UQ_FLAG_OUT_ROTATED) && a.rot.k_only == 0u;
   a.constopt = (flags & UQ_FLAG_SCALE_CONSTOPT) != 0u;

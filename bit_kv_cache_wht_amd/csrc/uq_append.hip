@@ -142,11 +142,14 @@ __global__ __launch_bounds__(256) void append_plain_kernel(AppendArgs a) {
   uint8_t* blk = (is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes + (int64_t)h * BLK;
   if constexpr (FMT == UQ_KV_FP8) {
     const uint32_t b0 = e4m3x4_f32(f[0], f[1], f[2], f[3]), b1 = e4m3x4_f32(f[4], f[5], f[6], f[7]);
+    uint8_t* pg = (is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes;
+    const uint32_t rot = fp8_rot(page, a.units, a.umask), pb = (uint32_t)a.page_bytes, hb = (uint32_t)(h * BLK);
     if (!is_v) {
-      *reinterpret_cast<uint2*>(blk + off * D + c0) = make_uint2(b0, b1);
+      *reinterpret_cast<uint2*>(pg + fp8_wrap(hb + off * D + c0, rot, pb)) = make_uint2(b0, b1);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) blk[(c0 + i) * kPage + off] = (uint8_t)((i < 4 ? b0 : b1) >> (8 * (i & 3)));
+      for (int i = 0; i < 8; ++i)
+        pg[fp8_wrap(hb + (c0 + i) * kPage + off, rot, pb)] = (uint8_t)((i < 4 ? b0 : b1) >> (8 * (i & 3)));
     }
   } else {
     uint16_t* blk16 = reinterpret_cast<uint16_t*>(blk);

@@ -60,6 +60,7 @@ struct PageGeo {
   int head0;
   int H;
   int mask;
+  int units, umask;   // FP8 byte rotation (fp8_rot)
 };
 
 // One of a step's page ids (wave-uniform values) by a lane-dependent index.
@@ -87,15 +88,19 @@ __device__ __forceinline__ v4f mma2(const v8h& a, const v8h (&p)[2], v4f c) {
 }
 
 // p0, p1 ~= hi + lo as packed float16 pairs: hi = f16(p), lo = f16(p - hi) (the
-// float32 difference is exact: hi is within 2^-11 of p).  Written as plain code,
-// not inline asm: the packed operands feed an MFMA right away, and only
-// instructions the compiler sees get the wait states that a VALU write needs
-// before an MFMA reads the register (an inline-asm v_fma_mix here was followed
-// by the MFMA one cycle later, which then read the register's old high half).
+// float32 difference is exact: hi is within 2^-11 of p), lo by v_fma_mix straight
+// from the packed hi halves.  lo feeds an MFMA, which must not read a register
+// sooner than two wait states after a VALU instruction writes it, and the
+// compiler pads only around instructions it sees: the asm block therefore ends
+// with s_nop 1 (without it the MFMA followed the last write after one wait state
+// and could read the register's old high half).
 __device__ __forceinline__ void split_f16x2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
-  const _Float16 h0 = (_Float16)p0, h1 = (_Float16)p1;
-  hi = __builtin_bit_cast(uint32_t, v2h{h0, h1});
-  lo = __builtin_bit_cast(uint32_t, v2h{(_Float16)(p0 - (float)h0), (_Float16)(p1 - (float)h1)});
+  hi = __builtin_bit_cast(uint32_t, v2h{(_Float16)p0, (_Float16)p1});
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "s_nop 1"
+      : "=&v"(lo)
+      : "v"(hi), "v"(p0), "v"(p1));
 }
 
 // E4M3 query as the FP8 B operand: lane (h, j) holds k = 16j..16j+15 and
@@ -415,13 +420,15 @@ template <int D> struct Fp8Pol {
   }
   __device__ static void load_k(KStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
                                 const PageGeo& g, int r16, int j4) {
-    const uint8_t* kb = pool + (int64_t)pick_id(ids, r16 >> 2) * page_bytes + (int64_t)g.head0 * kBlk;
+    const int pid = pick_id(ids, r16 >> 2);
+    const uint8_t* pg = pool + (int64_t)pid * page_bytes;
+    const uint32_t rot = fp8_rot(pid, g.units, g.umask), pb = (uint32_t)page_bytes, hb = (uint32_t)(g.head0 * kBlk);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int slot = 4 * m + (r16 & 3);
       if (j4 < kLanesK) {
-        st.k[m][0] = load16_stream(kb + slot * D + 32 * j4);
-        st.k[m][1] = load16_stream(kb + slot * D + 32 * j4 + 16);
+        st.k[m][0] = load16_stream(pg + fp8_wrap(hb + slot * D + 32 * j4, rot, pb));
+        st.k[m][1] = load16_stream(pg + fp8_wrap(hb + slot * D + 32 * j4 + 16, rot, pb));
       } else {
         st.k[m][0] = st.k[m][1] = make_uint4(0, 0, 0, 0);
       }
@@ -429,9 +436,11 @@ template <int D> struct Fp8Pol {
   }
   __device__ static void load_v(VStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
                                 const PageGeo& g, int r16, int j4) {
-    const uint8_t* vb = pool + (int64_t)pick_id(ids, j4) * page_bytes + (int64_t)g.head0 * kBlk;
+    const int pid = pick_id(ids, j4);
+    const uint8_t* pg = pool + (int64_t)pid * page_bytes;
+    const uint32_t rot = fp8_rot(pid, g.units, g.umask), pb = (uint32_t)page_bytes, hb = (uint32_t)(g.head0 * kBlk);
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) st.vc[t] = load16_stream(vb + (16 * t + r16) * kPage);
+    for (int t = 0; t < kTiles; ++t) st.vc[t] = load16_stream(pg + fp8_wrap(hb + (16 * t + r16) * kPage, rot, pb));
   }
   __device__ static void qk(const KStep& st, const QOp& qo, v4f (&S)[4]) {
 #pragma unroll
@@ -605,8 +614,9 @@ template <int NP> __device__ __forceinline__ int seq_steps(int L) { return ((L +
 
 // Run by all 64 * NW threads; red: 2 NW ints of scratch.  Steps are NP pages;
 // each sequence has Hi items (KV heads, or KV-head pairs).  Returns, in every
-// thread, bit 0 set when the sequences' step counts differ and bit 1 when one of
-// them has none.
+// thread, bit 0 set when the sequences' step counts differ, bit 1 when one of
+// them has none and bit 2 when a length lies outside [0, 16 max_pages] (it is
+// used clamped to that range).
 template <int NW, int NP>
 __device__ int wg_plan(const int32_t* __restrict__ seq_lens, int B, int Hi, int max_pages, int32_t* sbase,
                        int32_t* lens, int32_t* red) {
@@ -617,12 +627,14 @@ __device__ int wg_plan(const int32_t* __restrict__ seq_lens, int B, int Hi, int 
   int bits = 0;
   for (int b0 = 0; b0 < B; b0 += NT) {
     const int b = b0 + tid;
-    const int L = b < B ? clamp_len(seq_lens[b], max_pages) : 0;
+    const int raw = b < B ? seq_lens[b] : 0;
+    const int L = clamp_len(raw, max_pages);
     if (b < B) lens[b] = L;
     const int s = seq_steps<NP>(L);
     const int ns = b < B ? s * Hi : 0;
     const int incl = wave_incl_scan(ns);
-    const int wbits = (__any(b < B && s != s0) ? 1 : 0) | (__any(b < B && s == 0) ? 2 : 0);
+    const int wbits = (__any(b < B && s != s0) ? 1 : 0) | (__any(b < B && s == 0) ? 2 : 0) |
+                      (__any(raw != L) ? 4 : 0);
     if (lane == 63) {
       red[wave] = incl;
       red[NW + wave] = wbits;
@@ -888,11 +900,14 @@ struct KArgs {
   const void* q;             // caller's query [B][Hq][D], bf16 or f32
   int32_t B, Hq, Hkv, G;
   int32_t hmask;             // Hkv - 1 when Hkv is a power of two, else -1
+  int32_t units, umask;      // FP8: page_bytes / 256, units - 1 when a power of two, else -1
   float scale_log2;          // sm_scale * log2(e)
   float* out;                // [B][Hq][D]
   float* ml;                 // [2 * grid][16][2] partial (m in log2 units, l) of cut items
   float* po;                 // [2 * grid][16][D] partial O of cut items
   int32_t* cnt;              // [B][Hkv] arrival counters, zero between calls
+  uint32_t* err;             // UQ_FLAG_CHECK: error word (UQ_CHECK_* bits OR-ed in), else null
+  int32_t num_pages;         // pages in each pool (checked page ids lie in [0, num_pages))
   int32_t R;                 // items per round of a workgroup
   const void* k_new;         // fused step (FP4): the newest token's K and V, [B][Hkv][D]
   const void* v_new;         // in the query's dtype; null: attention only
@@ -1000,7 +1015,9 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
   // T = sq * grid + sr (w * sr < 2^20).
   int alpha = Pol::kShareAlpha;
   if (grid > 0 && 2 * alpha > T / grid) alpha = (T / grid) / 2;
-  if (plan_bits != 1 || grid < 1) alpha = 0;
+  if ((plan_bits & 3) != 1 || grid < 1) alpha = 0;
+  // UQ_FLAG_CHECK: bits found by this wave, OR-ed into the error word at the end
+  uint32_t chk = a.err != nullptr && blockIdx.x == 0 && wave == 0 && (plan_bits & 4) ? UQ_CHECK_BAD_LEN : 0u;
   int32_t* sb = reinterpret_cast<int32_t*>(smem + lay.sb);
   if (alpha > 0) {
     share_plan<NW, NP>(base, lens, a.B, Hi, T, grid, alpha, sb);
@@ -1133,7 +1150,12 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
           nv = nr >= Pol::kNH;
           const int b = __builtin_amdgcn_readlane(sg_b, wave), it = __builtin_amdgcn_readlane(sg_hk, wave);
           const int t = lens[b] - 1;
-          const int page = page_table[(int64_t)b * a.max_pages + (t >> 4)];
+          int page = page_table[(int64_t)b * a.max_pages + (t >> 4)];
+          if (a.err != nullptr && (uint32_t)page >= (uint32_t)a.num_pages) {   // checked: no write
+            chk |= UQ_CHECK_BAD_PAGE;
+            page = 0;
+            nlive = false;
+          }
           const int head = Pol::kNH * it + (nlive ? nr % Pol::kNH : 0);
           nrow.load(nv && nlive ? a.v_new : a.k_new, (int64_t)b * a.Hkv + head, np);
           nblk = const_cast<uint8_t*>(nv && nlive ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes +
@@ -1187,16 +1209,26 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
       const int32_t* pt = page_table + (int64_t)b * a.max_pages + p_begin;
 #pragma unroll
       for (int x = 0; x < 4; ++x) c.ids[x] = x < NP ? pt[min(NP * s + x, npg - 1)] : 0;
+      if (a.err != nullptr) {                    // checked: an id outside the pool reads page 0
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          if ((uint32_t)c.ids[x] >= (uint32_t)a.num_pages) {
+            c.ids[x] = 0;
+            chk |= UQ_CHECK_BAD_PAGE;
+          }
+      }
       const bool full = (NP * s + NP <= npg) && ((NP * s + NP) * kPage <= lrel);
       c.meta = (full ? 1 << 28 : 0) | (k << 20) | s;
       return c;
     };
     auto claim = [&]() { return claim_at(take()); };
     auto load_k = [&](typename Pol::KStep& st, const Claim& c) {
-      Pol::load_k(st, a.k_pool, c.ids, a.page_bytes, PageGeo{c.hk * Pol::kNH, a.Hkv, a.hmask}, r16, j4);
+      Pol::load_k(st, a.k_pool, c.ids, a.page_bytes, PageGeo{c.hk * Pol::kNH, a.Hkv, a.hmask, a.units, a.umask},
+                  r16, j4);
     };
     auto load_v = [&](typename Pol::VStep& st, const Claim& c) {
-      Pol::load_v(st, a.v_pool, c.ids, a.page_bytes, PageGeo{c.hk * Pol::kNH, a.Hkv, a.hmask}, r16, j4);
+      Pol::load_v(st, a.v_pool, c.ids, a.page_bytes, PageGeo{c.hk * Pol::kNH, a.Hkv, a.hmask, a.units, a.umask},
+                  r16, j4);
     };
 
     // ---- prologue: N K and N - 1 V buffers.  K is consumed by the QK at the
@@ -1497,6 +1529,8 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     __syncthreads();                               // LDS is reused by the next round
   }
 
+  if (chk != 0u && lane == 0) __hip_atomic_fetch_or(a.err, chk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
   // rows of empty sequences are zero
   for (int b = wg; b < a.B; b += gridDim.x) {
     if (clamp_len(seq_lens[b], a.max_pages) > 0) continue;
@@ -1565,12 +1599,16 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   k.Hq = a.Hq;
   k.Hkv = a.Hkv;
   k.hmask = a.hmask;
+  k.units = (int32_t)(a.page_bytes >> 8);
+  k.umask = pow2_mask(k.units);
   k.G = a.Hq / a.Hkv;
   k.scale_log2 = a.sm_scale * 1.4426950408889634f;
   k.out = a.out;
   k.ml = reinterpret_cast<float*>(a.ws + L.ml);
   k.po = reinterpret_cast<float*>(a.ws + L.po);
   k.cnt = reinterpret_cast<int32_t*>(a.ws + L.cnt);
+  k.err = a.check ? reinterpret_cast<uint32_t*>(a.ws + L.err) : nullptr;
+  k.num_pages = a.num_pages;
   k.k_new = a.k_new;
   k.v_new = a.v_new;
   k.constopt = a.constopt ? 1 : 0;
@@ -1613,6 +1651,7 @@ DecodeLayout decode_layout(int format, int B, int Hq, int Hkv, int D) {
   const size_t G = 16;   // rows of an item, at most (query heads per KV head, or per KV-head pair)
   DecodeLayout L;
   size_t off = 0;
+  L.err = off; off = align256(off + sizeof(uint32_t));
   L.cnt = off; off = align256(off + sizeof(int32_t) * (size_t)B * Hkv);
   L.ml = off; off = align256(off + sizeof(float) * 2 * (2 * (size_t)kMaxGrid) * G);
   L.po = off; off = align256(off + sizeof(float) * (2 * (size_t)kMaxGrid) * G * D);
@@ -1795,7 +1834,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   }
 
   const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
-  const PageGeo geo{hk, a.Hkv, a.hmask};
+  const PageGeo geo{hk, a.Hkv, a.hmask, 0, -1};   // FP4 pages only
   auto ids_of = [&](int s, int (&ids)[4]) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) ids[x] = pt[max(min(4 * s + x, npages - 1), 0)];   // within the row

@@ -52,6 +52,18 @@ __device__ __forceinline__ int fp4_block_pos(int h, int page, int H, int mask) {
   return (h + 2 * (page % H)) % H;
 }
 
+// FP8 pages rotate their bytes with the page id: byte b of the page laid out as
+// blocks back to back is stored at (b + 256 (page mod units)) mod page_bytes,
+// units = page_bytes / 256 (umask = units - 1 when units is a power of two,
+// else -1).  Every 16-byte load or store stays inside one 256-byte unit.
+__device__ __forceinline__ uint32_t fp8_rot(int page, int units, int umask) {
+  return (uint32_t)(umask >= 0 ? (page & umask) : page % units) << 8;
+}
+__device__ __forceinline__ uint32_t fp8_wrap(uint32_t b, uint32_t rot, uint32_t page_bytes) {
+  const uint32_t x = b + rot;                      // both below page_bytes
+  return x >= page_bytes ? x - page_bytes : x;
+}
+
 template <int D> struct Fp4Block {
   static constexpr int kCodeBytes = kPage * D / 2;          // codes of 16 slots
   static constexpr int kBytes = kCodeBytes + kPage * D / 32; // + one scale byte per group

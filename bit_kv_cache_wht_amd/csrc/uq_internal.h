@@ -26,6 +26,7 @@ struct AppendArgs {
   int64_t page_bytes;         // bytes of one page of one pool
   int32_t T, H;
   int32_t hmask;              // H - 1 when H is a power of two, else -1 (FP4 block positions)
+  int32_t units, umask;       // FP8: page_bytes / 256, and units - 1 when a power of two, else -1
   int32_t constopt;           // FP4: constOpt group scales (UQ_FLAG_SCALE_CONSTOPT)
   Rot rot;                    // FP4: the cache's rotation variant
 };
@@ -40,7 +41,7 @@ hipError_t launch_query(const void* q, int in_dtype, uint8_t* q_fp8, int rows, i
 
 
 struct DecodeLayout {
-  size_t cnt, ml, po, total;   // byte offsets into the workspace
+  size_t err, cnt, ml, po, total;   // byte offsets into the workspace
 };
 
 constexpr int kMaxDecodeSeqs = 8192;   // per-workgroup plan lives in LDS
@@ -63,6 +64,8 @@ struct DecodeArgs {
   float* out;
   uint8_t* ws;
   DecodeLayout lay;
+  bool check;                // UQ_FLAG_CHECK: validate page ids and lengths, report in the error word
+  int32_t num_pages;         // pages in each pool (for the check)
   bool unrotate;             // FP4: rotate the output back (through R^T)
   bool constopt;             // fused FP4 step: constOpt scales for the written token
   Rot rot;                   // FP4: the cache's rotation variant
@@ -90,7 +93,8 @@ struct PrefillArgs {
   Rot rot;                     // the cache's rotation variant
 };
 
-// H - 1 when H is a power of two, else -1 (the FP4 block-position mask).
+// H - 1 when H is a power of two, else -1 (the FP4 block-position and FP8
+// rotation masks).
 inline int32_t pow2_mask(int32_t H) { return H > 0 && (H & (H - 1)) == 0 ? H - 1 : -1; }
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 int prefill_max_seqs();

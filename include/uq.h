@@ -49,20 +49,27 @@
  *   Every call enqueues its kernels on `stream` (NULL = the default stream) and
  *   returns without synchronizing.  Arguments are validated on the host before
  *   any launch; device-resident contents (page ids, slots, lengths) are trusted:
- *   an out-of-range value there is undefined behaviour.
+ *   an out-of-range value there is undefined behaviour, except that the decode
+ *   entry points check page ids and lengths under UQ_FLAG_CHECK.
  *
  * Paged layout (part of the ABI).  A pool is [num_pages][uq_page_bytes]; a page
  * holds the num_kv_heads head-blocks back to back, nothing else (FP4: exactly
  * 17 bytes per 32 elements); token position t of a sequence lives in page
  * page_table[t / 16] at slot t % 16.  The pages fix 17 B per group and paging,
  * not the byte order inside a page; the order below serves the decode's
- * operand loads, and FP4 pages rotate their KV-head pairs so that a pair's
- * blocks start at different offsets modulo 512 B from page to page (on MI355X
- * a pair that always starts at the same such offset can stream more slowly).
+ * operand loads, and FP4 and FP8 pages rotate their contents with the page id
+ * so that blocks start at different offsets from page to page (on MI355X
+ * blocks that always start at the same offset can stream more slowly).
  *   FP4: the block of KV head h in page P is at block position (h + 2P) mod
  *        num_kv_heads (for an even head count, a pair's two blocks stay
  *        adjacent and the pairs rotate by one pair position per page);
- *   FP8, BF16: the block of KV head h is at position h.
+ *   FP8: the page (blocks back to back, head h at position h) is rotated by
+ *        256 bytes per page id: byte b of it is stored at byte
+ *        (b + 256 * (P mod (page_bytes / 256))) mod page_bytes, so that pages
+ *        start their blocks at different offsets modulo 16 KB (FP8 pages of 8
+ *        heads are exactly 16 KB, and the FP8 decode streamed up to 1.5x more
+ *        slowly without it);
+ *   BF16: the block of KV head h is at position h.
  * Head-block layouts (d = head_dim, 16 slots):
  *   FP4  K: codes [16 slot][d/2 B] (byte j: channel 2j low nibble, 2j+1 high),
  *           then scales [slot % 4][d/32 group][slot / 4]       = 17*d/2 bytes
@@ -106,6 +113,22 @@ enum uq_in_dtype { UQ_IN_BF16 = 0, UQ_IN_F32 = 1 };
  * log domain), clamped to [-127, 127], m = 0 giving -127; codes x / 2^E then
  * saturate at +-6.  Without it E is the least integer with m <= 6 * 2^E. */
 #define UQ_FLAG_SCALE_CONSTOPT 2u
+/* Decode entry points with a workspace (uq_decode_attention, _fp8, _bf16 and
+ * uq_append_decode_attention): check the device-resident contents that are
+ * otherwise trusted.  A sequence length outside [0, 16 * max_pages_per_seq]
+ * ORs UQ_CHECK_BAD_LEN, a page id read outside [0, num_pages) ORs
+ * UQ_CHECK_BAD_PAGE into the 32-bit error word at byte offset 0 of the
+ * workspace.  The word is never cleared by the library: zero it before a call
+ * to see that call's findings (it is read after the call, in stream order).
+ * A bad length is used clamped to that range; a bad page id is replaced by
+ * page 0 before any address is formed from it, and the fused step writes no
+ * token into a page whose id is bad, so the call reads and writes only inside
+ * the pools, the page table and its other arguments.  Rows of a sequence with
+ * a bad length or page id are then meaningless.  Without the flag these
+ * contents are trusted and an out-of-range value is undefined behaviour. */
+#define UQ_FLAG_CHECK 4u
+#define UQ_CHECK_BAD_LEN 1u
+#define UQ_CHECK_BAD_PAGE 2u
 
 /* Cache descriptor; read at call time, never retained. */
 /* Rotation variants of an FP4 cache (uq_kv_cache.rotation; 0 = K and V rotated
@@ -133,7 +156,7 @@ typedef struct uq_kv_cache {
   int32_t format;        /* enum uq_kv_format                                   */
   int32_t num_pages;     /* pages in each pool                                  */
   int32_t page_size;     /* tokens per page; must be 16                          */
-  int32_t num_kv_heads;  /* >= 1                                                 */
+  int32_t num_kv_heads;  /* 1 .. 65536                                            */
   int32_t head_dim;      /* 64 or 128                                            */
   void* k_pool;          /* device, [num_pages][uq_page_bytes], 256-B aligned; see
                             "Paged layout" for the block positions in a page     */
@@ -214,8 +237,10 @@ size_t uq_decode_workspace_bytes(const uq_kv_cache* cache, int32_t num_seqs, int
  *               any input; a sequence of length 0 gives a zero row
  *   workspace   device, >= uq_decode_workspace_bytes(...) bytes, 256-B aligned,
  *               zero-filled before its first use; every call leaves it ready for
- *               the next one (no clearing needed).  Calls that overlap in time
- *               must not share a workspace.
+ *               the next one (no clearing needed).  Its first 4 bytes are the
+ *               UQ_FLAG_CHECK error word.  Calls that overlap in time must not
+ *               share a workspace.
+ *   flags       UQ_FLAG_OUT_ROTATED (FP4), UQ_FLAG_CHECK
  * num_q_heads must be a multiple of num_kv_heads with a ratio of 1..16,
  * num_seqs at most 8192, max_pages_per_seq at most 2^21 and
  * num_seqs * ceil(max_pages_per_seq / 4) * num_kv_heads below 2^31 (else

@@ -73,7 +73,7 @@ __all__ = [
     "e4m3_decode", "e4m3_encode", "bf16_bits_to_f64", "f32_to_f64", "bf16_round_bits",
     "head_block_bytes", "page_bytes", "new_pool", "prefill_attention",
     "fp4_block_position", "fp4_k_code_offset", "fp4_k_scale_offset", "fp4_v_code_offset", "fp4_v_scale_offset",
-    "fp8_k_offset", "fp8_v_offset", "bf16_k_index", "bf16_v_index",
+    "fp8_k_offset", "fp8_v_offset", "fp8_page_offset", "bf16_k_index", "bf16_v_index",
     "append", "gather_dequant", "rotate_quantize_query", "attention",
     "decode_attention", "decode_attention_rows",
     "pv_f16_hi_lo", "fold_p_fp8", "pv_fp8_scaled",
@@ -371,13 +371,14 @@ def bf16_round_bits(x32) -> np.ndarray:
 # a page is H_kv blocks back to back, 17 bytes per 32 elements for FP4, with no
 # padding.  The order of bytes inside a page is not fixed by the pages; the
 # layout below serves the decode's operand loads, and the FP4 block positions
-# rotate with the page id, so that a KV-head pair's blocks start at different
-# offsets from page to page.
+# and the FP8 page bytes rotate with the page id, so that blocks start at
+# different offsets from page to page.
 #   FP4: KV head h's block at position (h + 2 page) mod H_kv of page `page`
 #   FP4 K block: codes[16 tok][d/2] (token-major) then scales[tok % 4][d/32][tok // 4]
 #   FP4 V block: codes[d/2 rows][16 tok] (channel pair c in row 16*(c % (d/32)) + c // (d/32))
 #                then scales[d/32 groups][16 tok]
-#   FP8 K block: [16 tok][d] bytes;  FP8 V block: [d][16 tok] bytes
+#   FP8 K block: [16 tok][d] bytes;  FP8 V block: [d][16 tok] bytes; the FP8 page
+#                (blocks back to back) rotated by 256 * page bytes, fp8_page_offset
 #   BF16 K block: [16 tok][d] bf16;  BF16 V block: [d][16 tok] bf16 (little endian)
 # --------------------------------------------------------------------------
 def head_block_bytes(fmt: int, d: int) -> int:
@@ -435,6 +436,18 @@ def fp8_v_offset(tok, ch, d):
     return ch * PAGE_SIZE + tok
 
 
+def fp8_page_offset(head, offset, page, num_kv_heads, d):
+    """Byte of an FP8 page holding byte `offset` of KV head `head`'s block: the
+    page is its blocks back to back, rotated by 256 * page bytes (mod the page
+    size) -- byte b of the unrotated page sits at (b + 256 page) mod page_bytes,
+    so every byte keeps the address modulo 16 KB that a page stride of 16 KB +
+    256 would give it (reading R8)."""
+    pb = num_kv_heads * head_block_bytes(FMT_FP8, d)
+    units = pb // 256
+    b = np.asarray(head, np.int64) * head_block_bytes(FMT_FP8, d) + np.asarray(offset, np.int64)
+    return (b + 256 * (np.asarray(page, np.int64) % units)) % pb
+
+
 def bf16_k_index(tok, ch, d):      # index into the block viewed as uint16
     return tok * d + ch
 
@@ -483,8 +496,10 @@ def append(fmt, k_pool, v_pool, k_new, v_new, slot_mapping, in_dtype="bf16", sca
             b = e4m3_encode(x)
             c = np.arange(d)
             fn = fp8_v_offset if is_v else fp8_k_offset
+            flat_p = pool.reshape(pool.shape[0], -1)
             for h in range(H):
-                flat[page[:, None], h, fn(off[:, None], c[None, :], d)] = b[:, h]
+                pos = fp8_page_offset(h, fn(off[:, None], c[None, :], d), page[:, None], H, d)
+                flat_p[page[:, None], pos] = b[:, h]
         elif fmt == FMT_BF16:
             bits = src[keep].astype(np.uint16) if in_dtype == "bf16" else bf16_round_bits(src[keep])
             c = np.arange(d)
@@ -518,7 +533,8 @@ def gather_dequant(fmt, pool, page_row, seq_len, head, d, is_v) -> np.ndarray:
     c = np.arange(d)[None, :]
     if fmt == FMT_FP8:
         fn = fp8_v_offset if is_v else fp8_k_offset
-        return e4m3_decode(flat[page, head, fn(off, c, d)])
+        flat_p = pool.reshape(pool.shape[0], -1)
+        return e4m3_decode(flat_p[page, fp8_page_offset(head, fn(off, c, d), page, H, d)])
     if fmt == FMT_BF16:
         fn = bf16_v_index if is_v else bf16_k_index
         return bf16_bits_to_f64(flat.view(np.uint16)[page, head, fn(off, c, d)])

@@ -385,6 +385,30 @@ def test_fp4_block_positions_permute_heads_and_rotate_pairs(H):
     assert O.fp4_block_position(3, 0, 8) == 3
 
 
+@pytest.mark.parametrize("H", [1, 3, 8])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_page_rotation_tiles_the_page_like_a_256_byte_stride(H, d):
+    # Reading R8: the FP8 page's bytes (blocks back to back) rotate by 256 bytes
+    # per page id.  Each page is covered once, and a byte's address modulo
+    # 16 KB equals the one a page stride of page_bytes + 256 would give it
+    # (when the page is 16 KB).
+    pb = O.page_bytes(O.FMT_FP8, H, d)
+    tok, ch = np.arange(16)[:, None], np.arange(d)[None, :]
+    for page in (0, 1, 5, 63, 64, 1000, 2 ** 31 - 1):
+        cnt = np.zeros(pb, np.int64)
+        for h in range(H):
+            for fn in (O.fp8_k_offset, O.fp8_v_offset):
+                np.add.at(cnt, O.fp8_page_offset(h, fn(tok, ch, d), page, H, d).ravel(), 1)
+        assert np.all(cnt == 2)                  # K and V offsets each tile the page once
+    if pb == 16384:
+        b = np.arange(pb)
+        h, within = b // O.head_block_bytes(O.FMT_FP8, d), b % O.head_block_bytes(O.FMT_FP8, d)
+        for page in (0, 3, 77):
+            rotated = page * pb + O.fp8_page_offset(h, within, page, H, d)
+            strided = page * (pb + 256) + b
+            assert np.array_equal(rotated % 16384, strided % 16384)
+
+
 # ---------------------------------------------------------------- E4M3 / bf16
 def test_e4m3_decode_matches_torch_all_codes():
     codes = np.arange(256, dtype=np.uint8)
