@@ -43,23 +43,22 @@ def parse():
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="before the warm-up steps, run steps for this long so that the GPU clocks reach their "
                          "sustained-load state (a cold start reads ~5%% slow)")
-    ap.add_argument("--workload", default="decode_gqa", choices=["decode_gqa", "long", "ragged", "tiny"])
+    ap.add_argument("--workloads", default="decode_gqa,long,ragged",
+                    help="decode workloads to time, comma-separated; the first is the headline")
     ap.add_argument("--no-baselines", action="store_true", help="skip the FP8/BF16 KV kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
-    ap.add_argument("--unfused", action="store_true",
-                    help="also time the FP4 step as two launches (append kernel, then decode kernel)")
+    ap.add_argument("--no-append", action="store_true", help="skip the append-only measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time each oracle worker may spend building its pairs' caches before the timed step")
-    ap.add_argument("--scrub-mb", type=int, default=0,
-                    help="read a buffer of this size between the event-timed steps (evicts the last-level cache)")
-    ap.add_argument("--cold-mb", type=int, default=1024,
-                    help="after the warm passes, time the decode kernel again with a read of a buffer of this "
-                         "size before every step (0: skip); reported as the cold kernel time")
-    ap.add_argument("--pmc-pass", action="store_true",
-                    help="run FP4 steps and a 1 GiB device copy only (for rocprofv3 --pmc runs)")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the HBM-traffic summary from two rocprofv3 counter_collection.csv files")
+    ap.add_argument("--scrub-mb", type=int, default=1024,
+                    help="read a buffer of this size before every scrubbed step, so that the 256 MB last-level "
+                         "cache holds no cache page; the headline is the scrubbed step")
+    ap.add_argument("--pmc-pass", choices=sorted(PMC_KINDS),
+                    help="run only one kernel's calls and a 1 GiB device copy (for rocprofv3 --pmc runs)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
+                    help="KIND CSV [CSV ...]: write the counter summary of one --pmc-pass kind from rocprofv3 "
+                         "counter_collection.csv files into profiles/")
     return ap.parse_args()
 
 
@@ -76,7 +75,8 @@ def make_workload(name):
 
 DECODE_SOURCES = ["bit_kv_cache_wht_amd/csrc/uq_decode.hip", "bit_kv_cache_wht_amd/csrc/uq_device.h",
                   "bit_kv_cache_wht_amd/csrc/uq_fp4_row.h", "bit_kv_cache_wht_amd/csrc/uq_internal.h"]
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_fp4_64x8192_hbm_traffic.md")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_SUMMARY = os.path.join(PROFILES, "decode_fp4_64x8192_hbm_traffic.md")
 COPY_BYTES = 1 << 30
 
 
@@ -106,55 +106,116 @@ def recorded_traffic():
         return None
 
 
-def summarize_pmc(fetch_csv, write_csv, workload):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the FP4 decode kernel, each
-    scaled by what the same counter reads for a device copy of COPY_BYTES."""
-    import csv
+# Counter passes (rocprofv3 --pmc), one kernel per kind.  Each pass runs the
+# kernel's calls and then a device copy of COPY_BYTES, which calibrates
+# FETCH_SIZE / WRITE_SIZE; the summary is written by --summarize-pmc.
+PMC_KINDS = {
+    "decode": dict(match=("decode_kernel", "Fp4PairPol"), workload="decode_gqa_64x8192, fused FP4 step",
+                   out="decode_fp4_64x8192_counters.md"),
+    "append": dict(match=("append_fp4_stream_kernel",), workload="append_65536x8x128, bf16 K/V",
+                   out="append_fp4_65536x8_counters.md"),
+    "prefill": dict(match=("prefill_kernel",), workload="ragged_128, 256-token chunks",
+                    out="prefill_fp4_ragged_counters.md"),
+}
+PMC_PASSES = [["FETCH_SIZE"], ["WRITE_SIZE"],
+              ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+              ["SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F6F4", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES"]]
+MI355X_CUS = 256
+MI355X_XCDS = 8
 
-    def per_kernel(path, counter):
-        vals = {}
+
+def read_counters(paths, match):
+    """{counter: [value per dispatch]} of the kernel whose name holds every string
+    of `match`, and {counter: largest value} of the runtime's copy kernel."""
+    import csv
+    kern, copy = {}, {}
+    for path in paths:
         with open(path, newline="") as fh:
             for row in csv.DictReader(fh):
-                if row.get("Counter_Name") != counter:
+                name, counter, value = row.get("Kernel_Name", ""), row.get("Counter_Name"), row.get("Counter_Value")
+                if counter is None or value is None:
                     continue
-                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
-        return vals
+                if all(m in name for m in match):
+                    kern.setdefault(counter, []).append(float(value))
+                elif "copyBuffer" in name:
+                    copy[counter] = max(copy.get(counter, 0.0), float(value))
+    return kern, copy
 
-    out = {}
-    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
-        vals = per_kernel(path, name)
-        dec = [v for k, v in vals.items() if "decode_kernel" in k and ("Fp4Pol" in k or "Fp4PairPol" in k)]
-        cpy = [v for k, v in vals.items() if "copyBuffer" in k]
-        if not dec or not cpy:
-            raise SystemExit(f"{path}: no FP4 decode or copy dispatches for {name}")
-        dec = dec[0]
-        cpy = max(cpy, key=lambda v: max(v))
-        cpy_kib = max(cpy)
-        out[name] = dict(dispatches=len(dec), kib=float(np.mean(dec)), copy_kib=cpy_kib,
-                         factor=COPY_BYTES / (cpy_kib * 1024.0))
-    f, w = out["FETCH_SIZE"], out["WRITE_SIZE"]
-    traffic = int(round(f["kib"] * 1024 * f["factor"] + w["kib"] * 1024 * w["factor"]))
-    lines = [
-        f"# HBM traffic of the FP4 decode kernel (fused step) on {workload}",
-        "",
-        "Counters from two rocprofv3 runs of the same program (one counter each), then",
-        "`python3 bench.py --summarize-pmc <fetch csv> <write csv>`:",
-        "",
-        "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- python3 bench.py --pmc-pass",
-        "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o write -- python3 bench.py --pmc-pass",
-        "",
-        f"Calibration: the largest dispatch of the runtime's copy kernel moves {COPY_BYTES} bytes each way.",
-        "",
-        "| counter | decode dispatches | decode KiB/dispatch | copy KiB | scale factor | decode bytes |",
-        "|---|---|---|---|---|---|",
-    ]
-    for name, r in out.items():
-        lines.append(f"| {name} | {r['dispatches']} | {r['kib']:.0f} | {r['copy_kib']:.0f} | {r['factor']:.4f} | "
-                     f"{r['kib'] * 1024 * r['factor']:.4g} |")
-    lines += ["", f"source_sha256: {decode_source_sha()}", f"traffic_bytes_per_launch: {traffic}", ""]
-    with open(TRAFFIC_SUMMARY, "w") as fh:
+
+def summarize_counters(kind, paths):
+    """Writes profiles/<kind summary>: per-dispatch means of every counter of the
+    kind's kernel, HBM bytes (FETCH_SIZE / WRITE_SIZE scaled by the copy of
+    COPY_BYTES), MFMA busy fraction and instruction mix.  For the decode it also
+    writes the traffic summary the bench's roofline reports."""
+    k = PMC_KINDS[kind]
+    kern, copy = read_counters(paths, k["match"])
+    if not kern:
+        raise SystemExit(f"no dispatches of {' '.join(k['match'])} in {paths}")
+    mean = {c: float(np.mean(v)) for c, v in kern.items()}
+    lines = [f"# Counters of the {kind} kernel on {k['workload']}", "",
+             "Each counter set is one rocprofv3 run of the same program; then",
+             f"`python3 bench.py --summarize-pmc {kind} <csv files>`:", ""]
+    for ctrs in PMC_PASSES:
+        lines.append(f"    rocprofv3 --pmc {' '.join(ctrs)} --output-format csv -d <dir> -o <name> -- "
+                     f"python3 bench.py --pmc-pass {kind}")
+    lines += ["", "| counter | dispatches | mean per dispatch |", "|---|---|---|"]
+    for c in sorted(mean):
+        lines.append(f"| {c} | {len(kern[c])} | {mean[c]:.6g} |")
+    lines += ["", "Derived (per dispatch):", ""]
+    derived = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        if c in mean and copy.get(c):
+            factor = COPY_BYTES / (copy[c] * 1024.0)
+            derived[c] = mean[c] * 1024.0 * factor
+            lines.append(f"- {c}: {mean[c]:.0f} KiB x {factor:.4f} (a {COPY_BYTES}-byte copy reads "
+                         f"{copy[c]:.0f} KiB) = {derived[c]:.4g} bytes")
+    if "FETCH_SIZE" in derived and "WRITE_SIZE" in derived:
+        derived["traffic"] = derived["FETCH_SIZE"] + derived["WRITE_SIZE"]
+        lines.append(f"- HBM traffic: {derived['traffic']:.4g} bytes")
+    if "GRBM_GUI_ACTIVE" in mean:
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs: elapsed cycles = value / 8
+        cycles = mean["GRBM_GUI_ACTIVE"] / MI355X_XCDS
+        lines.append(f"- elapsed: GRBM_GUI_ACTIVE / {MI355X_XCDS} XCDs = {cycles:.4g} cycles "
+                     f"({cycles / 2.4e3:.1f} us at 2.4 GHz)")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * MI355X_CUS * 4)
+            derived["mfma_busy"] = busy
+            lines.append(f"- MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (elapsed cycles x {MI355X_CUS} CUs x 4 SIMDs) = "
+                         f"{busy:.2%}")
+    if mean.get("SQ_INSTS_MFMA"):
+        lines.append(f"- VALU : MFMA instructions = {mean['SQ_INSTS_VALU'] / mean['SQ_INSTS_MFMA']:.2f}")
+    mops = sum(mean.get(c, 0.0) for c in ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F6F4"))
+    if mops:
+        lines.append(f"- MFMA work counted: {mops * 512:.4g} flops (MOPS x 512: f16 "
+                     f"{mean.get('SQ_INSTS_VALU_MFMA_MOPS_F16', 0):.4g}, f8f6f4 "
+                     f"{mean.get('SQ_INSTS_VALU_MFMA_MOPS_F6F4', 0):.4g}; the block-scaled FP4 x FP8 MFMAs of "
+                     f"the QK product read 0 in these MOPS counters)")
+    if kind == "append" and "SQ_INSTS_VALU" in mean:
+        elems = 65536 * 8 * 2 * 128
+        lines.append(f"- VALU lane instructions per element: SQ_INSTS_VALU x 64 / {elems} = "
+                     f"{mean['SQ_INSTS_VALU'] * 64 / elems:.2f}")
+    lines += ["", f"source_sha256: {decode_source_sha()}", ""]
+    out = os.path.join(PROFILES, k["out"])
+    with open(out, "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
+    if kind == "decode" and "traffic" in derived:
+        write_traffic_summary(derived, kern, copy)
+    return derived
+
+
+def write_traffic_summary(derived, kern, copy):
+    lines = ["# HBM traffic of the FP4 decode kernel (fused step) on decode_gqa", "",
+             "From the FETCH_SIZE and WRITE_SIZE passes of `python3 bench.py --pmc-pass decode` (see",
+             "decode_fp4_64x8192_counters.md), each scaled by what the counter reads for a device copy of",
+             f"{COPY_BYTES} bytes.", "",
+             "| counter | decode dispatches | decode bytes |", "|---|---|---|"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        lines.append(f"| {c} | {len(kern[c])} | {derived[c]:.4g} |")
+    lines += ["", f"source_sha256: {decode_source_sha()}", f"traffic_bytes_per_launch: {int(round(derived['traffic']))}",
+              ""]
+    with open(TRAFFIC_SUMMARY, "w") as fh:
+        fh.write("\n".join(lines))
 
 
 def stream_read_gbs(reps=20):
@@ -268,22 +329,27 @@ def prefill_throughput(reps, warmup):
 
 
 def pmc_pass(args):
-    """FP4 steps on the workload, then a plain device copy of known size."""
+    """One kernel's calls (the --pmc-pass kind), then a plain device copy of
+    COPY_BYTES that calibrates the traffic counters."""
     import torch
     torch.cuda.set_device(0)
-    wl = make_workload(args.workload)
-    r = Runner("fp4", wl, fused=True)
-    for _ in range(args.warmup + args.steps):
-        r.step()
-    torch.cuda.synchronize()
-    del r
+    if args.pmc_pass == "decode":
+        r = Runner("fp4", make_workload("decode_gqa"), fused=True)
+        for _ in range(args.warmup + args.steps):
+            r.step()
+        torch.cuda.synchronize()
+        del r
+    elif args.pmc_pass == "append":
+        append_throughput(args.steps, args.warmup, 0.0)
+    else:
+        prefill_throughput(max(3, args.steps // 10), 1)
     torch.cuda.empty_cache()
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    log("pmc pass done")
+    log(f"pmc pass ({args.pmc_pass}) done")
 
 
 def fp4_kv_bytes_per_token_head(d):
@@ -359,26 +425,33 @@ class Runner:
             self.v_new = self.v_new.reshape(wl.batch, wl.num_kv_heads, d)
         torch.cuda.synchronize()
 
-    def step(self, ev=None):
+    def step(self, ev=None, ev_app=None):
+        """One step; `ev`: a hipEvent_t pair the library records around its decode
+        kernel; `ev_app`: torch events recorded around the append launch."""
         if self.fused:
             if ev is not None:
                 self.uq.uq_profile_next_decode(ev[0], ev[1])
             self.uq.uq_append_decode_attention(self.cache, self.k_new, self.v_new, self.q, self.page_table,
                                                self.seq_lens, self.sm_scale, self.out, self.ws)
             return
+        if ev_app is not None:
+            ev_app[0].record()
         self.append(self.cache, self.k_new, self.v_new, self.slots_new)
+        if ev_app is not None:
+            ev_app[1].record()
         if ev is not None:
             self.uq.uq_profile_next_decode(ev[0], ev[1])
         self.decode(self.cache, self.q, self.page_table, self.seq_lens, self.sm_scale, self.out, self.ws)
 
-    def run(self, steps, warmup, scrub=None, settle_s=0.0, cold=None):
-        """After `settle_s` seconds of untimed steps and `warmup` more, pass 1
-        times `steps` whole steps back to back with nothing else in the timed
-        region.  Pass 2 repeats them with HIP events that the library records
-        around its decode kernel, on the kernel's own stream; with `scrub` (a device
-        tensor) a read of it between steps, outside the events, evicts the
-        last-level cache first.  With `cold` (a device tensor) pass 3 does the
-        same with that read between every two steps."""
+    def run(self, steps, warmup, scrub=None, settle_s=0.0):
+        """After `settle_s` seconds of untimed steps and `warmup` more:
+        - warm: `steps` whole steps back to back between two HIP events (nothing
+          else in the timed region);
+        - scrubbed: `steps` steps each preceded by a read of `scrub` (a device
+          tensor larger than the last-level cache, outside the timed events),
+          timed in three passes by events on the launch stream: around the
+          whole step, around the decode kernel alone (recorded by the library)
+          and around the append launch of a two-launch step."""
         torch = self.torch
         t_settle = time.perf_counter()
         while time.perf_counter() - t_settle < settle_s:
@@ -388,8 +461,8 @@ class Runner:
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        t0, t1 = ev(), ev()
         wall0 = time.perf_counter()
         t0.record()
         for _ in range(steps):
@@ -397,43 +470,61 @@ class Runner:
         t1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-        ms_step = t0.elapsed_time(t1) / steps
-        evs = HipEvents(steps)
+        res = dict(warm_ms_per_step=t0.elapsed_time(t1) / steps, wall_ms_per_step=1e3 * wall / steps)
+        # whole steps and single kernels are timed in separate passes, so that no
+        # step carries more than one pair of events
+        whole = [(ev(), ev()) for _ in range(steps)]
         for i in range(steps):
             if scrub is not None:
                 scrub.max()                        # a read: evicts without leaving dirty lines
+            whole[i][0].record()
+            self.step()
+            whole[i][1].record()
+        torch.cuda.synchronize()
+        evs = HipEvents(steps)
+        for i in range(steps):
+            if scrub is not None:
+                scrub.max()
             self.step(evs.pairs[i])
         torch.cuda.synchronize()
-        k_ms = [evs.elapsed_ms(i) for i in range(steps)]
-        res = dict(ms_per_step=ms_step, wall_ms_per_step=1e3 * wall / steps,
-                   decode_kernel_ms=float(np.mean(k_ms)), decode_kernel_ms_median=float(np.median(k_ms)),
-                   decode_kernel_ms_p10=float(np.percentile(k_ms, 10)),
-                   decode_kernel_ms_p90=float(np.percentile(k_ms, 90)))
-        if cold is not None:
+        app = None
+        if not self.fused:
+            app = [(ev(), ev()) for _ in range(steps)]
             for i in range(steps):
-                cold.max()                         # a read of >= 1 GiB: the 256 MB last-level cache holds none of the pages
-                self.step(evs.pairs[i])
+                if scrub is not None:
+                    scrub.max()
+                self.step(None, app[i])
             torch.cuda.synchronize()
-            res["decode_kernel_ms_cold"] = float(np.mean([evs.elapsed_ms(i) for i in range(steps)]))
+        stat = lambda v: dict(mean=float(np.mean(v)), median=float(np.median(v)), p10=float(np.percentile(v, 10)),
+                              p90=float(np.percentile(v, 90)))
+        res["step_ms"] = stat([a.elapsed_time(b) for a, b in whole])
+        res["decode_ms"] = stat([evs.elapsed_ms(i) for i in range(steps)])
+        if app is not None:
+            res["append_ms"] = stat([a.elapsed_time(b) for a, b in app])
         evs.close()
         return res
 
     def kernel_bytes(self):
-        """Algorithmic bytes of one launch of the split-K attention kernel: every
-        cached K/V byte of every context token once, the query operand and the
-        page-table entries, and for the fused step the new tokens' K/V rows read
-        and their cache bytes written; split partials are overhead and not
-        counted."""
+        """Algorithmic bytes of one decode launch -- every cached K/V byte of every
+        context token once, the query as read, the output written, the page-table
+        entries of the context, and for the fused step the new tokens' K/V rows
+        read and their cache bytes written -- and of one append launch of a
+        two-launch step (new rows read, cache bytes and slots); split partials
+        are overhead and not counted."""
         wl = self.wl
         d = wl.head_dim
-        tok_heads = int(np.sum(wl.seq_lens.astype(np.int64))) * wl.num_kv_heads
-        kv = tok_heads * KV_BYTES[self.fmt](d)
-        q = wl.batch * wl.num_q_heads * d * (2 if self.fmt == "bf16" else 1)
-        pt = int(np.sum((wl.seq_lens.astype(np.int64) + 15) // 16)) * 4
-        if self.fused:
-            in_bytes = 2 if wl.in_dtype == "bf16" else 4
-            pt += wl.batch * wl.num_kv_heads * (2 * d * in_bytes + KV_BYTES["fp4"](d))
-        return kv + q + pt, kv
+        in_bytes = 2 if wl.in_dtype == "bf16" else 4
+        lens = wl.seq_lens.astype(np.int64)
+        kv = int(lens.sum()) * wl.num_kv_heads * KV_BYTES[self.fmt](d)
+        q = wl.batch * wl.num_q_heads * d * in_bytes
+        out = wl.batch * wl.num_q_heads * d * 4
+        pt = int(((lens + 15) // 16).sum()) * 4
+        new_rows = int(wl.new_lens.astype(np.int64).sum()) * wl.num_kv_heads
+        row_write = KV_BYTES[self.fmt](d)                 # K and V cache bytes of one (token, head)
+        new = new_rows * (2 * d * in_bytes + row_write)
+        decode = kv + q + out + pt + (new if self.fused else 0)
+        append = 0 if self.fused else new + int(wl.new_lens.sum()) * 4
+        return dict(decode=decode, append=append, kv=kv, new_rows=new_rows)
 
 
 def _oracle_pair_prepare(wl, pair):
@@ -523,10 +614,61 @@ def cpu_baseline(wl, budget_s):
                       f"float64 numpy; wall time scaled to the whole step (prefix quantization untimed)"}
 
 
+def describe(wl):
+    lens = wl.seq_lens
+    ctx = f"{int(lens.min())}..{int(lens.max())}" if lens.min() != lens.max() else f"{int(lens.max())}"
+    new = int(wl.new_lens.max())
+    return (f"{wl.name}: {wl.batch} seq x {ctx} ctx, {wl.num_q_heads} q heads / {wl.num_kv_heads} kv heads, "
+            f"head_dim {wl.head_dim}, 16-token pages permuted; step = append of {new} new token(s) per seq + decode")
+
+
+def time_workload(args, wl, fmts, torch):
+    """Per format: the step timed warm and scrubbed (see Runner.run), with the
+    decode kernel's rate against the HBM peak."""
+    out = {}
+    for fmt in fmts:
+        log(f"{wl.name} {fmt}: prefill + timing")
+        r = Runner(fmt, wl, fused=fmt == "fp4")
+        scrub = torch.ones((args.scrub_mb << 20) // 4, dtype=torch.int32, device="cuda") if args.scrub_mb else None
+        res = r.run(args.steps, args.warmup, scrub, settle_s=args.settle_ms * 1e-3)
+        by = r.kernel_bytes()
+        dec_us = res["decode_ms"]["mean"] * 1e3
+        e = {
+            "us_per_step": round(res["step_ms"]["median"] * 1e3, 2),
+            "us_per_step_p10_p90": [round(res["step_ms"]["p10"] * 1e3, 2), round(res["step_ms"]["p90"] * 1e3, 2)],
+            "us_per_step_warm": round(res["warm_ms_per_step"] * 1e3, 2),
+            "fused": r.fused,
+            "decode_kernel_us": round(dec_us, 2),
+            "decode_kernel_us_median": round(res["decode_ms"]["median"] * 1e3, 2),
+            "decode_algo_bytes": by["decode"],
+            "decode_gbs": round(by["decode"] / (dec_us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(by["decode"] / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "kv_bytes": by["kv"],
+        }
+        if r.fused:
+            # one launch per step: the warm region times the kernel back to back
+            e["decode_gbs_warm"] = round(by["decode"] / (res["warm_ms_per_step"] * 1e-3) / 1e9, 1)
+            e["frac_hbm_peak_warm"] = round(e["decode_gbs_warm"] / HBM_PEAK_GBS, 4)
+        if "append_ms" in res:
+            app_us = res["append_ms"]["mean"] * 1e3
+            toks = int(wl.new_lens.sum())
+            e["append_us"] = round(app_us, 2)
+            e["append_tokens_per_s"] = round(toks / (app_us * 1e-6))
+            e["append_algo_bytes"] = by["append"]
+            e["append_gbs"] = round(by["append"] / (app_us * 1e-6) / 1e9, 1)
+        out[fmt] = e
+        log(f"{wl.name} {fmt}: {e['us_per_step']} us/step scrubbed ({e['us_per_step_warm']} warm), decode kernel "
+            f"{e['decode_kernel_us']} us = {e['decode_gbs']} GB/s ({e['frac_hbm_peak']:.1%})"
+            + (f", append {e['append_us']} us" if "append_us" in e else ""))
+        del r, scrub
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+        summarize_counters(args.summarize_pmc[0], args.summarize_pmc[1:])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this hot path needs no "
@@ -535,95 +677,76 @@ def main():
     if args.pmc_pass:
         pmc_pass(args)
         return
-    import torch
-    log(f"generating workload {args.workload}")
+    names = [w for w in args.workloads.split(",") if w]
+    log(f"generating workload {names[0]}")
     t = time.perf_counter()
-    wl = make_workload(args.workload)
+    wl = make_workload(names[0])
     log(f"workload ready in {time.perf_counter() - t:.1f}s: B={wl.batch} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
         f"d={wl.head_dim} tokens={wl.total_tokens}")
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline (oracle on {oracle_cores()} host cores; before the GPU is touched)")
         cpu = cpu_baseline(wl, args.cpu_seconds)
+    import torch
     torch.cuda.set_device(0)
-    results = {}
-    fmts = ["fp4"] + ([] if args.no_baselines else ["fp8", "bf16"]) + (["fp4_unfused"] if args.unfused else [])
-    for fmt in fmts:
-        log(f"{fmt}: prefill + timing")
-        r = Runner(fmt.split("_")[0], wl, fused=fmt == "fp4")
-        scrub = torch.ones((args.scrub_mb << 20) // 4, dtype=torch.int32, device="cuda") if args.scrub_mb else None
-        cold = torch.ones((args.cold_mb << 20) // 4, dtype=torch.int32, device="cuda") if args.cold_mb else None
-        res = r.run(args.steps, args.warmup, scrub, settle_s=args.settle_ms * 1e-3, cold=cold)
-        algo, kv = r.kernel_bytes()
-        # A fused step is exactly one launch of the decode kernel, so HIP events
-        # around the K back-to-back steps time K launches (gaps included); event
-        # pairs around single launches add their own ~2 us and are kept as a
-        # cross-check.  Unfused steps hold two kernels: event pairs only.
-        res["kernel_region"] = r.fused and scrub is None
-        res["kernel_ms"] = res["ms_per_step"] if res["kernel_region"] else res["decode_kernel_ms"]
-        res["kernel_gbs"] = algo / (res["kernel_ms"] * 1e-3) / 1e9
-        res["kernel_algo_bytes"] = algo
-        res["kv_bytes"] = kv
-        res["fused"] = r.fused
-        results[fmt] = res
-        log(f"{fmt}: {1e3 * res['ms_per_step']:.1f} us/step, decode kernel {1e3 * res['kernel_ms']:.1f} us "
-            f"= {res['kernel_gbs']:.0f} GB/s (event pairs {1e3 * res['decode_kernel_ms']:.1f} us)")
-        del r, scrub, cold
-        torch.cuda.empty_cache()
-
-    fp4 = results["fp4"]
-    fused_fp4 = fp4["fused"]
+    fmts = ["fp4"] + ([] if args.no_baselines else ["fp8", "bf16"])
+    results, descr, shape = {}, {}, {}
+    for i, name in enumerate(names):
+        if i > 0:
+            log(f"generating workload {name}")
+            wl = make_workload(name)
+        descr[name] = describe(wl)
+        shape[name] = (int(wl.batch), int(wl.seq_lens.max()))
+        results[name] = time_workload(args, wl, fmts, torch)
+        del wl
+    head = results[names[0]]["fp4"]
+    fused = head["fused"]
+    traffic = recorded_traffic() if names[0] == "decode_gqa" else None
     line = {
         "metric": METRIC,
-        "value": round(fp4["ms_per_step"] * 1e3, 2),
+        "value": head["us_per_step"],
         "unit": "us/step",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "settle_ms": args.settle_ms,
-        "ms_per_step": round(fp4["ms_per_step"], 5),
+        "ms_per_step": round(head["us_per_step"] * 1e-3, 5),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp4_e2m1xfp8_e4m3->f32 (f16 PV)",
         "data": "synthetic (seeded Gaussian K/V with outlier channels, permuted pages)",
-        "config": {"workload": f"{wl.name}: {wl.batch} seq x {int(wl.seq_lens.max())} ctx, {wl.num_q_heads} q heads / "
-                               f"{wl.num_kv_heads} kv heads, head_dim {wl.head_dim}, 16-token pages permuted; step = "
-                               f"FP4 append of the new token(s) of every seq + decode"
-                               + (" in one fused launch" if fused_fp4 else ""),
-                   "global_batch": wl.batch, "seq_len": int(wl.seq_lens.max()), "parallelism": "none (1 GPU)"},
-        "kv_gbs_per_step": round(fp4["kv_bytes"] / (fp4["ms_per_step"] * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "hbm", "achieved": round(fp4["kernel_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(fp4["kernel_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic() if args.workload == "decode_gqa" else None,
-                     "kernel": "decode_kernel<Fp4PairPol<128>> (KV-head pairs" + (", fused append)" if fused_fp4 else ")"),
-                     "kernel_us": round(fp4["kernel_ms"] * 1e3, 2),
-                     "timing": ("HIP events on the launch stream around the K timed steps, one launch each"
-                                if fp4["kernel_region"] else
-                                "HIP events around each launch on its stream"
-                                + (f", {args.scrub_mb} MB scrub between steps" if args.scrub_mb else "")),
-                     "kernel_us_event_pairs": round(fp4["decode_kernel_ms"] * 1e3, 2),
-                     "kernel_us_event_pairs_cold": (round(fp4["decode_kernel_ms_cold"] * 1e3, 2)
-                                                    if "decode_kernel_ms_cold" in fp4 else None),
-                     "kernel_us_event_pairs_median": round(fp4["decode_kernel_ms_median"] * 1e3, 2),
-                     "kernel_us_event_pairs_p10_p90": [round(fp4["decode_kernel_ms_p10"] * 1e3, 2),
-                                                       round(fp4["decode_kernel_ms_p90"] * 1e3, 2)],
-                     "algo_bytes_per_launch": fp4["kernel_algo_bytes"]},
-        "baselines": {f: {"us_per_step": round(results[f]["ms_per_step"] * 1e3, 2),
-                          "decode_kernel_us": round(results[f]["kernel_ms"] * 1e3, 2),
-                          "decode_kernel_us_event_pairs_cold": (round(results[f]["decode_kernel_ms_cold"] * 1e3, 2)
-                                                                if "decode_kernel_ms_cold" in results[f] else None),
-                          "kernel_gbs": round(results[f]["kernel_gbs"], 1),
-                          "frac_hbm_peak": round(results[f]["kernel_gbs"] / HBM_PEAK_GBS, 4)}
-                      for f in results if f != "fp4"},
+        "timing": (f"value: median over {args.steps} steps, each preceded by a read of a {args.scrub_mb} MB buffer "
+                   "(outside the timed events) so that no cache page is in the 256 MB last-level cache; HIP "
+                   "events on the launch stream around each whole step.  value_warm: the same steps back to "
+                   "back, HIP events around all of them"),
+        "value_warm": head["us_per_step_warm"],
+        "config": {"workload": descr[names[0]] + (" in one fused launch" if fused else ""),
+                   "global_batch": shape[names[0]][0], "seq_len": shape[names[0]][1],
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": head["decode_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["frac_hbm_peak"], "traffic": traffic,
+                     "kernel": "decode_kernel<Fp4PairPol<128>> (KV-head pairs" + (", fused append)" if fused else ")"),
+                     "kernel_us": head["decode_kernel_us"],
+                     "timing": "mean over the scrubbed steps of HIP events the library records on the launch "
+                               "stream right before and after the kernel launch",
+                     "achieved_warm": head.get("decode_gbs_warm"), "frac_warm": head.get("frac_hbm_peak_warm"),
+                     "algo_bytes_per_launch": head["decode_algo_bytes"]},
+        "baselines": {f: {"us_per_step": results[names[0]][f]["us_per_step"],
+                          "us_per_step_warm": results[names[0]][f]["us_per_step_warm"],
+                          "decode_kernel_us": results[names[0]][f]["decode_kernel_us"],
+                          "kernel_gbs": results[names[0]][f]["decode_gbs"],
+                          "frac_hbm_peak": results[names[0]][f]["frac_hbm_peak"]}
+                      for f in fmts if f != "fp4"},
+        "workloads": {n: dict(description=descr[n], **results[n]) for n in names},
     }
     sr = stream_read_gbs()
     line["roofline"]["stream_read_gbs"] = round(sr["uq_stream_read"], 1)
     line["roofline"]["torch_max_read_gbs"] = round(sr["torch_max"], 1)
-    line["roofline"]["frac_of_stream_read"] = round(fp4["kernel_gbs"] / sr["uq_stream_read"], 4)
+    line["roofline"]["frac_of_stream_read"] = round(head["decode_gbs"] / sr["uq_stream_read"], 4)
     log(f"streaming read reference: {sr['uq_stream_read']:.0f} GB/s (torch max {sr['torch_max']:.0f}); "
-        f"FP4 decode at {fp4['kernel_gbs'] / sr['uq_stream_read']:.2%} of it")
-    if not args.no_baselines:
+        f"FP4 decode at {head['decode_gbs'] / sr['uq_stream_read']:.2%} of it")
+    if not args.no_append:
         log("append throughput (FP4 write path alone)")
         line["append"] = append_throughput(args.steps, args.warmup, args.settle_ms * 1e-3)
         log(f"append: {line['append']['us_per_call']} us per call, "
