@@ -57,6 +57,17 @@ Readings where the pages are silent (each listed with its reason in the design doc):
       is R = c_d H_d diag(s) with one caller-drawn s in {+1, -1}^d per cache,
       applied to K, V and the query alike; the output goes back through
       R^T = diag(s) c_d H_d.  Without signs R is the plain R2 transform.
+  R13 Scaled-MFMA PV (``pv_scaled``; [review] §3.2 "dequantization rule과
+      scaled-MFMA", §6.3 optimization ladder; [commentary] footnote 2: the
+      scaled matrix instruction takes FP4 codes with UE8M0 scales, so values
+      are never widened to BF16).  V's scales run along head_dim while PV
+      contracts over tokens, so they enter the product folded into FP8
+      probabilities: per 32-channel group and block of 32 tokens, P * 2^(E_t - M)
+      rounded to E4M3 with the block scale 2^M, M = the block's largest V
+      exponent minus 8 (at least -127).  For the rounding not to depend on the
+      order in which steps are visited, P is taken within each 128-token step
+      (positions 128 s .. 128 s + 127) against that step's largest logit; the
+      steps are combined as in the online softmax, with unrounded sums of P.
 
 Parity pins: tests/test_oracle_pins.py (no function here is "parity unpinned").
 """
@@ -76,7 +87,8 @@ __all__ = [
     "fp8_k_offset", "fp8_v_offset", "fp8_page_offset", "bf16_k_index", "bf16_v_index",
     "append", "gather_dequant", "rotate_quantize_query", "attention",
     "decode_attention", "decode_attention_rows",
-    "pv_f16_hi_lo", "fold_p_fp8", "pv_fp8_scaled",
+    "pv_f16_hi_lo", "fold_p_fp8", "pv_fp8_scaled", "SPV_STEP", "SPV_HEADROOM", "attention_pv_scaled",
+    "gather_fp4_codes",
 ]
 
 PAGE_SIZE = 16          # tokens per page (vLLM-style paged cache; [review] §6.5.1)
@@ -511,6 +523,26 @@ def append(fmt, k_pool, v_pool, k_new, v_new, slot_mapping, in_dtype="bf16", sca
             raise ValueError(fmt)
 
 
+def gather_fp4_codes(pool, page_row, seq_len, head, d, is_v):
+    """FP4 codes [seq_len][d] (0..15) and scale bytes [seq_len][d/32] of one KV
+    head of one sequence: token t lives in page page_row[t // 16] at offset t % 16."""
+    t = np.arange(seq_len)
+    page = np.asarray(page_row, dtype=np.int64)[t // PAGE_SIZE][:, None]
+    off = (t % PAGE_SIZE)[:, None]
+    H = pool.shape[1]
+    flat = pool.reshape(pool.shape[0], H, -1)
+    j = np.arange(d // 2)[None, :]
+    g = np.arange(d // GROUP)[None, :]
+    pos = fp4_block_position(head, page, H)
+    if is_v:
+        packed = flat[page, pos, fp4_v_code_offset(off, j, d)]
+        sb = flat[page, pos, fp4_v_scale_offset(off, g, d)]
+    else:
+        packed = flat[page, pos, fp4_k_code_offset(off, j, d)]
+        sb = flat[page, pos, fp4_k_scale_offset(off, g, d)]
+    return unpack_nibbles(packed), sb
+
+
 def gather_dequant(fmt, pool, page_row, seq_len, head, d, is_v) -> np.ndarray:
     """Dequantized [seq_len][d] rows of one KV head of one sequence: token t lives
     in page page_row[t // 16] at offset t % 16."""
@@ -520,16 +552,7 @@ def gather_dequant(fmt, pool, page_row, seq_len, head, d, is_v) -> np.ndarray:
     H = pool.shape[1]
     flat = pool.reshape(pool.shape[0], H, -1)
     if fmt == FMT_FP4:
-        j = np.arange(d // 2)[None, :]
-        g = np.arange(d // GROUP)[None, :]
-        pos = fp4_block_position(head, page, H)
-        if is_v:
-            packed = flat[page, pos, fp4_v_code_offset(off, j, d)]
-            sb = flat[page, pos, fp4_v_scale_offset(off, g, d)]
-        else:
-            packed = flat[page, pos, fp4_k_code_offset(off, j, d)]
-            sb = flat[page, pos, fp4_k_scale_offset(off, g, d)]
-        return dequantize_fp4(unpack_nibbles(packed), sb)
+        return dequantize_fp4(*gather_fp4_codes(pool, page_row, seq_len, head, d, is_v))
     c = np.arange(d)[None, :]
     if fmt == FMT_FP8:
         fn = fp8_v_offset if is_v else fp8_k_offset
@@ -581,25 +604,26 @@ def pv_f16_hi_lo(p, v) -> np.ndarray:
     return hi @ v16 + lo @ v16
 
 
-def fold_p_fp8(p, exps, block=32) -> np.ndarray:
+def fold_p_fp8(p, exps, block=32, headroom=0) -> np.ndarray:
     """The B operand of a scaled-MFMA PV for one 32-channel group: V's per-token
-    exponent E_t folded into the probabilities, normalized by the largest E of
-    each block of 32 tokens (that block's UE8M0 operand scale 2^M) and rounded
-    to E4M3.  p [R][T], exps [T] (V's group exponents) -> the rounded operand
-    times 2^M, [R][T] (so that sum_t result[r, t] * code[t] is the PV)."""
+    exponent E_t folded into the probabilities, normalized by M = (the largest E
+    of each block of 32 tokens) - ``headroom``, at least -127 (that block's
+    UE8M0 operand scale 2^M), and rounded to E4M3.  p [R][T], exps [T] (V's
+    group exponents) -> the rounded operand times 2^M, [R][T] (so that
+    sum_t result[r, t] * code[t] is the PV)."""
     p = np.asarray(p, dtype=np.float64)
     e = np.asarray(exps, dtype=np.int64)
     T = e.size
     out = np.zeros_like(p)
     for b0 in range(0, T, block):
         sl = slice(b0, min(b0 + block, T))
-        M = int(e[sl].max())
+        M = max(int(e[sl].max()) - headroom, -127)
         folded = np.ldexp(p[:, sl], (e[sl] - M)[None, :])
         out[:, sl] = np.ldexp(e4m3_decode(e4m3_encode(folded)), M)
     return out
 
 
-def pv_fp8_scaled(p, codes, scale_bytes) -> np.ndarray:
+def pv_fp8_scaled(p, codes, scale_bytes, headroom=0) -> np.ndarray:
     """sum_t P[r, t] V[t, c] computed as the scaled-MFMA PV would: FP4 codes as the
     A operand (scale 1), and per 32-channel group g the probabilities folded with
     V's exponents of that group (``fold_p_fp8``) as the FP8 B operand.
@@ -611,22 +635,64 @@ def pv_fp8_scaled(p, codes, scale_bytes) -> np.ndarray:
     out = np.zeros((np.asarray(p).shape[0], d))
     for g in range(d // GROUP):
         cs = slice(GROUP * g, GROUP * (g + 1))
-        out[:, cs] = fold_p_fp8(p, e[:, g]) @ vals[:, cs]
+        out[:, cs] = fold_p_fp8(p, e[:, g], headroom=headroom) @ vals[:, cs]
     return out
 
 
+# The decode with the scaled-MFMA PV (reading R13): softmax steps of SPV_STEP
+# tokens at positions SPV_STEP * s .. of the sequence; the largest folded
+# probability is 2^SPV_HEADROOM (E4M3 reaches 448).
+SPV_STEP = 128
+SPV_HEADROOM = 8
+
+
+def attention_pv_scaled(qhat, k, v_codes, v_scale_bytes, sm_scale, step=SPV_STEP, fold=True) -> np.ndarray:
+    """softmax(sm_scale * qhat k^T) V for one KV head with the PV of each step of
+    ``step`` tokens on the scaled FP8 x FP4 product (R13): within the step the
+    probabilities are taken against the step's own largest logit of each row, so
+    that each is at most 1; per 32-channel group and 32-token block they are
+    folded with V's exponents (headroom SPV_HEADROOM) and rounded to E4M3, and
+    multiplied by V's FP4 codes.  The steps' products and their unrounded
+    probability sums are then combined, each weighted by exp(its maximum minus
+    the overall maximum), and the output is their quotient.  ``fold=False``
+    takes the exact product instead (no rounding), which makes the result the
+    plain softmax attention.  qhat [G][d], k [L][d], v_codes [L][d] (0..15),
+    v_scale_bytes [L][d/32] -> [G][d]."""
+    s = sm_scale * (np.asarray(qhat, dtype=np.float64) @ np.asarray(k, dtype=np.float64).T)   # [G][L]
+    G, L = s.shape
+    d = np.asarray(v_codes).shape[1]
+    m = np.full(G, -np.inf)
+    l = np.zeros(G)
+    o = np.zeros((G, d))
+    for t0 in range(0, L, step):
+        blk = slice(t0, min(t0 + step, L))
+        ms = s[:, blk].max(axis=1)
+        p = np.exp(s[:, blk] - ms[:, None])
+        if fold:
+            ostep = pv_fp8_scaled(p, v_codes[blk], v_scale_bytes[blk], headroom=SPV_HEADROOM)
+        else:
+            ostep = p @ dequantize_fp4(v_codes[blk], v_scale_bytes[blk])
+        mn = np.maximum(m, ms)
+        a, b = np.exp(m - mn), np.exp(ms - mn)
+        o = o * a[:, None] + ostep * b[:, None]
+        l = l * a + p.sum(axis=1) * b
+        m = mn
+    return o / l[:, None]
+
+
 def decode_attention_rows(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table, seq_lens,
-                          sm_scale, rows, in_dtype="bf16", k_only=False, signs=None) -> np.ndarray:
+                          sm_scale, rows, in_dtype="bf16", k_only=False, signs=None, pv_scaled=False) -> np.ndarray:
     """Output rows for the (sequence, query head) pairs in ``rows`` ([n][2]).
 
     FP4: q rotated and rounded to E4M3, output rotated back with the transpose of
     the rotation (R2's normalized WHT is its own inverse); with ``k_only`` (R11)
-    the output stays as attended, V being unrotated; ``signs`` as in R12.  FP8:
-    q rounded to E4M3, no rotation; BF16: q as given.  A sequence of length 0
-    gives a zero row.
+    the output stays as attended, V being unrotated; ``signs`` as in R12;
+    ``pv_scaled`` takes the scaled-MFMA PV of R13 (``attention_pv_scaled``).
+    FP8: q rounded to E4M3, no rotation; BF16: q as given.  A sequence of length
+    0 gives a zero row.
     """
-    if fmt != FMT_FP4 and (k_only or signs is not None):
-        raise ValueError("rotation variants apply to the FP4 cache only")
+    if fmt != FMT_FP4 and (k_only or signs is not None or pv_scaled):
+        raise ValueError("rotation variants and the scaled PV apply to the FP4 cache only")
     q = np.asarray(q)
     Hq = q.shape[1]
     group = Hq // num_kv_heads
@@ -640,8 +706,9 @@ def decode_attention_rows(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table, s
         hk = h // group
         key = (b, hk)
         if key not in cache:
-            cache = {key: (gather_dequant(fmt, k_pool, page_table[b], L, hk, d, False),
-                           gather_dequant(fmt, v_pool, page_table[b], L, hk, d, True))}
+            V = (gather_fp4_codes(v_pool, page_table[b], L, hk, d, True) if pv_scaled
+                 else gather_dequant(fmt, v_pool, page_table[b], L, hk, d, True))
+            cache = {key: (gather_dequant(fmt, k_pool, page_table[b], L, hk, d, False), V)}
         K, V = cache[key]
         if fmt == FMT_FP4:
             qhat = e4m3_decode(rotate_quantize_query(q[b, h], in_dtype, signs))
@@ -649,13 +716,16 @@ def decode_attention_rows(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table, s
             qhat = e4m3_decode(e4m3_encode(to64(q[b, h])))
         else:
             qhat = to64(q[b, h])
-        o = attention(qhat[None, :], K, V, float(sm_scale))[0]
+        if pv_scaled:
+            o = attention_pv_scaled(qhat[None, :], K, V[0], V[1], float(sm_scale))[0]
+        else:
+            o = attention(qhat[None, :], K, V, float(sm_scale))[0]
         out[n] = unrotate(o, signs) if (fmt == FMT_FP4 and not k_only) else o
     return out
 
 
 def prefill_attention(fmt, k_pool, v_pool, num_kv_heads, d, q, q_lens, page_table, seq_lens,
-                      sm_scale, in_dtype="bf16", k_only=False, signs=None) -> np.ndarray:
+                      sm_scale, in_dtype="bf16", k_only=False, signs=None, pv_scaled=False) -> np.ndarray:
     """Causal attention of chunks of query tokens over the cache ([review] §1 and
     §5.4: a new turn's tokens read the resident prefix instead of re-prefilling
     it; reading R10).  q [T_q][H_q][d] holds sequence 0's chunk, then sequence
@@ -669,15 +739,15 @@ def prefill_attention(fmt, k_pool, v_pool, num_kv_heads, d, q, q_lens, page_tabl
     prefix = seq_lens[b_of] - q_lens[b_of] + j_of + 1                  # positions 0 .. P
     table = np.asarray(page_table)[b_of]
     return decode_attention(fmt, k_pool, v_pool, num_kv_heads, d, q, table, prefix, sm_scale, in_dtype,
-                            k_only, signs)
+                            k_only, signs, pv_scaled)
 
 
 def decode_attention(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table, seq_lens,
-                     sm_scale, in_dtype="bf16", k_only=False, signs=None) -> np.ndarray:
+                     sm_scale, in_dtype="bf16", k_only=False, signs=None, pv_scaled=False) -> np.ndarray:
     """All output rows [B][H_q][d] (float64)."""
     q = np.asarray(q)
     B, Hq = q.shape[0], q.shape[1]
     rows = [(b, h) for b in range(B) for h in range(Hq)]
     out = decode_attention_rows(fmt, k_pool, v_pool, num_kv_heads, d, q, page_table,
-                                seq_lens, sm_scale, rows, in_dtype, k_only, signs)
+                                seq_lens, sm_scale, rows, in_dtype, k_only, signs, pv_scaled)
     return out.reshape(B, Hq, d)

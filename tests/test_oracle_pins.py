@@ -843,6 +843,95 @@ def test_fold_p_fp8_error_within_e4m3_half_ulp():
     assert np.all(out[folded < 2.0 ** -10] == 0.0)
 
 
+def test_fold_p_fp8_with_headroom_rounds_like_torch_fp8():
+    # R13's fold: block scale 2^M with M = (largest E of the 32-token block) - 8,
+    # at least -127; the folded values P 2^(E_t - M) (at most 2^8) rounded by
+    # torch's float8_e4m3fn cast.
+    rng = np.random.default_rng(64)
+    T = 80                                             # two whole blocks and a block of 16
+    p = rng.uniform(0.0, 1.0, size=(3, T))
+    p[:, 5] = 1.0
+    e = rng.integers(-40, 6, size=T)
+    e[64:] = rng.integers(-127, -121, size=T - 64)     # a block whose M is clamped to -127
+    want = np.zeros_like(p)
+    for b0 in range(0, T, 32):
+        blk = range(b0, min(b0 + 32, T))
+        M = max(max(int(e[t]) for t in blk) - 8, -127)
+        for r in range(p.shape[0]):
+            for t in blk:
+                x = torch.tensor(math.ldexp(float(p[r, t]), int(e[t]) - M), dtype=torch.float64)
+                want[r, t] = math.ldexp(float(x.to(torch.float8_e4m3fn).to(torch.float64)), M)
+    got = O.fold_p_fp8(p, e, headroom=O.SPV_HEADROOM)
+    np.testing.assert_array_equal(got, want)
+    assert (got == 0).any() and (got > 0).any()
+
+
+def _spv_case(rng, L, d, G=3, spread=(100, 141)):
+    k = rng.standard_normal((L, d))
+    vc = rng.integers(0, 16, size=(L, d)).astype(np.uint8)
+    vs = rng.integers(spread[0], spread[1], size=(L, d // 32)).astype(np.uint8)
+    q = rng.standard_normal((G, d))
+    return q, k, vc, vs
+
+
+@pytest.mark.parametrize("step", [128, 32, 7])
+def test_scaled_pv_decode_without_rounding_is_plain_attention(step):
+    # Closed form: the step-wise combination (each step against its own maximum,
+    # weighted by exp(m_s - m)) is an identity of the softmax, so with the fold
+    # left unrounded the result is the plain attention.
+    rng = np.random.default_rng(65 + step)
+    q, k, vc, vs = _spv_case(rng, 300, 64)
+    got = O.attention_pv_scaled(q, k, vc, vs, 0.3, step=step, fold=False)
+    want = O.attention(q, k, O.dequantize_fp4(vc, vs), 0.3)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def test_scaled_pv_decode_uniform_probabilities_closed_form():
+    # q = 0: every logit is 0, so every probability is exactly 1 and the fold
+    # rounds only exact powers of two: 2^(E_t - M) for E_t - M >= -9 (down to the
+    # least E4M3 subnormal), 0 below (2^-10 is a tie and rounds to the even 0).
+    # The output is the mean over tokens of the values that survive.
+    rng = np.random.default_rng(66)
+    L, d = 300, 64
+    _, k, vc, vs = _spv_case(rng, L, d, spread=(96, 141))      # exponent spreads up to 44 within a block
+    vs[256:288] = rng.integers(0, 9, size=(32, d // 32))        # E <= -119: M clamped to -127
+    q = np.zeros((2, d))
+    vals = O.dequantize_fp4(vc, vs)
+    e = vs.astype(np.int64) - 127
+    want = np.zeros(d)
+    for t in range(L):
+        b0 = 32 * (t // 32)                                     # 32-token blocks of 128-token steps
+        for c in range(d):
+            g = c // 32
+            M = max(max(int(e[u, g]) for u in range(b0, min(b0 + 32, L))) - 8, -127)
+            if e[t, g] - M >= -9:
+                want[c] += vals[t, c]
+    want /= L
+    dropped = sum(int(e[t, g] - max(e[32 * (t // 32):32 * (t // 32) + 32, g].max() - 8, -127) < -9)
+                  for t in range(L) for g in range(d // 32))
+    assert dropped > 0
+    got = O.attention_pv_scaled(q, k, vc, vs, 1.0)
+    np.testing.assert_allclose(got, np.tile(want, (2, 1)), rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def test_scaled_pv_decode_rows_gather_and_rotate_back():
+    # On a cache written by append with q = 0 (probabilities exactly 1) and V's
+    # exponents within 17 binades of each block's largest, every fold is exact,
+    # so the scaled-PV decode rows equal the plain decode rows (same gather of
+    # V, same rotation back).
+    wl = W.make_workload("spv_rows", 2, 8, 2, 128, [200, 37], [200, 37], seed=67)
+    kp = O.new_pool(O.FMT_FP4, wl.num_pages, 2, 128)
+    vp = O.new_pool(O.FMT_FP4, wl.num_pages, 2, 128)
+    O.append(O.FMT_FP4, kp, vp, wl.k, wl.v, wl.slot_mapping)
+    q = np.zeros_like(wl.q)
+    plain = O.decode_attention(O.FMT_FP4, kp, vp, 2, 128, q, wl.page_table, wl.seq_lens, 0.1)
+    spv = O.decode_attention(O.FMT_FP4, kp, vp, 2, 128, q, wl.page_table, wl.seq_lens, 0.1, pv_scaled=True)
+    np.testing.assert_allclose(spv, plain, rtol=0, atol=1e-12 * np.abs(plain).max())
+    assert np.abs(plain).max() > 0
+    with pytest.raises(ValueError):
+        O.decode_attention(O.FMT_FP8, kp, vp, 2, 128, q, wl.page_table, wl.seq_lens, 0.1, pv_scaled=True)
+
+
 def test_pv_f16_hi_lo_carries_22_bits():
     rng = np.random.default_rng(62)
     p = rng.uniform(2.0 ** -10, 1.0, size=(4, 200))
@@ -878,6 +967,11 @@ def test_pv_precision_choice_on_decode_statistics():
     for name, got in (("f16_hi_lo", O.pv_f16_hi_lo(p, V)), ("fp8_scaled", O.pv_fp8_scaled(p, vc, vsb))):
         o = O.wht(got / l)
         res[name] = (np.linalg.norm(o - exact) / np.linalg.norm(exact), np.abs(o - exact).max())
+    # R13's decode: 128-token steps against their own maxima, headroom 8
+    vcodes = O.unpack_nibbles(O.pack_nibbles(vc))
+    o = O.wht(O.attention_pv_scaled(qhat, K, vcodes, vsb, 1 / math.sqrt(128)))
+    res["r13_decode"] = (np.linalg.norm(o - exact) / np.linalg.norm(exact), np.abs(o - exact).max())
     print("PV precision (rel-L2, max-abs):", res)
     assert res["f16_hi_lo"][0] < 1e-5 and res["f16_hi_lo"][1] < 1e-4
     assert res["fp8_scaled"][0] > 1e-3
+    assert 1e-3 < res["r13_decode"][0] < res["fp8_scaled"][0]
