@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--workloads", default="decode_gqa,long,ragged",
                     help="decode workloads to time, comma-separated; the first is the headline")
     ap.add_argument("--no-baselines", action="store_true", help="skip the FP8/BF16 KV kernels")
+    ap.add_argument("--no-pv-scaled", action="store_true",
+                    help="skip the FP4 step with the PV on the scaled FP4 x FP8 MFMA (UQ_FLAG_PV_SCALED)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--no-append", action="store_true", help="skip the append-only measurement")
@@ -391,10 +393,10 @@ class HipEvents:
 class Runner:
     """Holds device buffers for one format and runs steps through the C ABI."""
 
-    def __init__(self, fmt, wl, fused=False):
+    def __init__(self, fmt, wl, fused=False, flags=0):
         import torch
         import bit_kv_cache_wht_amd as uq
-        self.fmt, self.wl, self.uq, self.torch = fmt, wl, uq, torch
+        self.fmt, self.wl, self.uq, self.torch, self.flags = fmt, wl, uq, torch, flags
         fid = {"fp4": uq.UQ_KV_FP4, "fp8": uq.UQ_KV_FP8, "bf16": uq.UQ_KV_BF16}[fmt]
         self.append = {"fp4": uq.uq_quantize_append, "fp8": uq.uq_append_fp8, "bf16": uq.uq_append_bf16}[fmt]
         self.decode = {"fp4": uq.uq_decode_attention, "fp8": uq.uq_decode_attention_fp8,
@@ -432,7 +434,7 @@ class Runner:
             if ev is not None:
                 self.uq.uq_profile_next_decode(ev[0], ev[1])
             self.uq.uq_append_decode_attention(self.cache, self.k_new, self.v_new, self.q, self.page_table,
-                                               self.seq_lens, self.sm_scale, self.out, self.ws)
+                                               self.seq_lens, self.sm_scale, self.out, self.ws, flags=self.flags)
             return
         if ev_app is not None:
             ev_app[0].record()
@@ -441,7 +443,8 @@ class Runner:
             ev_app[1].record()
         if ev is not None:
             self.uq.uq_profile_next_decode(ev[0], ev[1])
-        self.decode(self.cache, self.q, self.page_table, self.seq_lens, self.sm_scale, self.out, self.ws)
+        self.decode(self.cache, self.q, self.page_table, self.seq_lens, self.sm_scale, self.out, self.ws,
+                    flags=self.flags)
 
     def run(self, steps, warmup, scrub=None, settle_s=0.0):
         """After `settle_s` seconds of untimed steps and `warmup` more:
@@ -625,10 +628,13 @@ def describe(wl):
 def time_workload(args, wl, fmts, torch):
     """Per format: the step timed warm and scrubbed (see Runner.run), with the
     decode kernel's rate against the HBM peak."""
+    import bit_kv_cache_wht_amd as uq
     out = {}
-    for fmt in fmts:
-        log(f"{wl.name} {fmt}: prefill + timing")
-        r = Runner(fmt, wl, fused=fmt == "fp4")
+    for key in fmts:
+        # fp4_pv_scaled: the FP4 step with the PV on the scaled FP4 x FP8 MFMA
+        fmt, flags = ("fp4", uq.UQ_FLAG_PV_SCALED) if key == "fp4_pv_scaled" else (key, 0)
+        log(f"{wl.name} {key}: prefill + timing")
+        r = Runner(fmt, wl, fused=fmt == "fp4", flags=flags)
         scrub = torch.ones((args.scrub_mb << 20) // 4, dtype=torch.int32, device="cuda") if args.scrub_mb else None
         res = r.run(args.steps, args.warmup, scrub, settle_s=args.settle_ms * 1e-3)
         by = r.kernel_bytes()
@@ -656,8 +662,8 @@ def time_workload(args, wl, fmts, torch):
             e["append_tokens_per_s"] = round(toks / (app_us * 1e-6))
             e["append_algo_bytes"] = by["append"]
             e["append_gbs"] = round(by["append"] / (app_us * 1e-6) / 1e9, 1)
-        out[fmt] = e
-        log(f"{wl.name} {fmt}: {e['us_per_step']} us/step scrubbed ({e['us_per_step_warm']} warm), decode kernel "
+        out[key] = e
+        log(f"{wl.name} {key}: {e['us_per_step']} us/step scrubbed ({e['us_per_step_warm']} warm), decode kernel "
             f"{e['decode_kernel_us']} us = {e['decode_gbs']} GB/s ({e['frac_hbm_peak']:.1%})"
             + (f", append {e['append_us']} us" if "append_us" in e else ""))
         del r, scrub
@@ -689,7 +695,7 @@ def main():
         cpu = cpu_baseline(wl, args.cpu_seconds)
     import torch
     torch.cuda.set_device(0)
-    fmts = ["fp4"] + ([] if args.no_baselines else ["fp8", "bf16"])
+    fmts = ["fp4"] + ([] if args.no_pv_scaled else ["fp4_pv_scaled"]) + ([] if args.no_baselines else ["fp8", "bf16"])
     results, descr, shape = {}, {}, {}
     for i, name in enumerate(names):
         if i > 0:
@@ -737,7 +743,7 @@ def main():
                           "decode_kernel_us": results[names[0]][f]["decode_kernel_us"],
                           "kernel_gbs": results[names[0]][f]["decode_gbs"],
                           "frac_hbm_peak": results[names[0]][f]["frac_hbm_peak"]}
-                      for f in fmts if f != "fp4"},
+                      for f in fmts if f not in ("fp4", "fp4_pv_scaled")},
         "workloads": {n: dict(description=descr[n], **results[n]) for n in names},
     }
     sr = stream_read_gbs()

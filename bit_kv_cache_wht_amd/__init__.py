@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     UQ_CHECK_BAD_PAGE,
     UQ_FLAG_CHECK,
     UQ_FLAG_OUT_ROTATED,
+    UQ_FLAG_PV_SCALED,
     UQ_FLAG_SCALE_CONSTOPT,
     UQ_IN_BF16,
     UQ_IN_F32,

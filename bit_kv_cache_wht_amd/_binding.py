@@ -12,6 +12,7 @@ UQ_PAGE_SIZE = 16
 UQ_FLAG_OUT_ROTATED = 1
 UQ_FLAG_SCALE_CONSTOPT = 2
 UQ_FLAG_CHECK = 4
+UQ_FLAG_PV_SCALED = 8
 UQ_CHECK_BAD_LEN, UQ_CHECK_BAD_PAGE = 1, 2
 UQ_ROT_K_ONLY = 1
 UQ_ROT_SIGNS = 2

@@ -149,7 +149,8 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   // check reports into the workspace, which the no-allocation variant hides
   const uint32_t allowed = (noalloc ? 0u : UQ_FLAG_CHECK) |
                            (format != UQ_KV_FP4 ? 0u
-                            : UQ_FLAG_OUT_ROTATED | (k_new != nullptr ? UQ_FLAG_SCALE_CONSTOPT : 0u));
+                            : UQ_FLAG_OUT_ROTATED | UQ_FLAG_PV_SCALED |
+                                  (k_new != nullptr ? UQ_FLAG_SCALE_CONSTOPT : 0u));
   if ((flags & ~allowed) != 0u) return UQ_ERR_INVALID_ARG;
   if (q_dtype != UQ_IN_BF16 && q_dtype != UQ_IN_F32) return UQ_ERR_INVALID_ARG;
   if (format == UQ_KV_BF16 && q_dtype != UQ_IN_BF16) return UQ_ERR_UNSUPPORTED;
@@ -203,6 +204,7 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   a.rot = rot_of(cache);
   a.unrotate = format == UQ_KV_FP4 && !(flags & UQ_FLAG_OUT_ROTATED) && a.rot.k_only == 0u;
   a.constopt = (flags & UQ_FLAG_SCALE_CONSTOPT) != 0u;
+  a.pv_scaled = (flags & UQ_FLAG_PV_SCALED) != 0u;
   a.k_new = k_new;
   a.v_new = v_new;
   a.ev_start = g_prof_start;

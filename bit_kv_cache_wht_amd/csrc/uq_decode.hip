@@ -381,6 +381,217 @@ template <int D> struct Fp4PairPol {
   __device__ static int channel(int tile, int j4, int v) { return 2 * (kCPL * (4 * j4 + v) + (tile >> 1)) + (tile & 1); }
 };
 
+// FP4 with the PV on the scaled FP4 x FP8 MFMA as well (UQ_FLAG_PV_SCALED; the
+// pages' dequantization folded into the scaled matrix instruction, [review] §3.2
+// and [commentary] footnote 2).  V's group scales run along head_dim while PV
+// contracts over tokens, so they cannot be block scales of the FP4 operand:
+// they are folded into the probabilities instead, which become the FP8 operand,
+// P * 2^(E_t - M) rounded to E4M3 per 32-channel group and 32-token block with
+// block scale 2^M, M = the block's largest V exponent - 8 (at least -127).
+// One KV head per item; a step is 8 pages (128 tokens), the contraction length
+// of one scaled MFMA, and its probabilities are taken against the step's own
+// largest logit (so that the rounding does not depend on which wave visits
+// which step), then merged into the running state with the step maximum.
+//
+// Operand layouts of the 16x16x128 scaled MFMA (contraction index k): an FP4
+// operand lane (row, j) holds k = 32j .. 32j + 31; an FP8 operand lane (col, j)
+// holds k = 16j .. 16j + 15 (bytes 0..15) and 64 + 16j .. 64 + 16j + 15 (bytes
+// 16..31); the block scale of lane (., j) applies to k = 32j .. 32j + 31
+// whichever lanes hold those elements.  Token of k: block J = k / 32 is pages
+// 2J, 2J + 1 of the step; inside it k = 32J + 8i + 2u + e is slot 4i + u of
+// page 2J + e.
+//   PV, FP4 operand (V^T, rows = channels): lane (r, j) takes the 16-byte code
+//     rows of channel pair 16g + r in pages 2j and 2j + 1; two bit-field merges
+//     give the even and the odd channel's 32 codes in that k order.
+//   PV, FP8 operand (P, columns = query rows): dword m of lane (r, j) holds
+//     k = 64(m >> 2) + 16j + 4(m & 3) + v, v = 0..3, i.e. page
+//     4(m >> 2) + 2(j >> 1) + (v & 1), slot 8(j & 1) + 2(m & 3) + (v >> 1).
+//   QK: token row i of MFMA m is that token with j = i >> 2, v = i & 3, so that
+//     lane (r, j) of the result holds exactly its FP8 dword m in S[m].
+//   Block maxima: the lane sees half of each of its two blocks (8 slots of both
+//     pages); lane l ^ 16 has the other half.  The lane's own block scale (block
+//     j) is held as a fold exponent by lane (r, 2(j & 1)).
+template <int D> struct Fp4SpvPol {
+  static constexpr bool kSpv = true;
+  static constexpr int kShareAlpha = 6;
+  static constexpr int kOcc = 1;
+  static constexpr int kBuf = 2;
+  static constexpr int kNH = 1, kNP = 8, kTok = 32;
+  static constexpr int kBlk = Fp4Block<D>::kBytes;
+  static constexpr int kCode = Fp4Block<D>::kCodeBytes;
+  static constexpr int kGroups = D / 32;
+  static constexpr int kCPL = D / 32;
+  static constexpr int kTiles = D / 16;
+  struct KStep {
+    uint4 kc[8];          // MFMA m: token row lane%16 (see above), group lane/16
+    uint32_t ks[4];       // scale bytes: MFMA m uses byte (m & 3) >> 1 of ks[2(m >> 2) + (m & 1)]
+  };
+  struct VStep {
+    uint4 xc[kGroups], yc[kGroups];   // code rows of channel pair 16g + lane%16, pages 2j, 2j + 1
+    uint2 e[4][kGroups];              // scale bytes of group g, slots 8(j & 1) .. + 7 of the lane's
+                                      // FP8 pages 2(j >> 1), + 1, + 4, + 5
+  };
+  struct QOp { v8i b; };
+  // The page id of a lane-dependent index x < 8: selects between the
+  // wave-uniform ids (taken through readfirstlane, so that the selects are not
+  // turned into an indexed load from a stack copy of the array).
+  __device__ static int pick8(const int (&ids)[8], int x) {
+    int r = __builtin_amdgcn_readfirstlane(ids[0]);
+#pragma unroll
+    for (int k = 1; k < 8; ++k) r = x == k ? __builtin_amdgcn_readfirstlane(ids[k]) : r;
+    return r;
+  }
+  __device__ static const uint8_t* block(const uint8_t* pool, int pid, int64_t page_bytes, const PageGeo& g) {
+    return pool + (int64_t)pid * page_bytes + (int64_t)fp4_block_pos(g.head0, pid, g.H, g.mask) * kBlk;
+  }
+  __device__ static void load_q(QOp& qo, const uint8_t* qrow, bool valid, int j4, int) {
+    qo.b = load_q_fp8<D>(qrow, valid, j4);
+  }
+  // K of token row r16 of MFMA m: page 4(m >> 2) + 2(r16 >> 3) + (r16 & 1), slot
+  // 8((r16 >> 2) & 1) + 2(m & 3) + ((r16 >> 1) & 1).
+  __device__ static void load_k(KStep& st, const uint8_t* pool, const int (&ids)[8], int64_t page_bytes,
+                                const PageGeo& g, int r16, int j4) {
+    const int pa = 2 * (r16 >> 3) + (r16 & 1);
+    const uint8_t* kb[2] = {block(pool, pick8(ids, pa), page_bytes, g), block(pool, pick8(ids, pa + 4), page_bytes, g)};
+    const int par = (r16 >> 1) & 1, half = (r16 >> 2) & 1;
+    const int slot0 = 8 * half + par;
+    if (j4 < kGroups) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) st.kc[m] = load16_stream(kb[m >> 2] + (slot0 + 2 * (m & 3)) * (D / 2) + 16 * j4);
+      // scale bytes are stored [slot % 4][group][slot / 4]; slot 8 half + 2(m & 3)
+      // + par has slot % 4 = 2(m & 1) + par and slot / 4 = 2 half + ((m & 3) >> 1)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        st.ks[2 * x] = load4_stream(kb[x] + kCode + 4 * (par * kGroups + j4)) >> (16 * half);
+        st.ks[2 * x + 1] = load4_stream(kb[x] + kCode + 4 * ((2 + par) * kGroups + j4)) >> (16 * half);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) st.kc[m] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) st.ks[x] = 0x7F7F7F7Fu;
+    }
+  }
+  __device__ static void load_v(VStep& st, const uint8_t* pool, const int (&ids)[8], int64_t page_bytes,
+                                const PageGeo& g, int r16, int j4) {
+    const uint8_t* xb = block(pool, pick8(ids, 2 * j4), page_bytes, g);
+    const uint8_t* yb = block(pool, pick8(ids, 2 * j4 + 1), page_bytes, g);
+#pragma unroll
+    for (int gg = 0; gg < kGroups; ++gg) {
+      const int p = 16 * gg + r16;                              // channel pair
+      const int row = 16 * (p % kCPL) + p / kCPL;               // its 16-byte code row
+      st.xc[gg] = load16_stream(xb + row * kPage);
+      st.yc[gg] = load16_stream(yb + row * kPage);
+    }
+    const int pe = 2 * (j4 >> 1), w = 8 * (j4 & 1);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const uint8_t* eb = block(pool, pick8(ids, pe + (x & 1) + 4 * (x >> 1)), page_bytes, g) + kCode + w;
+#pragma unroll
+      for (int gg = 0; gg < kGroups; ++gg) st.e[x][gg] = load8_stream(eb + kPage * gg);
+    }
+  }
+  template <int M> __device__ static v4f qk1(const KStep& st, const QOp& qo) {
+    const v8i a = v8i{(int)st.kc[M].x, (int)st.kc[M].y, (int)st.kc[M].z, (int)st.kc[M].w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qo.b, v4f{0, 0, 0, 0}, 4 /*A fp4*/, 0 /*B fp8*/,
+                                                           (M & 3) >> 1, (int)st.ks[2 * (M >> 2) + (M & 1)], 0, 127);
+  }
+  __device__ static void qk(const KStep& st, const QOp& qo, v4f (&S)[8]) {
+    S[0] = qk1<0>(st, qo);
+    S[1] = qk1<1>(st, qo);
+    S[2] = qk1<2>(st, qo);
+    S[3] = qk1<3>(st, qo);
+    S[4] = qk1<4>(st, qo);
+    S[5] = qk1<5>(st, qo);
+    S[6] = qk1<6>(st, qo);
+    S[7] = qk1<7>(st, qo);
+  }
+  // Largest bytes of two pairs of words, one per 16-bit half of the result
+  // (packed u16 maxima: the high byte of a half decides the unsigned 16-bit
+  // order, so the maxima of the words and of the words shifted left by 8 carry
+  // the largest odd and even bytes).
+  __device__ static uint32_t umax16(uint32_t x, uint32_t y) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, x), __builtin_bit_cast(us2, y)));
+  }
+  __device__ static uint32_t max_byte4(uint2 a, uint2 b) {
+    const uint32_t t = umax16(umax16(umax16(a.x, a.y), umax16(b.x, b.y)),
+                              umax16(umax16(a.x << 8, a.y << 8), umax16(b.x << 8, b.y << 8)));
+    return max(t >> 24, (t >> 8) & 0xFFu);
+  }
+  // Step PV: Z[tile] = the FP8 operand (folded P) times the V codes.  pf[4m + v]
+  // is the probability of S[m][v]'s token (0 past the item); nv[x]: valid slots
+  // of the lane's FP8 page x (2(j >> 1), + 1, + 4, + 5) inside its 8-slot window.
+  __device__ static void pv(VStep& st, const float (&pf)[32], const int (&nv)[4], v4f (&Z)[kTiles], int lane) {
+    const int j4 = lane >> 4, r16 = lane & 15;
+    // exponents of slots past the item do not enter the block maxima
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const uint32_t k0 = slot_bytes_kept(nv[x], 0), k1 = slot_bytes_kept(nv[x], 4);
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        st.e[x][g].x &= k0;
+        st.e[x][g].y &= k1;
+      }
+    }
+    // block maxima: half 0 (pages 2(j >> 1), + 1: block j >> 1) in the low 16
+    // bits, half 1 (block 2 + (j >> 1)) in the high 16 bits; completed with lane
+    // l ^ 16, which holds the blocks' other 8 slots
+    uint32_t bm[kGroups], sc[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      uint32_t mm = max_byte4(st.e[0][g], st.e[1][g]) | (max_byte4(st.e[2][g], st.e[3][g]) << 16);
+      mm = umax16(mm, (uint32_t)__shfl_xor((int)mm, 16));
+      // block scale bytes M + 127 = max(largest byte - 8, 0), per half
+      bm[g] = umax16(mm, 0x00080008u) - 0x00080008u;
+    }
+    // the lane's own block scale (block j): half j >> 1 of lane (r, 2(j & 1))
+    const int src = 32 * (j4 & 1) + r16;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      const uint32_t o = (uint32_t)__shfl((int)bm[g], src);
+      sc[g] = (j4 >> 1) ? o >> 16 : o & 0xFFFFu;
+    }
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      const int bma = (int)(bm[g] & 0xFFFFu), bmb = (int)(bm[g] >> 16);
+      uint32_t bw[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        // S[m][v]: FP8 page 2(m >> 2) + (v & 1) of the lane, window slot
+        // 2(m & 3) + (v >> 1): byte 2(m & 1) + (v >> 1) of word (m & 3) >> 1
+        const int bmx = (m >> 2) ? bmb : bma;
+        const uint2 e0 = st.e[2 * (m >> 2)][g], e1 = st.e[2 * (m >> 2) + 1][g];
+        const uint32_t w0 = ((m & 3) >> 1) ? e0.y : e0.x, w1 = ((m & 3) >> 1) ? e1.y : e1.x;
+        const int sh0 = 16 * (m & 1), sh1 = sh0 + 8;
+        const float f0 = __builtin_amdgcn_ldexpf(pf[4 * m + 0], (int)((w0 >> sh0) & 0xFFu) - bmx);
+        const float f1 = __builtin_amdgcn_ldexpf(pf[4 * m + 1], (int)((w1 >> sh0) & 0xFFu) - bmx);
+        const float f2 = __builtin_amdgcn_ldexpf(pf[4 * m + 2], (int)((w0 >> sh1) & 0xFFu) - bmx);
+        const float f3 = __builtin_amdgcn_ldexpf(pf[4 * m + 3], (int)((w1 >> sh1) & 0xFFu) - bmx);
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+        bw[m] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, lo, true);
+      }
+      const v8i b = v8i{(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3], (int)bw[4], (int)bw[5], (int)bw[6], (int)bw[7]};
+      const uint32_t xc[4] = {st.xc[g].x, st.xc[g].y, st.xc[g].z, st.xc[g].w};
+      const uint32_t yc[4] = {st.yc[g].x, st.yc[g].y, st.yc[g].z, st.yc[g].w};
+      uint32_t ev[4], od[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ev[i] = (xc[i] & 0x0F0F0F0Fu) | ((yc[i] << 4) & 0xF0F0F0F0u);   // even channel: X, Y slot pairs
+        od[i] = ((xc[i] >> 4) & 0x0F0F0F0Fu) | (yc[i] & 0xF0F0F0F0u);   // odd channel
+      }
+      const v8i ae = v8i{(int)ev[0], (int)ev[1], (int)ev[2], (int)ev[3], 0, 0, 0, 0};
+      const v8i ao = v8i{(int)od[0], (int)od[1], (int)od[2], (int)od[3], 0, 0, 0, 0};
+      Z[2 * g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ae, b, Z[2 * g], 4 /*A fp4*/, 0 /*B fp8*/, 0, 127,
+                                                                  0, (int)sc[g]);
+      Z[2 * g + 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ao, b, Z[2 * g + 1], 4, 0, 0, 127, 0,
+                                                                      (int)sc[g]);
+    }
+  }
+  // Tile 2g + par, row 4j + v: channel pair 16g + 4j + v, channel 2 * pair + par.
+  __device__ static int channel(int tile, int j4, int v) { return 2 * (16 * (tile >> 1) + 4 * j4 + v) + (tile & 1); }
+};
+
 // FP8 baseline.  QK runs on f16 MFMAs after an exact E4M3 -> f16 conversion:
 // the FP8 x FP8 MFMAs (16x16x128 scaled and 16x16x32) drop low-order bits of
 // small products when large ones are present in the same instruction, which
@@ -570,6 +781,10 @@ template <int D> struct Bf16Pol {
   }
   __device__ static int channel(int tile, int j4, int v) { return 16 * tile + 4 * j4 + v; }
 };
+
+// Policies with the scaled-MFMA PV declare kSpv.
+template <class P, class = void> struct SpvOf : std::false_type {};
+template <class P> struct SpvOf<P, std::void_t<decltype(P::kSpv)>> : std::bool_constant<P::kSpv> {};
 
 // ------------------------------------------------------------------ plan
 // The work of a call is the list of steps (4 pages) of all (sequence b, KV head
@@ -1137,7 +1352,8 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     int np = 0;                        // lane part of the lane's row
     bool nlive = false, nv = false;    // the lane's row exists / is a V row
     if constexpr (FMT == UQ_KV_FP4) {
-      static_assert(kMaxR <= NW, "segment k of a round is written by wave k");
+      // segment k of a round is written by wave k: rounds hold at most NW
+      // segments (launch_one)
       if (a.k_new != nullptr) {
         const uint64_t nm = __ballot(sg_new);
         if ((nm >> wave) & 1) {
@@ -1173,10 +1389,11 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     }
 
     // ---- step claims
+    constexpr int kIds = NP < 4 ? 4 : NP;
     struct Claim {
       int meta;          // < 0: no step; else full << 28 | item << 20 | step
       int hk;
-      int ids[4];        // page ids of the step's 4 pages (page 0 of the pool when none)
+      int ids[kIds];     // page ids of the step's NP pages (page 0 of the pool when none)
     };
     // A claim takes the next step index from the LDS counter, then reads the
     // step's page ids.  The prologue takes all its indices first: LDS and
@@ -1193,7 +1410,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         c.meta = -1;
         c.hk = 0;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) c.ids[x] = 0;
+        for (int x = 0; x < kIds; ++x) c.ids[x] = 0;
         return c;
       }
       // segment k: the last one whose first step is <= g
@@ -1208,10 +1425,10 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
       // vector-memory counter of the key/value loads
       const int32_t* pt = page_table + (int64_t)b * a.max_pages + p_begin;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) c.ids[x] = x < NP ? pt[min(NP * s + x, npg - 1)] : 0;
+      for (int x = 0; x < kIds; ++x) c.ids[x] = x < NP ? pt[min(NP * s + x, npg - 1)] : 0;
       if (a.err != nullptr) {                    // checked: an id outside the pool reads page 0
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int x = 0; x < kIds; ++x)
           if ((uint32_t)c.ids[x] >= (uint32_t)a.num_pages) {
             c.ids[x] = 0;
             chk |= UQ_CHECK_BAD_PAGE;
@@ -1307,6 +1524,52 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     // on full ones), which costs a few ALU operations but keeps a single copy of
     // the step code and its register allocation.
     auto finish_step = [&](v4f (&S)[TOK / 4], typename Pol::VStep& st, int s, bool full) {
+     if constexpr (SpvOf<Pol>::value) {
+      // Scaled-MFMA PV: the step's probabilities against its own largest logit
+      // of each row, its PV into fresh accumulators, then merged into the running
+      // state (m_run = -inf before the first step: weight 0 for the empty state).
+      // valid slots of the lane's FP8 pages 2(j >> 1), + 1, + 4, + 5 inside its
+      // 8-slot window 8(j & 1) .. + 7
+      int nv[4] = {8, 8, 8, 8};
+      if (!full) {
+        const int npg = rec[8 * acc_k + kRecNpg], lrel = rec[8 * acc_k + kRecLRel];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int px = NP * s + 2 * (j4 >> 1) + (x & 1) + 4 * (x >> 1);
+          nv[x] = px < npg ? max(min(8, lrel - px * kPage - 8 * (j4 & 1)), 0) : 0;
+        }
+      }
+      float t[TOK];
+#pragma unroll
+      for (int m = 0; m < TOK / 4; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          t[4 * m + v] = 2 * (m & 3) + (v >> 1) < nv[2 * (m >> 2) + (v & 1)] ? S[m][v] : -INFINITY;
+      float mx = t[0];
+#pragma unroll
+      for (int i = 1; i < TOK; ++i) mx = fmaxf(mx, t[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float neg = -mx * a.scale_log2;
+      float pf[TOK];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < TOK; ++i) {
+        pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg));
+        psum += pf[i];
+      }
+      v4f Z[Pol::kTiles];
+#pragma unroll
+      for (int tt = 0; tt < Pol::kTiles; ++tt) Z[tt] = v4f{0, 0, 0, 0};
+      Pol::pv(st, pf, nv, Z, lane);
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2);
+      const float beta = __builtin_amdgcn_exp2f((mx - m_new) * a.scale_log2);
+      l_run = __builtin_fmaf(l_run, alpha, psum * beta);
+#pragma unroll
+      for (int tt = 0; tt < Pol::kTiles; ++tt) O[tt] = O[tt] * alpha + Z[tt] * beta;
+      m_run = m_new;
+     } else {
       int nvalid = TOK;                            // valid ones among this lane's TOK slots
       if (!full) {
         const int npg = rec[8 * acc_k + kRecNpg], lrel = rec[8 * acc_k + kRecLRel];
@@ -1363,6 +1626,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
       }
       Pol::mask_v(st, nvalid);
       Pol::pv(st, Pm, O, lane_head);
+     }
     };
 
     for (;;) {
@@ -1566,7 +1830,7 @@ hipError_t launch_one(const DecodeArgs& a, const KArgs& k0, hipStream_t s) {
   const int grid = dl.cus < kMaxGrid ? dl.cus : kMaxGrid;
   // segments per round: as many as fit in LDS (the share of a workgroup usually
   // spans a few items)
-  int R = kMaxR;
+  int R = kMaxR < NW ? kMaxR : NW;     // the fused step's write of segment k is done by wave k
   while (R > 1 && Lds(R, NW, G, D, ESZ, a.B).total > dl.lds) --R;
   const int lds = Lds(R, NW, G, D, ESZ, a.B).total;
   if (lds > dl.lds) return hipErrorInvalidConfiguration;
@@ -1627,7 +1891,9 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
               : launch_one<D, UQ_IN_F32, UQ_KV_FP4, false, P, RV>(a, k, s);
   };
   const bool rv = a.rot.k_only != 0u || (a.rot.s[0] | a.rot.s[1] | a.rot.s[2] | a.rot.s[3]) != 0u;
-  if (a.format == UQ_KV_FP4 && k.G <= 8 && a.Hkv % 2 == 0) {
+  if (a.format == UQ_KV_FP4 && a.pv_scaled) {
+    e = rv ? fp4(PolTag<Fp4SpvPol<D>>{}, std::true_type{}) : fp4(PolTag<Fp4SpvPol<D>>{}, std::false_type{});
+  } else if (a.format == UQ_KV_FP4 && k.G <= 8 && a.Hkv % 2 == 0) {
     // KV-head pairs fill the 16 MFMA columns
     e = rv ? fp4(PolTag<Fp4PairPol<D>>{}, std::true_type{}) : fp4(PolTag<Fp4PairPol<D>>{}, std::false_type{});
   } else if (a.format == UQ_KV_FP4) {

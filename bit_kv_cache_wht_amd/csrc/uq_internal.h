@@ -67,6 +67,7 @@ struct DecodeArgs {
   bool check;                // UQ_FLAG_CHECK: validate page ids and lengths, report in the error word
   int32_t num_pages;         // pages in each pool (for the check)
   bool unrotate;             // FP4: rotate the output back (through R^T)
+  bool pv_scaled;            // FP4: PV on the scaled FP4 x FP8 MFMA (UQ_FLAG_PV_SCALED)
   bool constopt;             // fused FP4 step: constOpt scales for the written token
   Rot rot;                   // FP4: the cache's rotation variant
   const void* k_new;         // fused FP4 step: newest token's K/V [B][Hkv][D] (q_dtype), or null

@@ -129,6 +129,21 @@ enum uq_in_dtype { UQ_IN_BF16 = 0, UQ_IN_F32 = 1 };
 #define UQ_FLAG_CHECK 4u
 #define UQ_CHECK_BAD_LEN 1u
 #define UQ_CHECK_BAD_PAGE 2u
+/* FP4 decode (uq_decode_attention, its no-allocation variant and
+ * uq_append_decode_attention): run PV on the scaled FP4 x FP8 matrix
+ * instruction as well ([review] §3.2 "dequantization rule과 scaled-MFMA", §6.3;
+ * [commentary] footnote 2).  V's group scales run along head_dim while PV sums
+ * over tokens, so they are folded into the probabilities: each 128-token step
+ * (positions 128 s .. 128 s + 127 of a sequence) takes its probabilities
+ * against its own largest logit of each query row; per 32-channel group and
+ * 32-token block, P * 2^(E_t - M) is rounded to FP8 E4M3 (M = the block's
+ * largest V exponent minus 8, at least -127, as the block's UE8M0 scale) and
+ * multiplied by V's FP4 codes; the steps are combined as in the online
+ * softmax, with the unrounded sums of P.  The E4M3 rounding costs accuracy:
+ * about 3.5e-3 relative L2 on 8K-token decode statistics (against ~1e-6 for
+ * the default PV, f16 hi + lo probabilities times the exactly converted V);
+ * an opt-in variant, not the default. */
+#define UQ_FLAG_PV_SCALED 8u
 
 /* Cache descriptor; read at call time, never retained. */
 /* Rotation variants of an FP4 cache (uq_kv_cache.rotation; 0 = K and V rotated
@@ -240,14 +255,16 @@ size_t uq_decode_workspace_bytes(const uq_kv_cache* cache, int32_t num_seqs, int
  *               the next one (no clearing needed).  Its first 4 bytes are the
  *               UQ_FLAG_CHECK error word.  Calls that overlap in time must not
  *               share a workspace.
- *   flags       UQ_FLAG_OUT_ROTATED (FP4), UQ_FLAG_CHECK
+ *   flags       UQ_FLAG_OUT_ROTATED and UQ_FLAG_PV_SCALED (FP4), UQ_FLAG_CHECK
  * num_q_heads must be a multiple of num_kv_heads with a ratio of 1..16,
  * num_seqs at most 8192, max_pages_per_seq at most 2^21 and
  * num_seqs * ceil(max_pages_per_seq / 4) * num_kv_heads below 2^31 (else
  * UQ_ERR_UNSUPPORTED), and sm_scale positive and finite.
  * Accuracy: codes and scales enter exactly; logits and the softmax are float32,
  * probabilities and dequantized values enter the PV product as float16, so V
- * groups must have E <= 13 (|v| <= 49152) to stay finite in float16.
+ * groups must have E <= 13 (|v| <= 49152) to stay finite in float16 (with
+ * UQ_FLAG_PV_SCALED the probabilities are FP8 instead, see there, and V's
+ * codes and scales enter the product exactly).
  */
 int uq_decode_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtype,
                         const int32_t* page_table, int32_t max_pages_per_seq,
@@ -263,8 +280,9 @@ int uq_decode_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtype
  * bytes per GPU it runs on, held until the process ends; the call itself
  * allocates nothing.  The first call on a device finds the array's address
  * (hipGetSymbolAddress) and clears its counters with a fill kernel on `stream`.
- * Arguments and results as uq_decode_attention; in addition num_seqs *
- * num_kv_heads above 65,536 is UQ_ERR_WORKSPACE.  Every call on one GPU shares
+ * Arguments and results as uq_decode_attention, except that UQ_FLAG_CHECK is
+ * refused (UQ_ERR_INVALID_ARG: there is no workspace to hold its error word);
+ * in addition num_seqs * num_kv_heads above 65,536 is UQ_ERR_WORKSPACE.  Every call on one GPU shares
  * the array: calls that overlap in time on one GPU (other streams, other host
  * threads) race and must not be issued; calls in stream order are safe.
  */
@@ -284,8 +302,9 @@ int uq_decode_attention_noalloc(const uq_kv_cache* cache, const void* q, int32_t
  * uq_decode_attention.
  *   k_new, v_new  device [num_seqs][num_kv_heads][head_dim], in_dtype
  *   q             device [num_seqs][num_q_heads][head_dim], in_dtype
- *   flags         UQ_FLAG_OUT_ROTATED as for uq_decode_attention, and
- *                 UQ_FLAG_SCALE_CONSTOPT for the write as for uq_quantize_append
+ *   flags         UQ_FLAG_OUT_ROTATED and UQ_FLAG_PV_SCALED as for
+ *                 uq_decode_attention, and UQ_FLAG_SCALE_CONSTOPT for the write
+ *                 as for uq_quantize_append
  *   other arguments and limits as uq_decode_attention; cache->format must be
  *   UQ_KV_FP4.  Sequences of length 0 write nothing.  The written slot must not
  *   be shared with another sequence's range (it never is when page tables do

@@ -614,13 +614,13 @@ def fold_p_fp8(p, exps, block=32, headroom=0) -> np.ndarray:
     p = np.asarray(p, dtype=np.float64)
     e = np.asarray(exps, dtype=np.int64)
     T = e.size
-    out = np.zeros_like(p)
-    for b0 in range(0, T, block):
-        sl = slice(b0, min(b0 + block, T))
-        M = max(int(e[sl].max()) - headroom, -127)
-        folded = np.ldexp(p[:, sl], (e[sl] - M)[None, :])
-        out[:, sl] = np.ldexp(e4m3_decode(e4m3_encode(folded)), M)
-    return out
+    nb = -(-T // block)
+    padded = np.full(nb * block, -(1 << 20), dtype=np.int64)          # below every exponent
+    padded[:T] = e
+    M = np.maximum(padded.reshape(nb, block).max(axis=1) - headroom, -127)
+    Mt = np.repeat(M, block)[:T]
+    folded = np.ldexp(p, (e - Mt)[None, :])
+    return np.ldexp(e4m3_decode(e4m3_encode(folded)), Mt[None, :])
 
 
 def pv_fp8_scaled(p, codes, scale_bytes, headroom=0) -> np.ndarray:
@@ -658,25 +658,37 @@ def attention_pv_scaled(qhat, k, v_codes, v_scale_bytes, sm_scale, step=SPV_STEP
     takes the exact product instead (no rounding), which makes the result the
     plain softmax attention.  qhat [G][d], k [L][d], v_codes [L][d] (0..15),
     v_scale_bytes [L][d/32] -> [G][d]."""
+    if fold and step % GROUP:
+        raise ValueError("the 32-token blocks of the fold must tile the steps")
     s = sm_scale * (np.asarray(qhat, dtype=np.float64) @ np.asarray(k, dtype=np.float64).T)   # [G][L]
     G, L = s.shape
-    d = np.asarray(v_codes).shape[1]
-    m = np.full(G, -np.inf)
-    l = np.zeros(G)
-    o = np.zeros((G, d))
-    for t0 in range(0, L, step):
-        blk = slice(t0, min(t0 + step, L))
-        ms = s[:, blk].max(axis=1)
-        p = np.exp(s[:, blk] - ms[:, None])
-        if fold:
-            ostep = pv_fp8_scaled(p, v_codes[blk], v_scale_bytes[blk], headroom=SPV_HEADROOM)
-        else:
-            ostep = p @ dequantize_fp4(v_codes[blk], v_scale_bytes[blk])
-        mn = np.maximum(m, ms)
-        a, b = np.exp(m - mn), np.exp(ms - mn)
-        o = o * a[:, None] + ostep * b[:, None]
-        l = l * a + p.sum(axis=1) * b
-        m = mn
+    codes = np.asarray(v_codes)
+    d = codes.shape[1]
+    nS = -(-L // step)
+    sp = np.full((G, nS * step), -np.inf)
+    sp[:, :L] = s
+    ms = sp.reshape(G, nS, step).max(axis=2)                          # [G][steps], each step has a token
+    p = np.exp(sp - np.repeat(ms, step, axis=1))                       # 0 past the sequence
+    if fold:
+        vals = e2m1_decode(codes)
+        e = np.asarray(v_scale_bytes, dtype=np.int64) - 127
+        ops = [fold_p_fp8(p[:, :L], e[:, g], headroom=SPV_HEADROOM) for g in range(d // GROUP)]
+    else:
+        vals = dequantize_fp4(codes, v_scale_bytes)
+        ops = [p[:, :L]] * (d // GROUP)
+    vp = np.zeros((nS * step, d))
+    vp[:L] = vals
+    vp = vp.reshape(nS, step, d)
+    ostep = np.zeros((G, nS, d))                                       # each step's product
+    for g, op in enumerate(ops):
+        cs = slice(GROUP * g, GROUP * (g + 1))
+        opp = np.zeros((G, nS * step))
+        opp[:, :L] = op
+        ostep[:, :, cs] = np.einsum("gst,stc->gsc", opp.reshape(G, nS, step), vp[:, :, cs])
+    lstep = p.reshape(G, nS, step).sum(axis=2)
+    w = np.exp(ms - ms.max(axis=1, keepdims=True))                     # exp(m_s - m)
+    o = np.einsum("gs,gsc->gc", w, ostep)
+    l = (w * lstep).sum(axis=1)
     return o / l[:, None]
 
 

@@ -114,9 +114,10 @@ def oracle_append_all(fmt, wl, chunk=4096):
     return kp, vp
 
 
-def oracle_decode_all(fmt, wl, pools):
+def oracle_decode_all(fmt, wl, pools, pv_scaled=False):
     """Every output row [B][H_q][d] of the oracle's decode over its pools, the
-    (sequence, KV head) pairs on separate threads."""
+    (sequence, KV head) pairs on separate threads (``pv_scaled``: the oracle's
+    scaled-MFMA PV decode)."""
     B, Hq, d = wl.batch, wl.num_q_heads, wl.head_dim
     G = Hq // wl.num_kv_heads
     out = np.zeros((B, Hq, d))
@@ -126,7 +127,7 @@ def oracle_decode_all(fmt, wl, pools):
         rows = [(b, hk * G + g) for g in range(G)]
         out[b, hk * G:(hk + 1) * G] = O.decode_attention_rows(
             FMT_ID[fmt], pools[0], pools[1], wl.num_kv_heads, d, wl.q, wl.page_table, wl.seq_lens, sm_scale(d),
-            rows, in_dtype=wl.in_dtype)
+            rows, in_dtype=wl.in_dtype, pv_scaled=pv_scaled)
 
     _threaded(one, range(B * wl.num_kv_heads))
     return out
@@ -168,15 +169,16 @@ def sm_scale(d):
     return float(np.float32(1.0 / np.sqrt(d)))
 
 
-def oracle_decode(fmt, wl, pools, rows=None, seq_lens=None, k_only=False, signs=None):
+def oracle_decode(fmt, wl, pools, rows=None, seq_lens=None, k_only=False, signs=None, pv_scaled=False, q=None):
     lens = wl.seq_lens if seq_lens is None else seq_lens
+    q = wl.q if q is None else q
     if rows is None:
-        return O.decode_attention(FMT_ID[fmt], pools[0], pools[1], wl.num_kv_heads, wl.head_dim, wl.q,
+        return O.decode_attention(FMT_ID[fmt], pools[0], pools[1], wl.num_kv_heads, wl.head_dim, q,
                                   wl.page_table, lens, sm_scale(wl.head_dim), in_dtype=wl.in_dtype,
-                                  k_only=k_only, signs=signs)
-    return O.decode_attention_rows(FMT_ID[fmt], pools[0], pools[1], wl.num_kv_heads, wl.head_dim, wl.q,
+                                  k_only=k_only, signs=signs, pv_scaled=pv_scaled)
+    return O.decode_attention_rows(FMT_ID[fmt], pools[0], pools[1], wl.num_kv_heads, wl.head_dim, q,
                                    wl.page_table, lens, sm_scale(wl.head_dim), rows, in_dtype=wl.in_dtype,
-                                   k_only=k_only, signs=signs)
+                                   k_only=k_only, signs=signs, pv_scaled=pv_scaled)
 
 
 def oracle_decode_rows_from_inputs(fmt, wl, rows):

@@ -192,12 +192,14 @@ def test_decode_validation(name, fmt):
     assert call(w=None) == B.UQ_ERR_WORKSPACE
     assert call(wb=ws - 1) == B.UQ_ERR_WORKSPACE
     assert call(fl=2) == B.UQ_ERR_INVALID_ARG
-    assert call(fl=8) == B.UQ_ERR_INVALID_ARG
+    assert call(fl=16) == B.UQ_ERR_INVALID_ARG
     assert call(fl=B.UQ_FLAG_CHECK, w=None) == B.UQ_ERR_WORKSPACE                # accepted by every format
     if fmt == B.UQ_KV_FP4:
-        assert call(fl=B.UQ_FLAG_OUT_ROTATED, w=None) == B.UQ_ERR_WORKSPACE     # flag accepted
+        assert call(fl=B.UQ_FLAG_OUT_ROTATED, w=None) == B.UQ_ERR_WORKSPACE     # flags accepted
+        assert call(fl=B.UQ_FLAG_PV_SCALED, w=None) == B.UQ_ERR_WORKSPACE
     else:
         assert call(fl=B.UQ_FLAG_OUT_ROTATED) == B.UQ_ERR_INVALID_ARG
+        assert call(fl=B.UQ_FLAG_PV_SCALED) == B.UQ_ERR_INVALID_ARG
     if fmt == B.UQ_KV_BF16:
         assert call(qd=B.UQ_IN_F32) == B.UQ_ERR_UNSUPPORTED
     assert call(B_=0, q=None, pt=None, sl=None, out=None, w=None) == B.UQ_OK
@@ -225,8 +227,9 @@ def test_fused_step_validation():
     assert call(dt=4) == B.UQ_ERR_INVALID_ARG
     assert call(Hq=15) == B.UQ_ERR_UNSUPPORTED
     assert call(w=None) == B.UQ_ERR_WORKSPACE
-    assert call(fl=8) == B.UQ_ERR_INVALID_ARG
+    assert call(fl=16) == B.UQ_ERR_INVALID_ARG
     assert call(fl=B.UQ_FLAG_OUT_ROTATED, w=None) == B.UQ_ERR_WORKSPACE
+    assert call(fl=B.UQ_FLAG_PV_SCALED | B.UQ_FLAG_SCALE_CONSTOPT, w=None) == B.UQ_ERR_WORKSPACE
     assert call(fl=B.UQ_FLAG_SCALE_CONSTOPT | B.UQ_FLAG_OUT_ROTATED, w=None) == B.UQ_ERR_WORKSPACE
     assert call(fl=B.UQ_FLAG_CHECK | B.UQ_FLAG_SCALE_CONSTOPT, w=None) == B.UQ_ERR_WORKSPACE
     assert call(B_=0, k=None, v=None, q=None, pt=None, sl=None, out=None, w=None) == B.UQ_OK
@@ -248,6 +251,7 @@ def test_noalloc_decode_validation():
     assert call(scale=0.0) == B.UQ_ERR_INVALID_ARG
     assert call(fl=2) == B.UQ_ERR_INVALID_ARG
     assert call(fl=B.UQ_FLAG_CHECK) == B.UQ_ERR_INVALID_ARG      # its error word would be in the hidden scratch
+    assert call(fl=B.UQ_FLAG_PV_SCALED, Hq=15) == B.UQ_ERR_UNSUPPORTED   # the flag passes, the shape does not
     assert call(mp=(1 << 21) + 1, B_=1) == B.UQ_ERR_UNSUPPORTED
     # more (sequence, KV head) items than the static array's 65,536 counters
     assert call(c=cache(B.UQ_KV_FP4, heads=9), B_=8000, Hq=9) == B.UQ_ERR_WORKSPACE
