@@ -6,10 +6,12 @@ One step is one pass of the hot path over a batch: append the new token of every
 sequence to the paged cache (rotate + quantize + pack for FP4) and run decode
 attention over the whole context (query rotation to E4M3, split-K attention,
 merge + inverse rotation).  The FP4 step is one launch of the fused entry point
-(uq_append_decode_attention) when every sequence adds one token; the FP8 / BF16
-baselines (append kernel, then decode kernel) are reported beside it, and with
---unfused the FP4 step as two launches as well.  Default workload: 64 sequences x 8,192 context,
-64 query heads / 8 KV heads, head_dim 128, 16-token pages randomly permuted.
+(uq_append_decode_attention) when every sequence adds one token; the FP4 step with
+the PV on the scaled FP4 x FP8 matrix instruction (UQ_FLAG_PV_SCALED) and the
+FP8 / BF16 baselines (append kernel, then decode kernel) are reported beside it.
+Workloads: 64 sequences x 8,192 context (the headline), 8 x 65,536 and 128 ragged
+sequences with 256-token appends; 64 (32) query heads / 8 (4) KV heads,
+head_dim 128, 16-token pages randomly permuted.
 
 Prints one JSON line.  Progress goes to stderr.
 """
