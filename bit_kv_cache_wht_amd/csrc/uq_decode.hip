@@ -103,6 +103,16 @@ __device__ __forceinline__ void split_f16x2(float p0, float p1, uint32_t& hi, ui
       : "v"(hi), "v"(p0), "v"(p1));
 }
 
+// p0, p1 ~= hi + lo as packed bf16 pairs: hi = bf16(p) (nearest even), lo =
+// bf16(p - hi) (the float32 difference is exact: hi is within 2^-9 of p); 16
+// significant bits of each probability.
+__device__ __forceinline__ void split_bf16x2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
+  const __bf16 l0 = (__bf16)(p0 - (float)h0), l1 = (__bf16)(p1 - (float)h1);
+  hi = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+  lo = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+}
+
 // E4M3 query as the FP8 B operand: lane (h, j) holds k = 16j..16j+15 and
 // 64+16j..64+16j+15 of query row h (zero rows past the GQA group).
 template <int D> __device__ __forceinline__ v8i load_q_fp8(const uint8_t* qrow, bool valid, int j4) {
@@ -694,7 +704,10 @@ template <int D> struct Fp8Pol {
   __device__ static int channel(int tile, int j4, int v) { return 16 * tile + 4 * j4 + v; }
 };
 
+// BF16 baseline: K, q and V enter bf16 MFMAs as stored (every bf16 value exact),
+// P as bf16 hi + lo.
 template <int D> struct Bf16Pol {
+  static constexpr bool kPBf16 = true;  // the PV takes P as bf16 hi + lo
   static constexpr int kShareAlpha = 3;
   static constexpr int kOcc = 1;
   static constexpr int kBuf = 2;
@@ -709,20 +722,12 @@ template <int D> struct Bf16Pol {
   // loads measured ~2% slower (the FP4 and FP8 policies gain 7-11% from them).
   struct KStep { uint4 k[4][kK]; };      // K bf16 channels 32kk + 8j..+7 of token slot 4m + (lane%16)%4
   struct VStep { uint4 v[kTiles][2]; };  // V bf16 of channel 16t + lane%16, slots 0..7 and 8..15
-  // q as f16 B operands: MFMA kk, lane (h, j) holds channels 32kk + 8j..+7 of head h
-  struct QOp { v8h b[kK]; };
-  // bf16 pairs -> f16 pairs (exact for |x| >= 2^-14; smaller values lose bits as
-  // f16 subnormals, far below the output tolerance)
-  __device__ static uint32_t bf2h(uint32_t w) {
-    return pack_h2((_Float16)__uint_as_float(w << 16), (_Float16)__uint_as_float(w & 0xFFFF0000u));
-  }
-  __device__ static v8h bf2h8(const uint4& u) {
-    return __builtin_bit_cast(v8h, make_uint4(bf2h(u.x), bf2h(u.y), bf2h(u.z), bf2h(u.w)));
-  }
+  // q as bf16 B operands: MFMA kk, lane (h, j) holds channels 32kk + 8j..+7 of head h
+  struct QOp { v8bf b[kK]; };
   __device__ static void load_q(QOp& qo, const uint8_t* qrow, bool valid, int j4, int) {
 #pragma unroll
     for (int kk = 0; kk < kK; ++kk)
-      qo.b[kk] = bf2h8(valid ? load16(qrow + 2 * (32 * kk + 8 * j4)) : make_uint4(0, 0, 0, 0));
+      qo.b[kk] = __builtin_bit_cast(v8bf, valid ? load16(qrow + 2 * (32 * kk + 8 * j4)) : make_uint4(0, 0, 0, 0));
   }
   __device__ static void load_k(KStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
                                 const PageGeo& g, int r16, int j4) {
@@ -743,16 +748,13 @@ template <int D> struct Bf16Pol {
       st.v[t][1] = load16(vb + 2 * ((16 * t + r16) * kPage + 8));
     }
   }
-  // QK on f16 MFMAs after widening K: feeding the loaded bf16 registers straight
-  // to bf16 MFMAs gave wrong logits on a wave's later steps (reproduced by the
-  // multi-step parity cases), while the widened form is exact and correct.
   __device__ static void qk(const KStep& st, const QOp& qo, v4f (&S)[4]) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       v4f acc = {0, 0, 0, 0};
 #pragma unroll
       for (int kk = 0; kk < kK; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf2h8(st.k[m][kk]), qo.b[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, st.k[m][kk]), qo.b[kk], acc, 0, 0, 0);
       S[m] = acc;
     }
   }
@@ -769,22 +771,26 @@ template <int D> struct Bf16Pol {
         st.v[t][half].z &= k[4 * half + 2]; st.v[t][half].w &= k[4 * half + 3];
       }
   }
-  __device__ static void pv(const VStep& st, const v8h (&P)[2][2], v4f (&O)[kTiles], int) {
+  __device__ static void pv(const VStep& st, const v8bf (&P)[2][2], v4f (&O)[kTiles], int) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const uint32_t c[4] = {st.v[t][half].x, st.v[t][half].y, st.v[t][half].z, st.v[t][half].w};
-        O[t] = mma2(__builtin_bit_cast(v8h, make_uint4(bf2h(c[0]), bf2h(c[1]), bf2h(c[2]), bf2h(c[3]))), P[half], O[t]);
+        const v8bf a = __builtin_bit_cast(v8bf, st.v[t][half]);
+        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, P[half][0], O[t], 0, 0, 0);
+        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, P[half][1], O[t], 0, 0, 0);
       }
     }
   }
   __device__ static int channel(int tile, int j4, int v) { return 16 * tile + 4 * j4 + v; }
 };
 
-// Policies with the scaled-MFMA PV declare kSpv.
+// Policies with the scaled-MFMA PV declare kSpv; those whose PV takes P as
+// bf16 hi + lo (instead of f16 hi + lo) declare kPBf16.
 template <class P, class = void> struct SpvOf : std::false_type {};
 template <class P> struct SpvOf<P, std::void_t<decltype(P::kSpv)>> : std::bool_constant<P::kSpv> {};
+template <class P, class = void> struct PBf16Of : std::false_type {};
+template <class P> struct PBf16Of<P, std::void_t<decltype(P::kPBf16)>> : std::bool_constant<P::kPBf16> {};
 
 // ------------------------------------------------------------------ plan
 // The work of a call is the list of steps (4 pages) of all (sequence b, KV head
@@ -1615,14 +1621,18 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         for (int i = 1; i < TOK; ++i) psum += pf[i];
       }
       l_run += psum;
-      v8h Pm[TOK / 8][2];
+      using POp = std::conditional_t<PBf16Of<Pol>::value, v8bf, v8h>;
+      POp Pm[TOK / 8][2];
 #pragma unroll
       for (int half = 0; half < TOK / 8; ++half) {
         uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) split_f16x2(pf[8 * half + 2 * i], pf[8 * half + 2 * i + 1], hw[i], lw[i]);
-        Pm[half][0] = __builtin_bit_cast(v8h, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-        Pm[half][1] = __builtin_bit_cast(v8h, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (PBf16Of<Pol>::value) split_bf16x2(pf[8 * half + 2 * i], pf[8 * half + 2 * i + 1], hw[i], lw[i]);
+          else split_f16x2(pf[8 * half + 2 * i], pf[8 * half + 2 * i + 1], hw[i], lw[i]);
+        }
+        Pm[half][0] = __builtin_bit_cast(POp, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        Pm[half][1] = __builtin_bit_cast(POp, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
       Pol::mask_v(st, nvalid);
       Pol::pv(st, Pm, O, lane_head);

@@ -345,7 +345,8 @@ int uq_prefill_attention(const uq_kv_cache* cache, const void* q, int32_t q_dtyp
 
 /* FP8 baseline decode: same arguments; cache->format must be UQ_KV_FP8; the
  * query is rounded to E4M3 without rotation and `out` needs no unrotation
- * (flags must be 0). */
+ * (flags: 0 or UQ_FLAG_CHECK).  E4M3 K, q and V convert exactly to float16 for
+ * the matrix products; P enters as float16 hi + lo, as in the FP4 decode. */
 int uq_decode_attention_fp8(const uq_kv_cache* cache, const void* q, int32_t q_dtype,
                             const int32_t* page_table, int32_t max_pages_per_seq,
                             const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -353,7 +354,9 @@ int uq_decode_attention_fp8(const uq_kv_cache* cache, const void* q, int32_t q_d
                             uint32_t flags, uq_stream_t stream);
 
 /* BF16 baseline decode: same arguments; cache->format must be UQ_KV_BF16 and
- * q_dtype must be UQ_IN_BF16 (flags must be 0). */
+ * q_dtype must be UQ_IN_BF16 (flags: 0 or UQ_FLAG_CHECK).  K, q and V enter
+ * bf16 matrix products as stored (every finite bf16 value exactly; products
+ * summed in float32), P as bf16 hi + lo (16 significant bits). */
 int uq_decode_attention_bf16(const uq_kv_cache* cache, const void* q, int32_t q_dtype,
                              const int32_t* page_table, int32_t max_pages_per_seq,
                              const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,

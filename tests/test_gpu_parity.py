@@ -325,3 +325,25 @@ def test_fp4_decode_with_disparate_group_scales():
     want = oracle_decode("fp4", wl, pools)
     # compare per output element relative to that row's scale
     assert_close(got / np.abs(want).max(), want / np.abs(want).max(), "fp4 wide scales (normalized)")
+
+
+def _scale_bf16_bits(bits, k):
+    """bf16 bit patterns times 2^k (exact: normal values stay normal here)."""
+    f = (np.asarray(bits).astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** k)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_bf16_decode_outside_the_float16_range():
+    # The BF16 baseline takes K, q and V into bf16 matrix products as stored:
+    # values far outside float16's range (V near 2^60, K near 2^-60, q near 2^60)
+    # must give the oracle's result, scaled.
+    wl = _wl("gqa_ragged")
+    wl.k = _scale_bf16_bits(wl.k, -60)
+    wl.v = _scale_bf16_bits(wl.v, 60)
+    wl.q = _scale_bf16_bits(wl.q, 60)
+    pools = oracle_append("bf16", wl)
+    announce("decode bf16 with |V| ~ 2^60, |K| ~ 2^-60")
+    got = gpu_decode("bf16", wl, gpu_cache("bf16", wl, pools))
+    want = oracle_decode("bf16", wl, pools)
+    assert np.abs(want).max() > 2.0 ** 55
+    assert_close(got * 2.0 ** -60, want * 2.0 ** -60, "bf16 outside the float16 range (scaled by 2^-60)")
