@@ -55,49 +55,69 @@ __global__ __launch_bounds__(256) void append_fp4_kernel(AppendArgs a) {
 // Large writes: a persistent grid-stride loop over groups of RPW rows per wave,
 // each wave fetching its next group's inputs (and slots) before working on the
 // current one, so that the float64 work of one group hides the memory latency
-// of the next.  Rows r < 2T H are indexed in 32 bits (the host bounds T H).
+// of the next.  A group is RPW consecutive tokens of one KV head of K or of V
+// (group g: K|V head kvh = g / nblk, tokens RPW (g % nblk) ..), so that when
+// the tokens fill a page's slots in order, the lanes of one store instruction
+// write adjacent bytes of a page (V: one 16-byte slot row per channel pair; K:
+// whole rows) and the stores merge into full lines.
 template <int D, int IN, int LPR, bool RV>
 __global__ __launch_bounds__(256) void append_fp4_stream_kernel(AppendArgs a) {
   using Row = Fp4Row<D, IN, LPR>;
   constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63;
   const int p = lane % LPR;
-  const int kv_rows = a.T * a.H, nrows = 2 * kv_rows;
-  const int groups = (nrows + RPW - 1) / RPW;
+  const int nblk = (a.T + RPW - 1) / RPW;          // token blocks per K|V head
+  const int groups = 2 * a.H * nblk;               // < 2^31: the host bounds 2 T H
   const int nwaves = gridDim.x * (blockDim.x >> 6);
   int g = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (g >= groups) return;                         // whole wave idle (no barriers used)
+  const double rblk = 1.0 / (double)nblk;
   struct In {
     Row x;
-    int slot, tr;
+    int slot, tr, h;
     bool is_v, live;
   };
   auto fetch = [&](In& in, int grp) {
-    const int row = grp * RPW + lane / LPR;
-    in.live = row < nrows;
-    const int r = in.live ? row : 0;               // idle lanes read row 0 (in bounds)
-    in.is_v = r >= kv_rows;
-    in.tr = in.is_v ? r - kv_rows : r;             // token * H + head
-    in.slot = a.slot_mapping[in.tr / a.H];
+    // grp / nblk through a float64 reciprocal (grp < 2^31: the quotient is off
+    // by at most one), then corrected
+    int kvh = (int)((double)grp * rblk);
+    kvh -= kvh * nblk > grp ? 1 : 0;
+    kvh += (kvh + 1) * nblk <= grp ? 1 : 0;
+    const int t = (grp - kvh * nblk) * RPW + lane / LPR;
+    in.live = t < a.T;
+    const int tt = in.live ? t : 0;                // idle lanes read token 0 (in bounds)
+    in.is_v = kvh >= a.H;
+    in.h = in.is_v ? kvh - a.H : kvh;
+    in.tr = tt * a.H + in.h;                       // token * H + head
+    in.slot = a.slot_mapping[tt];
     in.x.load(in.is_v ? a.v : a.k, in.tr, p);
   };
-  In cur, nxt;
-  fetch(cur, g);
-  for (;;) {
-    const int gn = g + nwaves;
-    const bool more = gn < groups;                 // wave-uniform
-    if (more) fetch(nxt, gn);
-    cur.x.template quantize<RV>(p, a.constopt != 0, a.rot, cur.is_v);
-    if (cur.live && cur.slot >= 0) {
-      const int h = cur.tr % a.H;
-      const int page = cur.slot >> 4, off = cur.slot & 15;
-      uint8_t* blk = (cur.is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes +
-                     (int64_t)fp4_block_pos(h, page, a.H, a.hmask) * Row::BLK;
-      if (!cur.is_v) cur.x.store_k(blk, off, p);
-      else cur.x.store_v(blk, off, p);
+  auto work = [&](In& in) {
+    in.x.template quantize<RV>(p, a.constopt != 0, a.rot, in.is_v);
+    if (in.live && in.slot >= 0) {
+      const int page = in.slot >> 4, off = in.slot & 15;
+      uint8_t* blk = (in.is_v ? a.v_pool : a.k_pool) + (int64_t)page * a.page_bytes +
+                     (int64_t)fp4_block_pos(in.h, page, a.H, a.hmask) * Row::BLK;
+      if (!in.is_v) in.x.store_k(blk, off, p);
+      else in.x.store_v(blk, off, p);
     }
-    if (!more) break;
-    cur = nxt;
+  };
+  // Two input buffers used in turn (no copy between iterations).  The next
+  // group is fetched unconditionally (the last wave's fetch reads the final
+  // group again and goes unused): a fetch on one path only would make the wait
+  // for the current group's loads also wait for the prefetch.
+  In b0, b1;
+  fetch(b0, g);
+  for (;;) {
+    int gn = g + nwaves;
+    fetch(b1, min(gn, groups - 1));
+    work(b0);
+    if (gn >= groups) break;
+    g = gn;
+    gn = g + nwaves;
+    fetch(b0, min(gn, groups - 1));
+    work(b1);
+    if (gn >= groups) break;
     g = gn;
   }
 }

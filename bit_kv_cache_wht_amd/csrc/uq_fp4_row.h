@@ -54,6 +54,25 @@ template <int D, int IN, int LPR> struct Fp4Row {
   __device__ __forceinline__ void quantize(int p, bool constopt, const Rot& rot, bool is_v) {
     const bool rotate = !RV || !(is_v && rot.k_only != 0u);   // the same for all lanes of the row
     double x[E];
+    to_f64(x);
+    if (rotate) {
+      if (RV && has_signs(rot)) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = flip_sign(x[e], sign_mask(rot, E * p + e));
+      }
+      butterfly<1, E>(x);
+      // the partner lanes of a cross stage belong to the same row
+      if constexpr (LPR > 1) cross_stage<E, 1>(x, p);
+      if constexpr (LPR > 2) cross_stage<E, 2>(x, p);
+      if constexpr (LPR > 4) cross_stage<E, 4>(x, p);
+      if constexpr (LPR > 8) cross_stage<E, 8>(x, p);
+    }
+
+    codes(x, rotate ? wht_c<D>() : 1.0, constopt);
+  }
+
+  // The lane's inputs as float64, in raw order (exact).
+  __device__ __forceinline__ void to_f64(double (&x)[E]) const {
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
       const uint32_t d[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
@@ -67,33 +86,29 @@ template <int D, int IN, int LPR> struct Fp4Row {
         }
       }
     }
-    if (rotate) {
-      if (RV && has_signs(rot)) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = flip_sign(x[e], sign_mask(rot, E * p + e));
-      }
-#pragma unroll
-      for (int hh = 1; hh < E; hh <<= 1)
-#pragma unroll
-        for (int i = 0; i < E; i += 2 * hh)
-#pragma unroll
-          for (int j = i; j < i + hh; ++j) {
-            const double a0 = x[j], a1 = x[j + hh];
-            x[j] = a0 + a1;
-            x[j + hh] = a0 - a1;
-          }
-      // the partner lanes of a cross stage belong to the same row
-      if constexpr (LPR > 1) cross_stage<E, 1>(x, p);
-      if constexpr (LPR > 2) cross_stage<E, 2>(x, p);
-      if constexpr (LPR > 4) cross_stage<E, 4>(x, p);
-      if constexpr (LPR > 8) cross_stage<E, 8>(x, p);
-    }
+  }
 
+  // Sylvester butterfly stages h = H0, 2 H0, .. < H1 over the local index.
+  template <int H0, int H1> __device__ __forceinline__ static void butterfly(double (&x)[E]) {
+#pragma unroll
+    for (int hh = H0; hh < H1; hh <<= 1)
+#pragma unroll
+      for (int i = 0; i < E; i += 2 * hh)
+#pragma unroll
+        for (int j = i; j < i + hh; ++j) {
+          const double a0 = x[j], a1 = x[j + hh];
+          x[j] = a0 + a1;
+          x[j + hh] = a0 - a1;
+        }
+  }
+
+  // Group absmax, UE8M0 exponent and E2M1 codes of the lane's rotated channels
+  // x (not yet multiplied by c).
+  __device__ __forceinline__ void codes(double (&x)[E], double c, bool constopt) {
     // The normalized channel is RN(c_d x + 0) (one float64 rounding; the + 0
     // makes an exact zero +0 whatever the butterfly's signed zeros; unrotated,
     // c = 1 and x + 0 is x with a zero of either sign made +0).  Rounding is
     // monotone, so the group absmax of those is RN(c max |x|).
-    const double c = rotate ? wht_c<D>() : 1.0;
     constexpr int EG = E / GPL;                           // channels of one group held by the lane
 #pragma unroll
     for (int g = 0; g < GPL; ++g) {
@@ -105,18 +120,34 @@ template <int D, int IN, int LPR> struct Fp4Row {
       const int xg = constopt ? constopt_exponent(m * c) : scale_exponent(m * c);
       ex[g] = xg;
       if (xg >= -100 && xg <= 100) {
-        // hardware E2M1 rounding (nearest even, saturating at 6, sign kept) of
-        // the round-to-odd float32 value, divided by the scale 2^xg
+        // hardware E2M1 rounding (nearest even, saturating at 6, sign kept) of a
+        // float32 image, divided by the scale 2^xg.  The image is the float32
+        // nearest the value: rounding that again to E2M1 decides as the value
+        // itself would unless the image is exactly an E2M1 decision point
+        // ((2k + 1) 2^(xg-2) for k < 3, 2.5, 3.5 or 5 times 2^xg), and every
+        // decision point has its 21 low significand bits clear.  When some
+        // lane of the wave holds an image with those bits clear (exact zeros
+        // included), the wave takes the round-to-odd image instead, which
+        // keeps every decision.
         const float sc = __uint_as_float((uint32_t)(xg + 127) << 23);
+        float f[EG];
+        uint32_t low = ~0u;
+#pragma unroll
+        for (int i = 0; i < EG; ++i) {
+          f[i] = (float)__builtin_fma(x[EG * g + i], c, 0.0);
+          low = min(low, __float_as_uint(f[i]) << 11);
+        }
+        if (__builtin_expect(__any(low == 0u), 0)) {
+#pragma unroll
+          for (int i = 0; i < EG; ++i) f[i] = f32_round_to_odd(__builtin_fma(x[EG * g + i], c, 0.0));
+        }
 #pragma unroll
         for (int q = EG / 8 * g; q < EG / 8 * (g + 1); ++q) {
-          float f[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) f[i] = f32_round_to_odd(__builtin_fma(x[8 * q + i], c, 0.0));
-          uint32_t acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0], f[1], sc, 0);
-          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[2], f[3], sc, 1);
-          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[4], f[5], sc, 2);
-          w[q] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[6], f[7], sc, 3);
+          const int i0 = 8 * q - EG * g;
+          uint32_t acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[i0], f[i0 + 1], sc, 0);
+          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[i0 + 2], f[i0 + 3], sc, 1);
+          acc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[i0 + 4], f[i0 + 5], sc, 2);
+          w[q] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(acc, f[i0 + 6], f[i0 + 7], sc, 3);
         }
       } else {                                            // scales beyond the float32 range: float64 rounding
 #pragma unroll
@@ -153,11 +184,12 @@ template <int D, int IN, int LPR> struct Fp4Row {
   // Stores into the V head block `blk` at page slot `off`: channel pair c in
   // code row 16 (c % CPL) + c / CPL, column `off`; scales [group][slot].
   __device__ __forceinline__ void store_v(uint8_t* blk, int off, int p) const {
+    // pair c = (E/2) p + i lies in row 16 (i % CPL) + ((E/2) p + i) / CPL: a lane
+    // base and constant offsets (E/2 is a multiple of CPL)
+    static_assert((E / 2) % CPL == 0, "a lane's channel pairs start at a multiple of CPL");
+    uint8_t* b = blk + off + kPage * ((E / 2) / CPL * p);
 #pragma unroll
-    for (int i = 0; i < E / 2; ++i) {
-      const int c = (E / 2) * p + i;
-      blk[(16 * (c % CPL) + c / CPL) * kPage + off] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
-    }
+    for (int i = 0; i < E / 2; ++i) b[(16 * (i % CPL) + i / CPL) * kPage] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
     if (p % LPG == 0) {
 #pragma unroll
       for (int g = 0; g < GPL; ++g) blk[CODE + (p / LPG * GPL + g) * kPage + off] = (uint8_t)(ex[g] + 127);
