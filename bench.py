@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
                     help="KIND CSV [CSV ...]: write the counter summary of one --pmc-pass kind from rocprofv3 "
                          "counter_collection.csv files into profiles/")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("KIND", "STATS_CSV", "TRACE_CSV"),
+                    help="write the kernel-trace summary of one kind (decode, prefill) from a rocprofv3 "
+                         "--kernel-trace --stats run into profiles/")
     return ap.parse_args()
 
 
@@ -220,6 +223,67 @@ def write_traffic_summary(derived, kern, copy):
               ""]
     with open(TRAFFIC_SUMMARY, "w") as fh:
         fh.write("\n".join(lines))
+
+
+TRACE_KINDS = {
+    "decode": dict(match="Fp4PairPol", out="decode_fp4_64x8192_kernel_trace.md",
+                   cmd="rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 -u bench.py "
+                       "--workloads decode_gqa --no-cpu-baseline --no-prefill --no-append",
+                   title="decode_gqa 64 x 8192 (64 q / 8 kv heads, d 128), FP4 step = one fused launch"),
+    "prefill": dict(match="prefill_kernel", out="prefill_fp4_ragged_kernel_trace.md",
+                    cmd="rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o trace -- python3 -u bench.py "
+                        "--workloads ragged --no-cpu-baseline --no-baselines --no-pv-scaled --no-append",
+                    title="chunked prefill on ragged_128 (128 sequences, 256-token chunks, 32 q / 4 kv heads, d 128)"),
+}
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def summarize_trace(kind, stats_csv, trace_csv):
+    """profiles/ summary of a rocprofv3 --kernel-trace --stats run of the command in
+    TRACE_KINDS[kind]: the per-kernel statistics, and for the decode the FP4 launches
+    of bench.py's passes taken from the dispatch order (the last `steps` of them are
+    the event-pair pass after a 1 GiB read each, the `steps` before that the
+    whole-step pass after the same read, the `steps` before those the warm pass)."""
+    k = TRACE_KINDS[kind]
+    stats = _csv_rows(stats_csv)
+    pick = lambda row, *names: next(row[n] for n in names if n in row)
+    lines = [f"# Kernel trace: {k['title']}", "", "Command (from the repository root):", "", f"    {k['cmd']}", "",
+             f"then `python3 bench.py --summarize-trace {kind} <dir>/trace_kernel_stats.csv "
+             "<dir>/trace_kernel_trace.csv`.", "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    rows = sorted(stats, key=lambda r: -float(pick(r, "TotalDurationNs")))
+    for r in rows[:12]:
+        name = pick(r, "Name", "KernelName")
+        name = name if len(name) <= 100 else name[:97] + "..."
+        lines.append(f"| `{name}` | {pick(r, 'Calls')} | {float(pick(r, 'AverageNs')) / 1e3:.2f} | "
+                     f"{float(pick(r, 'MinNs')) / 1e3:.2f} | {float(pick(r, 'MaxNs')) / 1e3:.2f} | "
+                     f"{float(pick(r, 'Percentage')):.2f} |")
+    trace = _csv_rows(trace_csv)
+    durs = [(int(pick(r, "Start_Timestamp")), (int(pick(r, "End_Timestamp")) - int(pick(r, "Start_Timestamp"))) / 1e3)
+            for r in trace if k["match"] in pick(r, "Kernel_Name", "KernelName")]
+    durs = [d for _, d in sorted(durs)]
+    lines.append("")
+    if kind == "decode" and len(durs) >= 300:
+        n = 100
+        warm, whole, ev = durs[-3 * n:-2 * n], durs[-2 * n:-n], durs[-n:]
+        lines += [f"FP4 decode launches ({k['match']}, {len(durs)} in all), the last three passes of {n}:", "",
+                  f"- warm (back to back): mean {np.mean(warm):.2f} us, median {np.median(warm):.2f} us",
+                  f"- whole steps after a 1 GiB read each: mean {np.mean(whole):.2f} us, median "
+                  f"{np.median(whole):.2f} us",
+                  f"- event-pair and clock pass after a 1 GiB read each: mean {np.mean(ev):.2f} us, median "
+                  f"{np.median(ev):.2f} us (bench `roofline.kernel_us` is the mean of the kernel's own clock "
+                  "span over the same launches)"]
+    elif durs:
+        lines += [f"`{k['match']}` launches: {len(durs)}, mean {np.mean(durs):.2f} us, median {np.median(durs):.2f} us"]
+    lines.append("")
+    with open(os.path.join(PROFILES, k["out"]), "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 def stream_read_gbs(reps=20):
@@ -429,9 +493,12 @@ class Runner:
             self.v_new = self.v_new.reshape(wl.batch, wl.num_kv_heads, d)
         torch.cuda.synchronize()
 
-    def step(self, ev=None, ev_app=None):
+    def step(self, ev=None, ev_app=None, clk=None):
         """One step; `ev`: a hipEvent_t pair the library records around its decode
-        kernel; `ev_app`: torch events recorded around the append launch."""
+        kernel; `ev_app`: torch events recorded around the append launch; `clk`: a
+        device pair the decode kernel fills with its wall-clock span."""
+        if clk is not None:
+            self.clock_khz = self.uq.uq_profile_next_decode_clock(clk)
         if self.fused:
             if ev is not None:
                 self.uq.uq_profile_next_decode(ev[0], ev[1])
@@ -487,11 +554,14 @@ class Runner:
             whole[i][1].record()
         torch.cuda.synchronize()
         evs = HipEvents(steps)
+        clocks = torch.zeros((steps, 2), dtype=torch.int64, device="cuda")
+        clocks[:, 0] = -1                          # the unsigned maximum
         for i in range(steps):
             if scrub is not None:
                 scrub.max()
-            self.step(evs.pairs[i])
+            self.step(evs.pairs[i], clk=clocks[i])
         torch.cuda.synchronize()
+        ticks = clocks.cpu().numpy().view(np.uint64).astype(np.float64)
         app = None
         if not self.fused:
             app = [(ev(), ev()) for _ in range(steps)]
@@ -504,6 +574,7 @@ class Runner:
                               p90=float(np.percentile(v, 90)))
         res["step_ms"] = stat([a.elapsed_time(b) for a, b in whole])
         res["decode_ms"] = stat([evs.elapsed_ms(i) for i in range(steps)])
+        res["decode_clock_ms"] = stat(list((ticks[:, 1] - ticks[:, 0]) / self.clock_khz))
         if app is not None:
             res["append_ms"] = stat([a.elapsed_time(b) for a, b in app])
         evs.close()
@@ -640,14 +711,15 @@ def time_workload(args, wl, fmts, torch):
         scrub = torch.ones((args.scrub_mb << 20) // 4, dtype=torch.int32, device="cuda") if args.scrub_mb else None
         res = r.run(args.steps, args.warmup, scrub, settle_s=args.settle_ms * 1e-3)
         by = r.kernel_bytes()
-        dec_us = res["decode_ms"]["mean"] * 1e3
+        dec_us = res["decode_clock_ms"]["mean"] * 1e3
         e = {
             "us_per_step": round(res["step_ms"]["median"] * 1e3, 2),
             "us_per_step_p10_p90": [round(res["step_ms"]["p10"] * 1e3, 2), round(res["step_ms"]["p90"] * 1e3, 2)],
             "us_per_step_warm": round(res["warm_ms_per_step"] * 1e3, 2),
             "fused": r.fused,
             "decode_kernel_us": round(dec_us, 2),
-            "decode_kernel_us_median": round(res["decode_ms"]["median"] * 1e3, 2),
+            "decode_kernel_us_median": round(res["decode_clock_ms"]["median"] * 1e3, 2),
+            "decode_kernel_us_event_pairs": round(res["decode_ms"]["mean"] * 1e3, 2),
             "decode_algo_bytes": by["decode"],
             "decode_gbs": round(by["decode"] / (dec_us * 1e-6) / 1e9, 1),
             "frac_hbm_peak": round(by["decode"] / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -677,6 +749,9 @@ def main():
     args = parse()
     if args.summarize_pmc:
         summarize_counters(args.summarize_pmc[0], args.summarize_pmc[1:])
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this hot path needs no "
@@ -736,8 +811,11 @@ def main():
                      "frac": head["frac_hbm_peak"], "traffic": traffic,
                      "kernel": "decode_kernel<Fp4PairPol<128>> (KV-head pairs" + (", fused append)" if fused else ")"),
                      "kernel_us": head["decode_kernel_us"],
-                     "timing": "mean over the scrubbed steps of HIP events the library records on the launch "
-                               "stream right before and after the kernel launch",
+                     "timing": "mean over the scrubbed steps of the kernel's own span: the device's constant "
+                               "wall clock read by the first workgroup as it starts and by the last as it ends "
+                               "(uq_profile_next_decode_clock); HIP events the library records around the same "
+                               "launches read more (kernel_us_event_pairs: launch overhead included)",
+                     "kernel_us_event_pairs": head["decode_kernel_us_event_pairs"],
                      "achieved_warm": head.get("decode_gbs_warm"), "frac_warm": head.get("frac_hbm_peak_warm"),
                      "algo_bytes_per_launch": head["decode_algo_bytes"]},
         "baselines": {f: {"us_per_step": results[names[0]][f]["us_per_step"],

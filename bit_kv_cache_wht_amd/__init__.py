@@ -37,6 +37,7 @@ from ._binding import (  # noqa: F401
     uq_last_hip_error,
     uq_page_bytes,
     uq_profile_next_decode,
+    uq_profile_next_decode_clock,
     uq_stream_read,
     uq_prefill_attention,
     uq_quantize_append,

@@ -57,6 +57,7 @@ _SIGS = {
     "uq_decode_attention_fp8": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
     "uq_decode_attention_bf16": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
     "uq_profile_next_decode": (ctypes.c_int, [_P, _P]),
+    "uq_profile_next_decode_clock": (ctypes.c_int, [_P, _P]),
     "uq_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
     "uq_prefill_attention": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _U, _P]),
     "uq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -362,6 +363,18 @@ def uq_decode_attention_bf16(cache, q, page_table, seq_lens, sm_scale, out, work
 def uq_profile_next_decode(start_event, stop_event) -> None:
     """Record two hipEvent_t handles (ints) around the next decode call's main kernel."""
     _check("uq_profile_next_decode", lib().uq_profile_next_decode(start_event, stop_event))
+
+
+def uq_profile_next_decode_clock(clocks) -> int:
+    """Arm the wall-clock span of the next decode call's main kernel: `clocks` is a
+    device tensor of two int64 set to (-1, 0) (the unsigned maximum and zero);
+    the kernel leaves (earliest workgroup start, latest workgroup end) there.
+    Returns the clock's rate in kHz."""
+    _need(clocks is not None and clocks.numel() == 2 and clocks.element_size() == 8, "clocks: two 64-bit integers")
+    _on_device(clocks=clocks)
+    khz = ctypes.c_int32(0)
+    _check("uq_profile_next_decode_clock", lib().uq_profile_next_decode_clock(_ptr(clocks), ctypes.byref(khz)))
+    return khz.value
 
 
 def uq_stream_read(src, sink, stream=None) -> None:

@@ -10,6 +10,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+thread_local uint64_t* g_prof_clocks = nullptr;
 
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return UQ_OK;
@@ -209,6 +210,8 @@ int decode_common(const uq_kv_cache* cache, int format, const void* q, int32_t q
   a.v_new = v_new;
   a.ev_start = g_prof_start;
   a.ev_stop = g_prof_stop;
+  a.clocks = g_prof_clocks;
+  g_prof_clocks = nullptr;
   g_prof_start = g_prof_stop = nullptr;
   return hip_status(uq::launch_decode(a, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -313,6 +316,17 @@ int uq_profile_next_decode(void* start_event, void* stop_event) {
   if ((start_event == nullptr) != (stop_event == nullptr)) return UQ_ERR_INVALID_ARG;
   g_prof_start = static_cast<hipEvent_t>(start_event);
   g_prof_stop = static_cast<hipEvent_t>(stop_event);
+  return UQ_OK;
+}
+
+int uq_profile_next_decode_clock(uint64_t* clocks, int32_t* clock_khz) {
+  if (clock_khz != nullptr) {
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+      return UQ_ERR_HIP;
+    *clock_khz = khz;
+  }
+  g_prof_clocks = clocks;
   return UQ_OK;
 }
 

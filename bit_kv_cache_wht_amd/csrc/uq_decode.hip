@@ -1134,6 +1134,7 @@ struct KArgs {
   const void* v_new;         // in the query's dtype; null: attention only
   int32_t constopt;          // fused step: constOpt group scales for the written token
   Rot rot;                   // FP4: the cache's rotation variant
+  unsigned long long* clocks;  // instrumentation: [min start, max end] wall clock, or null
 };
 
 // Split partials cross workgroups that may sit on different compute dies,
@@ -1225,6 +1226,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, j4 = lane >> 4;
+  if (a.clocks != nullptr && tid == 0) atomicMin(&a.clocks[0], (unsigned long long)__builtin_amdgcn_s_memrealtime());
   if (tid == 0) *ctr = 0;                          // ordered before the first claim by the plan's barriers
   const int plan_bits = wg_plan<NW, NP>(seq_lens, a.B, Hi, a.max_pages, base, lens, red);
   const int T = base[a.B];                       // < 2^31: the host bounds the step count
@@ -1810,6 +1812,10 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     if (clamp_len(seq_lens[b], a.max_pages) > 0) continue;
     for (int i = tid; i < a.Hq * D; i += NT) a.out[(int64_t)b * a.Hq * D + i] = 0.f;
   }
+  if (a.clocks != nullptr) {                       // after every wave of the workgroup has finished
+    __syncthreads();
+    if (tid == 0) atomicMax(&a.clocks[1], (unsigned long long)__builtin_amdgcn_s_memrealtime());
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1887,6 +1893,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   k.v_new = a.v_new;
   k.constopt = a.constopt ? 1 : 0;
   k.rot = a.rot;
+  k.clocks = reinterpret_cast<unsigned long long*>(a.clocks);
   hipError_t e;
   if (a.ev_start != nullptr && (e = hipEventRecord(a.ev_start, s)) != hipSuccess) return e;
   const bool bf = a.q_dtype == UQ_IN_BF16;

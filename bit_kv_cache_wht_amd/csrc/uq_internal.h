@@ -73,6 +73,7 @@ struct DecodeArgs {
   const void* k_new;         // fused FP4 step: newest token's K/V [B][Hkv][D] (q_dtype), or null
   const void* v_new;
   hipEvent_t ev_start, ev_stop;   // optional, recorded around the main kernel
+  uint64_t* clocks;               // optional: wall-clock span of the main kernel (min start, max end)
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

@@ -370,6 +370,18 @@ int uq_decode_attention_bf16(const uq_kv_cache* cache, const void* q, int32_t q_
  * for both cancels a pending request.  Nothing is skipped or reordered. */
 int uq_profile_next_decode(void* start_event, void* stop_event);
 
+/* Instrumentation: the next decode call on this host thread (any decode entry
+ * point) has its attention kernel record the device's constant wall clock
+ * (s_memrealtime) as each workgroup starts and after it ends:
+ * clocks[0] = min(clocks[0], earliest start), clocks[1] = max(clocks[1], latest
+ * end), by device-scope atomics, in stream order with the kernel.  `clocks` is
+ * caller-owned device memory holding two uint64_t, set to {UINT64_MAX, 0}
+ * beforehand; clocks[1] - clocks[0] is the kernel's span in ticks.  If
+ * clock_khz is not NULL it receives the clock's rate (kHz) for the current
+ * device.  Passing clocks = NULL cancels a pending request.  Nothing is skipped
+ * or reordered; the kernel adds two atomics per workgroup and one barrier. */
+int uq_profile_next_decode_clock(uint64_t* clocks, int32_t* clock_khz);
+
 /* Instrumentation: a plain streaming read of `bytes` bytes of device memory at
  * `src`, the reference rate for a kernel bound by HBM reads (each byte loaded
  * once, coalesced, with nontemporal loads; nothing written but one 32-bit

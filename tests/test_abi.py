@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     h = uq.lib()
     for n in names:
         assert hasattr(h, n), n
@@ -279,6 +279,11 @@ def test_profile_events_validation():
     assert f(FAKE, None) == B.UQ_ERR_INVALID_ARG
     assert f(None, FAKE) == B.UQ_ERR_INVALID_ARG
     assert f(None, None) == B.UQ_OK
+
+
+def test_profile_clock_cancel():
+    # NULL clocks and no rate wanted: a pending request is cancelled, no device call
+    assert uq.lib().uq_profile_next_decode_clock(None, None) == B.UQ_OK
 
 
 def test_stream_read_validation():
