@@ -80,8 +80,10 @@ def make_workload(name):
     return W.tiny()
 
 
+# the kernel sources and the compiler flags (build.py) that fix the decode binary
 DECODE_SOURCES = ["bit_kv_cache_wht_amd/csrc/uq_decode.hip", "bit_kv_cache_wht_amd/csrc/uq_device.h",
-                  "bit_kv_cache_wht_amd/csrc/uq_fp4_row.h", "bit_kv_cache_wht_amd/csrc/uq_internal.h"]
+                  "bit_kv_cache_wht_amd/csrc/uq_fp4_row.h", "bit_kv_cache_wht_amd/csrc/uq_internal.h",
+                  "bit_kv_cache_wht_amd/build.py"]
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_SUMMARY = os.path.join(PROFILES, "decode_fp4_64x8192_hbm_traffic.md")
 COPY_BYTES = 1 << 30

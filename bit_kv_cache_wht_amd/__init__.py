@@ -42,5 +42,6 @@ from ._binding import (  # noqa: F401
     uq_prefill_attention,
     uq_quantize_append,
     uq_rotate_quantize_query,
+    uq_rotate_quantize_query_cache,
     uq_status_string,
 )

@@ -49,6 +49,7 @@ _SIGS = {
     "uq_append_fp8": (ctypes.c_int, [_CP, _P, _P, _I, _P, _I, _U, _P]),
     "uq_append_bf16": (ctypes.c_int, [_CP, _P, _P, _I, _P, _I, _U, _P]),
     "uq_rotate_quantize_query": (ctypes.c_int, [_P, _I, _P, _I, _I, _P]),
+    "uq_rotate_quantize_query_cache": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P]),
     "uq_decode_workspace_bytes": (_SZ, [_CP, _I, _I, _I]),
     "uq_decode_attention": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _SZ, _U, _P]),
     "uq_decode_attention_noalloc": (ctypes.c_int, [_CP, _P, _I, _P, _I, _P, _I, _I, ctypes.c_float, _P, _U, _P]),
@@ -261,6 +262,23 @@ def uq_append_fp8(cache: KvCache, k_new, v_new, slot_mapping, flags: int = 0, st
 
 def uq_append_bf16(cache: KvCache, k_new, v_new, slot_mapping, flags: int = 0, stream=None) -> None:
     _append("uq_append_bf16", cache, k_new, v_new, slot_mapping, flags, stream)
+
+
+def uq_rotate_quantize_query_cache(cache, q, q_fp8, stream=None) -> None:
+    """The query rotation of FP4 cache `cache`, with its rotation variant:
+    q [rows][head_dim] bf16/f32 -> q_fp8 uint8 [rows][head_dim]."""
+    import torch
+    _contig(q, q_fp8)
+    code = _dtype_code(q)
+    _need(q.dim() == 2 and int(q.shape[1]) == cache.head_dim,
+          f"q: shape {tuple(q.shape)}, expected [rows][{cache.head_dim}]")
+    rows = int(q.shape[0])
+    _need(q_fp8.dtype == torch.uint8, f"q_fp8: dtype {q_fp8.dtype}, expected torch.uint8", TypeError)
+    _shape(q_fp8, (rows, cache.head_dim), "q_fp8")
+    _on_device(q=q, q_fp8=q_fp8)
+    c = cache.c()
+    st = lib().uq_rotate_quantize_query_cache(ctypes.byref(c), _ptr(q), code, _ptr(q_fp8), rows, _stream(stream))
+    _check("uq_rotate_quantize_query_cache", st)
 
 
 def uq_rotate_quantize_query(q, q_fp8, stream=None) -> None:

@@ -260,7 +260,20 @@ int uq_rotate_quantize_query(const void* q, int32_t in_dtype, uint8_t* q_fp8, in
   if (rows < 0) return UQ_ERR_INVALID_ARG;
   if (rows == 0) return UQ_OK;
   if (q == nullptr || q_fp8 == nullptr) return UQ_ERR_INVALID_ARG;
-  return hip_status(uq::launch_query(q, in_dtype, q_fp8, rows, head_dim, true, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(uq::launch_query(q, in_dtype, q_fp8, rows, head_dim, true, uq::Rot{},
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+int uq_rotate_quantize_query_cache(const uq_kv_cache* cache, const void* q, int32_t in_dtype, uint8_t* q_fp8,
+                                   int32_t rows, uq_stream_t stream) {
+  const int st = check_cache(cache, UQ_KV_FP4);
+  if (st != UQ_OK) return st;
+  if (in_dtype != UQ_IN_BF16 && in_dtype != UQ_IN_F32) return UQ_ERR_INVALID_ARG;
+  if (rows < 0) return UQ_ERR_INVALID_ARG;
+  if (rows == 0) return UQ_OK;
+  if (q == nullptr || q_fp8 == nullptr) return UQ_ERR_INVALID_ARG;
+  return hip_status(uq::launch_query(q, in_dtype, q_fp8, rows, cache->head_dim, true, rot_of(cache),
+                                     reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t uq_decode_workspace_bytes(const uq_kv_cache* cache, int32_t num_seqs, int32_t num_q_heads,

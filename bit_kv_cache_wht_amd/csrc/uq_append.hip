@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void append_plain_kernel(AppendArgs a) {
 // Same row mapping as the FP4 write path; ROT = false gives the unrotated
 // E4M3 query of the FP8 baseline.
 template <int D, int IN, bool ROT>
-__global__ __launch_bounds__(256) void query_kernel(const void* q, uint8_t* out, int rows) {
+__global__ __launch_bounds__(256) void query_kernel(const void* q, uint8_t* out, int rows, Rot rot) {
   constexpr int LPR = D / 32;
   constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63;
@@ -199,7 +199,13 @@ __global__ __launch_bounds__(256) void query_kernel(const void* q, uint8_t* out,
   const int64_t r = in_range ? row : 0;
   double x[32];
   load_row32<IN>(q, r * D + 32 * p, x);
-  if constexpr (ROT) wht_row<D>(x, lane);
+  if constexpr (ROT) {
+    if (has_signs(rot)) {                          // R = c_d H diag(s): the signs first
+#pragma unroll
+      for (int e = 0; e < 32; ++e) x[e] = flip_sign(x[e], sign_mask(rot, 32 * p + e));
+    }
+    wht_row<D>(x, lane);
+  }
   uint32_t w[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) w[i] = e4m3x4_f64(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
@@ -279,9 +285,10 @@ static hipError_t launch_plain(const AppendArgs& a, int D, int in, hipStream_t s
 hipError_t launch_append_fp8(const AppendArgs& a, int D, int in, hipStream_t s) { return launch_plain<UQ_KV_FP8>(a, D, in, s); }
 hipError_t launch_append_bf16(const AppendArgs& a, int D, int in, hipStream_t s) { return launch_plain<UQ_KV_BF16>(a, D, in, s); }
 
-hipError_t launch_query(const void* q, int in, uint8_t* out, int rows, int D, bool rot, hipStream_t s) {
+hipError_t launch_query(const void* q, int in, uint8_t* out, int rows, int D, bool rot, const Rot& signs,
+                        hipStream_t s) {
   const dim3 grid(grid_rows(rows, 64 / (D / 32))), block(256);
-#define UQ_Q(DD, II, RR) hipLaunchKernelGGL((query_kernel<DD, II, RR>), grid, block, 0, s, q, out, rows)
+#define UQ_Q(DD, II, RR) hipLaunchKernelGGL((query_kernel<DD, II, RR>), grid, block, 0, s, q, out, rows, signs)
   if (D == 128) {
     if (in == UQ_IN_BF16) { if (rot) UQ_Q(128, UQ_IN_BF16, true); else UQ_Q(128, UQ_IN_BF16, false); }
     else { if (rot) UQ_Q(128, UQ_IN_F32, true); else UQ_Q(128, UQ_IN_F32, false); }

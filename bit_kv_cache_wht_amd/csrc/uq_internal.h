@@ -37,7 +37,7 @@ hipError_t launch_append_fp8(const AppendArgs& a, int head_dim, int in_dtype, hi
 hipError_t launch_append_bf16(const AppendArgs& a, int head_dim, int in_dtype, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_query(const void* q, int in_dtype, uint8_t* q_fp8, int rows, int head_dim,
-                        bool rotate, hipStream_t s);
+                        bool rotate, const Rot& signs, hipStream_t s);
 
 
 struct DecodeLayout {

@@ -163,7 +163,8 @@ enum uq_in_dtype { UQ_IN_BF16 = 0, UQ_IN_F32 = 1 };
  * and the query go through R and the output back through R^T = diag(s) c_d H_d.
  * The caller draws s, once per cache.  Bits at or above head_dim must be 0, and
  * all four words must be 0 without this bit.  uq_rotate_quantize_query always
- * applies the plain transform. */
+ * applies the plain transform; uq_rotate_quantize_query_cache applies the
+ * cache's. */
 #define UQ_ROT_K_ONLY 1u
 #define UQ_ROT_SIGNS 2u
 
@@ -230,6 +231,18 @@ int uq_append_bf16(const uq_kv_cache* cache, const void* k_new, const void* v_ne
  */
 int uq_rotate_quantize_query(const void* q, int32_t in_dtype, uint8_t* q_fp8, int32_t rows,
                              int32_t head_dim, uq_stream_t stream);
+
+/* The query rotation of an FP4 cache, with the cache's rotation variant
+ * ([review] §3.2; [tq-guide] "랜덤 회전과 Beta 분포" for UQ_ROT_SIGNS): q_fp8[r][c] =
+ * E4M3((R q[r])[c]) with R = c_d H_d diag(s) for a UQ_ROT_SIGNS cache, c_d H_d
+ * otherwise (a UQ_ROT_K_ONLY cache rotates its queries like its keys), so
+ * that the bytes are the query operand the decode forms for this cache.
+ *   cache  FP4 descriptor (head_dim, rotation, rotation_signs are read; the
+ *          pools are not touched)
+ *   q, in_dtype, q_fp8, rows  as uq_rotate_quantize_query
+ */
+int uq_rotate_quantize_query_cache(const uq_kv_cache* cache, const void* q, int32_t in_dtype, uint8_t* q_fp8,
+                                   int32_t rows, uq_stream_t stream);
 
 /* Workspace bytes needed by the decode entry points for this shape (an upper
  * bound valid for every seq_lens content).  0 if the arguments are invalid. */

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     h = uq.lib()
     for n in names:
         assert hasattr(h, n), n
@@ -279,6 +279,17 @@ def test_profile_events_validation():
     assert f(FAKE, None) == B.UQ_ERR_INVALID_ARG
     assert f(None, FAKE) == B.UQ_ERR_INVALID_ARG
     assert f(None, None) == B.UQ_OK
+
+
+def test_query_rotation_of_a_cache_validation():
+    f = uq.lib().uq_rotate_quantize_query_cache
+    ok = cache(B.UQ_KV_FP4, heads=2)
+    assert f(None, FAKE, 0, FAKE, 4, None) == B.UQ_ERR_INVALID_ARG
+    assert f(ctypes.byref(cache(B.UQ_KV_FP8, heads=2)), FAKE, 0, FAKE, 4, None) == B.UQ_ERR_INVALID_ARG
+    assert f(ctypes.byref(ok), FAKE, 7, FAKE, 4, None) == B.UQ_ERR_INVALID_ARG
+    assert f(ctypes.byref(ok), FAKE, 0, FAKE, -1, None) == B.UQ_ERR_INVALID_ARG
+    assert f(ctypes.byref(ok), None, 0, FAKE, 4, None) == B.UQ_ERR_INVALID_ARG
+    assert f(ctypes.byref(ok), None, 0, None, 0, None) == B.UQ_OK       # no rows: no launch
 
 
 def test_profile_clock_cancel():

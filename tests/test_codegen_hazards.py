@@ -20,7 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "bit_kv_cache_wht_amd", "csrc", "uq_decode.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang",
-         "-packed-fp32-ops", "--cuda-device-only", "-S"]
+         "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1", "--cuda-device-only", "-S"]
 
 
 def _regs(tok):

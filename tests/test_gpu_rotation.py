@@ -138,3 +138,26 @@ def test_mixed_layer_formats():
         wants.append(oracle_decode(fmt, wl, pools, k_only=k_only, signs=signs))
     for i, (g, w) in enumerate(zip(outs, wants)):
         assert_close(g, w, f"layer {i} ({layers[i][0]})")
+
+
+@pytest.mark.parametrize("variant", ["plain", "k_only", "signs", "k_only_signs"])
+@pytest.mark.parametrize("in_dtype,d", [("bf16", 128), ("f32", 64)])
+def test_query_rotation_of_a_cache(variant, in_dtype, d):
+    # uq_rotate_quantize_query_cache: the E4M3 bytes of R q with the cache's R
+    # (c_d H diag(s) for a signed cache; K-only caches rotate queries as usual)
+    torch = torch_mod()
+    k_only, signs = (False, None) if variant == "plain" else _variant(variant, d, seed=d + 5)
+    rng = np.random.default_rng(d + 11)
+    rows = 257
+    x = (rng.standard_normal((rows, d)) * 10.0 ** rng.integers(-4, 2, (rows, 1))).astype(np.float32)
+    arr = W._to_bf16_bits(x) if in_dtype == "bf16" else x
+    wl = W.make_workload("qrot", 1, 1, 1, d, [16], [16], in_dtype=in_dtype, seed=1)
+    cache = gpu_cache("fp4", wl, k_only=k_only, signs=signs)
+    out = torch.empty((rows, d), dtype=torch.uint8, device="cuda")
+    announce(f"query rotation of a {variant} cache, {in_dtype} d={d}")
+    uq().uq_rotate_quantize_query_cache(cache, dev(arr, in_dtype), out)
+    torch.cuda.synchronize()
+    want = O.rotate_quantize_query(arr, in_dtype=in_dtype, signs=signs)
+    assert np.array_equal(out.cpu().numpy(), want)
+    if signs is not None:                              # the plain rotation differs
+        assert not np.array_equal(want, O.rotate_quantize_query(arr, in_dtype=in_dtype))
