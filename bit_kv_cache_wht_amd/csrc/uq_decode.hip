@@ -157,7 +157,11 @@ template <int D> struct Fp4Pol {
   }
   __device__ static void load_k(KStep& st, const uint8_t* pool, const int (&ids)[4], int64_t page_bytes,
                                 const PageGeo& g, int r16, int j4) {
-    const int pid = pick_id(ids, r16 >> 2);
+    load_k_page(st, pool, pick_id(ids, r16 >> 2), page_bytes, g, r16, j4);
+  }
+  // the same with the lane's page id (that of page (lane % 16) / 4 of the step)
+  __device__ static void load_k_page(KStep& st, const uint8_t* pool, int pid, int64_t page_bytes, const PageGeo& g,
+                                     int r16, int j4) {
     const uint8_t* kb = pool + (int64_t)pid * page_bytes + (int64_t)fp4_block_pos(g.head0, pid, g.H, g.mask) * kBlk;
     if (j4 < kGroups) {
 #pragma unroll
@@ -1946,20 +1950,30 @@ DecodeLayout decode_layout(int format, int B, int Hq, int Hkv, int D) {
 // ------------------------------------------------------------------ chunked prefill
 // Causal attention of chunks of query tokens over the FP4 cache ([review] §1 and
 // §5.4: a new turn's tokens read the resident prefix instead of re-prefilling it).
-// A workgroup takes kPfRows query rows, rows r = t G + h for QT = kPfRows / G
-// consecutive chunk tokens t of one sequence and the G query heads of one KV
-// head, and walks the cache from position 0 to its last token's position in
-// steps of 4 pages (64 keys), exactly as the FP4 decode steps: K/V double-
-// buffered in registers, scaled-MFMA QK, online softmax with lazy rescaling,
-// hi + lo float16 P in the PV.  Each of the 4 waves owns kPfNB 16-row column
-// blocks and reuses every loaded K/V step for all of them.  Logits past a row's
-// own position get -inf (causal), value slots past the sequence end are
-// cleared.  Rows are rotated back and stored like the decode's.
+// A workgroup of 8 waves (two per SIMD) takes kPfRows query rows, rows
+// r = t G + h for QT = kPfRows / G consecutive chunk tokens t of one sequence and
+// the G query heads of one KV head, and walks the cache from position 0 to its
+// last token's position in steps of 4 pages (64 keys).  Per step:
+//   - the values are converted once for the whole workgroup: each lane takes
+//     part of one code row of one page (a channel pair, 8 slots at d = 128),
+//     turns it into float16 with the hardware FP4 converter and the slots' group
+//     scales, and writes both channels transposed ([channel][token]) into one of
+//     two LDS buffers (the next step's, while this step's is read);
+//   - every wave loads the keys itself in the FP4 decode's operand layout
+//     (double-buffered in registers) and runs, for its two 16-row column
+//     blocks, the scaled-MFMA QK, the online softmax with lazy rescaling, and
+//     the PV on f16 MFMAs with P as hi + lo and V^T operands read from LDS;
+//   - one barrier, after which the buffer just read may be written again.
+// Logits past a row's own position get -inf (causal); steps that lie wholly
+// before a wave's rows take no mask, and steps wholly past them no work.  Value
+// slots past the sequence end convert to zero.  Rows are rotated back and stored
+// like the decode's.
 namespace {
-constexpr int kPfWaves = 4;
-constexpr int kPfNB = 4;                                  // column blocks per wave
+constexpr int kPfWaves = 8;                               // two per SIMD
+constexpr int kPfNB = 2;                                  // column blocks per wave
 constexpr int kPfRows = 16 * kPfNB * kPfWaves;            // query rows of a workgroup
 constexpr int kPfMaxSeqs = 4096;                          // plan in LDS
+constexpr int kPfKeys = 4 * kPage;                        // keys per step
 
 struct PfArgs {
   const uint8_t* k_pool;
@@ -1980,66 +1994,116 @@ struct PfArgs {
 
 template <int D>
 struct PfLds {
+  // The query rows and the value buffers are dead once the last step has ended;
+  // the output stage then reuses their bytes.
   static constexpr int kQs = 0;                                   // [kPfRows][D] E4M3 query rows
-  static constexpr int kStage = kQs + kPfRows * D;                // [kPfWaves][16][D] float rows
-  static constexpr int kL = kStage + kPfWaves * 16 * D * 4;       // [kPfWaves][16] float l
+  static constexpr int kVBuf = D * kPfKeys * 2;                   // [D][64] float16 (pf_v_off)
+  static constexpr int kV = kQs + kPfRows * D;                    // two value buffers
+  static constexpr int kLoopEnd = kV + 2 * kVBuf;
+  static constexpr int kStage = 0;                                // [kPfWaves][16][D] float rows
+  static constexpr int kStageEnd = kPfWaves * 16 * D * 4;
+  static constexpr int kL = kLoopEnd > kStageEnd ? kLoopEnd : kStageEnd;   // [kPfWaves][16] float l
   static constexpr int kPlan = kL + kPfWaves * 16 * 4;            // [kPfMaxSeqs + 1] block prefix
-  static constexpr int kMisc = kPlan + (kPfMaxSeqs + 1) * 4;      // [2 * kPfWaves] scratch
-  static constexpr int kTotal = kMisc + 2 * kPfWaves * 4;
+  static constexpr int kMisc = kPlan + (kPfMaxSeqs + 1) * 4;      // [kPfWaves] scan partials
+  static constexpr int kTotal = kMisc + kPfWaves * 4;
 };
 
-// The value step of Fp4Pol as f16 MFMA A operands, converted once and shared by
-// the wave's column blocks: VA[q][half][0 / 1] holds the even / odd channels of
-// channel pairs kCPL*(lane%16) + q for slots 8 half .. 8 half + 7 (the same
-// operands Fp4Pol::pv forms for its MMAs).
+// Byte offset, in a value buffer, of channel c's tokens 8 tb .. 8 tb + 7 (16 B).
+// Rows of 128 B; the 16-B chunks of row c are permuted by c so that the
+// conversion's stores (8 lanes: channels 8 apart) and the PV operand reads (8
+// lanes: 8 consecutive channels) each cover all eight chunks.
+__device__ __forceinline__ int pf_v_off(int c, int tb) { return c * (2 * kPfKeys) + 16 * (tb ^ ((c ^ (c >> 3)) & 7)); }
+
+// A step's values are converted by all the workgroup's lanes: lane u takes page
+// x = u / 128 of the step, code row rho = (u % 128) / kParts of it (row
+// rho = 16 q + r holds channel pair p = (D/32) r + q, byte t = slot t) and the
+// kSlots slots kSlots part .. of that row, with their scale bytes (those of p's
+// group, byte t = slot t).
+template <int D> struct PfV {
+  static constexpr int kRows = D / 2;                          // code rows of a page
+  static constexpr int kParts = 16 * kPfWaves / kRows;         // lanes per row: 2 (d 128), 4 (d 64)
+  static constexpr int kSlots = kPage / kParts;                // slots per lane: 8, 4
+  static constexpr int kW = kSlots / 4;
+  uint32_t c[kW], s[kW];
+};
+template <int D> __device__ __forceinline__ int pf_pair(int rho) { return (D / 32) * (rho % 16) + rho / 16; }
+
 template <int D>
-__device__ __forceinline__ void pf_convert_v(const typename Fp4Pol<D>::VStep& st, v8h (&VA)[D / 32][2][2]) {
-  constexpr int kCPL = D / 32;
-  const uint32_t s[4] = {st.vs.x, st.vs.y, st.vs.z, st.vs.w};
-  float sc[16];
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int k = t & 3;
-    sc[t] = __uint_as_float(k == 3 ? s[t >> 2] >> 1 : s[t >> 2] << (23 - 8 * k));
+__device__ __forceinline__ void pf_load_v(PfV<D>& r, const uint8_t* vb, int rho, int part) {
+  using V = PfV<D>;
+  const uint8_t* cb = vb + rho * kPage + V::kSlots * part;
+  const uint8_t* sb = vb + Fp4Block<D>::kCodeBytes + kPage * (pf_pair<D>(rho) / 16) + V::kSlots * part;
+  if constexpr (V::kW == 2) {
+    const uint2 c = load8_stream(cb), sc = load8_stream(sb);
+    r.c[0] = c.x; r.c[1] = c.y;
+    r.s[0] = sc.x; r.s[1] = sc.y;
+  } else {
+    r.c[0] = load4_stream(cb);
+    r.s[0] = load4_stream(sb);
   }
+}
+
+// Channels 2p and 2p + 1 of the lane's slots as float16 (slots at or past nvalid
+// give zero: their codes are cleared and their scale set to 2^0), stored as
+// tokens 16 x + kSlots part .. of the value buffer.
+template <int D>
+__device__ __forceinline__ void pf_store_v(PfV<D> r, uint8_t* vbuf, int x, int rho, int part, int nvalid) {
+  using V = PfV<D>;
+  constexpr int NS = V::kSlots;
+  const int p = pf_pair<D>(rho);
+  const int first = NS * part;
+  if (nvalid < first + NS) {
 #pragma unroll
-  for (int q = 0; q < kCPL; ++q) {
-    const uint32_t c[4] = {st.vc[q].x, st.vc[q].y, st.vc[q].z, st.vc[q].w};
-    uint32_t X[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      v2h h;
-      switch (t & 3) {
-        case 0: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 0); break;
-        case 1: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 1); break;
-        case 2: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 2); break;
-        default: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[t >> 2], sc[t], 3); break;
-      }
-      X[t] = __builtin_bit_cast(uint32_t, h);
+    for (int w = 0; w < V::kW; ++w) {
+      const uint32_t k = slot_bytes_kept(nvalid, first + 4 * w);
+      r.c[w] &= k;
+      r.s[w] = (r.s[w] & k) | (~k & 0x7F7F7F7Fu);
     }
+  }
+  uint32_t X[NS];   // slot first + t: (channel 2p, channel 2p + 1)
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint32_t ev[4], od[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t x0 = X[8 * half + 2 * i], x1 = X[8 * half + 2 * i + 1];
-        ev[i] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-        od[i] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-      }
-      VA[q][half][0] = __builtin_bit_cast(v8h, make_uint4(ev[0], ev[1], ev[2], ev[3]));
-      VA[q][half][1] = __builtin_bit_cast(v8h, make_uint4(od[0], od[1], od[2], od[3]));
+  for (int t = 0; t < NS; ++t) {
+    // the converter reads only the exponent field of its scale: byte k of a
+    // scale word shifted into bits 23..30
+    const int k = t & 3;
+    const float sc = __uint_as_float(k == 3 ? r.s[t >> 2] >> 1 : r.s[t >> 2] << (23 - 8 * k));
+    v2h h;
+    switch (k) {
+      case 0: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r.c[t >> 2], sc, 0); break;
+      case 1: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r.c[t >> 2], sc, 1); break;
+      case 2: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r.c[t >> 2], sc, 2); break;
+      default: h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r.c[t >> 2], sc, 3); break;
     }
+    X[t] = __builtin_bit_cast(uint32_t, h);
+  }
+  uint32_t ev[NS / 2], od[NS / 2];
+#pragma unroll
+  for (int i = 0; i < NS / 2; ++i) {
+    ev[i] = __builtin_amdgcn_perm(X[2 * i + 1], X[2 * i], 0x05040100u);   // low halves: channel 2p
+    od[i] = __builtin_amdgcn_perm(X[2 * i + 1], X[2 * i], 0x07060302u);   // high halves: channel 2p + 1
+  }
+  if constexpr (NS == 8) {
+    *reinterpret_cast<uint4*>(vbuf + pf_v_off(2 * p, 2 * x + part)) = make_uint4(ev[0], ev[1], ev[2], ev[3]);
+    *reinterpret_cast<uint4*>(vbuf + pf_v_off(2 * p + 1, 2 * x + part)) = make_uint4(od[0], od[1], od[2], od[3]);
+  } else {
+    const int half = 8 * (part & 1);
+    *reinterpret_cast<uint2*>(vbuf + pf_v_off(2 * p, 2 * x + (part >> 1)) + half) = make_uint2(ev[0], ev[1]);
+    *reinterpret_cast<uint2*>(vbuf + pf_v_off(2 * p + 1, 2 * x + (part >> 1)) + half) = make_uint2(od[0], od[1]);
   }
 }
 
 template <int D, int IN>
 __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) {
   using Pol = Fp4Pol<D>;
+  using KStep = typename Pol::KStep;
   constexpr int NT = 64 * kPfWaves;
   constexpr int TOK = Pol::kTok;                               // 16 slots of one page per lane
+  constexpr int kTiles = D / 16;
   using L = PfLds<D>;
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* qs = smem + L::kQs;
+  uint8_t* vbuf0 = smem + L::kV;
+  uint8_t* vbuf1 = smem + L::kV + L::kVBuf;
   float* stage = reinterpret_cast<float*>(smem + L::kStage);
   float* stage_l = reinterpret_cast<float*>(smem + L::kL);
   int32_t* bb = reinterpret_cast<int32_t*>(smem + L::kPlan);
@@ -2077,18 +2141,18 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   const int b = lo;
   const int q0 = a.cu_q[b], qlen = a.cu_q[b + 1] - q0;
   const int t0 = (blk - bb[b]) * a.QT;                          // first chunk token of the block
-  const int nt = min(a.QT, qlen - t0);                          // its tokens
+  const int nt = min(a.QT, qlen - t0);                          // its tokens (at least one)
   const int Ls = clamp_len(a.seq_lens[b], a.max_pages);
   const int pos0 = Ls - qlen + t0;                              // position of token t0
   const int nrows = nt * a.G;
   const int npages = (Ls + kPage - 1) / kPage;
-  // position of row r (padding rows attend to position 0 and are not stored)
+  // position of row r; padding rows (r >= nrows: zero queries, not stored) take
+  // the last row's, so that positions never decrease with r
   auto row_pos = [&](int r) -> int {
-    const int p = r < nrows ? pos0 + r / a.G : 0;
+    const int p = pos0 + min(r, nrows - 1) / a.G;
     return p < 0 ? 0 : p;
   };
-  const int last_pos = row_pos(nrows - 1);
-  const int steps = last_pos / (4 * kPage) + 1;                 // 64 keys per step
+  const int steps = row_pos(nrows - 1) / kPfKeys + 1;
 
   // ---- query rows: rotate, round to E4M3, into LDS
   for (int r = tid >> 4; r < kPfRows; r += NT / 16) {
@@ -2104,7 +2168,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   typename Pol::QOp qo[kPfNB];
   int rpos[kPfNB];                                             // position of this lane's row in block c
   float m_run[kPfNB], l_run[kPfNB];
-  v4f O[kPfNB][Pol::kTiles];
+  v4f O[kPfNB][kTiles];
 #pragma unroll
   for (int c = 0; c < kPfNB; ++c) {
     const int row = (wave * kPfNB + c) * 16 + r16;
@@ -2113,122 +2177,157 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
     m_run[c] = -INFINITY;
     l_run[c] = 0.f;
 #pragma unroll
-    for (int t = 0; t < Pol::kTiles; ++t) O[c][t] = v4f{0, 0, 0, 0};
+    for (int t = 0; t < kTiles; ++t) O[c][t] = v4f{0, 0, 0, 0};
   }
+  // steps before s_free hold no key past any row of the wave; steps past s_last
+  // hold none at or before them
+  const int s_free = (row_pos(wave * kPfNB * 16) + 1) / kPfKeys;
+  const int s_last = row_pos(wave * kPfNB * 16 + kPfNB * 16 - 1) / kPfKeys;
 
   const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
   const PageGeo geo{hk, a.Hkv, a.hmask, 0, -1};   // FP4 pages only
-  auto ids_of = [&](int s, int (&ids)[4]) {
-#pragma unroll
-    for (int x = 0; x < 4; ++x) ids[x] = pt[max(min(4 * s + x, npages - 1), 0)];   // within the row
+  // Page ids are read two steps ahead, and every load of the loop is issued
+  // whether or not its step exists (indices clamped into the sequence's row of
+  // the table, so the bytes read are the cache's own), in a fixed order: a wait
+  // for one load then never waits for loads issued after it.  Lane l reads the
+  // id of page (l % 16) / 4 of a step: its own page for the keys; the
+  // conversion takes page vx's id from lane 4 vx.
+  auto page_of = [&](int s) { return pt[max(min(4 * s + (r16 >> 2), npages - 1), 0)]; };
+  using VC = PfV<D>;
+  const int vx = __builtin_amdgcn_readfirstlane(tid >> 7);     // the page whose values this lane converts
+  const int vrho = (tid & 127) / VC::kParts, vpart = (tid & 127) % VC::kParts;
+  auto v_block = [&](int ids) -> const uint8_t* {
+    const int pid = __builtin_amdgcn_readlane(ids, 4 * vx);
+    return a.v_pool + (int64_t)pid * a.page_bytes + (int64_t)fp4_block_pos(hk, pid, a.Hkv, a.hmask) * Pol::kBlk;
   };
-  // K/V buffers alternate between two named pairs (the step loop is unrolled by
-  // two, so that no buffer is indexed at run time and all stay in registers)
-  typename Pol::KStep k0, k1;
-  typename Pol::VStep v0, v1;
+  auto v_valid = [&](int s) { return min(max(Ls - (kPfKeys * s + kPage * vx), 0), kPage); };
+  auto load_k = [&](KStep& st, int pid) { Pol::load_k_page(st, a.k_pool, pid, a.page_bytes, geo, r16, j4); };
+
+  VC vr;
+  KStep k0, k1;
+  int kid, vid;                                                // ids: keys of step s + 1, values of step s + 2
   {
-    int ids[4];
-    ids_of(0, ids);
-    Pol::load_k(k0, a.k_pool, ids, a.page_bytes, geo, r16, j4);
-    Pol::load_v(v0, a.v_pool, ids, a.page_bytes, geo, r16, j4);
+    const int id0 = page_of(0);
+    load_k(k0, id0);
+    pf_load_v<D>(vr, v_block(id0), vrho, vpart);
+    const int id1 = page_of(1);
+    pf_store_v<D>(vr, vbuf0, vx, vrho, vpart, v_valid(0));
+    pf_load_v<D>(vr, v_block(id1), vrho, vpart);
+    kid = id1;
+    vid = page_of(2);
   }
-  auto step = [&](int s, typename Pol::KStep& kc, typename Pol::VStep& vc, typename Pol::KStep& kn,
-                  typename Pol::VStep& vn) {
-    if (s + 1 < steps) {                                       // prefetch the next step
-      int ids[4];
-      ids_of(s + 1, ids);
-      Pol::load_k(kn, a.k_pool, ids, a.page_bytes, geo, r16, j4);
-      Pol::load_v(vn, a.v_pool, ids, a.page_bytes, geo, r16, j4);
-    }
-    const int key0 = 4 * kPage * s + kPage * j4;                // first key of this lane's page
-    if (__any(Ls - key0 < TOK)) Pol::mask_v(vc, min(max(Ls - key0, 0), TOK));   // slots past the sequence end
-    v8h VA[D / 32][2][2];
-    pf_convert_v<D>(vc, VA);
-    // PV of block c (its probabilities as f16 hi + lo in Pprev) runs while block
-    // c + 1 takes its exponentials: the two are independent, and the scheduling
-    // barriers below alternate their MFMAs and VALU instructions
-    v8h Pprev[TOK / 8][2];
-    auto pv_block = [&](v4f (&Oc)[Pol::kTiles]) {
+  __syncthreads();
+
+  // One step s: K(s) in kc, the values of step s in LDS buffer s & 1, the raw
+  // values of step s + 1 in vr.  MASK: the step reaches past some row of the wave.
+  auto step = [&](auto mask_t, int s, KStep& kc, KStep& kn) {
+    constexpr bool MASK = decltype(mask_t)::value;
+    load_k(kn, kid);                                           // K(s + 1)
+    kid = page_of(s + 2);
+    const bool active = !MASK || s <= s_last;                  // wave-uniform
+    const int key0 = kPfKeys * s + kPage * j4;                 // first key of this lane's page
+    v8h P[kPfNB][TOK / 8][2];
+    if (active) {
 #pragma unroll
-      for (int q = 0; q < D / 32; ++q)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          Oc[2 * q] = mma2(VA[q][half][0], Pprev[half], Oc[2 * q]);
-          Oc[2 * q + 1] = mma2(VA[q][half][1], Pprev[half], Oc[2 * q + 1]);
-        }
-    };
-#pragma unroll
-    for (int c = 0; c < kPfNB; ++c) {
-      v4f S[TOK / 4];
-      Pol::qk(kc, qo[c], S);
-      const int nvalid = min(max(rpos[c] - key0 + 1, 0), TOK);  // causal: keys <= the row's position
-      float t[TOK];
-      if (__all(nvalid == TOK)) {                                // steps wholly before the rows: no mask
+      for (int c = 0; c < kPfNB; ++c) {
+        v4f S[TOK / 4];
+        Pol::qk(kc, qo[c], S);
+        float t[TOK];
 #pragma unroll
         for (int m = 0; m < TOK / 4; ++m)
 #pragma unroll
           for (int v = 0; v < 4; ++v) t[4 * m + v] = S[m][v];
-      } else {
+        if constexpr (MASK) {
+          const int nvalid = min(max(rpos[c] - key0 + 1, 0), TOK);   // causal: keys <= the row's position
 #pragma unroll
-        for (int m = 0; m < TOK / 4; ++m)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) t[4 * m + v] = 4 * m + v < nvalid ? S[m][v] : -INFINITY;
-      }
-      float neg_mc = -m_run[c] * a.scale_log2;
-      float pf[TOK];
-#pragma unroll
-      for (int i = 0; i < TOK; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
-      float psum = pf[0];
-#pragma unroll
-      for (int i = 1; i < TOK; ++i) psum += pf[i];
-      if (c > 0) {
-        pv_block(O[c - 1]);
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // two VALU instructions
+          for (int i = 0; i < TOK; ++i) t[i] = i < nvalid ? t[i] : -INFINITY;
         }
-      }
-      if (__any(!(psum <= 256.f))) {
-        float mx = t[0];
-#pragma unroll
-        for (int i = 1; i < TOK; ++i) mx = fmaxf(mx, t[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[c], mx);
-        // a row whose every key so far is masked keeps m = -inf and takes no rescale
-        const float alpha = m_new > -INFINITY ? __builtin_amdgcn_exp2f((m_run[c] - m_new) * a.scale_log2) : 1.f;
-        const float keep = m_run[c] > -INFINITY ? alpha : 0.f;
-        l_run[c] *= keep;
-#pragma unroll
-        for (int tt = 0; tt < Pol::kTiles; ++tt) O[c][tt] *= keep;
-        m_run[c] = m_new;
-        neg_mc = m_new > -INFINITY ? -m_new * a.scale_log2 : 0.f;
+        float neg_mc = -m_run[c] * a.scale_log2;
+        float pf[TOK];
 #pragma unroll
         for (int i = 0; i < TOK; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
-        psum = pf[0];
+        float psum = pf[0];
 #pragma unroll
         for (int i = 1; i < TOK; ++i) psum += pf[i];
-      }
-      l_run[c] += psum;
+        if (__any(!(psum <= 256.f))) {
+          float mx = t[0];
 #pragma unroll
-      for (int half = 0; half < TOK / 8; ++half) {
-        uint32_t hw[4], lw[4];
+          for (int i = 1; i < TOK; ++i) mx = fmaxf(mx, t[i]);
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float m_new = fmaxf(m_run[c], mx);
+          // a row whose every key so far is masked keeps m = -inf and takes no rescale
+          const float alpha = m_new > -INFINITY ? __builtin_amdgcn_exp2f((m_run[c] - m_new) * a.scale_log2) : 1.f;
+          const float keep = m_run[c] > -INFINITY ? alpha : 0.f;
+          l_run[c] *= keep;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) split_f16x2(pf[8 * half + 2 * i], pf[8 * half + 2 * i + 1], hw[i], lw[i]);
-        Pprev[half][0] = __builtin_bit_cast(v8h, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-        Pprev[half][1] = __builtin_bit_cast(v8h, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+          for (int tt = 0; tt < kTiles; ++tt) O[c][tt] *= keep;
+          m_run[c] = m_new;
+          neg_mc = m_new > -INFINITY ? -m_new * a.scale_log2 : 0.f;
+#pragma unroll
+          for (int i = 0; i < TOK; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
+          psum = pf[0];
+#pragma unroll
+          for (int i = 1; i < TOK; ++i) psum += pf[i];
+        }
+        l_run[c] += psum;
+#pragma unroll
+        for (int half = 0; half < TOK / 8; ++half) {
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) split_f16x2(pf[8 * half + 2 * i], pf[8 * half + 2 * i + 1], hw[i], lw[i]);
+          P[c][half][0] = __builtin_bit_cast(v8h, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+          P[c][half][1] = __builtin_bit_cast(v8h, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        }
       }
     }
-    pv_block(O[kPfNB - 1]);
+    // the next step's values (past the last step: a clamped page, cleared)
+    pf_store_v<D>(vr, (s & 1) ? vbuf0 : vbuf1, vx, vrho, vpart, v_valid(s + 1));
+    pf_load_v<D>(vr, v_block(vid), vrho, vpart);               // V(s + 2)
+    vid = page_of(s + 3);
+    if (active) {
+      // V^T operands read one tile ahead of their MFMAs
+      const uint8_t* vb = (s & 1) ? vbuf1 : vbuf0;
+      auto rd = [&](int q, int h) { return *reinterpret_cast<const v8h*>(vb + pf_v_off(16 * q + r16, 2 * j4 + h)); };
+      v8h va[2][2];
+      va[0][0] = rd(0, 0);
+      va[0][1] = rd(0, 1);
+#pragma unroll
+      for (int q = 0; q < kTiles; ++q) {
+        if (q + 1 < kTiles) {
+          va[(q + 1) & 1][0] = rd(q + 1, 0);
+          va[(q + 1) & 1][1] = rd(q + 1, 1);
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int c = 0; c < kPfNB; ++c) O[c][q] = mma2(va[q & 1][half], P[c][half], O[c][q]);
+      }
+    }
+    __syncthreads();                                           // buffer s & 1 is free again
   };
-  for (int s = 0; s < steps; s += 2) {
-    step(s, k0, v0, k1, v1);
-    if (s + 1 < steps) step(s + 1, k1, v1, k0, v0);
+  using Free = std::false_type;
+  using Masked = std::true_type;
+  // the step loop is unrolled by two so that the key buffers are named, not
+  // indexed, and stay in registers
+  int s = 0;
+  for (; s + 2 <= s_free && s + 2 <= steps; s += 2) {
+    step(Free{}, s, k0, k1);
+    step(Free{}, s + 1, k1, k0);
+  }
+  if (s < s_free && s < steps) {
+    step(Free{}, s, k0, k1);
+    ++s;
+    if (s < steps) k0 = k1;                                    // K(s), prefetched into k1
+  }
+  for (; s < steps; s += 2) {
+    step(Masked{}, s, k0, k1);
+    if (s + 1 < steps) step(Masked{}, s + 1, k1, k0);
   }
 
   // ---- rows out: block by block through the wave's LDS stage (16 rows), two
-  // rows at a time per wave (one per 32-lane half), normalized, rotated back
+  // rows at a time per wave (one per 32-lane half), normalized, rotated back.
+  // Every wave has passed the last step's barrier: the stage's bytes are free.
   constexpr int PC = D / 32;
   float* st = stage + wave * 16 * D;
   float* stl = stage_l + wave * 16;
@@ -2238,9 +2337,9 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
     float l_tot = l_run[c] + __shfl_xor(l_run[c], 16);
     l_tot += __shfl_xor(l_tot, 32);
 #pragma unroll
-    for (int tt = 0; tt < Pol::kTiles; ++tt)
+    for (int tt = 0; tt < kTiles; ++tt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) st[r16 * D + Pol::channel(tt, j4, v)] = O[c][tt][v];
+      for (int v = 0; v < 4; ++v) st[r16 * D + 16 * tt + 4 * j4 + v] = O[c][tt][v];
     if (j4 == 0) stl[r16] = l_tot;
     __builtin_amdgcn_s_waitcnt(0xC07F);                         // lgkmcnt(0): the stage is written
     __builtin_amdgcn_wave_barrier();

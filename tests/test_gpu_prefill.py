@@ -6,6 +6,7 @@ prefix) within relative L2 1e-3 and max-abs 5e-3.
 
 Cases: chunks after a prefix and whole prompts, chunk lengths that are not
 multiples of a workgroup's tokens, empty chunks, GQA groups of 1, 4, 8 and 16,
+whole prompts of several hundred tokens with one query head per KV head,
 d = 64 and 128, bf16 and f32 inputs, and single-token chunks (which must also
 agree with the decode entry point itself)."""
 import numpy as np
@@ -26,6 +27,9 @@ CASES = {
     "mha_d64_f32": (2, 4, 4, 64, [150, 90], [64, 90], "f32"),
     "group16": (2, 16, 1, 128, [520, 64], [129, 1], "bf16"),
     "empty_chunks": (4, 8, 2, 128, [100, 50, 300, 16], [0, 50, 0, 16], "bf16"),
+    # one query head per KV head: a workgroup's 256 rows are 256 consecutive
+    # positions, so its waves reach the diagonal at different steps
+    "mha_long_prompts": (3, 2, 2, 128, [1000, 531, 777], [300, 531, 777], "bf16"),
 }
 
 
