@@ -2003,9 +2003,10 @@ struct PfLds {
   static constexpr int kStage = 0;                                // [kPfWaves][16][D] float rows
   static constexpr int kStageEnd = kPfWaves * 16 * D * 4;
   static constexpr int kL = kLoopEnd > kStageEnd ? kLoopEnd : kStageEnd;   // [kPfWaves][16] float l
-  static constexpr int kPlan = kL + kPfWaves * 16 * 4;            // [kPfMaxSeqs + 1] block prefix
-  static constexpr int kMisc = kPlan + (kPfMaxSeqs + 1) * 4;      // [kPfWaves] scan partials
-  static constexpr int kTotal = kMisc + kPfWaves * 4;
+  static constexpr int kStart = kL + kPfWaves * 16 * 4;           // [kPfMaxSeqs] first block of the i-th sequence
+  static constexpr int kSeq = kStart + kPfMaxSeqs * 4;            // [kPfMaxSeqs] the i-th sequence of the order
+  static constexpr int kMisc = kSeq + kPfMaxSeqs * 4;             // [2][kPfWaves] scan partials, octave mask
+  static constexpr int kTotal = kMisc + 2 * kPfWaves * 4 + 4;
 };
 
 // Byte offset, in a value buffer, of channel c's tokens 8 tb .. 8 tb + 7 (16 B).
@@ -2106,41 +2107,71 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   uint8_t* vbuf1 = smem + L::kV + L::kVBuf;
   float* stage = reinterpret_cast<float*>(smem + L::kStage);
   float* stage_l = reinterpret_cast<float*>(smem + L::kL);
-  int32_t* bb = reinterpret_cast<int32_t*>(smem + L::kPlan);
+  int32_t* start = reinterpret_cast<int32_t*>(smem + L::kStart);
+  int32_t* seq = reinterpret_cast<int32_t*>(smem + L::kSeq);
   int32_t* red = reinterpret_cast<int32_t*>(smem + L::kMisc);
+  uint32_t* octaves = reinterpret_cast<uint32_t*>(smem + L::kMisc + 2 * kPfWaves * 4);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, j4 = lane >> 4;
-  const int hk = blockIdx.y;
+  const int hk = (int)(blockIdx.x % (unsigned)a.Hkv);
 
-  // ---- plan: bb[b] = first block of sequence b (blocks of QT chunk tokens)
-  int carry = 0;
-  for (int b0 = 0; b0 < a.B; b0 += NT) {
-    const int b = b0 + tid;
-    const int n = b < a.B ? (a.cu_q[b + 1] - a.cu_q[b] + a.QT - 1) / a.QT : 0;
-    const int incl = wave_incl_scan(n);
-    if (lane == 63) red[wave] = incl;
-    __syncthreads();
-    int woff = 0, chunk = 0;
+  // ---- plan.  The blocks (QT chunk tokens of one sequence) are handed out
+  // longest first, so that the long ones do not start last: sequences by the
+  // octave of their length, longest octave first, in index order within one; a
+  // sequence's blocks from its last; the KV heads of a block adjacent.  Every
+  // workgroup derives the same order: start[i] = first block of the i-th
+  // sequence of it, seq[i] = that sequence.
+  auto nblk_of = [&](int b) { return (a.cu_q[b + 1] - a.cu_q[b] + a.QT - 1) / a.QT; };
+  auto octave_of = [&](int b) { return 31 - __builtin_clz((uint32_t)max(clamp_len(a.seq_lens[b], a.max_pages), 1)); };
+  if (tid == 0) *octaves = 0u;
+  __syncthreads();
+  for (int b = tid; b < a.B; b += NT)
+    if (nblk_of(b) > 0) atomicOr(octaves, 1u << octave_of(b));
+  __syncthreads();
+  uint32_t left = __builtin_amdgcn_readfirstlane(*octaves);
+  int carry = 0, ncarry = 0;                                   // blocks, sequences so far
+  while (left != 0u) {
+    const int oct = 31 - __builtin_clz(left);
+    left &= ~(1u << oct);
+    for (int b0 = 0; b0 < a.B; b0 += NT) {
+      const int b = b0 + tid;
+      const int n = b < a.B && octave_of(b) == oct ? nblk_of(b) : 0;
+      const int one = n > 0 ? 1 : 0;
+      const int incl = wave_incl_scan(n), incl1 = wave_incl_scan(one);
+      if (lane == 63) {
+        red[wave] = incl;
+        red[kPfWaves + wave] = incl1;
+      }
+      __syncthreads();
+      int woff = 0, chunk = 0, woff1 = 0, chunk1 = 0;
 #pragma unroll
-    for (int w = 0; w < kPfWaves; ++w) {
-      woff += w < wave ? red[w] : 0;
-      chunk += red[w];
+      for (int w = 0; w < kPfWaves; ++w) {
+        woff += w < wave ? red[w] : 0;
+        chunk += red[w];
+        woff1 += w < wave ? red[kPfWaves + w] : 0;
+        chunk1 += red[kPfWaves + w];
+      }
+      if (one) {
+        const int i = ncarry + woff1 + incl1 - 1;
+        start[i] = carry + woff + incl - n;
+        seq[i] = b;
+      }
+      carry += chunk;
+      ncarry += chunk1;
+      __syncthreads();
     }
-    if (b < a.B) bb[b] = carry + woff + incl - n;
-    carry += chunk;
-    __syncthreads();
   }
-  const int blk = blockIdx.x;
-  if (blk >= carry) return;                                    // past the last block: idle
-  int lo = 0, hi = a.B - 1;                                    // the last b with bb[b] <= blk
+  const int item = (int)(blockIdx.x / (unsigned)a.Hkv);
+  if (item >= carry) return;                                   // past the last block: idle
+  int lo = 0, hi = ncarry - 1;                                 // the last i with start[i] <= item
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (bb[mid] <= blk) lo = mid;
+    if (start[mid] <= item) lo = mid;
     else hi = mid - 1;
   }
-  const int b = lo;
+  const int b = seq[lo];
   const int q0 = a.cu_q[b], qlen = a.cu_q[b + 1] - q0;
-  const int t0 = (blk - bb[b]) * a.QT;                          // first chunk token of the block
+  const int t0 = (nblk_of(b) - 1 - (item - start[lo])) * a.QT;  // first chunk token of the block
   const int nt = min(a.QT, qlen - t0);                          // its tokens (at least one)
   const int Ls = clamp_len(a.seq_lens[b], a.max_pages);
   const int pos0 = Ls - qlen + t0;                              // position of token t0
@@ -2286,22 +2317,34 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
     pf_load_v<D>(vr, v_block(vid), vrho, vpart);               // V(s + 2)
     vid = page_of(s + 3);
     if (active) {
-      // V^T operands read one tile ahead of their MFMAs
+      // Output tiles in pairs: the 16 MFMAs of a pair touch each of its four
+      // accumulators every fourth MFMA, so that no MFMA waits for the result of
+      // the one before it.  V^T operands are read a pair ahead.
       const uint8_t* vb = (s & 1) ? vbuf1 : vbuf0;
       auto rd = [&](int q, int h) { return *reinterpret_cast<const v8h*>(vb + pf_v_off(16 * q + r16, 2 * j4 + h)); };
-      v8h va[2][2];
-      va[0][0] = rd(0, 0);
-      va[0][1] = rd(0, 1);
+      v8h va[2][2][2];                                         // [pair buffer][tile of the pair][half]
 #pragma unroll
-      for (int q = 0; q < kTiles; ++q) {
-        if (q + 1 < kTiles) {
-          va[(q + 1) & 1][0] = rd(q + 1, 0);
-          va[(q + 1) & 1][1] = rd(q + 1, 1);
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) va[0][qq][h] = rd(qq, h);
+#pragma unroll
+      for (int qp = 0; qp < kTiles / 2; ++qp) {
+        if (qp + 1 < kTiles / 2) {
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) va[(qp + 1) & 1][qq][h] = rd(2 * (qp + 1) + qq, h);
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
-          for (int c = 0; c < kPfNB; ++c) O[c][q] = mma2(va[q & 1][half], P[c][half], O[c][q]);
+          for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+              for (int c = 0; c < kPfNB; ++c)
+                O[c][2 * qp + qq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[qp & 1][qq][half], P[c][half][hl],
+                                                                          O[c][2 * qp + qq], 0, 0, 0);
       }
     }
     __syncthreads();                                           // buffer s & 1 is free again
@@ -2381,10 +2424,11 @@ hipError_t launch_prefill(const PrefillArgs& p, hipStream_t s) {
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   a.rot = p.rot;
   a.unrot = p.rot.k_only ? 0 : 1;
-  // blocks: at most ceil(Tq / QT) + B (each sequence ends at most one partial block)
+  // blocks: at most ceil(Tq / QT) + B (each sequence ends at most one partial
+  // block); one workgroup per block and KV head
   const int64_t nblk = ((int64_t)p.Tq + a.QT - 1) / a.QT + p.B;
-  if (nblk > INT32_MAX / 2) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)nblk, (unsigned)p.Hkv);
+  if (nblk * p.Hkv > INT32_MAX / 2) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(nblk * p.Hkv));
   auto go = [&](auto kern, size_t lds) -> hipError_t {
     if (lds > 64 * 1024) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
