@@ -1959,10 +1959,11 @@ DecodeLayout decode_layout(int format, int B, int Hq, int Hkv, int D) {
 //     turns it into float16 with the hardware FP4 converter and the slots' group
 //     scales, and writes both channels transposed ([channel][token]) into one of
 //     two LDS buffers (the next step's, while this step's is read);
-//   - every wave loads the keys itself in the FP4 decode's operand layout
-//     (double-buffered in registers) and runs, for its two 16-row column
-//     blocks, the scaled-MFMA QK, the online softmax with lazy rescaling, and
-//     the PV on f16 MFMAs with P as hi + lo and V^T operands read from LDS;
+//   - the keys are staged the same way, as the pages' bytes (PfK), and every
+//     wave reads its operands from there in the FP4 decode's layout; then, for
+//     its two 16-row column blocks, it runs the scaled-MFMA QK, the online
+//     softmax with lazy rescaling, and the PV on f16 MFMAs with P as hi + lo
+//     and V^T operands read from LDS;
 //   - one barrier, after which the buffer just read may be written again.
 // Logits past a row's own position get -inf (causal); steps that lie wholly
 // before a wave's rows take no mask, and steps wholly past them no work.  Value
@@ -1999,7 +2000,9 @@ struct PfLds {
   static constexpr int kQs = 0;                                   // [kPfRows][D] E4M3 query rows
   static constexpr int kVBuf = D * kPfKeys * 2;                   // [D][64] float16 (pf_v_off)
   static constexpr int kV = kQs + kPfRows * D;                    // two value buffers
-  static constexpr int kLoopEnd = kV + 2 * kVBuf;
+  static constexpr int kKBuf = 4 * (Fp4Block<D>::kBytes + 16);    // a step's key blocks (PfK)
+  static constexpr int kK = kV + 2 * kVBuf;                       // two key buffers
+  static constexpr int kLoopEnd = kK + 2 * kKBuf;
   static constexpr int kStage = 0;                                // [kPfWaves][16][D] float rows
   static constexpr int kStageEnd = kPfWaves * 16 * D * 4;
   static constexpr int kL = kLoopEnd > kStageEnd ? kLoopEnd : kStageEnd;   // [kPfWaves][16] float l
@@ -2008,6 +2011,63 @@ struct PfLds {
   static constexpr int kMisc = kSeq + kPfMaxSeqs * 4;             // [2][kPfWaves] scan partials, octave mask
   static constexpr int kTotal = kMisc + 2 * kPfWaves * 4 + 4;
 };
+
+// The keys of a step are staged once per workgroup: the FP4 head block of each
+// of its 4 pages verbatim, at a stride of kBlk + 16 bytes (which spreads the
+// operand reads of a key row group's 16 lanes over all LDS banks).  Lane u
+// copies kCodeLane code bytes of page u / 128; lanes u < kScLanes also copy one
+// scale dword, of page u % 4 (the other lanes load one too, and drop it, so that
+// every lane issues the same loads).
+template <int D> struct PfK {
+  static constexpr int kBlk = Fp4Block<D>::kBytes;
+  static constexpr int kCode = Fp4Block<D>::kCodeBytes;
+  static constexpr int kStride = kBlk + 16;
+  static constexpr int kCodeLane = kCode / (16 * kPfWaves);    // 8 (d 128), 4 (d 64)
+  static constexpr int kScLanes = 4 * (kBlk - kCode) / 4;      // 4 pages x (scale dwords per page)
+  uint32_t c[kCodeLane / 4];
+  uint32_t s;
+};
+
+// kb: the head block of this lane's code page; kbs: that of page tid % 4.
+template <int D>
+__device__ __forceinline__ void pf_load_k(PfK<D>& r, const uint8_t* kb, const uint8_t* kbs, int tid) {
+  using K = PfK<D>;
+  const uint8_t* cp = kb + (tid & 127) * K::kCodeLane;
+  if constexpr (K::kCodeLane == 8) {
+    const uint2 v = load8_stream(cp);
+    r.c[0] = v.x;
+    r.c[1] = v.y;
+  } else {
+    r.c[0] = load4_stream(cp);
+  }
+  r.s = load4_stream(kbs + K::kCode + 4 * ((tid >> 2) % (K::kScLanes / 4)));
+}
+
+template <int D>
+__device__ __forceinline__ void pf_store_k(const PfK<D>& r, uint8_t* kbuf, int x, int tid) {
+  using K = PfK<D>;
+  uint8_t* cp = kbuf + x * K::kStride + (tid & 127) * K::kCodeLane;
+  if constexpr (K::kCodeLane == 8) *reinterpret_cast<uint2*>(cp) = make_uint2(r.c[0], r.c[1]);
+  else *reinterpret_cast<uint32_t*>(cp) = r.c[0];
+  if (tid < K::kScLanes) *reinterpret_cast<uint32_t*>(kbuf + (tid & 3) * K::kStride + K::kCode + 4 * (tid >> 2)) = r.s;
+}
+
+// The QK operand of Fp4Pol (its load_k layout) read from a staged step.
+template <int D>
+__device__ __forceinline__ void pf_read_k(typename Fp4Pol<D>::KStep& st, const uint8_t* kbuf, int r16, int j4) {
+  using K = PfK<D>;
+  const uint8_t* kb = kbuf + (r16 >> 2) * K::kStride;
+  if (j4 < D / 32) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) st.kc[m] = *reinterpret_cast<const uint4*>(kb + (4 * m + (r16 & 3)) * (D / 2) + 16 * j4);
+    // scale bytes are stored [slot % 4][group][slot / 4]: one dword per lane
+    st.ks = *reinterpret_cast<const uint32_t*>(kb + K::kCode + 4 * ((r16 & 3) * (D / 32) + j4));
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) st.kc[m] = make_uint4(0, 0, 0, 0);
+    st.ks = 0x7F7F7F7Fu;
+  }
+}
 
 // Byte offset, in a value buffer, of channel c's tokens 8 tb .. 8 tb + 7 (16 B).
 // Rows of 128 B; the 16-B chunks of row c are permuted by c so that the
@@ -2105,6 +2165,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   uint8_t* qs = smem + L::kQs;
   uint8_t* vbuf0 = smem + L::kV;
   uint8_t* vbuf1 = smem + L::kV + L::kVBuf;
+  uint8_t* kbuf0 = smem + L::kK;
+  uint8_t* kbuf1 = smem + L::kK + L::kKBuf;
   float* stage = reinterpret_cast<float*>(smem + L::kStage);
   float* stage_l = reinterpret_cast<float*>(smem + L::kL);
   int32_t* start = reinterpret_cast<int32_t*>(smem + L::kStart);
@@ -2216,49 +2278,51 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   const int s_last = row_pos(wave * kPfNB * 16 + kPfNB * 16 - 1) / kPfKeys;
 
   const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
-  const PageGeo geo{hk, a.Hkv, a.hmask, 0, -1};   // FP4 pages only
   // Page ids are read two steps ahead, and every load of the loop is issued
   // whether or not its step exists (indices clamped into the sequence's row of
   // the table, so the bytes read are the cache's own), in a fixed order: a wait
   // for one load then never waits for loads issued after it.  Lane l reads the
-  // id of page (l % 16) / 4 of a step: its own page for the keys; the
-  // conversion takes page vx's id from lane 4 vx.
-  auto page_of = [&](int s) { return pt[max(min(4 * s + (r16 >> 2), npages - 1), 0)]; };
+  // id of page l % 4 of a step; a lane copying page x's bytes takes its id from
+  // lane x.
+  auto page_ids = [&](int s) { return pt[max(min(4 * s + (lane & 3), npages - 1), 0)]; };
   using VC = PfV<D>;
-  const int vx = __builtin_amdgcn_readfirstlane(tid >> 7);     // the page whose values this lane converts
+  const int vx = __builtin_amdgcn_readfirstlane(tid >> 7);     // the page whose keys and values this lane copies
   const int vrho = (tid & 127) / VC::kParts, vpart = (tid & 127) % VC::kParts;
-  auto v_block = [&](int ids) -> const uint8_t* {
-    const int pid = __builtin_amdgcn_readlane(ids, 4 * vx);
-    return a.v_pool + (int64_t)pid * a.page_bytes + (int64_t)fp4_block_pos(hk, pid, a.Hkv, a.hmask) * Pol::kBlk;
+  auto head_block = [&](const uint8_t* pool, int pid) {
+    return pool + (int64_t)pid * a.page_bytes + (int64_t)fp4_block_pos(hk, pid, a.Hkv, a.hmask) * Pol::kBlk;
   };
   auto v_valid = [&](int s) { return min(max(Ls - (kPfKeys * s + kPage * vx), 0), kPage); };
-  auto load_k = [&](KStep& st, int pid) { Pol::load_k_page(st, a.k_pool, pid, a.page_bytes, geo, r16, j4); };
+  // raw keys and values of the step whose page ids are in ids
+  auto load_raw = [&](PfK<D>& kr, VC& vr, int ids) {
+    const int pid = __builtin_amdgcn_readlane(ids, vx);
+    pf_load_k<D>(kr, head_block(a.k_pool, pid), head_block(a.k_pool, ids), tid);
+    pf_load_v<D>(vr, head_block(a.v_pool, pid), vrho, vpart);
+  };
 
+  PfK<D> kr;
   VC vr;
-  KStep k0, k1;
-  int kid, vid;                                                // ids: keys of step s + 1, values of step s + 2
+  int ids;                                                     // page ids of step s + 2
   {
-    const int id0 = page_of(0);
-    load_k(k0, id0);
-    pf_load_v<D>(vr, v_block(id0), vrho, vpart);
-    const int id1 = page_of(1);
+    load_raw(kr, vr, page_ids(0));
+    const int id1 = page_ids(1);
+    pf_store_k<D>(kr, kbuf0, vx, tid);
     pf_store_v<D>(vr, vbuf0, vx, vrho, vpart, v_valid(0));
-    pf_load_v<D>(vr, v_block(id1), vrho, vpart);
-    kid = id1;
-    vid = page_of(2);
+    load_raw(kr, vr, id1);
+    ids = page_ids(2);
   }
   __syncthreads();
 
-  // One step s: K(s) in kc, the values of step s in LDS buffer s & 1, the raw
-  // values of step s + 1 in vr.  MASK: the step reaches past some row of the wave.
-  auto step = [&](auto mask_t, int s, KStep& kc, KStep& kn) {
+  // One step s: the keys and values of step s in LDS buffers s & 1, the raw keys
+  // and values of step s + 1 in kr, vr.  MASK: the step reaches past some row of
+  // the wave.
+  auto step = [&](auto mask_t, int s) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_t)::value;
-    load_k(kn, kid);                                           // K(s + 1)
-    kid = page_of(s + 2);
     const bool active = !MASK || s <= s_last;                  // wave-uniform
     const int key0 = kPfKeys * s + kPage * j4;                 // first key of this lane's page
     v8h P[kPfNB][TOK / 8][2];
     if (active) {
+      KStep kc;
+      pf_read_k<D>(kc, (s & 1) ? kbuf1 : kbuf0, r16, j4);
 #pragma unroll
       for (int c = 0; c < kPfNB; ++c) {
         v4f S[TOK / 4];
@@ -2312,10 +2376,12 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
         }
       }
     }
-    // the next step's values (past the last step: a clamped page, cleared)
+    // the next step's keys and values (past the last step: a clamped page; its
+    // values cleared)
+    pf_store_k<D>(kr, (s & 1) ? kbuf0 : kbuf1, vx, tid);
     pf_store_v<D>(vr, (s & 1) ? vbuf0 : vbuf1, vx, vrho, vpart, v_valid(s + 1));
-    pf_load_v<D>(vr, v_block(vid), vrho, vpart);               // V(s + 2)
-    vid = page_of(s + 3);
+    load_raw(kr, vr, ids);                                     // step s + 2
+    ids = page_ids(s + 3);
     if (active) {
       // Output tiles in pairs: the 16 MFMAs of a pair touch each of its four
       // accumulators every fourth MFMA, so that no MFMA waits for the result of
@@ -2347,26 +2413,13 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
                                                                           O[c][2 * qp + qq], 0, 0, 0);
       }
     }
-    __syncthreads();                                           // buffer s & 1 is free again
+    __syncthreads();                                           // buffers s & 1 are free again
   };
   using Free = std::false_type;
   using Masked = std::true_type;
-  // the step loop is unrolled by two so that the key buffers are named, not
-  // indexed, and stay in registers
   int s = 0;
-  for (; s + 2 <= s_free && s + 2 <= steps; s += 2) {
-    step(Free{}, s, k0, k1);
-    step(Free{}, s + 1, k1, k0);
-  }
-  if (s < s_free && s < steps) {
-    step(Free{}, s, k0, k1);
-    ++s;
-    if (s < steps) k0 = k1;                                    // K(s), prefetched into k1
-  }
-  for (; s < steps; s += 2) {
-    step(Masked{}, s, k0, k1);
-    if (s + 1 < steps) step(Masked{}, s + 1, k1, k0);
-  }
+  for (; s < s_free && s < steps; ++s) step(Free{}, s);
+  for (; s < steps; ++s) step(Masked{}, s);
 
   // ---- rows out: block by block through the wave's LDS stage (16 rows), two
   // rows at a time per wave (one per 32-lane half), normalized, rotated back.
