@@ -2315,14 +2315,15 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   // One step s: the keys and values of step s in LDS buffers s & 1, the raw keys
   // and values of step s + 1 in kr, vr.  MASK: the step reaches past some row of
   // the wave.
-  auto step = [&](auto mask_t, int s) __attribute__((always_inline)) {
+  auto step = [&](auto mask_t, auto odd_t, int s) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(odd_t)::value;                // s & 1, known where the step is placed
     constexpr bool MASK = decltype(mask_t)::value;
     const bool active = !MASK || s <= s_last;                  // wave-uniform
     const int key0 = kPfKeys * s + kPage * j4;                 // first key of this lane's page
     v8h P[kPfNB][TOK / 8][2];
     if (active) {
       KStep kc;
-      pf_read_k<D>(kc, (s & 1) ? kbuf1 : kbuf0, r16, j4);
+      pf_read_k<D>(kc, ODD ? kbuf1 : kbuf0, r16, j4);
 #pragma unroll
       for (int c = 0; c < kPfNB; ++c) {
         v4f S[TOK / 4];
@@ -2378,15 +2379,15 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
     }
     // the next step's keys and values (past the last step: a clamped page; its
     // values cleared)
-    pf_store_k<D>(kr, (s & 1) ? kbuf0 : kbuf1, vx, tid);
-    pf_store_v<D>(vr, (s & 1) ? vbuf0 : vbuf1, vx, vrho, vpart, v_valid(s + 1));
+    pf_store_k<D>(kr, ODD ? kbuf0 : kbuf1, vx, tid);
+    pf_store_v<D>(vr, ODD ? vbuf0 : vbuf1, vx, vrho, vpart, v_valid(s + 1));
     load_raw(kr, vr, ids);                                     // step s + 2
     ids = page_ids(s + 3);
     if (active) {
       // Output tiles in pairs: the 16 MFMAs of a pair touch each of its four
       // accumulators every fourth MFMA, so that no MFMA waits for the result of
       // the one before it.  V^T operands are read a pair ahead.
-      const uint8_t* vb = (s & 1) ? vbuf1 : vbuf0;
+      const uint8_t* vb = ODD ? vbuf1 : vbuf0;
       auto rd = [&](int q, int h) { return *reinterpret_cast<const v8h*>(vb + pf_v_off(16 * q + r16, 2 * j4 + h)); };
       v8h va[2][2][2];                                         // [pair buffer][tile of the pair][half]
 #pragma unroll
@@ -2417,9 +2418,21 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   };
   using Free = std::false_type;
   using Masked = std::true_type;
+  using Even = std::false_type;
+  using Odd = std::true_type;
+  // The step loop is unrolled by two so that each step's LDS buffers are fixed
+  // offsets.
   int s = 0;
-  for (; s < s_free && s < steps; ++s) step(Free{}, s);
-  for (; s < steps; ++s) step(Masked{}, s);
+  for (; s + 2 <= s_free && s + 2 <= steps; s += 2) {
+    step(Free{}, Even{}, s);
+    step(Free{}, Odd{}, s + 1);
+  }
+  if (s < s_free && s < steps) step(Free{}, Even{}, s++);
+  if ((s & 1) && s < steps) step(Masked{}, Odd{}, s++);
+  for (; s < steps; s += 2) {
+    step(Masked{}, Even{}, s);
+    if (s + 1 < steps) step(Masked{}, Odd{}, s + 1);
+  }
 
   // ---- rows out: block by block through the wave's LDS stage (16 rows), two
   // rows at a time per wave (one per 32-lane half), normalized, rotated back.
