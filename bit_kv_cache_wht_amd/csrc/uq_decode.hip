@@ -1480,15 +1480,19 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
     }
     ck = claim_at(g0[N]);
     meta[N] = ck.meta;
-    if constexpr (FMT == UQ_KV_FP4) {
-      if (nwrite) write_new<RV>(nrow, nblk, noff, nlive, nv, np, a.constopt != 0, a.rot);   // ordered before the main loop's claims by its barrier
-    }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       load_k(kst[i], c0[i]);
       if (i < N - 1) load_v(vst[i], c0[i]);
     }
     cv = c0[N - 1];
+    // The newest token's write, while the first steps' loads are in flight: those
+    // steps do not hold its slot (when one of the round's first NW (N + 1) steps
+    // is an item's last, the write went out before the claims, above); it is
+    // ordered before the main loop's claims by the barrier below.
+    if constexpr (FMT == UQ_KV_FP4) {
+      if (nwrite) write_new<RV>(nrow, nblk, noff, nlive, nv, np, a.constopt != 0, a.rot);
+    }
 
     if (qr0 < nrows) qrows.template finish<RV>(qs + qr0 * D * ESZ, qp, a.rot);
     for (int r = qr0 + NT / 16; r < nrows; r += NT / 16) {
@@ -1813,7 +1817,7 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
 
   // rows of empty sequences are zero
   for (int b = wg; b < a.B; b += gridDim.x) {
-    if (clamp_len(seq_lens[b], a.max_pages) > 0) continue;
+    if (lens[b] > 0) continue;                     // the plan's clamped lengths, still in LDS
     for (int i = tid; i < a.Hq * D; i += NT) a.out[(int64_t)b * a.Hq * D + i] = 0.f;
   }
   if (a.clocks != nullptr) {                       // after every wave of the workgroup has finished
