@@ -1750,63 +1750,85 @@ __global__ __launch_bounds__(256 * Pol::kOcc, 1) void decode_kernel(const KArgs 
         flags[tid] = is_last;
       }
       __syncthreads();
-      for (int row = wave; row < nrows; row += NW) {
-        const int k = row / G, h = row - k * G;
-        if (!flags[k]) continue;
+      // Two rows per wave at a time, lanes 0-31 the first and 32-63 the second
+      // (channels (lane % 32) + 32 c).  A row's contributors go 32 at a time, lane
+      // i of the half holding contributor c0 + i's (m, l); their O rows are read
+      // 16 contributors per batch, the first batch together with the (m, l)
+      // reads, so that a merge of up to 16 contributors waits for one round trip
+      // (each read goes past the L2 to the device level).
+      constexpr int PC = D / 32;
+      constexpr int BATCH = 16;
+      const int half = lane >> 5, l32 = lane & 31;
+      for (int row0 = 2 * __builtin_amdgcn_readfirstlane(wave); row0 < nrows; row0 += 2 * NW) {
+        const int row = row0 + half;
+        const int rr = row < nrows ? row : row0;
+        const int k = rr / G, h = rr - k * G;
+        const bool mine = row < nrows && flags[k] != 0;
+        if (!__any(mine)) continue;
         const int32_t* r = rec + 8 * k;
         const int b = r[kRecB], hk = r[kRecHk];
         const int steps = seq_steps<NP>(lens[b]);
         const int start = base[b] + hk * steps;
-        const int w0 = owner(start, b * Hi + hk), n = r[kRecNContrib];
+        const int w0 = owner(start, b * Hi + hk), n = mine ? r[kRecNContrib] : 0;
         // partial of contributor w0 + i: slot 2w if the item begins its share, else 2w + 1
         auto prow_of = [&](int i) -> int64_t {
           const int w = w0 + i;
           return (int64_t)(2 * w + (share_begin(w) >= start ? 0 : 1)) * G + h;
         };
-        // Contributors 64 at a time, lane i holding contributor c0 + i's (m, l);
-        // their O rows are read 8 contributors per batch, all loads of a batch
-        // in flight together (each read goes past the L2 to the device level).
-        float m = -INFINITY, l = 0.f, o[PER];
+        const int nmax = max(n, __shfl_xor(n, 32));              // the wave's loop bound
+        float m = -INFINITY, l = 0.f, o[PC];
 #pragma unroll
-        for (int kk = 0; kk < PER; ++kk) o[kk] = 0.f;
-        for (int c0 = 0; c0 < n; c0 += 64) {
-          const int nc = min(64, n - c0);
+        for (int c = 0; c < PC; ++c) o[c] = 0.f;
+        for (int c0 = 0; c0 < nmax; c0 += 32) {
+          const int nc = min(32, n - c0);                         // <= 0: no contributor left in this half
           float vm = -INFINITY, vl = 0.f;
-          if (lane < nc) {
-            const float* v = a.ml + 2 * prow_of(c0 + lane);
+          if (l32 < nc) {
+            const float* v = a.ml + 2 * prow_of(c0 + l32);
             vm = ld_dev(v);
             vl = ld_dev(v + 1);
           }
+          const int ncmax = min(32, nmax - c0);
+          float buf[BATCH][PC];
+          auto fetch = [&](int i0) {                              // contributors c0 + i0 ..: past nc, weight 0
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) {
+              if (nc > 0) {
+                const float* src = a.po + prow_of(c0 + min(i0 + j, nc - 1)) * D + l32;
+#pragma unroll
+                for (int c = 0; c < PC; ++c) buf[j][c] = ld_dev(src + 32 * c);
+              } else {
+#pragma unroll
+                for (int c = 0; c < PC; ++c) buf[j][c] = 0.f;
+              }
+            }
+          };
+          fetch(0);
           float mc = vm;
 #pragma unroll
-          for (int x = 32; x >= 1; x >>= 1) mc = fmaxf(mc, __shfl_xor(mc, x));
+          for (int x = 16; x >= 1; x >>= 1) mc = fmaxf(mc, __shfl_xor(mc, x));
           const float mn = fmaxf(m, mc);
           const float keep = m > -INFINITY ? __builtin_amdgcn_exp2f(m - mn) : 0.f;   // rescale of earlier chunks
           const float wt = vm > -INFINITY ? __builtin_amdgcn_exp2f(vm - mn) : 0.f;
           float lw = wt * vl;
 #pragma unroll
-          for (int x = 32; x >= 1; x >>= 1) lw += __shfl_xor(lw, x);
+          for (int x = 16; x >= 1; x >>= 1) lw += __shfl_xor(lw, x);
           l = l * keep + lw;
 #pragma unroll
-          for (int kk = 0; kk < PER; ++kk) o[kk] *= keep;
+          for (int c = 0; c < PC; ++c) o[c] *= keep;
           m = mn;
-          for (int i0 = 0; i0 < nc; i0 += 8) {
-            float buf[8][PER];
+          for (int i0 = 0; i0 < ncmax; i0 += BATCH) {
+            if (i0 > 0) fetch(i0);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float* src = a.po + prow_of(c0 + min(i0 + j, nc - 1)) * D + lane;   // past nc: weight 0
+            for (int j = 0; j < BATCH; ++j) {
+              // the weight of contributor c0 + i0 + j, from its lane of the half (0 past nc)
+              const float ws = __shfl(wt, 32 * half + min(i0 + j, 31));
+              const float wj = i0 + j < nc ? ws : 0.f;
 #pragma unroll
-              for (int kk = 0; kk < PER; ++kk) buf[j][kk] = ld_dev(src + 64 * kk);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float ws = __shfl(wt, i0 + j);             // i0 + j < 64; 0 past nc (lane >= nc)
-#pragma unroll
-              for (int kk = 0; kk < PER; ++kk) o[kk] += ws * buf[j][kk];
+              for (int c = 0; c < PC; ++c) o[c] += wj * buf[j][c];
             }
           }
         }
-        store_row<D, UNROT, RV>(o, l, a.out + ((int64_t)b * a.Hq + (int64_t)hk * G + h) * D, lane, a.rot);
+        store_row32<D, UNROT, RV>(o, l, a.out + ((int64_t)b * a.Hq + (int64_t)hk * G + h) * D, mine, lane, a.rot);
       }
     }
     if (tid == 0) *ctr = 0;                        // every claim of this round is done (barrier above)
