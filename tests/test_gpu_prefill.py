@@ -6,7 +6,8 @@ prefix) within relative L2 1e-3 and max-abs 5e-3.
 
 Cases: chunks after a prefix and whole prompts, chunk lengths that are not
 multiples of a workgroup's tokens, empty chunks, GQA groups of 1, 4, 8 and 16,
-whole prompts of several hundred tokens with one query head per KV head,
+whole prompts of several hundred tokens with one query head per KV head, 600
+sequences (the workgroups' plan in several chunks),
 d = 64 and 128, bf16 and f32 inputs, and single-token chunks (which must also
 agree with the decode entry point itself)."""
 import numpy as np
@@ -60,6 +61,28 @@ def test_prefill_matches_oracle(name):
     want = O.prefill_attention(FMT_ID["fp4"], kp, vp, wl.num_kv_heads, wl.head_dim, q, np.diff(cu),
                                wl.page_table, wl.seq_lens, sm_scale(wl.head_dim), in_dtype=wl.in_dtype)
     assert_close(got, want, f"prefill {name}")
+
+
+def test_many_sequences_across_plan_chunks():
+    # 600 sequences: the workgroups' plan scans lengths 512 at a time, and orders
+    # them by length octave (1 .. 256 tokens here: nine octaves) with the blocks of
+    # each sequence last-first; some chunks are empty, some whole sequences
+    rng = np.random.default_rng(700)
+    B = 600
+    lens = np.exp2(rng.uniform(0, 8, B)).astype(np.int64)
+    chunks = np.minimum(rng.integers(0, 12, B), lens)
+    chunks[rng.random(B) < 0.1] = 0
+    whole = rng.random(B) < 0.05
+    chunks[whole] = lens[whole]
+    wl = W.make_workload("many_seqs", B, 4, 2, 128, lens.tolist(), chunks.tolist(), seed=701)
+    q, cu = W.prefill_queries(wl, seed=702)
+    announce(f"prefill fp4 many_seqs B={B} lens {int(lens.min())}..{int(lens.max())} Tq={q.shape[0]}")
+    cache = gpu_append("fp4", wl)
+    got = _gpu_prefill(wl, q, cu, cache)
+    kp, vp = oracle_append("fp4", wl)
+    want = O.prefill_attention(FMT_ID["fp4"], kp, vp, wl.num_kv_heads, wl.head_dim, q, np.diff(cu),
+                               wl.page_table, wl.seq_lens, sm_scale(wl.head_dim), in_dtype=wl.in_dtype)
+    assert_close(got, want, "prefill many_seqs")
 
 
 def test_single_token_chunks_equal_decode():
