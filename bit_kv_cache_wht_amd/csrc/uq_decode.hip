@@ -2199,7 +2199,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   int32_t* seq = reinterpret_cast<int32_t*>(smem + L::kSeq);
   int32_t* red = reinterpret_cast<int32_t*>(smem + L::kMisc);
   uint32_t* octaves = reinterpret_cast<uint32_t*>(smem + L::kMisc + 2 * kPfWaves * 4);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform values stay scalar
   const int r16 = lane & 15, j4 = lane >> 4;
   const int hk = (int)(blockIdx.x % (unsigned)a.Hkv);
 
@@ -2257,9 +2258,10 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
     if (start[mid] <= item) lo = mid;
     else hi = mid - 1;
   }
-  const int b = seq[lo];
+  // the block's sequence and first chunk token: the same in every lane (scalar)
+  const int b = __builtin_amdgcn_readfirstlane(seq[lo]);
   const int q0 = a.cu_q[b], qlen = a.cu_q[b + 1] - q0;
-  const int t0 = (nblk_of(b) - 1 - (item - start[lo])) * a.QT;  // first chunk token of the block
+  const int t0 = (nblk_of(b) - 1 - (item - __builtin_amdgcn_readfirstlane(start[lo]))) * a.QT;  // first chunk token of the block
   const int nt = min(a.QT, qlen - t0);                          // its tokens (at least one)
   const int Ls = clamp_len(a.seq_lens[b], a.max_pages);
   const int pos0 = Ls - qlen + t0;                              // position of token t0
