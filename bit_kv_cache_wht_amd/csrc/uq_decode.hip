@@ -2000,7 +2000,10 @@ constexpr int kPfWaves = 8;                               // two per SIMD
 constexpr int kPfNB = 2;                                  // column blocks per wave
 constexpr int kPfRows = 16 * kPfNB * kPfWaves;            // query rows of a workgroup
 constexpr int kPfMaxSeqs = 4096;                          // plan in LDS
-constexpr int kPfKeys = 4 * kPage;                        // keys per step
+constexpr int kPfPages = 8;                               // pages per staged step
+constexpr int kPfKeys = kPfPages * kPage;                 // keys per staged step
+constexpr int kPfSubKeys = 4 * kPage;                     // keys per MFMA sub-step (Fp4Pol's step)
+constexpr int kPfVRow = 2 * kPfKeys + 16;                 // bytes per channel row of a value buffer (pf_v_off)
 
 struct PfArgs {
   const uint8_t* k_pool;
@@ -2013,6 +2016,7 @@ struct PfArgs {
   const int32_t* seq_lens;    // [B]
   float* out;                 // [Tq][Hq][D]
   int32_t B, Hq, Hkv, G, QT;
+  uint32_t g_mul;             // ceil(2^16 / G): (x g_mul) >> 16 = x / G for 0 <= x < 256, G <= 256
   int32_t hmask;              // Hkv - 1 when Hkv is a power of two, else -1
   float scale_log2;
   Rot rot;                    // the cache's rotation variant
@@ -2024,9 +2028,9 @@ struct PfLds {
   // The query rows and the value buffers are dead once the last step has ended;
   // the output stage then reuses their bytes.
   static constexpr int kQs = 0;                                   // [kPfRows][D] E4M3 query rows
-  static constexpr int kVBuf = D * kPfKeys * 2;                   // [D][64] float16 (pf_v_off)
+  static constexpr int kVBuf = D * kPfVRow;                       // [D][kPfKeys] float16 (pf_v_off)
   static constexpr int kV = kQs + kPfRows * D;                    // two value buffers
-  static constexpr int kKBuf = 4 * (Fp4Block<D>::kBytes + 16);    // a step's key blocks (PfK)
+  static constexpr int kKBuf = kPfPages * (Fp4Block<D>::kBytes + 16);   // a step's key blocks (PfK)
   static constexpr int kK = kV + 2 * kVBuf;                       // two key buffers
   static constexpr int kLoopEnd = kK + 2 * kKBuf;
   static constexpr int kStage = 0;                                // [kPfWaves][16][D] float rows
@@ -2039,43 +2043,48 @@ struct PfLds {
 };
 
 // The keys of a step are staged once per workgroup: the FP4 head block of each
-// of its 4 pages verbatim, at a stride of kBlk + 16 bytes (which spreads the
-// operand reads of a key row group's 16 lanes over all LDS banks).  Lane u
-// copies kCodeLane code bytes of page u / 128; lanes u < kScLanes also copy one
-// scale dword, of page u % 4 (the other lanes load one too, and drop it, so that
-// every lane issues the same loads).
+// of its kPfPages pages verbatim, at a stride of kBlk + 16 bytes (which spreads
+// the operand reads of a key row group's 16 lanes over all LDS banks).  Lane u
+// copies kCodeLane code bytes of page u / 64 (the wave's page); lanes
+// u < kScLanes also copy one scale dword, of page u % 8 (the other lanes load
+// one too, and drop it, so that every lane issues the same loads).
 template <int D> struct PfK {
   static constexpr int kBlk = Fp4Block<D>::kBytes;
   static constexpr int kCode = Fp4Block<D>::kCodeBytes;
   static constexpr int kStride = kBlk + 16;
-  static constexpr int kCodeLane = kCode / (16 * kPfWaves);    // 8 (d 128), 4 (d 64)
-  static constexpr int kScLanes = 4 * (kBlk - kCode) / 4;      // 4 pages x (scale dwords per page)
+  static constexpr int kCodeLane = kCode / 64;                 // 16 (d 128), 8 (d 64)
+  static constexpr int kScWords = (kBlk - kCode) / 4;          // scale dwords of a page
+  static constexpr int kScLanes = kPfPages * kScWords;
   uint32_t c[kCodeLane / 4];
   uint32_t s;
 };
 
-// kb: the head block of this lane's code page; kbs: that of page tid % 4.
+// kb: the head block of this lane's code page; kbs: that of page tid % 8.
 template <int D>
 __device__ __forceinline__ void pf_load_k(PfK<D>& r, const uint8_t* kb, const uint8_t* kbs, int tid) {
   using K = PfK<D>;
-  const uint8_t* cp = kb + (tid & 127) * K::kCodeLane;
-  if constexpr (K::kCodeLane == 8) {
+  const uint8_t* cp = kb + (tid & 63) * K::kCodeLane;
+  if constexpr (K::kCodeLane == 16) {
+    const uint4 v = load16_stream(cp);
+    r.c[0] = v.x;
+    r.c[1] = v.y;
+    r.c[2] = v.z;
+    r.c[3] = v.w;
+  } else {
     const uint2 v = load8_stream(cp);
     r.c[0] = v.x;
     r.c[1] = v.y;
-  } else {
-    r.c[0] = load4_stream(cp);
   }
-  r.s = load4_stream(kbs + K::kCode + 4 * ((tid >> 2) % (K::kScLanes / 4)));
+  r.s = load4_stream(kbs + K::kCode + 4 * ((tid >> 3) % K::kScWords));
 }
 
 template <int D>
 __device__ __forceinline__ void pf_store_k(const PfK<D>& r, uint8_t* kbuf, int x, int tid) {
   using K = PfK<D>;
-  uint8_t* cp = kbuf + x * K::kStride + (tid & 127) * K::kCodeLane;
-  if constexpr (K::kCodeLane == 8) *reinterpret_cast<uint2*>(cp) = make_uint2(r.c[0], r.c[1]);
-  else *reinterpret_cast<uint32_t*>(cp) = r.c[0];
-  if (tid < K::kScLanes) *reinterpret_cast<uint32_t*>(kbuf + (tid & 3) * K::kStride + K::kCode + 4 * (tid >> 2)) = r.s;
+  uint8_t* cp = kbuf + x * K::kStride + (tid & 63) * K::kCodeLane;
+  if constexpr (K::kCodeLane == 16) *reinterpret_cast<uint4*>(cp) = make_uint4(r.c[0], r.c[1], r.c[2], r.c[3]);
+  else *reinterpret_cast<uint2*>(cp) = make_uint2(r.c[0], r.c[1]);
+  if (tid < K::kScLanes) *reinterpret_cast<uint32_t*>(kbuf + (tid & 7) * K::kStride + K::kCode + 4 * (tid >> 3)) = r.s;
 }
 
 // The QK operand of Fp4Pol (its load_k layout) read from a staged step.
@@ -2096,37 +2105,41 @@ __device__ __forceinline__ void pf_read_k(typename Fp4Pol<D>::KStep& st, const u
 }
 
 // Byte offset, in a value buffer, of channel c's tokens 8 tb .. 8 tb + 7 (16 B).
-// Rows of 128 B; the 16-B chunks of row c are permuted by c so that the
-// conversion's stores (8 lanes: channels 8 apart) and the PV operand reads (8
-// lanes: 8 consecutive channels) each cover all eight chunks.
-__device__ __forceinline__ int pf_v_off(int c, int tb) { return c * (2 * kPfKeys) + 16 * (tb ^ ((c ^ (c >> 3)) & 7)); }
+// Rows of kPfVRow = 2 kPfKeys + 16 bytes: the padding puts 16 consecutive channels' chunk
+// tb in 16 different bank groups, so the PV operand reads (16 lanes, 16
+// consecutive channels) are conflict free with one base address per lane, and
+// the conversion's stores (16 lanes, 8 consecutive channel pairs) meet at most
+// two to a bank group.
+__device__ __forceinline__ int pf_v_off(int c, int tb) { return c * kPfVRow + 16 * tb; }
 
 // A step's values are converted by all the workgroup's lanes: lane u takes page
-// x = u / 128 of the step, code row rho = (u % 128) / kParts of it (row
-// rho = 16 q + r holds channel pair p = (D/32) r + q, byte t = slot t) and the
+// x = u / 64 of the step (the wave's), channel pair p = (u % 64) / kParts of it
+// (held by code row 16 q + r for p = (D/32) r + q, byte t = slot t) and the
 // kSlots slots kSlots part .. of that row, with their scale bytes (those of p's
 // group, byte t = slot t).
 template <int D> struct PfV {
   static constexpr int kRows = D / 2;                          // code rows of a page
-  static constexpr int kParts = 16 * kPfWaves / kRows;         // lanes per row: 2 (d 128), 4 (d 64)
-  static constexpr int kSlots = kPage / kParts;                // slots per lane: 8, 4
+  static constexpr int kParts = 64 / kRows;                    // lanes per row: 1 (d 128), 2 (d 64)
+  static constexpr int kSlots = kPage / kParts;                // slots per lane: 16, 8
   static constexpr int kW = kSlots / 4;
   uint32_t c[kW], s[kW];
 };
-template <int D> __device__ __forceinline__ int pf_pair(int rho) { return (D / 32) * (rho % 16) + rho / 16; }
+// the code row that holds channel pair p
+template <int D> __device__ __forceinline__ int pf_row(int p) { return 16 * (p % (D / 32)) + p / (D / 32); }
 
 template <int D>
-__device__ __forceinline__ void pf_load_v(PfV<D>& r, const uint8_t* vb, int rho, int part) {
+__device__ __forceinline__ void pf_load_v(PfV<D>& r, const uint8_t* vb, int p, int part) {
   using V = PfV<D>;
-  const uint8_t* cb = vb + rho * kPage + V::kSlots * part;
-  const uint8_t* sb = vb + Fp4Block<D>::kCodeBytes + kPage * (pf_pair<D>(rho) / 16) + V::kSlots * part;
-  if constexpr (V::kW == 2) {
+  const uint8_t* cb = vb + pf_row<D>(p) * kPage + V::kSlots * part;
+  const uint8_t* sb = vb + Fp4Block<D>::kCodeBytes + kPage * (p / 16) + V::kSlots * part;
+  if constexpr (V::kW == 4) {
+    const uint4 c = load16_stream(cb), sc = load16_stream(sb);
+    r.c[0] = c.x; r.c[1] = c.y; r.c[2] = c.z; r.c[3] = c.w;
+    r.s[0] = sc.x; r.s[1] = sc.y; r.s[2] = sc.z; r.s[3] = sc.w;
+  } else {
     const uint2 c = load8_stream(cb), sc = load8_stream(sb);
     r.c[0] = c.x; r.c[1] = c.y;
     r.s[0] = sc.x; r.s[1] = sc.y;
-  } else {
-    r.c[0] = load4_stream(cb);
-    r.s[0] = load4_stream(sb);
   }
 }
 
@@ -2134,10 +2147,9 @@ __device__ __forceinline__ void pf_load_v(PfV<D>& r, const uint8_t* vb, int rho,
 // give zero: their codes are cleared and their scale set to 2^0), stored as
 // tokens 16 x + kSlots part .. of the value buffer.
 template <int D>
-__device__ __forceinline__ void pf_store_v(PfV<D> r, uint8_t* vbuf, int x, int rho, int part, int nvalid) {
+__device__ __forceinline__ void pf_store_v(PfV<D> r, uint8_t* vbuf, int x, int p, int part, int nvalid) {
   using V = PfV<D>;
   constexpr int NS = V::kSlots;
-  const int p = pf_pair<D>(rho);
   const int first = NS * part;
   if (nvalid < first + NS) {
 #pragma unroll
@@ -2169,13 +2181,12 @@ __device__ __forceinline__ void pf_store_v(PfV<D> r, uint8_t* vbuf, int x, int r
     ev[i] = __builtin_amdgcn_perm(X[2 * i + 1], X[2 * i], 0x05040100u);   // low halves: channel 2p
     od[i] = __builtin_amdgcn_perm(X[2 * i + 1], X[2 * i], 0x07060302u);   // high halves: channel 2p + 1
   }
-  if constexpr (NS == 8) {
-    *reinterpret_cast<uint4*>(vbuf + pf_v_off(2 * p, 2 * x + part)) = make_uint4(ev[0], ev[1], ev[2], ev[3]);
-    *reinterpret_cast<uint4*>(vbuf + pf_v_off(2 * p + 1, 2 * x + part)) = make_uint4(od[0], od[1], od[2], od[3]);
-  } else {
-    const int half = 8 * (part & 1);
-    *reinterpret_cast<uint2*>(vbuf + pf_v_off(2 * p, 2 * x + (part >> 1)) + half) = make_uint2(ev[0], ev[1]);
-    *reinterpret_cast<uint2*>(vbuf + pf_v_off(2 * p + 1, 2 * x + (part >> 1)) + half) = make_uint2(od[0], od[1]);
+  // 8 slots (one 16-B chunk of tokens) per store
+#pragma unroll
+  for (int h = 0; h < NS / 8; ++h) {
+    const int tb = 2 * x + (NS == 16 ? h : part);
+    *reinterpret_cast<uint4*>(vbuf + pf_v_off(2 * p, tb)) = make_uint4(ev[4 * h], ev[4 * h + 1], ev[4 * h + 2], ev[4 * h + 3]);
+    *reinterpret_cast<uint4*>(vbuf + pf_v_off(2 * p + 1, tb)) = make_uint4(od[4 * h], od[4 * h + 1], od[4 * h + 2], od[4 * h + 3]);
   }
 }
 
@@ -2266,11 +2277,14 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   const int Ls = clamp_len(a.seq_lens[b], a.max_pages);
   const int pos0 = Ls - qlen + t0;                              // position of token t0
   const int nrows = nt * a.G;
+  // row / G for a workgroup row (below kPfRows) by a multiply: no division
+  // sequence whose reciprocal would stay live through the step loop
+  auto div_g = [&](int r) { return (int)(__umul24((uint32_t)r, a.g_mul) >> 16); };
   const int npages = (Ls + kPage - 1) / kPage;
   // position of row r; padding rows (r >= nrows: zero queries, not stored) take
   // the last row's, so that positions never decrease with r
   auto row_pos = [&](int r) -> int {
-    const int p = pos0 + min(r, nrows - 1) / a.G;
+    const int p = pos0 + div_g(min(r, nrows - 1));
     return p < 0 ? 0 : p;
   };
   const int steps = row_pos(nrows - 1) / kPfKeys + 1;
@@ -2280,7 +2294,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
     const int p = tid & 15;
     QueryRows<D, IN, UQ_KV_FP4> qr;
     const bool valid = r < nrows;
-    const int64_t qrow = (int64_t)(q0 + t0 + (valid ? r / a.G : 0)) * a.Hq + (int64_t)hk * a.G + (valid ? r % a.G : 0);
+    const int rg = valid ? div_g(r) : 0;
+    const int64_t qrow = (int64_t)(q0 + t0 + rg) * a.Hq + (int64_t)hk * a.G + (valid ? r - rg * a.G : 0);
     qr.load(a.q, qrow, valid, p);
     qr.template finish<true>(qs + r * D, p, a.rot);
   }
@@ -2310,12 +2325,12 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   // whether or not its step exists (indices clamped into the sequence's row of
   // the table, so the bytes read are the cache's own), in a fixed order: a wait
   // for one load then never waits for loads issued after it.  Lane l reads the
-  // id of page l % 4 of a step; a lane copying page x's bytes takes its id from
+  // id of page l % 8 of a step; a lane copying page x's bytes takes its id from
   // lane x.
-  auto page_ids = [&](int s) { return pt[max(min(4 * s + (lane & 3), npages - 1), 0)]; };
+  auto page_ids = [&](int s) { return pt[max(min(kPfPages * s + (lane & 7), npages - 1), 0)]; };
   using VC = PfV<D>;
-  const int vx = __builtin_amdgcn_readfirstlane(tid >> 7);     // the page whose keys and values this lane copies
-  const int vrho = (tid & 127) / VC::kParts, vpart = (tid & 127) % VC::kParts;
+  const int vx = wave;                                         // the page whose keys and values this lane copies
+  const int vp = (tid & 63) / VC::kParts, vpart = (tid & 63) % VC::kParts;
   auto head_block = [&](const uint8_t* pool, int pid) {
     return pool + (int64_t)pid * a.page_bytes + (int64_t)fp4_block_pos(hk, pid, a.Hkv, a.hmask) * Pol::kBlk;
   };
@@ -2324,7 +2339,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
   auto load_raw = [&](PfK<D>& kr, VC& vr, int ids) {
     const int pid = __builtin_amdgcn_readlane(ids, vx);
     pf_load_k<D>(kr, head_block(a.k_pool, pid), head_block(a.k_pool, ids), tid);
-    pf_load_v<D>(vr, head_block(a.v_pool, pid), vrho, vpart);
+    pf_load_v<D>(vr, head_block(a.v_pool, pid), vp, vpart);
   };
 
   PfK<D> kr;
@@ -2334,114 +2349,128 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
     load_raw(kr, vr, page_ids(0));
     const int id1 = page_ids(1);
     pf_store_k<D>(kr, kbuf0, vx, tid);
-    pf_store_v<D>(vr, vbuf0, vx, vrho, vpart, v_valid(0));
+    pf_store_v<D>(vr, vbuf0, vx, vp, vpart, v_valid(0));
     load_raw(kr, vr, id1);
     ids = page_ids(2);
   }
   __syncthreads();
 
-  // One step s: the keys and values of step s in LDS buffers s & 1, the raw keys
-  // and values of step s + 1 in kr, vr.  MASK: the step reaches past some row of
-  // the wave.
-  auto step = [&](auto mask_t, auto odd_t, int s) __attribute__((always_inline)) {
-    constexpr bool ODD = decltype(odd_t)::value;                // s & 1, known where the step is placed
+  // A staged step is two MFMA sub-steps of 4 pages (64 keys) each, the FP4
+  // decode's step: the keys of sub-step `sub` are pages 4 sub .. 4 sub + 3 of
+  // the staged ones, its values tokens 64 sub .. of the value buffer.
+  v8h P[kPfNB][TOK / 8][2];
+  // QK and online softmax of both column blocks, leaving P.  MASK: the step
+  // reaches past some row of the wave.
+  auto softmax_sub = [&](auto mask_t, int s, int sub, const uint8_t* kb) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_t)::value;
-    const bool active = !MASK || s <= s_last;                  // wave-uniform
-    const int key0 = kPfKeys * s + kPage * j4;                 // first key of this lane's page
-    v8h P[kPfNB][TOK / 8][2];
-    if (active) {
-      KStep kc;
-      pf_read_k<D>(kc, ODD ? kbuf1 : kbuf0, r16, j4);
+    const int key0 = kPfKeys * s + kPfSubKeys * sub + kPage * j4;   // first key of this lane's page
+    KStep kc;
+    pf_read_k<D>(kc, kb + 4 * sub * PfK<D>::kStride, r16, j4);
 #pragma unroll
-      for (int c = 0; c < kPfNB; ++c) {
-        v4f S[TOK / 4];
-        Pol::qk(kc, qo[c], S);
-        float t[TOK];
+    for (int c = 0; c < kPfNB; ++c) {
+      v4f S[TOK / 4];
+      Pol::qk(kc, qo[c], S);
+      float t[TOK];
 #pragma unroll
-        for (int m = 0; m < TOK / 4; ++m)
+      for (int m = 0; m < TOK / 4; ++m)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) t[4 * m + v] = S[m][v];
-        if constexpr (MASK) {
-          const int nvalid = min(max(rpos[c] - key0 + 1, 0), TOK);   // causal: keys <= the row's position
+        for (int v = 0; v < 4; ++v) t[4 * m + v] = S[m][v];
+      if constexpr (MASK) {
+        const int nvalid = min(max(rpos[c] - key0 + 1, 0), TOK);   // causal: keys <= the row's position
 #pragma unroll
-          for (int i = 0; i < TOK; ++i) t[i] = i < nvalid ? t[i] : -INFINITY;
-        }
-        float neg_mc = -m_run[c] * a.scale_log2;
-        float pf[TOK];
+        for (int i = 0; i < TOK; ++i) t[i] = i < nvalid ? t[i] : -INFINITY;
+      }
+      float neg_mc = -m_run[c] * a.scale_log2;
+      float pf[TOK];
+#pragma unroll
+      for (int i = 0; i < TOK; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
+      float psum = pf[0];
+#pragma unroll
+      for (int i = 1; i < TOK; ++i) psum += pf[i];
+      if (__any(!(psum <= 256.f))) {
+        float mx = t[0];
+#pragma unroll
+        for (int i = 1; i < TOK; ++i) mx = fmaxf(mx, t[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[c], mx);
+        // a row whose every key so far is masked keeps m = -inf and takes no rescale
+        const float alpha = m_new > -INFINITY ? __builtin_amdgcn_exp2f((m_run[c] - m_new) * a.scale_log2) : 1.f;
+        const float keep = m_run[c] > -INFINITY ? alpha : 0.f;
+        l_run[c] *= keep;
+#pragma unroll
+        for (int tt = 0; tt < kTiles; ++tt) O[c][tt] *= keep;
+        m_run[c] = m_new;
+        neg_mc = m_new > -INFINITY ? -m_new * a.scale_log2 : 0.f;
 #pragma unroll
         for (int i = 0; i < TOK; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
-        float psum = pf[0];
+        psum = pf[0];
 #pragma unroll
         for (int i = 1; i < TOK; ++i) psum += pf[i];
-        if (__any(!(psum <= 256.f))) {
-          float mx = t[0];
+      }
+      l_run[c] += psum;
 #pragma unroll
-          for (int i = 1; i < TOK; ++i) mx = fmaxf(mx, t[i]);
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float m_new = fmaxf(m_run[c], mx);
-          // a row whose every key so far is masked keeps m = -inf and takes no rescale
-          const float alpha = m_new > -INFINITY ? __builtin_amdgcn_exp2f((m_run[c] - m_new) * a.scale_log2) : 1.f;
-          const float keep = m_run[c] > -INFINITY ? alpha : 0.f;
-          l_run[c] *= keep;
+      for (int half = 0; half < TOK / 8; ++half) {
+        uint32_t hw[4], lw[4];
 #pragma unroll
-          for (int tt = 0; tt < kTiles; ++tt) O[c][tt] *= keep;
-          m_run[c] = m_new;
-          neg_mc = m_new > -INFINITY ? -m_new * a.scale_log2 : 0.f;
-#pragma unroll
-          for (int i = 0; i < TOK; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[i], a.scale_log2, neg_mc));
-          psum = pf[0];
-#pragma unroll
-          for (int i = 1; i < TOK; ++i) psum += pf[i];
-        }
-        l_run[c] += psum;
-#pragma unroll
-        for (int half = 0; half < TOK / 8; ++half) {
-          uint32_t hw[4], lw[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) split_f16x2(pf[8 * half + 2 * i], pf[8 * half + 2 * i + 1], hw[i], lw[i]);
-          P[c][half][0] = __builtin_bit_cast(v8h, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-          P[c][half][1] = __builtin_bit_cast(v8h, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-        }
+        for (int i = 0; i < 4; ++i) split_f16x2(pf[8 * half + 2 * i], pf[8 * half + 2 * i + 1], hw[i], lw[i]);
+        P[c][half][0] = __builtin_bit_cast(v8h, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        P[c][half][1] = __builtin_bit_cast(v8h, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
     }
-    // the next step's keys and values (past the last step: a clamped page; its
-    // values cleared)
-    pf_store_k<D>(kr, ODD ? kbuf0 : kbuf1, vx, tid);
-    pf_store_v<D>(vr, ODD ? vbuf0 : vbuf1, vx, vrho, vpart, v_valid(s + 1));
-    load_raw(kr, vr, ids);                                     // step s + 2
-    ids = page_ids(s + 3);
-    if (active) {
-      // Output tiles in pairs: the 16 MFMAs of a pair touch each of its four
-      // accumulators every fourth MFMA, so that no MFMA waits for the result of
-      // the one before it.  V^T operands are read a pair ahead.
-      const uint8_t* vb = ODD ? vbuf1 : vbuf0;
-      auto rd = [&](int q, int h) { return *reinterpret_cast<const v8h*>(vb + pf_v_off(16 * q + r16, 2 * j4 + h)); };
-      v8h va[2][2][2];                                         // [pair buffer][tile of the pair][half]
+  };
+  // PV of both column blocks.  Output tiles in pairs: the 16 MFMAs of a pair
+  // touch each of its four accumulators every fourth MFMA, so that no MFMA waits
+  // for the result of the one before it.  V^T operands are read a pair ahead.
+  auto pv_sub = [&](int sub, const uint8_t* vb) __attribute__((always_inline)) {
+    auto rd = [&](int q, int h) {
+      return *reinterpret_cast<const v8h*>(vb + pf_v_off(16 * q + r16, 8 * sub + 2 * j4 + h));
+    };
+    v8h va[2][2][2];                                           // [pair buffer][tile of the pair][half]
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq)
+    for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) va[0][qq][h] = rd(qq, h);
+      for (int h = 0; h < 2; ++h) va[0][qq][h] = rd(qq, h);
 #pragma unroll
-      for (int qp = 0; qp < kTiles / 2; ++qp) {
-        if (qp + 1 < kTiles / 2) {
+    for (int qp = 0; qp < kTiles / 2; ++qp) {
+      if (qp + 1 < kTiles / 2) {
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) va[(qp + 1) & 1][qq][h] = rd(2 * (qp + 1) + qq, h);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
           for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) va[(qp + 1) & 1][qq][h] = rd(2 * (qp + 1) + qq, h);
-        }
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-            for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-              for (int c = 0; c < kPfNB; ++c)
-                O[c][2 * qp + qq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[qp & 1][qq][half], P[c][half][hl],
-                                                                          O[c][2 * qp + qq], 0, 0, 0);
-      }
+            for (int c = 0; c < kPfNB; ++c)
+              O[c][2 * qp + qq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[qp & 1][qq][half], P[c][half][hl],
+                                                                        O[c][2 * qp + qq], 0, 0, 0);
     }
+  };
+
+  // One step s: the keys and values of step s in LDS buffers s & 1, the raw keys
+  // and values of step s + 1 in kr, vr.
+  auto step = [&](auto mask_t, auto odd_t, int s) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(odd_t)::value;                // s & 1, known where the step is placed
+    const bool active = !decltype(mask_t)::value || s <= s_last;   // wave-uniform
+    const uint8_t* kb = ODD ? kbuf1 : kbuf0;
+    const uint8_t* vb = ODD ? vbuf1 : vbuf0;
+    if (active) {
+      softmax_sub(mask_t, s, 0, kb);
+      pv_sub(0, vb);
+      softmax_sub(mask_t, s, 1, kb);
+      pv_sub(1, vb);
+    }
+    // the next step's keys and values (past the last step: a clamped page; its
+    // values cleared), after the PV so that the probabilities are no longer live
+    pf_store_k<D>(kr, ODD ? kbuf0 : kbuf1, vx, tid);
+    pf_store_v<D>(vr, ODD ? vbuf0 : vbuf1, vx, vp, vpart, v_valid(s + 1));
+    load_raw(kr, vr, ids);                                     // step s + 2
+    ids = page_ids(s + 3);
     __syncthreads();                                           // buffers s & 1 are free again
   };
   using Free = std::false_type;
@@ -2488,7 +2517,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
       for (int k = 0; k < PC; ++k) o[k] = st[rloc * D + l32 + 32 * k];
       const float l = stl[rloc];
       const bool live = row < nrows;
-      const int64_t orow = live ? (int64_t)(q0 + t0 + row / a.G) * a.Hq + (int64_t)hk * a.G + row % a.G : 0;
+      const int rg = div_g(row);
+      const int64_t orow = live ? (int64_t)(q0 + t0 + rg) * a.Hq + (int64_t)hk * a.G + row - rg * a.G : 0;
       if (a.unrot) store_row32<D, true, true>(o, l, a.out + orow * D, live, lane, a.rot);
       else store_row32<D, false, true>(o, l, a.out + orow * D, live, lane, a.rot);
     }
@@ -2515,6 +2545,7 @@ hipError_t launch_prefill(const PrefillArgs& p, hipStream_t s) {
   a.hmask = p.hmask;
   a.G = p.Hq / p.Hkv;
   a.QT = kPfRows / a.G;
+  a.g_mul = (65536u + (uint32_t)a.G - 1u) / (uint32_t)a.G;
   a.scale_log2 = p.sm_scale * 1.4426950408889634f;
   a.rot = p.rot;
   a.unrot = p.rot.k_only ? 0 : 1;
