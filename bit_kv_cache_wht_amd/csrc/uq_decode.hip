@@ -2462,15 +2462,19 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PfArgs a) 
     if (active) {
       softmax_sub(mask_t, s, 0, kb);
       pv_sub(0, vb);
-      softmax_sub(mask_t, s, 1, kb);
-      pv_sub(1, vb);
     }
     // the next step's keys and values (past the last step: a clamped page; its
-    // values cleared), after the PV so that the probabilities are no longer live
+    // values cleared), between the sub-steps: after a PV, so that no
+    // probabilities are live, and with a sub-step's work on each side for the
+    // other wave of the SIMD to overlap (at the step's end it ran 3% slower)
     pf_store_k<D>(kr, ODD ? kbuf0 : kbuf1, vx, tid);
     pf_store_v<D>(vr, ODD ? vbuf0 : vbuf1, vx, vp, vpart, v_valid(s + 1));
     load_raw(kr, vr, ids);                                     // step s + 2
     ids = page_ids(s + 3);
+    if (active) {
+      softmax_sub(mask_t, s, 1, kb);
+      pv_sub(1, vb);
+    }
     __syncthreads();                                           // buffers s & 1 are free again
   };
   using Free = std::false_type;
