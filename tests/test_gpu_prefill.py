@@ -31,6 +31,11 @@ CASES = {
     # one query head per KV head: a workgroup's 256 rows are 256 consecutive
     # positions, so its waves reach the diagonal at different steps
     "mha_long_prompts": (3, 2, 2, 128, [1000, 531, 777], [300, 531, 777], "bf16"),
+    # query groups that do not divide a workgroup's 256 rows: 42 tokens x 6 heads
+    # (4 padding rows) and 51 x 5 (1), so row / G and row % G cross token
+    # boundaries inside a 16-row block
+    "group6": (3, 12, 2, 128, [600, 257, 90], [300, 257, 45], "bf16"),
+    "group5_d64_f32": (2, 10, 2, 64, [333, 129], [200, 129], "f32"),
 }
 
 
