@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--scrub-mb", type=int, default=1024,
                     help="read a buffer of this size before every scrubbed step, so that the 256 MB last-level "
                          "cache holds no cache page; the headline is the scrubbed step")
+    ap.add_argument("--oracle-times", action="store_true",
+                    help="time only the CPU oracle on every configuration (tiny, the 65,536 x 8 append, "
+                         "decode_gqa, long, ragged) on this host's cores and print one JSON line; no GPU")
     ap.add_argument("--pmc-pass", choices=sorted(PMC_KINDS),
                     help="run only one kernel's calls and a 1 GiB device copy (for rocprofv3 --pmc runs)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
@@ -613,8 +616,9 @@ def _oracle_pair_prepare(wl, pair):
     npg = (L + 15) // 16
     t0, n_new = int(wl.tok_offsets[b]), int(wl.new_lens[b])
     kp, vp = O.new_pool(O.FMT_FP4, npg, 1, d), O.new_pool(O.FMT_FP4, npg, 1, d)
-    O.append(O.FMT_FP4, kp, vp, wl.k[t0:t0 + L - n_new, hk:hk + 1], wl.v[t0:t0 + L - n_new, hk:hk + 1],
-             np.arange(L - n_new, dtype=np.int32), in_dtype=wl.in_dtype)
+    if L > n_new:                                        # a prefix (the tiny config has none)
+        O.append(O.FMT_FP4, kp, vp, wl.k[t0:t0 + L - n_new, hk:hk + 1], wl.v[t0:t0 + L - n_new, hk:hk + 1],
+                 np.arange(L - n_new, dtype=np.int32), in_dtype=wl.in_dtype)
     return b, hk, kp, vp
 
 
@@ -692,6 +696,73 @@ def cpu_baseline(wl, budget_s):
                       f"float64 numpy; wall time scaled to the whole step (prefix quantization untimed)"}
 
 
+def _oracle_append_worker(wl, lo, hi, barrier, out):
+    import threadpoolctl
+    import oracle as O
+    with threadpoolctl.threadpool_limits(1):
+        kp = O.new_pool(O.FMT_FP4, wl.num_pages, wl.num_kv_heads, wl.head_dim)
+        vp = O.new_pool(O.FMT_FP4, wl.num_pages, wl.num_kv_heads, wl.head_dim)
+        barrier.wait()
+        t0 = time.perf_counter()
+        if hi > lo:
+            O.append(O.FMT_FP4, kp, vp, wl.k[lo:hi], wl.v[lo:hi], wl.slot_mapping[lo:hi], in_dtype=wl.in_dtype)
+        t1 = time.perf_counter()
+    out.put((hi - lo, t0, t1))
+
+
+def cpu_append_baseline(wl):
+    """The oracle's FP4 append of the whole workload, its tokens split into one
+    contiguous slice per host core (forked workers, BLAS on one thread, each
+    with a pool of its own); the wall time from the common start to the last
+    worker's end."""
+    import multiprocessing as mp
+    cores = oracle_cores()
+    T = wl.total_tokens
+    cuts = [T * w // cores for w in range(cores + 1)]
+    ctx = mp.get_context("fork")
+    barrier, out = ctx.Barrier(cores), ctx.Queue()
+    procs = [ctx.Process(target=_oracle_append_worker, args=(wl, cuts[w], cuts[w + 1], barrier, out))
+             for w in range(cores)]
+    for p in procs:
+        p.start()
+    res = [out.get() for _ in procs]
+    for p in procs:
+        p.join()
+    wall = max(r[2] for r in res) - min(r[1] for r in res)
+    return {"value": round(wall * 1e6, 1), "unit": "us/call", "cores": cores, "kind": "oracle",
+            "tokens_per_s": round(T / wall),
+            "sample": f"all {T} tokens x {wl.num_kv_heads} KV heads, one slice of tokens per worker process, "
+                      f"float64 numpy"}
+
+
+def oracle_times(args):
+    """The oracle alone on every configuration, on the host cores this process
+    may use (no GPU): the whole step of the tiny config, the 65,536 x 8 append,
+    and the decode step (append of the new token(s) + decode) of decode_gqa,
+    long and ragged, each as cpu_baseline measures it."""
+    import platform
+    from bit_kv_cache_wht_amd import workloads as W
+    res = {}
+    for name in ("tiny", "decode_gqa", "long", "ragged"):
+        log(f"oracle: generating {name}")
+        wl = make_workload(name)
+        log(f"oracle: {describe(wl)}")
+        res[name] = cpu_baseline(wl, args.cpu_seconds)
+        log(f"oracle: {name} {res[name]['value'] / 1e3:.1f} ms per step")
+        del wl
+    log("oracle: generating the append workload")
+    wl = W.append_only()
+    res["append_65536x8x128"] = cpu_append_baseline(wl)
+    log(f"oracle: append {res['append_65536x8x128']['value'] / 1e3:.1f} ms per call")
+    cpu = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    print(json.dumps({"oracle_times": res, "cores": oracle_cores(), "cpu": cpu}), flush=True)
+
+
 def describe(wl):
     lens = wl.seq_lens
     ctx = f"{int(lens.min())}..{int(lens.max())}" if lens.min() != lens.max() else f"{int(lens.max())}"
@@ -754,6 +825,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.oracle_times:
+        oracle_times(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this hot path needs no "

@@ -71,3 +71,21 @@ def test_counter_summary_needs_the_kernels_dispatches(tmp_path, monkeypatch):
     _counter_csv(fetch, "FETCH_SIZE", [], [1.0 * (1 << 20)])
     with pytest.raises(SystemExit):
         bench.summarize_counters("decode", [str(fetch)])
+
+
+def test_oracle_baseline_of_a_step_without_prefix():
+    # the tiny configuration writes its whole sequence in the step: no prefix to
+    # build, one (sequence, KV head) pair
+    from bit_kv_cache_wht_amd import workloads as W
+    r = bench.cpu_baseline(W.tiny(), 1.0)
+    assert r["kind"] == "oracle" and r["unit"] == "us/step" and r["value"] > 0
+    assert r["sample"].startswith("1 of 1 ")
+
+
+def test_oracle_append_baseline_covers_every_token():
+    from bit_kv_cache_wht_amd import workloads as W
+    wl = W.make_workload("append_small", 1, 2, 2, 64, [300], [300], seed=5)
+    r = bench.cpu_append_baseline(wl)
+    assert r["kind"] == "oracle" and r["unit"] == "us/call" and r["value"] > 0
+    assert r["sample"].startswith("all 300 tokens x 2 KV heads")
+    assert abs(r["tokens_per_s"] - 300 / (r["value"] * 1e-6)) <= 0.01 * r["tokens_per_s"]
