@@ -1979,17 +1979,19 @@ DecodeLayout decode_layout(int format, int B, int Hq, int Hkv, int D) {
 // A workgroup of 8 waves (two per SIMD) takes kPfRows query rows, rows
 // r = t G + h for QT = kPfRows / G consecutive chunk tokens t of one sequence and
 // the G query heads of one KV head, and walks the cache from position 0 to its
-// last token's position in steps of 4 pages (64 keys).  Per step:
-//   - the values are converted once for the whole workgroup: each lane takes
-//     part of one code row of one page (a channel pair, 8 slots at d = 128),
+// last token's position in steps of 8 pages (128 keys), each two MFMA sub-steps
+// of 4 pages (64 keys).  Per step:
+//   - the values are converted once for the whole workgroup: wave x takes page
+//     x of the step, each lane one channel pair of it (all 16 slots at d = 128),
 //     turns it into float16 with the hardware FP4 converter and the slots' group
 //     scales, and writes both channels transposed ([channel][token]) into one of
 //     two LDS buffers (the next step's, while this step's is read);
 //   - the keys are staged the same way, as the pages' bytes (PfK), and every
 //     wave reads its operands from there in the FP4 decode's layout; then, for
-//     its two 16-row column blocks, it runs the scaled-MFMA QK, the online
-//     softmax with lazy rescaling, and the PV on f16 MFMAs with P as hi + lo
-//     and V^T operands read from LDS;
+//     its two 16-row column blocks and each sub-step, it runs the scaled-MFMA
+//     QK, the online softmax with lazy rescaling, and the PV on f16 MFMAs with
+//     P as hi + lo and V^T operands read from LDS (the next step's staging sits
+//     between the two sub-steps);
 //   - one barrier, after which the buffer just read may be written again.
 // Logits past a row's own position get -inf (causal); steps that lie wholly
 // before a wave's rows take no mask, and steps wholly past them no work.  Value
