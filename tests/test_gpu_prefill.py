@@ -5,7 +5,9 @@ Outputs are compared with the oracle (each row = the decode over its causal
 prefix) within relative L2 1e-3 and max-abs 5e-3.
 
 Cases: chunks after a prefix and whole prompts, chunk lengths that are not
-multiples of a workgroup's tokens, empty chunks, GQA groups of 1, 4, 8 and 16,
+multiples of a workgroup's tokens, empty chunks, GQA groups of 1, 4, 5, 6, 8, 16, 32
+and 128 (5 and 6 do not divide a workgroup's 256 rows; 128 is the largest the
+boundary takes),
 whole prompts of several hundred tokens with one query head per KV head, 600
 sequences (the workgroups' plan in several chunks),
 d = 64 and 128, bf16 and f32 inputs, and single-token chunks (which must also
@@ -36,6 +38,10 @@ CASES = {
     # boundaries inside a 16-row block
     "group6": (3, 12, 2, 128, [600, 257, 90], [300, 257, 45], "bf16"),
     "group5_d64_f32": (2, 10, 2, 64, [333, 129], [200, 129], "f32"),
+    # the largest group the boundary takes (128 query heads per KV head: two
+    # chunk tokens per workgroup), and 32
+    "group128_d64": (2, 128, 1, 64, [90, 40], [20, 40], "bf16"),
+    "group32": (2, 64, 2, 128, [300, 77], [100, 77], "bf16"),
 }
 
 
